@@ -1,0 +1,223 @@
+"""fp64 definition of LR precompute, the per-agent value cache and causal GQA attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Every array is widened
+to float64 on entry; results are float64.
+
+Notation (LRAgent page, "prerequisites" and "core method"; PReCache summary
+page, "how it works"):
+  X        hidden states, one row per token             [T, d_model]
+  W0       frozen projection of the backbone
+  A_k, B_k LoRA down / up projection of agent k, A_k: d_model x r, B_k: r x d_out
+  V_base = X W0          the base value cache, shared by all agents
+  V_lr   = X A_k         the agent's rank-r value cache (L x r)
+  V_k    = V_base + V_lr B_k   the agent's full value cache (never built by the GPU path)
+Keys carry no low-rank part (LoRA on the query and value projections only:
+PReCache summary page, "setup and results"), so K_base is the key cache of
+every agent.
+
+Readings where the pages are silent (each is also listed in the design notes):
+  * scale is passed in; the workloads use 1/sqrt(d_head) (FlashAttention's
+    convention; the pages state no scale).
+  * query head h reads KV head floor(h / G), G = n_q / n_kv (contiguous GQA
+    groups, the Llama convention; the pages name Llama/Ministral models).
+  * V_lr holds all agents side by side: agent k owns columns k*r .. k*r+r-1
+    (PReCache: every agent's down-projection is applied to the same hidden
+    states in one pass, so their outputs sit in one row per token).
+  * B_k is r x (n_kv * d_head); KV head g uses its columns g*d .. g*d+d-1.
+  * no LoRA scaling factor (alpha / r) appears on the pages: B_k is used as given.
+  * causal mask is bottom-right aligned: query i of a chunk of L_C new tokens
+    sits at absolute position L_P + i and sees keys 0 .. L_P + i. A decode
+    query sits at the last position of its range and sees all kv_len keys.
+  * a query with no visible key (kv_len = 0) returns zeros.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------- a1: LR precompute
+def lr_precompute(X, A) -> np.ndarray:
+    """All agents' rank-r caches in one product: ``X [A_1 .. A_N]``.
+
+    PReCache page, PreLRShared subsection: when a segment is first processed,
+    every agent's down-projection is applied to its hidden states. LRAgent
+    page, "method steps" step (2): ``V_lr = X A`` is stored with shape L x r.
+    X: [T, d_model]; A: [d_model, N*r] (agent k = column block k). Returns [T, N*r].
+    """
+    return _f64(X) @ _f64(A)
+
+
+def lr_precompute_into(V_lr, X, A, out_rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Return a copy of the cache ``V_lr`` [rows, ld] whose rows ``out_rows[t]`` (default t)
+    hold row t of ``lr_precompute(X, A)`` in columns 0 .. N*r-1; every other entry is unchanged."""
+    res = _f64(V_lr).copy()
+    new = lr_precompute(X, A)
+    rows = np.arange(new.shape[0]) if out_rows is None else np.asarray(out_rows, dtype=np.int64)
+    res[rows, : new.shape[1]] = new
+    return res
+
+
+# --------------------------------------------------------------------------- layout maps
+def kv_head_of(h: int, group: int) -> int:
+    """KV head read by query head h: contiguous groups of ``group`` query heads share one KV head."""
+    return h // group
+
+
+def agent_columns(agent: int, rank: int) -> slice:
+    """Columns of the stacked LR cache owned by ``agent``."""
+    return slice(agent * rank, (agent + 1) * rank)
+
+
+# --------------------------------------------------------------------------- V_k materialised
+def agent_values(V_base, V_lr, B, agent: int) -> np.ndarray:
+    """The agent's full value cache ``V_base + V_lr[:, agent cols] B_agent``, built explicitly.
+
+    LRAgent page, "core method": the adapted value projection splits into the
+    shared ``X W0`` and the agent's ``(X A_i) B_i``; the LR cache keeps
+    ``X A_i`` and B_i restores the full width on demand.
+    V_base: [L, n_kv, d]; V_lr: [L, >= N*r]; B: [N, r, n_kv*d]. Returns [L, n_kv, d].
+    """
+    V_base = _f64(V_base)
+    B = _f64(B)
+    L, n_kv, d = V_base.shape
+    rank = B.shape[1]
+    lr = _f64(V_lr)[:, agent_columns(agent, rank)] @ B[agent]  # [L, n_kv*d]
+    return V_base + lr.reshape(L, n_kv, d)
+
+
+# --------------------------------------------------------------------------- mask + softmax
+def visible(q_pos: Iterable[int], L: int) -> np.ndarray:
+    """Causal visibility [len(q_pos), L]: key j is visible to a query at absolute position p iff j <= p."""
+    q_pos = np.asarray(list(q_pos) if not isinstance(q_pos, np.ndarray) else q_pos, dtype=np.int64)
+    return np.arange(L, dtype=np.int64)[None, :] <= q_pos[:, None]
+
+
+def softmax_rows(S, mask) -> np.ndarray:
+    """Two-pass softmax of each row of S over its visible entries (fp64).
+
+    Pass 1 takes the row maximum over visible entries, pass 2 exponentiates the
+    shifted scores and divides by their sum. Masked entries are exactly 0; a
+    row with no visible entry is all zeros.
+    """
+    S = _f64(S)
+    mask = np.asarray(mask, dtype=bool)
+    Sm = np.where(mask, S, -np.inf)
+    m = Sm.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    E = np.where(mask, np.exp(Sm - m), 0.0)
+    l = E.sum(axis=-1, keepdims=True)
+    return np.divide(E, l, out=np.zeros_like(E), where=l > 0)
+
+
+def attention_probs(Q, K, q_pos, scale: float, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Softmax probabilities P [len(heads), Lq, L] of scaled dot-product scores under the causal mask.
+
+    Q: [Lq, n_q, d] queries at absolute positions q_pos; K: [L, n_kv, d].
+    Score of query i, head h, key j: ``scale * <Q[i, h], K[j, kv_head_of(h)]>``.
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    Lq, n_q, d = Q.shape
+    L, n_kv, _ = K.shape
+    G = n_q // n_kv
+    heads = range(n_q) if heads is None else heads
+    mask = visible(q_pos, L)
+    out = []
+    for h in heads:
+        g = kv_head_of(h, G)
+        S = scale * (Q[:, h, :] @ K[:, g, :].T)
+        out.append(softmax_rows(S, mask))
+    return np.stack(out) if out else np.zeros((0, Lq, L))
+
+
+def attention(Q, K, Vfull, q_pos, scale: float, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O[i, h] = sum_j P[h, i, j] * Vfull[j, kv_head_of(h)]  with P from ``attention_probs``.
+
+    Returns [Lq, len(heads), d]."""
+    Q = _f64(Q)
+    Vfull = _f64(Vfull)
+    n_q = Q.shape[1]
+    G = n_q // Vfull.shape[1]
+    heads = list(range(n_q)) if heads is None else list(heads)
+    P = attention_probs(Q, K, q_pos, scale, heads)
+    O = np.empty((Q.shape[0], len(heads), Vfull.shape[2]))
+    for t, h in enumerate(heads):
+        O[:, t, :] = P[t] @ Vfull[:, kv_head_of(h, G), :]
+    return O
+
+
+# --------------------------------------------------------------------------- the three calls
+def attn_prefill(Q, K_base, V_base, V_lr, B, agent: int, L_P: int, scale: float,
+                 rows: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Causal chunked prefill for one agent: L_C new queries over the L_P + L_C keys.
+
+    LRAgent page, "method steps" (3)-(4): attention over the shared key cache
+    and the agent's value cache; here the value cache is materialised.
+    PReCache summary page: the new chunk L_C follows the reused context L_P.
+    Q: [L_C, n_q, d]; K_base, V_base: [>= L_P+L_C, n_kv, d]; V_lr: [>= L_P+L_C, >= N*r];
+    B: [N, r, n_kv*d]. ``rows``/``heads`` restrict the output to some query rows / heads.
+    Returns [len(rows), len(heads), d].
+    """
+    Q = _f64(Q)
+    L_C = Q.shape[0]
+    L = L_P + L_C
+    rows = np.arange(L_C) if rows is None else np.asarray(rows, dtype=np.int64)
+    Va = agent_values(_f64(V_base)[:L], _f64(V_lr)[:L], B, agent)
+    return attention(Q[rows], _f64(K_base)[:L], Va, L_P + rows, scale, heads)
+
+
+def attn_decode(Q, K_base, V_base, V_lr, B, kv_start, kv_len, agents, scale: float,
+                requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """One new query per request over its key range [kv_start[b], kv_start[b] + kv_len[b]).
+
+    The query is the newest token of its range, so every key of the range is
+    visible. Requests may share rows (agents share the base cache: PReCache
+    page, PreLRShared; LRAgent page, "core method"). kv_len[b] = 0 gives zeros.
+    Q: [batch, n_q, d]. Returns [len(requests), len(heads), d].
+    """
+    Q = _f64(Q)
+    n_q, d = Q.shape[1], Q.shape[2]
+    requests = range(Q.shape[0]) if requests is None else requests
+    heads = list(range(n_q)) if heads is None else list(heads)
+    out = []
+    for b in requests:
+        n = int(kv_len[b])
+        if n == 0:
+            out.append(np.zeros((len(heads), d)))
+            continue
+        r0 = int(kv_start[b])
+        K = _f64(K_base[r0:r0 + n])
+        Va = agent_values(V_base[r0:r0 + n], V_lr[r0:r0 + n], B, int(agents[b]))
+        out.append(attention(Q[b:b + 1], K, Va, [n - 1], scale, heads)[0])
+    return np.stack(out) if out else np.zeros((0, len(heads), d))
+
+
+def attn_factored(Q, K, V_base, V_lr, B, agent: int, q_pos, scale: float) -> np.ndarray:
+    """Attend-then-expand: ``P V_base + (P V_lr[:, agent cols]) B_agent`` per head.
+
+    LRAgent page, "core method" and "technical novelty": by associativity the
+    LR cache is attended in rank space and expanded by B once per query row,
+    instead of expanding every cached row first. Equal to ``attention`` over
+    ``agent_values`` in exact arithmetic; kept here so that identity can be
+    tested. Returns [Lq, n_q, d].
+    """
+    Q = _f64(Q)
+    V_base = _f64(V_base)
+    B = _f64(B)
+    Lq, n_q, d = Q.shape
+    L, n_kv, _ = V_base.shape
+    rank = B.shape[1]
+    G = n_q // n_kv
+    P = attention_probs(Q, K, q_pos, scale)
+    lr = _f64(V_lr)[:L, agent_columns(agent, rank)]
+    O = np.empty((Lq, n_q, d))
+    for h in range(n_q):
+        g = kv_head_of(h, G)
+        O[:, h, :] = P[h] @ V_base[:, g, :] + (P[h] @ lr) @ B[agent][:, g * d:(g + 1) * d]
+    return O

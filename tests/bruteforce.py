@@ -1,0 +1,58 @@
+"""Pure-Python brute force of LoRA-valued causal attention, for tiny inputs only.
+
+Written independently of ``oracle``: nested lists, ``math.exp`` and
+``math.fsum``, no NumPy. It follows the definitions directly: the agent's value
+row is the base row plus the LR row times B (LRAgent page, core method), and
+each query takes a max-shifted softmax over the keys at or before its position.
+"""
+import math
+
+
+def _tolist(a):
+    return a.tolist() if hasattr(a, "tolist") else a
+
+
+def _value(Vb, Vlr, B, j, g, c, agent, r, d):
+    lr = math.fsum(Vlr[j][agent * r + k] * B[agent][k][g * d + c] for k in range(r))
+    return Vb[j][g][c] + lr
+
+
+def _one_query(q_h, K, Vb, Vlr, B, keys, g, agent, scale):
+    d = len(q_h)
+    r = len(B[0])
+    if not keys:
+        return [0.0] * d
+    s = [scale * math.fsum(q_h[c] * K[j][g][c] for c in range(d)) for j in keys]
+    top = max(s)
+    w = [math.exp(x - top) for x in s]
+    tot = math.fsum(w)
+    return [math.fsum(w[t] * _value(Vb, Vlr, B, j, g, c, agent, r, d) for t, j in enumerate(keys)) / tot
+            for c in range(d)]
+
+
+def prefill(Q, K, Vb, Vlr, B, agent, L_P, scale):
+    Q, K, Vb, Vlr, B = map(_tolist, (Q, K, Vb, Vlr, B))
+    n_q = len(Q[0])
+    n_kv = len(K[0])
+    out = []
+    for i in range(len(Q)):
+        keys = list(range(L_P + i + 1))
+        out.append([_one_query(Q[i][h], K, Vb, Vlr, B, keys, (h * n_kv) // n_q, agent, scale) for h in range(n_q)])
+    return out
+
+
+def decode(Q, K, Vb, Vlr, B, kv_start, kv_len, agents, scale):
+    Q, K, Vb, Vlr, B = map(_tolist, (Q, K, Vb, Vlr, B))
+    n_q = len(Q[0])
+    n_kv = len(K[0])
+    out = []
+    for b in range(len(Q)):
+        keys = list(range(int(kv_start[b]), int(kv_start[b]) + int(kv_len[b])))
+        out.append([_one_query(Q[b][h], K, Vb, Vlr, B, keys, (h * n_kv) // n_q, int(agents[b]), scale)
+                    for h in range(n_q)])
+    return out
+
+
+def precompute(X, A):
+    X, A = _tolist(X), _tolist(A)
+    return [[math.fsum(X[t][c] * A[c][n] for c in range(len(A))) for n in range(len(A[0]))] for t in range(len(X))]

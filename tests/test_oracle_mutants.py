@@ -1,0 +1,102 @@
+"""Planted mistakes in the oracle (CPU only) must each be caught by the pins.
+
+Every mutant below replaces one step of ``oracle.lora_attention`` with a
+plausible slip (dropped term, wrong sign, off-by-one, wrong index, transposed
+operand). The test runs the pin checks of ``test_oracle_pins`` against the
+mutated oracle and asserts that at least one of them fails. The mutation is
+undone after each test by ``monkeypatch``.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import lora_attention as LA
+from tests import test_oracle_pins as pins
+
+_orig_softmax = LA.softmax_rows
+_orig_agent_values = LA.agent_values
+
+
+def _checks():
+    golden = pins._load_golden()
+    yield lambda: [pins.test_golden_prefill(c) for c in golden["prefill"]]
+    yield lambda: [pins.test_golden_decode(c) for c in golden["decode"]]
+    yield lambda: [pins.test_golden_precompute(c) for c in golden["precompute"]]
+    yield lambda: pins.test_zero_lora_is_standard_causal_gqa_attention(4, 2, 5, 7)
+    yield lambda: pins.test_bruteforce_prefill(4, 2, 8, 2, 3, 5, 2)
+    yield lambda: pins.test_bruteforce_prefill(8, 2, 4, 4, 0, 7, 1)
+    yield lambda: pins.test_bruteforce_decode_with_shared_and_empty_ranges()
+    yield lambda: pins.test_precompute_triple_loop_and_one_hot()
+    yield lambda: pins.test_projection_level_lora_split()
+    yield lambda: pins.test_probability_rows_and_causal_zeros()
+
+
+def _some_pin_fails():
+    for check in _checks():
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _mut_agent_values_no_lr(V_base, V_lr, B, agent):
+    return np.asarray(V_base, np.float64).copy()
+
+
+def _mut_agent_values_transposed(V_base, V_lr, B, agent):
+    V_base = np.asarray(V_base, np.float64)
+    L, n_kv, d = V_base.shape
+    r = np.asarray(B).shape[1]
+    lr = np.asarray(V_lr, np.float64)[:, agent * r:(agent + 1) * r] @ np.asarray(B, np.float64)[agent]
+    return V_base + lr.reshape(L, d, n_kv).transpose(0, 2, 1)
+
+
+def _mut_agent_values_minus(V_base, V_lr, B, agent):
+    return 2 * np.asarray(V_base, np.float64) - _orig_agent_values(V_base, V_lr, B, agent)
+
+
+def _mut_softmax_no_normalise(S, mask):
+    S = np.where(mask, np.asarray(S, np.float64), -np.inf)
+    return np.where(mask, np.exp(S - S.max(-1, keepdims=True)), 0.0)
+
+
+def _mut_softmax_flipped(S, mask):
+    return _orig_softmax(-np.asarray(S, np.float64), mask)
+
+
+MUTANTS = {
+    "head_map_interleaved": ("kv_head_of", lambda h, group: h % group),
+    "head_map_coarse": ("kv_head_of", lambda h, group: h // (2 * group)),
+    "agent_cols_off_by_one": ("agent_columns", lambda a, r: slice(a * r + 1, (a + 1) * r + 1)),
+    "agent_cols_wrong_agent": ("agent_columns", lambda a, r: slice(((a + 1) % 3) * r, ((a + 1) % 3 + 1) * r)),
+    "mask_strict": ("visible", lambda q_pos, L: np.arange(L)[None, :] < np.asarray(q_pos)[:, None]),
+    "mask_top_left": ("visible", lambda q_pos, L: np.arange(L)[None, :] <= (np.asarray(q_pos) - np.min(q_pos))[:, None]),
+    "mask_none": ("visible", lambda q_pos, L: np.ones((len(np.asarray(q_pos)), L), bool)),
+    "lr_term_dropped": ("agent_values", _mut_agent_values_no_lr),
+    "lr_term_transposed": ("agent_values", _mut_agent_values_transposed),
+    "lr_term_sign": ("agent_values", _mut_agent_values_minus),
+    "softmax_unnormalised": ("softmax_rows", _mut_softmax_no_normalise),
+    "softmax_sign": ("softmax_rows", _mut_softmax_flipped),
+    "precompute_transposed_operand": ("lr_precompute", lambda X, A: np.asarray(X, float) @ np.asarray(A, float)[::-1]),
+    "precompute_dropped_row": ("lr_precompute", lambda X, A: (np.asarray(X, float) @ np.asarray(A, float)) * (np.arange(len(X)) > 0)[:, None]),
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not _some_pin_fails()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(LA, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _some_pin_fails(), f"mutant {name} passed every pin"
+
+
+def test_scale_dropped_is_caught(monkeypatch):
+    orig = LA.attention_probs
+    monkeypatch.setattr(LA, "attention_probs", lambda Q, K, q_pos, scale, heads=None: orig(Q, K, q_pos, 1.0, heads))
+    assert _some_pin_fails()

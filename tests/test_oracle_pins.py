@@ -1,0 +1,265 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against what the pages and the mathematics fix:
+a library routine for the B = 0 special case, the associativity identity the
+kernel is built on, invariants of softmax attention, closed forms, the
+hand-derived fixtures in tests/golden/, and a pure-Python brute force.
+``test_oracle_mutants.py`` plants mistakes in the oracle and checks that these
+pins catch them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def small_shape(n_q=4, n_kv=2, d=8, r=2, N=3, d_model=16):
+    return W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=N, d_model=d_model, dtype="f32")
+
+
+def f64(t):
+    return t.as_f64()
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ----------------------------------------------------------------------------- golden fixtures
+def _load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _load_golden()["prefill"], ids=lambda c: c["name"])
+def test_golden_prefill(case):
+    for agent, exp in case["expected"].items():
+        O = oracle.attn_prefill(case["Q"], case["K"], case["V_base"], case["V_lr"], case["B"],
+                                int(agent), case["L_P"], case["scale"])
+        np.testing.assert_allclose(O, np.array(exp), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", _load_golden()["decode"], ids=lambda c: c["name"])
+def test_golden_decode(case):
+    O = oracle.attn_decode(case["Q"], np.array(case["K"]), np.array(case["V_base"]), np.array(case["V_lr"]),
+                           case["B"], case["kv_start"], case["kv_len"], case["agent"], case["scale"])
+    np.testing.assert_allclose(O, np.array(case["expected"]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", _load_golden()["precompute"], ids=lambda c: c["name"])
+def test_golden_precompute(case):
+    np.testing.assert_array_equal(oracle.lr_precompute(case["X"], case["A"]), np.array(case["expected_product"]))
+    cache = np.zeros((case["cache_rows"], case["cache_cols"]))
+    got = oracle.lr_precompute_into(cache, case["X"], case["A"], case["out_rows"])
+    np.testing.assert_array_equal(got, np.array(case["expected_cache"]))
+
+
+# ----------------------------------------------------------------------------- library special case
+@pytest.mark.parametrize("n_q,n_kv,L_P,L_C", [(4, 2, 5, 7), (8, 2, 0, 9), (6, 6, 11, 3), (4, 1, 3, 1)])
+def test_zero_lora_is_standard_causal_gqa_attention(n_q, n_kv, L_P, L_C):
+    """B = 0 (and separately V_lr = 0) must reduce to torch's scaled_dot_product_attention in float64
+    with an explicit bottom-right causal mask and KV heads shared by contiguous query-head groups."""
+    s = small_shape(n_q=n_q, n_kv=n_kv, d=16, r=4)
+    c = W.random_prefill((900, n_q, n_kv, L_P, L_C), s, L_P, L_C, agent=1, b_std=1.0)
+    L = L_P + L_C
+    q = torch.from_numpy(f64(c.Q)).permute(1, 0, 2)          # [n_q, L_C, d]
+    k = torch.from_numpy(f64(c.K)).permute(1, 0, 2)          # [n_kv, L, d]
+    v = torch.from_numpy(f64(c.V)).permute(1, 0, 2)
+    mask = torch.arange(L)[None, :] <= (L_P + torch.arange(L_C))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q[None], k[None], v[None], attn_mask=mask, scale=s.scale, enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    # second library route: explicit repeat of each KV head over its query-head group
+    G = n_q // n_kv
+    ref2 = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, dim=0), v.repeat_interleave(G, dim=0), attn_mask=mask,
+        scale=s.scale).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(ref, ref2, rtol=1e-13, atol=1e-14)
+    zero_B = np.zeros_like(f64(c.B))
+    O = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), zero_B, 1, L_P, s.scale)
+    assert rel_err(O, ref) <= 1e-12
+    O2 = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), np.zeros_like(f64(c.V_lr)), f64(c.B), 1, L_P, s.scale)
+    assert rel_err(O2, ref) <= 1e-12
+
+
+# ----------------------------------------------------------------------------- associativity
+@pytest.mark.parametrize("agent", [0, 1, 2])
+def test_associativity_materialised_equals_factored(agent):
+    """P (V_lr B) = (P V_lr) B: expand-then-attend equals attend-then-expand (LRAgent, core method)."""
+    s = small_shape(n_q=8, n_kv=2, d=16, r=4)
+    c = W.random_prefill((901, agent), s, 9, 12, agent=agent, b_std=1.0)
+    O = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), agent, c.L_P, s.scale)
+    Of = oracle.attn_factored(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), agent,
+                              c.L_P + np.arange(c.L_C), s.scale)
+    assert rel_err(O, Of) <= 1e-12
+
+
+def test_projection_level_lora_split():
+    """X (W0 + A_a B_a) = X W0 + (X A_a) B_a: the merged LoRA weight (LRAgent, Multi-LoRA prerequisite)
+    against the oracle's precompute + agent value cache, for every agent."""
+    s = W.TINY_SHAPE
+    tw = W.tiny_workload()
+    X = tw.X.as_f64()
+    A = tw.A.as_f64()
+    B = tw.B.as_f64()
+    W0 = tw.W0_v.astype(np.float64)
+    V_base = (X @ W0).reshape(-1, s.n_kv, s.d_head)
+    V_lr = oracle.lr_precompute(X, A)
+    for a in range(s.n_agents):
+        merged = X @ (W0 + A[:, a * s.rank:(a + 1) * s.rank] @ B[a])
+        got = oracle.agent_values(V_base, V_lr, B, a).reshape(X.shape[0], -1)
+        assert rel_err(got, merged) <= 1e-12
+
+
+# ----------------------------------------------------------------------------- invariants
+def test_probability_rows_and_causal_zeros():
+    s = small_shape(n_q=4, n_kv=2, d=8)
+    c = W.random_prefill((902,), s, 6, 10)
+    L = c.L_P + c.L_C
+    qpos = c.L_P + np.arange(c.L_C)
+    P = oracle.attention_probs(f64(c.Q), f64(c.K), qpos, s.scale)
+    assert P.shape == (s.n_q, c.L_C, L)
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(-1) - 1.0)) <= 1e-14
+    hidden = np.arange(L)[None, :] > qpos[:, None]
+    assert np.all(P[:, hidden] == 0.0)
+    assert np.all(P[:, ~hidden] > 0.0)
+
+
+def test_softmax_shift_invariance():
+    g = np.random.default_rng(5)
+    S = g.standard_normal((7, 13))
+    mask = g.random((7, 13)) < 0.7
+    mask[:, 0] = True
+    shift = g.standard_normal((7, 1)) * 50
+    np.testing.assert_allclose(oracle.softmax_rows(S + shift, mask), oracle.softmax_rows(S, mask), rtol=0, atol=1e-14)
+
+
+def test_output_is_affine_in_B():
+    s = small_shape(n_q=4, n_kv=2, d=8, r=2)
+    c = W.random_prefill((903,), s, 4, 6, agent=2, b_std=1.0)
+    g = np.random.default_rng(6)
+    B1 = g.standard_normal(f64(c.B).shape)
+    B2 = g.standard_normal(f64(c.B).shape)
+    run = lambda B: oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), B, 2, c.L_P, s.scale)
+    lhs = run(B1 + B2)
+    rhs = run(B1) + run(B2) - run(np.zeros_like(B1))
+    assert rel_err(lhs, rhs) <= 1e-12
+
+
+def test_equal_queries_in_one_group_give_equal_outputs():
+    s = small_shape(n_q=8, n_kv=2, d=8)
+    c = W.random_prefill((904,), s, 3, 5)
+    Q = f64(c.Q).copy()
+    Q[:, 1] = Q[:, 0]   # heads 0..3 share KV head 0
+    Q[:, 5] = Q[:, 0]   # head 5 reads KV head 1
+    O = oracle.attn_prefill(Q, f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), 0, c.L_P, s.scale)
+    np.testing.assert_array_equal(O[:, 1], O[:, 0])
+    assert np.max(np.abs(O[:, 5] - O[:, 0])) > 1e-3
+
+
+def test_decode_equals_last_prefill_row():
+    s = small_shape(n_q=4, n_kv=2, d=8)
+    L = 13
+    c = W.random_prefill((905,), s, L - 1, 1, agent=1)
+    Op = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), 1, L - 1, s.scale)
+    Od = oracle.attn_decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), [0], [L], [1], s.scale)
+    assert rel_err(Od, Op) <= 1e-13
+
+
+def test_chunk_split_equivalence():
+    """Prefilling L_C = c1 + c2 tokens equals prefilling c1 then c2 with L_P advanced by c1."""
+    s = small_shape(n_q=4, n_kv=2, d=8)
+    c = W.random_prefill((906,), s, 5, 11, agent=2)
+    args = (f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), 2)
+    full = oracle.attn_prefill(f64(c.Q), *args, c.L_P, s.scale)
+    first = oracle.attn_prefill(f64(c.Q)[:4], *args, c.L_P, s.scale)
+    second = oracle.attn_prefill(f64(c.Q)[4:], *args, c.L_P + 4, s.scale)
+    assert rel_err(np.concatenate([first, second]), full) <= 1e-13
+
+
+# ----------------------------------------------------------------------------- closed forms
+def test_single_key_returns_its_value_row():
+    s = small_shape(n_q=4, n_kv=2, d=8)
+    c = W.random_prefill((907,), s, 0, 1, agent=1)
+    O = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), 1, 0, s.scale)
+    Va = f64(c.V)[0] + (f64(c.V_lr)[0, 2:4] @ f64(c.B)[1]).reshape(s.n_kv, s.d_head)
+    for h in range(s.n_q):
+        np.testing.assert_allclose(O[0, h], Va[h // 2], rtol=0, atol=1e-15)
+
+
+def test_zero_query_averages_visible_rows():
+    s = small_shape(n_q=2, n_kv=1, d=8, r=2)
+    c = W.random_prefill((908,), s, 4, 6, agent=0)
+    Q = np.zeros_like(f64(c.Q))
+    O = oracle.attn_prefill(Q, f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), 0, c.L_P, s.scale)
+    Va = f64(c.V)[:, 0] + f64(c.V_lr)[:, 0:2] @ f64(c.B)[0]
+    for i in range(c.L_C):
+        np.testing.assert_allclose(O[i, 0], Va[: c.L_P + i + 1].mean(0), rtol=0, atol=1e-14)
+
+
+def test_dominant_score_selects_its_row():
+    """One visible score above all others by >= 60 gives that key's value row to within e^-60."""
+    s = small_shape(n_q=1, n_kv=1, d=8, r=2)
+    c = W.random_prefill((909,), s, 7, 1, agent=0)
+    Q = np.zeros((1, 1, 8))
+    Q[0, 0, 0] = 1.0
+    K = np.zeros_like(f64(c.K))
+    K[3, 0, 0] = 60.0 / s.scale
+    O = oracle.attn_prefill(Q, K, f64(c.V), f64(c.V_lr), f64(c.B), 0, c.L_P, s.scale)
+    Va3 = f64(c.V)[3, 0] + f64(c.V_lr)[3, 0:2] @ f64(c.B)[0]
+    assert np.max(np.abs(O[0, 0] - Va3)) <= 8 * math.exp(-60) * (1 + np.max(np.abs(f64(c.V))) * 10)
+
+
+# ----------------------------------------------------------------------------- brute force
+@pytest.mark.parametrize("n_q,n_kv,d,r,L_P,L_C,agent", [
+    (4, 2, 8, 2, 3, 5, 0), (4, 2, 8, 2, 3, 5, 2), (8, 2, 4, 4, 0, 7, 1), (2, 2, 5, 1, 10, 6, 1), (4, 1, 8, 3, 15, 1, 2)])
+def test_bruteforce_prefill(n_q, n_kv, d, r, L_P, L_C, agent):
+    s = small_shape(n_q=n_q, n_kv=n_kv, d=d, r=r)
+    c = W.random_prefill((910, n_q, d, r, L_P, L_C), s, L_P, L_C, agent=agent, b_std=0.7)
+    O = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), agent, L_P, s.scale)
+    ref = bruteforce.prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), agent, L_P, s.scale)
+    assert rel_err(O, ref) <= 1e-13
+
+
+def test_bruteforce_decode_with_shared_and_empty_ranges():
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    c = W.random_decode((911,), s, kv_lens=[9, 16, 0, 1, 5], kv_starts=[0, 0, 3, 15, 4], rows=16,
+                        agents=[0, 1, 2, 1, 2], b_std=0.7)
+    O = oracle.attn_decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    ref = bruteforce.decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    assert rel_err(O, ref) <= 1e-13
+    assert np.all(O[2] == 0.0)
+
+
+def test_precompute_triple_loop_and_one_hot():
+    g = np.random.default_rng(7)
+    X = g.standard_normal((6, 11))
+    A = g.standard_normal((11, 9))
+    assert rel_err(oracle.lr_precompute(X, A), bruteforce.precompute(X, A)) <= 1e-14
+    onehot = np.zeros((11, 4))
+    cols = [3, 0, 10, 3]
+    for n, c in enumerate(cols):
+        onehot[c, n] = 1.0
+    np.testing.assert_array_equal(oracle.lr_precompute(X, onehot), X[:, cols])
+
+
+def test_precompute_scatter_leaves_other_rows_and_columns():
+    g = np.random.default_rng(8)
+    X = g.standard_normal((3, 5))
+    A = g.standard_normal((5, 4))
+    cache = g.standard_normal((7, 6))
+    got = oracle.lr_precompute_into(cache, X, A, [6, 0, 2])
+    np.testing.assert_array_equal(got[[1, 3, 4, 5]], cache[[1, 3, 4, 5]])
+    np.testing.assert_array_equal(got[:, 4:], cache[:, 4:])
+    np.testing.assert_array_equal(got[[6, 0, 2], :4], X @ A)

@@ -1,0 +1,411 @@
+"""Seeded synthetic inputs for the Flash-LoRA-Attention workloads.
+
+This module only draws random tensors of the right shapes, distributions and
+storage dtype. It holds none of the attention or LoRA arithmetic: both the
+fp64 CPU oracle (``oracle/``) and the HIP path consume what it produces, and
+neither imports the other.
+
+Sources of the shapes (LRAgent and PReCache pages):
+  * LoRA on the query and value projections with rank r = 8; keys carry no
+    low-rank part (PReCache summary page, "setup and results" paragraph;
+    LRAgent page, "reproducibility" section).
+  * Three role agents (plan / action / reflect) share one trajectory
+    (PReCache page, section 4.1 agent setup).
+  * Trajectories from 1.9k to 66.4k tokens (PReCache summary page, results).
+  * LLaMA-3.1-8B / Ministral-8B layer shapes: 32 query heads, 8 KV heads,
+    d_head = 128, d_model = 4096 (public model cards; the pages name the models).
+  * Root seed 42, the seed the LRAgent page reports for its experiments.
+
+Random streams: one PCG64 stream per (workload, layer, request, tensor, block)
+via ``SeedSequence(42, spawn_key=...)``. Large tensors are drawn in fixed row
+blocks, each with its own stream, so the values do not depend on how many
+threads draw them. Normals are drawn in float32, multiplied by the standard
+deviation in float32, then rounded to the storage dtype (bf16 by
+round-to-nearest-even on the bit pattern).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+ROOT_SEED = 42
+
+# Workload ids used in spawn keys (stable; never renumber).
+TINY, LLAMA_DECODE, LLAMA_PREFILL, LLAMA_LONG_DECODE, MINISTRAL_STEP = 0, 1, 2, 3, 4
+WORKLOAD_NAMES = {
+    TINY: "tiny_fp32",
+    LLAMA_DECODE: "llama31_8b_decode_b1_L1900_r8",
+    LLAMA_PREFILL: "llama31_8b_prefill_LP16384_LC2048_r8",
+    LLAMA_LONG_DECODE: "llama31_8b_decode_b16_L66400_r8",
+    MINISTRAL_STEP: "ministral_8b_step_36x_b32_L1.9k-32k_r16",
+}
+
+# Tensor ids used in spawn keys.
+T_X, T_W0K, T_W0V, T_A, T_B, T_Q, T_K, T_V, T_VLR, T_AGENT, T_LEN, T_XDEC, T_QDEC = range(13)
+
+_BLOCK_ROWS = 4096  # rows per independently seeded block of a large tensor
+
+
+# --------------------------------------------------------------------------- dtype helpers
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits.
+
+    NaN inputs stay NaN (quiet bit forced)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class HostTensor:
+    """A host tensor in its storage dtype. ``data`` is float32, or uint16 bf16 bits."""
+    data: np.ndarray
+    dtype: str  # "f32" or "bf16"
+
+    @property
+    def shape(self) -> Tuple[int, ...]:
+        return tuple(self.data.shape)
+
+    def as_f64(self) -> np.ndarray:
+        """Exact widening of the stored values to float64 (what the oracle consumes)."""
+        if self.dtype == "bf16":
+            return bf16_bits_to_f32(self.data).astype(np.float64)
+        return self.data.astype(np.float64)
+
+    def as_f32(self) -> np.ndarray:
+        if self.dtype == "bf16":
+            return bf16_bits_to_f32(self.data)
+        return np.asarray(self.data, dtype=np.float32)
+
+
+def to_storage(x32: np.ndarray, dtype: str) -> HostTensor:
+    if dtype == "bf16":
+        return HostTensor(f32_to_bf16_bits(x32), "bf16")
+    if dtype == "f32":
+        return HostTensor(np.ascontiguousarray(x32, dtype=np.float32), "f32")
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------- random streams
+def rng(*key: int) -> np.random.Generator:
+    """Independent PCG64 stream for a spawn key (workload, layer, request, tensor, ...)."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED, spawn_key=tuple(int(k) for k in key))))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal(key: Sequence[int], shape: Tuple[int, ...], std: float, dtype: str) -> HostTensor:
+    """N(0, std^2) tensor, drawn in row blocks of ``_BLOCK_ROWS`` (block b uses key + (b,))."""
+    shape = tuple(int(s) for s in shape)
+    rows = shape[0] if shape else 1
+    inner = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    nblk = max(1, math.ceil(rows / _BLOCK_ROWS))
+    out_dtype = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((rows, inner), dtype=out_dtype)
+
+    def fill(b: int) -> None:
+        r0 = b * _BLOCK_ROWS
+        r1 = min(rows, r0 + _BLOCK_ROWS)
+        g = rng(*key, b)
+        x = g.standard_normal((r1 - r0) * inner, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        x = x.reshape(r1 - r0, inner)
+        out[r0:r1] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    if nblk == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return HostTensor(out.reshape(shape), dtype)
+
+
+def fill_rows(t: HostTensor, rows: np.ndarray, value: float) -> None:
+    """Overwrite whole rows (first axis) of a host tensor with ``value`` in its storage dtype."""
+    v = np.full(t.data.shape[1:], value, dtype=np.float32)
+    t.data[rows] = f32_to_bf16_bits(v) if t.dtype == "bf16" else v
+
+
+# --------------------------------------------------------------------------- workload shapes
+@dataclass(frozen=True)
+class Shape:
+    n_q: int
+    n_kv: int
+    d_head: int
+    rank: int
+    n_agents: int
+    d_model: int
+    dtype: str
+
+    @property
+    def group(self) -> int:
+        return self.n_q // self.n_kv
+
+    @property
+    def d_kv(self) -> int:
+        return self.n_kv * self.d_head
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_head)
+
+
+TINY_SHAPE = Shape(n_q=4, n_kv=2, d_head=64, rank=8, n_agents=3, d_model=256, dtype="f32")
+LLAMA_SHAPE = Shape(n_q=32, n_kv=8, d_head=128, rank=8, n_agents=3, d_model=4096, dtype="bf16")
+MINISTRAL_SHAPE = Shape(n_q=32, n_kv=8, d_head=128, rank=16, n_agents=3, d_model=4096, dtype="bf16")
+
+
+@dataclass
+class DecodeBatch:
+    """Inputs of one decode call: a packed key/value cache and per-request ranges."""
+    shape: Shape
+    Q: HostTensor            # [batch, n_q, d]
+    K: HostTensor            # [rows, n_kv, d]
+    V: HostTensor            # [rows, n_kv, d]
+    V_lr: HostTensor         # [rows, n_agents * rank]
+    B: HostTensor            # [n_agents, rank, n_kv * d]
+    kv_start: np.ndarray     # int64 [batch]
+    kv_len: np.ndarray       # int32 [batch]
+    agent: np.ndarray        # int32 [batch]
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_len.max()) if self.batch else 0
+
+    def attended_rows(self) -> int:
+        return int(self.kv_len.astype(np.int64).sum())
+
+
+@dataclass
+class PrefillCase:
+    shape: Shape
+    Q: HostTensor            # [L_C, n_q, d]
+    K: HostTensor            # [L_P + L_C, n_kv, d]
+    V: HostTensor            # [L_P + L_C, n_kv, d]
+    V_lr: HostTensor         # [L_P + L_C, n_agents * rank]
+    B: HostTensor            # [n_agents, rank, n_kv * d]
+    L_P: int
+    L_C: int
+    agent: int = 0
+
+
+@dataclass
+class PrecomputeCase:
+    shape: Shape
+    X: HostTensor            # [T, d_model]
+    A: HostTensor            # [d_model, n_agents * rank]
+
+
+def _adapters(key: Tuple[int, ...], s: Shape, a_std: float) -> Tuple[HostTensor, HostTensor]:
+    """Stacked down-projections A = [A_1 .. A_N] (column block k = agent k) and up-projections B."""
+    A = normal(key + (T_A,), (s.d_model, s.n_agents * s.rank), a_std, s.dtype)
+    B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), 0.05, s.dtype)
+    return A, B
+
+
+# ---- tiny fp32 workload: projections are drawn and K/V_base are X W0 (host fp64, rounded to fp32)
+@dataclass
+class TinyWorkload:
+    shape: Shape
+    X: HostTensor          # [256, d_model]
+    W0_k: np.ndarray       # fp32 [d_model, d_kv]
+    W0_v: np.ndarray       # fp32 [d_model, d_kv]
+    A: HostTensor          # [d_model, N*r]
+    B: HostTensor          # [N, r, d_kv]
+    Q: HostTensor          # [L_C, n_q, d]
+    K: HostTensor          # [L_P + L_C, n_kv, d]  (= X W0_k)
+    V: HostTensor          # [L_P + L_C, n_kv, d]  (= X W0_v)
+    L_P: int
+    L_C: int
+    x_dec: HostTensor      # [steps, d_model] new tokens appended one per decode step
+    K_dec: HostTensor      # [steps, n_kv, d]  (= x_dec W0_k)
+    V_dec: HostTensor      # [steps, n_kv, d]  (= x_dec W0_v)
+    Q_dec: HostTensor      # [steps, N, n_q, d] one query per agent per step
+
+
+def _base_projection(x: HostTensor, W: np.ndarray, s: Shape) -> HostTensor:
+    """Input synthesis for the tiny workload: base keys/values of drawn tokens (fp64 product, fp32 storage)."""
+    y = x.as_f64() @ W.astype(np.float64)
+    return HostTensor(y.astype(np.float32).reshape(x.shape[0], s.n_kv, s.d_head), "f32")
+
+
+def tiny_workload(steps: int = 8) -> TinyWorkload:
+    s = TINY_SHAPE
+    L_P, L_C = 192, 64
+    key = (TINY, 0, 0)
+    X = normal(key + (T_X,), (L_P + L_C, s.d_model), 1.0, "f32")
+    W0_k = normal(key + (T_W0K,), (s.d_model, s.d_kv), 1.0 / math.sqrt(s.d_model), "f32").data
+    W0_v = normal(key + (T_W0V,), (s.d_model, s.d_kv), 1.0 / math.sqrt(s.d_model), "f32").data
+    A, B = _adapters(key, s, 1.0 / math.sqrt(s.d_model))
+    Q = normal(key + (T_Q,), (L_C, s.n_q, s.d_head), 1.0, "f32")
+    x_dec = normal(key + (T_XDEC,), (steps, s.d_model), 1.0, "f32")
+    Q_dec = normal(key + (T_QDEC,), (steps, s.n_agents, s.n_q, s.d_head), 1.0, "f32")
+    return TinyWorkload(s, X, W0_k, W0_v, A, B, Q,
+                        _base_projection(X, W0_k, s), _base_projection(X, W0_v, s), L_P, L_C,
+                        x_dec, _base_projection(x_dec, W0_k, s), _base_projection(x_dec, W0_v, s), Q_dec)
+
+
+# ---- single-request decode (Llama-3.1-8B layer, L = 1900)
+def llama_decode(L: int = 1900, agent: int = 0) -> DecodeBatch:
+    s = LLAMA_SHAPE
+    key = (LLAMA_DECODE, 0, 0)
+    K = normal(key + (T_K,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V_lr = normal(key + (T_VLR,), (L, s.n_agents * s.rank), 1.0, s.dtype)
+    _, B = _adapters(key, s, 1.0 / math.sqrt(s.d_model))
+    Q = normal(key + (T_Q,), (1, s.n_q, s.d_head), 1.0, s.dtype)
+    return DecodeBatch(s, Q, K, V, V_lr, B, np.zeros(1, np.int64), np.array([L], np.int32),
+                       np.array([agent], np.int32))
+
+
+# ---- chunked prefill (L_P = 16384 cached, L_C = 2048 new) and its LR precompute
+def llama_prefill(L_P: int = 16384, L_C: int = 2048, agent: int = 0) -> PrefillCase:
+    s = LLAMA_SHAPE
+    key = (LLAMA_PREFILL, 0, 0)
+    L = L_P + L_C
+    K = normal(key + (T_K,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V_lr = normal(key + (T_VLR,), (L, s.n_agents * s.rank), 1.0, s.dtype)
+    _, B = _adapters(key, s, 1.0 / math.sqrt(s.d_model))
+    Q = normal(key + (T_Q,), (L_C, s.n_q, s.d_head), 1.0, s.dtype)
+    return PrefillCase(s, Q, K, V, V_lr, B, L_P, L_C, agent)
+
+
+def llama_precompute(T: int = 2048) -> PrecomputeCase:
+    s = LLAMA_SHAPE
+    key = (LLAMA_PREFILL, 0, 0)
+    X = normal(key + (T_X,), (T, s.d_model), 1.0, s.dtype)
+    A, _ = _adapters(key, s, 1.0 / math.sqrt(s.d_model))
+    return PrecomputeCase(s, X, A)
+
+
+# ---- concurrent long-context decode: 16 requests, each over its own 66,400-token trajectory
+def llama_long_decode(n_req: int = 16, L: int = 66400, requests: Optional[Sequence[int]] = None) -> DecodeBatch:
+    """Packed caches: request b owns rows [b*L, (b+1)*L). Every tensor of request b is drawn from
+    its own stream, so a subset of requests (``requests``) can be drawn alone with identical values."""
+    s = LLAMA_SHAPE
+    reqs = list(range(n_req)) if requests is None else list(requests)
+    Ks, Vs, Ls = [], [], []
+    for b in reqs:
+        key = (LLAMA_LONG_DECODE, 0, b)
+        Ks.append(normal(key + (T_K,), (L, s.n_kv, s.d_head), 1.0, s.dtype).data)
+        Vs.append(normal(key + (T_V,), (L, s.n_kv, s.d_head), 1.0, s.dtype).data)
+        Ls.append(normal(key + (T_VLR,), (L, s.n_agents * s.rank), 1.0, s.dtype).data)
+    key0 = (LLAMA_LONG_DECODE, 0, 10_000)
+    _, B = _adapters(key0, s, 1.0 / math.sqrt(s.d_model))
+    agents_all = rng(LLAMA_LONG_DECODE, 0, 10_000, T_AGENT).integers(0, s.n_agents, size=n_req).astype(np.int32)
+    Qall = normal(key0 + (T_Q,), (n_req, s.n_q, s.d_head), 1.0, s.dtype)
+    Q = HostTensor(Qall.data[reqs], s.dtype)
+    n = len(reqs)
+    return DecodeBatch(s, Q,
+                       HostTensor(np.concatenate(Ks), s.dtype), HostTensor(np.concatenate(Vs), s.dtype),
+                       HostTensor(np.concatenate(Ls), s.dtype), B,
+                       np.arange(n, dtype=np.int64) * L, np.full(n, L, np.int32), agents_all[reqs])
+
+
+# ---- Ministral-8B-shaped decode step: 36 layers x (precompute + decode), 32 requests
+MINISTRAL_LAYERS = 36
+MINISTRAL_REQUESTS = 32
+
+
+def ministral_lengths(n_req: int = MINISTRAL_REQUESTS, lo: float = 1900.0, hi: float = 32000.0) -> np.ndarray:
+    """Context lengths log-uniform in [lo, hi], rounded to the nearest integer; the same for every layer."""
+    u = rng(MINISTRAL_STEP, 0, 10_000, T_LEN).uniform(math.log(lo), math.log(hi), size=n_req)
+    return np.rint(np.exp(u)).astype(np.int32)
+
+
+def ministral_agents(n_req: int = MINISTRAL_REQUESTS) -> np.ndarray:
+    return rng(MINISTRAL_STEP, 0, 10_000, T_AGENT).integers(0, MINISTRAL_SHAPE.n_agents, size=n_req).astype(np.int32)
+
+
+def ministral_layer(layer: int, requests: Optional[Sequence[int]] = None) -> Tuple[DecodeBatch, PrecomputeCase]:
+    """One layer of the step. Request b's cache occupies rows [start_b, start_b + L_b) of the packed
+    layer cache (starts are the prefix sums of all 32 lengths, also when only a subset is drawn).
+    The precompute computes the LR rows of the 32 newest tokens (one per request)."""
+    s = MINISTRAL_SHAPE
+    lens = ministral_lengths()
+    agents = ministral_agents()
+    starts = np.concatenate([[0], np.cumsum(lens.astype(np.int64))[:-1]])
+    reqs = list(range(len(lens))) if requests is None else list(requests)
+    Ks, Vs, Ls = [], [], []
+    for b in reqs:
+        key = (MINISTRAL_STEP, layer, b)
+        Ks.append(normal(key + (T_K,), (int(lens[b]), s.n_kv, s.d_head), 1.0, s.dtype).data)
+        Vs.append(normal(key + (T_V,), (int(lens[b]), s.n_kv, s.d_head), 1.0, s.dtype).data)
+        Ls.append(normal(key + (T_VLR,), (int(lens[b]), s.n_agents * s.rank), 1.0, s.dtype).data)
+    keyL = (MINISTRAL_STEP, layer, 10_000)
+    A, B = _adapters(keyL, s, 1.0 / math.sqrt(s.d_model))
+    Qall = normal(keyL + (T_Q,), (len(lens), s.n_q, s.d_head), 1.0, s.dtype)
+    X = normal(keyL + (T_X,), (len(lens), s.d_model), 1.0, s.dtype)
+    sub_starts = np.concatenate([[0], np.cumsum(lens[reqs].astype(np.int64))[:-1]]) if requests is not None else starts
+    dec = DecodeBatch(s, HostTensor(Qall.data[reqs], s.dtype),
+                      HostTensor(np.concatenate(Ks), s.dtype), HostTensor(np.concatenate(Vs), s.dtype),
+                      HostTensor(np.concatenate(Ls), s.dtype), B,
+                      sub_starts.astype(np.int64), lens[reqs].astype(np.int32), agents[reqs].astype(np.int32))
+    pre = PrecomputeCase(s, HostTensor(X.data[reqs], s.dtype), A)
+    return dec, pre
+
+
+# ---- small random cases (any shape) for tests
+def random_decode(key: Sequence[int], s: Shape, kv_lens: Sequence[int], kv_starts: Optional[Sequence[int]] = None,
+                  rows: Optional[int] = None, agents: Optional[Sequence[int]] = None, b_std: float = 0.05) -> DecodeBatch:
+    key = tuple(key)
+    n = len(kv_lens)
+    kv_lens = np.asarray(kv_lens, np.int32)
+    if kv_starts is None:
+        kv_starts = np.concatenate([[0], np.cumsum(kv_lens.astype(np.int64))[:-1]]) if n else np.zeros(0, np.int64)
+    kv_starts = np.asarray(kv_starts, np.int64)
+    if rows is None:
+        rows = int(max([0] + [int(a + b) for a, b in zip(kv_starts, kv_lens)]))
+    rows = max(rows, 1)
+    K = normal(key + (T_K,), (rows, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (rows, s.n_kv, s.d_head), 1.0, s.dtype)
+    V_lr = normal(key + (T_VLR,), (rows, s.n_agents * s.rank), 1.0, s.dtype)
+    B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
+    Q = normal(key + (T_Q,), (n, s.n_q, s.d_head), 1.0, s.dtype)
+    if agents is None:
+        agents = rng(*key, T_AGENT).integers(0, s.n_agents, size=n)
+    return DecodeBatch(s, Q, K, V, V_lr, B, kv_starts, kv_lens, np.asarray(agents, np.int32))
+
+
+def random_prefill(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int = 0, b_std: float = 0.05) -> PrefillCase:
+    key = tuple(key)
+    L = L_P + L_C
+    K = normal(key + (T_K,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (L, s.n_kv, s.d_head), 1.0, s.dtype)
+    V_lr = normal(key + (T_VLR,), (L, s.n_agents * s.rank), 1.0, s.dtype)
+    B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
+    Q = normal(key + (T_Q,), (L_C, s.n_q, s.d_head), 1.0, s.dtype)
+    return PrefillCase(s, Q, K, V, V_lr, B, L_P, L_C, agent)
+
+
+def random_precompute(key: Sequence[int], s: Shape, T: int) -> PrecomputeCase:
+    key = tuple(key)
+    X = normal(key + (T_X,), (T, s.d_model), 1.0, s.dtype)
+    A = normal(key + (T_A,), (s.d_model, s.n_agents * s.rank), 1.0 / math.sqrt(s.d_model), s.dtype)
+    return PrecomputeCase(s, X, A)

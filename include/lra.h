@@ -1,0 +1,160 @@
+/*
+ * lra.h - C ABI of the Flash-LoRA-Attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (LRAgent: "Efficient KV Cache Sharing for Multi-LoRA LLM
+ * Agents", core method and method steps (2)-(4); PReCache, PreLRShared):
+ * agents share one key cache K_base and one base value cache V_base = X W0.
+ * Each agent k keeps only a rank-r value cache V_lr = X A_k. Attention for
+ * agent a streams K/V_base/V_lr tiles with an online softmax, accumulates the
+ * base output O and a rank-r output O_lr, and after the last tile applies one
+ * up-projection O += O_lr B_a, then normalises. V_base + V_lr B_a is never
+ * built. The LR precompute produces X [A_1 .. A_N] for all agents at once.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are device pointers on the current HIP device;
+ *    pointers marked (host) are host pointers. Scalars are host values.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the null
+ *    stream). A return of LRA_OK means the work was enqueued.
+ *  - The caller allocates and owns every buffer, including workspaces. The
+ *    library allocates nothing, keeps no pointer after it returns, and holds no
+ *    state between calls, so calls on different streams with different
+ *    workspaces may run concurrently.
+ *  - All tensors are dense and row-major; one element type (`dtype`) per call:
+ *    LRA_F32 (IEEE float) or LRA_BF16 (bfloat16 bits). Accumulation is fp32;
+ *    bf16 outputs are rounded to nearest, ties to even.
+ *  - Scalar arguments are validated on the host before anything is enqueued;
+ *    a failing call enqueues nothing and returns a negative lra_status.
+ *    lra_last_error() gives a message for the calling thread's last failure.
+ *    Errors reported by the HIP runtime at launch come back as LRA_ERR_HIP.
+ *  - Device-side index arrays (kv_start, kv_len, agent, out_rows) cannot be
+ *    checked on the host. The kernels check them against the sizes passed in
+ *    and never access memory outside the buffers those sizes describe: a
+ *    decode request with an invalid range or agent gets NaN in every output
+ *    element; a precompute row whose out_rows entry is out of range is not
+ *    written.
+ *  - Supported: d_head in {64, 128}; rank in {8, 16}; n_q % n_kv == 0 with
+ *    group size n_q / n_kv in 1..8. Anything else returns LRA_ERR_UNSUPPORTED.
+ *
+ * Names follow the pages: Q, K_base, V_base, V_lr, B_i, agent i, L_P (tokens
+ * already cached), L_C (new tokens of the chunk), r (rank), N (agents).
+ */
+#ifndef LRA_H
+#define LRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRA_ABI_VERSION 1
+
+typedef enum {
+    LRA_OK = 0,
+    LRA_ERR_NULL = -1,        /* a required pointer is NULL */
+    LRA_ERR_SHAPE = -2,       /* sizes, strides or ranges are inconsistent */
+    LRA_ERR_UNSUPPORTED = -3, /* a dtype / d_head / rank / group size the kernels do not cover */
+    LRA_ERR_INDEX = -4,       /* a host-side index (agent) is out of range */
+    LRA_ERR_WORKSPACE = -5,   /* workspace missing, too small or misaligned */
+    LRA_ERR_HIP = -6          /* the HIP runtime reported an error */
+} lra_status;
+
+typedef enum { LRA_F32 = 0, LRA_BF16 = 1 } lra_dtype;
+
+/* ABI version of the loaded library (LRA_ABI_VERSION at build time). */
+int lra_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* lra_status_str(int status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char* lra_last_error(void);
+
+/* ------------------------------------------------------------------------------------------------
+ * LR precompute (PReCache, PreLRShared: when a segment is first processed, every agent's
+ * down-projection is applied to its hidden states; LRAgent method step (2): V_lr = X A, L x r).
+ *
+ *   V_lr[out_rows[t], k*rank + j] = sum_c X[t, c] * A[k*rank + j, c]    t < T, k < n_agents, j < rank
+ *
+ * X        (device) [T x d_model], row stride ldx elements (ldx >= d_model, multiple of 8)
+ * A        (device) [n_agents*rank x d_model] row-major: row k*rank + j holds column j of A_k,
+ *          i.e. the agents' LoRA down-projection weights (each r x d_model) stacked
+ * V_lr     (device) [vlr_rows x ld_vlr] output cache (ld_vlr >= n_agents*rank); only columns
+ *          0 .. n_agents*rank-1 of the addressed rows are written
+ * out_rows (device) [T] int64 destination row of each X row, or NULL for row t -> row t
+ *          (then vlr_rows >= T is required)
+ * workspace(device) scratch of lra_lr_precompute_workspace_bytes() bytes, 256-byte aligned.
+ *          It must be zero-filled before its first use; every call leaves it zero-filled again.
+ *          Calls that share one workspace must not overlap in time.
+ * T = 0 is allowed and enqueues nothing. d_model must be a multiple of 32; ld_vlr a multiple of 8.
+ * Every tensor pointer must be 16-byte aligned.
+ */
+size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, int32_t n_agents, int32_t rank);
+
+int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
+                      const void* A, int32_t n_agents, int32_t rank,
+                      void* V_lr, int64_t ld_vlr, int64_t vlr_rows, const int64_t* out_rows,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Causal chunked prefill for one agent (LRAgent method steps (3)-(4); PReCache: the new chunk of
+ * L_C tokens follows L_P reused tokens). Query i (0 <= i < L_C) sits at absolute position L_P + i
+ * and attends keys 0 .. L_P + i. Query head h reads KV head g = h / (n_q / n_kv).
+ *
+ *   O[i, h] = ( sum_j p_ij V_base[j, g] + (sum_j p_ij V_lr[j, agent*rank : agent*rank+rank]) B_agent[:, g*d : g*d+d] )
+ *             / sum_j p_ij,        p_ij = exp(scale * <Q[i, h], K_base[j, g]> - m_i)
+ *
+ * Q        (device) [L_C x n_q x d_head]
+ * K_base   (device) [L_P+L_C x n_kv x d_head]    (rows 0 .. L_P+L_C-1 are read)
+ * V_base   (device) [L_P+L_C x n_kv x d_head]
+ * V_lr     (device) [L_P+L_C x ld_vlr], agent a owns columns a*rank .. a*rank+rank-1
+ * B        (device) [n_agents x rank x n_kv*d_head]: B_a, one r x (n_kv*d_head) matrix per agent
+ * O        (device) [L_C x n_q x d_head] output
+ * In bf16 the probabilities are rounded to bf16 before the P.V products; l, m, O, O_lr are fp32.
+ * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. L_C = 0 enqueues nothing.
+ */
+int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                     const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                     const void* B, int32_t n_agents, int32_t agent,
+                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                     void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Batched decode, one new query token per request, split along the key axis (each split writes a
+ * partial (m, l, O, O_lr) in fp32 to the workspace; a second kernel merges the partials with the
+ * log-sum-exp rule, applies B_agent once and normalises). Request b attends all rows
+ * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
+ * kv_len[b] = 0 gives a zero output row.
+ *
+ * Q        (device) [batch x n_q x d_head]
+ * K_base, V_base (device) [kv_rows x n_kv x d_head]
+ * V_lr     (device) [kv_rows x ld_vlr]
+ * kv_start (device) [batch] int64, kv_len (device) [batch] int32, agent (device) [batch] int32
+ * max_kv_len (host) an upper bound on every kv_len[b]; it sizes the launch
+ * B        (device) [n_agents x rank x n_kv*d_head]
+ * keys_per_split  keys handled by one split (multiple of 64), or 0 for the library's choice
+ * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned, no initial contents
+ * O        (device) [batch x n_q x d_head] output
+ * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues nothing.
+ */
+size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
+                                       int32_t rank, int64_t max_kv_len, int32_t keys_per_split);
+
+int lra_attn_decode(int dtype, const void* Q, int32_t batch,
+                    const void* K_base, const void* V_base, int64_t kv_rows,
+                    const void* V_lr, int64_t ld_vlr,
+                    const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                    const void* B, int32_t n_agents, const int32_t* agent,
+                    int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                    int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                    void* O, void* stream);
+
+/* Keys per split the library picks for these sizes when keys_per_split = 0. */
+int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRA_H */

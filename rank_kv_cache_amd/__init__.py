@@ -1,0 +1,230 @@
+"""Python binding of liblra (Flash-LoRA-Attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``liblra.so``. PyTorch is used for device memory and streams. The binding checks that the
+tensors handed over agree with each other (device, dtype, contiguity), derives the sizes and
+strides the C ABI asks for, and turns a negative status into ``LraError``.
+
+Importing this package loads ``liblra.so`` and fails loudly if it has not been built
+(``python -m rank_kv_cache_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "LraError", "LIB_PATH", "abi_version", "status_str",
+    "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
+    "lra_attn_prefill",
+    "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
+    "LRA_F32", "LRA_BF16", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
+LRA_F32, LRA_BF16 = 0, 1
+
+_c = ctypes
+_p = _c.c_void_p
+_i32, _i64, _sz, _f = _c.c_int32, _c.c_int64, _c.c_size_t, _c.c_float
+
+# name -> (restype, argtypes); mirrors include/lra.h
+_SIGNATURES = {
+    "lra_abi_version": (_c.c_int, []),
+    "lra_status_str": (_c.c_char_p, [_c.c_int]),
+    "lra_last_error": (_c.c_char_p, []),
+    "lra_lr_precompute_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "lra_lr_precompute": (_c.c_int, [_c.c_int, _p, _i64, _i32, _i64, _p, _i32, _i32, _p, _i64, _i64, _p,
+                                     _p, _sz, _p]),
+    "lra_attn_prefill": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
+    "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
+                                   _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
+    "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class LraError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {status_str(status)} ({status}): {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rank_kv_cache_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return int(_lib.lra_abi_version())
+
+
+def status_str(status: int) -> str:
+    return _lib.lra_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LraError(status, where, _lib.lra_last_error().decode())
+
+
+# ---------------------------------------------------------------------------------- marshalling
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LRA_F32
+    if t.dtype == torch.bfloat16:
+        return LRA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _same(ref: torch.Tensor, *ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != ref.dtype:
+            raise TypeError(f"dtype mismatch: {t.dtype} vs {ref.dtype}")
+        if t.device != ref.device:
+            raise ValueError(f"device mismatch: {t.device} vs {ref.device}")
+
+
+def _dense(name: str, t: torch.Tensor) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rows_dense(name: str, t: torch.Tensor) -> None:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ---------------------------------------------------------------------------------- LR precompute
+def lra_lr_precompute_workspace_bytes(T: int, d_model: int, n_agents: int, rank: int) -> int:
+    return int(_lib.lra_lr_precompute_workspace_bytes(T, d_model, n_agents, rank))
+
+
+def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int, V_lr: torch.Tensor,
+                      out_rows: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """V_lr[out_rows[t], :n_agents*rank] = X[t] @ A.T, with A = [A_1^T; ...; A_N^T] ([N*r, d_model]).
+
+    ``workspace`` (uint8, zero-filled before first use) is allocated zeroed when omitted."""
+    _same(X, A, V_lr)
+    _rows_dense("X", X)
+    _dense("A", A)
+    _rows_dense("V_lr", V_lr)
+    T, d_model = X.shape
+    if A.shape != (n_agents * rank, d_model):
+        raise ValueError(f"A has shape {tuple(A.shape)}, expected {(n_agents * rank, d_model)}")
+    if out_rows is not None:
+        if out_rows.dtype != torch.int64 or out_rows.numel() != T or not out_rows.is_contiguous():
+            raise ValueError("out_rows must be a contiguous int64 tensor with one entry per row of X")
+    need = lra_lr_precompute_workspace_bytes(T, d_model, n_agents, rank)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lra_lr_precompute(_dtype_code(X), _ptr(X), T, d_model, X.stride(0), _ptr(A), n_agents, rank,
+                                  _ptr(V_lr), V_lr.stride(0), V_lr.shape[0], _ptr(out_rows),
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "lra_lr_precompute")
+    return V_lr
+
+
+# ---------------------------------------------------------------------------------- prefill
+def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                     B: torch.Tensor, agent: int, scale: float, O: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Causal prefill of the L_C = Q.shape[0] new tokens over L_P cached + L_C new keys for ``agent``.
+
+    Q [L_C, n_q, d]; K_base, V_base [>= L_P+L_C, n_kv, d]; V_lr [>= L_P+L_C, ld]; B [N, r, n_kv*d]."""
+    _same(Q, K_base, V_base, V_lr, B)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    L_C, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    L = L_P + L_C
+    if K_base.shape[0] < L or V_base.shape[0] < L or V_lr.shape[0] < L:
+        raise ValueError(f"caches hold fewer than L_P + L_C = {L} rows")
+    if K_base.shape[1:] != (n_kv, d) or V_base.shape[1:] != (n_kv, d) or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/B shapes disagree with Q")
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_prefill(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
+                                 V_lr.stride(0), _ptr(B), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(O),
+                                 _stream(stream)), "lra_attn_prefill")
+    return O
+
+
+# ---------------------------------------------------------------------------------- decode
+def lra_attn_decode_default_split(batch: int, n_kv: int, max_kv_len: int) -> int:
+    return int(_lib.lra_attn_decode_default_split(batch, n_kv, max_kv_len))
+
+
+def lra_attn_decode_workspace_bytes(batch: int, n_q: int, n_kv: int, d_head: int, rank: int, max_kv_len: int,
+                                    keys_per_split: int = 0) -> int:
+    return int(_lib.lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split))
+
+
+def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                    kv_start: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int, B: torch.Tensor,
+                    agent: torch.Tensor, scale: float, keys_per_split: int = 0,
+                    workspace: Optional[torch.Tensor] = None, O: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One query per request over rows [kv_start[b], kv_start[b] + kv_len[b]) of the shared caches.
+
+    Q [batch, n_q, d]; K_base, V_base [rows, n_kv, d]; V_lr [rows, ld]; kv_start int64 [batch];
+    kv_len, agent int32 [batch]; B [N, r, n_kv*d]."""
+    _same(Q, K_base, V_base, V_lr, B)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    batch, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32 or agent.dtype != torch.int32:
+        raise TypeError("kv_start must be int64, kv_len and agent int32")
+    for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
+        if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
+    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/V_lr/B shapes disagree")
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_decode(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
+                                _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
+                                _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O

@@ -1,0 +1,224 @@
+// C ABI of liblra: host-side validation, workspace layout and dispatch to the gfx950 kernels.
+// Every failing check returns before anything is enqueued; see include/lra.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/lra.h"
+#include "lra_kernels.h"
+
+#define LRA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return LRA_OK;
+    return fail(LRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// -------------------------------------------------------------------------- decode workspace
+struct DecodeLayout {
+    int chunk, n_split;
+    size_t ml_bytes, o_off, total;
+};
+
+DecodeLayout decode_layout(int batch, int n_q, int d_head, int rank, int64_t max_kv_len, int chunk) {
+    DecodeLayout L{};
+    L.chunk = chunk;
+    L.n_split = max_kv_len > 0 ? int((max_kv_len + chunk - 1) / chunk) : 0;
+    const size_t recs = size_t(batch) * size_t(n_q) * size_t(L.n_split);
+    L.ml_bytes = recs * 2 * sizeof(float);
+    L.o_off = align_up(L.ml_bytes, 256);
+    L.total = recs ? L.o_off + recs * size_t(d_head + rank) * sizeof(float) : 0;
+    return L;
+}
+
+int check_heads(int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank) {
+    if (n_q <= 0 || n_kv <= 0) return fail(LRA_ERR_SHAPE, "n_q=%d and n_kv=%d must be positive", n_q, n_kv);
+    if (n_q % n_kv != 0) return fail(LRA_ERR_SHAPE, "n_q=%d is not a multiple of n_kv=%d", n_q, n_kv);
+    if (n_q / n_kv > 8) return fail(LRA_ERR_UNSUPPORTED, "group size n_q/n_kv=%d exceeds 8", n_q / n_kv);
+    if (d_head != 64 && d_head != 128) return fail(LRA_ERR_UNSUPPORTED, "d_head=%d (supported: 64, 128)", d_head);
+    if (rank != 8 && rank != 16) return fail(LRA_ERR_UNSUPPORTED, "rank=%d (supported: 8, 16)", rank);
+    return LRA_OK;
+}
+
+int check_dtype(int dtype) {
+    if (dtype != LRA_F32 && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "dtype=%d", dtype);
+    return LRA_OK;
+}
+
+}  // namespace
+
+LRA_EXPORT int lra_abi_version(void) { return LRA_ABI_VERSION; }
+
+LRA_EXPORT const char* lra_status_str(int status) {
+    switch (status) {
+        case LRA_OK: return "LRA_OK";
+        case LRA_ERR_NULL: return "LRA_ERR_NULL";
+        case LRA_ERR_SHAPE: return "LRA_ERR_SHAPE";
+        case LRA_ERR_UNSUPPORTED: return "LRA_ERR_UNSUPPORTED";
+        case LRA_ERR_INDEX: return "LRA_ERR_INDEX";
+        case LRA_ERR_WORKSPACE: return "LRA_ERR_WORKSPACE";
+        case LRA_ERR_HIP: return "LRA_ERR_HIP";
+        default: return "LRA_ERR_UNKNOWN";
+    }
+}
+
+LRA_EXPORT const char* lra_last_error(void) { return g_last_error.c_str(); }
+
+// ============================================================================ LR precompute
+LRA_EXPORT size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, int32_t n_agents, int32_t rank) {
+    if (T <= 0 || d_model <= 0 || n_agents <= 0 || rank <= 0) return 0;
+    const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, n_agents * rank, true);
+    if (pl.ksplit <= 1) return 0;
+    return align_up(pl.count_bytes, 256) + pl.part_bytes;
+}
+
+LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
+                                 const void* A, int32_t n_agents, int32_t rank,
+                                 void* V_lr, int64_t ld_vlr, int64_t vlr_rows, const int64_t* out_rows,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (T < 0) return fail(LRA_ERR_SHAPE, "T=%lld is negative", (long long)T);
+    if (n_agents <= 0 || rank <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d, rank=%d must be positive", n_agents, rank);
+    const int64_t NR = int64_t(n_agents) * rank;
+    if (NR % 8 != 0 || NR > (1 << 20)) return fail(LRA_ERR_UNSUPPORTED, "n_agents*rank=%lld must be a multiple of 8", (long long)NR);
+    if (d_model <= 0 || d_model % 32 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model=%d must be a positive multiple of 32", d_model);
+    if (ldx < d_model || ldx % 8 != 0) return fail(LRA_ERR_SHAPE, "ldx=%lld must be >= d_model and a multiple of 8", (long long)ldx);
+    if (ld_vlr < NR || ld_vlr % 8 != 0) return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (vlr_rows < 0) return fail(LRA_ERR_SHAPE, "vlr_rows is negative");
+    if (!out_rows && vlr_rows < T) return fail(LRA_ERR_SHAPE, "vlr_rows=%lld < T=%lld with identity row map", (long long)vlr_rows, (long long)T);
+    if (T == 0) return LRA_OK;
+    if (!X || !A || !V_lr) return fail(LRA_ERR_NULL, "X, A and V_lr must not be NULL");
+    if (!aligned(X, 16) || !aligned(A, 16) || !aligned(V_lr, 16)) return fail(LRA_ERR_SHAPE, "X, A and V_lr must be 16-byte aligned");
+
+    const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, int(NR), dtype == LRA_BF16);
+    lra::PrecomputeParams p{};
+    if (pl.ksplit > 1) {
+        const size_t need = align_up(pl.count_bytes, 256) + pl.part_bytes;
+        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+        if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+        p.ws_count = static_cast<uint32_t*>(workspace);
+        p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(pl.count_bytes, 256));
+    }
+    p.X = X; p.A = A; p.Vlr = V_lr; p.out_rows = out_rows;
+    p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_rows = vlr_rows;
+    p.d_model = d_model; p.NR = int(NR); p.kr = pl.kr; p.ksplit = pl.ksplit; p.n_cg = pl.n_cg;
+    p.bf16 = dtype == LRA_BF16;
+    return hip_status(lra::launch_precompute(p, static_cast<hipStream_t>(stream)), "lra_lr_precompute launch");
+}
+
+// ============================================================================ prefill
+LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                                const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                                const void* B, int32_t n_agents, int32_t agent,
+                                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                void* O, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (L_C < 0 || L_P < 0) return fail(LRA_ERR_SHAPE, "L_C=%lld and L_P=%lld must be >= 0", (long long)L_C, (long long)L_P);
+    if (L_P + L_C > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "L_P + L_C exceeds 2^31 - 1");
+    if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
+    if (agent < 0 || agent >= n_agents) return fail(LRA_ERR_INDEX, "agent=%d outside [0, %d)", agent, n_agents);
+    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (!std::isfinite(scale)) return fail(LRA_ERR_SHAPE, "scale must be finite");
+    if (L_C == 0) return LRA_OK;
+    if (!Q || !K_base || !V_base || !V_lr || !B || !O) return fail(LRA_ERR_NULL, "Q, K_base, V_base, V_lr, B and O must not be NULL");
+    if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
+        return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    lra::PrefillParams p{};
+    p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B; p.O = O;
+    p.L_C = L_C; p.L_P = L_P; p.ld_vlr = ld_vlr;
+    p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.d_head = d_head; p.rank = rank;
+    p.agent = agent; p.n_agents = n_agents; p.scale = scale; p.bf16 = dtype == LRA_BF16;
+    return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), "lra_attn_prefill launch");
+}
+
+// ============================================================================ decode
+LRA_EXPORT int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len) {
+    return lra::decode_default_chunk(batch, n_kv, max_kv_len);
+}
+
+LRA_EXPORT size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
+                                                  int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
+    if (batch <= 0 || n_q <= 0 || n_kv <= 0 || max_kv_len <= 0 || d_head <= 0 || rank <= 0) return 0;
+    if (keys_per_split < 0 || keys_per_split % 64 != 0) return 0;
+    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
+    return decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk).total;
+}
+
+LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
+                               const void* K_base, const void* V_base, int64_t kv_rows,
+                               const void* V_lr, int64_t ld_vlr,
+                               const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                               const void* B, int32_t n_agents, const int32_t* agent,
+                               int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                               int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                               void* O, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
+    if (kv_rows < 0 || max_kv_len < 0) return fail(LRA_ERR_SHAPE, "kv_rows and max_kv_len must be >= 0");
+    if (max_kv_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^31 - 1");
+    if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
+    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (keys_per_split < 0 || keys_per_split % 64 != 0)
+        return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
+    if (!std::isfinite(scale)) return fail(LRA_ERR_SHAPE, "scale must be finite");
+    if (batch == 0) return LRA_OK;
+    if (!Q || !K_base || !V_base || !V_lr || !B || !O || !kv_start || !kv_len || !agent)
+        return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
+    if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
+        return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
+    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
+    if (L.total) {
+        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
+        if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (workspace_bytes < L.total) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
+    }
+    lra::DecodeParams p{};
+    p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B;
+    p.kv_start = kv_start; p.kv_len = kv_len; p.agent = agent;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
+    p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
+    p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
+    p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
+    p.bf16 = dtype == LRA_BF16;
+    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), "lra_attn_decode launch");
+}
+
+namespace lra {
+
+int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len) {
+    // aim for about 8k (request, KV head, split) work items; splits are whole 256-key rounds of the
+    // 4 waves when they are long, single 64-key tiles when the whole job is small
+    const int64_t work = int64_t(batch) * n_kv * max_kv_len;
+    int64_t chunk = (work + 8191) / 8192;
+    if (chunk <= 64) return 64;
+    chunk = (chunk + 255) / 256 * 256;
+    return int(chunk > 16384 ? 16384 : chunk);
+}
+
+}  // namespace lra

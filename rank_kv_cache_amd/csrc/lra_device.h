@@ -1,0 +1,143 @@
+// Device-side building blocks shared by the gfx950 kernels: element types, 8-wide operand
+// fragments, the 16x16x32 matrix-core step, DPP row reductions and conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lra {
+
+typedef uint16_t bf16;  // bfloat16 bit pattern in memory
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------------------------
+// conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16 b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return f32_to_bf16(v); }
+
+// ---------------------------------------------------------------------------------------------
+// Vector of N consecutive elements held by one lane, loaded with the widest aligned accesses.
+template <typename T, int N> struct Vec;
+
+template <int N> struct Vec<float, N> {
+    static_assert(N % 4 == 0 || N == 2 || N == 1, "fp32 vector width");
+    float v[N];
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < N / 4; ++i) {
+                float4 t = reinterpret_cast<const float4*>(p)[i];
+                v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+            }
+        } else if constexpr (N == 2) {
+            float2 t = *reinterpret_cast<const float2*>(p);
+            v[0] = t.x; v[1] = t.y;
+        } else {
+            v[0] = *p;
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = 0.f;
+    }
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+template <int N> struct Vec<bf16, N> {
+    static_assert(N % 2 == 0, "bf16 vector width");
+    uint32_t w[N / 2];
+    __device__ __forceinline__ void load(const bf16* p) {
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < N / 8; ++i) {
+                uint4 t = reinterpret_cast<const uint4*>(p)[i];
+                w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+            }
+        } else if constexpr (N == 4) {
+            uint2 t = *reinterpret_cast<const uint2*>(p);
+            w[0] = t.x; w[1] = t.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) w[i] = 0u;
+    }
+    __device__ __forceinline__ float get(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+};
+
+// ---------------------------------------------------------------------------------------------
+// One 16x16x32 matrix-core step on 8-element operand fragments.
+// Lane l holds row/column (l % 16) and reduction slots 8*(l/16) .. 8*(l/16)+7 of both operands; the
+// hardware pairs A's and B's slots identically, so any assignment of k indices to slots that is the
+// same for both operands yields the full dot product. Output: lane l, register j holds
+// C[4*(l/16) + j][l % 16].
+//   bf16: one v_mfma_f32_16x16x32_bf16.
+//   fp32: eight v_mfma_f32_16x16x4_f32, the e-th taking element e of every lane.
+__device__ __forceinline__ f32x4 mma16x16x32(const Vec<bf16, 8>& a, const Vec<bf16, 8>& b, f32x4 c) {
+    bf16x8_t av = __builtin_bit_cast(bf16x8_t, a.w);
+    bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b.w);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma16x16x32(const Vec<float, 8>& a, const Vec<float, 8>& b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+    return c;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cross-lane helpers (wave64). DPP row operations act inside each row of 16 lanes.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// all-reduce over the 16 lanes of a row: xor 1, xor 2 (quad permutes), then rotate by 4 and 8
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x128>(v);
+    return v;
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// compiler-level ordering point for LDS traffic that stays inside one wave
+__device__ __forceinline__ void wave_sync() { __builtin_amdgcn_wave_barrier(); }
+
+}  // namespace lra

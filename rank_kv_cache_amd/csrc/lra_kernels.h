@@ -1,0 +1,78 @@
+// Internal interface between the C ABI layer (api.hip) and the kernel launchers.
+// Arguments reaching these launchers have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lra {
+
+struct DecodeParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const void* Vlr;
+    const void* B;
+    const int64_t* kv_start;
+    const int32_t* kv_len;
+    const int32_t* agent;
+    float* ws_ml;   // [batch*n_q*n_split][2]: running max (base-2 units) and sum of each split
+    float* ws_o;    // [batch*n_q*n_split][d_head + rank]: unnormalised O | O_lr of each split
+    void* O;
+    int64_t ld_vlr;
+    int64_t kv_rows;
+    int64_t max_kv_len;
+    int batch, n_q, n_kv, G, n_agents, d_head, rank;
+    int n_split, chunk;
+    float scale;
+    bool bf16;
+};
+
+struct PrecomputeParams {
+    const void* X;
+    const void* A;
+    void* Vlr;
+    const int64_t* out_rows;
+    float* ws_part;      // [ksplit][T][NR] fp32 partial products (ksplit > 1)
+    uint32_t* ws_count;  // [row tiles * column groups] arrival counters, zero between calls
+    int64_t T;
+    int64_t ldx;
+    int64_t ld_vlr;
+    int64_t vlr_rows;
+    int d_model;
+    int NR;        // n_agents * rank
+    int kr;        // reduction length handled by one workgroup (multiple of 32)
+    int ksplit;    // workgroups along the reduction
+    int n_cg;      // column groups of up to 64 columns
+    bool bf16;
+};
+
+struct PrefillParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    const void* Vlr;
+    const void* B;
+    void* O;
+    int64_t L_C;
+    int64_t L_P;
+    int64_t ld_vlr;
+    int n_q, n_kv, G, d_head, rank, agent, n_agents;
+    float scale;
+    bool bf16;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_precompute(const PrecomputeParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// Host-side launch geometry shared by the workspace-size query and the launch itself.
+struct PrecomputePlan {
+    int kr, ksplit, n_rt, n_cg;
+    size_t part_bytes, count_bytes;
+};
+PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);
+
+int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len);
+
+}  // namespace lra

@@ -1,0 +1,152 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function that include/lra.h declares, and reject every
+invalid scalar argument with the documented status before anything is enqueued. Pointers
+passed here are fake but 16/256-byte aligned: validation never dereferences them, and every
+call below fails validation, so nothing reaches the GPU runtime.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rank_kv_cache_amd as lra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lra.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000  # fake aligned device address (never dereferenced: every call here fails validation)
+WS = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(lra.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lra.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lra.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (lra_[a-z0-9_]+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings():
+    assert lra.abi_version() == 1
+    names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
+    assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
+
+
+# ---------------------------------------------------------------------------------------- decode
+def decode(**kw):
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+             max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
+             split=0, ws=WS, ws_bytes=1 << 30, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"],
+                                    a["kv_start"], a["kv_len"], a["max_kv_len"], a["B"], a["n_agents"], a["agent"],
+                                    a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"], a["split"], a["ws"],
+                                    a["ws_bytes"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), E_UNSUP), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_q=36, n_kv=4), E_UNSUP),
+    (dict(n_q=30, n_kv=8), E_SHAPE), (dict(n_kv=0), E_SHAPE), (dict(batch=-1), E_SHAPE),
+    (dict(ld_vlr=16), E_SHAPE), (dict(ld_vlr=28), E_SHAPE), (dict(split=100), E_SHAPE), (dict(split=-64), E_SHAPE),
+    (dict(max_kv_len=-1), E_SHAPE), (dict(kv_rows=-5), E_SHAPE), (dict(n_agents=0), E_SHAPE),
+    (dict(scale=float("nan")), E_SHAPE), (dict(Q=None), E_NULL), (dict(kv_len=None), E_NULL),
+    (dict(agent=None), E_NULL), (dict(O=None), E_NULL), (dict(K=P + 8), E_SHAPE),
+    (dict(ws=None), E_WS), (dict(ws=WS + 64), E_WS), (dict(ws_bytes=16), E_WS),
+    (dict(max_kv_len=1 << 31), E_SHAPE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert decode(**kw) == status
+    assert lra._lib.lra_last_error().decode() != ""
+
+
+def test_decode_empty_batch_is_a_no_op():
+    assert decode(batch=0, Q=None, ws=None, ws_bytes=0) == OK
+
+
+def test_decode_workspace_size_follows_split():
+    b, n_q, d, r = 16, 32, 128, 8
+    chunk = lra.lra_attn_decode_default_split(b, 8, 66400)
+    assert chunk % 64 == 0 and chunk >= 64
+    n_split = -(-66400 // chunk)
+    recs = b * n_q * n_split
+    ml = recs * 2 * 4
+    expect = -(-ml // 256) * 256 + recs * (d + r) * 4
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == expect
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == (
+        -(-(b * n_q * 65 * 8) // 256) * 256 + b * n_q * 65 * (d + r) * 4)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
+    assert lra.lra_attn_decode_default_split(1, 8, 1900) == 64
+
+
+# ---------------------------------------------------------------------------------------- prefill
+def prefill(**kw):
+    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, B=P, n_agents=3, agent=0,
+             n_q=4, n_kv=2, d=64, r=8, scale=0.125, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_prefill(a["dtype"], a["Q"], a["L_C"], a["L_P"], a["K"], a["V"], a["Vlr"], a["ld_vlr"],
+                                     a["B"], a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"],
+                                     a["scale"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=-1), E_UNSUP), (dict(d=32), E_UNSUP), (dict(r=32), E_UNSUP), (dict(n_q=3), E_SHAPE),
+    (dict(L_C=-1), E_SHAPE), (dict(L_P=-1), E_SHAPE), (dict(L_P=1 << 31), E_SHAPE), (dict(agent=3), E_INDEX),
+    (dict(agent=-1), E_INDEX), (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=float("inf")), E_SHAPE),
+    (dict(B=None), E_NULL), (dict(Vlr=None), E_NULL), (dict(O=P + 2), E_SHAPE),
+])
+def test_prefill_rejects_bad_arguments(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_empty_chunk_is_a_no_op():
+    assert prefill(L_C=0, Q=None, O=None) == OK
+
+
+# ---------------------------------------------------------------------------------------- precompute
+def precompute(**kw):
+    a = dict(dtype=1, X=P, T=2048, d_model=4096, ldx=4096, A=P, n_agents=3, r=8, Vlr=P, ld_vlr=24,
+             vlr_rows=18432, out_rows=None, ws=WS, ws_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return lra._lib.lra_lr_precompute(a["dtype"], a["X"], a["T"], a["d_model"], a["ldx"], a["A"], a["n_agents"],
+                                      a["r"], a["Vlr"], a["ld_vlr"], a["vlr_rows"], a["out_rows"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), E_UNSUP), (dict(d_model=4004), E_UNSUP), (dict(n_agents=3, r=3), E_UNSUP),
+    (dict(T=-1), E_SHAPE), (dict(ldx=4095), E_SHAPE), (dict(ldx=4092), E_SHAPE), (dict(ld_vlr=20), E_SHAPE),
+    (dict(vlr_rows=100), E_SHAPE), (dict(vlr_rows=-1, out_rows=P), E_SHAPE), (dict(n_agents=0), E_SHAPE),
+    (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(Vlr=P + 4), E_SHAPE),
+    (dict(ws=None), E_WS), (dict(ws_bytes=100), E_WS), (dict(ws=WS + 16), E_WS),
+])
+def test_precompute_rejects_bad_arguments(kw, status):
+    assert precompute(**kw) == status
+
+
+def test_precompute_empty_is_a_no_op():
+    assert precompute(T=0, X=None, ws=None, ws_bytes=0) == OK
+
+
+def test_precompute_workspace_sizes():
+    # large T: 128 row tiles x 2 reduction splits; tiny T: many splits, counters + partials
+    ws = lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8)
+    assert ws == 512 + 2 * 2048 * 24 * 4      # 128 counters (512 B) + 2 partial planes
+    ws5 = lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16)
+    assert ws5 == 256 + 32 * 32 * 48 * 4      # 2 counters padded to 256 B + 32 partial planes
+    assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0

@@ -1,0 +1,171 @@
+"""GPU parity of lra_attn_decode against the fp64 oracle (needs an MI355X and liblra.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_kv_cache_amd as lra
+import workloads as W
+from tests.gpu_util import check, dev, dev_idx, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+class F64Rows:
+    """Row-sliceable view of a host tensor that widens only the rows asked for (big caches)."""
+
+    def __init__(self, t: W.HostTensor):
+        self.t = t
+
+    def __getitem__(self, idx):
+        return W.HostTensor(self.t.data[idx], self.t.dtype).as_f64()
+
+
+def run_decode(c: W.DecodeBatch, keys_per_split=0, max_kv_len=None, kv_rows=None):
+    s = c.shape
+    K, V, L = dev(c.K), dev(c.V), dev(c.V_lr)
+    O = lra.lra_attn_decode(dev(c.Q), K, V, L, dev_idx(c.kv_start, torch.int64), dev_idx(c.kv_len, torch.int32),
+                            c.max_kv_len if max_kv_len is None else max_kv_len, dev(c.B),
+                            dev_idx(c.agent, torch.int32), s.scale, keys_per_split)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_decode(c: W.DecodeBatch, requests=None):
+    return oracle.attn_decode(c.Q.as_f64(), F64Rows(c.K), F64Rows(c.V), F64Rows(c.V_lr), c.B.as_f64(),
+                              c.kv_start, c.kv_len, c.agent, c.shape.scale, requests=requests)
+
+
+@pytest.mark.parametrize("agent", [0, 1, 2])
+def test_llama_decode_L1900_every_agent(agent):
+    c = W.llama_decode(agent=agent)
+    say(f"decode llama L=1900 agent={agent}")
+    check(run_decode(c), ref_decode(c), "bf16", f"agent {agent}")
+
+
+@pytest.mark.parametrize("split", [64, 128, 192, 256, 512, 1024, 2048, 4096])
+def test_llama_decode_every_split_size(split):
+    c = W.llama_decode(agent=1)
+    say(f"decode llama L=1900 keys_per_split={split}")
+    check(run_decode(c, keys_per_split=split), ref_decode(c), "bf16", f"split {split}")
+
+
+SHAPES = [
+    # dtype, n_q, n_kv, d, r
+    ("bf16", 32, 8, 128, 8), ("bf16", 32, 8, 128, 16), ("bf16", 8, 2, 64, 8), ("bf16", 64, 8, 128, 8),
+    ("bf16", 24, 8, 128, 16), ("bf16", 8, 8, 64, 16), ("bf16", 40, 8, 64, 8),
+    ("f32", 4, 2, 64, 8), ("f32", 32, 8, 128, 16), ("f32", 16, 2, 128, 8),
+]
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d,r", SHAPES)
+def test_decode_shapes_ragged_lengths(dtype, n_q, n_kv, d, r):
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype=dtype)
+    lens = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700, 0, 1000]
+    c = W.random_decode((100, n_q, n_kv, d, r, 0 if dtype == "f32" else 1), s, lens)
+    say(f"decode shape {dtype} n_q={n_q} n_kv={n_kv} d={d} r={r}")
+    ref = ref_decode(c)
+    for split in (0, 64, 320):
+        got = run_decode(c, keys_per_split=split)
+        check(got, ref, dtype, f"{dtype} {n_q}/{n_kv} d={d} r={r} split={split}")
+        assert np.all(got[12] == 0.0)
+
+
+def test_tiny_fp32_decode_shared_ranges():
+    s = W.TINY_SHAPE
+    c = W.random_decode((101,), s, kv_lens=[257, 257, 257, 100, 1], kv_starts=[0, 0, 0, 157, 256], rows=257,
+                        agents=[0, 1, 2, 1, 0])
+    say("decode tiny fp32 shared ranges")
+    check(run_decode(c), ref_decode(c), "f32")
+
+
+def test_decode_never_reads_outside_ranges():
+    """Rows outside every request's range hold NaN; a tile that over-read them would poison O."""
+    s = W.LLAMA_SHAPE
+    lens = [1, 70, 129, 300, 64]
+    starts = [3, 80, 160, 400, 900]
+    c = W.random_decode((102,), s, kv_lens=lens, kv_starts=starts, rows=1100, agents=[0, 1, 2, 0, 2])
+    used = np.zeros(1100, bool)
+    for a, n in zip(starts, lens):
+        used[a:a + n] = True
+    for t in (c.K, c.V, c.V_lr):
+        W.fill_rows(t, np.where(~used)[0], float("nan"))
+    say("decode NaN poison outside ranges")
+    for split in (0, 64, 128):
+        check(run_decode(c, keys_per_split=split), ref_decode(c), "bf16", f"split {split}")
+
+
+def test_decode_invalid_requests_give_nan_rows():
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((103,), s, kv_lens=[50, 60, 40, 30, 20, 10], kv_starts=[0, 100, 0, 200, 10, 0], rows=300,
+                        agents=[0, 3, 1, -1, 2, 0])
+    kv_len = c.kv_len.copy()
+    kv_start = c.kv_start.copy()
+    kv_len[2] = 400            # beyond max_kv_len (passed as 100) and beyond the cache
+    kv_start[4] = 290          # range runs past kv_rows = 300
+    kv_start[5] = -1           # negative start
+    cc = W.DecodeBatch(s, c.Q, c.K, c.V, c.V_lr, c.B, kv_start, kv_len, c.agent)
+    say("decode invalid requests")
+    got = run_decode(cc, max_kv_len=100)
+    assert np.all(np.isnan(got[[1, 2, 3, 4, 5]]))
+    check(got[[0]], ref_decode(c, requests=[0]), "bf16")
+
+
+def test_decode_agent_signature():
+    """B_k = 0.5 (k+1) everywhere and the LR slice of agent k offset by 10k: a wrong slice or B is off by O(1)."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((104,), s, kv_lens=[500, 500, 500, 333], kv_starts=[0, 0, 0, 50], rows=500,
+                        agents=[0, 1, 2, 2])
+    lr = c.V_lr.as_f32()
+    for k in range(3):
+        lr[:, k * s.rank:(k + 1) * s.rank] += 10.0 * k
+    B = np.concatenate([np.full((1, s.rank, s.d_kv), 0.5 * (k + 1), np.float32) for k in range(3)])
+    cc = W.DecodeBatch(s, c.Q, c.K, c.V, W.to_storage(lr, "bf16"), W.to_storage(B, "bf16"), c.kv_start, c.kv_len,
+                       c.agent)
+    say("decode agent signature")
+    ref = ref_decode(cc)
+    assert np.abs(ref[2] - ref[1]).max() > 50
+    check(run_decode(cc), ref, "bf16")
+
+
+def test_decode_lr_isolation():
+    """V_base = 0 and B ~ N(0,1): the output is the LR path alone, so errors in it cannot hide under atol."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((105,), s, kv_lens=[4000, 1234, 77], agents=[2, 0, 1], b_std=1.0)
+    zero = W.to_storage(np.zeros(c.V.shape, np.float32), "bf16")
+    cc = W.DecodeBatch(s, c.Q, c.K, zero, c.V_lr, c.B, c.kv_start, c.kv_len, c.agent)
+    say("decode LR isolation")
+    ref = ref_decode(cc)
+    got = run_decode(cc)
+    st = check(got, ref, "bf16")
+    assert st["normwise"] < 2e-2
+
+
+def test_decode_is_deterministic():
+    c = W.llama_decode(agent=2)
+    say("decode determinism")
+    a = run_decode(c)
+    b = run_decode(c)
+    assert np.array_equal(a, b)
+
+
+def test_long_context_decode_16x66400():
+    """The full 16-request x 66,400-token launch (default split) with three requests checked end to end."""
+    say("decode 16 x 66400: generating inputs")
+    c = W.llama_long_decode()
+    say("decode 16 x 66400: running")
+    got = run_decode(c)
+    for b in (0, 7, 15):
+        say(f"decode 16 x 66400: oracle request {b}")
+        check(got[b:b + 1], ref_decode(c, requests=[b]), "bf16", f"request {b}")
+
+
+def test_ministral_layer_decode_full_size():
+    say("decode ministral layer 0: generating inputs")
+    dec, _ = W.ministral_layer(0)
+    got = run_decode(dec)
+    lens = dec.kv_len
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 5, 17]
+    for b in picks:
+        say(f"decode ministral layer 0: oracle request {b} (L={int(lens[b])})")
+        check(got[b:b + 1], ref_decode(dec, requests=[b]), "bf16", f"request {b}")

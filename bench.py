@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Throughput of the Flash-LoRA-Attention hot path on one MI355X.
+
+Headline (the JSON line's ``value``): decode over 16 requests x 66,400 cached tokens each,
+Llama-3.1-8B layer shapes (32 query / 8 KV heads, d_head 128), rank r = 8, 3 agents, bf16;
+one step = one lra_attn_decode call over the whole batch. Reported as algorithmic HBM GB/s.
+
+The same run also measures, as extra fields: the causal chunked prefill at L_P = 16,384 +
+L_C = 2,048 (TFLOP/s), the LR precompute of 2,048 x 4,096 hidden states (GB/s), decode of one
+request at L = 1,900, and the Ministral-8B-shaped 36-layer step (precompute + decode per layer,
+32 requests, r = 16). The CPU baseline is the fp64 oracle timed on a bounded sample of the
+headline workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode HBM GB/s & prefill TFLOP/s (frac. of peak) at 1.9k–66.4k ctx, r=8"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 (and fp16) matrix-core peak, TFLOP/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ("rank_kv_cache_amd/csrc/decode.hip", "rank_kv_cache_amd/csrc/lra_device.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------- algorithmic work
+def decode_bytes(kv_len, agents, n_q, n_kv, d, r, elem=2) -> int:
+    """K and V_base rows once per request, the agent's r-column V_lr slice, Q and O, and each
+    distinct agent's B once."""
+    rows = int(sum(int(x) for x in kv_len))
+    return (rows * (2 * n_kv * d + r) + len(kv_len) * 2 * n_q * d + len(set(int(a) for a in agents)) * r * n_kv * d) * elem
+
+
+def precompute_bytes(T, d_model, NR, elem=2) -> int:
+    return (T * d_model + NR * d_model + T * NR) * elem
+
+
+def prefill_flops(L_P, L_C, n_q, d, r) -> int:
+    """Unmasked (query, key) pairs x (4d: QK^T and PV_base, + 2r: PV_lr) per head, plus the
+    up-projection O_lr B (2 r d per query row)."""
+    pairs = L_C * L_P + L_C * (L_C + 1) // 2
+    return pairs * n_q * (4 * d + 2 * r) + L_C * n_q * 2 * r * d
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name: str, sources) -> tuple:
+    """HBM bytes per launch from a committed counter summary, if it was taken on the current source."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_hash(sources):
+        return None, "kernel source changed since the counters were taken"
+    try:
+        return int(float(fields["hbm_bytes_per_launch"])), path
+    except (KeyError, ValueError):
+        return None, "summary lacks hbm_bytes_per_launch"
+
+
+# ------------------------------------------------------------------------------- timing helpers
+def time_launches(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+# ------------------------------------------------------------------------------- workloads
+def upload(t, torch):
+    import numpy as np
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.data)).cuda()
+
+
+def bench_long_decode(args, torch, lra, W, out):
+    log("[bench] decode 16 x 66400: generating inputs")
+    c = W.llama_long_decode()
+    s = c.shape
+    Q, K, V, L, B = (upload(t, torch) for t in (c.Q, c.K, c.V, c.V_lr, c.B))
+    ks = torch.as_tensor(c.kv_start, dtype=torch.int64).cuda()
+    kl = torch.as_tensor(c.kv_len, dtype=torch.int32).cuda()
+    ag = torch.as_tensor(c.agent, dtype=torch.int32).cuda()
+    ws = torch.zeros(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(Q)
+
+    def step():
+        lra.lra_attn_decode(Q, K, V, L, ks, kl, c.max_kv_len, B, ag, s.scale, 0, ws, O)
+
+    log(f"[bench] decode 16 x 66400: {args.warmup} warmup + {args.steps} timed steps")
+    ms = time_launches(step, args.steps, args.warmup, torch)
+    nbytes = decode_bytes(c.kv_len, c.agent, s.n_q, s.n_kv, s.d_head, s.rank)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic, src = counter_traffic("decode_16x66400_counters.txt", DECODE_SOURCES)
+    out["headline"] = {
+        "ms_per_step": ms, "gbs": gbs, "bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_split_kernel<bf16, 128, 8, 4>", "bytes_per_launch": nbytes,
+                     "traffic_source": src},
+        "config": {"workload": W.WORKLOAD_NAMES[W.LLAMA_LONG_DECODE], "batch": c.batch, "kv_len": int(c.kv_len[0]),
+                   "n_q": s.n_q, "n_kv": s.n_kv, "d_head": s.d_head, "rank": s.rank, "n_agents": s.n_agents,
+                   "keys_per_split": lra.lra_attn_decode_default_split(c.batch, s.n_kv, c.max_kv_len),
+                   "parallelism": "none"},
+    }
+    out["_long_decode_case"] = c
+    del Q, K, V, L, B, O, ws
+    torch.cuda.empty_cache()
+
+
+def bench_prefill(args, torch, lra, W, out):
+    log("[bench] prefill 16384 + 2048: generating inputs")
+    c = W.llama_prefill()
+    s = c.shape
+    Q, K, V, L, B = (upload(t, torch) for t in (c.Q, c.K, c.V, c.V_lr, c.B))
+    O = torch.empty_like(Q)
+
+    def step():
+        lra.lra_attn_prefill(Q, c.L_P, K, V, L, B, 0, s.scale, O)
+
+    reps = max(3, args.steps // 10)
+    ms = time_launches(step, reps, 2, torch)
+    fl = prefill_flops(c.L_P, c.L_C, s.n_q, s.d_head, s.rank)
+    tf = fl / (ms * 1e-3) / 1e12
+    out["prefill_llama_LP16384_LC2048_r8"] = {
+        "ms": round(ms, 4), "tflops": round(tf, 2), "flops": fl, "peak_tflops": BF16_PEAK_TFLOPS,
+        "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma", "reps": reps}
+    del Q, K, V, L, B, O
+    torch.cuda.empty_cache()
+
+
+def bench_precompute(args, torch, lra, W, out):
+    """X rotates over enough copies (> 256 MB Infinity Cache) that every launch streams X from HBM."""
+    case = W.llama_precompute()
+    s = case.shape
+    n_copies = 40
+    X0 = upload(case.X, torch)
+    Xs = [X0.clone() for _ in range(n_copies)]
+    A = upload(W.HostTensor(case.A.data.T.copy(), case.A.dtype), torch)
+    Vlr = torch.zeros((case.X.shape[0], s.n_agents * s.rank), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(lra.lra_lr_precompute_workspace_bytes(case.X.shape[0], s.d_model, s.n_agents, s.rank),
+                     dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def step():
+        lra.lra_lr_precompute(Xs[it[0] % n_copies], A, s.n_agents, s.rank, Vlr, None, ws)
+        it[0] += 1
+
+    ms = time_launches(step, 400, 40, torch)
+    nb = precompute_bytes(case.X.shape[0], s.d_model, s.n_agents * s.rank)
+    gbs = nb / (ms * 1e-3) / 1e9
+    out["precompute_llama_2048x4096_r8"] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1), "bytes": nb,
+                                           "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm",
+                                           "x_copies_rotated": n_copies}
+    del Xs, X0, A, Vlr, ws
+    torch.cuda.empty_cache()
+
+
+def bench_short_decode(args, torch, lra, W, out):
+    """One request over 1,900 keys (7.8 MB): latency-bound; caches rotate over 64 copies."""
+    c = W.llama_decode()
+    s = c.shape
+    n_copies = 64
+    Ks = [upload(c.K, torch) for _ in range(n_copies)]
+    Vs = [upload(c.V, torch) for _ in range(n_copies)]
+    L, B, Q = upload(c.V_lr, torch), upload(c.B, torch), upload(c.Q, torch)
+    ks = torch.as_tensor(c.kv_start, dtype=torch.int64).cuda()
+    kl = torch.as_tensor(c.kv_len, dtype=torch.int32).cuda()
+    ag = torch.as_tensor(c.agent, dtype=torch.int32).cuda()
+    ws = torch.zeros(lra.lra_attn_decode_workspace_bytes(1, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(Q)
+    it = [0]
+
+    def step():
+        i = it[0] % n_copies
+        lra.lra_attn_decode(Q, Ks[i], Vs[i], L, ks, kl, c.max_kv_len, B, ag, s.scale, 0, ws, O)
+        it[0] += 1
+
+    ms = time_launches(step, 400, 40, torch)
+    nb = decode_bytes(c.kv_len, c.agent, s.n_q, s.n_kv, s.d_head, s.rank)
+    gbs = nb / (ms * 1e-3) / 1e9
+    out["decode_llama_b1_L1900_r8"] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1), "bytes": nb,
+                                       "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "latency (7.8 MB)"}
+    del Ks, Vs
+    torch.cuda.empty_cache()
+
+
+def bench_ministral_step(args, torch, lra, W, out):
+    """36 layers x (LR precompute of the 32 newest tokens -> decode of 32 requests), per-layer caches.
+    Layer caches are drawn on the GPU (seeded torch generator) to keep set-up to seconds; the host
+    generator with identical shapes feeds the parity tests of layers 0 and 35."""
+    s = W.MINISTRAL_SHAPE
+    lens = W.ministral_lengths()
+    agents = W.ministral_agents()
+    starts = [0]
+    for x in lens[:-1]:
+        starts.append(starts[-1] + int(x))
+    rows = int(sum(int(x) for x in lens))
+    n_layers = W.MINISTRAL_LAYERS
+    g = torch.Generator(device="cuda")
+    layers = []
+    log(f"[bench] ministral step: drawing {n_layers} layer caches ({rows} rows each) on the GPU")
+    for layer in range(n_layers):
+        g.manual_seed(1_000_003 * (layer + 1) + 42)
+        K = torch.randn((rows, s.n_kv, s.d_head), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        V = torch.randn((rows, s.n_kv, s.d_head), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        L = torch.randn((rows, s.n_agents * s.rank), generator=g, device="cuda").to(torch.bfloat16)
+        A = (torch.randn((s.n_agents * s.rank, s.d_model), generator=g, device="cuda") / 64.0).to(torch.bfloat16)
+        B = (torch.randn((s.n_agents, s.rank, s.d_kv), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+        X = torch.randn((len(lens), s.d_model), generator=g, device="cuda").to(torch.bfloat16)
+        Q = torch.randn((len(lens), s.n_q, s.d_head), generator=g, device="cuda").to(torch.bfloat16)
+        layers.append((K, V, L, A, B, X, Q))
+    ks = torch.as_tensor(starts, dtype=torch.int64).cuda()
+    kl = torch.as_tensor(lens, dtype=torch.int32).cuda()
+    ag = torch.as_tensor(agents, dtype=torch.int32).cuda()
+    new_rows = ks + kl.to(torch.int64) - 1
+    max_len = int(max(lens))
+    ws_dec = torch.zeros(lra.lra_attn_decode_workspace_bytes(len(lens), s.n_q, s.n_kv, s.d_head, s.rank, max_len),
+                         dtype=torch.uint8, device="cuda")
+    ws_pre = torch.zeros(max(256, lra.lra_lr_precompute_workspace_bytes(len(lens), s.d_model, s.n_agents, s.rank)),
+                         dtype=torch.uint8, device="cuda")
+    O = torch.empty((len(lens), s.n_q, s.d_head), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        for (K, V, L, A, B, X, Q) in layers:
+            lra.lra_lr_precompute(X, A, s.n_agents, s.rank, L, new_rows, ws_pre)
+            lra.lra_attn_decode(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, 0, ws_dec, O)
+
+    reps = max(3, args.steps // 10)
+    ms = time_launches(step, reps, 1, torch)
+    nb = n_layers * (decode_bytes(lens, agents, s.n_q, s.n_kv, s.d_head, s.rank)
+                     + precompute_bytes(len(lens), s.d_model, s.n_agents * s.rank))
+    gbs = nb / (ms * 1e-3) / 1e9
+    out["ministral_step_36x_b32_r16"] = {"ms": round(ms, 3), "gbs": round(gbs, 1), "bytes": nb,
+                                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm", "reps": reps,
+                                         "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
+                                         "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
+    del layers
+    torch.cuda.empty_cache()
+
+
+def cpu_baseline(case, W, budget_s: float):
+    """The fp64 oracle (as it stands) on whole requests of the headline workload, until the budget is used."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    s = case.shape
+    t_total, done, nbytes = 0.0, 0, 0
+    while done < case.batch and (t_total < budget_s or done == 0):
+        b = done
+        r0, n = int(case.kv_start[b]), int(case.kv_len[b])
+        K = W.HostTensor(case.K.data[r0:r0 + n], "bf16").as_f64()
+        V = W.HostTensor(case.V.data[r0:r0 + n], "bf16").as_f64()
+        L = W.HostTensor(case.V_lr.data[r0:r0 + n], "bf16").as_f64()
+        Q = case.Q.as_f64()[b:b + 1]
+        t0 = time.perf_counter()
+        oracle.attn_decode(Q, K, V, L, case.B.as_f64(), [0], [n], [int(case.agent[b])], s.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        nbytes += decode_bytes([n], [int(case.agent[b])], s.n_q, s.n_kv, s.d_head, s.rank)
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {case.batch} requests of the 16 x 66,400 decode (fp64 oracle, whole requests; "
+                      f"{t_total:.1f} s of CPU work, input widening excluded)",
+            "seconds": round(t_total, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", nargs="*", default=None,
+                    choices=["decode", "prefill", "precompute", "short", "ministral", "cpu"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_kv_cache_amd as lra
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    only = set(args.only) if args.only is not None else {"decode", "prefill", "precompute", "short", "ministral", "cpu"}
+    out = {}
+    if "decode" in only or "cpu" in only:
+        bench_long_decode(args, torch, lra, W, out)
+    for name, fn in (("prefill", bench_prefill), ("precompute", bench_precompute), ("short", bench_short_decode),
+                     ("ministral", bench_ministral_step)):
+        if name in only:
+            log(f"[bench] {name}")
+            fn(args, torch, lra, W, out)
+    cpu = None
+    if "cpu" in only:
+        log("[bench] CPU baseline (fp64 oracle)")
+        cpu = cpu_baseline(out["_long_decode_case"], W, args.cpu_budget)
+    head = out.get("headline")
+    extra = {k: v for k, v in out.items() if k not in ("headline", "_long_decode_case")}
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 1) if head else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4) if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"] if head else {"workload": "partial run"},
+        "roofline": head["roofline"] if head else None,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -111,7 +111,10 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * V_lr     (device) [L_P+L_C x ld_vlr], agent a owns columns a*rank .. a*rank+rank-1
  * B        (device) [n_agents x rank x n_kv*d_head]: B_a, one r x (n_kv*d_head) matrix per agent
  * O        (device) [L_C x n_q x d_head] output
- * In bf16 the probabilities are rounded to bf16 before the P.V products; l, m, O, O_lr are fp32.
+ * bf16 inputs: Q.K products are exact (bf16 operands, fp32 accumulation); for P.V the
+ * probabilities are rounded to fp16 and V_base / V_lr converted exactly to fp16, so entries of the
+ * KV head's V_base rows 0 .. L_P+L_C-1 and of the agent's V_lr slice must satisfy |v| <= 65504:
+ * a query row whose workgroup meets a larger entry gets NaN. l, m, O and O_lr are fp32.
  * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. L_C = 0 enqueues nothing.
  */
 int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
@@ -121,9 +124,10 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
- * Batched decode, one new query token per request, split along the key axis (each split writes a
- * partial (m, l, O, O_lr) in fp32 to the workspace; a second kernel merges the partials with the
- * log-sum-exp rule, applies B_agent once and normalises). Request b attends all rows
+ * Batched decode, one new query token per request, split along the key axis: each split writes a
+ * partial (m, l, O, O_lr) in fp32 to the workspace, and the split that finishes last for its
+ * (request, KV head) merges the partials with the log-sum-exp rule, applies B_agent once and
+ * normalises (one kernel launch per call). Request b attends all rows
  * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
  * kv_len[b] = 0 gives a zero output row.
  *
@@ -134,7 +138,9 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * max_kv_len (host) an upper bound on every kv_len[b]; it sizes the launch
  * B        (device) [n_agents x rank x n_kv*d_head]
  * keys_per_split  keys handled by one split (multiple of 64), or 0 for the library's choice
- * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned, no initial contents
+ * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned. It must be
+ *          zero-filled before its first use; every call leaves it zero-filled again (only its
+ *          arrival counters matter). Calls that share one workspace must not overlap in time.
  * O        (device) [batch x n_q x d_head] output
  * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues nothing.
  */

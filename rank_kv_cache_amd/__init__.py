@@ -200,7 +200,8 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
     """One query per request over rows [kv_start[b], kv_start[b] + kv_len[b]) of the shared caches.
 
     Q [batch, n_q, d]; K_base, V_base [rows, n_kv, d]; V_lr [rows, ld]; kv_start int64 [batch];
-    kv_len, agent int32 [batch]; B [N, r, n_kv*d]."""
+    kv_len, agent int32 [batch]; B [N, r, n_kv*d]. ``workspace`` (uint8, zero-filled before first
+    use, left zero-filled by every call) is allocated zeroed when omitted."""
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)
@@ -217,7 +218,7 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if O is None:
         O = torch.empty_like(Q)

@@ -36,16 +36,17 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // -------------------------------------------------------------------------- decode workspace
 struct DecodeLayout {
     int chunk, n_split;
-    size_t ml_bytes, o_off, total;
+    size_t ml_off, o_off, total;
 };
 
-DecodeLayout decode_layout(int batch, int n_q, int d_head, int rank, int64_t max_kv_len, int chunk) {
+// [arrival counters: batch*n_kv uint32][m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], 256-aligned parts
+DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, int64_t max_kv_len, int chunk) {
     DecodeLayout L{};
     L.chunk = chunk;
     L.n_split = max_kv_len > 0 ? int((max_kv_len + chunk - 1) / chunk) : 0;
     const size_t recs = size_t(batch) * size_t(n_q) * size_t(L.n_split);
-    L.ml_bytes = recs * 2 * sizeof(float);
-    L.o_off = align_up(L.ml_bytes, 256);
+    L.ml_off = align_up(size_t(batch) * size_t(n_kv) * sizeof(uint32_t), 256);
+    L.o_off = L.ml_off + align_up(recs * 2 * sizeof(float), 256);
     L.total = recs ? L.o_off + recs * size_t(d_head + rank) * sizeof(float) : 0;
     return L;
 }
@@ -163,7 +164,7 @@ LRA_EXPORT size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, in
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || max_kv_len <= 0 || d_head <= 0 || rank <= 0) return 0;
     if (keys_per_split < 0 || keys_per_split % 64 != 0) return 0;
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    return decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk).total;
+    return decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, chunk).total;
 }
 
 LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
@@ -191,7 +192,7 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
+    const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, chunk);
     if (L.total) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -200,7 +201,8 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
     lra::DecodeParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B;
     p.kv_start = kv_start; p.kv_len = kv_len; p.agent = agent;
-    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_count = static_cast<uint32_t*>(workspace);
+    p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;

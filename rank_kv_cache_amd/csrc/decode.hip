@@ -7,7 +7,7 @@
 // d_head (LRAgent page, "core method" / "technical novelty": associativity moves the d_out-wide
 // product out of the key loop).
 //
-// Kernel 1 (decode_split): one workgroup per (request b, KV head g, key split s), 4 waves.
+// One kernel, one workgroup per (request b, KV head g, key split s), 4 waves.
 //   * the G query heads of KV head g share every K/V/V_lr load (grouped-query attention)
 //   * S = Q K^T on the matrix cores: A operand = the G queries (rows padded to 16), B operand =
 //     16 keys, 8 contiguous d-elements per lane (128-bit loads)
@@ -17,8 +17,10 @@
 //     of every 4, with P broadcast through LDS; keys past the split end are clamped to a valid row
 //     (finite data) and get P = 0, so no row outside [kv_start, kv_start+kv_len) is ever read
 //   * the 4 waves merge their states in LDS and write one fp32 partial (m, l, O, O_lr) per query head
-// Kernel 2 (decode_combine): one workgroup per (request, query head): merges the splits with
-//   weights 2^(m_s - max m), then O = (O + O_lr B_agent[:, g*d:(g+1)*d]) / l, rounded to the output type.
+//   * the split that arrives last for its (request, KV head) (release fence + arrival counter) merges
+//     the partials with weights 2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d:(g+1)*d]) / l
+//     once per query row, rounds to the output type and zeroes the counter for the next call.
+//     Empty requests get zeros and requests with an invalid range or agent get NaN (split 0 writes them).
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -68,10 +70,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int64_t start = p.kv_start[b];
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
-    if (!decode_request_ok(start, len, a, p)) return;       // the combine writes NaN for it
+    const int G = p.G;
+    const bool ok = decode_request_ok(start, len, a, p);
+    if (!ok || len == 0) {
+        // no key to attend: zeros for an empty range, NaN for an invalid request (split 0 writes them)
+        if (s == 0) {
+            T* Op = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * G) * D;
+            const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
+            for (int idx = threadIdx.x; idx < G * D; idx += kThreads) Op[idx] = fill;
+        }
+        return;
+    }
     const int k0 = s * p.chunk;
-    if (k0 >= len) return;                                   // the combine reads only live splits
+    if (k0 >= len) return;                                   // splits past the request's end do nothing
     const int k1 = min(k0 + p.chunk, len);
+    const int ns = (len + p.chunk - 1) / p.chunk;            // live splits of this request
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -82,7 +95,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const T* __restrict__ Vp = static_cast<const T*>(p.V);
     const T* __restrict__ Lp = static_cast<const T*>(p.Vlr);
     const T* __restrict__ Qp = static_cast<const T*>(p.Q);
-    const int G = p.G;
     const int64_t row_stride = int64_t(p.n_kv) * D;
 
     // queries of the group as the MFMA A operand (rows >= G are zero)
@@ -271,68 +283,58 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             p.ws_ml[rec * 2 + 1] = L;
         }
     }
-}
 
-template <typename T, int D, int R>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
-    __shared__ float olr_s[R];
-    __shared__ float ml_s[2];
-    const int bh = blockIdx.x;
-    const int b = bh / p.n_q;
-    const int hq = bh - b * p.n_q;
-    const int g = hq / p.G;
-    const int tid = threadIdx.x;
-    T* __restrict__ Op = static_cast<T*>(p.O) + int64_t(bh) * D;
+    // ---- the last split of (b, g) to arrive merges all splits of the group's query heads
+    __shared__ int last_s;
+    __threadfence();
+    __syncthreads();
+    uint32_t* counter = p.ws_count + int64_t(b) * p.n_kv + g;
+    if (threadIdx.x == 0) last_s = atomicAdd(counter, 1u) == uint32_t(ns - 1);
+    __syncthreads();
+    if (!last_s) return;
+    __threadfence();
 
-    const int64_t start = p.kv_start[b];
-    const int32_t len = p.kv_len[b];
-    const int32_t a = p.agent[b];
-    if (!decode_request_ok(start, len, a, p)) {
-        if (tid < D) Op[tid] = from_f32<T>(__builtin_nanf(""));
-        return;
-    }
-    if (len == 0) {
-        if (tid < D) Op[tid] = from_f32<T>(0.f);
-        return;
-    }
-    const int ns = (len + p.chunk - 1) / p.chunk;
-    const int64_t rec0 = int64_t(bh) * p.n_split;
-
-    // global max over the live splits (wave 0), then weights
-    if (tid < 64) {
+    // per-head maximum and normaliser over the live splits (one wave per head)
+    for (int h = wv; h < G; h += kWaves) {
+        const int64_t rec0 = (bh0 + h) * p.n_split;
         float M = -INFINITY;
-        for (int sidx = tid; sidx < ns; sidx += 64) M = fmaxf(M, p.ws_ml[(rec0 + sidx) * 2]);
+        for (int sidx = lane; sidx < ns; sidx += 64) M = fmaxf(M, p.ws_ml[(rec0 + sidx) * 2]);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
         float L = 0.f;
-        for (int sidx = tid; sidx < ns; sidx += 64) {
+        for (int sidx = lane; sidx < ns; sidx += 64) {
             const float* ml = p.ws_ml + (rec0 + sidx) * 2;
             L = fmaf(fast_exp2(ml[0] - M), ml[1], L);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-        if (tid == 0) { ml_s[0] = M; ml_s[1] = L; }
+        if (lane == 0) { red_m[0][h] = M; red_l[0][h] = L; }
     }
     __syncthreads();
-    const float M = ml_s[0];
-    const float L = ml_s[1];
-
-    float acc = 0.f, acc_lr = 0.f;
-    for (int sidx = 0; sidx < ns; ++sidx) {
-        const float wgt = fast_exp2(p.ws_ml[(rec0 + sidx) * 2] - M);
-        const float* rec = p.ws_o + (rec0 + sidx) * (D + R);
-        if (tid < D) acc = fmaf(wgt, rec[tid], acc);
-        if (tid < R) acc_lr = fmaf(wgt, rec[D + tid], acc_lr);
+    // weighted sums of O | O_lr over the splits
+    for (int idx = threadIdx.x; idx < G * (D + R); idx += kThreads) {
+        const int h = idx / (D + R);
+        const int col = idx - h * (D + R);
+        const int64_t rec0 = (bh0 + h) * p.n_split;
+        const float M = red_m[0][h];
+        float acc = 0.f;
+        for (int sidx = 0; sidx < ns; ++sidx)
+            acc = fmaf(fast_exp2(p.ws_ml[(rec0 + sidx) * 2] - M), p.ws_o[(rec0 + sidx) * (D + R) + col], acc);
+        red_o[1][h][col] = acc;
     }
-    if (tid < R) olr_s[tid] = acc_lr;
     __syncthreads();
-    if (tid < D) {
-        // up-projection once per query row: O += O_lr B_agent[:, g*D + col], then normalise
-        const T* Bp = static_cast<const T*>(p.B) + int64_t(a) * R * (int64_t(p.n_kv) * D) + int64_t(g) * D + tid;
+    // up-projection once per query row: O += O_lr B_agent[:, g*D + col], then normalise and store
+    T* __restrict__ Op = static_cast<T*>(p.O);
+    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * row_stride + int64_t(g) * D;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int h = idx / D;
+        const int col = idx - h * D;
+        float acc = red_o[1][h][col];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) acc = fmaf(olr_s[rr], to_f32<T>(Bp[int64_t(rr) * p.n_kv * D]), acc);
-        Op[tid] = from_f32<T>(acc / L);
+        for (int rr = 0; rr < R; ++rr) acc = fmaf(red_o[1][h][D + rr], to_f32<T>(Bp[int64_t(rr) * row_stride + col]), acc);
+        Op[(bh0 + h) * D + col] = from_f32<T>(acc / red_l[0][h]);
     }
+    if (threadIdx.x == 0) *counter = 0u;
 }
 
 template <typename T, int D, int R, int GP>
@@ -341,9 +343,6 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     const int64_t groups = (bs + 7) / 8;
     const int64_t n_wg = groups * 8 * p.n_kv;
     hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, R>), dim3(unsigned(int64_t(p.batch) * p.n_q)), dim3(128), 0, stream, p);
     return hipGetLastError();
 }
 

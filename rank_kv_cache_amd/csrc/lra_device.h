@@ -27,9 +27,19 @@ __device__ __forceinline__ bf16 f32_to_bf16(float f) {
     return bf16(u >> 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 / fp16, round to nearest even (one v_cvt_pk_* instruction on gfx950)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
+constexpr float kF16Max = 65504.f;
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
@@ -103,6 +113,16 @@ __device__ __forceinline__ f32x4 mma16x16x32(const Vec<bf16, 8>& a, const Vec<bf
     bf16x8_t av = __builtin_bit_cast(bf16x8_t, a.w);
     bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b.w);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// the same step on fp16 operands (8 halves per lane, bit patterns in 4 dwords)
+struct H8 {
+    uint32_t w[4];
+};
+__device__ __forceinline__ f32x4 mma16x16x32_f16(const H8& a, const H8& b, f32x4 c) {
+    f16x8_t av = __builtin_bit_cast(f16x8_t, a.w);
+    f16x8_t bv = __builtin_bit_cast(f16x8_t, b.w);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mma16x16x32(const Vec<float, 8>& a, const Vec<float, 8>& b, f32x4 c) {

@@ -18,6 +18,7 @@ struct DecodeParams {
     const int32_t* agent;
     float* ws_ml;   // [batch*n_q*n_split][2]: running max (base-2 units) and sum of each split
     float* ws_o;    // [batch*n_q*n_split][d_head + rank]: unnormalised O | O_lr of each split
+    uint32_t* ws_count;  // [batch*n_kv] arrival counters of the splits, zero between calls
     void* O;
     int64_t ld_vlr;
     int64_t kv_rows;

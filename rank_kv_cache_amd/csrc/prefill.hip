@@ -7,7 +7,7 @@
 // at positions L_P .. L_P+L_C-1 after the reused context (PReCache summary page), causal mask
 // bottom-right aligned.
 //
-// gfx950 mapping (16x16x32 matrix-core steps, bf16 in / fp32 accumulate; fp32 inputs run the same
+// gfx950 mapping (16x16x32 matrix-core steps with fp32 accumulation; fp32 inputs run the same
 // template on 16x16x4 fp32 steps):
 //   * one workgroup = 4 waves = 128 "query rows" of one KV head; a query row is one (query, head)
 //     pair of that head's group, so all G heads of a group share every K/V tile (grouped-query)
@@ -16,6 +16,10 @@
 //     holds keys 4r..4r+3 (of each 16) for query row n
 //   * that layout is already the B operand of O^T = V^T P^T: two 16-key groups give each lane the
 //     8 keys of its reduction slot, so P never leaves the lane; V is staged transposed in LDS
+//   * bf16 inputs: Q.K runs on bf16 steps; P.V runs on fp16 steps, with V and V_lr converted
+//     bf16 -> fp16 while they are staged (exact for |v| <= 65504) and P rounded to fp16, whose 11
+//     significant bits keep the product within the bf16 tolerance even when a row attends only a
+//     few keys. A workgroup that meets a value beyond the fp16 range writes NaN for its rows.
 //   * the agent's V_lr slice is staged as 16 extra rows of V^T (rows >= r are zero): O_lr^T comes
 //     out of the same P tile as one more 16-row output tile
 //   * online softmax per query row in base 2 (scale*log2(e) folded in): row max over the 4 lanes
@@ -23,6 +27,8 @@
 //   * the next K/V/V_lr tile is fetched into registers while the current one is multiplied
 //   * epilogue: gather O_lr of the row across its 4 lanes, add O_lr B_agent (B slice in LDS),
 //     divide by l, store in the input type (bf16 round-to-nearest-even)
+#include <type_traits>
+
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -36,6 +42,7 @@ constexpr int kMT = 2;            // 16-row tiles per wave
 
 template <typename T> struct PrefillTile {
     static constexpr int BK = sizeof(T) == 2 ? 64 : 32;   // keys per tile
+    using TV = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
 };
 
 template <typename T, int D, int R>
@@ -52,9 +59,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     static_assert(FK >= 1 && BK * D / 8 % kThreads == 0, "tile split");
     constexpr int FL = BK * R / 8;              // 8-element fragments of the V_lr tile
 
+    using TV = typename PrefillTile<T>::TV;   // P.V operand type in LDS (fp16 bits for bf16 inputs)
     __shared__ __align__(16) T k_s[BK * LDK];
-    __shared__ __align__(16) T vt_s[(D + 16) * LDV];
+    __shared__ __align__(16) TV vt_s[(D + 16) * LDV];
     __shared__ float b_s[R * D];
+    __shared__ int range_bad;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, n = lane & 15, rg = lane >> 4;
@@ -106,7 +115,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         b_s[idx] = to_f32<T>(Bp[(int64_t(p.agent) * R + rr) * kv_stride + int64_t(g) * D + c]);
     }
     // rows D+R .. D+15 of V^T stay zero
-    for (int idx = tid; idx < (16 - R) * LDV; idx += kThreads) vt_s[(D + R) * LDV + idx] = from_f32<T>(0.f);
+    for (int idx = tid; idx < (16 - R) * LDV; idx += kThreads) vt_s[(D + R) * LDV + idx] = TV(0);
+    if (tid == 0) range_bad = 0;
+    float vmax = 0.f;   // largest |V| / |V_lr| staged by this thread (fp16 range check)
 
     // ---- tile fetch (registers) and store (LDS)
     Vec<T, 8> kpre[FK], vpre[FK], lpre;
@@ -134,9 +145,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             else lpre.zero();
         }
     };
-    auto element = [](const Vec<T, 8>& v, int e) -> T {
-        if constexpr (sizeof(T) == 2) return T((v.w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        else return v.v[e];
+    // write 8 consecutive elements of one key as 8 rows of the transposed tile (fp16 for bf16 inputs)
+    auto store_col = [&](const Vec<T, 8>& v, int row0, int key) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float lo = bf16_lo(v.w[e2]), hi = bf16_hi(v.w[e2]);
+                vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+                const uint32_t h2 = pack_f16x2(lo, hi);
+                vt_s[(row0 + 2 * e2) * LDV + key] = uint16_t(h2 & 0xffffu);
+                vt_s[(row0 + 2 * e2 + 1) * LDV + key] = uint16_t(h2 >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt_s[(row0 + e) * LDV + key] = v.v[e];
+        }
     };
     auto store = [&]() {
 #pragma unroll
@@ -149,14 +172,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
                 *reinterpret_cast<float4*>(&k_s[key * LDK + d0]) = make_float4(kpre[c].v[0], kpre[c].v[1], kpre[c].v[2], kpre[c].v[3]);
                 *reinterpret_cast<float4*>(&k_s[key * LDK + d0 + 4]) = make_float4(kpre[c].v[4], kpre[c].v[5], kpre[c].v[6], kpre[c].v[7]);
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt_s[(d0 + e) * LDV + key] = element(vpre[c], e);
+            store_col(vpre[c], d0, key);
         }
         if (tid < FL) {
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt_s[(D + r0 + e) * LDV + key] = element(lpre, e);
+            store_col(lpre, D + r0, key);
         }
     };
 
@@ -198,7 +219,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             }
 
         // online softmax per query row; P packed as the B operand of O^T = V^T P^T
-        Vec<T, 8> pf[MT][NKB];
+        using PF = typename std::conditional<sizeof(T) == 2, H8, Vec<float, 8>>::type;
+        PF pf[MT][NKB];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float sv[NU][4];
@@ -232,10 +254,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int kb2 = 0; kb2 < NKB; ++kb2) {
                 if constexpr (sizeof(T) == 2) {
-                    pf[mt][kb2].w[0] = pack_bf16x2(sv[2 * kb2][0], sv[2 * kb2][1]);
-                    pf[mt][kb2].w[1] = pack_bf16x2(sv[2 * kb2][2], sv[2 * kb2][3]);
-                    pf[mt][kb2].w[2] = pack_bf16x2(sv[2 * kb2 + 1][0], sv[2 * kb2 + 1][1]);
-                    pf[mt][kb2].w[3] = pack_bf16x2(sv[2 * kb2 + 1][2], sv[2 * kb2 + 1][3]);
+                    pf[mt][kb2].w[0] = pack_f16x2(sv[2 * kb2][0], sv[2 * kb2][1]);
+                    pf[mt][kb2].w[1] = pack_f16x2(sv[2 * kb2][2], sv[2 * kb2][3]);
+                    pf[mt][kb2].w[2] = pack_f16x2(sv[2 * kb2 + 1][0], sv[2 * kb2 + 1][1]);
+                    pf[mt][kb2].w[3] = pack_f16x2(sv[2 * kb2 + 1][2], sv[2 * kb2 + 1][3]);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -251,8 +273,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
             for (int dt = 0; dt <= NDT; ++dt) {
-                Vec<T, 8> va;
-                const T* vrow = &vt_s[(16 * dt + n) * LDV + 32 * kb2 + 4 * rg];
+                PF va;
+                const TV* vrow = &vt_s[(16 * dt + n) * LDV + 32 * kb2 + 4 * rg];
                 if constexpr (sizeof(T) == 2) {
                     const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
                     const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
@@ -264,7 +286,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
                     va.v[4] = hi.x; va.v[5] = hi.y; va.v[6] = hi.z; va.v[7] = hi.w;
                 }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) oacc[mt][dt] = mma16x16x32(va, pf[mt][kb2], oacc[mt][dt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    if constexpr (sizeof(T) == 2) oacc[mt][dt] = mma16x16x32_f16(va, pf[mt][kb2], oacc[mt][dt]);
+                    else oacc[mt][dt] = mma16x16x32(va, pf[mt][kb2], oacc[mt][dt]);
+                }
             }
 
         __syncthreads();
@@ -275,6 +300,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
 
     // ---- epilogue: l over the row's 4 lanes, O += O_lr B_agent, normalise, store
+    if (sizeof(T) == 2 && !(vmax <= kF16Max)) range_bad = 1;
+    __syncthreads();
+    const bool poison = range_bad != 0;
     T* __restrict__ Op = static_cast<T*>(p.O);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         const int64_t qi = r / G;
         const int qh = int(r - qi * G);
         T* orow = Op + (qi * p.n_q + int64_t(g) * G + qh) * D;
-        const float inv = 1.f / l;
+        const float inv = poison ? __builtin_nanf("") : 1.f / l;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             float o4[4];

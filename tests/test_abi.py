@@ -82,13 +82,14 @@ def test_decode_workspace_size_follows_split():
     b, n_q, d, r = 16, 32, 128, 8
     chunk = lra.lra_attn_decode_default_split(b, 8, 66400)
     assert chunk % 64 == 0 and chunk >= 64
-    n_split = -(-66400 // chunk)
-    recs = b * n_q * n_split
-    ml = recs * 2 * 4
-    expect = -(-ml // 256) * 256 + recs * (d + r) * 4
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == expect
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == (
-        -(-(b * n_q * 65 * 8) // 256) * 256 + b * n_q * 65 * (d + r) * 4)
+    up = lambda v: -(-v // 256) * 256
+
+    def layout(n_split):
+        recs = b * n_q * n_split
+        return up(b * 8 * 4) + up(recs * 2 * 4) + recs * (d + r) * 4   # counters | m, l | O, O_lr
+
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(-(-66400 // chunk))
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(65)
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
     assert lra.lra_attn_decode_default_split(1, 8, 1900) == 64

@@ -1,0 +1,144 @@
+"""GPU parity of lra_attn_prefill against the fp64 oracle (needs an MI355X and liblra.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_kv_cache_amd as lra
+import workloads as W
+from tests.gpu_util import check, dev, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(c: W.PrefillCase, agent=None):
+    s = c.shape
+    O = lra.lra_attn_prefill(dev(c.Q), c.L_P, dev(c.K), dev(c.V), dev(c.V_lr), dev(c.B),
+                             c.agent if agent is None else agent, s.scale)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_prefill(c: W.PrefillCase, agent=None, rows=None, heads=None):
+    L = c.L_P + c.L_C
+    return oracle.attn_prefill(c.Q.as_f64(), W.HostTensor(c.K.data[:L], c.K.dtype).as_f64(),
+                               W.HostTensor(c.V.data[:L], c.V.dtype).as_f64(),
+                               W.HostTensor(c.V_lr.data[:L], c.V_lr.dtype).as_f64(), c.B.as_f64(),
+                               c.agent if agent is None else agent, c.L_P, c.shape.scale, rows=rows, heads=heads)
+
+
+def test_llama_prefill_full_size_sampled_rows():
+    """L_P = 16,384 cached + L_C = 2,048 new queries over 18,432 keys (the timed launch); rows spanning
+    first/last query tiles, tile edges and the diagonal are checked for every head against the oracle."""
+    say("prefill llama 16384+2048: generating inputs")
+    c = W.llama_prefill()
+    say("prefill llama 16384+2048: running")
+    got = run_prefill(c)
+    rows = np.array([0, 1, 2, 15, 16, 31, 32, 33, 63, 64, 127, 128, 129, 511, 1000, 1023, 1024, 1500, 2015, 2046, 2047])
+    say("prefill llama 16384+2048: oracle on sampled rows")
+    ref = ref_prefill(c, rows=rows)
+    check(got[rows], ref, "bf16")
+
+
+@pytest.mark.parametrize("agent", [0, 1, 2])
+def test_prefill_every_agent(agent):
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill((300, agent), s, L_P=300, L_C=200, agent=agent)
+    say(f"prefill llama-shaped agent={agent}")
+    check(run_prefill(c), ref_prefill(c), "bf16")
+
+
+SHAPES = [
+    # dtype, n_q, n_kv, d, r, L_P, L_C
+    ("bf16", 32, 8, 128, 8, 0, 1), ("bf16", 32, 8, 128, 8, 0, 97), ("bf16", 32, 8, 128, 16, 63, 65),
+    ("bf16", 8, 2, 64, 8, 200, 130), ("bf16", 64, 8, 128, 8, 1, 33), ("bf16", 24, 8, 128, 16, 128, 40),
+    ("bf16", 8, 8, 64, 16, 64, 129), ("bf16", 40, 8, 64, 8, 17, 50), ("bf16", 7, 1, 128, 8, 5, 70),
+    ("f32", 4, 2, 64, 8, 192, 64), ("f32", 32, 8, 128, 16, 40, 37), ("f32", 16, 2, 128, 8, 0, 100),
+]
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d,r,L_P,L_C", SHAPES)
+def test_prefill_shapes(dtype, n_q, n_kv, d, r, L_P, L_C):
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype=dtype)
+    c = W.random_prefill((301, n_q, n_kv, d, r, L_P, L_C), s, L_P, L_C, agent=2)
+    say(f"prefill {dtype} n_q={n_q} n_kv={n_kv} d={d} r={r} L_P={L_P} L_C={L_C}")
+    check(run_prefill(c), ref_prefill(c), dtype, f"{dtype} {n_q}/{n_kv} d={d} r={r} L_P={L_P} L_C={L_C}")
+
+
+def test_prefill_never_reads_past_the_chunk():
+    """Cache rows after L_P + L_C hold NaN; the kernel must not read them."""
+    s = W.LLAMA_SHAPE
+    L_P, L_C = 150, 77
+    c = W.random_prefill((302,), s, L_P, L_C + 100, agent=1)
+    c = W.PrefillCase(s, W.HostTensor(c.Q.data[:L_C], c.Q.dtype), c.K, c.V, c.V_lr, c.B, L_P, L_C, 1)
+    tail = np.arange(L_P + L_C, L_P + L_C + 100)
+    for t in (c.K, c.V, c.V_lr):
+        W.fill_rows(t, tail, float("nan"))
+    say("prefill NaN past the chunk")
+    check(run_prefill(c), ref_prefill(c), "bf16")
+
+
+def test_prefill_mask_bombs():
+    """Keys just past a query's diagonal get huge scores and values: a mask leak shows as O ~ 1e4."""
+    s = W.LLAMA_SHAPE
+    L_P, L_C = 100, 300
+    c = W.random_prefill((303,), s, L_P, L_C, agent=0)
+    g = np.random.default_rng(3)
+    u = g.standard_normal(s.d_head).astype(np.float32)
+    u /= np.linalg.norm(u)
+    Q = c.Q.as_f32() * 0.1 + u[None, None, :] * 3.0
+    K = c.K.as_f32()
+    V = c.V.as_f32()
+    bombs = [L_P + 16 * k + 1 for k in range(0, L_C // 16)]
+    for j in bombs:
+        K[j] = 1e3 * u / np.sqrt(s.d_head) * 0.5 + 0.0 * K[j]
+        V[j] = 1e4
+    cc = W.PrefillCase(s, W.to_storage(Q, "bf16"), W.to_storage(K, "bf16"), W.to_storage(V, "bf16"), c.V_lr, c.B,
+                       L_P, L_C, 0)
+    say("prefill mask bombs")
+    ref = ref_prefill(cc)
+    got = run_prefill(cc)
+    # rows before the first bomb must stay O(1); rows after see one and saturate to it
+    assert np.abs(ref[0]).max() < 100 and np.abs(ref[-1]).max() > 1e3
+    check(got, ref, "bf16")
+
+
+def test_prefill_agent_signature_and_lr_isolation():
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill((304,), s, 64, 96, agent=0, b_std=1.0)
+    lr = c.V_lr.as_f32()
+    for k in range(3):
+        lr[:, k * s.rank:(k + 1) * s.rank] += 10.0 * k
+    B = np.concatenate([np.full((1, s.rank, s.d_kv), 0.5 * (k + 1), np.float32) for k in range(3)])
+    sig = W.PrefillCase(s, c.Q, c.K, c.V, W.to_storage(lr, "bf16"), W.to_storage(B, "bf16"), 64, 96, 0)
+    for a in range(3):
+        say(f"prefill agent signature agent={a}")
+        check(run_prefill(sig, agent=a), ref_prefill(sig, agent=a), "bf16", f"signature agent {a}")
+    zero = W.to_storage(np.zeros(c.V.shape, np.float32), "bf16")
+    iso = W.PrefillCase(s, c.Q, c.K, zero, c.V_lr, c.B, 64, 96, 2)
+    say("prefill LR isolation")
+    st = check(run_prefill(iso), ref_prefill(iso), "bf16")
+    assert st["normwise"] < 2e-2
+
+
+def test_prefill_is_deterministic():
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill((305,), s, 500, 300, agent=1)
+    assert np.array_equal(run_prefill(c), run_prefill(c))
+
+
+def test_prefill_value_beyond_fp16_range_gives_nan_rows_of_that_head_only():
+    """|V| above 65504 cannot enter the fp16 P.V product: the affected KV head's rows come out NaN,
+    every other head stays exact."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill((306,), s, 40, 60, agent=1)
+    V = c.V.as_f32()
+    V[10, 3, 7] = 1.0e5
+    cc = W.PrefillCase(s, c.Q, c.K, W.to_storage(V, "bf16"), c.V_lr, c.B, 40, 60, 1)
+    say("prefill fp16 range guard")
+    got = run_prefill(cc)
+    G = s.group
+    bad = list(range(3 * G, 4 * G))
+    good = [h for h in range(s.n_q) if h not in bad]
+    assert np.all(np.isnan(got[:, bad]))
+    check(got[:, good], ref_prefill(cc, heads=good), "bf16")

@@ -191,6 +191,20 @@ def bench_precompute(args, torch, lra, W, out):
     torch.cuda.empty_cache()
 
 
+def bench_copy(args, torch, lra, W, out):
+    """Device-to-device copy of 1 GiB: the achievable streaming bandwidth on this GPU (context for the
+    roofline fractions) and the reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_launches(lambda: dst.copy_(src), 20, 3, torch)
+    nb = 2 * n * 2
+    out["copy_1GiB"] = {"ms": round(ms, 4), "gbs": round(nb / (ms * 1e-3) / 1e9, 1), "bytes_read": n * 2,
+                        "bytes_written": n * 2}
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def bench_short_decode(args, torch, lra, W, out):
     """One request over 1,900 keys (7.8 MB): latency-bound; caches rotate over 64 copies."""
     c = W.llama_decode()
@@ -310,7 +324,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", nargs="*", default=None,
-                    choices=["decode", "prefill", "precompute", "short", "ministral", "cpu"])
+                    choices=["decode", "prefill", "precompute", "short", "ministral", "copy", "cpu"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -323,12 +337,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    only = set(args.only) if args.only is not None else {"decode", "prefill", "precompute", "short", "ministral", "cpu"}
+    only = set(args.only) if args.only is not None else {"decode", "prefill", "precompute", "short", "ministral", "copy",
+                                                          "cpu"}
     out = {}
     if "decode" in only or "cpu" in only:
         bench_long_decode(args, torch, lra, W, out)
     for name, fn in (("prefill", bench_prefill), ("precompute", bench_precompute), ("short", bench_short_decode),
-                     ("ministral", bench_ministral_step)):
+                     ("ministral", bench_ministral_step), ("copy", bench_copy)):
         if name in only:
             log(f"[bench] {name}")
             fn(args, torch, lra, W, out)

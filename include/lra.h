@@ -84,9 +84,9 @@ const char* lra_last_error(void);
  *          0 .. n_agents*rank-1 of the addressed rows are written
  * out_rows (device) [T] int64 destination row of each X row, or NULL for row t -> row t
  *          (then vlr_rows >= T is required)
- * workspace(device) scratch of lra_lr_precompute_workspace_bytes() bytes, 256-byte aligned.
- *          It must be zero-filled before its first use; every call leaves it zero-filled again.
- *          Calls that share one workspace must not overlap in time.
+ * workspace(device) scratch of lra_lr_precompute_workspace_bytes() bytes (0 when the reduction is
+ *          not split: then workspace may be NULL), 256-byte aligned; its contents need no
+ *          initialisation. Calls that share one workspace must be ordered (same stream).
  * T = 0 is allowed and enqueues nothing. d_model must be a multiple of 32; ld_vlr a multiple of 8.
  * Every tensor pointer must be 16-byte aligned.
  */
@@ -124,10 +124,10 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
- * Batched decode, one new query token per request, split along the key axis: each split writes a
- * partial (m, l, O, O_lr) in fp32 to the workspace, and the split that finishes last for its
- * (request, KV head) merges the partials with the log-sum-exp rule, applies B_agent once and
- * normalises (one kernel launch per call). Request b attends all rows
+ * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
+ * (3)-(4) with L_C = 1): each (request, KV head, split) writes a partial (m, l, O, O_lr) in fp32 to
+ * the workspace; a second kernel merges the partials of a (request, KV head) with the log-sum-exp
+ * rule, applies B_agent once and normalises. Request b attends all rows
  * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
  * kv_len[b] = 0 gives a zero output row.
  *
@@ -138,9 +138,8 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * max_kv_len (host) an upper bound on every kv_len[b]; it sizes the launch
  * B        (device) [n_agents x rank x n_kv*d_head]
  * keys_per_split  keys handled by one split (multiple of 64), or 0 for the library's choice
- * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned. It must be
- *          zero-filled before its first use; every call leaves it zero-filled again (only its
- *          arrival counters matter). Calls that share one workspace must not overlap in time.
+ * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
+ *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output
  * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues nothing.
  */

@@ -132,7 +132,7 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
                       stream=None) -> torch.Tensor:
     """V_lr[out_rows[t], :n_agents*rank] = X[t] @ A.T, with A = [A_1^T; ...; A_N^T] ([N*r, d_model]).
 
-    ``workspace`` (uint8, zero-filled before first use) is allocated zeroed when omitted."""
+    ``workspace`` (uint8, any contents) is allocated when omitted and the reduction is split."""
     _same(X, A, V_lr)
     _rows_dense("X", X)
     _dense("A", A)
@@ -145,7 +145,7 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
             raise ValueError("out_rows must be a contiguous int64 tensor with one entry per row of X")
     need = lra_lr_precompute_workspace_bytes(T, d_model, n_agents, rank)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lra_lr_precompute(_dtype_code(X), _ptr(X), T, d_model, X.stride(0), _ptr(A), n_agents, rank,
                                   _ptr(V_lr), V_lr.stride(0), V_lr.shape[0], _ptr(out_rows),
@@ -218,7 +218,7 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=Q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if O is None:
         O = torch.empty_like(Q)

@@ -39,14 +39,14 @@ struct DecodeLayout {
     size_t ml_off, o_off, total;
 };
 
-// [arrival counters: batch*n_kv uint32][m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], 256-aligned parts
-DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, int64_t max_kv_len, int chunk) {
+// [m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], recs = batch * n_q * n_split, 256-aligned parts
+DecodeLayout decode_layout(int batch, int n_q, int d_head, int rank, int64_t max_kv_len, int chunk) {
     DecodeLayout L{};
     L.chunk = chunk;
     L.n_split = max_kv_len > 0 ? int((max_kv_len + chunk - 1) / chunk) : 0;
     const size_t recs = size_t(batch) * size_t(n_q) * size_t(L.n_split);
-    L.ml_off = align_up(size_t(batch) * size_t(n_kv) * sizeof(uint32_t), 256);
-    L.o_off = L.ml_off + align_up(recs * 2 * sizeof(float), 256);
+    L.ml_off = 0;
+    L.o_off = align_up(recs * 2 * sizeof(float), 256);
     L.total = recs ? L.o_off + recs * size_t(d_head + rank) * sizeof(float) : 0;
     return L;
 }
@@ -88,8 +88,7 @@ LRA_EXPORT const char* lra_last_error(void) { return g_last_error.c_str(); }
 LRA_EXPORT size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, int32_t n_agents, int32_t rank) {
     if (T <= 0 || d_model <= 0 || n_agents <= 0 || rank <= 0) return 0;
     const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, n_agents * rank, true);
-    if (pl.ksplit <= 1) return 0;
-    return align_up(pl.count_bytes, 256) + pl.part_bytes;
+    return pl.part_bytes;
 }
 
 LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
@@ -113,12 +112,11 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
     const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, int(NR), dtype == LRA_BF16);
     lra::PrecomputeParams p{};
     if (pl.ksplit > 1) {
-        const size_t need = align_up(pl.count_bytes, 256) + pl.part_bytes;
+        const size_t need = pl.part_bytes;
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         if (workspace_bytes < need) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
-        p.ws_count = static_cast<uint32_t*>(workspace);
-        p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(pl.count_bytes, 256));
+        p.ws_part = static_cast<float*>(workspace);
     }
     p.X = X; p.A = A; p.Vlr = V_lr; p.out_rows = out_rows;
     p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_rows = vlr_rows;
@@ -164,7 +162,7 @@ LRA_EXPORT size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, in
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || max_kv_len <= 0 || d_head <= 0 || rank <= 0) return 0;
     if (keys_per_split < 0 || keys_per_split % 64 != 0) return 0;
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    return decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, chunk).total;
+    return decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk).total;
 }
 
 LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
@@ -192,7 +190,7 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, chunk);
+    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
     if (L.total) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -201,7 +199,6 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
     lra::DecodeParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B;
     p.kv_start = kv_start; p.kv_len = kv_len; p.agent = agent;
-    p.ws_count = static_cast<uint32_t*>(workspace);
     p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
@@ -214,13 +211,14 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
 namespace lra {
 
 int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len) {
-    // aim for about 8k (request, KV head, split) work items; splits are whole 256-key rounds of the
-    // 4 waves when they are long, single 64-key tiles when the whole job is small
+    // about 4k (request, KV head, split) workgroups (16 x 66,400 keys x 8 heads: flat within 2%
+    // from 1,280 to 4,096 keys per split on MI355X); splits are whole 128-key rounds of the 4 waves'
+    // 32-key tiles, between 128 and 8192 keys
     const int64_t work = int64_t(batch) * n_kv * max_kv_len;
-    int64_t chunk = (work + 8191) / 8192;
-    if (chunk <= 64) return 64;
-    chunk = (chunk + 255) / 256 * 256;
-    return int(chunk > 16384 ? 16384 : chunk);
+    int64_t chunk = (work + 4095) / 4096;
+    chunk = (chunk + 127) / 128 * 128;
+    if (chunk < 128) chunk = 128;
+    return int(chunk > 8192 ? 8192 : chunk);
 }
 
 }  // namespace lra

@@ -1,4 +1,4 @@
-// Flash-LoRA-Attention decode for gfx950: split along the key axis, then a log-sum-exp combine.
+// Flash-LoRA-Attention decode for gfx950: split along the key axis, merged by log-sum-exp.
 //
 // Method (LRAgent page, "method steps" (3)-(4)): stream key/value tiles, keep the online-softmax
 // statistics, accumulate the base output O and the rank-r output O_lr from the agent's LR cache,
@@ -7,20 +7,33 @@
 // d_head (LRAgent page, "core method" / "technical novelty": associativity moves the d_out-wide
 // product out of the key loop).
 //
-// One kernel, one workgroup per (request b, KV head g, key split s), 4 waves.
-//   * the G query heads of KV head g share every K/V/V_lr load (grouped-query attention)
-//   * S = Q K^T on the matrix cores: A operand = the G queries (rows padded to 16), B operand =
-//     16 keys, 8 contiguous d-elements per lane (128-bit loads)
-//   * online softmax per 64-key tile in the base-2 domain (log2(e) folded into the scale),
-//     row maxima/sums with DPP inside 16-lane rows
-//   * P.V_base and P.V_lr on the vector ALUs: lane (slot, c) owns d-columns c*VEC.. of one key out
-//     of every 4, with P broadcast through LDS; keys past the split end are clamped to a valid row
-//     (finite data) and get P = 0, so no row outside [kv_start, kv_start+kv_len) is ever read
-//   * the 4 waves merge their states in LDS and write one fp32 partial (m, l, O, O_lr) per query head
-//   * the split that arrives last for its (request, KV head) (release fence + arrival counter) merges
-//     the partials with weights 2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d:(g+1)*d]) / l
-//     once per query row, rounds to the output type and zeroes the counter for the next call.
-//     Empty requests get zeros and requests with an invalid range or agent get NaN (split 0 writes them).
+// One kernel, one workgroup per (request b, KV head g, key split s), 4 waves. Each wave streams
+// 32-key tiles (tiles w, w+4, ... of the split): the K registers of the next tile are refilled as
+// soon as the scores are computed and the V registers as soon as P.V is done, so one tile's loads
+// are always in flight behind the arithmetic. Everything per key runs on the matrix cores; the
+// vector ALUs only do the softmax and an in-register transpose.
+//   * S^T = K Q^T (16x16x32 steps): A = 16 keys x 8 d-elements (128-bit loads of K rows),
+//     B = the G query heads of the group as columns (columns >= G are zero). Lane (n, q) then
+//     holds the scores of head n for keys 4q..4q+3 of each 16-key half: the lane's 8 keys of the
+//     tile are key(q, e) = 16*(e/4) + 4q + e%4, e = 0..7.
+//   * O^T = V^T P^T: the same 8 keys are the reduction slots, so P never leaves the lane. Output
+//     row r of O^T tile t is d = VEC*r + t (VEC = d_head/16), which lets lane (n, q) fetch its V
+//     operand as one 128-bit load per key (V[key][VEC*n .. VEC*n+VEC-1]); an 8 x VEC transpose of
+//     16-bit values in registers (byte permutes) turns the 8 loaded rows into the VEC operands.
+//   * P enters the bf16 step as a hi + lo pair (two steps), so the product keeps ~16 bits of P.
+//   * O_lr^T = V_lr^T P^T on one more step: row n is column n of the agent's V_lr slice.
+//   * fp32 inputs run the same loads on 16x16x4 fp32 steps (one key per slot, no transpose).
+//   * keys past the split end are clamped to its last row (finite data) and get P = 0, so no row
+//     outside [kv_start, kv_start+kv_len) is read
+//   * the 4 waves merge their states in LDS and write one fp32 partial (m, l, O, O_lr) per head
+//   * a second kernel, one workgroup per (request, KV head), merges the partials with weights
+//     2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d..]) / l once per query row and rounds
+//     to the output type. Empty requests get zeros and requests with an invalid range or agent NaN.
+//     The kernel boundary orders the partial writes before the merge: a device-scope fence per
+//     workgroup (to let the last split merge in place) writes back and invalidates an XCD's L2,
+//     which cost more than the whole merge at thousands of splits.
+#include <type_traits>
+
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -30,30 +43,43 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-
-template <typename T, int D, int R, int GP>
-struct DecodeCfg {
-    static constexpr int VEC = D / 16;        // d-columns per lane in the P.V step
-    static constexpr int KCH = D / 32;        // 32-wide reduction chunks of Q.K
-    static constexpr int NU = 4;              // 16-key subtiles per wave tile
-    static constexpr int TK = 16 * NU;        // keys per wave tile
-    static constexpr int NP = GP * R / 16;    // O_lr elements per lane
-    static_assert(GP == 4 || GP == 8, "padded group");
-    static_assert(NP >= 2 && R % NP == 0, "O_lr lane split");
-};
+constexpr int kTile = 32;   // keys per wave tile
 
 __device__ __forceinline__ bool decode_request_ok(int64_t start, int32_t len, int32_t a, const DecodeParams& p) {
     return len >= 0 && int64_t(len) <= p.max_kv_len && start >= 0 && start + int64_t(len) <= p.kv_rows &&
            a >= 0 && a < p.n_agents;
 }
 
-template <typename T, int D, int R, int GP>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-    using C = DecodeCfg<T, D, R, GP>;
-    constexpr int VEC = C::VEC, KCH = C::KCH, NU = C::NU, TK = C::TK, NP = C::NP;
+// key of the tile held by lane group q in slot e
+__device__ __forceinline__ int tile_key(int q, int e) { return 16 * (e >> 2) + 4 * q + (e & 3); }
 
-    __shared__ float plds[kWaves][TK][16];          // probabilities of the current tile, per wave
-    __shared__ float red_o[kWaves][GP][D + R];      // per-wave O | O_lr after the slot reduction
+// One wave's loads of a 32-key tile: K (consumed by the scores) and V / V_lr (consumed by P.V) are
+// fetched in two groups so each group's registers are refilled as soon as they have been used.
+template <typename T, int D> struct DecodeTile {
+    static constexpr int VEC = D / 16;
+    static constexpr int KCH = D / 32;
+    Vec<T, 8> k[2][KCH];   // K rows 16u + n, d = 32i + 8q .. +7
+    Vec<T, VEC> v[8];      // V rows key(q, e), d = VEC*n .. +VEC-1
+    Vec<T, 8> lr;          // V_lr[key(q, e)][agent*R + n % R] in slot e
+};
+
+// A operand of O^T tile t from the 8 loaded V rows: slot e <- v[e][t] (16-bit transpose).
+template <int VEC>
+__device__ __forceinline__ Vec<bf16, 8> v_operand(const Vec<bf16, VEC> (&v)[8], int t) {
+    Vec<bf16, 8> a;
+    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) a.w[pp] = __builtin_amdgcn_perm(v[2 * pp + 1].w[t >> 1], v[2 * pp].w[t >> 1], sel);
+    return a;
+}
+
+template <typename T, int D, int R, int GP>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
+    using Tile = DecodeTile<T, D>;
+    constexpr int VEC = Tile::VEC, KCH = Tile::KCH;
+    static_assert(R <= 16 && GP <= 16, "one 16-wide matrix-core tile covers the rank and the group");
+
+    __shared__ float red_o[kWaves][GP][D + R];      // per-wave O | O_lr
     __shared__ float red_m[kWaves][GP], red_l[kWaves][GP];
 
     // XCD-aware order: workgroup w runs on XCD w % 8. All KV heads of one (request, split) get the
@@ -71,191 +97,195 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
     const int G = p.G;
-    const bool ok = decode_request_ok(start, len, a, p);
-    if (!ok || len == 0) {
-        // no key to attend: zeros for an empty range, NaN for an invalid request (split 0 writes them)
-        if (s == 0) {
-            T* Op = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * G) * D;
-            const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
-            for (int idx = threadIdx.x; idx < G * D; idx += kThreads) Op[idx] = fill;
-        }
-        return;
-    }
+    if (!decode_request_ok(start, len, a, p)) return;   // the combine writes zeros / NaN
     const int k0 = s * p.chunk;
     if (k0 >= len) return;                                   // splits past the request's end do nothing
     const int k1 = min(k0 + p.chunk, len);
-    const int ns = (len + p.chunk - 1) / p.chunk;            // live splits of this request
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int n = lane & 15;   // MFMA row/column; P.V column group
-    const int rg = lane >> 4;  // MFMA reduction group; P.V key slot
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;   // key row of K, head column of Q^T / P^T, O^T row
+    const int q = lane >> 4;   // reduction slot group
 
-    const T* __restrict__ Kp = static_cast<const T*>(p.K);
-    const T* __restrict__ Vp = static_cast<const T*>(p.V);
-    const T* __restrict__ Lp = static_cast<const T*>(p.Vlr);
+    // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
+    // offset per operand, so the loads use the scalar-base + vector-offset form.
+    const int64_t row_bytes = int64_t(p.n_kv) * D * sizeof(T);
+    const int64_t lr_bytes = p.ld_vlr * int64_t(sizeof(T));
+    const char* __restrict__ Kg = static_cast<const char*>(p.K) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
+    const char* __restrict__ Vg = static_cast<const char*>(p.V) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
+    const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(a) * R) * int64_t(sizeof(T));
     const T* __restrict__ Qp = static_cast<const T*>(p.Q);
-    const int64_t row_stride = int64_t(p.n_kv) * D;
+    const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
+    const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
+    const uint32_t l_lane = uint32_t(4 * q * lr_bytes + (n % R) * sizeof(T));
 
-    // queries of the group as the MFMA A operand (rows >= G are zero)
+    // the group's queries as the B operand (columns >= G are zero)
     Vec<T, 8> qf[KCH];
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-        if (n < G) qf[i].load(Qp + (int64_t(b) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * rg);
+        if (n < G) qf[i].load(Qp + (int64_t(b) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * q);
         else qf[i].zero();
     }
 
-    const int lr_p0 = n * NP;
-    const int h_lr = lr_p0 / R;   // head of this lane's O_lr elements
-    const int rr0 = lr_p0 % R;    // first rank column of them
-    const int64_t lr_col = int64_t(a) * R + rr0;
+    // Tile loads. A full tile addresses each operand as a wave-uniform base (scalar registers) plus
+    // one 32-bit lane offset. Only a split's last tile can run past k1: its rows are clamped to
+    // k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads into the same
+    // registers, so the choice is a uniform branch around address arithmetic only.
+    auto load_k = [&](Tile& t, int kt) {
+        const char* kb = Kg + int64_t(kt) * row_bytes;
+        if (kt + kTile <= k1) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < KCH; ++i)
+                    t.k[u][i].load(reinterpret_cast<const T*>(kb + 16 * u * row_bytes + k_lane) + 32 * i);
+        } else {
+            const int lim = k1 - 1 - kt;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t o = uint32_t(min(16 * u + n, lim) * row_bytes + 8 * q * sizeof(T));
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) t.k[u][i].load(reinterpret_cast<const T*>(kb + o) + 32 * i);
+            }
+        }
+    };
+    auto load_v = [&](Tile& t, int kt) {
+        const char* vb = Vg + int64_t(kt) * row_bytes;
+        const char* lb = Lg + int64_t(kt) * lr_bytes;
+        // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
+        // so no load sits behind a lane mask
+        uint32_t h[8];
+        if (kt + kTile <= k1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                t.v[e].load(reinterpret_cast<const T*>(vb + tile_key(0, e) * row_bytes + v_lane));
+                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + tile_key(0, e) * lr_bytes + l_lane);
+                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + tile_key(0, e) * lr_bytes + l_lane);
+            }
+        } else {
+            const int lim = k1 - 1 - kt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = min(tile_key(q, e), lim);
+                t.v[e].load(reinterpret_cast<const T*>(vb + uint32_t(key * row_bytes + VEC * n * sizeof(T))));
+                const uint32_t lo = uint32_t(key * lr_bytes + (n % R) * sizeof(T));
+                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + lo);
+                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + lo);
+            }
+        }
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
+        }
+    };
 
-    float m_run[4], l_run[4];
+    f32x4 acc[VEC];
+    f32x4 acc_lr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.f; }
-    float o[GP][VEC];
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
-    float olr[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) olr[i] = 0.f;
-
+    for (int t = 0; t < VEC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale * kLog2e;
 
-    for (int kt = k0 + wv * TK; kt < k1; kt += kWaves * TK) {
-        // ---- loads: K as MFMA B operands, V and V_lr in the P.V layout; rows past k1 clamp to k1-1
-        Vec<T, 8> kf[NU][KCH];
+    // One tile: scores, online softmax, P.V. With PREFETCH the K registers are refilled with the
+    // next tile as soon as the scores are done and the V registers as soon as P.V is done, so one
+    // tile's loads are always in flight behind the arithmetic.
+    auto tile_step = [&](Tile& t, int kt, auto prefetch) {
+        constexpr bool PREFETCH = decltype(prefetch)::value;
+        const int kn = kt + kWaves * kTile;
+        f32x4 sacc[2];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int kr = min(kt + 16 * u + n, k1 - 1);
-            const T* kp = Kp + (start + kr) * row_stride + int64_t(g) * D + 8 * rg;
+        for (int u = 0; u < 2; ++u) {
+            sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < KCH; ++i) kf[u][i].load(kp + 32 * i);
+            for (int i = 0; i < KCH; ++i) sacc[u] = mma16x16x32(t.k[u][i], qf[i], sacc[u]);
         }
-        Vec<T, VEC> vf[TK / 4];
-        Vec<T, NP> lf[TK / 4];
+        if constexpr (PREFETCH) load_k(t, kn);
+        float sc[8];
 #pragma unroll
-        for (int t = 0; t < TK / 4; ++t) {
-            const int64_t row = start + min(kt + 4 * t + rg, k1 - 1);
-            vf[t].load(Vp + row * row_stride + int64_t(g) * D + VEC * n);
-            lf[t].load(Lp + row * p.ld_vlr + lr_col);
+        for (int e = 0; e < 8; ++e) sc[e] = sacc[e >> 2][e & 3] * sl2;
+        if (!PREFETCH && kt + kTile > k1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (kt + tile_key(q, e) >= k1) sc[e] = -INFINITY;
         }
-
-        // ---- scores on the matrix cores: lane holds S[head 4*rg+j][key kt+16u+n]
-        float sc[NU][4];
+        float mx = sc[0];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // online softmax (base 2); key kt is live, so mnew is finite
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+        float pr[8], ls = 0.f;
 #pragma unroll
-            for (int i = 0; i < KCH; ++i) acc = mma16x16x32(qf[i], kf[u][i], acc);
-            const bool live = (kt + 16 * u + n) < k1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[u][j] = live ? acc[j] * sl2 : -INFINITY;
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = fast_exp2(sc[e] - mnew);
+            ls += pr[e];
         }
-
-        // ---- online softmax (base 2)
-        float alpha[4];
+        l_run = fmaf(l_run, alpha, ls);
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float mt = sc[0][j];
-#pragma unroll
-            for (int u = 1; u < NU; ++u) mt = fmaxf(mt, sc[u][j]);
-            mt = row16_max(mt);
-            const float mnew = fmaxf(m_run[j], mt);  // finite: key kt is live
-            alpha[j] = fast_exp2(m_run[j] - mnew);
-            float ls = 0.f;
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                sc[u][j] = fast_exp2(sc[u][j] - mnew);
-                ls += sc[u][j];
-            }
-            l_run[j] = alpha[j] * l_run[j] + ls;
-            m_run[j] = mnew;
+            for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
+            acc_lr *= alpha;
         }
-
-        wave_sync();
+        // O^T += V^T P^T, O_lr^T += V_lr^T P^T
+        if constexpr (sizeof(T) == 2) {
+            Vec<bf16, 8> phi, plo;
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-            *reinterpret_cast<float4*>(&plds[wv][16 * u + n][4 * rg]) = make_float4(sc[u][0], sc[u][1], sc[u][2], sc[u][3]);
-        wave_sync();
-
-        // ---- rescale the accumulators by 2^(m_old - m_new) of each head (wave-uniform values)
-        float ah[GP];
-        bool any = false;
-#pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            ah[h] = readlane_f(alpha[h & 3], 16 * (h >> 2));
-            any |= ah[h] != 1.f;
-        }
-        if (any) {
-            float alr = ah[0];
-#pragma unroll
-            for (int h = 1; h < GP; ++h) alr = (h_lr == h) ? ah[h] : alr;
-#pragma unroll
-            for (int h = 0; h < GP; ++h)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) o[h][e] *= ah[h];
-#pragma unroll
-            for (int i = 0; i < NP; ++i) olr[i] *= alr;
-        }
-
-        // ---- P.V_base and P.V_lr: slot rg takes keys 4t+rg
-#pragma unroll
-        for (int t = 0; t < TK / 4; ++t) {
-            const int kl = 4 * t + rg;
-            float ph[GP];
-            const float4 p0 = *reinterpret_cast<const float4*>(&plds[wv][kl][0]);
-            ph[0] = p0.x; ph[1] = p0.y; ph[2] = p0.z; ph[3] = p0.w;
-            if constexpr (GP == 8) {
-                const float4 p1 = *reinterpret_cast<const float4*>(&plds[wv][kl][4]);
-                ph[4] = p1.x; ph[5] = p1.y; ph[6] = p1.z; ph[7] = p1.w;
-            }
-            const float plr = plds[wv][kl][h_lr];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float v = vf[t].get(e);
-#pragma unroll
-                for (int h = 0; h < GP; ++h) o[h][e] = fmaf(ph[h], v, o[h][e]);
+            for (int qq = 0; qq < 4; ++qq) {
+                phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
+                plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
             }
 #pragma unroll
-            for (int i = 0; i < NP; ++i) olr[i] = fmaf(plr, lf[t].get(i), olr[i]);
+            for (int tt = 0; tt < VEC; ++tt) {
+                const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
+                acc[tt] = mma16x16x32(va, phi, acc[tt]);
+                acc[tt] = mma16x16x32(va, plo, acc[tt]);
+            }
+            acc_lr = mma16x16x32(t.lr, phi, acc_lr);
+            acc_lr = mma16x16x32(t.lr, plo, acc_lr);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                for (int tt = 0; tt < VEC; ++tt)
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
+                acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
+            }
+        }
+        if constexpr (PREFETCH) load_v(t, kn);
+    };
+
+    // the wave's tiles kt = k0 + 32*wv + 128*j, j < nt; only the last one can be partial
+    {
+        constexpr int step = kWaves * kTile;
+        const int kt0 = k0 + kTile * wv;
+        const int nt = kt0 < k1 ? (k1 - kt0 + step - 1) / step : 0;
+        if (nt > 0) {
+            Tile t;
+            load_k(t, kt0);
+            load_v(t, kt0);
+            int kt = kt0;
+            for (int j = 0; j + 1 < nt; ++j, kt += step) tile_step(t, kt, std::true_type{});
+            tile_step(t, kt, std::false_type{});
         }
     }
 
-    // ---- per-wave reduction: l over the 16 lanes of a row, O / O_lr over the 4 key slots
+    // ---- per-wave state to LDS: lane (n, q) holds O^T rows 4q+j (d = VEC*(4q+j) + t) of head n
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (n < G) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l_run[j] = row16_sum(l_run[j]);
+        for (int tt = 0; tt < VEC; ++tt)
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
+            for (int j = 0; j < 4; ++j) red_o[wv][n][VEC * (4 * q + j) + tt] = acc[tt][j];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            float v = o[h][e];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            o[h][e] = v;
-        }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        float v = olr[i];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        olr[i] = v;
-    }
-    if (rg == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) red_o[wv][h][VEC * n + e] = o[h][e];
-#pragma unroll
-        for (int i = 0; i < NP; ++i) red_o[wv][h_lr][D + rr0 + i] = olr[i];
-    }
-    if (n == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = 4 * rg + j;
-            if (h < GP) { red_m[wv][h] = m_run[j]; red_l[wv][h] = l_run[j]; }
+        for (int j = 0; j < 4; ++j)
+            if (4 * q + j < R) red_o[wv][n][D + 4 * q + j] = acc_lr[j];
+        if (q == 0) {
+            red_m[wv][n] = m_run;
+            red_l[wv][n] = l_run;
         }
     }
     __syncthreads();
@@ -268,73 +298,84 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         float M = red_m[0][h];
 #pragma unroll
         for (int v = 1; v < kWaves; ++v) M = fmaxf(M, red_m[v][h]);
-        float acc = 0.f, L = 0.f;
+        float accv = 0.f, L = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
             const float mv = red_m[v][h];
             const float wgt = (mv == -INFINITY) ? 0.f : fast_exp2(mv - M);
-            acc = fmaf(wgt, red_o[v][h][col], acc);
+            accv = fmaf(wgt, red_o[v][h][col], accv);
             L = fmaf(wgt, red_l[v][h], L);
         }
         const int64_t rec = (bh0 + h) * p.n_split + s;
-        p.ws_o[rec * (D + R) + col] = acc;
+        p.ws_o[rec * (D + R) + col] = accv;
         if (col == 0) {
             p.ws_ml[rec * 2 + 0] = M;
             p.ws_ml[rec * 2 + 1] = L;
         }
     }
+}
 
-    // ---- the last split of (b, g) to arrive merges all splits of the group's query heads
-    __shared__ int last_s;
-    __threadfence();
-    __syncthreads();
-    uint32_t* counter = p.ws_count + int64_t(b) * p.n_kv + g;
-    if (threadIdx.x == 0) last_s = atomicAdd(counter, 1u) == uint32_t(ns - 1);
-    __syncthreads();
-    if (!last_s) return;
-    __threadfence();
-
-    // per-head maximum and normaliser over the live splits (one wave per head)
+// Merge of the splits of one (request b, KV head g): weights 2^(m_s - max m) (log-sum-exp rule),
+// then the up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l once per query row, rounded
+// to the output type. Requests with no key get zeros; requests with an invalid range or agent NaN.
+template <typename T, int D, int R, int GP>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
+    __shared__ float o_s[GP][D + R];
+    __shared__ float m_s[GP], l_s[GP];
+    const int b = blockIdx.x / p.n_kv;
+    const int g = blockIdx.x - b * p.n_kv;
+    const int G = p.G;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b];
+    const int32_t a = p.agent[b];
+    const int64_t bh0 = int64_t(b) * p.n_q + int64_t(g) * G;
+    T* __restrict__ Op = static_cast<T*>(p.O);
+    const bool ok = decode_request_ok(start, len, a, p);
+    if (!ok || len == 0) {
+        const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
+        for (int idx = threadIdx.x; idx < G * D; idx += kThreads) Op[bh0 * D + idx] = fill;
+        return;
+    }
+    const int ns = (len + p.chunk - 1) / p.chunk;   // splits that hold a partial
+    // per-head maximum and normaliser over the splits (one wave per head)
     for (int h = wv; h < G; h += kWaves) {
-        const int64_t rec0 = (bh0 + h) * p.n_split;
+        const float* ml = p.ws_ml + (bh0 + h) * p.n_split * 2;
         float M = -INFINITY;
-        for (int sidx = lane; sidx < ns; sidx += 64) M = fmaxf(M, p.ws_ml[(rec0 + sidx) * 2]);
+        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
         float L = 0.f;
-        for (int sidx = lane; sidx < ns; sidx += 64) {
-            const float* ml = p.ws_ml + (rec0 + sidx) * 2;
-            L = fmaf(fast_exp2(ml[0] - M), ml[1], L);
-        }
+        for (int s = lane; s < ns; s += 64) L = fmaf(fast_exp2(ml[2 * s] - M), ml[2 * s + 1], L);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-        if (lane == 0) { red_m[0][h] = M; red_l[0][h] = L; }
+        if (lane == 0) { m_s[h] = M; l_s[h] = L; }
     }
     __syncthreads();
     // weighted sums of O | O_lr over the splits
     for (int idx = threadIdx.x; idx < G * (D + R); idx += kThreads) {
         const int h = idx / (D + R);
         const int col = idx - h * (D + R);
-        const int64_t rec0 = (bh0 + h) * p.n_split;
-        const float M = red_m[0][h];
+        const float* ml = p.ws_ml + (bh0 + h) * p.n_split * 2;
+        const float* po = p.ws_o + (bh0 + h) * p.n_split * (D + R) + col;
+        const float M = m_s[h];
         float acc = 0.f;
-        for (int sidx = 0; sidx < ns; ++sidx)
-            acc = fmaf(fast_exp2(p.ws_ml[(rec0 + sidx) * 2] - M), p.ws_o[(rec0 + sidx) * (D + R) + col], acc);
-        red_o[1][h][col] = acc;
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) acc = fmaf(fast_exp2(ml[2 * s] - M), po[int64_t(s) * (D + R)], acc);
+        o_s[h][col] = acc;
     }
     __syncthreads();
-    // up-projection once per query row: O += O_lr B_agent[:, g*D + col], then normalise and store
-    T* __restrict__ Op = static_cast<T*>(p.O);
-    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * row_stride + int64_t(g) * D;
+    // up-projection once per query row, normalise, store
+    const int64_t d_kv = int64_t(p.n_kv) * D;
+    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
         const int h = idx / D;
         const int col = idx - h * D;
-        float acc = red_o[1][h][col];
+        float acc = o_s[h][col];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) acc = fmaf(red_o[1][h][D + rr], to_f32<T>(Bp[int64_t(rr) * row_stride + col]), acc);
-        Op[(bh0 + h) * D + col] = from_f32<T>(acc / red_l[0][h]);
+        for (int rr = 0; rr < R; ++rr) acc = fmaf(o_s[h][D + rr], to_f32<T>(Bp[int64_t(rr) * d_kv + col]), acc);
+        Op[(bh0 + h) * D + col] = from_f32<T>(acc / l_s[h]);
     }
-    if (threadIdx.x == 0) *counter = 0u;
 }
 
 template <typename T, int D, int R, int GP>
@@ -342,7 +383,8 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     const int64_t bs = int64_t(p.batch) * p.n_split;
     const int64_t groups = (bs + 7) / 8;
     const int64_t n_wg = groups * 8 * p.n_kv;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+    if (n_wg > 0) hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, R, GP>), dim3(unsigned(p.batch * p.n_kv)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -18,7 +18,6 @@ struct DecodeParams {
     const int32_t* agent;
     float* ws_ml;   // [batch*n_q*n_split][2]: running max (base-2 units) and sum of each split
     float* ws_o;    // [batch*n_q*n_split][d_head + rank]: unnormalised O | O_lr of each split
-    uint32_t* ws_count;  // [batch*n_kv] arrival counters of the splits, zero between calls
     void* O;
     int64_t ld_vlr;
     int64_t kv_rows;
@@ -35,7 +34,6 @@ struct PrecomputeParams {
     void* Vlr;
     const int64_t* out_rows;
     float* ws_part;      // [ksplit][T][NR] fp32 partial products (ksplit > 1)
-    uint32_t* ws_count;  // [row tiles * column groups] arrival counters, zero between calls
     int64_t T;
     int64_t ldx;
     int64_t ld_vlr;
@@ -70,7 +68,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 // Host-side launch geometry shared by the workspace-size query and the launch itself.
 struct PrecomputePlan {
     int kr, ksplit, n_rt, n_cg;
-    size_t part_bytes, count_bytes;
+    size_t part_bytes;
 };
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);
 

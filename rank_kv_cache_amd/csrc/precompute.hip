@@ -9,11 +9,13 @@
 // the LoRA "A" weights), so both MFMA operands are contiguous 8-element runs along d_model:
 //   A operand: lane (row n, slot q) <- X[row][k + 8q .. +7]
 //   B operand: lane (col n, slot q) <- At[col][k + 8q .. +7]   (small, L2-resident)
-// Grid (16-row tiles, reduction splits, column groups of <= 64). The 4 waves of a workgroup take
-// interleaved 32-wide chunks of the workgroup's reduction range and are summed through LDS. With
-// several splits each workgroup stores an fp32 partial, release-fences and counts its arrival; the
-// last workgroup of a tile sums the partials in split order (deterministic), stores the rows and
-// zeroes the counter for the next call.
+// Grid (16-row tiles, reduction splits, column groups of <= 64); 8 waves per workgroup, each wave
+// takes a contiguous eighth of the workgroup's reduction range and issues its loads in batches of
+// 8 chunks (32 elements each) ahead of the multiplies, so the whole of X is in flight at once for
+// the workload sizes of a prefill chunk. The waves are summed through LDS. With one split the
+// workgroup writes the output rows; with several, each writes an fp32 partial and a second kernel
+// sums the partials in split order (deterministic), converts and stores the rows. No workgroup
+// waits on another: a device-scope fence per workgroup writes back and invalidates an XCD's L2.
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -22,55 +24,60 @@ namespace lra {
 namespace {
 
 constexpr int kRows = 16;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBatch = 8;   // 32-element chunks whose loads a wave issues before multiplying
 
 template <typename T, int NT>
-__global__ __launch_bounds__(256) void precompute_kernel(PrecomputeParams p) {
+__global__ __launch_bounds__(kThreads) void precompute_kernel(PrecomputeParams p) {
     constexpr int NRP = 16 * NT;
-    __shared__ float red[4][kRows][NRP + 1];
-    __shared__ int last_s;
+    __shared__ float red[kWaves][kRows][NRP + 1];
 
     const int rt = blockIdx.x, ks = blockIdx.y, cg = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, n = lane & 15, q = lane >> 4;
     const int c0 = cg * 64;
     const int ncol = min(p.NR - c0, NRP);
-    const int kb = ks * p.kr;
-    const int ke = min(kb + p.kr, p.d_model);
-    const int nkc = (ke - kb) / 32;
+    // this workgroup's chunks [kc0, kc1) of 32 reduction elements, and this wave's share of them
+    const int nkc_all = p.d_model / 32;
+    const int kc0 = ks * (p.kr / 32);
+    const int kc1 = min(kc0 + p.kr / 32, nkc_all);
+    const int per_wave = (kc1 - kc0 + kWaves - 1) / kWaves;
+    const int w0 = kc0 + wv * per_wave;
+    const int w1 = min(w0 + per_wave, kc1);
 
     const T* __restrict__ Xp = static_cast<const T*>(p.X);
     const T* __restrict__ Ap = static_cast<const T*>(p.A);
-
-    const int64_t xrow = int64_t(rt) * kRows + n;
-    const bool xrow_ok = xrow < p.T;
-    const T* xptr = Xp + (xrow_ok ? xrow : 0) * p.ldx + kb + 8 * q;
+    // rows past T and columns past ncol read a valid row / column; their outputs are never stored
+    const int64_t xrow = min<int64_t>(int64_t(rt) * kRows + n, p.T - 1);
+    const T* xptr = Xp + xrow * p.ldx + 8 * q;
     const T* aptr[NT];
-    bool acol_ok[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int c = 16 * nt + n;
-        acol_ok[nt] = c < ncol;
-        aptr[nt] = Ap + int64_t(c0 + (acol_ok[nt] ? c : 0)) * p.d_model + kb + 8 * q;
-    }
+    for (int nt = 0; nt < NT; ++nt) aptr[nt] = Ap + int64_t(c0 + min(16 * nt + n, ncol - 1)) * p.d_model + 8 * q;
 
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = wv; kc < nkc; kc += 4) {
-        Vec<T, 8> xf;
-        if (xrow_ok) xf.load(xptr + 32 * kc);
-        else xf.zero();
+    for (int b0 = w0; b0 < w1; b0 += kBatch) {
+        Vec<T, 8> xf[kBatch], af[kBatch][NT];
+        // chunks past w1 re-read chunk w1 - 1 and are multiplied by zero
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            Vec<T, 8> af;
-            if (acol_ok[nt]) af.load(aptr[nt] + 32 * kc);
-            else af.zero();
-            acc[nt] = mma16x16x32(xf, af, acc[nt]);
+        for (int u = 0; u < kBatch; ++u) {
+            const int kc = min(b0 + u, w1 - 1);
+            xf[u].load(xptr + 32 * kc);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) af[u][nt].load(aptr[nt] + 32 * kc);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (b0 + u >= w1) xf[u].zero();
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = mma16x16x32(xf[u], af[u][nt], acc[nt]);
         }
     }
 
-    // lane holds C[row 4q+j][col 16nt+n]; sum the 4 waves
+    // lane holds C[row 4q+j][col 16nt+n]; sum the waves
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -79,40 +86,32 @@ __global__ __launch_bounds__(256) void precompute_kernel(PrecomputeParams p) {
 
     const int64_t r0 = int64_t(rt) * kRows;
     const int nrows = int(min<int64_t>(kRows, p.T - r0));
-    T* __restrict__ Op = static_cast<T*>(p.Vlr);
-    if (p.ksplit == 1) {
-        for (int idx = tid; idx < nrows * ncol; idx += 256) {
-            const int rr = idx / ncol;
-            const int c = idx - rr * ncol;
-            const float v = red[0][rr][c] + red[1][rr][c] + red[2][rr][c] + red[3][rr][c];
+    for (int idx = tid; idx < nrows * ncol; idx += kThreads) {
+        const int rr = idx / ncol;
+        const int c = idx - rr * ncol;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += red[w][rr][c];
+        if (p.ksplit == 1) {
             const int64_t orow = p.out_rows ? p.out_rows[r0 + rr] : r0 + rr;
-            if (orow >= 0 && orow < p.vlr_rows) Op[orow * p.ld_vlr + c0 + c] = from_f32<T>(v);
+            if (orow >= 0 && orow < p.vlr_rows) static_cast<T*>(p.Vlr)[orow * p.ld_vlr + c0 + c] = from_f32<T>(v);
+        } else {
+            p.ws_part[(int64_t(ks) * p.T + r0 + rr) * p.NR + c0 + c] = v;
         }
-        return;
     }
+}
 
-    for (int idx = tid; idx < nrows * ncol; idx += 256) {
-        const int rr = idx / ncol;
-        const int c = idx - rr * ncol;
-        const float v = red[0][rr][c] + red[1][rr][c] + red[2][rr][c] + red[3][rr][c];
-        p.ws_part[(int64_t(ks) * p.T + r0 + rr) * p.NR + c0 + c] = v;
-    }
-    __threadfence();
-    __syncthreads();
-    uint32_t* counter = p.ws_count + int64_t(rt) * p.n_cg + cg;
-    if (tid == 0) last_s = atomicAdd(counter, 1u) == uint32_t(p.ksplit - 1);
-    __syncthreads();
-    if (!last_s) return;
-    __threadfence();
-    for (int idx = tid; idx < nrows * ncol; idx += 256) {
-        const int rr = idx / ncol;
-        const int c = idx - rr * ncol;
-        float sum = 0.f;
-        for (int k = 0; k < p.ksplit; ++k) sum += p.ws_part[(int64_t(k) * p.T + r0 + rr) * p.NR + c0 + c];
-        const int64_t orow = p.out_rows ? p.out_rows[r0 + rr] : r0 + rr;
-        if (orow >= 0 && orow < p.vlr_rows) Op[orow * p.ld_vlr + c0 + c] = from_f32<T>(sum);
-    }
-    if (tid == 0) *counter = 0u;
+// Sum of the split partials in split order, then the row store (with the optional row map).
+template <typename T>
+__global__ __launch_bounds__(256) void precompute_reduce_kernel(PrecomputeParams p) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= p.T * p.NR) return;
+    const int64_t t = idx / p.NR;
+    const int c = int(idx - t * p.NR);
+    float v = 0.f;
+    for (int k = 0; k < p.ksplit; ++k) v += p.ws_part[(int64_t(k) * p.T + t) * p.NR + c];
+    const int64_t orow = p.out_rows ? p.out_rows[t] : t;
+    if (orow >= 0 && orow < p.vlr_rows) static_cast<T*>(p.Vlr)[orow * p.ld_vlr + c] = from_f32<T>(v);
 }
 
 template <typename T>
@@ -121,10 +120,14 @@ hipError_t launch_t(const PrecomputeParams& p, hipStream_t stream) {
     const dim3 grid(n_rt, p.ksplit, p.n_cg);
     const int width = p.NR < 64 ? p.NR : 64;
     switch ((width + 15) / 16) {
-        case 1: hipLaunchKernelGGL((precompute_kernel<T, 1>), grid, dim3(256), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((precompute_kernel<T, 2>), grid, dim3(256), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((precompute_kernel<T, 3>), grid, dim3(256), 0, stream, p); break;
-        default: hipLaunchKernelGGL((precompute_kernel<T, 4>), grid, dim3(256), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((precompute_kernel<T, 1>), grid, dim3(kThreads), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((precompute_kernel<T, 2>), grid, dim3(kThreads), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((precompute_kernel<T, 3>), grid, dim3(kThreads), 0, stream, p); break;
+        default: hipLaunchKernelGGL((precompute_kernel<T, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    }
+    if (p.ksplit > 1) {
+        const int64_t n = p.T * p.NR;
+        hipLaunchKernelGGL((precompute_reduce_kernel<T>), dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -132,19 +135,16 @@ hipError_t launch_t(const PrecomputeParams& p, hipStream_t stream) {
 }  // namespace
 
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool /*bf16*/) {
+    // split the reduction only when there are too few row tiles to spread over the chip, and never
+    // below 256 elements per workgroup (32 per wave)
     PrecomputePlan pl{};
     pl.n_rt = int((T + kRows - 1) / kRows);
     pl.n_cg = (NR + 63) / 64;
     const int64_t tiles = int64_t(pl.n_rt) * pl.n_cg;
     int ks = 1;
-    for (;;) {
-        const int kr = ((d_model + ks - 1) / ks + 31) / 32 * 32;
-        if (tiles * ks >= 256 || kr <= 128 || ks >= 32) break;
-        ks *= 2;
-    }
+    while (tiles * ks < 128 && d_model / (2 * ks) >= 256 && ks < 64) ks *= 2;
     pl.kr = ((d_model + ks - 1) / ks + 31) / 32 * 32;
     pl.ksplit = (d_model + pl.kr - 1) / pl.kr;
-    pl.count_bytes = size_t(tiles) * sizeof(uint32_t);
     pl.part_bytes = pl.ksplit > 1 ? size_t(pl.ksplit) * size_t(T) * size_t(NR) * sizeof(float) : 0;
     return pl;
 }

@@ -86,13 +86,14 @@ def test_decode_workspace_size_follows_split():
 
     def layout(n_split):
         recs = b * n_q * n_split
-        return up(b * 8 * 4) + up(recs * 2 * 4) + recs * (d + r) * 4   # counters | m, l | O, O_lr
+        return up(recs * 2 * 4) + recs * (d + r) * 4   # m, l | O, O_lr
 
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(-(-66400 // chunk))
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(65)
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
-    assert lra.lra_attn_decode_default_split(1, 8, 1900) == 64
+    assert lra.lra_attn_decode_default_split(1, 8, 1900) == 128
+    assert chunk % 128 == 0 and 128 <= chunk <= 8192
 
 
 # ---------------------------------------------------------------------------------------- prefill
@@ -134,7 +135,7 @@ def precompute(**kw):
     (dict(T=-1), E_SHAPE), (dict(ldx=4095), E_SHAPE), (dict(ldx=4092), E_SHAPE), (dict(ld_vlr=20), E_SHAPE),
     (dict(vlr_rows=100), E_SHAPE), (dict(vlr_rows=-1, out_rows=P), E_SHAPE), (dict(n_agents=0), E_SHAPE),
     (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(Vlr=P + 4), E_SHAPE),
-    (dict(ws=None), E_WS), (dict(ws_bytes=100), E_WS), (dict(ws=WS + 16), E_WS),
+    (dict(T=32, ws=None), E_WS), (dict(T=32, ws_bytes=100), E_WS), (dict(T=32, ws=WS + 16), E_WS),
 ])
 def test_precompute_rejects_bad_arguments(kw, status):
     assert precompute(**kw) == status
@@ -145,9 +146,9 @@ def test_precompute_empty_is_a_no_op():
 
 
 def test_precompute_workspace_sizes():
-    # large T: 128 row tiles x 2 reduction splits; tiny T: many splits, counters + partials
-    ws = lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8)
-    assert ws == 512 + 2 * 2048 * 24 * 4      # 128 counters (512 B) + 2 partial planes
-    ws5 = lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16)
-    assert ws5 == 256 + 32 * 32 * 48 * 4      # 2 counters padded to 256 B + 32 partial planes
+    # enough row tiles (2048 rows = 128 tiles): no split, no workspace; 32 rows: the reduction is
+    # split 16 ways (256 elements each) and the fp32 partials need 16 planes of 32 x 48
+    assert lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8) == 0
+    assert lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16) == 16 * 32 * 48 * 4
+    assert lra.lra_lr_precompute_workspace_bytes(1, 256, 3, 8) == 0
     assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0

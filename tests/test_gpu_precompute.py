@@ -61,7 +61,7 @@ def test_precompute_shapes(dtype, T, d_model, N, r):
 
 
 def test_precompute_workspace_reuse_and_bad_rows():
-    """One workspace for several calls of different sizes (the arrival counters must come back to zero);
+    """One workspace (split reduction partials) for several calls of different sizes in a row;
     out_rows entries outside the cache are skipped."""
     s = W.MINISTRAL_SHAPE
     ws = torch.zeros(lra.lra_lr_precompute_workspace_bytes(64, 4096, 3, 16), dtype=torch.uint8, device="cuda")
@@ -75,7 +75,6 @@ def test_precompute_workspace_reuse_and_bad_rows():
         got = run_pre(case, cache, rows, ws)
         ref = oracle.lr_precompute_into(cache, case.X.as_f64()[1:-1], case.A.as_f64(), rows[1:-1])
         check(got, ref, "bf16")
-    assert int(ws[:256].sum()) == 0
 
 
 def test_precompute_is_deterministic():

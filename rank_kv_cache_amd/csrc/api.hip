@@ -211,11 +211,12 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
 namespace lra {
 
 int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len) {
-    // about 4k (request, KV head, split) workgroups (16 x 66,400 keys x 8 heads: flat within 2%
-    // from 1,280 to 4,096 keys per split on MI355X); splits are whole 128-key rounds of the 4 waves'
-    // 32-key tiles, between 128 and 8192 keys
+    // about 8k (request, KV head, split) workgroups for batch x max_kv_len keys. On MI355X the 16 x
+    // 66,400-key batch is flat within 2% from 1,152 to 4,096 keys per split; batches of mixed
+    // lengths (fewer live splits than the grid) keep their balance only with the smaller splits.
+    // Splits are whole 128-key rounds of the 4 waves' 32-key tiles, between 128 and 8192 keys.
     const int64_t work = int64_t(batch) * n_kv * max_kv_len;
-    int64_t chunk = (work + 4095) / 4096;
+    int64_t chunk = (work + 8191) / 8192;
     chunk = (chunk + 127) / 128 * 128;
     if (chunk < 128) chunk = 128;
     return int(chunk > 8192 ? 8192 : chunk);

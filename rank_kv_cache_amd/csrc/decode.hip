@@ -26,7 +26,7 @@
 //   * keys past the split end are clamped to its last row (finite data) and get P = 0, so no row
 //     outside [kv_start, kv_start+kv_len) is read
 //   * the 4 waves merge their states in LDS and write one fp32 partial (m, l, O, O_lr) per head
-//   * a second kernel, one workgroup per (request, KV head), merges the partials with weights
+//   * a second kernel, one workgroup per (request, query head), merges the partials with weights
 //     2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d..]) / l once per query row and rounds
 //     to the output type. Empty requests get zeros and requests with an invalid range or agent NaN.
 //     The kernel boundary orders the partial writes before the merge: a device-scope fence per
@@ -315,66 +315,73 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     }
 }
 
-// Merge of the splits of one (request b, KV head g): weights 2^(m_s - max m) (log-sum-exp rule),
-// then the up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l once per query row, rounded
-// to the output type. Requests with no key get zeros; requests with an invalid range or agent NaN.
-template <typename T, int D, int R, int GP>
+// Merge of the splits of one (request b, query head h): weights 2^(m_s - max m) (log-sum-exp rule),
+// then the up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l, rounded to the output type.
+// Wave w sums the splits s = w, w+4, ...; lane c holds columns c, c+64, c+128 of O | O_lr, so every
+// lane has several independent loads in flight. Requests with no key get zeros; requests with an
+// invalid range or agent NaN.
+template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
-    __shared__ float o_s[GP][D + R];
-    __shared__ float m_s[GP], l_s[GP];
-    const int b = blockIdx.x / p.n_kv;
-    const int g = blockIdx.x - b * p.n_kv;
-    const int G = p.G;
+    constexpr int W = D + R;
+    constexpr int NC = (W + 63) / 64;
+    __shared__ float part[kWaves][NC * 64];
+    __shared__ float ml_s[2];
+    const int b = blockIdx.x / p.n_q;
+    const int h = blockIdx.x - b * p.n_q;
+    const int g = h / p.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t start = p.kv_start[b];
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
-    const int64_t bh0 = int64_t(b) * p.n_q + int64_t(g) * G;
-    T* __restrict__ Op = static_cast<T*>(p.O);
+    const int64_t bh = int64_t(b) * p.n_q + h;
+    T* __restrict__ Op = static_cast<T*>(p.O) + bh * D;
     const bool ok = decode_request_ok(start, len, a, p);
     if (!ok || len == 0) {
         const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
-        for (int idx = threadIdx.x; idx < G * D; idx += kThreads) Op[bh0 * D + idx] = fill;
+        for (int c = threadIdx.x; c < D; c += kThreads) Op[c] = fill;
         return;
     }
     const int ns = (len + p.chunk - 1) / p.chunk;   // splits that hold a partial
-    // per-head maximum and normaliser over the splits (one wave per head)
-    for (int h = wv; h < G; h += kWaves) {
-        const float* ml = p.ws_ml + (bh0 + h) * p.n_split * 2;
-        float M = -INFINITY;
-        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+    const float* ml = p.ws_ml + bh * p.n_split * 2;
+    const float* po = p.ws_o + bh * p.n_split * W;
+    // maximum over the splits (every wave computes it; the partials are few)
+    float M = -INFINITY;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        float L = 0.f;
-        for (int s = lane; s < ns; s += 64) L = fmaf(fast_exp2(ml[2 * s] - M), ml[2 * s + 1], L);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    // this wave's splits: weighted O | O_lr columns and the weighted normaliser
+    float acc[NC];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-        if (lane == 0) { m_s[h] = M; l_s[h] = L; }
+    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+    float L = 0.f;
+#pragma unroll 4
+    for (int s = wv; s < ns; s += kWaves) {
+        const float wgt = fast_exp2(ml[2 * s] - M);
+        L = fmaf(wgt, ml[2 * s + 1], L);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (64 * c + lane < W) acc[c] = fmaf(wgt, po[int64_t(s) * W + 64 * c + lane], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) part[wv][64 * c + lane] = acc[c];
+    if (lane == 0) part[wv][NC * 64 - 1] = L;   // column NC*64-1 >= W is free
+    __syncthreads();
+    if (threadIdx.x < 64 * NC) {
+        const int c = threadIdx.x;
+        part[0][c] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
     }
     __syncthreads();
-    // weighted sums of O | O_lr over the splits
-    for (int idx = threadIdx.x; idx < G * (D + R); idx += kThreads) {
-        const int h = idx / (D + R);
-        const int col = idx - h * (D + R);
-        const float* ml = p.ws_ml + (bh0 + h) * p.n_split * 2;
-        const float* po = p.ws_o + (bh0 + h) * p.n_split * (D + R) + col;
-        const float M = m_s[h];
-        float acc = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) acc = fmaf(fast_exp2(ml[2 * s] - M), po[int64_t(s) * (D + R)], acc);
-        o_s[h][col] = acc;
-    }
+    if (threadIdx.x == 0) ml_s[0] = part[0][NC * 64 - 1];
     __syncthreads();
     // up-projection once per query row, normalise, store
     const int64_t d_kv = int64_t(p.n_kv) * D;
     const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int h = idx / D;
-        const int col = idx - h * D;
-        float acc = o_s[h][col];
+    const float inv = 1.f / ml_s[0];
+    for (int c = threadIdx.x; c < D; c += kThreads) {
+        float o = part[0][c];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) acc = fmaf(o_s[h][D + rr], to_f32<T>(Bp[int64_t(rr) * d_kv + col]), acc);
-        Op[(bh0 + h) * D + col] = from_f32<T>(acc / l_s[h]);
+        for (int rr = 0; rr < R; ++rr) o = fmaf(part[0][D + rr], to_f32<T>(Bp[int64_t(rr) * d_kv + c]), o);
+        Op[c] = from_f32<T>(o * inv);
     }
 }
 
@@ -384,7 +391,7 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     const int64_t groups = (bs + 7) / 8;
     const int64_t n_wg = groups * 8 * p.n_kv;
     if (n_wg > 0) hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, R, GP>), dim3(unsigned(p.batch * p.n_kv)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, R>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

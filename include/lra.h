@@ -22,6 +22,7 @@
  *  - All tensors are dense and row-major; one element type (`dtype`) per call:
  *    LRA_F32 (IEEE float) or LRA_BF16 (bfloat16 bits). Accumulation is fp32;
  *    bf16 outputs are rounded to nearest, ties to even.
+ *  - The softmax scale must be positive and finite (the workloads use 1/sqrt(d_head)).
  *  - Scalar arguments are validated on the host before anything is enqueued;
  *    a failing call enqueues nothing and returns a negative lra_status.
  *    lra_last_error() gives a message for the calling thread's last failure.

@@ -139,7 +139,7 @@ LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L
     if (agent < 0 || agent >= n_agents) return fail(LRA_ERR_INDEX, "agent=%d outside [0, %d)", agent, n_agents);
     if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
-    if (!std::isfinite(scale)) return fail(LRA_ERR_SHAPE, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
     if (L_C == 0) return LRA_OK;
     if (!Q || !K_base || !V_base || !V_lr || !B || !O) return fail(LRA_ERR_NULL, "Q, K_base, V_base, V_lr, B and O must not be NULL");
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
@@ -183,7 +183,7 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
     if (keys_per_split < 0 || keys_per_split % 64 != 0)
         return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
-    if (!std::isfinite(scale)) return fail(LRA_ERR_SHAPE, "scale must be finite");
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
     if (batch == 0) return LRA_OK;
     if (!Q || !K_base || !V_base || !V_lr || !B || !O || !kv_start || !kv_len || !agent)
         return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");

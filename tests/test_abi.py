@@ -64,7 +64,7 @@ def decode(**kw):
     (dict(n_q=30, n_kv=8), E_SHAPE), (dict(n_kv=0), E_SHAPE), (dict(batch=-1), E_SHAPE),
     (dict(ld_vlr=16), E_SHAPE), (dict(ld_vlr=28), E_SHAPE), (dict(split=100), E_SHAPE), (dict(split=-64), E_SHAPE),
     (dict(max_kv_len=-1), E_SHAPE), (dict(kv_rows=-5), E_SHAPE), (dict(n_agents=0), E_SHAPE),
-    (dict(scale=float("nan")), E_SHAPE), (dict(Q=None), E_NULL), (dict(kv_len=None), E_NULL),
+    (dict(scale=float("nan")), E_SHAPE), (dict(scale=0.0), E_SHAPE), (dict(scale=-0.1), E_SHAPE), (dict(Q=None), E_NULL), (dict(kv_len=None), E_NULL),
     (dict(agent=None), E_NULL), (dict(O=None), E_NULL), (dict(K=P + 8), E_SHAPE),
     (dict(ws=None), E_WS), (dict(ws=WS + 64), E_WS), (dict(ws_bytes=16), E_WS),
     (dict(max_kv_len=1 << 31), E_SHAPE),
@@ -110,6 +110,7 @@ def prefill(**kw):
     (dict(dtype=-1), E_UNSUP), (dict(d=32), E_UNSUP), (dict(r=32), E_UNSUP), (dict(n_q=3), E_SHAPE),
     (dict(L_C=-1), E_SHAPE), (dict(L_P=-1), E_SHAPE), (dict(L_P=1 << 31), E_SHAPE), (dict(agent=3), E_INDEX),
     (dict(agent=-1), E_INDEX), (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=float("inf")), E_SHAPE),
+    (dict(scale=0.0), E_SHAPE), (dict(scale=-1.0), E_SHAPE),
     (dict(B=None), E_NULL), (dict(Vlr=None), E_NULL), (dict(O=P + 2), E_SHAPE),
 ])
 def test_prefill_rejects_bad_arguments(kw, status):

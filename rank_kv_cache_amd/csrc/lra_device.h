@@ -151,6 +151,28 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<0x128>(v);
     return v;
 }
+// max over lanes l and l ^ 16 / l ^ 32 on the VALU (gfx950 permlane swaps: no LDS round trip).
+// A swap with both operands = x leaves (x_l, x_partner) in the result pair, in some order.
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// LDS transpose read of 16-bit elements (gfx950). Within each group of 16 lanes, let M[j] be the
+// four consecutive elements at lane j's address; lane i receives M[i/4 + 4k][i%4] in element k.
+// Pointing lane j at row key(j/4), columns c0 + 4*(j%4) .. +3 of a row-major [key][col] tile gives
+// lane i the column c0 + i of rows key(0..3): four reduction slots of a matrix-core operand.
+typedef short lds_s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+    const lds_s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) lds_s16x4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

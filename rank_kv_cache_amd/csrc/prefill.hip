@@ -9,27 +9,29 @@
 //
 // gfx950 mapping (16x16x32 matrix-core steps, fp32 accumulation; fp32 inputs run the same template
 // on 16x16x4 fp32 steps):
-//   * one workgroup = 4 waves = 256 "query rows" of one KV head; a query row is one (query, head)
-//     pair of that head's group, so all G heads of a group share every K/V tile (grouped-query).
-//     Each wave owns 4 tiles of 16 rows; their queries stay in registers as MFMA B operands.
+//   * one workgroup = 8 waves (two per SIMD, so one wave's softmax overlaps the other's matrix-core
+//     work) = 256 "query rows" of one KV head; a query row is one (query, head) pair of the head's
+//     group, so all G heads of a group share every K/V tile (grouped-query). Each wave owns 2 tiles
+//     of 16 rows; their queries stay in registers as MFMA B operands.
 //   * 64-key tiles are staged in LDS in their natural row layout with 128-bit stores, double
 //     buffered: the next tile's global loads are in flight while the current one is multiplied,
-//     one barrier per tile.
-//   * S^T = K Q^T: A operand = 16 keys x 8 d-elements of the K tile; output lane (r, n) holds keys
-//     4r..4r+3 of each 16-key group for query row n. Two groups give the lane the 8 keys it feeds
-//     as the B operand of O^T = V^T P^T, so P never leaves the lane.
-//   * V^T operand: row s of O^T tile t is d = NDT*s + t (NDT = d_head/16 tiles), so a lane reads
-//     its 8 keys' V[key][NDT*n .. NDT*n+NDT-1] as one LDS load each and an 8 x NDT 16-bit transpose
-//     in registers (byte permutes) yields the NDT operands, shared by the wave's 4 row tiles.
+//     one barrier per tile. The tile is consumed in two 32-key blocks.
+//   * S^T = K Q^T: A operand = 16 keys x 8 d-elements of the K tile; output lane (q, n) holds keys
+//     4q..4q+3 of each 16-key group for query row n. The two groups of a block give the lane the 8
+//     keys it feeds as the B operand of O^T = V^T P^T, so P never leaves the lane.
+//   * V^T operand: LDS transpose reads (ds_read_b64_tr_b16) turn the row-major V tile into the
+//     operand directly: two per 16-d tile give lane n column d0+n of the lane group's 8 keys.
 //   * bf16 inputs: Q.K runs on bf16 steps; P.V on fp16 steps, with V and V_lr converted bf16 ->
 //     fp16 once while they are staged (exact for |v| <= 65504) and P rounded to fp16. A workgroup
 //     that meets a value beyond the fp16 range writes NaN for its rows.
-//   * one more 16-row tile of V^T holds the agent's V_lr slice (rows 0..r-1) and a row of ones:
+//   * one more 16-column tile holds the agent's V_lr slice (columns 0..r-1) and a column of ones:
 //     O_lr^T and the softmax normaliser l come out of the same matrix-core product as O (l is the
-//     sum of exactly the rounded P the products used). For r = 16 the ones row is a second tile.
+//     sum of exactly the rounded P the products used). For r = 16 the ones column is a second tile.
 //   * online softmax per query row and 32-key block in base 2, scale*log2(e) folded into one fma
-//     per score; the row max is reduced over the 4 lanes sharing a row
-//   * epilogue: gather O_lr of the row across its 4 lanes, add O_lr B_agent (B slice in LDS),
+//     per score; the row max is reduced over the 4 lanes sharing a row with permlane swaps. The
+//     reference max m only moves (and O, O_lr, l are rescaled) when a row's block max exceeds it by
+//     more than a factor 2^8 in P; otherwise P may reach 2^8, well inside fp16.
+//   * epilogue: gather O_lr and l of the row across its 4 lanes, add O_lr B_agent (B slice in LDS),
 //     divide by l, store in the input type (bf16 round-to-nearest-even)
 #include <type_traits>
 
@@ -40,11 +42,12 @@ namespace lra {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMT = 4;                          // 16-row tiles per wave
+constexpr int kMT = 2;                          // 16-row tiles per wave
 constexpr int kRowsPerWG = 16 * kMT * kWaves;   // 256 query rows
-constexpr int kBK = 64;                         // keys per tile
+constexpr int kBK = 64;                         // keys per LDS tile
+constexpr float kRescaleLog2 = 8.f;             // m moves when P would exceed 2^8
 
 template <typename T> struct PrefillTypes {
     // element type of the P.V operands in LDS: fp16 bits for bf16 inputs, fp32 for fp32 inputs
@@ -56,35 +59,33 @@ template <typename T> struct PrefillTypes {
 template <typename T, int D, int R>
 struct PrefillShared {
     using TV = typename PrefillTypes<T>::TV;
-    static constexpr int LDK = D + 16 / sizeof(T);    // K row (elements), padded by 16 bytes
-    static constexpr int LDV = D + 16 / sizeof(TV);   // V row
-    static constexpr int NAUX = R < 16 ? 1 : 2;       // V_lr + ones tiles
-    static constexpr int LDA = kBK + 16 / sizeof(TV); // aux row (keys)
+    static constexpr int NAUX = R < 16 ? 1 : 2;        // V_lr + ones tiles
+    static constexpr int LDK = D + 16 / sizeof(T);     // K row (elements), padded by 16 bytes
+    static constexpr int LDV = D + 16 / sizeof(TV);    // V row
+    static constexpr int LDX = 16 * NAUX;              // aux row: V_lr columns, then the ones column
     T k[2][kBK * LDK];
     TV v[2][kBK * LDV];
-    TV aux[2][NAUX * 16 * LDA];   // [tile row][key]: rows < R = V_lr columns, row R (or 16) = ones
-    float b[R * D];               // B_agent[:, g*D .. g*D+D-1]
+    TV aux[2][kBK * LDX];
+    float b[R * D];   // B_agent[:, g*D .. g*D+D-1]
     int range_bad;
 };
-
-// fp32 -> fp16 bits (round to nearest even) of two values
-__device__ __forceinline__ uint32_t h2(float lo, float hi) { return pack_f16x2(lo, hi); }
 
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     using TV = typename PrefillTypes<T>::TV;
     using PF = typename PrefillTypes<T>::PF;
     using SH = PrefillShared<T, D, R>;
-    constexpr int KCH = D / 32;           // Q.K reduction chunks
-    constexpr int NKB = kBK / 32;         // 32-key blocks of P.V
-    constexpr int NDT = D / 16;           // O^T tiles of 16 d-rows (d = NDT*s + t)
+    constexpr int KCH = D / 32;      // Q.K reduction chunks
+    constexpr int NKB = kBK / 32;    // 32-key blocks of a tile
+    constexpr int NDT = D / 16;      // O^T tiles: tile t holds d = 16t .. 16t+15
     constexpr int NAUX = SH::NAUX;
-    constexpr int LDK = SH::LDK, LDV = SH::LDV, LDA = SH::LDA;
+    constexpr int LDK = SH::LDK, LDV = SH::LDV, LDX = SH::LDX;
     constexpr int MT = kMT;
-    constexpr int KF = kBK * D / 8 / kThreads;      // 8-element fragments per thread of K (and of V)
+    constexpr int KF = kBK * D / 8 / kThreads;   // 8-element fragments per thread of K (and of V)
     static_assert(KF >= 1 && kBK * D / 8 % kThreads == 0, "tile split");
-    constexpr int LF = kBK * R / 8;                 // 8-element fragments of the V_lr tile
+    constexpr int LF = kBK * R / 8;              // 8-element fragments of the V_lr tile
     static_assert(LF <= kThreads, "V_lr tile split");
+    constexpr int LROW = R < 16 ? R : 16;        // aux column holding the ones (l)
 
     __shared__ __align__(16) SH sh;
 
@@ -128,46 +129,63 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // ---- key range of the workgroup
     const int64_t i_min = R0 / G;
     const int64_t i_max = min<int64_t>(p.L_C - 1, (R0 + kRowsPerWG - 1) / G);
-    const int64_t kv_end = p.L_P + i_max + 1;     // keys [0, kv_end) are visible to some row
-    const int64_t full_end = p.L_P + i_min + 1;   // keys [0, full_end) are visible to every row
-    const int n_tiles = int((kv_end + kBK - 1) / kBK);
+    const int kv_end = int(p.L_P + i_max + 1);     // keys [0, kv_end) are visible to some row
+    const int full_end = int(p.L_P + i_min + 1);   // keys [0, full_end) are visible to every row
+    const int n_tiles = (kv_end + kBK - 1) / kBK;
 
-    // ---- constants in LDS: B_agent slice (fp32), the ones / zero rows of the aux tiles
+    // ---- constants in LDS: B_agent slice (fp32), the ones / zero columns of the aux tiles
     for (int idx = tid; idx < R * D; idx += kThreads) {
         const int rr = idx / D, c = idx - rr * D;
         sh.b[idx] = to_f32<T>(Bp[(int64_t(p.agent) * R + rr) * kv_stride + int64_t(g) * D + c]);
     }
-    for (int idx = tid; idx < 2 * (NAUX * 16 - R) * LDA; idx += kThreads) {
-        const int buf = idx / ((NAUX * 16 - R) * LDA);
-        const int rem = idx - buf * ((NAUX * 16 - R) * LDA);
-        const int row = R + rem / LDA;
-        float v = row == (R < 16 ? R : 16) ? 1.f : 0.f;
+    for (int idx = tid; idx < 2 * kBK * (LDX - R); idx += kThreads) {
+        const int buf = idx / (kBK * (LDX - R));
+        const int rem = idx - buf * (kBK * (LDX - R));
+        const int key = rem / (LDX - R);
+        const int col = R + rem % (LDX - R);
+        const float v = col == LROW ? 1.f : 0.f;
         TV tv;
-        if constexpr (sizeof(T) == 2) tv = TV(h2(v, 0.f) & 0xffffu);
+        if constexpr (sizeof(T) == 2) tv = TV(pack_f16x2(v, 0.f) & 0xffffu);
         else tv = v;
-        sh.aux[buf][row * LDA + (rem % LDA)] = tv;
+        sh.aux[buf][key * LDX + col] = tv;
     }
     if (tid == 0) sh.range_bad = 0;
     float vmax = 0.f;   // largest |V| / |V_lr| staged by this thread (fp16 range check)
 
-    // ---- tile fetch (registers) and store (LDS)
+    // ---- tile fetch (registers) and store (LDS); keys past kv_end read row kv_end-1 (finite, P = 0)
     Vec<T, 8> kpre[KF], vpre[KF], lpre;
     auto fetch = [&](int t) {
-        const int64_t kb = int64_t(t) * kBK;
+        const int kb = t * kBK;
 #pragma unroll
         for (int c = 0; c < KF; ++c) {
             const int f = tid + kThreads * c;
             const int key = f / (D / 8);
             const int d0 = (f - key * (D / 8)) * 8;
-            const int64_t j = min<int64_t>(kb + key, kv_end - 1);   // rows past kv_end: a valid row, P = 0
+            const int64_t j = min(kb + key, kv_end - 1);
             kpre[c].load(Kp + j * kv_stride + int64_t(g) * D + d0);
             vpre[c].load(Vp + j * kv_stride + int64_t(g) * D + d0);
         }
         if (tid < LF) {
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
-            const int64_t j = min<int64_t>(kb + key, kv_end - 1);
+            const int64_t j = min(kb + key, kv_end - 1);
             lpre.load(Lp + j * p.ld_vlr + int64_t(p.agent) * R + r0);
+        }
+    };
+    // 8 values of one key's row as fp16 (bf16 inputs; exact within the fp16 range) or fp32
+    auto put8 = [&](TV* dst, const Vec<T, 8>& src) {
+        if constexpr (sizeof(T) == 2) {
+            uint32_t hv[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float lo = bf16_lo(src.w[e2]), hi = bf16_hi(src.w[e2]);
+                vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+                hv[e2] = pack_f16x2(lo, hi);
+            }
+            *reinterpret_cast<uint4*>(dst) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(src.v[0], src.v[1], src.v[2], src.v[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(src.v[4], src.v[5], src.v[6], src.v[7]);
         }
     };
     auto store = [&](int buf) {
@@ -178,46 +196,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             const int d0 = (f - key * (D / 8)) * 8;
             if constexpr (sizeof(T) == 2) {
                 *reinterpret_cast<uint4*>(&sh.k[buf][key * LDK + d0]) = *reinterpret_cast<const uint4*>(kpre[c].w);
-                uint32_t hv[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float lo = bf16_lo(vpre[c].w[e2]), hi = bf16_hi(vpre[c].w[e2]);
-                    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
-                    hv[e2] = h2(lo, hi);
-                }
-                *reinterpret_cast<uint4*>(&sh.v[buf][key * LDV + d0]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
             } else {
                 float* kd = &sh.k[buf][key * LDK + d0];
-                float* vd = &sh.v[buf][key * LDV + d0];
                 *reinterpret_cast<float4*>(kd) = make_float4(kpre[c].v[0], kpre[c].v[1], kpre[c].v[2], kpre[c].v[3]);
                 *reinterpret_cast<float4*>(kd + 4) = make_float4(kpre[c].v[4], kpre[c].v[5], kpre[c].v[6], kpre[c].v[7]);
-                *reinterpret_cast<float4*>(vd) = make_float4(vpre[c].v[0], vpre[c].v[1], vpre[c].v[2], vpre[c].v[3]);
-                *reinterpret_cast<float4*>(vd + 4) = make_float4(vpre[c].v[4], vpre[c].v[5], vpre[c].v[6], vpre[c].v[7]);
             }
+            put8(&sh.v[buf][key * LDV + d0], vpre[c]);
         }
         if (tid < LF) {
-            // the agent's V_lr slice goes to the aux tile transposed: row = rank column, column = key
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = lpre.get(e);
-                if constexpr (sizeof(T) == 2) {
-                    vmax = fmaxf(vmax, fabsf(v));
-                    sh.aux[buf][(r0 + e) * LDA + key] = TV(h2(v, 0.f) & 0xffffu);
-                } else {
-                    sh.aux[buf][(r0 + e) * LDA + key] = v;
-                }
-            }
+            put8(&sh.aux[buf][key * LDX + r0], lpre);
         }
     };
 
-    // ---- accumulators: O^T tiles 0..NDT-1 (row s of tile t is d = NDT*s + t), aux tiles (O_lr^T
-    // rows 0..R-1, l in row R or in the second aux tile). Lane (q, n) holds rows 4q..4q+3 of each
-    // tile for query row n.
+    // ---- accumulators: O^T tiles (tile t holds d = 16t .. 16t+15), aux tiles (O_lr^T rows
+    // 0..R-1, l in row LROW). Lane (q, n) holds rows 4q..4q+3 of each tile for query row n.
     f32x4 oacc[MT][NDT];
     f32x4 xacc[MT][NAUX];
-    float m_run[MT];
+    float m_run[MT];   // raw-score reference maximum of the exponentials
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         m_run[mt] = -INFINITY;
@@ -235,16 +232,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     for (int t = 0; t < n_tiles; ++t) {
         const int buf = t & 1;
         if (t + 1 < n_tiles) fetch(t + 1);
-        const int64_t kbase = int64_t(t) * kBK;
         const T* ks = sh.k[buf];
         const TV* vs = sh.v[buf];
         const TV* xs = sh.aux[buf];
 
-        // the tile in two 32-key blocks, each: S^T = K Q^T, online softmax, O^T += V^T P^T
 #pragma unroll 1
         for (int kb2 = 0; kb2 < NKB; ++kb2) {
-            const int64_t kblk = kbase + 32 * kb2;
-            // scores: lane (q, n) holds keys 32kb2 + 16u + 4q + j (u = 0, 1; j = 0..3) of query row n
+            const int kblk = t * kBK + 32 * kb2;
+            // scores: lane (q, n) holds keys kblk + 16u + 4q + j (u = 0, 1; j = 0..3) of query row n
             f32x4 sacc[MT][2];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -262,40 +257,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
             // online softmax per query row (raw scores; scale folded into the exponent)
             PF pf[MT];
-            const bool need_mask = kblk + 32 > full_end;
+            if (kblk + 32 > full_end) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if (need_mask) {
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             if (kblk + 16 * u + 4 * q + j > qpos[mt]) sacc[mt][u][j] = -INFINITY;
-                }
-                float mx = -INFINITY;
+            }
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[mt][u][j]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                // mnew is finite: key 0 (in the first block) is visible to every row
-                const float mnew = fmaxf(m_run[mt], mx);
-                const float alpha = fast_exp2((m_run[mt] - mnew) * sl2);
-                m_run[mt] = mnew;
-                const float mb = -mnew * sl2;
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][e >> 2][e & 3], sl2, mb));
-                if (__ballot(alpha != 1.f)) {
+            for (int mt = 0; mt < MT; ++mt) {
+                float mx = fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3]));
+                mx = fmaxf(mx, fmaxf(fmaxf(sacc[mt][1][0], sacc[mt][1][1]), fmaxf(sacc[mt][1][2], sacc[mt][1][3])));
+                mx = xor32_max(xor16_max(mx));
+                // a row moves its reference max only when P would otherwise exceed 2^8; the first
+                // block (key 0 is visible to every row) always sets it, so it stays finite
+                const bool grow = (mx - m_run[mt]) * sl2 > kRescaleLog2;
+                if (__ballot(grow)) {
+                    const float mnew = grow ? mx : m_run[mt];
+                    const float alpha = fast_exp2((m_run[mt] - mnew) * sl2);
+                    m_run[mt] = mnew;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) oacc[mt][dt] *= alpha;
 #pragma unroll
                     for (int x = 0; x < NAUX; ++x) xacc[mt][x] *= alpha;
                 }
+                const float mb = -m_run[mt] * sl2;
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][e >> 2][e & 3], sl2, mb));
                 if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) pf[mt].w[w2] = h2(pv[2 * w2], pv[2 * w2 + 1]);
+                    for (int w2 = 0; w2 < 4; ++w2) pf[mt].w[w2] = pack_f16x2(pv[2 * w2], pv[2 * w2 + 1]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pf[mt].v[e] = pv[e];
@@ -304,53 +298,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
             // O^T += V^T P^T; the lane's 8 keys of the block are key(e) = 32kb2 + 16(e/4) + 4q + e%4
             if constexpr (sizeof(T) == 2) {
-                // V rows of the lane's keys, d = NDT*n .. (fp16), then the 8 x NDT 16-bit transpose
-                uint32_t vr[8][NDT / 2];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = 32 * kb2 + 16 * (e >> 2) + 4 * q + (e & 3);
-                    const TV* src = &vs[key * LDV + NDT * n];
-                    if constexpr (NDT == 8) {
-                        const uint4 w4 = *reinterpret_cast<const uint4*>(src);
-                        vr[e][0] = w4.x; vr[e][1] = w4.y; vr[e][2] = w4.z; vr[e][3] = w4.w;
-                    } else {
-                        const uint2 w2 = *reinterpret_cast<const uint2*>(src);
-                        vr[e][0] = w2.x; vr[e][1] = w2.y;
-                    }
-                }
+                // transpose reads: lane j of group q points at key 32kb2 + 4q + j/4 (+16), columns
+                // c0 + 4(j%4); lane n then holds column c0 + n of the group's keys in slot order
+                const int rkey = 32 * kb2 + 4 * q + (n >> 2);
+                const int rcol = 4 * (n & 3);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
+                    const uint2 lo = lds_read_tr16(&vs[rkey * LDV + 16 * dt + rcol]);
+                    const uint2 hi = lds_read_tr16(&vs[(rkey + 16) * LDV + 16 * dt + rcol]);
                     H8 va;
-                    const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) va.w[pp] = __builtin_amdgcn_perm(vr[2 * pp + 1][dt >> 1], vr[2 * pp][dt >> 1], sel);
+                    va.w[0] = lo.x; va.w[1] = lo.y; va.w[2] = hi.x; va.w[3] = hi.y;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) oacc[mt][dt] = mma16x16x32_f16(va, pf[mt], oacc[mt][dt]);
                 }
 #pragma unroll
                 for (int x = 0; x < NAUX; ++x) {
+                    const uint2 lo = lds_read_tr16(&xs[rkey * LDX + 16 * x + rcol]);
+                    const uint2 hi = lds_read_tr16(&xs[(rkey + 16) * LDX + 16 * x + rcol]);
                     H8 xa;
-                    const TV* xr = &xs[(16 * x + n) * LDA + 32 * kb2 + 4 * q];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(xr);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(xr + 16);
                     xa.w[0] = lo.x; xa.w[1] = lo.y; xa.w[2] = hi.x; xa.w[3] = hi.y;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) xacc[mt][x] = mma16x16x32_f16(xa, pf[mt], xacc[mt][x]);
                 }
             } else {
+                // fp32: one key per 16x16x4 step; lane n supplies column 16t + n of its key
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int key = 32 * kb2 + 16 * (e >> 2) + 4 * q + (e & 3);
-                    Vec<float, NDT> vv;
-                    vv.load(&vs[key * LDV + NDT * n]);
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const float vv = vs[key * LDV + 16 * dt + n];
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
-                            oacc[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.v[dt], pf[mt].v[e], oacc[mt][dt], 0, 0, 0);
+                            oacc[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, pf[mt].v[e], oacc[mt][dt], 0, 0, 0);
+                    }
 #pragma unroll
                     for (int x = 0; x < NAUX; ++x) {
-                        const float xv = xs[(16 * x + n) * LDA + key];
+                        const float xv = xs[key * LDX + 16 * x + n];
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
                             xacc[mt][x] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, pf[mt].v[e], xacc[mt][x], 0, 0, 0);
@@ -368,48 +352,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     __syncthreads();
     const bool poison = sh.range_bad != 0;
     T* __restrict__ Op = static_cast<T*>(p.O);
-    constexpr int LROW = R < 16 ? R : 16;   // aux row holding l (in the second tile when R = 16)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        // aux tile rows 4q'+j live in lane (q', n): gather all of them for row n
+        // aux row 4q'+j of tile x lives in lane (q', n), register j: gather them for row n
         float olr[R];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) olr[rr] = __shfl(xacc[mt][0][rr & 3], n + 16 * (rr >> 2));
-        const float l = __shfl(xacc[mt][LROW / 16][LROW % 16 & 3], n + 16 * ((LROW % 16) >> 2));
+        for (int rr = 0; rr < R; ++rr) olr[rr] = __shfl(xacc[mt][rr / 16][rr & 3], n + 16 * ((rr & 15) >> 2));
+        const float l = __shfl(xacc[mt][LROW / 16][LROW & 3], n + 16 * ((LROW & 15) >> 2));
         const int64_t r = R0 + (wv * MT + mt) * 16 + n;
         if (r >= rows_total) continue;
         const int64_t qi = r / G;
         const int qh = int(r - qi * G);
         T* orow = Op + (qi * p.n_q + int64_t(g) * G + qh) * D;
         const float inv = poison ? __builtin_nanf("") : 1.f / l;
-        // lane (q, n) holds O^T rows 4q+j of tile dt, i.e. d = NDT*(4q+j) + dt: the 4*NDT contiguous
-        // values d = 4*NDT*q .. 4*NDT*q + 4*NDT - 1
-        float o[4 * NDT];
+        // lane (q, n) holds O^T rows 4q+j of tile dt: d = 16dt + 4q + j
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int dt = 0; dt < NDT; ++dt) {
+            float o4[4];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int d = NDT * (4 * q + j) + dt;
+            for (int j = 0; j < 4; ++j) {
+                const int d = 16 * dt + 4 * q + j;
                 float acc = oacc[mt][dt][j];
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) acc = fmaf(olr[rr], sh.b[rr * D + d], acc);
-                o[NDT * j + dt] = acc * inv;
+                o4[j] = acc * inv;
             }
-        T* dst = orow + 4 * NDT * q;
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int c = 0; c < NDT / 2; ++c) {
-                uint4 w;
-                w.x = pack_bf16x2(o[8 * c + 0], o[8 * c + 1]);
-                w.y = pack_bf16x2(o[8 * c + 2], o[8 * c + 3]);
-                w.z = pack_bf16x2(o[8 * c + 4], o[8 * c + 5]);
-                w.w = pack_bf16x2(o[8 * c + 6], o[8 * c + 7]);
-                *reinterpret_cast<uint4*>(dst + 8 * c) = w;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < NDT; ++c)
-                *reinterpret_cast<float4*>(dst + 4 * c) = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+            T* dst = orow + 16 * dt + 4 * q;
+            if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
+            else
+                *reinterpret_cast<float4*>(dst) = make_float4(o4[0], o4[1], o4[2], o4[3]);
         }
     }
 }

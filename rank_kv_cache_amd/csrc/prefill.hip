@@ -61,7 +61,7 @@ struct PrefillShared {
     using TV = typename PrefillTypes<T>::TV;
     static constexpr int NAUX = R < 16 ? 1 : 2;        // V_lr + ones tiles
     static constexpr int LDK = D + 16 / sizeof(T);     // K row (elements), padded by 16 bytes
-    static constexpr int LDV = D + 16 / sizeof(TV);    // V row
+    static constexpr int LDV = D + 32 / sizeof(TV);    // V row, padded by 32 bytes (transpose reads)
     static constexpr int LDX = 16 * NAUX;              // aux row: V_lr columns, then the ones column
     T k[2][kBK * LDK];
     TV v[2][kBK * LDV];
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 // a row moves its reference max only when P would otherwise exceed 2^8; the first
                 // block (key 0 is visible to every row) always sets it, so it stays finite
                 const bool grow = (mx - m_run[mt]) * sl2 > kRescaleLog2;
-                if (__ballot(grow)) {
+                if (__builtin_expect(__ballot(grow) != 0, 0)) {
                     const float mnew = grow ? mx : m_run[mt];
                     const float alpha = fast_exp2((m_run[mt] - mnew) * sl2);
                     m_run[mt] = mnew;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const int64_t qi = r / G;
         const int qh = int(r - qi * G);
         T* orow = Op + (qi * p.n_q + int64_t(g) * G + qh) * D;
-        const float inv = poison ? __builtin_nanf("") : 1.f / l;
+        const float inv = poison ? __uint_as_float(0x7fc00000u) : 1.f / l;   // quiet NaN by its bits
         // lane (q, n) holds O^T rows 4q+j of tile dt: d = 16dt + 4q + j
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {

@@ -121,6 +121,7 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
     p.X = X; p.A = A; p.Vlr = V_lr; p.out_rows = out_rows;
     p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_rows = vlr_rows;
     p.d_model = d_model; p.NR = int(NR); p.kr = pl.kr; p.ksplit = pl.ksplit; p.n_cg = pl.n_cg;
+    p.rows_per_wg = pl.rows_per_wg;
     p.bf16 = dtype == LRA_BF16;
     return hip_status(lra::launch_precompute(p, static_cast<hipStream_t>(stream)), "lra_lr_precompute launch");
 }

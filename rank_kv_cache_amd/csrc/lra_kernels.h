@@ -43,6 +43,7 @@ struct PrecomputeParams {
     int kr;        // reduction length handled by one workgroup (multiple of 32)
     int ksplit;    // workgroups along the reduction
     int n_cg;      // column groups of up to 64 columns
+    int rows_per_wg;   // X rows per workgroup (16 or 32)
     bool bf16;
 };
 
@@ -67,7 +68,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // Host-side launch geometry shared by the workspace-size query and the launch itself.
 struct PrecomputePlan {
-    int kr, ksplit, n_rt, n_cg;
+    int kr, ksplit, n_rt, n_cg, rows_per_wg;
     size_t part_bytes;
 };
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);

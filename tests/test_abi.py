@@ -137,6 +137,7 @@ def precompute(**kw):
     (dict(vlr_rows=100), E_SHAPE), (dict(vlr_rows=-1, out_rows=P), E_SHAPE), (dict(n_agents=0), E_SHAPE),
     (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(Vlr=P + 4), E_SHAPE),
     (dict(T=32, ws=None), E_WS), (dict(T=32, ws_bytes=100), E_WS), (dict(T=32, ws=WS + 16), E_WS),
+    (dict(T=256, ws_bytes=8 * 256 * 24 * 4 - 1), E_WS),
 ])
 def test_precompute_rejects_bad_arguments(kw, status):
     assert precompute(**kw) == status
@@ -147,9 +148,11 @@ def test_precompute_empty_is_a_no_op():
 
 
 def test_precompute_workspace_sizes():
-    # enough row tiles (2048 rows = 128 tiles): no split, no workspace; 32 rows: the reduction is
-    # split 16 ways (256 elements each) and the fp32 partials need 16 planes of 32 x 48
+    # enough row tiles (2048 rows = 128 tiles): no split, no workspace; one new token per request
+    # (32 rows): two reduction splits, whose fp32 partials need 2 planes of 32 x 48
     assert lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8) == 0
-    assert lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16) == 16 * 32 * 48 * 4
+    assert lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16) == 2 * 32 * 48 * 4
     assert lra.lra_lr_precompute_workspace_bytes(1, 256, 3, 8) == 0
     assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0
+    # 256 rows = 16 tiles: split 8 ways (512 elements each)
+    assert lra.lra_lr_precompute_workspace_bytes(256, 4096, 3, 8) == 8 * 256 * 24 * 4

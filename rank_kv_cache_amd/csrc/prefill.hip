@@ -28,9 +28,10 @@
 //     O_lr^T and the softmax normaliser l come out of the same matrix-core product as O (l is the
 //     sum of exactly the rounded P the products used). For r = 16 the ones column is a second tile.
 //   * online softmax per query row and 32-key block in base 2, scale*log2(e) folded into one fma
-//     per score; the row max is reduced over the 4 lanes sharing a row with permlane swaps. The
-//     reference max m only moves (and O, O_lr, l are rescaled) when a row's block max exceeds it by
-//     more than a factor 2^8 in P; otherwise P may reach 2^8, well inside fp16.
+//     per score. The reference max m only moves (and O, O_lr, l are rescaled) when a score of the
+//     block exceeds it by more than a factor 2^8 in P; otherwise P may reach 2^8, well inside fp16.
+//     Each lane tests its own 8 scores against that threshold; only when some lane of the wave
+//     crosses it is the row max reduced over the 4 lanes sharing a row (permlane swaps).
 //   * epilogue: gather O_lr and l of the row across its 4 lanes, add O_lr B_agent (B slice in LDS),
 //     divide by l, store in the input type (bf16 round-to-nearest-even)
 #include <type_traits>
@@ -215,15 +216,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     f32x4 oacc[MT][NDT];
     f32x4 xacc[MT][NAUX];
     float m_run[MT];   // raw-score reference maximum of the exponentials
+    float m_thr[MT];   // raw score at which P would exceed 2^kRescaleLog2
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         m_run[mt] = -INFINITY;
+        m_thr[mt] = -INFINITY;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[mt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < NAUX; ++x) xacc[mt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float sl2 = p.scale * kLog2e;
+    const float thr_gap = kRescaleLog2 / sl2;   // scale > 0
 
     fetch(0);
     store(0);
@@ -266,23 +270,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                         for (int j = 0; j < 4; ++j)
                             if (kblk + 16 * u + 4 * q + j > qpos[mt]) sacc[mt][u][j] = -INFINITY;
             }
+            // a row moves its reference max only when P would otherwise exceed 2^8 (the first block
+            // always does: key 0 is visible to every row, so m stays finite)
+            float lmx[MT];
+            bool any_grow = false;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                float mx = fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3]));
-                mx = fmaxf(mx, fmaxf(fmaxf(sacc[mt][1][0], sacc[mt][1][1]), fmaxf(sacc[mt][1][2], sacc[mt][1][3])));
-                mx = xor32_max(xor16_max(mx));
-                // a row moves its reference max only when P would otherwise exceed 2^8; the first
-                // block (key 0 is visible to every row) always sets it, so it stays finite
-                const bool grow = (mx - m_run[mt]) * sl2 > kRescaleLog2;
-                if (__builtin_expect(__ballot(grow) != 0, 0)) {
+                lmx[mt] = fmaxf(fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3])),
+                                fmaxf(fmaxf(sacc[mt][1][0], sacc[mt][1][1]), fmaxf(sacc[mt][1][2], sacc[mt][1][3])));
+                any_grow |= lmx[mt] > m_thr[mt];
+            }
+            if (__builtin_expect(__ballot(any_grow) != 0, 0)) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float mx = xor32_max(xor16_max(lmx[mt]));
+                    const bool grow = mx > m_thr[mt];
                     const float mnew = grow ? mx : m_run[mt];
                     const float alpha = fast_exp2((m_run[mt] - mnew) * sl2);
                     m_run[mt] = mnew;
+                    m_thr[mt] = mnew + thr_gap;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) oacc[mt][dt] *= alpha;
 #pragma unroll
                     for (int x = 0; x < NAUX; ++x) xacc[mt][x] *= alpha;
                 }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
                 const float mb = -m_run[mt] * sl2;
                 float pv[8];
 #pragma unroll

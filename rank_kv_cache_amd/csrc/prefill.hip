@@ -9,10 +9,12 @@
 //
 // gfx950 mapping (16x16x32 matrix-core steps, fp32 accumulation; fp32 inputs run the same template
 // on 16x16x4 fp32 steps):
-//   * one workgroup = 8 waves (two per SIMD, so one wave's softmax overlaps the other's matrix-core
-//     work) = 256 "query rows" of one KV head; a query row is one (query, head) pair of the head's
-//     group, so all G heads of a group share every K/V tile (grouped-query). Each wave owns 2 tiles
-//     of 16 rows; their queries stay in registers as MFMA B operands.
+//   * one workgroup = 8 waves (two per SIMD) = 256 "query rows" of one KV head; a query row is one
+//     (query, head) pair of the head's group, so all G heads of a group share every K/V tile
+//     (grouped-query). Each wave owns 2 tiles of 16 rows; their queries stay in registers as MFMA B
+//     operands. The two halves of a workgroup take 128-row pieces from the two ends of the chunk,
+//     one with a short causal key range and one with a long one, which evens out the work per
+//     workgroup and per SIMD; a wave stops multiplying after its own last visible key.
 //   * 64-key tiles are staged in LDS in their natural row layout with 128-bit stores, double
 //     buffered: the next tile's global loads are in flight while the current one is multiplied,
 //     one barrier per tile. The tile is consumed in two 32-key blocks.
@@ -47,6 +49,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMT = 2;                          // 16-row tiles per wave
 constexpr int kRowsPerWG = 16 * kMT * kWaves;   // 256 query rows
+constexpr int kPieceRows = kRowsPerWG / 2;      // rows of one half of a workgroup
 constexpr int kBK = 64;                         // keys per LDS tile
 constexpr float kRescaleLog2 = 8.f;             // m moves when P would exceed 2^8
 
@@ -95,11 +98,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int G = p.G;
     const int n_kv = p.n_kv;
     const int64_t rows_total = p.L_C * G;
-    const int nblk = int((rows_total + kRowsPerWG - 1) / kRowsPerWG);
-    // KV head = w mod n_kv keeps one head per XCD when n_kv = 8; heavier (later) blocks start first
-    const int g = blockIdx.x % n_kv;
-    const int blk = nblk - 1 - int(blockIdx.x / n_kv);
-    const int64_t R0 = int64_t(blk) * kRowsPerWG;
+    // The rows of one KV head are cut into pieces of kPieceRows; the two halves of workgroup `pair`
+    // take pieces pair and n_pieces-1-pair, a short and a long causal key range, so workgroups
+    // (and SIMDs, each of which runs one wave of each half) get about the same number of
+    // query-key pairs. With an odd count the middle workgroup's second half has no rows.
+    const int n_pieces = int((rows_total + kPieceRows - 1) / kPieceRows);
+    const int g = blockIdx.x % n_kv;   // KV head = w mod n_kv keeps one head per XCD when n_kv = 8
+    const int pair = int(blockIdx.x / n_kv);
+    const int half = wv / (kWaves / 2);
+    const int piece = half ? n_pieces - 1 - pair : pair;
+    const bool half_empty = half && piece == pair;
+    const int64_t R0 = int64_t(piece) * kPieceRows + (wv % (kWaves / 2)) * (16 * MT);   // wave's first row
+    const bool wave_rows = !half_empty && R0 < rows_total;
 
     const T* __restrict__ Qp = static_cast<const T*>(p.Q);
     const T* __restrict__ Kp = static_cast<const T*>(p.K);
@@ -113,9 +123,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     Vec<T, 8> qf[MT][KCH];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t r = R0 + (wv * MT + mt) * 16 + n;
-        const bool ok = r < rows_total;
-        const int64_t rc = ok ? r : rows_total - 1;
+        const int64_t r = R0 + mt * 16 + n;
+        const bool ok = wave_rows && r < rows_total;
+        const int64_t rc = min(r, rows_total - 1);
         const int64_t qi = rc / G;
         const int qh = int(rc - qi * G);
         qpos[mt] = int(p.L_P + qi);
@@ -127,12 +137,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         }
     }
 
-    // ---- key range of the workgroup
-    const int64_t i_min = R0 / G;
-    const int64_t i_max = min<int64_t>(p.L_C - 1, (R0 + kRowsPerWG - 1) / G);
-    const int kv_end = int(p.L_P + i_max + 1);     // keys [0, kv_end) are visible to some row
-    const int full_end = int(p.L_P + i_min + 1);   // keys [0, full_end) are visible to every row
+    // ---- key ranges: the workgroup stages keys [0, kv_end) (visible to some row of its long
+    // piece); a wave computes the blocks below its own end and masks from its full_end on
+    const int64_t heavy_last = min<int64_t>(rows_total, int64_t(n_pieces - pair) * kPieceRows) - 1;
+    const int kv_end = int(p.L_P + heavy_last / G + 1);
     const int n_tiles = (kv_end + kBK - 1) / kBK;
+    const int64_t i_min = min(R0, rows_total - 1) / G;
+    const int64_t i_max = min<int64_t>(p.L_C - 1, (R0 + 16 * MT - 1) / G);
+    const int wave_end = wave_rows ? int(p.L_P + i_max + 1) : 0;   // keys [0, wave_end) visible to some row
+    const int full_end = int(p.L_P + i_min + 1);                   // keys [0, full_end) visible to every row
 
     // ---- constants in LDS: B_agent slice (fp32), the ones / zero columns of the aux tiles
     for (int idx = tid; idx < R * D; idx += kThreads) {
@@ -240,8 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const TV* vs = sh.v[buf];
         const TV* xs = sh.aux[buf];
 
+        // blocks of this tile holding a key visible to the wave (wave-uniform)
+        const int nkb = min(NKB, max(0, (wave_end - t * kBK + 31) / 32));
 #pragma unroll 1
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        for (int kb2 = 0; kb2 < nkb; ++kb2) {
             const int kblk = t * kBK + 32 * kb2;
             // scores: lane (q, n) holds keys kblk + 16u + 4q + j (u = 0, 1; j = 0..3) of query row n
             f32x4 sacc[MT][2];
@@ -373,8 +388,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) olr[rr] = __shfl(xacc[mt][rr / 16][rr & 3], n + 16 * ((rr & 15) >> 2));
         const float l = __shfl(xacc[mt][LROW / 16][LROW & 3], n + 16 * ((LROW & 15) >> 2));
-        const int64_t r = R0 + (wv * MT + mt) * 16 + n;
-        if (r >= rows_total) continue;
+        const int64_t r = R0 + mt * 16 + n;
+        if (!wave_rows || r >= rows_total) continue;
         const int64_t qi = r / G;
         const int qh = int(r - qi * G);
         T* orow = Op + (qi * p.n_q + int64_t(g) * G + qh) * D;
@@ -403,8 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 template <typename T, int D, int R>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     const int64_t rows = p.L_C * p.G;
-    const int64_t nblk = (rows + kRowsPerWG - 1) / kRowsPerWG;
-    hipLaunchKernelGGL((prefill_kernel<T, D, R>), dim3(unsigned(nblk * p.n_kv)), dim3(kThreads), 0, stream, p);
+    const int64_t n_pieces = (rows + kPieceRows - 1) / kPieceRows;
+    const int64_t n_pairs = (n_pieces + 1) / 2;
+    hipLaunchKernelGGL((prefill_kernel<T, D, R>), dim3(unsigned(n_pairs * p.n_kv)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

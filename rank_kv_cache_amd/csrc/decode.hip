@@ -315,17 +315,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     }
 }
 
-// Merge of the splits of one (request b, query head h): weights 2^(m_s - max m) (log-sum-exp rule),
-// then the up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l, rounded to the output type.
-// Wave w sums the splits s = w, w+4, ...; lane c holds columns c, c+64, c+128 of O | O_lr, so every
-// lane has several independent loads in flight. Requests with no key get zeros; requests with an
-// invalid range or agent NaN.
+// Merge of the splits of one (request b, query head h) by the log-sum-exp rule, then the
+// up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l, rounded to the output type.
+// Wave w merges the splits s = w, w+4, ... in one pass with a running maximum (lane c holds columns
+// c, c+64, c+128 of O | O_lr), so the loads of all its splits are independent of each other; the
+// four wave states are merged in LDS. The B slice is fetched first and used last. Requests with
+// no key get zeros; requests with an invalid range or agent NaN.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
     constexpr int W = D + R;
     constexpr int NC = (W + 63) / 64;
     __shared__ float part[kWaves][NC * 64];
-    __shared__ float ml_s[2];
+    __shared__ float wm[kWaves], wl[kWaves];
+    __shared__ float comb[NC * 64];
     const int b = blockIdx.x / p.n_q;
     const int h = blockIdx.x - b * p.n_q;
     const int g = h / p.G;
@@ -341,47 +343,66 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
         for (int c = threadIdx.x; c < D; c += kThreads) Op[c] = fill;
         return;
     }
-    const int ns = (len + p.chunk - 1) / p.chunk;   // splits that hold a partial
+    // column c of the agent's B slice for this KV head (threads c < D)
+    const int64_t d_kv = int64_t(p.n_kv) * D;
+    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
+    float bcol[R];
+    if (threadIdx.x < D) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) bcol[rr] = to_f32<T>(Bp[int64_t(rr) * d_kv + threadIdx.x]);
+    }
+    const int ns = (len + p.chunk - 1) / p.chunk;   // splits that hold a partial (each has a key)
     const float* ml = p.ws_ml + bh * p.n_split * 2;
     const float* po = p.ws_o + bh * p.n_split * W;
-    // maximum over the splits (every wave computes it; the partials are few)
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    // this wave's splits: weighted O | O_lr columns and the weighted normaliser
+    float m = -INFINITY, l = 0.f;
     float acc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-    float L = 0.f;
 #pragma unroll 4
     for (int s = wv; s < ns; s += kWaves) {
-        const float wgt = fast_exp2(ml[2 * s] - M);
-        L = fmaf(wgt, ml[2 * s + 1], L);
+        const float ms = ml[2 * s], ls = ml[2 * s + 1];
+        float v[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            if (64 * c + lane < W) acc[c] = fmaf(wgt, po[int64_t(s) * W + 64 * c + lane], acc[c]);
+        for (int c = 0; c < NC; ++c) v[c] = (64 * c + lane < W) ? po[int64_t(s) * W + 64 * c + lane] : 0.f;
+        const float mn = fmaxf(m, ms);            // finite: every merged split holds a key
+        const float keep = fast_exp2(m - mn);     // 0 for the first split (m = -inf)
+        const float wgt = fast_exp2(ms - mn);
+        l = fmaf(l, keep, wgt * ls);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = fmaf(acc[c], keep, wgt * v[c]);
+        m = mn;
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) part[wv][64 * c + lane] = acc[c];
-    if (lane == 0) part[wv][NC * 64 - 1] = L;   // column NC*64-1 >= W is free
-    __syncthreads();
-    if (threadIdx.x < 64 * NC) {
-        const int c = threadIdx.x;
-        part[0][c] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+    if (lane == 0) {
+        wm[wv] = m;
+        wl[wv] = l;
     }
     __syncthreads();
-    if (threadIdx.x == 0) ml_s[0] = part[0][NC * 64 - 1];
+    // the four wave states (a wave without splits has m = -inf and weight 0)
+    float M = wm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
+    float e[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) e[w] = fast_exp2(wm[w] - M);
+    if (threadIdx.x < W) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o = fmaf(e[w], part[w][threadIdx.x], o);
+        comb[threadIdx.x] = o;
+    }
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L = fmaf(e[w], wl[w], L);
     __syncthreads();
     // up-projection once per query row, normalise, store
-    const int64_t d_kv = int64_t(p.n_kv) * D;
-    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
-    const float inv = 1.f / ml_s[0];
-    for (int c = threadIdx.x; c < D; c += kThreads) {
-        float o = part[0][c];
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        float o = comb[c];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) o = fmaf(part[0][D + rr], to_f32<T>(Bp[int64_t(rr) * d_kv + c]), o);
-        Op[c] = from_f32<T>(o * inv);
+        for (int rr = 0; rr < R; ++rr) o = fmaf(comb[D + rr], bcol[rr], o);
+        Op[c] = from_f32<T>(o / L);
     }
 }
 

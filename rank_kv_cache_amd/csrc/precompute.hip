@@ -125,8 +125,19 @@ __global__ __launch_bounds__(256) void precompute_reduce_kernel(PrecomputeParams
     if (idx >= p.T * p.NR) return;
     const int64_t t = idx / p.NR;
     const int c = int(idx - t * p.NR);
+    // partials in split order, eight loads in flight at a time
+    const int64_t stride = p.T * p.NR;
+    const float* src = p.ws_part + idx;
     float v = 0.f;
-    for (int k = 0; k < p.ksplit; ++k) v += p.ws_part[(int64_t(k) * p.T + t) * p.NR + c];
+    int k = 0;
+    for (; k + 8 <= p.ksplit; k += 8) {
+        float part[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) part[u] = src[(k + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += part[u];
+    }
+    for (; k < p.ksplit; ++k) v += src[k * stride];
     const int64_t orow = p.out_rows ? p.out_rows[t] : t;
     if (orow >= 0 && orow < p.vlr_rows) static_cast<T*>(p.Vlr)[orow * p.ld_vlr + c] = from_f32<T>(v);
 }
@@ -160,9 +171,10 @@ hipError_t launch_t(const PrecomputeParams& p, hipStream_t stream) {
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool /*bf16*/) {
     // Every workgroup reads the A fragments of its reduction range from L2 once per 16-row tile;
     // with many rows (>= 8192) a workgroup takes two tiles, so A costs half the L2 traffic. The
-    // reduction is split when there are too few row tiles to spread over the chip (never below 256
-    // elements per workgroup, 32 per wave); a handful of rows (one new token per request) takes
-    // two splits, which measured fastest on MI355X against one and against four or more.
+    // reduction is split until the grid reaches 256 workgroups (never below 256 elements per
+    // workgroup, 32 per wave); a handful of rows (one new token per request) takes two splits.
+    // Measured on MI355X: 2048 x 4096 rows run fastest with two splits (11.4 us against 13.6 with
+    // one, 16 with four); 32 x 4096 rows with two (11.0 us; 11.4 with four to sixteen).
     PrecomputePlan pl{};
     pl.rows_per_wg = T >= 8192 ? 2 * kRows : kRows;
     pl.n_rt = int((T + pl.rows_per_wg - 1) / pl.rows_per_wg);
@@ -172,7 +184,7 @@ PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool /*bf16*/) {
     if (T <= 64) {
         ks = d_model >= 512 ? 2 : 1;
     } else {
-        while (tiles * ks < 128 && d_model / (2 * ks) >= 256 && ks < 64) ks *= 2;
+        while (tiles * ks < 256 && d_model / (2 * ks) >= 256 && ks < 64) ks *= 2;
     }
     pl.kr = ((d_model + ks - 1) / ks + 31) / 32 * 32;
     pl.ksplit = (d_model + pl.kr - 1) / pl.kr;

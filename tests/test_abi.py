@@ -148,11 +148,13 @@ def test_precompute_empty_is_a_no_op():
 
 
 def test_precompute_workspace_sizes():
-    # enough row tiles (2048 rows = 128 tiles): no split, no workspace; one new token per request
-    # (32 rows): two reduction splits, whose fp32 partials need 2 planes of 32 x 48
-    assert lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8) == 0
+    # the reduction is split until the grid holds 256 workgroups: 2048 rows = 128 tiles of 16 ->
+    # two splits, whose fp32 partials need 2 planes of 2048 x 24; 8192 rows = 256 tiles of 32 ->
+    # no split, no workspace; one new token per request (32 rows): two splits of 32 x 48
+    assert lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8) == 2 * 2048 * 24 * 4
+    assert lra.lra_lr_precompute_workspace_bytes(8192, 4096, 3, 8) == 0
     assert lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16) == 2 * 32 * 48 * 4
     assert lra.lra_lr_precompute_workspace_bytes(1, 256, 3, 8) == 0
     assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0
-    # 256 rows = 16 tiles: split 8 ways (512 elements each)
-    assert lra.lra_lr_precompute_workspace_bytes(256, 4096, 3, 8) == 8 * 256 * 24 * 4
+    # 256 rows = 16 tiles: split 16 ways (256 elements each, the minimum)
+    assert lra.lra_lr_precompute_workspace_bytes(256, 4096, 3, 8) == 16 * 256 * 24 * 4

@@ -51,6 +51,8 @@ def test_ministral_precompute_scatter_into_cache():
     ("bf16", 1, 4096, 3, 8), ("bf16", 37, 4096, 3, 16), ("bf16", 100, 256, 3, 8), ("bf16", 513, 1024, 2, 16),
     ("bf16", 64, 512, 9, 8), ("bf16", 20, 2048, 5, 16), ("f32", 1, 256, 3, 8), ("f32", 300, 256, 3, 8),
     ("f32", 17, 1024, 9, 16),
+    # 8192 rows and more run 32-row tiles
+    ("bf16", 8200, 512, 3, 8), ("bf16", 9000, 256, 2, 16),
 ])
 def test_precompute_shapes(dtype, T, d_model, N, r):
     s = W.Shape(n_q=4, n_kv=2, d_head=64, rank=r, n_agents=N, d_model=d_model, dtype=dtype)

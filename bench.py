@@ -184,8 +184,10 @@ def bench_prefill(args, torch, lra, W, out):
     def step():
         lra.lra_attn_prefill(Q, c.L_P, K, V, L, B, 0, s.scale, O)
 
-    reps = max(3, args.steps // 10)
-    ms = time_launches(step, reps, 2, torch)
+    # ~20 ms of warm-up launches first: the first launches after the inputs are built run at
+    # lower clocks (about 0.75 ms against 0.6 ms in steady state on MI355X)
+    reps = max(10, args.steps // 2)
+    ms = time_launches(step, reps, 30, torch)
     fl = prefill_flops(c.L_P, c.L_C, s.n_q, s.d_head, s.rank)
     tf = fl / (ms * 1e-3) / 1e12
     out["prefill_llama_LP16384_LC2048_r8"] = {
@@ -318,14 +320,17 @@ def bench_ministral_step(args, torch, lra, W, out):
     reps = max(3, args.steps // 10)
     ms = time_launches(step, reps, 1, torch)
     ms_g = time_graph(step, 1, reps, torch)
-    best = ms_g if ms_g is not None else ms
+    # the step is 72 launches of 0.01-0.25 ms: the faster of the graph replay and the eager loop
+    graph_best = ms_g is not None and ms_g <= ms
+    best = ms_g if graph_best else ms
     nb = n_layers * (decode_bytes(lens, agents, s.n_q, s.n_kv, s.d_head, s.rank)
                      + precompute_bytes(len(lens), s.d_model, s.n_agents * s.rank))
     gbs = nb / (best * 1e-3) / 1e9
     out["ministral_step_36x_b32_r16"] = {"ms": round(best, 3), "gbs": round(gbs, 1), "bytes": nb,
                                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm", "reps": reps,
                                          "ms_eager": round(ms, 3),
-                                         "timing": "HIP graph of one step" if ms_g is not None else "eager",
+                                         "ms_graph": round(ms_g, 3) if ms_g is not None else None,
+                                         "timing": "HIP graph of one step" if graph_best else "eager launches",
                                          "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
                                          "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
     del layers

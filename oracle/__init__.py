@@ -16,9 +16,9 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` (library special case, associativity identity,
 invariants, closed forms, hand-derived fixtures in ``tests/golden/`` and a
 pure-Python brute force). Bit-for-bit agreement with the bf16 rounding points
-of the GPU path (P rounded to bf16 before the P.V product in prefill) is not
-something the pages fix: that part is "parity unpinned" beyond the stated
-tolerance.
+of the GPU path (prefill rounds P to fp16 before the P.V product; decode splits
+P into bf16 hi + lo parts) is not something the pages fix: that part is
+"parity unpinned" beyond the stated tolerance.
 """
 from .lora_attention import (  # noqa: F401
     lr_precompute,
@@ -33,4 +33,5 @@ from .lora_attention import (  # noqa: F401
     attn_prefill,
     attn_decode,
     attn_factored,
+    ADAPTER_FREE,
 )

@@ -29,6 +29,10 @@ Readings where the pages are silent (each is also listed in the design notes):
     sits at absolute position L_P + i and sees keys 0 .. L_P + i. A decode
     query sits at the last position of its range and sees all kv_len keys.
   * a query with no visible key (kv_len = 0) returns zeros.
+  * agent = -1 (ADAPTER_FREE) is the adapter-free view of double batching
+    (PReCache paper page, section 3, ReBaseShared: the adapter-free path runs
+    beside the adapted one over the same tokens and attends only to the
+    neutral base cache). Its values are V_base; V_lr and B are not read.
 """
 from __future__ import annotations
 
@@ -74,6 +78,9 @@ def agent_columns(agent: int, rank: int) -> slice:
     return slice(agent * rank, (agent + 1) * rank)
 
 
+ADAPTER_FREE = -1
+
+
 # --------------------------------------------------------------------------- V_k materialised
 def agent_values(V_base, V_lr, B, agent: int) -> np.ndarray:
     """The agent's full value cache ``V_base + V_lr[:, agent cols] B_agent``, built explicitly.
@@ -82,8 +89,12 @@ def agent_values(V_base, V_lr, B, agent: int) -> np.ndarray:
     shared ``X W0`` and the agent's ``(X A_i) B_i``; the LR cache keeps
     ``X A_i`` and B_i restores the full width on demand.
     V_base: [L, n_kv, d]; V_lr: [L, >= N*r]; B: [N, r, n_kv*d]. Returns [L, n_kv, d].
+    agent = ADAPTER_FREE gives the neutral base cache itself (PReCache paper page, section 3,
+    double batching: the adapter-free path attends to the base cache only).
     """
     V_base = _f64(V_base)
+    if agent == ADAPTER_FREE:
+        return V_base.copy()
     B = _f64(B)
     L, n_kv, d = V_base.shape
     rank = B.shape[1]
@@ -205,7 +216,8 @@ def attn_factored(Q, K, V_base, V_lr, B, agent: int, q_pos, scale: float) -> np.
     LR cache is attended in rank space and expanded by B once per query row,
     instead of expanding every cached row first. Equal to ``attention`` over
     ``agent_values`` in exact arithmetic; kept here so that identity can be
-    tested. Returns [Lq, n_q, d].
+    tested. The adapter-free view (agent = ADAPTER_FREE) has no LR term.
+    Returns [Lq, n_q, d].
     """
     Q = _f64(Q)
     V_base = _f64(V_base)
@@ -219,5 +231,7 @@ def attn_factored(Q, K, V_base, V_lr, B, agent: int, q_pos, scale: float) -> np.
     O = np.empty((Lq, n_q, d))
     for h in range(n_q):
         g = kv_head_of(h, G)
-        O[:, h, :] = P[h] @ V_base[:, g, :] + (P[h] @ lr) @ B[agent][:, g * d:(g + 1) * d]
+        O[:, h, :] = P[h] @ V_base[:, g, :]
+        if agent != ADAPTER_FREE:
+            O[:, h, :] += (P[h] @ lr) @ B[agent][:, g * d:(g + 1) * d]
     return O

@@ -13,6 +13,8 @@ def _tolist(a):
 
 
 def _value(Vb, Vlr, B, j, g, c, agent, r, d):
+    if agent == -1:   # adapter-free view: the base row alone
+        return Vb[j][g][c]
     lr = math.fsum(Vlr[j][agent * r + k] * B[agent][k][g * d + c] for k in range(r))
     return Vb[j][g][c] + lr
 

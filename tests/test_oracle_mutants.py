@@ -26,6 +26,7 @@ def _checks():
     yield lambda: pins.test_bruteforce_prefill(4, 2, 8, 2, 3, 5, 2)
     yield lambda: pins.test_bruteforce_prefill(8, 2, 4, 4, 0, 7, 1)
     yield lambda: pins.test_bruteforce_decode_with_shared_and_empty_ranges()
+    yield lambda: pins.test_bruteforce_decode_mixed_adapted_and_adapter_free()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()
@@ -65,7 +66,12 @@ def _mut_softmax_flipped(S, mask):
     return _orig_softmax(-np.asarray(S, np.float64), mask)
 
 
+def _mut_adapter_free_reads_agent_zero(V_base, V_lr, B, agent):
+    return _orig_agent_values(V_base, V_lr, B, max(agent, 0))
+
+
 MUTANTS = {
+    "adapter_free_reads_agent_zero": ("agent_values", _mut_adapter_free_reads_agent_zero),
     "head_map_interleaved": ("kv_head_of", lambda h, group: h % group),
     "head_map_coarse": ("kv_head_of", lambda h, group: h // (2 * group)),
     "agent_cols_off_by_one": ("agent_columns", lambda a, r: slice(a * r + 1, (a + 1) * r + 1)),

@@ -90,6 +90,12 @@ def test_zero_lora_is_standard_causal_gqa_attention(n_q, n_kv, L_P, L_C):
     assert rel_err(O, ref) <= 1e-12
     O2 = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), np.zeros_like(f64(c.V_lr)), f64(c.B), 1, L_P, s.scale)
     assert rel_err(O2, ref) <= 1e-12
+    # the adapter-free view (agent -1) attends the base cache alone, whatever V_lr and B hold
+    O3 = oracle.attn_prefill(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), oracle.ADAPTER_FREE, L_P, s.scale)
+    assert rel_err(O3, ref) <= 1e-12
+    Of = oracle.attn_factored(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), oracle.ADAPTER_FREE,
+                              L_P + np.arange(L_C), s.scale)
+    assert rel_err(Of, ref) <= 1e-12
 
 
 # ----------------------------------------------------------------------------- associativity
@@ -240,6 +246,22 @@ def test_bruteforce_decode_with_shared_and_empty_ranges():
     ref = bruteforce.decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
     assert rel_err(O, ref) <= 1e-13
     assert np.all(O[2] == 0.0)
+
+
+def test_bruteforce_decode_mixed_adapted_and_adapter_free():
+    """Double batching (PReCache paper page, section 3): adapted and adapter-free requests over the
+    same rows in one batch; the adapter-free ones (agent -1) see the base cache alone."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    c = W.random_decode((912,), s, kv_lens=[12, 12, 7, 7, 1], kv_starts=[0, 0, 5, 5, 11], rows=12,
+                        agents=[1, -1, -1, 2, -1], b_std=0.7)
+    O = oracle.attn_decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    ref = bruteforce.decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    assert rel_err(O, ref) <= 1e-13
+    # the adapted request differs from the adapter-free one over the same rows with the same query
+    Q2 = f64(c.Q).copy()
+    Q2[1] = Q2[0]
+    O2 = oracle.attn_decode(Q2, f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    assert np.max(np.abs(O2[0] - O2[1])) > 1e-3
 
 
 def test_precompute_triple_loop_and_one_hot():

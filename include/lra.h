@@ -33,6 +33,11 @@
  *    decode request with an invalid range or agent gets NaN in every output
  *    element; a precompute row whose out_rows entry is out of range is not
  *    written.
+ *  - Agent index -1 (LRA_ADAPTER_FREE) selects the adapter-free view of double
+ *    batching (PReCache paper, section 3, ReBaseShared: the adapter-free path
+ *    processes the same tokens and attends only to the neutral base cache):
+ *    O is attention over K_base and V_base alone, with no LR term. Adapted and
+ *    adapter-free decode requests can share one launch.
  *  - Supported: d_head in {64, 128}; rank in {8, 16}; n_q % n_kv == 0 with
  *    group size n_q / n_kv in 1..8. Anything else returns LRA_ERR_UNSUPPORTED.
  *
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 1
+#define LRA_ABI_VERSION 2   /* 2: agent index -1 selects the adapter-free view */
 
 typedef enum {
     LRA_OK = 0,
@@ -62,6 +67,9 @@ typedef enum {
 } lra_status;
 
 typedef enum { LRA_F32 = 0, LRA_BF16 = 1 } lra_dtype;
+
+/* agent index of the adapter-free view (attention over the base cache alone, no LR term) */
+#define LRA_ADAPTER_FREE (-1)
 
 /* ABI version of the loaded library (LRA_ABI_VERSION at build time). */
 int lra_abi_version(void);
@@ -111,6 +119,8 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * V_base   (device) [L_P+L_C x n_kv x d_head]
  * V_lr     (device) [L_P+L_C x ld_vlr], agent a owns columns a*rank .. a*rank+rank-1
  * B        (device) [n_agents x rank x n_kv*d_head]: B_a, one r x (n_kv*d_head) matrix per agent
+ * agent    (host) in [0, n_agents), or -1 for the adapter-free view (V_lr and B are not read);
+ *          anything else returns LRA_ERR_INDEX
  * O        (device) [L_C x n_q x d_head] output
  * bf16 inputs: Q.K products are exact (bf16 operands, fp32 accumulation); for P.V the
  * probabilities are rounded to fp16 and V_base / V_lr converted exactly to fp16, so entries of the
@@ -135,7 +145,9 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * Q        (device) [batch x n_q x d_head]
  * K_base, V_base (device) [kv_rows x n_kv x d_head]
  * V_lr     (device) [kv_rows x ld_vlr]
- * kv_start (device) [batch] int64, kv_len (device) [batch] int32, agent (device) [batch] int32
+ * kv_start (device) [batch] int64, kv_len (device) [batch] int32, agent (device) [batch] int32:
+ *          agent[b] in [0, n_agents), or -1 for the adapter-free view (B is not read; the split
+ *          kernel streams agent 0's V_lr columns of the range and the merge drops that product)
  * max_kv_len (host) an upper bound on every kv_len[b]; it sizes the launch
  * B        (device) [n_agents x rank x n_kv*d_head]
  * keys_per_split  keys handled by one split (multiple of 64), or 0 for the library's choice

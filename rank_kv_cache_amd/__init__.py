@@ -26,6 +26,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
 LRA_F32, LRA_BF16 = 0, 1
+ADAPTER_FREE = -1   # agent index of the adapter-free view (attention over the base cache alone)
 
 _c = ctypes
 _p = _c.c_void_p
@@ -159,7 +160,9 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
                      stream=None) -> torch.Tensor:
     """Causal prefill of the L_C = Q.shape[0] new tokens over L_P cached + L_C new keys for ``agent``.
 
-    Q [L_C, n_q, d]; K_base, V_base [>= L_P+L_C, n_kv, d]; V_lr [>= L_P+L_C, ld]; B [N, r, n_kv*d]."""
+    Q [L_C, n_q, d]; K_base, V_base [>= L_P+L_C, n_kv, d]; V_lr [>= L_P+L_C, ld]; B [N, r, n_kv*d].
+    ``agent`` = ADAPTER_FREE (-1) selects the adapter-free view: attention over the base cache
+    alone, V_lr and B unread."""
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)
@@ -200,8 +203,10 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
     """One query per request over rows [kv_start[b], kv_start[b] + kv_len[b]) of the shared caches.
 
     Q [batch, n_q, d]; K_base, V_base [rows, n_kv, d]; V_lr [rows, ld]; kv_start int64 [batch];
-    kv_len, agent int32 [batch]; B [N, r, n_kv*d]. ``workspace`` (uint8, zero-filled before first
-    use, left zero-filled by every call) is allocated zeroed when omitted."""
+    kv_len, agent int32 [batch]; B [N, r, n_kv*d]. ``agent[b]`` = ADAPTER_FREE (-1) gives request b
+    the adapter-free view (base cache alone, no LR term), so adapted and adapter-free requests
+    share one launch. ``workspace`` (uint8, lra_attn_decode_workspace_bytes() bytes, contents
+    need no initialisation) is allocated when omitted."""
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)

@@ -8,6 +8,8 @@
 #include "../../include/lra.h"
 #include "lra_kernels.h"
 
+static_assert(lra::kAdapterFree == LRA_ADAPTER_FREE, "adapter-free agent index");
+
 #define LRA_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -137,7 +139,8 @@ LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L
     if (L_C < 0 || L_P < 0) return fail(LRA_ERR_SHAPE, "L_C=%lld and L_P=%lld must be >= 0", (long long)L_C, (long long)L_P);
     if (L_P + L_C > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "L_P + L_C exceeds 2^31 - 1");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
-    if (agent < 0 || agent >= n_agents) return fail(LRA_ERR_INDEX, "agent=%d outside [0, %d)", agent, n_agents);
+    if (agent < lra::kAdapterFree || agent >= n_agents)
+        return fail(LRA_ERR_INDEX, "agent=%d outside [-1, %d)", agent, n_agents);
     if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");

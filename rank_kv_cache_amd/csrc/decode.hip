@@ -47,7 +47,7 @@ constexpr int kTile = 32;   // keys per wave tile
 
 __device__ __forceinline__ bool decode_request_ok(int64_t start, int32_t len, int32_t a, const DecodeParams& p) {
     return len >= 0 && int64_t(len) <= p.max_kv_len && start >= 0 && start + int64_t(len) <= p.kv_rows &&
-           a >= 0 && a < p.n_agents;
+           a >= kAdapterFree && a < p.n_agents;
 }
 
 // key of the tile held by lane group q in slot e
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     const int64_t lr_bytes = p.ld_vlr * int64_t(sizeof(T));
     const char* __restrict__ Kg = static_cast<const char*>(p.K) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
     const char* __restrict__ Vg = static_cast<const char*>(p.V) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
-    const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(a) * R) * int64_t(sizeof(T));
+    // an adapter-free request streams agent 0's columns (same rows, valid memory) through the same
+    // instructions; the combine drops that product
+    const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(max(a, 0)) * R) * int64_t(sizeof(T));
     const T* __restrict__ Qp = static_cast<const T*>(p.Q);
     const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
     const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
@@ -316,7 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 }
 
 // Merge of the splits of one (request b, query head h) by the log-sum-exp rule, then the
-// up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l, rounded to the output type.
+// up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l (O / l for an adapter-free request),
+// rounded to the output type.
 // Wave w merges the splits s = w, w+4, ... in one pass with a running maximum (lane c holds columns
 // c, c+64, c+128 of O | O_lr), so the loads of all its splits are independent of each other; the
 // four wave states are merged in LDS. The B slice is fetched first and used last. Requests with
@@ -343,11 +346,13 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
         for (int c = threadIdx.x; c < D; c += kThreads) Op[c] = fill;
         return;
     }
-    // column c of the agent's B slice for this KV head (threads c < D)
+    // column c of the agent's B slice for this KV head (threads c < D); the adapter-free view has
+    // no LR term
+    const bool adapted = a != kAdapterFree;
     const int64_t d_kv = int64_t(p.n_kv) * D;
-    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
+    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(max(a, 0)) * R * d_kv + int64_t(g) * D;
     float bcol[R];
-    if (threadIdx.x < D) {
+    if (threadIdx.x < D && adapted) {
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) bcol[rr] = to_f32<T>(Bp[int64_t(rr) * d_kv + threadIdx.x]);
     }
@@ -400,8 +405,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
     if (threadIdx.x < D) {
         const int c = threadIdx.x;
         float o = comb[c];
+        if (adapted) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) o = fmaf(comb[D + rr], bcol[rr], o);
+            for (int rr = 0; rr < R; ++rr) o = fmaf(comb[D + rr], bcol[rr], o);
+        }
         Op[c] = from_f32<T>(o / L);
     }
 }

@@ -7,6 +7,9 @@
 
 namespace lra {
 
+// agent index of the adapter-free view (double batching: attends the base cache alone, no LR term)
+constexpr int kAdapterFree = -1;
+
 struct DecodeParams {
     const void* Q;
     const void* K;

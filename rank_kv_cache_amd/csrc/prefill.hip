@@ -147,10 +147,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int wave_end = wave_rows ? int(p.L_P + i_max + 1) : 0;   // keys [0, wave_end) visible to some row
     const int full_end = int(p.L_P + i_min + 1);                   // keys [0, full_end) visible to every row
 
-    // ---- constants in LDS: B_agent slice (fp32), the ones / zero columns of the aux tiles
+    // ---- constants in LDS: B_agent slice (fp32; zero for the adapter-free view, which has no LR
+    // term), the ones / zero columns of the aux tiles
+    const bool adapted = p.agent != kAdapterFree;
     for (int idx = tid; idx < R * D; idx += kThreads) {
         const int rr = idx / D, c = idx - rr * D;
-        sh.b[idx] = to_f32<T>(Bp[(int64_t(p.agent) * R + rr) * kv_stride + int64_t(g) * D + c]);
+        sh.b[idx] = adapted ? to_f32<T>(Bp[(int64_t(p.agent) * R + rr) * kv_stride + int64_t(g) * D + c]) : 0.f;
     }
     for (int idx = tid; idx < 2 * kBK * (LDX - R); idx += kThreads) {
         const int buf = idx / (kBK * (LDX - R));
@@ -168,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
     // ---- tile fetch (registers) and store (LDS); keys past kv_end read row kv_end-1 (finite, P = 0)
     Vec<T, 8> kpre[KF], vpre[KF], lpre;
+    lpre.zero();   // the adapter-free view stages zero V_lr columns
     auto fetch = [&](int t) {
         const int kb = t * kBK;
 #pragma unroll
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             kpre[c].load(Kp + j * kv_stride + int64_t(g) * D + d0);
             vpre[c].load(Vp + j * kv_stride + int64_t(g) * D + d0);
         }
-        if (tid < LF) {
+        if (tid < LF && adapted) {
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
             const int64_t j = min(kb + key, kv_end - 1);

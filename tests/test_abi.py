@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 1
+    assert lra.abi_version() == 2
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -109,12 +109,18 @@ def prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=-1), E_UNSUP), (dict(d=32), E_UNSUP), (dict(r=32), E_UNSUP), (dict(n_q=3), E_SHAPE),
     (dict(L_C=-1), E_SHAPE), (dict(L_P=-1), E_SHAPE), (dict(L_P=1 << 31), E_SHAPE), (dict(agent=3), E_INDEX),
-    (dict(agent=-1), E_INDEX), (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=float("inf")), E_SHAPE),
+    (dict(agent=-2), E_INDEX), (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=float("inf")), E_SHAPE),
     (dict(scale=0.0), E_SHAPE), (dict(scale=-1.0), E_SHAPE),
     (dict(B=None), E_NULL), (dict(Vlr=None), E_NULL), (dict(O=P + 2), E_SHAPE),
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert prefill(**kw) == status
+
+
+def test_prefill_accepts_the_adapter_free_view():
+    # agent -1 passes the index check; the ld_vlr check that follows it then fails, so nothing launches
+    assert prefill(agent=lra.ADAPTER_FREE, ld_vlr=8) == E_SHAPE
+    assert prefill(agent=-2, ld_vlr=8) == E_INDEX
 
 
 def test_prefill_empty_chunk_is_a_no_op():

@@ -98,7 +98,7 @@ def test_decode_never_reads_outside_ranges():
 def test_decode_invalid_requests_give_nan_rows():
     s = W.LLAMA_SHAPE
     c = W.random_decode((103,), s, kv_lens=[50, 60, 40, 30, 20, 10], kv_starts=[0, 100, 0, 200, 10, 0], rows=300,
-                        agents=[0, 3, 1, -1, 2, 0])
+                        agents=[0, 3, 1, -2, 2, 0])
     kv_len = c.kv_len.copy()
     kv_start = c.kv_start.copy()
     kv_len[2] = 400            # beyond max_kv_len (passed as 100) and beyond the cache
@@ -109,6 +109,35 @@ def test_decode_invalid_requests_give_nan_rows():
     got = run_decode(cc, max_kv_len=100)
     assert np.all(np.isnan(got[[1, 2, 3, 4, 5]]))
     check(got[[0]], ref_decode(c, requests=[0]), "bf16")
+
+
+def test_decode_mixed_adapted_and_adapter_free():
+    """Double batching (PReCache paper, section 3): adapted requests and adapter-free ones (agent -1,
+    base cache alone) over shared rows in one launch."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((106,), s, kv_lens=[900, 900, 900, 130, 130, 1, 0], kv_starts=[0, 0, 0, 700, 700, 5, 0],
+                        rows=900, agents=[1, -1, 2, -1, 0, -1, -1], b_std=1.0)
+    say("decode mixed adapted / adapter-free")
+    ref = ref_decode(c)
+    for split in (0, 64, 256):
+        got = run_decode(c, keys_per_split=split)
+        check(got, ref, "bf16", f"split {split}")
+        assert np.all(got[6] == 0.0)
+
+
+def test_decode_adapter_free_reads_no_B():
+    """Adapter-free requests only, with B all NaN and agent 0's LR columns huge: B is never read and the
+    LR product of the streamed V_lr columns is dropped."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((107,), s, kv_lens=[500, 64, 1], kv_starts=[0, 400, 499], rows=500, agents=[-1, -1, -1])
+    lr = c.V_lr.as_f32()
+    lr[:, :s.rank] = 1.0e30
+    nanB = W.to_storage(np.full(c.B.shape, np.nan, np.float32), "bf16")
+    cc = W.DecodeBatch(s, c.Q, c.K, c.V, W.to_storage(lr, "bf16"), nanB, c.kv_start, c.kv_len, c.agent)
+    say("decode adapter-free, B = NaN")
+    got = run_decode(cc)
+    assert np.all(np.isfinite(got))
+    check(got, ref_decode(cc), "bf16")
 
 
 def test_decode_agent_signature():

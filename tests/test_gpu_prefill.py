@@ -48,6 +48,22 @@ def test_prefill_every_agent(agent):
     check(run_prefill(c), ref_prefill(c), "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_adapter_free_reads_neither_V_lr_nor_B(dtype):
+    """The adapter-free view (agent -1, PReCache paper, section 3) attends the base cache alone: with
+    V_lr and B all NaN the output still matches the oracle's base-only attention."""
+    s = W.LLAMA_SHAPE if dtype == "bf16" else W.Shape(n_q=8, n_kv=2, d_head=64, rank=16, n_agents=3, d_model=256,
+                                                      dtype="f32")
+    c = W.random_prefill((307, 0 if dtype == "bf16" else 1), s, L_P=250, L_C=140, agent=-1)
+    nan_lr = W.to_storage(np.full(c.V_lr.shape, np.nan, np.float32), dtype)
+    nan_B = W.to_storage(np.full(c.B.shape, np.nan, np.float32), dtype)
+    cc = W.PrefillCase(s, c.Q, c.K, c.V, nan_lr, nan_B, c.L_P, c.L_C, -1)
+    say(f"prefill adapter-free {dtype}")
+    got = run_prefill(cc)
+    assert np.all(np.isfinite(got))
+    check(got, ref_prefill(c), dtype)
+
+
 SHAPES = [
     # dtype, n_q, n_kv, d, r, L_P, L_C
     ("bf16", 32, 8, 128, 8, 0, 1), ("bf16", 32, 8, 128, 8, 0, 97), ("bf16", 32, 8, 128, 16, 63, 65),

@@ -31,6 +31,7 @@ from .lora_attention import (  # noqa: F401
     attention_probs,
     attention,
     attn_prefill,
+    attn_prefill_varlen,
     attn_decode,
     attn_factored,
     ADAPTER_FREE,

@@ -183,6 +183,30 @@ def attn_prefill(Q, K_base, V_base, V_lr, B, agent: int, L_P: int, scale: float,
     return attention(Q[rows], _f64(K_base)[:L], Va, L_P + rows, scale, heads)
 
 
+def attn_prefill_varlen(Q, K_base, V_base, V_lr, B, q_start, q_len, kv_start, kv_prefix, agents,
+                        scale: float) -> np.ndarray:
+    """Several causal chunked prefills in one batch: request b's q_len[b] queries are rows
+    q_start[b] .. of Q, its cache rows start at kv_start[b], it has kv_prefix[b] cached tokens
+    (L_P) before its chunk, and it attends with agent agents[b] (ADAPTER_FREE for the base view).
+
+    Each request is ``attn_prefill`` on its own rows (PReCache summary page: a new chunk L_C
+    follows the reused context L_P; requests are batched for concurrent serving). Returns an
+    array shaped like Q holding every request's output rows; rows of Q that no request covers
+    are zero.
+    """
+    Q = _f64(Q)
+    out = np.zeros_like(Q)
+    for b in range(len(q_len)):
+        n = int(q_len[b])
+        if n == 0:
+            continue
+        q0, k0, lp = int(q_start[b]), int(kv_start[b]), int(kv_prefix[b])
+        L = lp + n
+        out[q0:q0 + n] = attn_prefill(Q[q0:q0 + n], _f64(K_base[k0:k0 + L]), _f64(V_base[k0:k0 + L]),
+                                      _f64(V_lr[k0:k0 + L]), B, int(agents[b]), lp, scale)
+    return out
+
+
 def attn_decode(Q, K_base, V_base, V_lr, B, kv_start, kv_len, agents, scale: float,
                 requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> np.ndarray:
     """One new query per request over its key range [kv_start[b], kv_start[b] + kv_len[b]).

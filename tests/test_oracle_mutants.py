@@ -27,6 +27,7 @@ def _checks():
     yield lambda: pins.test_bruteforce_prefill(8, 2, 4, 4, 0, 7, 1)
     yield lambda: pins.test_bruteforce_decode_with_shared_and_empty_ranges()
     yield lambda: pins.test_bruteforce_decode_mixed_adapted_and_adapter_free()
+    yield lambda: pins.test_bruteforce_prefill_varlen_batch()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()

@@ -248,6 +248,31 @@ def test_bruteforce_decode_with_shared_and_empty_ranges():
     assert np.all(O[2] == 0.0)
 
 
+def test_bruteforce_prefill_varlen_batch():
+    """Several prefills in one batch (own query rows, cache offsets, L_P and agent; shared cache rows;
+    an empty chunk; the adapter-free view) against the brute force, request by request."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    rng = np.random.default_rng(913)
+    rows, q_rows = 30, 20
+    K = rng.standard_normal((rows, s.n_kv, s.d_head))
+    V = rng.standard_normal((rows, s.n_kv, s.d_head))
+    Vlr = rng.standard_normal((rows, s.n_agents * s.rank))
+    B = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Q = rng.standard_normal((q_rows, s.n_q, s.d_head))
+    q_start, q_len = [0, 5, 9, 9, 14], [5, 4, 0, 3, 6]
+    kv_start, kv_prefix = [0, 0, 7, 10, 2], [3, 12, 4, 0, 22]
+    agents = [1, oracle.ADAPTER_FREE, 0, 2, 0]
+    O = oracle.attn_prefill_varlen(Q, K, V, Vlr, B, q_start, q_len, kv_start, kv_prefix, agents, s.scale)
+    for b in range(5):
+        q0, n, k0, lp = q_start[b], q_len[b], kv_start[b], kv_prefix[b]
+        if n == 0:
+            continue
+        ref = bruteforce.prefill(Q[q0:q0 + n], K[k0:k0 + lp + n], V[k0:k0 + lp + n], Vlr[k0:k0 + lp + n], B,
+                                 agents[b], lp, s.scale)
+        assert rel_err(O[q0:q0 + n], ref) <= 1e-13, b
+    assert np.all(O[12:14] == 0.0)   # rows no request covers
+
+
 def test_bruteforce_decode_mixed_adapted_and_adapter_free():
     """Double batching (PReCache paper page, section 3): adapted and adapter-free requests over the
     same rows in one batch; the adapter-free ones (agent -1) see the base cache alone."""

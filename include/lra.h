@@ -135,6 +135,38 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Batched variable-length prefill: several causal chunked prefills (each as lra_attn_prefill) in
+ * one launch, for concurrent serving (PReCache summary page: each new chunk L_C follows its reused
+ * context L_P; requests are batched together). Request b owns
+ *   queries   rows q_start[b] .. q_start[b]+q_len[b]-1 of Q (and the same rows of O),
+ *             at absolute positions kv_prefix[b] .. kv_prefix[b]+q_len[b]-1,
+ *   cache     rows kv_start[b] .. kv_start[b]+kv_prefix[b]+q_len[b]-1 of K_base, V_base, V_lr
+ *             (its own L_P cached tokens followed by its chunk; requests may share cache rows),
+ *   agent     agent[b] in [0, n_agents), or -1 for the adapter-free view.
+ * Query i of request b attends its cache rows 0 .. kv_prefix[b]+i (relative to kv_start[b]).
+ *
+ * Q, O     (device) [q_rows x n_q x d_head]; rows no request covers are not written
+ * q_start  (device) [batch] int64, q_len (device) [batch] int32
+ * max_q_len (host) an upper bound on every q_len[b]; it sizes the launch
+ * K_base, V_base (device) [kv_rows x n_kv x d_head]; V_lr (device) [kv_rows x ld_vlr]
+ * kv_start (device) [batch] int64, kv_prefix (device) [batch] int32, agent (device) [batch] int32
+ * B        (device) [n_agents x rank x n_kv*d_head]
+ * A request with q_len[b] = 0 writes nothing; one whose query rows fall outside [0, q_rows) is
+ * skipped. One with q_len[b] > max_q_len, a cache range outside [0, kv_rows), kv_prefix[b]+q_len[b]
+ * >= 2^31 or an agent outside [-1, n_agents) gets NaN in all its output rows. Precision, the fp16
+ * range condition on V_base / V_lr, alignment and ld_vlr are as for lra_attn_prefill.
+ * batch = 0 or max_q_len = 0 enqueues nothing.
+ */
+int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,
+                            const int64_t* q_start, const int32_t* q_len, int64_t max_q_len,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            const void* V_lr, int64_t ld_vlr,
+                            const int64_t* kv_start, const int32_t* kv_prefix,
+                            const void* B, int32_t n_agents, const int32_t* agent,
+                            int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                            void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
  * (3)-(4) with L_C = 1): each (request, KV head, split) writes a partial (m, l, O, O_lr) in fp32 to
  * the workspace; a second kernel merges the partials of a (request, KV head) with the log-sum-exp

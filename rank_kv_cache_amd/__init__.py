@@ -19,9 +19,9 @@ import torch
 __all__ = [
     "LraError", "LIB_PATH", "abi_version", "status_str",
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
-    "lra_attn_prefill",
+    "lra_attn_prefill", "lra_attn_prefill_varlen",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
-    "LRA_F32", "LRA_BF16", "EXPORTED_SYMBOLS",
+    "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
@@ -42,6 +42,8 @@ _SIGNATURES = {
                                      _p, _sz, _p]),
     "lra_attn_prefill": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_attn_prefill_varlen": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p,
+                                           _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
@@ -182,6 +184,49 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
     _check(_lib.lra_attn_prefill(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
                                  V_lr.stride(0), _ptr(B), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(O),
                                  _stream(stream)), "lra_attn_prefill")
+    return O
+
+
+def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch.Tensor, max_q_len: int,
+                            K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                            kv_start: torch.Tensor, kv_prefix: torch.Tensor, B: torch.Tensor, agent: torch.Tensor,
+                            scale: float, O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Several causal chunked prefills in one launch. Request b: queries Q[q_start[b] : +q_len[b]] at
+    positions kv_prefix[b] .., cache rows kv_start[b] : +kv_prefix[b]+q_len[b], agent[b] (or
+    ADAPTER_FREE). Q, O [q_rows, n_q, d]; K_base, V_base [kv_rows, n_kv, d]; V_lr [kv_rows, ld];
+    q_start, kv_start int64 [batch]; q_len, kv_prefix, agent int32 [batch]; B [N, r, n_kv*d].
+    ``max_q_len`` bounds every q_len[b]. Rows of O that no request covers are left as they were
+    (O is allocated zeroed when omitted)."""
+    _same(Q, K_base, V_base, V_lr, B)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    q_rows, n_q, d = Q.shape
+    kv_rows, n_kv = K_base.shape[0], K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if K_base.shape[1:] != (n_kv, d) or V_base.shape != K_base.shape or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/B shapes disagree with Q")
+    if V_lr.shape[0] != kv_rows:
+        raise ValueError("V_lr must have as many rows as K_base")
+    for name, t, dt in (("q_start", q_start, torch.int64), ("q_len", q_len, torch.int32),
+                        ("kv_start", kv_start, torch.int64), ("kv_prefix", kv_prefix, torch.int32),
+                        ("agent", agent, torch.int32)):
+        if t.dtype != dt or t.dim() != 1 or t.device != Q.device or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous 1-d {dt} tensor on {Q.device}")
+    batch = q_start.shape[0]
+    if any(t.shape[0] != batch for t in (q_len, kv_start, kv_prefix, agent)):
+        raise ValueError("per-request tables disagree in length")
+    if O is None:
+        O = torch.zeros_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    if O.shape != Q.shape:
+        raise ValueError("O must have Q's shape")
+    _check(_lib.lra_attn_prefill_varlen(_dtype_code(Q), _ptr(Q), q_rows, batch, _ptr(q_start), _ptr(q_len), max_q_len,
+                                        _ptr(K_base), _ptr(V_base), kv_rows, _ptr(V_lr), V_lr.stride(0),
+                                        _ptr(kv_start), _ptr(kv_prefix), _ptr(B), n_agents, _ptr(agent),
+                                        n_q, n_kv, d, rank, scale, _ptr(O), _stream(stream)),
+           "lra_attn_prefill_varlen")
     return O
 
 

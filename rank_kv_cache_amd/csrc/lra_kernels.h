@@ -63,7 +63,22 @@ struct PrefillParams {
     int n_q, n_kv, G, d_head, rank, agent, n_agents;
     float scale;
     bool bf16;
+    // batched variable-length prefill: per-request tables (all null for one request given by
+    // L_C, L_P and agent above)
+    const int64_t* q_start;     // [batch] first row of the request's queries in Q and O
+    const int32_t* q_len;       // [batch] its L_C
+    const int64_t* kv_start;    // [batch] first row of its cache range in K, V and V_lr
+    const int32_t* kv_prefix;   // [batch] its L_P
+    const int32_t* agents;      // [batch] its agent (or kAdapterFree)
+    int64_t q_rows;             // rows of Q and O
+    int64_t kv_rows;            // rows of K, V and V_lr
+    int64_t max_q_len;          // bound on every q_len[b] (host value that sized the grid)
+    int batch;                  // requests in the grid
+    int max_pairs;              // workgroups per (request, KV head): enough for the longest chunk
 };
+
+// workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries
+int prefill_pairs(int64_t L_C, int G);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_precompute(const PrecomputeParams& p, hipStream_t stream);

@@ -97,26 +97,61 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int lane = tid & 63, wv = tid >> 6, n = lane & 15, q = lane >> 4;
     const int G = p.G;
     const int n_kv = p.n_kv;
-    const int64_t rows_total = p.L_C * G;
+    // workgroup -> (request, pair of row pieces, KV head); KV head = w mod n_kv keeps one head per
+    // XCD when n_kv = 8
+    const int per_req = p.max_pairs * n_kv;
+    const int req = int(blockIdx.x) / per_req;
+    const int wrem = int(blockIdx.x) - req * per_req;
+    const int g = wrem % n_kv;
+    const int pair = wrem / n_kv;
+    // The request's chunk: L_C queries (rows q0 .. of Q and O) at positions L_P .. L_P+L_C-1, over
+    // cache rows k0 .. k0+L_P+L_C-1. A batched request is checked here: one without rows that can
+    // be written is skipped; one with a bad cache range or agent, or longer than max_q_len, gets
+    // NaN in all its rows (spread over its workgroups) and nothing is read.
+    const int64_t kv_stride = int64_t(n_kv) * D;
+    const int64_t q_stride = int64_t(p.n_q) * D;
+    int64_t L_C = p.L_C, L_P = p.L_P, q0 = 0, k0 = 0;
+    int agent = p.agent;
+    if (p.q_len) {
+        L_C = p.q_len[req];
+        L_P = p.kv_prefix[req];
+        q0 = p.q_start[req];
+        k0 = p.kv_start[req];
+        agent = p.agents[req];
+        if (L_C <= 0 || q0 < 0 || q0 + L_C > p.q_rows) return;
+        const bool req_bad = L_C > p.max_q_len || L_P < 0 || k0 < 0 || k0 + L_P + L_C > p.kv_rows ||
+                             L_P + L_C > int64_t(INT32_MAX) || agent < kAdapterFree || agent >= p.n_agents;
+        if (req_bad) {   // workgroup-uniform
+            T* Ob = static_cast<T*>(p.O) + q0 * q_stride;
+            const int64_t n_el = L_C * G * D;   // this KV head's query rows of the request
+            for (int64_t idx = int64_t(pair) * kThreads + tid; idx < n_el; idx += int64_t(p.max_pairs) * kThreads) {
+                const int64_t r = idx / D;
+                const int c = int(idx - r * D);
+                const int64_t qi = r / G;
+                Ob[qi * q_stride + (int64_t(g) * G + (r - qi * G)) * D + c] = from_f32<T>(__uint_as_float(0x7fc00000u));
+            }
+            return;
+        }
+    }
+    const int64_t rows_total = L_C * G;
     // The rows of one KV head are cut into pieces of kPieceRows; the two halves of workgroup `pair`
     // take pieces pair and n_pieces-1-pair, a short and a long causal key range, so workgroups
     // (and SIMDs, each of which runs one wave of each half) get about the same number of
     // query-key pairs. With an odd count the middle workgroup's second half has no rows.
     const int n_pieces = int((rows_total + kPieceRows - 1) / kPieceRows);
-    const int g = blockIdx.x % n_kv;   // KV head = w mod n_kv keeps one head per XCD when n_kv = 8
-    const int pair = int(blockIdx.x / n_kv);
+    if (pair >= (n_pieces + 1) / 2) return;   // a shorter chunk than the longest in the batch
     const int half = wv / (kWaves / 2);
     const int piece = half ? n_pieces - 1 - pair : pair;
     const bool half_empty = half && piece == pair;
     const int64_t R0 = int64_t(piece) * kPieceRows + (wv % (kWaves / 2)) * (16 * MT);   // wave's first row
     const bool wave_rows = !half_empty && R0 < rows_total;
 
-    const T* __restrict__ Qp = static_cast<const T*>(p.Q);
-    const T* __restrict__ Kp = static_cast<const T*>(p.K);
-    const T* __restrict__ Vp = static_cast<const T*>(p.V);
-    const T* __restrict__ Lp = static_cast<const T*>(p.Vlr);
+    const T* __restrict__ Qp = static_cast<const T*>(p.Q) + q0 * q_stride;
+    const T* __restrict__ Kp = static_cast<const T*>(p.K) + k0 * kv_stride;
+    const T* __restrict__ Vp = static_cast<const T*>(p.V) + k0 * kv_stride;
+    const T* __restrict__ Lp = static_cast<const T*>(p.Vlr) + k0 * p.ld_vlr;
     const T* __restrict__ Bp = static_cast<const T*>(p.B);
-    const int64_t kv_stride = int64_t(n_kv) * D;
+    T* __restrict__ Op = static_cast<T*>(p.O) + q0 * q_stride;
 
     // ---- this lane's query rows (B operand column n of each 16-row tile)
     int qpos[MT];   // absolute positions (< 2^31, checked on the host)
@@ -128,8 +163,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const int64_t rc = min(r, rows_total - 1);
         const int64_t qi = rc / G;
         const int qh = int(rc - qi * G);
-        qpos[mt] = int(p.L_P + qi);
-        const T* qp = Qp + (qi * p.n_q + int64_t(g) * G + qh) * D + 8 * q;
+        qpos[mt] = int(L_P + qi);
+        const T* qp = Qp + qi * q_stride + (int64_t(g) * G + qh) * D + 8 * q;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             if (ok) qf[mt][i].load(qp + 32 * i);
@@ -140,19 +175,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // ---- key ranges: the workgroup stages keys [0, kv_end) (visible to some row of its long
     // piece); a wave computes the blocks below its own end and masks from its full_end on
     const int64_t heavy_last = min<int64_t>(rows_total, int64_t(n_pieces - pair) * kPieceRows) - 1;
-    const int kv_end = int(p.L_P + heavy_last / G + 1);
+    const int kv_end = int(L_P + heavy_last / G + 1);
     const int n_tiles = (kv_end + kBK - 1) / kBK;
     const int64_t i_min = min(R0, rows_total - 1) / G;
-    const int64_t i_max = min<int64_t>(p.L_C - 1, (R0 + 16 * MT - 1) / G);
-    const int wave_end = wave_rows ? int(p.L_P + i_max + 1) : 0;   // keys [0, wave_end) visible to some row
-    const int full_end = int(p.L_P + i_min + 1);                   // keys [0, full_end) visible to every row
+    const int64_t i_max = min<int64_t>(L_C - 1, (R0 + 16 * MT - 1) / G);
+    const int wave_end = wave_rows ? int(L_P + i_max + 1) : 0;   // keys [0, wave_end) visible to some row
+    const int full_end = int(L_P + i_min + 1);                   // keys [0, full_end) visible to every row
 
     // ---- constants in LDS: B_agent slice (fp32; zero for the adapter-free view, which has no LR
     // term), the ones / zero columns of the aux tiles
-    const bool adapted = p.agent != kAdapterFree;
+    const bool adapted = agent != kAdapterFree;
     for (int idx = tid; idx < R * D; idx += kThreads) {
         const int rr = idx / D, c = idx - rr * D;
-        sh.b[idx] = adapted ? to_f32<T>(Bp[(int64_t(p.agent) * R + rr) * kv_stride + int64_t(g) * D + c]) : 0.f;
+        sh.b[idx] = adapted ? to_f32<T>(Bp[(int64_t(agent) * R + rr) * kv_stride + int64_t(g) * D + c]) : 0.f;
     }
     for (int idx = tid; idx < 2 * kBK * (LDX - R); idx += kThreads) {
         const int buf = idx / (kBK * (LDX - R));
@@ -186,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
             const int64_t j = min(kb + key, kv_end - 1);
-            lpre.load(Lp + j * p.ld_vlr + int64_t(p.agent) * R + r0);
+            lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * R + r0);
         }
     };
     // 8 values of one key's row as fp16 (bf16 inputs; exact within the fp16 range) or fp32
@@ -383,7 +418,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     if (sizeof(T) == 2 && !(vmax <= kF16Max)) sh.range_bad = 1;
     __syncthreads();
     const bool poison = sh.range_bad != 0;
-    T* __restrict__ Op = static_cast<T*>(p.O);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         // aux row 4q'+j of tile x lives in lane (q', n), register j: gather them for row n
@@ -395,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         if (!wave_rows || r >= rows_total) continue;
         const int64_t qi = r / G;
         const int qh = int(r - qi * G);
-        T* orow = Op + (qi * p.n_q + int64_t(g) * G + qh) * D;
+        T* orow = Op + qi * q_stride + (int64_t(g) * G + qh) * D;
         const float inv = poison ? __uint_as_float(0x7fc00000u) : 1.f / l;   // quiet NaN by its bits
         // lane (q, n) holds O^T rows 4q+j of tile dt: d = 16dt + 4q + j
 #pragma unroll
@@ -420,10 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
 template <typename T, int D, int R>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
-    const int64_t rows = p.L_C * p.G;
-    const int64_t n_pieces = (rows + kPieceRows - 1) / kPieceRows;
-    const int64_t n_pairs = (n_pieces + 1) / 2;
-    hipLaunchKernelGGL((prefill_kernel<T, D, R>), dim3(unsigned(n_pairs * p.n_kv)), dim3(kThreads), 0, stream, p);
+    const int64_t grid = int64_t(p.batch) * p.max_pairs * p.n_kv;
+    hipLaunchKernelGGL((prefill_kernel<T, D, R>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -437,6 +469,11 @@ hipError_t dispatch_d(const PrefillParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int prefill_pairs(int64_t L_C, int G) {
+    const int64_t n_pieces = (L_C * G + kPieceRows - 1) / kPieceRows;
+    return int((n_pieces + 1) / 2);
+}
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     return p.bf16 ? dispatch_d<bf16>(p, stream) : dispatch_d<float>(p, stream);

@@ -123,6 +123,34 @@ def test_prefill_accepts_the_adapter_free_view():
     assert prefill(agent=-2, ld_vlr=8) == E_INDEX
 
 
+def prefill_varlen(**kw):
+    a = dict(dtype=1, Q=P, q_rows=100, batch=3, q_start=P, q_len=P, max_q_len=64, K=P, V=P, kv_rows=500, Vlr=P,
+             ld_vlr=24, kv_start=P, kv_prefix=P, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
+             O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_prefill_varlen(a["dtype"], a["Q"], a["q_rows"], a["batch"], a["q_start"], a["q_len"],
+                                            a["max_q_len"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"],
+                                            a["kv_start"], a["kv_prefix"], a["B"], a["n_agents"], a["agent"], a["n_q"],
+                                            a["n_kv"], a["d"], a["r"], a["scale"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=-1), E_UNSUP), (dict(d=32), E_UNSUP), (dict(r=32), E_UNSUP), (dict(n_q=3), E_SHAPE),
+    (dict(batch=-1), E_SHAPE), (dict(q_rows=-1), E_SHAPE), (dict(kv_rows=-1), E_SHAPE), (dict(max_q_len=-1), E_SHAPE),
+    (dict(max_q_len=1 << 31), E_SHAPE), (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE),
+    (dict(scale=0.0), E_SHAPE), (dict(scale=float("nan")), E_SHAPE),
+    (dict(q_start=None), E_NULL), (dict(q_len=None), E_NULL), (dict(kv_start=None), E_NULL),
+    (dict(kv_prefix=None), E_NULL), (dict(agent=None), E_NULL), (dict(B=None), E_NULL), (dict(O=P + 2), E_SHAPE),
+])
+def test_prefill_varlen_rejects_bad_arguments(kw, status):
+    assert prefill_varlen(**kw) == status
+
+
+def test_prefill_varlen_empty_batch_is_a_no_op():
+    assert prefill_varlen(batch=0, Q=None, O=None, q_start=None) == OK
+    assert prefill_varlen(max_q_len=0, Q=None, O=None) == OK
+
+
 def test_prefill_empty_chunk_is_a_no_op():
     assert prefill(L_C=0, Q=None, O=None) == OK
 

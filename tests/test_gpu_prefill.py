@@ -6,7 +6,7 @@ import torch
 import oracle
 import rank_kv_cache_amd as lra
 import workloads as W
-from tests.gpu_util import check, dev, host64, say
+from tests.gpu_util import check, dev, dev_idx, host64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,29 @@ def ref_prefill(c: W.PrefillCase, agent=None, rows=None, heads=None):
                                W.HostTensor(c.V.data[:L], c.V.dtype).as_f64(),
                                W.HostTensor(c.V_lr.data[:L], c.V_lr.dtype).as_f64(), c.B.as_f64(),
                                c.agent if agent is None else agent, c.L_P, c.shape.scale, rows=rows, heads=heads)
+
+
+def run_prefill_varlen(c: W.PrefillBatch, max_q_len=None, O=None):
+    s = c.shape
+    O = lra.lra_attn_prefill_varlen(dev(c.Q), dev_idx(c.q_start, torch.int64), dev_idx(c.q_len, torch.int32),
+                                    c.max_q_len if max_q_len is None else max_q_len, dev(c.K), dev(c.V), dev(c.V_lr),
+                                    dev_idx(c.kv_start, torch.int64), dev_idx(c.kv_prefix, torch.int32), dev(c.B),
+                                    dev_idx(c.agents, torch.int32), s.scale, O=O)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_prefill_varlen(c: W.PrefillBatch):
+    return oracle.attn_prefill_varlen(c.Q.as_f64(), c.K.as_f64(), c.V.as_f64(), c.V_lr.as_f64(), c.B.as_f64(),
+                                      c.q_start, c.q_len, c.kv_start, c.kv_prefix, c.agents, c.shape.scale)
+
+
+def covered_rows(c: W.PrefillBatch, only=None):
+    rows = []
+    for b in range(len(c.q_len)):
+        if only is None or b in only:
+            rows += list(range(int(c.q_start[b]), int(c.q_start[b]) + int(c.q_len[b])))
+    return np.asarray(rows, np.int64)
 
 
 def test_llama_prefill_full_size_sampled_rows():
@@ -158,3 +181,81 @@ def test_prefill_value_beyond_fp16_range_gives_nan_rows_of_that_head_only():
     good = [h for h in range(s.n_q) if h not in bad]
     assert np.all(np.isnan(got[:, bad]))
     check(got[:, good], ref_prefill(cc, heads=good), "bf16")
+
+
+# ------------------------------------------------------------------------------ batched variable length
+def test_prefill_varlen_batch():
+    """Six requests in one launch: own L_P / L_C / agent (one adapter-free, one empty chunk, one single
+    query, one long chunk), ragged tails; uncovered rows of O stay as they were."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_batch((320,), s, [(300, 200, 1), (0, 64, -1), (1000, 1, 2), (77, 130, 0), (5, 0, 1),
+                                          (900, 513, 2)])
+    say("prefill varlen batch of 6")
+    got = run_prefill_varlen(c)
+    ref = ref_prefill_varlen(c)
+    rows = covered_rows(c)
+    check(got[rows], ref[rows], "bf16")
+    uncovered = np.setdiff1d(np.arange(c.Q.shape[0]), rows)
+    assert np.all(got[uncovered] == 0.0)
+
+
+def test_prefill_varlen_shared_cache_rows_and_fp32():
+    """Requests whose cache ranges overlap (agents sharing base rows), fp32, GQA 2:1, r = 16."""
+    s = W.Shape(n_q=8, n_kv=4, d_head=64, rank=16, n_agents=3, d_model=256, dtype="f32")
+    c = W.random_prefill_batch((321,), s, [(40, 30, 0), (40, 30, 2), (10, 60, 1), (0, 100, -1)],
+                               kv_starts=[0, 0, 20, 5])
+    say("prefill varlen shared cache rows fp32")
+    got = run_prefill_varlen(c)
+    rows = covered_rows(c)
+    check(got[rows], ref_prefill_varlen(c)[rows], "f32")
+
+
+def test_prefill_varlen_matches_single_request_calls():
+    """Each request of the batch gives the same bits as lra_attn_prefill on that request alone."""
+    s = W.LLAMA_SHAPE
+    reqs = [(200, 97, 0), (33, 128, 1), (0, 1, 2)]
+    c = W.random_prefill_batch((322,), s, reqs)
+    say("prefill varlen vs single calls")
+    got = run_prefill_varlen(c)
+    Q, K, V, L, B = dev(c.Q), dev(c.K), dev(c.V), dev(c.V_lr), dev(c.B)
+    for b, (lp, lc, a) in enumerate(reqs):
+        q0, k0 = int(c.q_start[b]), int(c.kv_start[b])
+        one = lra.lra_attn_prefill(Q[q0:q0 + lc].contiguous(), lp, K[k0:k0 + lp + lc].contiguous(),
+                                   V[k0:k0 + lp + lc].contiguous(), L[k0:k0 + lp + lc].contiguous(), B, a, s.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(host64(one), got[q0:q0 + lc]), b
+
+
+def test_prefill_varlen_invalid_requests_give_nan_rows():
+    """A cache range past kv_rows, an agent outside [-1, N), a chunk longer than max_q_len: NaN in every
+    row of that request; the valid request beside them is exact."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_batch((323,), s, [(100, 50, 0), (60, 40, 1), (30, 20, 3), (10, 300, 1)])
+    kv_start = c.kv_start.copy()
+    kv_start[1] = c.K.shape[0] - 50          # range runs past the cache
+    cc = W.PrefillBatch(s, c.Q, c.K, c.V, c.V_lr, c.B, c.q_start, c.q_len, kv_start, c.kv_prefix, c.agents)
+    say("prefill varlen invalid requests")
+    got = run_prefill_varlen(cc, max_q_len=64)  # request 3 (300 queries) exceeds it
+    for b in (1, 2, 3):
+        assert np.all(np.isnan(got[covered_rows(cc, only=[b])])), b
+    rows = covered_rows(cc, only=[0])
+    first = W.PrefillBatch(s, c.Q, c.K, c.V, c.V_lr, c.B, c.q_start[:1], c.q_len[:1], c.kv_start[:1],
+                           c.kv_prefix[:1], c.agents[:1])
+    check(got[rows], ref_prefill_varlen(first)[rows], "bf16")
+
+
+def test_prefill_varlen_never_reads_outside_ranges():
+    """Cache rows outside every request's range and query rows outside every chunk hold NaN."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_batch((324,), s, [(129, 70, 2), (0, 33, 0), (64, 64, -1)], gap=5)
+    used = np.zeros(c.K.shape[0], bool)
+    for b in range(3):
+        used[int(c.kv_start[b]):int(c.kv_start[b]) + int(c.kv_prefix[b]) + int(c.q_len[b])] = True
+    for t in (c.K, c.V, c.V_lr):
+        W.fill_rows(t, np.where(~used)[0], float("nan"))
+    rows = covered_rows(c)
+    W.fill_rows(c.Q, np.setdiff1d(np.arange(c.Q.shape[0]), rows), float("nan"))
+    say("prefill varlen NaN outside ranges")
+    got = run_prefill_varlen(c)
+    assert np.all(np.isfinite(got[rows]))
+    check(got[rows], ref_prefill_varlen(c)[rows], "bf16")

@@ -215,6 +215,27 @@ class PrefillCase:
 
 
 @dataclass
+class PrefillBatch:
+    """Several chunked prefills in one launch: request b's queries are rows q_start[b] .. of Q, its
+    cache rows start at kv_start[b] (kv_prefix[b] cached tokens, then its chunk of q_len[b])."""
+    shape: Shape
+    Q: HostTensor            # [q_rows, n_q, d]
+    K: HostTensor            # [kv_rows, n_kv, d]
+    V: HostTensor            # [kv_rows, n_kv, d]
+    V_lr: HostTensor         # [kv_rows, n_agents * rank]
+    B: HostTensor            # [n_agents, rank, n_kv * d]
+    q_start: np.ndarray      # int64 [batch]
+    q_len: np.ndarray        # int32 [batch]
+    kv_start: np.ndarray     # int64 [batch]
+    kv_prefix: np.ndarray    # int32 [batch]
+    agents: np.ndarray       # int32 [batch]
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_len.max()) if len(self.q_len) else 0
+
+
+@dataclass
 class PrecomputeCase:
     shape: Shape
     X: HostTensor            # [T, d_model]
@@ -402,6 +423,34 @@ def random_prefill(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int 
     B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
     Q = normal(key + (T_Q,), (L_C, s.n_q, s.d_head), 1.0, s.dtype)
     return PrefillCase(s, Q, K, V, V_lr, B, L_P, L_C, agent)
+
+
+def random_prefill_batch(key: Sequence[int], s: Shape, requests: Sequence[Tuple[int, int, int]],
+                         gap: int = 3, kv_starts: Optional[Sequence[int]] = None, b_std: float = 0.05) -> PrefillBatch:
+    """requests = [(L_P, L_C, agent), ...]. Query rows and (unless kv_starts is given) cache ranges are
+    laid out one after the other with `gap` uncovered rows before each."""
+    key = tuple(key)
+    q_start, kv_start_auto = [], []
+    q, k = 0, 0
+    for (lp, lc, _) in requests:
+        q += gap
+        k += gap
+        q_start.append(q)
+        kv_start_auto.append(k)
+        q += lc
+        k += lp + lc
+    kv_start = list(kv_starts) if kv_starts is not None else kv_start_auto
+    kv_rows = max([ks + lp + lc for ks, (lp, lc, _) in zip(kv_start, requests)] + [k]) + gap
+    q_rows = q + gap
+    K = normal(key + (T_K,), (kv_rows, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (kv_rows, s.n_kv, s.d_head), 1.0, s.dtype)
+    V_lr = normal(key + (T_VLR,), (kv_rows, s.n_agents * s.rank), 1.0, s.dtype)
+    B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
+    Q = normal(key + (T_Q,), (q_rows, s.n_q, s.d_head), 1.0, s.dtype)
+    return PrefillBatch(s, Q, K, V, V_lr, B, np.asarray(q_start, np.int64),
+                        np.asarray([lc for (_, lc, _) in requests], np.int32), np.asarray(kv_start, np.int64),
+                        np.asarray([lp for (lp, _, _) in requests], np.int32),
+                        np.asarray([a for (_, _, a) in requests], np.int32))
 
 
 def random_precompute(key: Sequence[int], s: Shape, T: int) -> PrecomputeCase:

@@ -33,6 +33,8 @@ from .lora_attention import (  # noqa: F401
     attn_prefill,
     attn_prefill_varlen,
     attn_decode,
+    attn_decode_paged,
+    gather_pages,
     attn_factored,
     ADAPTER_FREE,
 )

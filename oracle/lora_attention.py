@@ -233,6 +233,32 @@ def attn_decode(Q, K_base, V_base, V_lr, B, kv_start, kv_len, agents, scale: flo
     return np.stack(out) if out else np.zeros((0, len(heads), d))
 
 
+def gather_pages(pages, block_table_row, n_rows: int) -> np.ndarray:
+    """Logical rows 0 .. n_rows-1 of a paged cache: row j lives in page block_table_row[j // P] at
+    offset j % P (pages: [n_pages, P, ...]). The layout of concurrent serving (the pages' vLLM
+    deployments), written out as a plain gather."""
+    pages = np.asarray(pages)
+    P = pages.shape[1]
+    idx = np.arange(n_rows)
+    return pages[np.asarray(block_table_row, np.int64)[idx // P], idx % P]
+
+
+def attn_decode_paged(Q, K_pages, V_pages, Vlr_pages, B, block_table, kv_len, agents, scale: float,
+                      requests: Optional[Sequence[int]] = None) -> np.ndarray:
+    """``attn_decode`` over a paged cache: request b's rows 0 .. kv_len[b]-1 are gathered from the
+    pages its block-table row names, then attended as one contiguous range."""
+    Q = _f64(Q)
+    requests = range(Q.shape[0]) if requests is None else requests
+    out = []
+    for b in requests:
+        n = int(kv_len[b])
+        K = _f64(gather_pages(K_pages, block_table[b], n))
+        V = _f64(gather_pages(V_pages, block_table[b], n))
+        L = _f64(gather_pages(Vlr_pages, block_table[b], n))
+        out.append(attn_decode(Q[b:b + 1], K, V, L, B, [0], [n], [agents[b]], scale)[0])
+    return np.stack(out) if out else np.zeros((0,) + Q.shape[1:])
+
+
 def attn_factored(Q, K, V_base, V_lr, B, agent: int, q_pos, scale: float) -> np.ndarray:
     """Attend-then-expand: ``P V_base + (P V_lr[:, agent cols]) B_agent`` per head.
 

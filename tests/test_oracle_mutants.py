@@ -28,6 +28,7 @@ def _checks():
     yield lambda: pins.test_bruteforce_decode_with_shared_and_empty_ranges()
     yield lambda: pins.test_bruteforce_decode_mixed_adapted_and_adapter_free()
     yield lambda: pins.test_bruteforce_prefill_varlen_batch()
+    yield lambda: pins.test_bruteforce_decode_paged_cache()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()
@@ -72,6 +73,9 @@ def _mut_adapter_free_reads_agent_zero(V_base, V_lr, B, agent):
 
 
 MUTANTS = {
+    "page_offset_off_by_one": ("gather_pages", lambda pages, row, n: np.asarray(pages)[
+        np.asarray(row, np.int64)[np.arange(n) // np.asarray(pages).shape[1]],
+        (np.arange(n) + 1) % np.asarray(pages).shape[1]]),
     "adapter_free_reads_agent_zero": ("agent_values", _mut_adapter_free_reads_agent_zero),
     "head_map_interleaved": ("kv_head_of", lambda h, group: h % group),
     "head_map_coarse": ("kv_head_of", lambda h, group: h // (2 * group)),

@@ -273,6 +273,30 @@ def test_bruteforce_prefill_varlen_batch():
     assert np.all(O[12:14] == 0.0)   # rows no request covers
 
 
+def test_bruteforce_decode_paged_cache():
+    """A paged cache (pages of 4 rows, shuffled, one page shared by two requests as a common prefix)
+    against the brute force on the same rows laid out contiguously by hand."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    rng = np.random.default_rng(914)
+    P, n_pages = 4, 9
+    Kp = rng.standard_normal((n_pages, P, s.n_kv, s.d_head))
+    Vp = rng.standard_normal((n_pages, P, s.n_kv, s.d_head))
+    Lp = rng.standard_normal((n_pages, P, s.n_agents * s.rank))
+    B = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Q = rng.standard_normal((3, s.n_q, s.d_head))
+    table = np.array([[5, 2, 7, 0], [5, 8, 1, 0], [3, 0, 0, 0]])
+    kv_len, agents = [14, 9, 0], [2, oracle.ADAPTER_FREE, 1]
+    O = oracle.attn_decode_paged(Q, Kp, Vp, Lp, B, table, kv_len, agents, s.scale)
+    for b in range(2):
+        pages = table[b][:(kv_len[b] + P - 1) // P]
+        K = np.concatenate([Kp[i] for i in pages])[:kv_len[b]]
+        V = np.concatenate([Vp[i] for i in pages])[:kv_len[b]]
+        L = np.concatenate([Lp[i] for i in pages])[:kv_len[b]]
+        ref = bruteforce.decode(Q[b:b + 1], K, V, L, B, [0], [kv_len[b]], [agents[b]], s.scale)
+        assert rel_err(O[b:b + 1], ref) <= 1e-13, b
+    assert np.all(O[2] == 0.0)
+
+
 def test_bruteforce_decode_mixed_adapted_and_adapter_free():
     """Double batching (PReCache paper page, section 3): adapted and adapter-free requests over the
     same rows in one batch; the adapter-free ones (agent -1) see the base cache alone."""

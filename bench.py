@@ -170,7 +170,32 @@ def bench_long_decode(args, torch, lra, W, out):
                    "parallelism": "none"},
     }
     out["_long_decode_case"] = c
-    del Q, K, V, L, B, O, ws
+
+    # the same bytes as a paged cache: 32-row pages, the block table a seeded permutation of all pages
+    P = 32
+    n_pages = K.shape[0] // P
+    blocks = int(c.kv_len[0]) // P
+    g = torch.Generator(device="cpu")
+    g.manual_seed(42)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(c.batch, blocks).cuda()
+    Kp = K.view(n_pages, P, s.n_kv, s.d_head)
+    Vp = V.view(n_pages, P, s.n_kv, s.d_head)
+    Lp = L.view(n_pages, P, L.shape[1])
+    split_p = lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P)
+    ws_p = torch.empty(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len,
+                                                           split_p), dtype=torch.uint8, device="cuda")
+
+    def step_paged():
+        lra.lra_attn_decode_paged(Q, Kp, Vp, Lp, table, kl, c.max_kv_len, B, ag, s.scale, 0, ws_p, O)
+
+    log("[bench] paged decode 16 x 66400, 32-row pages")
+    ms_p = time_launches(step_paged, args.steps, args.warmup, torch)
+    gbs_p = nbytes / (ms_p * 1e-3) / 1e9
+    out["decode_paged_llama_b16_L66400_P32"] = {
+        "ms": round(ms_p, 4), "gbs": round(gbs_p, 1), "bytes": nbytes, "frac": round(gbs_p / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "page_size": P, "n_pages": n_pages, "keys_per_split": split_p,
+        "block_table": "seeded permutation of all pages"}
+    del Q, K, V, L, B, O, ws, ws_p, Kp, Vp, Lp, table
     torch.cuda.empty_cache()
 
 

@@ -203,6 +203,38 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
 /* Keys per split the library picks for these sizes when keys_per_split = 0. */
 int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len);
 
+/* ------------------------------------------------------------------------------------------------
+ * Batched decode over a paged cache, for concurrent serving (the pages' serving experiments run
+ * under vLLM, whose KV cache is paged): lra_attn_decode with request b's logical rows
+ * 0 .. kv_len[b]-1 spread over fixed-size pages. Logical row j of request b is row j % P of page
+ * block_table[b * max_blocks + j / P]. Requests may name the same pages (a shared prefix).
+ *
+ * K_pages, V_pages (device) [n_pages x P x n_kv x d_head]
+ * Vlr_pages (device) [n_pages x P x ld_vlr], the LR cache rows of the same tokens
+ * page_size P: a power of two in [32, 65536]
+ * block_table (device) [batch x max_blocks] int32; entries past a request's last page are unread
+ * kv_len, agent (device) [batch] int32; agent[b] in [0, n_agents) or -1 (adapter-free view)
+ * max_kv_len (host) an upper bound on every kv_len[b], at most max_blocks * P
+ * keys_per_split  0 for lra_attn_decode_paged_default_split(), or a multiple of 64 that spans at
+ *          most 64 pages (ceil(keys_per_split / P) + 1 <= 64), else LRA_ERR_UNSUPPORTED
+ * workspace(device) lra_attn_decode_workspace_bytes(..., keys_per_split) bytes, with the split the
+ *          call uses (the paged default split when keys_per_split = 0); no initialisation needed
+ * A request whose pages include an id outside [0, n_pages) gets NaN in every output element and
+ * reads page 0 in place of the bad ones. Everything else is as for lra_attn_decode.
+ */
+int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
+                          const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                          int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* kv_len, int64_t max_kv_len,
+                          const void* B, int32_t n_agents, const int32_t* agent,
+                          int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                          int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                          void* O, void* stream);
+
+/* Keys per split lra_attn_decode_paged uses when keys_per_split = 0 (0 for an unsupported P). */
+int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ __all__ = [
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
     "lra_attn_prefill", "lra_attn_prefill_varlen",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
+    "lra_attn_decode_paged", "lra_attn_decode_paged_default_split",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
@@ -48,6 +49,9 @@ _SIGNATURES = {
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+    "lra_attn_decode_paged": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _p, _i32, _p, _i64, _p, _i32,
+                                         _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
+    "lra_attn_decode_paged_default_split": (_i32, [_i32, _i32, _i64, _i32]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -278,4 +282,51 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O
+
+
+# ---------------------------------------------------------------------------------- paged decode
+def lra_attn_decode_paged_default_split(batch: int, n_kv: int, max_kv_len: int, page_size: int) -> int:
+    return int(_lib.lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, page_size))
+
+
+def lra_attn_decode_paged(Q: torch.Tensor, K_pages: torch.Tensor, V_pages: torch.Tensor, Vlr_pages: torch.Tensor,
+                          block_table: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int, B: torch.Tensor,
+                          agent: torch.Tensor, scale: float, keys_per_split: int = 0,
+                          workspace: Optional[torch.Tensor] = None, O: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """lra_attn_decode over a paged cache: request b's row j is row j % P of page block_table[b, j // P].
+
+    Q [batch, n_q, d]; K_pages, V_pages [n_pages, P, n_kv, d]; Vlr_pages [n_pages, P, ld];
+    block_table int32 [batch, max_blocks]; kv_len, agent int32 [batch]; B [N, r, n_kv*d]."""
+    _same(Q, K_pages, V_pages, Vlr_pages, B)
+    for name, t in (("Q", Q), ("K_pages", K_pages), ("V_pages", V_pages), ("B", B)):
+        _dense(name, t)
+    batch, n_q, d = Q.shape
+    n_pages, P, n_kv = K_pages.shape[0], K_pages.shape[1], K_pages.shape[2]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if V_pages.shape != K_pages.shape or K_pages.shape[3] != d or B.shape[2] != n_kv * d:
+        raise ValueError("K_pages/V_pages/B shapes disagree with Q")
+    if Vlr_pages.dim() != 3 or Vlr_pages.shape[:2] != (n_pages, P) or Vlr_pages.stride(2) != 1 or \
+            Vlr_pages.stride(0) != P * Vlr_pages.stride(1):
+        raise ValueError("Vlr_pages must be [n_pages, P, ld] with rows of one page adjacent")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous() or \
+            block_table.shape[0] != batch:
+        raise TypeError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
+    for name, t in (("kv_len", kv_len), ("agent", agent)):
+        if t.dtype != torch.int32 or t.shape != (batch,) or not t.is_contiguous() or t.device != Q.device:
+            raise TypeError(f"{name} must be a contiguous int32 [batch] tensor on {Q.device}")
+    split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_decode_paged(_dtype_code(Q), _ptr(Q), batch, _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages),
+                                      n_pages, P, Vlr_pages.stride(1), _ptr(block_table), block_table.shape[1],
+                                      _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank,
+                                      scale, keys_per_split, _ptr(workspace), workspace.numel(), _ptr(O),
+                                      _stream(stream)), "lra_attn_decode_paged")
     return O

@@ -1,5 +1,6 @@
 // C ABI of liblra: host-side validation, workspace layout and dispatch to the gfx950 kernels.
 // Every failing check returns before anything is enqueued; see include/lra.h for the contract.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -205,6 +206,70 @@ LRA_EXPORT size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, in
     if (keys_per_split < 0 || keys_per_split % 64 != 0) return 0;
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
     return decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk).total;
+}
+
+namespace {
+// keys per split for a paged cache: the library's choice, capped so a split spans at most 64 pages
+int paged_cap(int page_size) { return std::max(128, int(std::min<int64_t>(int64_t(63) * page_size, 1 << 30) / 128 * 128)); }
+bool paged_split_fits(int chunk, int page_size) { return (int64_t(chunk) + page_size - 1) / page_size + 1 <= 64; }
+}  // namespace
+
+LRA_EXPORT int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size) {
+    if (page_size < 32 || (page_size & (page_size - 1)) != 0) return 0;
+    return std::min(lra::decode_default_chunk(batch, n_kv, max_kv_len), paged_cap(page_size));
+}
+
+LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
+                                     const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                                     int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                                     const int32_t* block_table, int32_t max_blocks,
+                                     const int32_t* kv_len, int64_t max_kv_len,
+                                     const void* B, int32_t n_agents, const int32_t* agent,
+                                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                     void* O, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
+    if (page_size < 32 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0)
+        return fail(LRA_ERR_UNSUPPORTED, "page_size=%d must be a power of two in [32, 65536]", page_size);
+    if (n_pages <= 0 || max_blocks <= 0) return fail(LRA_ERR_SHAPE, "n_pages and max_blocks must be positive");
+    if (max_kv_len < 0 || max_kv_len > int64_t(max_blocks) * page_size)
+        return fail(LRA_ERR_SHAPE, "max_kv_len=%lld must be in [0, max_blocks * page_size]", (long long)max_kv_len);
+    if (max_kv_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^31 - 1");
+    if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
+    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (keys_per_split < 0 || keys_per_split % 64 != 0)
+        return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
+    if (keys_per_split && !paged_split_fits(keys_per_split, page_size))
+        return fail(LRA_ERR_UNSUPPORTED, "keys_per_split=%d spans more than 64 pages of %d rows", keys_per_split, page_size);
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
+    if (batch == 0) return LRA_OK;
+    if (!Q || !K_pages || !V_pages || !Vlr_pages || !B || !O || !block_table || !kv_len || !agent)
+        return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
+    if (!aligned(Q, 16) || !aligned(K_pages, 16) || !aligned(V_pages, 16) || !aligned(Vlr_pages, 16) || !aligned(B, 16) ||
+        !aligned(O, 16))
+        return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    const int chunk = keys_per_split ? keys_per_split : lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, page_size);
+    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
+    if (L.total) {
+        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
+        if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (workspace_bytes < L.total) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
+    }
+    lra::DecodeParams p{};
+    p.Q = Q; p.K = K_pages; p.V = V_pages; p.Vlr = Vlr_pages; p.B = B;
+    p.kv_start = nullptr; p.kv_len = kv_len; p.agent = agent;
+    p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
+    p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
+    p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
+    p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
+    p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
+    p.bf16 = dtype == LRA_BF16;
+    p.block_table = block_table; p.n_pages = n_pages; p.max_blocks = max_blocks;
+    p.page_shift = __builtin_ctz(unsigned(page_size));
+    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), "lra_attn_decode_paged launch");
 }
 
 LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,

@@ -73,7 +73,7 @@ __device__ __forceinline__ Vec<bf16, 8> v_operand(const Vec<bf16, VEC> (&v)[8], 
     return a;
 }
 
-template <typename T, int D, int R, int GP>
+template <typename T, int D, int R, int GP, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
     using Tile = DecodeTile<T, D>;
     constexpr int VEC = Tile::VEC, KCH = Tile::KCH;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     const int b = bs / p.n_split;
     const int s = bs - b * p.n_split;
 
-    const int64_t start = p.kv_start[b];
+    const int64_t start = PAGED ? 0 : p.kv_start[b];   // a paged request starts at its page 0
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
     const int G = p.G;
@@ -103,6 +103,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     const int k1 = min(k0 + p.chunk, len);
 
     const int lane = threadIdx.x & 63;
+
+    // Paged cache: lane i holds the page of the split's i-th block (at most 64 blocks per split,
+    // checked on the host); a tile never crosses a page (P is a power of two >= 32 and tiles are
+    // 32-aligned), so its page is one readlane away. Out-of-range page ids read page 0 instead
+    // and poison the split's partial with NaN.
+    int page_vec = 0, first_page = 0;
+    bool bad_pages = false;
+    if constexpr (PAGED) {
+        first_page = k0 >> p.page_shift;
+        const int n_pg = ((k1 - 1) >> p.page_shift) - first_page + 1;
+        int id = 0;
+        if (lane < n_pg) id = p.block_table[int64_t(b) * p.max_blocks + first_page + lane];
+        const bool lane_bad = lane < n_pg && (id < 0 || int64_t(id) >= p.n_pages);
+        bad_pages = __ballot(lane_bad) != 0;
+        page_vec = lane_bad ? 0 : id;
+    }
+    // first cache row of the 32-key tile starting at key kt of the request
+    auto tile_row = [&](int kt) -> int64_t {
+        if constexpr (PAGED) {
+            const int page = __builtin_amdgcn_readlane(page_vec, (kt >> p.page_shift) - first_page);
+            return (int64_t(page) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
+        } else {
+            return kt;
+        }
+    };
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;   // key row of K, head column of Q^T / P^T, O^T row
     const int q = lane >> 4;   // reduction slot group
@@ -134,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     // k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads into the same
     // registers, so the choice is a uniform branch around address arithmetic only.
     auto load_k = [&](Tile& t, int kt) {
-        const char* kb = Kg + int64_t(kt) * row_bytes;
+        const char* kb = Kg + tile_row(kt) * row_bytes;
         if (kt + kTile <= k1) {
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -152,8 +177,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         }
     };
     auto load_v = [&](Tile& t, int kt) {
-        const char* vb = Vg + int64_t(kt) * row_bytes;
-        const char* lb = Lg + int64_t(kt) * lr_bytes;
+        const int64_t row = tile_row(kt);
+        const char* vb = Vg + row * row_bytes;
+        const char* lb = Lg + row * lr_bytes;
         // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
         // so no load sits behind a lane mask
         uint32_t h[8];
@@ -311,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         const int64_t rec = (bh0 + h) * p.n_split + s;
         p.ws_o[rec * (D + R) + col] = accv;
         if (col == 0) {
-            p.ws_ml[rec * 2 + 0] = M;
+            p.ws_ml[rec * 2 + 0] = bad_pages ? __builtin_nanf("") : M;
             p.ws_ml[rec * 2 + 1] = L;
         }
     }
@@ -335,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
     const int h = blockIdx.x - b * p.n_q;
     const int g = h / p.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t start = p.kv_start[b];
+    const int64_t start = p.kv_start ? p.kv_start[b] : 0;
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
     const int64_t bh = int64_t(b) * p.n_q + h;
@@ -418,7 +444,12 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     const int64_t bs = int64_t(p.batch) * p.n_split;
     const int64_t groups = (bs + 7) / 8;
     const int64_t n_wg = groups * 8 * p.n_kv;
-    if (n_wg > 0) hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+    if (n_wg > 0) {
+        if (p.block_table)
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, true>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+    }
     hipLaunchKernelGGL((decode_combine_kernel<T, D, R>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -29,6 +29,12 @@ struct DecodeParams {
     int n_split, chunk;
     float scale;
     bool bf16;
+    // paged cache (null block_table: contiguous rows addressed by kv_start). Request b's logical row
+    // j lives in page block_table[b*max_blocks + j/P], at row j%P of that page; P = 2^page_shift.
+    const int32_t* block_table;
+    int64_t n_pages;
+    int max_blocks;
+    int page_shift;
 };
 
 struct PrecomputeParams {

@@ -192,3 +192,40 @@ def test_precompute_workspace_sizes():
     assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0
     # 256 rows = 16 tiles: split 16 ways (256 elements each, the minimum)
     assert lra.lra_lr_precompute_workspace_bytes(256, 4096, 3, 8) == 16 * 256 * 24 * 4
+
+
+# ---------------------------------------------------------------------------------------- paged decode
+def decode_paged(**kw):
+    a = dict(dtype=1, Q=P, batch=4, K=P, V=P, Vlr=P, n_pages=100, P=64, ld_vlr=24, table=P, max_blocks=10, kv_len=P,
+             max_kv_len=600, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088, split=0, ws=P,
+             ws_bytes=1 << 30, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode_paged(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["Vlr"], a["n_pages"],
+                                          a["P"], a["ld_vlr"], a["table"], a["max_blocks"], a["kv_len"], a["max_kv_len"],
+                                          a["B"], a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"],
+                                          a["scale"], a["split"], a["ws"], a["ws_bytes"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=48), E_UNSUP), (dict(P=16), E_UNSUP), (dict(P=1 << 17), E_UNSUP), (dict(n_pages=0), E_SHAPE),
+    (dict(max_blocks=0), E_SHAPE), (dict(max_kv_len=641), E_SHAPE), (dict(max_kv_len=-1), E_SHAPE),
+    (dict(P=32, max_kv_len=320, split=64 * 32), E_UNSUP), (dict(split=100), E_SHAPE), (dict(batch=-1), E_SHAPE),
+    (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=0.0), E_SHAPE), (dict(d=32), E_UNSUP),
+    (dict(table=None), E_NULL), (dict(kv_len=None), E_NULL), (dict(agent=None), E_NULL), (dict(Vlr=None), E_NULL),
+    (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS), (dict(O=P + 4), E_SHAPE),
+])
+def test_decode_paged_rejects_bad_arguments(kw, status):
+    assert decode_paged(**kw) == status
+
+
+def test_decode_paged_empty_batch_is_a_no_op():
+    assert decode_paged(batch=0, Q=None, O=None, ws=None) == OK
+
+
+def test_decode_paged_default_split_spans_at_most_64_pages():
+    for P in (32, 64, 128, 1024):
+        for batch, L in ((1, 1900), (16, 66400), (64, 131072), (1, 10 ** 6)):
+            split = lra.lra_attn_decode_paged_default_split(batch, 8, L, P)
+            assert split % 128 == 0 and 128 <= split <= lra.lra_attn_decode_default_split(batch, 8, L)
+            assert (split + P - 1) // P + 1 <= 64
+    assert lra.lra_attn_decode_paged_default_split(16, 8, 66400, 48) == 0

@@ -198,3 +198,77 @@ def test_ministral_layer_decode_full_size():
     for b in picks:
         say(f"decode ministral layer 0: oracle request {b} (L={int(lens[b])})")
         check(got[b:b + 1], ref_decode(dec, requests=[b]), "bf16", f"request {b}")
+
+
+
+# ------------------------------------------------------------------------------ paged cache
+def run_decode_paged(c: W.PagedDecodeBatch, keys_per_split=0, max_kv_len=None):
+    s = c.shape
+    O = lra.lra_attn_decode_paged(dev(c.Q), dev(c.K_pages), dev(c.V_pages), dev(c.Vlr_pages),
+                                  dev_idx(c.block_table, torch.int32), dev_idx(c.kv_len, torch.int32),
+                                  c.max_kv_len if max_kv_len is None else max_kv_len, dev(c.B),
+                                  dev_idx(c.agents, torch.int32), s.scale, keys_per_split)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_decode_paged(c: W.PagedDecodeBatch, requests=None):
+    return oracle.attn_decode_paged(c.Q.as_f64(), c.K_pages.as_f64(), c.V_pages.as_f64(), c.Vlr_pages.as_f64(),
+                                    c.B.as_f64(), c.block_table, c.kv_len, c.agents, c.shape.scale, requests=requests)
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 256])
+def test_decode_paged_cache(page_size):
+    """Shuffled pages, a prefix of pages shared by the longer requests, ragged and empty requests,
+    adapted and adapter-free; splits of several sizes."""
+    s = W.LLAMA_SHAPE
+    lens = [1, 31, 32, 33, 700, 0, 1999, 513, 64]
+    c = W.random_paged_decode((130, page_size), s, lens, page_size, agents=[0, 1, 2, -1, 1, 0, 2, -1, 0],
+                              shared_prefix_pages=1)
+    say(f"decode paged P={page_size}")
+    ref = ref_decode_paged(c)
+    for split in (0, 64, 384):
+        got = run_decode_paged(c, keys_per_split=split)
+        check(got, ref, "bf16", f"P={page_size} split={split}")
+        assert np.all(got[5] == 0.0)
+
+
+def test_decode_paged_equals_contiguous_bits():
+    """With the same split, the paged call gives the same bits as lra_attn_decode over the rows laid
+    out contiguously (the arithmetic order is the same; only addresses differ)."""
+    s = W.LLAMA_SHAPE
+    lens = [900, 130, 64, 1]
+    P = 64
+    c = W.random_paged_decode((131,), s, lens, P, agents=[2, 0, -1, 1], shared_prefix_pages=1)
+    got = run_decode_paged(c, keys_per_split=256)
+    rows, starts = [], []
+    for b, L in enumerate(lens):
+        starts.append(sum(len(r) for r in rows))
+        pages = c.block_table[b][:(L + P - 1) // P]
+        rows.append(np.concatenate([np.arange(pg * P, pg * P + P) for pg in pages])[:L] if L else np.zeros(0, np.int64))
+    idx = np.concatenate(rows)
+    flat = lambda t: W.HostTensor(t.data.reshape((-1,) + t.data.shape[2:])[idx], t.dtype)
+    cc = W.DecodeBatch(s, c.Q, flat(c.K_pages), flat(c.V_pages), flat(c.Vlr_pages), c.B, np.asarray(starts, np.int64),
+                       c.kv_len, c.agents)
+    say("decode paged vs contiguous bits")
+    assert np.array_equal(got, run_decode(cc, keys_per_split=256))
+
+
+def test_decode_paged_bad_page_gives_nan_request_and_unnamed_pages_are_unread():
+    """A page id outside [0, n_pages) poisons only its request; pages that no request names hold NaN."""
+    s = W.LLAMA_SHAPE
+    P = 32
+    c = W.random_paged_decode((132,), s, [200, 100, 64], P, agents=[0, 1, 2], spare_pages=4)
+    named = np.unique(np.concatenate([c.block_table[b][:(int(L) + P - 1) // P] for b, L in enumerate(c.kv_len)]))
+    unnamed = np.setdiff1d(np.arange(c.K_pages.shape[0]), named)
+    assert len(unnamed) >= 4
+    for t in (c.K_pages, c.V_pages, c.Vlr_pages):
+        W.fill_rows(t, unnamed, float("nan"))
+    ref = ref_decode_paged(c)
+    table = c.block_table.copy()
+    table[1, 2] = c.K_pages.shape[0] + 5      # request 1's third page is out of range
+    cc = W.PagedDecodeBatch(s, c.Q, c.K_pages, c.V_pages, c.Vlr_pages, c.B, table, c.kv_len, c.agents)
+    say("decode paged bad page / unread pages")
+    got = run_decode_paged(cc)
+    assert np.all(np.isnan(got[1]))
+    check(got[[0, 2]], ref[[0, 2]], "bf16")

@@ -236,6 +236,24 @@ class PrefillBatch:
 
 
 @dataclass
+class PagedDecodeBatch:
+    """Decode over a paged cache: request b's logical row j is row j % P of page block_table[b, j // P]."""
+    shape: Shape
+    Q: HostTensor            # [batch, n_q, d]
+    K_pages: HostTensor      # [n_pages, P, n_kv, d]
+    V_pages: HostTensor      # [n_pages, P, n_kv, d]
+    Vlr_pages: HostTensor    # [n_pages, P, n_agents * rank]
+    B: HostTensor            # [n_agents, rank, n_kv * d]
+    block_table: np.ndarray  # int32 [batch, max_blocks]
+    kv_len: np.ndarray       # int32 [batch]
+    agents: np.ndarray       # int32 [batch]
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.kv_len.max()) if len(self.kv_len) else 0
+
+
+@dataclass
 class PrecomputeCase:
     shape: Shape
     X: HostTensor            # [T, d_model]
@@ -451,6 +469,39 @@ def random_prefill_batch(key: Sequence[int], s: Shape, requests: Sequence[Tuple[
                         np.asarray([lc for (_, lc, _) in requests], np.int32), np.asarray(kv_start, np.int64),
                         np.asarray([lp for (lp, _, _) in requests], np.int32),
                         np.asarray([a for (_, _, a) in requests], np.int32))
+
+
+def random_paged_decode(key: Sequence[int], s: Shape, kv_lens: Sequence[int], page_size: int,
+                        agents: Optional[Sequence[int]] = None, shared_prefix_pages: int = 0,
+                        spare_pages: int = 3, b_std: float = 0.05) -> PagedDecodeBatch:
+    """Pages dealt out in a seeded random order. The first ``shared_prefix_pages`` pages of every request
+    that is long enough are the same physical pages (a common prefix). ``spare_pages`` pages are
+    named by no request."""
+    key = tuple(key)
+    n = len(kv_lens)
+    blocks = [(int(L) + page_size - 1) // page_size for L in kv_lens]
+    max_blocks = max(blocks + [1])
+    shared = list(range(shared_prefix_pages))
+    own = sum(max(0, bl - shared_prefix_pages) for bl in blocks)
+    n_pages = shared_prefix_pages + own + spare_pages
+    perm = rng(*key, T_AGENT + 1).permutation(n_pages).astype(np.int32)
+    table = np.zeros((n, max_blocks), np.int32)
+    nxt = shared_prefix_pages
+    for b, bl in enumerate(blocks):
+        for j in range(bl):
+            if j < shared_prefix_pages:
+                table[b, j] = perm[j]
+            else:
+                table[b, j] = perm[nxt]
+                nxt += 1
+    K = normal(key + (T_K,), (n_pages, page_size, s.n_kv, s.d_head), 1.0, s.dtype)
+    V = normal(key + (T_V,), (n_pages, page_size, s.n_kv, s.d_head), 1.0, s.dtype)
+    L = normal(key + (T_VLR,), (n_pages, page_size, s.n_agents * s.rank), 1.0, s.dtype)
+    B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
+    Q = normal(key + (T_Q,), (n, s.n_q, s.d_head), 1.0, s.dtype)
+    if agents is None:
+        agents = rng(*key, T_AGENT).integers(0, s.n_agents, size=n)
+    return PagedDecodeBatch(s, Q, K, V, L, B, table, np.asarray(kv_lens, np.int32), np.asarray(agents, np.int32))
 
 
 def random_precompute(key: Sequence[int], s: Shape, T: int) -> PrecomputeCase:

@@ -32,6 +32,7 @@ from .lora_attention import (  # noqa: F401
     attention,
     attn_prefill,
     attn_prefill_varlen,
+    attn_prefill_paged,
     attn_decode,
     attn_decode_paged,
     gather_pages,

@@ -207,6 +207,25 @@ def attn_prefill_varlen(Q, K_base, V_base, V_lr, B, q_start, q_len, kv_start, kv
     return out
 
 
+def attn_prefill_paged(Q, K_pages, V_pages, Vlr_pages, B, block_table, q_start, q_len, kv_prefix, agents,
+                       scale: float) -> np.ndarray:
+    """``attn_prefill_varlen`` over a paged cache: request b's cache rows 0 .. kv_prefix[b]+q_len[b]-1
+    are gathered from the pages its block-table row names (``gather_pages``)."""
+    Q = _f64(Q)
+    out = np.zeros_like(Q)
+    for b in range(len(q_len)):
+        n = int(q_len[b])
+        if n == 0:
+            continue
+        q0, lp = int(q_start[b]), int(kv_prefix[b])
+        L = lp + n
+        K = gather_pages(K_pages, block_table[b], L)
+        V = gather_pages(V_pages, block_table[b], L)
+        Vl = gather_pages(Vlr_pages, block_table[b], L)
+        out[q0:q0 + n] = attn_prefill(Q[q0:q0 + n], K, V, Vl, B, int(agents[b]), lp, scale)
+    return out
+
+
 def attn_decode(Q, K_base, V_base, V_lr, B, kv_start, kv_len, agents, scale: float,
                 requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> np.ndarray:
     """One new query per request over its key range [kv_start[b], kv_start[b] + kv_len[b]).

@@ -29,6 +29,7 @@ def _checks():
     yield lambda: pins.test_bruteforce_decode_mixed_adapted_and_adapter_free()
     yield lambda: pins.test_bruteforce_prefill_varlen_batch()
     yield lambda: pins.test_bruteforce_decode_paged_cache()
+    yield lambda: pins.test_bruteforce_prefill_paged_cache()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()

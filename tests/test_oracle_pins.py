@@ -297,6 +297,31 @@ def test_bruteforce_decode_paged_cache():
     assert np.all(O[2] == 0.0)
 
 
+def test_bruteforce_prefill_paged_cache():
+    """Two prefills over a paged cache (pages of 4 rows, shuffled, a shared first page) against the
+    brute force on the same rows laid out contiguously by hand."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    rng = np.random.default_rng(915)
+    P, n_pages = 4, 8
+    Kp = rng.standard_normal((n_pages, P, s.n_kv, s.d_head))
+    Vp = rng.standard_normal((n_pages, P, s.n_kv, s.d_head))
+    Lp = rng.standard_normal((n_pages, P, s.n_agents * s.rank))
+    B = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Q = rng.standard_normal((12, s.n_q, s.d_head))
+    table = np.array([[6, 1, 3, 0], [6, 4, 7, 2]])
+    q_start, q_len, kv_prefix, agents = [0, 5], [5, 7], [6, 9], [1, oracle.ADAPTER_FREE]
+    O = oracle.attn_prefill_paged(Q, Kp, Vp, Lp, B, table, q_start, q_len, kv_prefix, agents, s.scale)
+    for b in range(2):
+        L = kv_prefix[b] + q_len[b]
+        pages = table[b][:(L + P - 1) // P]
+        K = np.concatenate([Kp[i] for i in pages])[:L]
+        V = np.concatenate([Vp[i] for i in pages])[:L]
+        Vl = np.concatenate([Lp[i] for i in pages])[:L]
+        q0 = q_start[b]
+        ref = bruteforce.prefill(Q[q0:q0 + q_len[b]], K, V, Vl, B, agents[b], kv_prefix[b], s.scale)
+        assert rel_err(O[q0:q0 + q_len[b]], ref) <= 1e-13, b
+
+
 def test_bruteforce_decode_mixed_adapted_and_adapter_free():
     """Double batching (PReCache paper page, section 3): adapted and adapter-free requests over the
     same rows in one batch; the adapter-free ones (agent -1) see the base cache alone."""

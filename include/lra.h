@@ -167,6 +167,29 @@ int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t ba
                             void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Batched variable-length prefill over a paged cache: lra_attn_prefill_varlen with request b's
+ * cache rows 0 .. kv_prefix[b]+q_len[b]-1 spread over fixed-size pages (the layout of concurrent
+ * serving). Cache row j of request b is row j % P of page block_table[b * max_blocks + j / P];
+ * requests may name the same pages (a shared prefix). Queries and outputs are rows of Q and O as in
+ * lra_attn_prefill_varlen.
+ *
+ * K_pages, V_pages (device) [n_pages x P x n_kv x d_head]; Vlr_pages (device) [n_pages x P x ld_vlr]
+ * page_size P: a power of two in [64, 65536]
+ * block_table (device) [batch x max_blocks] int32; kv_prefix, q_len, agent (device) [batch] int32
+ * A request whose kv_prefix[b]+q_len[b] exceeds max_blocks * P is invalid (NaN rows, as in
+ * lra_attn_prefill_varlen). A page id outside [0, n_pages) reads page 0 in its place and turns the
+ * rows of every workgroup that met it to NaN.
+ */
+int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t batch,
+                           const int64_t* q_start, const int32_t* q_len, int64_t max_q_len,
+                           const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                           int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                           const int32_t* block_table, int32_t max_blocks, const int32_t* kv_prefix,
+                           const void* B, int32_t n_agents, const int32_t* agent,
+                           int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                           void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
  * (3)-(4) with L_C = 1): each (request, KV head, split) writes a partial (m, l, O, O_lr) in fp32 to
  * the workspace; a second kernel merges the partials of a (request, KV head) with the log-sum-exp

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "LraError", "LIB_PATH", "abi_version", "status_str",
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
-    "lra_attn_prefill", "lra_attn_prefill_varlen",
+    "lra_attn_prefill", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
@@ -45,6 +45,8 @@ _SIGNATURES = {
                                     _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_prefill_varlen": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p,
                                            _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_attn_prefill_paged": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _p, _i64, _i32, _i64, _p,
+                                          _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
@@ -231,6 +233,46 @@ def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch
                                         _ptr(kv_start), _ptr(kv_prefix), _ptr(B), n_agents, _ptr(agent),
                                         n_q, n_kv, d, rank, scale, _ptr(O), _stream(stream)),
            "lra_attn_prefill_varlen")
+    return O
+
+
+def lra_attn_prefill_paged(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch.Tensor, max_q_len: int,
+                           K_pages: torch.Tensor, V_pages: torch.Tensor, Vlr_pages: torch.Tensor,
+                           block_table: torch.Tensor, kv_prefix: torch.Tensor, B: torch.Tensor, agent: torch.Tensor,
+                           scale: float, O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """lra_attn_prefill_varlen over a paged cache: request b's cache row j is row j % P of page
+    block_table[b, j // P]. K_pages, V_pages [n_pages, P, n_kv, d]; Vlr_pages [n_pages, P, ld];
+    block_table int32 [batch, max_blocks]; q_start int64, q_len / kv_prefix / agent int32 [batch]."""
+    _same(Q, K_pages, V_pages, Vlr_pages, B)
+    for name, t in (("Q", Q), ("K_pages", K_pages), ("V_pages", V_pages), ("B", B)):
+        _dense(name, t)
+    q_rows, n_q, d = Q.shape
+    n_pages, P, n_kv = K_pages.shape[0], K_pages.shape[1], K_pages.shape[2]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if V_pages.shape != K_pages.shape or K_pages.shape[3] != d or B.shape[2] != n_kv * d:
+        raise ValueError("K_pages/V_pages/B shapes disagree with Q")
+    if Vlr_pages.dim() != 3 or Vlr_pages.shape[:2] != (n_pages, P) or Vlr_pages.stride(2) != 1 or \
+            Vlr_pages.stride(0) != P * Vlr_pages.stride(1):
+        raise ValueError("Vlr_pages must be [n_pages, P, ld] with rows of one page adjacent")
+    batch = q_start.shape[0]
+    for name, t, dt in (("q_start", q_start, torch.int64), ("q_len", q_len, torch.int32),
+                        ("kv_prefix", kv_prefix, torch.int32), ("agent", agent, torch.int32)):
+        if t.dtype != dt or t.shape != (batch,) or t.device != Q.device or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous 1-d {dt} tensor of length {batch} on {Q.device}")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous() or \
+            block_table.shape[0] != batch:
+        raise TypeError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
+    if O is None:
+        O = torch.zeros_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    if O.shape != Q.shape:
+        raise ValueError("O must have Q's shape")
+    _check(_lib.lra_attn_prefill_paged(_dtype_code(Q), _ptr(Q), q_rows, batch, _ptr(q_start), _ptr(q_len), max_q_len,
+                                       _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages), n_pages, P, Vlr_pages.stride(1),
+                                       _ptr(block_table), block_table.shape[1], _ptr(kv_prefix), _ptr(B), n_agents,
+                                       _ptr(agent), n_q, n_kv, d, rank, scale, _ptr(O), _stream(stream)),
+           "lra_attn_prefill_paged")
     return O
 
 

@@ -195,6 +195,46 @@ LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows,
     return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), "lra_attn_prefill_varlen launch");
 }
 
+LRA_EXPORT int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t batch,
+                                      const int64_t* q_start, const int32_t* q_len, int64_t max_q_len,
+                                      const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                                      int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                                      const int32_t* block_table, int32_t max_blocks, const int32_t* kv_prefix,
+                                      const void* B, int32_t n_agents, const int32_t* agent,
+                                      int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                      void* O, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (batch < 0 || q_rows < 0 || max_q_len < 0) return fail(LRA_ERR_SHAPE, "batch, q_rows and max_q_len must be >= 0");
+    if (max_q_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_q_len exceeds 2^31 - 1");
+    if (page_size < 64 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0)
+        return fail(LRA_ERR_UNSUPPORTED, "page_size=%d must be a power of two in [64, 65536]", page_size);
+    if (n_pages <= 0 || max_blocks <= 0) return fail(LRA_ERR_SHAPE, "n_pages and max_blocks must be positive");
+    if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
+    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
+    if (batch == 0 || max_q_len == 0) return LRA_OK;
+    if (!Q || !K_pages || !V_pages || !Vlr_pages || !B || !O || !q_start || !q_len || !block_table || !kv_prefix || !agent)
+        return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
+    if (!aligned(Q, 16) || !aligned(K_pages, 16) || !aligned(V_pages, 16) || !aligned(Vlr_pages, 16) || !aligned(B, 16) ||
+        !aligned(O, 16))
+        return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    lra::PrefillParams p{};
+    p.Q = Q; p.K = K_pages; p.V = V_pages; p.Vlr = Vlr_pages; p.B = B; p.O = O;
+    p.ld_vlr = ld_vlr;
+    p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.d_head = d_head; p.rank = rank;
+    p.n_agents = n_agents; p.scale = scale; p.bf16 = dtype == LRA_BF16;
+    p.q_start = q_start; p.q_len = q_len; p.kv_start = nullptr; p.kv_prefix = kv_prefix; p.agents = agent;
+    p.q_rows = q_rows; p.kv_rows = int64_t(max_blocks) * page_size; p.batch = batch; p.max_q_len = max_q_len;
+    p.block_table = block_table; p.n_pages = n_pages; p.max_blocks = max_blocks;
+    p.page_shift = __builtin_ctz(unsigned(page_size));
+    p.max_pairs = lra::prefill_pairs(max_q_len, p.G);
+    if (int64_t(batch) * p.max_pairs * n_kv > (int64_t(1) << 31) - 1)
+        return fail(LRA_ERR_SHAPE, "batch x max_q_len too large for one launch");
+    return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), "lra_attn_prefill_paged launch");
+}
+
 // ============================================================================ decode
 LRA_EXPORT int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len) {
     return lra::decode_default_chunk(batch, n_kv, max_kv_len);

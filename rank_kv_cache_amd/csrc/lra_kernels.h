@@ -81,6 +81,12 @@ struct PrefillParams {
     int64_t max_q_len;          // bound on every q_len[b] (host value that sized the grid)
     int batch;                  // requests in the grid
     int max_pairs;              // workgroups per (request, KV head): enough for the longest chunk
+    // paged cache (null block_table: rows from kv_start). Request b's logical cache row j lives in
+    // page block_table[b*max_blocks + j/P], at row j%P of that page; P = 2^page_shift >= 64.
+    const int32_t* block_table;
+    int64_t n_pages;
+    int max_blocks;
+    int page_shift;
 };
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries

@@ -74,7 +74,7 @@ struct PrefillShared {
     int range_bad;
 };
 
-template <typename T, int D, int R>
+template <typename T, int D, int R, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     using TV = typename PrefillTypes<T>::TV;
     using PF = typename PrefillTypes<T>::PF;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         L_C = p.q_len[req];
         L_P = p.kv_prefix[req];
         q0 = p.q_start[req];
-        k0 = p.kv_start[req];
+        k0 = PAGED ? 0 : p.kv_start[req];   // a paged request starts at its page 0
         agent = p.agents[req];
         if (L_C <= 0 || q0 < 0 || q0 + L_C > p.q_rows) return;
         const bool req_bad = L_C > p.max_q_len || L_P < 0 || k0 < 0 || k0 + L_P + L_C > p.kv_rows ||
@@ -206,21 +206,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // ---- tile fetch (registers) and store (LDS); keys past kv_end read row kv_end-1 (finite, P = 0)
     Vec<T, 8> kpre[KF], vpre[KF], lpre;
     lpre.zero();   // the adapter-free view stages zero V_lr columns
+    // Paged cache: each wave keeps the page ids of 64 consecutive blocks of the request, one per
+    // lane, and reloads that window when a tile moves past it (once per 64 pages). A 64-key tile
+    // never crosses a page (P >= 64, a power of two). A page id outside [0, n_pages) reads page 0
+    // instead and turns the workgroup's rows to NaN (the poison flag of the epilogue).
+    int pg_vec = 0, pg_base = -(1 << 30);
+    bool pg_bad = false;
+    const int n_blk = PAGED ? int((L_P + L_C + (int64_t(1) << p.page_shift) - 1) >> p.page_shift) : 0;
     auto fetch = [&](int t) {
         const int kb = t * kBK;
+        int64_t page_off = 0;   // cache row of key j = j + page_off for every key j of the tile
+        if constexpr (PAGED) {
+            const int pi = kb >> p.page_shift;
+            if (pi - pg_base >= 64) {
+                pg_base = pi;
+                int id = 0;
+                if (pg_base + lane < n_blk) id = p.block_table[int64_t(req) * p.max_blocks + pg_base + lane];
+                const bool bad = pg_base + lane < n_blk && (id < 0 || int64_t(id) >= p.n_pages);
+                pg_bad = pg_bad || bad;
+                pg_vec = bad ? 0 : id;
+            }
+            const int page = __builtin_amdgcn_readlane(pg_vec, pi - pg_base);
+            page_off = (int64_t(page) - pi) << p.page_shift;
+        }
 #pragma unroll
         for (int c = 0; c < KF; ++c) {
             const int f = tid + kThreads * c;
             const int key = f / (D / 8);
             const int d0 = (f - key * (D / 8)) * 8;
-            const int64_t j = min(kb + key, kv_end - 1);
+            const int64_t j = min(kb + key, kv_end - 1) + page_off;
             kpre[c].load(Kp + j * kv_stride + int64_t(g) * D + d0);
             vpre[c].load(Vp + j * kv_stride + int64_t(g) * D + d0);
         }
         if (tid < LF && adapted) {
             const int key = tid / (R / 8);
             const int r0 = (tid - key * (R / 8)) * 8;
-            const int64_t j = min(kb + key, kv_end - 1);
+            const int64_t j = min(kb + key, kv_end - 1) + page_off;
             lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * R + r0);
         }
     };
@@ -416,6 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
     // ---- epilogue: O_lr and l of the row from its 4 lanes, O += O_lr B_agent, normalise, store
     if (sizeof(T) == 2 && !(vmax <= kF16Max)) sh.range_bad = 1;
+    if (PAGED && pg_bad) sh.range_bad = 1;
     __syncthreads();
     const bool poison = sh.range_bad != 0;
 #pragma unroll
@@ -455,7 +477,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 template <typename T, int D, int R>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     const int64_t grid = int64_t(p.batch) * p.max_pairs * p.n_kv;
-    hipLaunchKernelGGL((prefill_kernel<T, D, R>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((prefill_kernel<T, D, R, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<T, D, R, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

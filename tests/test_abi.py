@@ -229,3 +229,31 @@ def test_decode_paged_default_split_spans_at_most_64_pages():
             assert split % 128 == 0 and 128 <= split <= lra.lra_attn_decode_default_split(batch, 8, L)
             assert (split + P - 1) // P + 1 <= 64
     assert lra.lra_attn_decode_paged_default_split(16, 8, 66400, 48) == 0
+
+
+# ---------------------------------------------------------------------------------------- paged prefill
+def prefill_paged(**kw):
+    a = dict(dtype=1, Q=P, q_rows=100, batch=3, q_start=P, q_len=P, max_q_len=64, K=P, V=P, Vlr=P, n_pages=50, P=64,
+             ld_vlr=24, table=P, max_blocks=8, kv_prefix=P, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8,
+             scale=0.088, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_prefill_paged(a["dtype"], a["Q"], a["q_rows"], a["batch"], a["q_start"], a["q_len"],
+                                           a["max_q_len"], a["K"], a["V"], a["Vlr"], a["n_pages"], a["P"], a["ld_vlr"],
+                                           a["table"], a["max_blocks"], a["kv_prefix"], a["B"], a["n_agents"],
+                                           a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"], a["O"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=32), E_UNSUP), (dict(P=96), E_UNSUP), (dict(P=1 << 17), E_UNSUP), (dict(n_pages=0), E_SHAPE),
+    (dict(max_blocks=0), E_SHAPE), (dict(batch=-1), E_SHAPE), (dict(q_rows=-1), E_SHAPE), (dict(max_q_len=-1), E_SHAPE),
+    (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=-1.0), E_SHAPE), (dict(r=4), E_UNSUP),
+    (dict(table=None), E_NULL), (dict(kv_prefix=None), E_NULL), (dict(q_start=None), E_NULL), (dict(Vlr=None), E_NULL),
+    (dict(O=P + 2), E_SHAPE),
+])
+def test_prefill_paged_rejects_bad_arguments(kw, status):
+    assert prefill_paged(**kw) == status
+
+
+def test_prefill_paged_empty_batch_is_a_no_op():
+    assert prefill_paged(batch=0, Q=None, O=None, table=None) == OK

@@ -259,3 +259,88 @@ def test_prefill_varlen_never_reads_outside_ranges():
     got = run_prefill_varlen(c)
     assert np.all(np.isfinite(got[rows]))
     check(got[rows], ref_prefill_varlen(c)[rows], "bf16")
+
+
+
+# ------------------------------------------------------------------------------ paged cache
+def run_prefill_paged(c: W.PagedPrefillBatch, table=None):
+    s = c.shape
+    O = lra.lra_attn_prefill_paged(dev(c.Q), dev_idx(c.q_start, torch.int64), dev_idx(c.q_len, torch.int32),
+                                   c.max_q_len, dev(c.K_pages), dev(c.V_pages), dev(c.Vlr_pages),
+                                   dev_idx(c.block_table if table is None else table, torch.int32),
+                                   dev_idx(c.kv_prefix, torch.int32), dev(c.B), dev_idx(c.agents, torch.int32), s.scale)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_prefill_paged(c: W.PagedPrefillBatch):
+    return oracle.attn_prefill_paged(c.Q.as_f64(), c.K_pages.as_f64(), c.V_pages.as_f64(), c.Vlr_pages.as_f64(),
+                                     c.B.as_f64(), c.block_table, c.q_start, c.q_len, c.kv_prefix, c.agents,
+                                     c.shape.scale)
+
+
+def paged_rows(c):
+    return np.concatenate([np.arange(int(c.q_start[b]), int(c.q_start[b]) + int(c.q_len[b]))
+                           for b in range(len(c.q_len))]).astype(np.int64)
+
+
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_prefill_paged_cache(page_size):
+    """Shuffled pages with a shared first page, requests of mixed L_P / L_C and agents (adapter-free too)."""
+    s = W.LLAMA_SHAPE
+    c = W.random_paged_prefill_batch((330, page_size), s, [(300, 200, 1), (0, 64, -1), (1000, 1, 2), (77, 130, 0),
+                                                           (640, 257, 2)], page_size, shared_prefix_pages=1)
+    say(f"prefill paged P={page_size}")
+    rows = paged_rows(c)
+    check(run_prefill_paged(c)[rows], ref_prefill_paged(c)[rows], "bf16")
+
+
+def test_prefill_paged_equals_varlen_bits():
+    """The paged call gives the same bits as lra_attn_prefill_varlen over the rows laid out contiguously."""
+    s = W.LLAMA_SHAPE
+    P = 64
+    reqs = [(200, 97, 0), (65, 128, -1), (0, 1, 2)]
+    c = W.random_paged_prefill_batch((331,), s, reqs, P, shared_prefix_pages=1)
+    got = run_prefill_paged(c)
+    idx, starts, n = [], [], 0
+    for b, (lp, lc, _) in enumerate(reqs):
+        L = lp + lc
+        pages = c.block_table[b][:(L + P - 1) // P]
+        idx.append(np.concatenate([np.arange(pg * P, pg * P + P) for pg in pages])[:L])
+        starts.append(n)
+        n += L
+    idx = np.concatenate(idx)
+    flat = lambda t: W.HostTensor(t.data.reshape((-1,) + t.data.shape[2:])[idx], t.dtype)
+    v = W.PrefillBatch(s, c.Q, flat(c.K_pages), flat(c.V_pages), flat(c.Vlr_pages), c.B, c.q_start, c.q_len,
+                       np.asarray(starts, np.int64), c.kv_prefix, c.agents)
+    say("prefill paged vs varlen bits")
+    assert np.array_equal(got, run_prefill_varlen(v))
+
+
+def test_prefill_paged_bad_page_and_unnamed_pages():
+    """Pages no request names hold NaN and are never read; a page id out of range makes NaN rows in
+    its own request only (rows whose workgroups never reached it stay exact)."""
+    s = W.LLAMA_SHAPE
+    P = 64
+    c = W.random_paged_prefill_batch((332,), s, [(300, 60, 0), (200, 90, 1)], P, spare_pages=3)
+    named = np.unique(np.concatenate([c.block_table[b][:(int(c.kv_prefix[b] + c.q_len[b]) + P - 1) // P]
+                                      for b in range(2)]))
+    unnamed = np.setdiff1d(np.arange(c.K_pages.shape[0]), named)
+    for t in (c.K_pages, c.V_pages, c.Vlr_pages):
+        W.fill_rows(t, unnamed, float("nan"))
+    ref = ref_prefill_paged(c)
+    rows0 = paged_rows(W.PagedPrefillBatch(s, c.Q, c.K_pages, c.V_pages, c.Vlr_pages, c.B, c.block_table[:1],
+                                           c.q_start[:1], c.q_len[:1], c.kv_prefix[:1], c.agents[:1]))
+    rows1 = np.arange(int(c.q_start[1]), int(c.q_start[1]) + int(c.q_len[1]))
+    say("prefill paged unnamed pages")
+    got = run_prefill_paged(c)
+    check(got[paged_rows(c)], ref[paged_rows(c)], "bf16")
+    table = c.block_table.copy()
+    table[1, 1] = c.K_pages.shape[0] + 7
+    say("prefill paged bad page")
+    bad = run_prefill_paged(c, table=table)
+    check(bad[rows0], ref[rows0], "bf16")
+    assert np.isnan(bad[rows1]).any()
+    fin = np.isfinite(bad[rows1]).all(axis=(1, 2))
+    if fin.any():
+        check(bad[rows1][fin], ref[rows1][fin], "bf16")

@@ -254,6 +254,27 @@ class PagedDecodeBatch:
 
 
 @dataclass
+class PagedPrefillBatch:
+    """Several chunked prefills over a paged cache: request b's cache row j is row j % P of page
+    block_table[b, j // P]; its queries are rows q_start[b] .. of Q."""
+    shape: Shape
+    Q: HostTensor            # [q_rows, n_q, d]
+    K_pages: HostTensor      # [n_pages, P, n_kv, d]
+    V_pages: HostTensor      # [n_pages, P, n_kv, d]
+    Vlr_pages: HostTensor    # [n_pages, P, n_agents * rank]
+    B: HostTensor            # [n_agents, rank, n_kv * d]
+    block_table: np.ndarray  # int32 [batch, max_blocks]
+    q_start: np.ndarray      # int64 [batch]
+    q_len: np.ndarray        # int32 [batch]
+    kv_prefix: np.ndarray    # int32 [batch]
+    agents: np.ndarray       # int32 [batch]
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_len.max()) if len(self.q_len) else 0
+
+
+@dataclass
 class PrecomputeCase:
     shape: Shape
     X: HostTensor            # [T, d_model]
@@ -502,6 +523,27 @@ def random_paged_decode(key: Sequence[int], s: Shape, kv_lens: Sequence[int], pa
     if agents is None:
         agents = rng(*key, T_AGENT).integers(0, s.n_agents, size=n)
     return PagedDecodeBatch(s, Q, K, V, L, B, table, np.asarray(kv_lens, np.int32), np.asarray(agents, np.int32))
+
+
+def random_paged_prefill_batch(key: Sequence[int], s: Shape, requests: Sequence[Tuple[int, int, int]],
+                               page_size: int, shared_prefix_pages: int = 0, spare_pages: int = 3,
+                               gap: int = 2, b_std: float = 0.05) -> PagedPrefillBatch:
+    """requests = [(L_P, L_C, agent), ...]; cache pages dealt out in a seeded random order, the first
+    ``shared_prefix_pages`` shared by every request long enough; query rows one after the other with
+    `gap` uncovered rows before each."""
+    key = tuple(key)
+    lens = [lp + lc for (lp, lc, _) in requests]
+    dec = random_paged_decode(key, s, lens, page_size, agents=[a for (_, _, a) in requests],
+                              shared_prefix_pages=shared_prefix_pages, spare_pages=spare_pages, b_std=b_std)
+    q_start, q = [], 0
+    for (_, lc, _) in requests:
+        q += gap
+        q_start.append(q)
+        q += lc
+    Q = normal(key + (T_Q, 1), (q + gap, s.n_q, s.d_head), 1.0, s.dtype)
+    return PagedPrefillBatch(s, Q, dec.K_pages, dec.V_pages, dec.Vlr_pages, dec.B, dec.block_table,
+                             np.asarray(q_start, np.int64), np.asarray([lc for (_, lc, _) in requests], np.int32),
+                             np.asarray([lp for (lp, _, _) in requests], np.int32), dec.agents)
 
 
 def random_precompute(key: Sequence[int], s: Shape, T: int) -> PrecomputeCase:

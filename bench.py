@@ -171,6 +171,23 @@ def bench_long_decode(args, torch, lra, W, out):
     }
     out["_long_decode_case"] = c
 
+    # double batching: every other request adapter-free (agent -1: K and V_base only, no LR term)
+    ag_dual = ag.clone()
+    ag_dual[1::2] = -1
+
+    def step_dual():
+        lra.lra_attn_decode(Q, K, V, L, ks, kl, c.max_kv_len, B, ag_dual, s.scale, 0, ws, O)
+
+    ms_d = time_launches(step_dual, args.steps, args.warmup, torch)
+    adapted = [int(a) for a in c.agent[0::2]]
+    nbytes_d = (decode_bytes(c.kv_len[0::2], adapted, s.n_q, s.n_kv, s.d_head, s.rank)
+                + (int(sum(int(x) for x in c.kv_len[1::2])) * 2 * s.n_kv * s.d_head
+                   + len(c.kv_len[1::2]) * 2 * s.n_q * s.d_head) * 2)
+    gbs_d = nbytes_d / (ms_d * 1e-3) / 1e9
+    out["decode_dual_view_llama_b16_L66400"] = {
+        "ms": round(ms_d, 4), "gbs": round(gbs_d, 1), "bytes": nbytes_d, "frac": round(gbs_d / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "requests": "8 adapted + 8 adapter-free (agent -1) in one launch"}
+
     # the same bytes as a paged cache: 32-row pages, the block table a seeded permutation of all pages
     P = 32
     n_pages = K.shape[0] // P
@@ -218,7 +235,46 @@ def bench_prefill(args, torch, lra, W, out):
     out["prefill_llama_LP16384_LC2048_r8"] = {
         "ms": round(ms, 4), "tflops": round(tf, 2), "flops": fl, "peak_tflops": BF16_PEAK_TFLOPS,
         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma", "reps": reps}
-    del Q, K, V, L, B, O
+
+    # the same work as four chunk requests of 512 queries in one batched launch (request b: queries
+    # 512b .., L_P = 16384 + 512b, all over the same cache rows)
+    nreq, lc = 4, c.L_C // 4
+    q_start = torch.arange(nreq, dtype=torch.int64, device="cuda") * lc
+    q_len = torch.full((nreq,), lc, dtype=torch.int32, device="cuda")
+    kv_start = torch.zeros(nreq, dtype=torch.int64, device="cuda")
+    kv_prefix = (c.L_P + torch.arange(nreq, device="cuda") * lc).to(torch.int32)
+    agents = torch.zeros(nreq, dtype=torch.int32, device="cuda")
+
+    def step_varlen():
+        lra.lra_attn_prefill_varlen(Q, q_start, q_len, lc, K, V, L, kv_start, kv_prefix, B, agents, s.scale, O)
+
+    ms_v = time_launches(step_varlen, reps, 10, torch)
+    tf_v = fl / (ms_v * 1e-3) / 1e12
+    out["prefill_varlen_4x512_LP16384"] = {
+        "ms": round(ms_v, 4), "tflops": round(tf_v, 2), "flops": fl, "frac": round(tf_v / BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma", "requests": "4 chunks of 512 queries, L_P = 16384 + 512 b, one launch"}
+
+    # the same single prefill over a paged cache: 64-row pages, block table a seeded permutation
+    P = 64
+    n_pages = K.shape[0] // P
+    g = torch.Generator(device="cpu")
+    g.manual_seed(42)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(1, n_pages).cuda()
+    Kp, Vp, Lp = K.view(n_pages, P, s.n_kv, s.d_head), V.view(n_pages, P, s.n_kv, s.d_head), L.view(n_pages, P, -1)
+    one64 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    len1 = torch.full((1,), c.L_C, dtype=torch.int32, device="cuda")
+    pre1 = torch.full((1,), c.L_P, dtype=torch.int32, device="cuda")
+    ag1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step_paged():
+        lra.lra_attn_prefill_paged(Q, one64, len1, c.L_C, Kp, Vp, Lp, table, pre1, B, ag1, s.scale, O)
+
+    ms_p = time_launches(step_paged, reps, 10, torch)
+    tf_p = fl / (ms_p * 1e-3) / 1e12
+    out["prefill_paged_llama_LP16384_LC2048_P64"] = {
+        "ms": round(ms_p, 4), "tflops": round(tf_p, 2), "flops": fl, "frac": round(tf_p / BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma", "page_size": P, "n_pages": n_pages, "block_table": "seeded permutation of the pages"}
+    del Q, K, V, L, B, O, Kp, Vp, Lp, table
     torch.cuda.empty_cache()
 
 

@@ -33,6 +33,9 @@ from .lora_attention import (  # noqa: F401
     attn_prefill,
     attn_prefill_varlen,
     attn_prefill_paged,
+    attn_prefill_qkvo,
+    agent_keys,
+    rope_rotate,
     attn_decode,
     attn_decode_paged,
     gather_pages,

@@ -183,6 +183,49 @@ def attn_prefill(Q, K_base, V_base, V_lr, B, agent: int, L_P: int, scale: float,
     return attention(Q[rows], _f64(K_base)[:L], Va, L_P + rows, scale, heads)
 
 
+def rope_rotate(Y, cos, sin) -> np.ndarray:
+    """Rotary position embedding of rows Y [L, ..., d] at positions 0 .. L-1, rotate-half pairing:
+    element i pairs with i + d/2 and turns by the angle whose cosine / sine are cos[p, i] / sin[p, i]
+    (tables [>= L, d/2], given by the caller). Llama's convention; the pages name RoPE as the reason
+    the key-side LR expansion cannot be reordered, without fixing its form."""
+    Y = _f64(Y)
+    L, d = Y.shape[0], Y.shape[-1]
+    h = d // 2
+    c = _f64(cos)[:L]
+    s_ = _f64(sin)[:L]
+    shape = (L,) + (1,) * (Y.ndim - 2) + (h,)
+    c, s_ = c.reshape(shape), s_.reshape(shape)
+    lo, hi = Y[..., :h], Y[..., h:]
+    return np.concatenate([lo * c - hi * s_, hi * c + lo * s_], axis=-1)
+
+
+def agent_keys(K_base, K_lr, B_k, agent: int, cos, sin) -> np.ndarray:
+    """The agent's full key cache when LoRA also adapts the key projection (the qkvo configuration):
+    ``K_base + RoPE(K_lr[:, agent cols] B_k[agent])``. K_base is stored after RoPE; the rank-r part
+    is expanded and then rotated at each row's position, which is why it cannot be moved out of
+    the key loop (LRAgent page, limitations; PReCache summary page, the QV default).
+    K_base: [L, n_kv, d]; K_lr: [L, >= N*r]; B_k: [N, r, n_kv*d]. Returns [L, n_kv, d]."""
+    K_base = _f64(K_base)
+    if agent == ADAPTER_FREE:
+        return K_base.copy()
+    B_k = _f64(B_k)
+    L, n_kv, d = K_base.shape
+    rank = B_k.shape[1]
+    lr = (_f64(K_lr)[:, agent_columns(agent, rank)] @ B_k[agent]).reshape(L, n_kv, d)
+    return K_base + rope_rotate(lr, cos, sin)
+
+
+def attn_prefill_qkvo(Q, K_base, V_base, V_lr, K_lr, B, B_k, cos, sin, agent: int, L_P: int,
+                      scale: float) -> np.ndarray:
+    """``attn_prefill`` with LoRA on the keys as well: the agent's keys are ``agent_keys``."""
+    Q = _f64(Q)
+    L_C = Q.shape[0]
+    L = L_P + L_C
+    Ka = agent_keys(_f64(K_base)[:L], _f64(K_lr)[:L], B_k, agent, cos, sin)
+    Va = agent_values(_f64(V_base)[:L], _f64(V_lr)[:L], B, agent)
+    return attention(Q, Ka, Va, L_P + np.arange(L_C), scale)
+
+
 def attn_prefill_varlen(Q, K_base, V_base, V_lr, B, q_start, q_len, kv_start, kv_prefix, agents,
                         scale: float) -> np.ndarray:
     """Several causal chunked prefills in one batch: request b's q_len[b] queries are rows

@@ -58,3 +58,24 @@ def decode(Q, K, Vb, Vlr, B, kv_start, kv_len, agents, scale):
 def precompute(X, A):
     X, A = _tolist(X), _tolist(A)
     return [[math.fsum(X[t][c] * A[c][n] for c in range(len(A))) for n in range(len(A[0]))] for t in range(len(X))]
+
+
+def prefill_qkvo(Q, K, Vb, Klr, Vlr, B, Bk, cos, sin, agent, L_P, scale):
+    """Causal prefill whose keys carry a rotated rank-r part: key row j of KV head g is
+    K[j][g][c] + rot_j(Klr[j] Bk)[c], rot_j pairing element i with i + d/2 (cos / sin tables per j)."""
+    Q, K, Vb, Klr, Vlr, B, Bk, cos, sin = map(_tolist, (Q, K, Vb, Klr, Vlr, B, Bk, cos, sin))
+    n_q, n_kv, d = len(Q[0]), len(K[0]), len(K[0][0])
+    r = len(Bk[0])
+    h = d // 2
+    L = L_P + len(Q)
+    Ka = []
+    for j in range(L):
+        row = []
+        for g in range(n_kv):
+            y = [math.fsum(Klr[j][agent * r + k] * Bk[agent][k][g * d + c] for k in range(r)) if agent >= 0 else 0.0
+                 for c in range(d)]
+            rot = [y[c] * cos[j][c] - y[c + h] * sin[j][c] if c < h else y[c] * cos[j][c - h] + y[c - h] * sin[j][c - h]
+                   for c in range(d)]
+            row.append([K[j][g][c] + rot[c] for c in range(d)])
+        Ka.append(row)
+    return prefill(Q, Ka, Vb, Vlr, B, agent, L_P, scale)

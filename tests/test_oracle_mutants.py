@@ -15,6 +15,7 @@ from tests import test_oracle_pins as pins
 
 _orig_softmax = LA.softmax_rows
 _orig_agent_values = LA.agent_values
+_orig_rope = LA.rope_rotate
 
 
 def _checks():
@@ -30,6 +31,8 @@ def _checks():
     yield lambda: pins.test_bruteforce_prefill_varlen_batch()
     yield lambda: pins.test_bruteforce_decode_paged_cache()
     yield lambda: pins.test_bruteforce_prefill_paged_cache()
+    yield lambda: pins.test_bruteforce_prefill_with_key_lora(2)
+    yield lambda: pins.test_key_lora_special_cases()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()
@@ -73,7 +76,21 @@ def _mut_adapter_free_reads_agent_zero(V_base, V_lr, B, agent):
     return _orig_agent_values(V_base, V_lr, B, max(agent, 0))
 
 
+def _mut_rope_adjacent_pairs(Y, cos, sin):
+    Y = np.asarray(Y, np.float64)
+    L, d = Y.shape[0], Y.shape[-1]
+    c = np.asarray(cos, np.float64)[:L].reshape((L,) + (1,) * (Y.ndim - 2) + (d // 2,))
+    s_ = np.asarray(sin, np.float64)[:L].reshape(c.shape)
+    ev, od = Y[..., 0::2], Y[..., 1::2]
+    out = np.empty_like(Y)
+    out[..., 0::2] = ev * c - od * s_
+    out[..., 1::2] = od * c + ev * s_
+    return out
+
+
 MUTANTS = {
+    "rope_adjacent_pairs": ("rope_rotate", _mut_rope_adjacent_pairs),
+    "rope_sign": ("rope_rotate", lambda Y, c, s_: _orig_rope(Y, c, -np.asarray(s_, np.float64))),
     "page_offset_off_by_one": ("gather_pages", lambda pages, row, n: np.asarray(pages)[
         np.asarray(row, np.int64)[np.arange(n) // np.asarray(pages).shape[1]],
         (np.arange(n) + 1) % np.asarray(pages).shape[1]]),

@@ -322,6 +322,54 @@ def test_bruteforce_prefill_paged_cache():
         assert rel_err(O[q0:q0 + q_len[b]], ref) <= 1e-13, b
 
 
+def _rope_tables(L, d, base=10000.0):
+    ang = np.arange(L)[:, None] * base ** (-2.0 * np.arange(d // 2)[None, :] / d)
+    return np.cos(ang), np.sin(ang)
+
+
+@pytest.mark.parametrize("agent", [0, 2, -1])
+def test_bruteforce_prefill_with_key_lora(agent):
+    """LoRA on the keys too (the qkvo configuration): rotated rank-r key part, against the brute force."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    rng = np.random.default_rng(916 + agent)
+    L_P, L_C = 5, 4
+    L = L_P + L_C
+    K = rng.standard_normal((L, s.n_kv, s.d_head))
+    V = rng.standard_normal((L, s.n_kv, s.d_head))
+    Klr = rng.standard_normal((L, s.n_agents * s.rank))
+    Vlr = rng.standard_normal((L, s.n_agents * s.rank))
+    B = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Bk = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Q = rng.standard_normal((L_C, s.n_q, s.d_head))
+    cos, sin = _rope_tables(L, s.d_head)
+    O = oracle.attn_prefill_qkvo(Q, K, V, Vlr, Klr, B, Bk, cos, sin, agent, L_P, s.scale)
+    ref = bruteforce.prefill_qkvo(Q, K, V, Klr, Vlr, B, Bk, cos, sin, agent, L_P, s.scale)
+    assert rel_err(O, ref) <= 1e-13
+
+
+def test_key_lora_special_cases():
+    """B_k = 0 is the value-only method; cos = 1, sin = 0 is an unrotated LoRA key; a rotation keeps
+    every pair's norm; with K_lr = 0 the keys are the base keys whatever the tables."""
+    s = small_shape(n_q=4, n_kv=2, d=8, r=2)
+    c = W.random_prefill((917,), s, 6, 5, agent=1, b_std=0.7)
+    rng = np.random.default_rng(917)
+    L = 11
+    Klr = rng.standard_normal((L, s.n_agents * s.rank))
+    Bk = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    cos, sin = _rope_tables(L, s.d_head)
+    args = (f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr))
+    base = oracle.attn_prefill(*args, f64(c.B), 1, 6, s.scale)
+    assert rel_err(oracle.attn_prefill_qkvo(*args, Klr, f64(c.B), np.zeros_like(Bk), cos, sin, 1, 6, s.scale), base) <= 1e-13
+    assert rel_err(oracle.attn_prefill_qkvo(*args, np.zeros_like(Klr), f64(c.B), Bk, cos, sin, 1, 6, s.scale), base) <= 1e-13
+    Ka = oracle.agent_keys(f64(c.K), Klr, Bk, 1, np.ones_like(cos), np.zeros_like(sin))
+    plain = f64(c.K) + (Klr[:, 2:4] @ Bk[1]).reshape(L, s.n_kv, s.d_head)
+    assert rel_err(Ka, plain) <= 1e-14
+    Y = rng.standard_normal((L, s.n_kv, s.d_head))
+    R = oracle.rope_rotate(Y, cos, sin)
+    h = s.d_head // 2
+    np.testing.assert_allclose(R[..., :h] ** 2 + R[..., h:] ** 2, Y[..., :h] ** 2 + Y[..., h:] ** 2, rtol=1e-12)
+
+
 def test_bruteforce_decode_mixed_adapted_and_adapter_free():
     """Double batching (PReCache paper page, section 3): adapted and adapter-free requests over the
     same rows in one batch; the adapter-free ones (agent -1) see the base cache alone."""

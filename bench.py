@@ -218,7 +218,8 @@ def bench_long_decode(args, torch, lra, W, out):
 
 def bench_prefill(args, torch, lra, W, out):
     log("[bench] prefill 16384 + 2048: generating inputs")
-    c = W.llama_prefill()
+    cq = W.llama_prefill_qkvo()
+    c = cq.base
     s = c.shape
     Q, K, V, L, B = (upload(t, torch) for t in (c.Q, c.K, c.V, c.V_lr, c.B))
     O = torch.empty_like(Q)
@@ -274,7 +275,25 @@ def bench_prefill(args, torch, lra, W, out):
     out["prefill_paged_llama_LP16384_LC2048_P64"] = {
         "ms": round(ms_p, 4), "tflops": round(tf_p, 2), "flops": fl, "frac": round(tf_p / BF16_PEAK_TFLOPS, 4),
         "bound": "mfma", "page_size": P, "n_pages": n_pages, "block_table": "seeded permutation of the pages"}
-    del Q, K, V, L, B, O, Kp, Vp, Lp, table
+
+    # LoRA on the keys as well (qkvo): one pass expands the agent's keys K_base + RoPE(K_lr B_k) into
+    # the workspace, then the attention runs over them; the algorithmic work adds one rank-r
+    # expansion per cached key and KV head
+    Klr, Bk = upload(cq.K_lr, torch), upload(cq.B_k, torch)
+    rc, rs = torch.from_numpy(cq.cos).cuda(), torch.from_numpy(cq.sin).cuda()
+    ws_k = torch.empty(lra.lra_attn_prefill_qkvo_workspace_bytes(c.L_P + c.L_C, s.n_kv, s.d_head),
+                       dtype=torch.uint8, device="cuda")
+
+    def step_qkvo():
+        lra.lra_attn_prefill_qkvo(Q, c.L_P, K, V, L, Klr, B, Bk, rc, rs, 0, s.scale, ws_k, O)
+
+    ms_k = time_launches(step_qkvo, reps, 10, torch)
+    fl_k = fl + 2 * (c.L_P + c.L_C) * s.n_kv * s.d_head * s.rank
+    tf_k = fl_k / (ms_k * 1e-3) / 1e12
+    out["prefill_qkvo_llama_LP16384_LC2048_r8"] = {
+        "ms": round(ms_k, 4), "tflops": round(tf_k, 2), "flops": fl_k, "frac": round(tf_k / BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma", "keys": "K_base + RoPE(K_lr B_k), rank 8, expanded once per call (one extra pass)"}
+    del Q, K, V, L, B, O, Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
     torch.cuda.empty_cache()
 
 

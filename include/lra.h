@@ -135,6 +135,41 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * lra_attn_prefill with LoRA on the key projection as well (the qkvo configuration; LRAgent page,
+ * limitations, and PReCache summary page, which adapt q and v by default): the agent's keys are
+ *
+ *   K_a[j, g] = K_base[j, g] + RoPE_j( (K_lr[j, agent*rank : agent*rank+rank] B_k[agent])[g*d : g*d+d] )
+ *
+ * where RoPE_j turns the pair (y_i, y_{i+d/2}) (i < d/2) by the angle whose cosine and sine are
+ * rope_cos[j, i] and rope_sin[j, i]: (y_i c - y_{i+d/2} s, y_{i+d/2} c + y_i s). K_base is stored
+ * after its own rotation. The rotation sits between the up-projection and the dot product, so the
+ * rank-r key part cannot be deferred like the value side: the call first expands the agent's
+ * L_P+L_C keys into the workspace (one pass), then runs the attention over them.
+ *
+ * K_lr     (device) [L_P+L_C x ld_klr], agent a owns columns a*rank .. a*rank+rank-1
+ * B_k      (device) [n_agents x rank x n_kv*d_head]
+ * rope_cos, rope_sin (device, fp32) [L_P+L_C x d_head/2], row j = position j
+ * workspace(device) lra_attn_prefill_qkvo_workspace_bytes(L_P+L_C, n_kv, d_head) bytes, 256-byte
+ *          aligned, no initialisation needed; calls sharing one workspace must be ordered (same
+ *          stream). It holds the expanded keys (fp16) and per-tile range flags.
+ * Every other argument is as for lra_attn_prefill. Agent -1 (adapter-free view) runs
+ * lra_attn_prefill's kernel on K_base: none of V_lr, B, K_lr, B_k, the tables or the workspace is
+ * read. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED). The Q.K products take fp16 operands with
+ * fp32 accumulation: Q is converted exactly (up to fp16 subnormals) and K_a is summed in fp32 and
+ * rounded to fp16 once. Entries of Q and K_a must therefore satisfy |x| <= 65504 like V_base and
+ * V_lr: a query row whose workgroup meets a larger one (or a NaN key) gets NaN. ld_klr must be
+ * >= n_agents*rank and a multiple of 8; every tensor pointer 16-byte aligned.
+ */
+size_t lra_attn_prefill_qkvo_workspace_bytes(int64_t n_rows, int32_t n_kv, int32_t d_head);
+
+int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                          const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                          const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
+                          const float* rope_cos, const float* rope_sin, int32_t n_agents, int32_t agent,
+                          int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                          void* workspace, size_t workspace_bytes, void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Batched variable-length prefill: several causal chunked prefills (each as lra_attn_prefill) in
  * one launch, for concurrent serving (PReCache summary page: each new chunk L_C follows its reused
  * context L_P; requests are batched together). Request b owns

@@ -216,14 +216,16 @@ def agent_keys(K_base, K_lr, B_k, agent: int, cos, sin) -> np.ndarray:
 
 
 def attn_prefill_qkvo(Q, K_base, V_base, V_lr, K_lr, B, B_k, cos, sin, agent: int, L_P: int,
-                      scale: float) -> np.ndarray:
-    """``attn_prefill`` with LoRA on the keys as well: the agent's keys are ``agent_keys``."""
+                      scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """``attn_prefill`` with LoRA on the keys as well: the agent's keys are ``agent_keys``.
+    ``rows`` restricts the output to some query rows."""
     Q = _f64(Q)
     L_C = Q.shape[0]
     L = L_P + L_C
+    rows = np.arange(L_C) if rows is None else np.asarray(rows, dtype=np.int64)
     Ka = agent_keys(_f64(K_base)[:L], _f64(K_lr)[:L], B_k, agent, cos, sin)
     Va = agent_values(_f64(V_base)[:L], _f64(V_lr)[:L], B, agent)
-    return attention(Q, Ka, Va, L_P + np.arange(L_C), scale)
+    return attention(Q[rows], Ka, Va, L_P + rows, scale)
 
 
 def attn_prefill_varlen(Q, K_base, V_base, V_lr, B, q_start, q_len, kv_start, kv_prefix, agents,

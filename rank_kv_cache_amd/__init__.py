@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "LraError", "LIB_PATH", "abi_version", "status_str",
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
-    "lra_attn_prefill", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
+    "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
@@ -43,6 +43,9 @@ _SIGNATURES = {
                                      _p, _sz, _p]),
     "lra_attn_prefill": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
                                     _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_attn_prefill_qkvo_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "lra_attn_prefill_qkvo": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p, _p, _p, _p,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f, _p, _sz, _p, _p]),
     "lra_attn_prefill_varlen": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p,
                                            _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_prefill_paged": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _p, _i64, _i32, _i64, _p,
@@ -191,6 +194,57 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
                                  V_lr.stride(0), _ptr(B), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(O),
                                  _stream(stream)), "lra_attn_prefill")
     return O
+
+
+def lra_attn_prefill_qkvo(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                          K_lr: torch.Tensor, B: torch.Tensor, B_k: torch.Tensor, rope_cos: torch.Tensor,
+                          rope_sin: torch.Tensor, agent: int, scale: float, workspace: Optional[torch.Tensor] = None,
+                          O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``lra_attn_prefill`` with LoRA on the keys too: the agent's keys are
+    K_base + RoPE(K_lr[:, agent cols] B_k[agent]) (rotate-half pairing, angle tables per position),
+    expanded once per call into ``workspace`` (allocated here when None; size from
+    ``lra_attn_prefill_qkvo_workspace_bytes``), then attended.
+
+    K_lr [>= L_P+L_C, ld]; B_k [N, r, n_kv*d]; rope_cos, rope_sin fp32 [>= L_P+L_C, d/2]. bf16 only."""
+    _same(Q, K_base, V_base, V_lr, K_lr, B, B_k)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("B_k", B_k),
+                    ("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    _rows_dense("K_lr", K_lr)
+    L_C, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    L = L_P + L_C
+    if min(K_base.shape[0], V_base.shape[0], V_lr.shape[0], K_lr.shape[0], rope_cos.shape[0], rope_sin.shape[0]) < L:
+        raise ValueError(f"caches and angle tables hold fewer than L_P + L_C = {L} rows")
+    if K_base.shape[1:] != (n_kv, d) or V_base.shape[1:] != (n_kv, d) or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/B shapes disagree with Q")
+    if B_k.shape != B.shape:
+        raise ValueError(f"B_k {tuple(B_k.shape)} must be shaped like B {tuple(B.shape)}")
+    if rope_cos.dtype != torch.float32 or rope_sin.dtype != torch.float32 or rope_cos.device != Q.device \
+            or rope_sin.device != Q.device:
+        raise ValueError("rope_cos / rope_sin must be float32 tensors on Q's device")
+    if rope_cos.shape[1:] != (d // 2,) or rope_sin.shape[1:] != (d // 2,):
+        raise ValueError("rope tables must be [positions, d/2]")
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    ws_bytes = lra_attn_prefill_qkvo_workspace_bytes(L, n_kv, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
+    _check(_lib.lra_attn_prefill_qkvo(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
+                                      V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(B), _ptr(B_k), _ptr(rope_cos),
+                                      _ptr(rope_sin), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _ptr(O), _stream(stream)),
+           "lra_attn_prefill_qkvo")
+    return O
+
+
+def lra_attn_prefill_qkvo_workspace_bytes(n_rows: int, n_kv: int, d_head: int) -> int:
+    """Bytes of the qkvo prefill's workspace for a call over n_rows = L_P + L_C cache rows."""
+    return int(_lib.lra_attn_prefill_qkvo_workspace_bytes(n_rows, n_kv, d_head))
 
 
 def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch.Tensor, max_q_len: int,

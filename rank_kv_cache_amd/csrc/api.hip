@@ -130,12 +130,39 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
 }
 
 // ============================================================================ prefill
-LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
-                                const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
-                                const void* B, int32_t n_agents, int32_t agent,
-                                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
-                                void* O, void* stream) {
+namespace {
+
+// key-side LoRA operands of the qkvo configuration (null: keys are K_base)
+struct KeyLora {
+    const void* K_lr;
+    int64_t ld_klr;
+    const void* B_k;
+    const float* cos;
+    const float* sin;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// qkvo workspace: [expanded keys: n_rows x n_kv x d_head fp16][range flags: tiles x n_kv int32]
+struct KeyExpandLayout {
+    size_t flags_off, total;
+};
+
+KeyExpandLayout key_expand_layout(int64_t n_rows, int n_kv, int d_head) {
+    KeyExpandLayout L{};
+    const int64_t tiles = (n_rows + lra::kKeyTile - 1) / lra::kKeyTile;
+    L.flags_off = align_up(size_t(n_rows) * size_t(n_kv) * size_t(d_head) * 2, 256);
+    L.total = n_rows > 0 ? L.flags_off + size_t(tiles) * size_t(n_kv) * sizeof(int32_t) : 0;
+    return L;
+}
+
+int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                   const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                   const void* B, int32_t n_agents, int32_t agent,
+                   int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                   void* O, void* stream, const KeyLora* kl) {
     if (int s = check_dtype(dtype)) return s;
+    if (kl && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "%s: bf16 only", name);
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
     if (L_C < 0 || L_P < 0) return fail(LRA_ERR_SHAPE, "L_C=%lld and L_P=%lld must be >= 0", (long long)L_C, (long long)L_P);
     if (L_P + L_C > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "L_P + L_C exceeds 2^31 - 1");
@@ -144,11 +171,25 @@ LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L
         return fail(LRA_ERR_INDEX, "agent=%d outside [-1, %d)", agent, n_agents);
     if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (kl && (kl->ld_klr < int64_t(n_agents) * rank || kl->ld_klr % 8 != 0))
+        return fail(LRA_ERR_SHAPE, "ld_klr=%lld must be >= n_agents*rank and a multiple of 8", (long long)kl->ld_klr);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
     if (L_C == 0) return LRA_OK;
     if (!Q || !K_base || !V_base || !V_lr || !B || !O) return fail(LRA_ERR_NULL, "Q, K_base, V_base, V_lr, B and O must not be NULL");
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    if (kl && agent == lra::kAdapterFree) kl = nullptr;   // the keys are K_base: the plain kernel
+    KeyExpandLayout kx{};
+    if (kl) {
+        if (!kl->K_lr || !kl->B_k || !kl->cos || !kl->sin) return fail(LRA_ERR_NULL, "K_lr, B_k, rope_cos and rope_sin must not be NULL");
+        if (!aligned(kl->K_lr, 16) || !aligned(kl->B_k, 16) || !aligned(kl->cos, 16) || !aligned(kl->sin, 16))
+            return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+        kx = key_expand_layout(L_P + L_C, n_kv, d_head);
+        if (!kl->workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", kx.total);
+        if (!aligned(kl->workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (kl->workspace_bytes < kx.total)
+            return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", kl->workspace_bytes, kx.total);
+    }
     lra::PrefillParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B; p.O = O;
     p.L_C = L_C; p.L_P = L_P; p.ld_vlr = ld_vlr;
@@ -157,7 +198,47 @@ LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L
     p.batch = 1;
     p.max_pairs = lra::prefill_pairs(L_C, p.G);
     if (int64_t(p.max_pairs) * n_kv > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "L_C too large for one launch");
-    return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), "lra_attn_prefill launch");
+    if (kl) {
+        // the agent's keys, expanded once per call, then the attention over them
+        char* ws = static_cast<char*>(kl->workspace);
+        lra::KeyExpandParams e{};
+        e.K = K_base; e.Klr = kl->K_lr; e.Bk = kl->B_k; e.rope_cos = kl->cos; e.rope_sin = kl->sin;
+        e.Ka = ws; e.flags = reinterpret_cast<int32_t*>(ws + kx.flags_off);
+        e.n_rows = L_P + L_C; e.ld_klr = kl->ld_klr;
+        e.n_kv = n_kv; e.d_head = d_head; e.rank = rank; e.agent = agent;
+        if (int s = hip_status(lra::launch_key_expand(e, static_cast<hipStream_t>(stream)), "lra_attn_prefill_qkvo key expansion"))
+            return s;
+        p.K = e.Ka;
+        p.key_flags = e.flags;
+    }
+    return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), name);
+}
+
+}  // namespace
+
+LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                                const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                                const void* B, int32_t n_agents, int32_t agent,
+                                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                void* O, void* stream) {
+    return prefill_single("lra_attn_prefill launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr, B,
+                          n_agents, agent, n_q, n_kv, d_head, rank, scale, O, stream, nullptr);
+}
+
+LRA_EXPORT size_t lra_attn_prefill_qkvo_workspace_bytes(int64_t n_rows, int32_t n_kv, int32_t d_head) {
+    if (n_rows <= 0 || n_kv <= 0 || d_head <= 0) return 0;
+    return key_expand_layout(n_rows, n_kv, d_head).total;
+}
+
+LRA_EXPORT int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
+                                     const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                                     const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
+                                     const float* rope_cos, const float* rope_sin, int32_t n_agents, int32_t agent,
+                                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                     void* workspace, size_t workspace_bytes, void* O, void* stream) {
+    const KeyLora kl{K_lr, ld_klr, B_k, rope_cos, rope_sin, workspace, workspace_bytes};
+    return prefill_single("lra_attn_prefill_qkvo launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr, B,
+                          n_agents, agent, n_q, n_kv, d_head, rank, scale, O, stream, &kl);
 }
 
 LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,

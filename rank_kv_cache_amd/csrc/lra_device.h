@@ -119,10 +119,23 @@ __device__ __forceinline__ f32x4 mma16x16x32(const Vec<bf16, 8>& a, const Vec<bf
 struct H8 {
     uint32_t w[4];
 };
+// 16x16x16 bf16 step (4 values per lane): A lane (row n, group q) holds A[n][4q..4q+3], B lane
+// (column n, group q) holds B[4q..4q+3][n], C lane (n, q) holds C[4q+j][n]
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma16x16x16_bf16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                     c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma16x16x32_f16(const H8& a, const H8& b, f32x4 c) {
     f16x8_t av = __builtin_bit_cast(f16x8_t, a.w);
     f16x8_t bv = __builtin_bit_cast(f16x8_t, b.w);
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
+}
+
+// the fp16 step on 16-bit vectors whose words hold fp16 bit patterns
+__device__ __forceinline__ f32x4 mma16x16x32_f16(const Vec<bf16, 8>& a, const Vec<bf16, 8>& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a.w), __builtin_bit_cast(f16x8_t, b.w), c,
+                                                  0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mma16x16x32(const Vec<float, 8>& a, const Vec<float, 8>& b, f32x4 c) {

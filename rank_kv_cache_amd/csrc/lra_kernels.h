@@ -87,7 +87,29 @@ struct PrefillParams {
     int64_t n_pages;
     int max_blocks;
     int page_shift;
+    // LoRA on the keys too: non-null key_flags means K holds the agent's keys as fp16 bit patterns
+    // (the key expansion pass's output) and key_flags[t*n_kv + g] != 0 marks a 64-key tile of KV
+    // head g that met a value beyond the fp16 range
+    const int32_t* key_flags;
 };
+
+// keys per tile of the key expansion pass's range flags (the prefill's LDS key tile)
+constexpr int kKeyTile = 64;
+
+// Key expansion of the qkvo configuration: Ka[j, g] = fp16(K_base[j, g] + RoPE_j(K_lr[j, agent] B_k)),
+// with per-(64-key tile, KV head) range flags.
+struct KeyExpandParams {
+    const void* K;              // bf16 [n_rows x n_kv x d_head]
+    const void* Klr;            // bf16 [n_rows x ld_klr]
+    const void* Bk;             // bf16 [n_agents x rank x n_kv*d_head]
+    const float* rope_cos;      // [n_rows x d_head/2]
+    const float* rope_sin;
+    void* Ka;                   // fp16 [n_rows x n_kv x d_head]
+    int32_t* flags;             // [ceil(n_rows/64) x n_kv]
+    int64_t n_rows, ld_klr;
+    int n_kv, d_head, rank, agent;
+};
+hipError_t launch_key_expand(const KeyExpandParams& p, hipStream_t stream);
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries
 int prefill_pairs(int64_t L_C, int G);

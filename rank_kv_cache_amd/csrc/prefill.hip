@@ -51,6 +51,7 @@ constexpr int kMT = 2;                          // 16-row tiles per wave
 constexpr int kRowsPerWG = 16 * kMT * kWaves;   // 256 query rows
 constexpr int kPieceRows = kRowsPerWG / 2;      // rows of one half of a workgroup
 constexpr int kBK = 64;                         // keys per LDS tile
+static_assert(kBK == kKeyTile, "the key expansion flags one LDS tile each");
 constexpr float kRescaleLog2 = 8.f;             // m moves when P would exceed 2^8
 
 template <typename T> struct PrefillTypes {
@@ -74,11 +75,12 @@ struct PrefillShared {
     int range_bad;
 };
 
-template <typename T, int D, int R, bool PAGED>
+template <typename T, int D, int R, bool PAGED, bool KLORA>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     using TV = typename PrefillTypes<T>::TV;
     using PF = typename PrefillTypes<T>::PF;
     using SH = PrefillShared<T, D, R>;
+    static_assert(!KLORA || (sizeof(T) == 2 && !PAGED), "key LoRA: bf16, contiguous cache");
     constexpr int KCH = D / 32;      // Q.K reduction chunks
     constexpr int NKB = kBK / 32;    // 32-key blocks of a tile
     constexpr int NDT = D / 16;      // O^T tiles: tile t holds d = 16t .. 16t+15
@@ -171,6 +173,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             else qf[mt][i].zero();
         }
     }
+    // LoRA on the keys (the qkvo configuration): K holds the agent's keys K_base + RoPE(K_lr B_k) as
+    // fp16, written by the key expansion pass, and the scores take fp16 operands (Q converted
+    // exactly within the fp16 range), so the rank-r key part keeps 11 significant bits
+    float qmax = 0.f;
+    if constexpr (KLORA) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < KCH; ++i)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const float lo = bf16_lo(qf[mt][i].w[e2]), hi = bf16_hi(qf[mt][i].w[e2]);
+                    qmax = fmaxf(qmax, fmaxf(fabsf(lo), fabsf(hi)));
+                    qf[mt][i].w[e2] = pack_f16x2(lo, hi);
+                }
+        // take the maximum here: sunk to its use in the epilogue it would keep the bf16 rows live
+        asm volatile("" : "+v"(qmax));
+    }
 
     // ---- key ranges: the workgroup stages keys [0, kv_end) (visible to some row of its long
     // piece); a wave computes the blocks below its own end and masks from its full_end on
@@ -212,6 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // instead and turns the workgroup's rows to NaN (the poison flag of the epilogue).
     int pg_vec = 0, pg_base = -(1 << 30);
     bool pg_bad = false;
+    bool key_bad = false;   // an expanded key tile met a value beyond the fp16 range
     const int n_blk = PAGED ? int((L_P + L_C + (int64_t(1) << p.page_shift) - 1) >> p.page_shift) : 0;
     auto fetch = [&](int t) {
         const int kb = t * kBK;
@@ -244,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             const int64_t j = min(kb + key, kv_end - 1) + page_off;
             lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * R + r0);
         }
+        if constexpr (KLORA) key_bad = key_bad || p.key_flags[int64_t(t) * n_kv + g] != 0;
     };
     // 8 values of one key's row as fp16 (bf16 inputs; exact within the fp16 range) or fp32
     auto put8 = [&](TV* dst, const Vec<T, 8>& src) {
@@ -330,7 +352,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                     Vec<T, 8> ka;
                     ka.load(&ks[(32 * kb2 + 16 * u + n) * LDK + 32 * i + 8 * q]);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) sacc[mt][u] = mma16x16x32(ka, qf[mt][i], sacc[mt][u]);
+                    for (int mt = 0; mt < MT; ++mt) {
+                        if constexpr (KLORA)
+                            sacc[mt][u] = mma16x16x32_f16(ka, qf[mt][i], sacc[mt][u]);
+                        else
+                            sacc[mt][u] = mma16x16x32(ka, qf[mt][i], sacc[mt][u]);
+                    }
                 }
 
             // online softmax per query row (raw scores; scale folded into the exponent)
@@ -437,6 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
     // ---- epilogue: O_lr and l of the row from its 4 lanes, O += O_lr B_agent, normalise, store
     if (sizeof(T) == 2 && !(vmax <= kF16Max)) sh.range_bad = 1;
+    if (KLORA && (key_bad || !(qmax <= kF16Max))) sh.range_bad = 1;
     if (PAGED && pg_bad) sh.range_bad = 1;
     __syncthreads();
     const bool poison = sh.range_bad != 0;
@@ -477,10 +505,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 template <typename T, int D, int R>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
     const int64_t grid = int64_t(p.batch) * p.max_pairs * p.n_kv;
+    if constexpr (sizeof(T) == 2) {
+        if (p.key_flags) {
+            hipLaunchKernelGGL((prefill_kernel<T, D, R, false, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     if (p.block_table)
-        hipLaunchKernelGGL((prefill_kernel<T, D, R, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, R, true, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, D, R, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<T, D, R, false, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -155,6 +155,43 @@ def test_prefill_empty_chunk_is_a_no_op():
     assert prefill(L_C=0, Q=None, O=None) == OK
 
 
+def prefill_qkvo(**kw):
+    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, Klr=P, ld_klr=24, B=P, Bk=P, cos=P, sin=P,
+             n_agents=3, agent=0, n_q=4, n_kv=2, d=64, r=8, scale=0.125, ws=None, ws_bytes=0, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_prefill_qkvo(a["dtype"], a["Q"], a["L_C"], a["L_P"], a["K"], a["V"], a["Vlr"],
+                                          a["ld_vlr"], a["Klr"], a["ld_klr"], a["B"], a["Bk"], a["cos"], a["sin"],
+                                          a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"],
+                                          a["ws"], a["ws_bytes"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), E_UNSUP), (dict(dtype=-1), E_UNSUP), (dict(d=32), E_UNSUP), (dict(r=32), E_UNSUP),
+    (dict(n_q=3), E_SHAPE), (dict(L_C=-1), E_SHAPE), (dict(agent=3), E_INDEX), (dict(agent=-2), E_INDEX),
+    (dict(ld_vlr=8), E_SHAPE), (dict(ld_klr=8), E_SHAPE), (dict(ld_klr=28), E_SHAPE), (dict(scale=0.0), E_SHAPE),
+    (dict(Klr=None), E_NULL), (dict(Bk=None), E_NULL), (dict(cos=None), E_NULL), (dict(sin=None), E_NULL),
+    (dict(B=None), E_NULL), (dict(cos=P + 4), E_SHAPE), (dict(Klr=P + 8), E_SHAPE), (dict(O=P + 2), E_SHAPE),
+    (dict(ws=None), E_WS), (dict(ws=WS + 64, ws_bytes=1 << 30), E_WS), (dict(ws=WS, ws_bytes=1000), E_WS),
+])
+def test_prefill_qkvo_rejects_bad_arguments(kw, status):
+    assert prefill_qkvo(**kw) == status
+
+
+def test_prefill_qkvo_empty_chunk_is_a_no_op():
+    assert prefill_qkvo(L_C=0, Q=None, O=None, Klr=None) == OK
+
+
+def test_prefill_qkvo_workspace_size():
+    # fp16 expanded keys (256-byte aligned part), then one int32 flag per (64-key tile, KV head)
+    assert lra.lra_attn_prefill_qkvo_workspace_bytes(18432, 8, 128) == 18432 * 8 * 128 * 2 + 288 * 8 * 4
+    assert lra.lra_attn_prefill_qkvo_workspace_bytes(65, 2, 64) == 65 * 2 * 64 * 2 + 2 * 2 * 4
+    assert lra.lra_attn_prefill_qkvo_workspace_bytes(3, 1, 64) == 512 + 4
+    assert lra.lra_attn_prefill_qkvo_workspace_bytes(0, 8, 128) == 0
+    # one byte short of the size is refused
+    need = lra.lra_attn_prefill_qkvo_workspace_bytes(256, 2, 64)
+    assert prefill_qkvo(ws=WS, ws_bytes=need - 1) == E_WS
+
+
 # ---------------------------------------------------------------------------------------- precompute
 def precompute(**kw):
     a = dict(dtype=1, X=P, T=2048, d_model=4096, ldx=4096, A=P, n_agents=3, r=8, Vlr=P, ld_vlr=24,

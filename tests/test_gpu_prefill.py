@@ -344,3 +344,138 @@ def test_prefill_paged_bad_page_and_unnamed_pages():
     fin = np.isfinite(bad[rows1]).all(axis=(1, 2))
     if fin.any():
         check(bad[rows1][fin], ref[rows1][fin], "bf16")
+
+
+# ---------------------------------------------------------------- LoRA on the keys (qkvo)
+def _dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run_prefill_qkvo(c: W.QkvoPrefillCase, agent=None, K_lr=None, B_k=None, V_lr=None, B=None, K=None,
+                     workspace=None):
+    b = c.base
+    O = lra.lra_attn_prefill_qkvo(dev(b.Q), b.L_P, dev(b.K if K is None else K), dev(b.V),
+                                  dev(b.V_lr if V_lr is None else V_lr), dev(c.K_lr if K_lr is None else K_lr),
+                                  dev(b.B if B is None else B), dev(c.B_k if B_k is None else B_k),
+                                  _dev_f32(c.cos), _dev_f32(c.sin), b.agent if agent is None else agent,
+                                  b.shape.scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_prefill_qkvo(c: W.QkvoPrefillCase, agent=None, rows=None):
+    b = c.base
+    return oracle.attn_prefill_qkvo(b.Q.as_f64(), b.K.as_f64(), b.V.as_f64(), b.V_lr.as_f64(), c.K_lr.as_f64(),
+                                    b.B.as_f64(), c.B_k.as_f64(), c.cos, c.sin,
+                                    b.agent if agent is None else agent, b.L_P, b.shape.scale, rows=rows)
+
+
+QKVO_SHAPES = [
+    # n_q, n_kv, d, r, L_P, L_C, agent
+    (32, 8, 128, 8, 0, 97, 0), (32, 8, 128, 16, 63, 65, 2), (8, 2, 64, 8, 200, 130, 1),
+    (8, 8, 64, 16, 64, 129, 0), (7, 1, 128, 8, 5, 70, 2), (24, 8, 128, 16, 128, 40, 1), (32, 8, 128, 8, 300, 1, 1),
+]
+
+
+@pytest.mark.parametrize("n_q,n_kv,d,r,L_P,L_C,agent", QKVO_SHAPES)
+def test_prefill_qkvo_shapes(n_q, n_kv, d, r, L_P, L_C, agent):
+    """LoRA on the keys as well: K_a = K_base + RoPE(K_lr B_k), several tiles and a ragged tail."""
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype="bf16")
+    c = W.random_prefill_qkvo((320, n_q, n_kv, d, r, L_P, L_C), s, L_P, L_C, agent=agent)
+    say(f"prefill qkvo n_q={n_q} n_kv={n_kv} d={d} r={r} L_P={L_P} L_C={L_C} agent={agent}")
+    check(run_prefill_qkvo(c), ref_prefill_qkvo(c), "bf16", f"qkvo {n_q}/{n_kv} d={d} r={r} L_P={L_P} L_C={L_C}")
+
+
+def test_prefill_qkvo_llama_full_size_sampled_rows():
+    """The Llama chunked prefill (16,384 cached + 2,048 new queries) with LoRA on the keys, in the
+    launch the benchmark times; sampled rows for every head against the oracle."""
+    say("prefill qkvo llama 16384+2048: generating inputs")
+    c = W.llama_prefill_qkvo()
+    say("prefill qkvo llama 16384+2048: running")
+    got = run_prefill_qkvo(c)
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 128, 1023, 1024, 2046, 2047])
+    say("prefill qkvo llama 16384+2048: oracle on sampled rows")
+    check(got[rows], ref_prefill_qkvo(c, rows=rows), "bf16")
+
+
+def test_prefill_qkvo_without_key_part_reduces_to_plain_prefill():
+    """With B_k = 0 the agent's keys are K_base, so the output is the plain prefill's (oracle
+    attn_prefill); the adapter-free view (agent -1) reads none of K_lr, B_k, V_lr, B (all NaN here)
+    and gives the base-only attention. The key path takes fp16 score operands and the plain path bf16,
+    so the two kernels agree to rounding, not bit for bit."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_qkvo((321,), s, L_P=190, L_C=150, agent=1)
+    zero_bk = W.to_storage(np.zeros(c.B_k.shape, np.float32), "bf16")
+    b = c.base
+    say("prefill qkvo B_k = 0 vs plain prefill")
+    check(run_prefill_qkvo(c, B_k=zero_bk), ref_prefill(b), "bf16")
+    nan = lambda t: W.to_storage(np.full(t.shape, np.nan, np.float32), "bf16")
+    say("prefill qkvo adapter-free with NaN adapters")
+    got = run_prefill_qkvo(c, agent=-1, K_lr=nan(c.K_lr), B_k=nan(c.B_k), V_lr=nan(b.V_lr), B=nan(b.B))
+    check(got, ref_prefill(b, agent=-1), "bf16")
+
+
+def test_prefill_qkvo_out_of_fp16_range_gives_nan_rows():
+    """A query or summed key entry beyond the fp16 range turns the rows of the workgroups that meet
+    it to NaN (the score operands are fp16); other KV heads stay finite and correct."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_qkvo((324,), s, L_P=0, L_C=64, agent=0)
+    q = c.base.Q.as_f64().astype(np.float32)
+    q[5, 3 * s.group, 7] = 1e5   # query head of KV head 3
+    cq = W.QkvoPrefillCase(W.PrefillCase(s, W.to_storage(q, "bf16"), *[getattr(c.base, f) for f in ("K", "V", "V_lr", "B")],
+                                         c.base.L_P, c.base.L_C, 0), c.K_lr, c.B_k, c.cos, c.sin)
+    got = run_prefill_qkvo(cq)
+    g = np.arange(s.n_q) // s.group
+    assert np.all(np.isnan(got[:, g == 3]))
+    check(got[:, g != 3], ref_prefill_qkvo(cq)[:, g != 3], "bf16")
+
+
+def test_prefill_qkvo_expanded_keys_in_the_workspace():
+    """The expansion pass leaves the agent's keys in the workspace (fp16, [L, n_kv, d]): each one is
+    the oracle's K_base + RoPE(K_lr B_k) rounded once to fp16 (2^-11 relative, plus the fp32 sum)."""
+    s = W.Shape(n_q=8, n_kv=2, d_head=128, rank=16, n_agents=3, d_model=256, dtype="bf16")
+    c = W.random_prefill_qkvo((325,), s, L_P=70, L_C=60, agent=2)
+    b = c.base
+    L = b.L_P + b.L_C
+    ws = torch.empty(lra.lra_attn_prefill_qkvo_workspace_bytes(L, s.n_kv, s.d_head), dtype=torch.uint8, device="cuda")
+    check(run_prefill_qkvo(c, workspace=ws), ref_prefill_qkvo(c), "bf16")
+    ka = ws[: L * s.n_kv * s.d_head * 2].view(torch.float16).float().cpu().numpy().astype(np.float64)
+    ref = oracle.agent_keys(b.K.as_f64(), c.K_lr.as_f64(), c.B_k.as_f64(), 2, c.cos, c.sin).reshape(-1)
+    assert np.all(np.abs(ka - ref) <= 2.0 ** -11 * np.abs(ref) + 1e-5)
+    # the same workspace serves a smaller call next (no initialisation needed)
+    c2 = W.random_prefill_qkvo((326,), s, L_P=10, L_C=20, agent=0)
+    check(run_prefill_qkvo(c2, workspace=ws), ref_prefill_qkvo(c2), "bf16")
+
+
+def test_prefill_qkvo_key_beyond_fp16_range_gives_nan_rows_of_that_head():
+    """A summed key beyond the fp16 range flags its 64-key tile: every query row of that KV head that
+    sees the tile gets NaN; the other heads are unaffected."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_qkvo((327,), s, L_P=100, L_C=50, agent=1)
+    k = c.base.K.as_f64().astype(np.float32)
+    k[10, 2, 0] = 7.0e4
+    got = run_prefill_qkvo(c, K=W.to_storage(k, "bf16"))
+    g = np.arange(s.n_q) // s.group
+    assert np.all(np.isnan(got[:, g == 2]))
+    check(got[:, g != 2], ref_prefill_qkvo(c)[:, g != 2], "bf16")
+
+
+def test_prefill_qkvo_key_part_matters():
+    """The rotated rank-r key part changes the output (a kernel that dropped it would fail here)
+    and each agent reads its own K_lr columns: NaN in another agent's columns leaves the rows finite."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_qkvo((322,), s, L_P=64, L_C=64, agent=2)
+    got = run_prefill_qkvo(c)
+    plain = run_prefill(c.base)
+    assert np.max(np.abs(got - plain)) > 0.05
+    klr = c.K_lr.as_f64().astype(np.float32)
+    klr[:, : 2 * s.rank] = np.nan
+    got2 = run_prefill_qkvo(c, K_lr=W.to_storage(klr, "bf16"))
+    assert np.array_equal(got, got2)
+
+
+def test_prefill_qkvo_rejects_fp32():
+    s = W.Shape(n_q=4, n_kv=2, d_head=64, rank=8, n_agents=2, d_model=256, dtype="f32")
+    c = W.random_prefill_qkvo((323,), s, L_P=8, L_C=8, agent=0)
+    with pytest.raises(lra.LraError, match="UNSUPPORTED"):
+        run_prefill_qkvo(c)

@@ -8,7 +8,8 @@ neither imports the other.
 Sources of the shapes (LRAgent and PReCache pages):
   * LoRA on the query and value projections with rank r = 8; keys carry no
     low-rank part (PReCache summary page, "setup and results" paragraph;
-    LRAgent page, "reproducibility" section).
+    LRAgent page, "reproducibility" section). The qkvo cases add a key-side
+    rank-r cache and its up-projection, with standard rotary angle tables.
   * Three role agents (plan / action / reflect) share one trajectory
     (PReCache page, section 4.1 agent setup).
   * Trajectories from 1.9k to 66.4k tokens (PReCache summary page, results).
@@ -46,7 +47,7 @@ WORKLOAD_NAMES = {
 }
 
 # Tensor ids used in spawn keys.
-T_X, T_W0K, T_W0V, T_A, T_B, T_Q, T_K, T_V, T_VLR, T_AGENT, T_LEN, T_XDEC, T_QDEC = range(13)
+T_X, T_W0K, T_W0V, T_A, T_B, T_Q, T_K, T_V, T_VLR, T_AGENT, T_LEN, T_XDEC, T_QDEC, T_KLR, T_BK = range(15)
 
 _BLOCK_ROWS = 4096  # rows per independently seeded block of a large tensor
 
@@ -356,6 +357,19 @@ def llama_prefill(L_P: int = 16384, L_C: int = 2048, agent: int = 0) -> PrefillC
     return PrefillCase(s, Q, K, V, V_lr, B, L_P, L_C, agent)
 
 
+def llama_prefill_qkvo(L_P: int = 16384, L_C: int = 2048, agent: int = 0) -> QkvoPrefillCase:
+    """The chunked prefill above with LoRA on the keys as well (the qkvo configuration): the same
+    Q, K_base, V_base, V_lr and B, plus K_lr ~ N(0, 1) and B_k ~ N(0, 0.3^2)."""
+    s = LLAMA_SHAPE
+    key = (LLAMA_PREFILL, 0, 0)
+    base = llama_prefill(L_P, L_C, agent)
+    L = L_P + L_C
+    K_lr = normal(key + (T_KLR,), (L, s.n_agents * s.rank), 1.0, s.dtype)
+    B_k = normal(key + (T_BK,), (s.n_agents, s.rank, s.d_kv), 0.3, s.dtype)
+    cos, sin = rope_tables(L, s.d_head)
+    return QkvoPrefillCase(base, K_lr, B_k, cos, sin)
+
+
 def llama_precompute(T: int = 2048) -> PrecomputeCase:
     s = LLAMA_SHAPE
     key = (LLAMA_PREFILL, 0, 0)
@@ -462,6 +476,38 @@ def random_prefill(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int 
     B = normal(key + (T_B,), (s.n_agents, s.rank, s.d_kv), b_std, s.dtype)
     Q = normal(key + (T_Q,), (L_C, s.n_q, s.d_head), 1.0, s.dtype)
     return PrefillCase(s, Q, K, V, V_lr, B, L_P, L_C, agent)
+
+
+@dataclass
+class QkvoPrefillCase:
+    """A prefill with LoRA on the keys as well (the qkvo configuration)."""
+    base: PrefillCase
+    K_lr: HostTensor         # [L_P + L_C, n_agents * rank]
+    B_k: HostTensor          # [n_agents, rank, n_kv * d]
+    cos: np.ndarray          # float32 [L_P + L_C, d/2]
+    sin: np.ndarray
+
+
+def rope_tables(positions: int, d_head: int, theta: float = 500000.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Cosine / sine tables [positions, d_head/2] (float32) of the standard rotary angles
+    p * theta^(-2i/d_head) (theta 500,000 as in Llama 3.1). They are an input of the key-side LoRA
+    path, which takes whatever tables the caller gives."""
+    inv = theta ** (-np.arange(0, d_head, 2, dtype=np.float64) / d_head)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def random_prefill_qkvo(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int = 0, b_std: float = 0.05,
+                        bk_std: float = 0.3) -> QkvoPrefillCase:
+    """random_prefill plus the key-side rank-r cache K_lr ~ N(0, 1), B_k ~ N(0, bk_std^2) (so the
+    rank-r part of a key is of the order of K_base's entries) and the rotary tables."""
+    key = tuple(key)
+    L = L_P + L_C
+    base = random_prefill(key, s, L_P, L_C, agent, b_std)
+    K_lr = normal(key + (T_KLR,), (L, s.n_agents * s.rank), 1.0, s.dtype)
+    B_k = normal(key + (T_BK,), (s.n_agents, s.rank, s.d_kv), bk_std, s.dtype)
+    cos, sin = rope_tables(L, s.d_head)
+    return QkvoPrefillCase(base, K_lr, B_k, cos, sin)
 
 
 def random_prefill_batch(key: Sequence[int], s: Shape, requests: Sequence[Tuple[int, int, int]],

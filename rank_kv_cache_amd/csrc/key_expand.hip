@@ -11,12 +11,12 @@
 // Rotation (rotate-half pairing): element i < d/2 pairs with i + d/2; with c = cos[j, i] and
 // s = sin[j, i], (y_i, y_{i+d/2}) -> (y_i c - y_{i+d/2} s, y_{i+d/2} c + y_i s).
 //
-// Mapping: one workgroup = 4 waves = one 64-key tile of one KV head; wave w takes keys 16w..16w+15.
-// For each pair of 16-dim tiles (dp, dp + d/32) the rank-r part comes out of two 16x16x16 bf16
-// matrix-core steps Y^T = B_k^T K_lr^T (rank padded to 16 with zeros): lane (key n, group q) gets
-// dims 16dp + 4q .. +3 of key n in both halves, which is exactly what the rotation pairs. The B_k
-// slice is staged in LDS transposed ([dim][rank]) so each operand is one 8-byte read. The sum is
-// taken in fp32 and rounded once to fp16; a tile that meets |value| > 65504 (or a NaN) sets its flag.
+// Mapping: one workgroup = one 64-key tile of one KV head, 256 threads; a thread owns 8 consecutive
+// dims i .. i+7 of the low half and their partners i+d/2 .. of one key (d/16 threads per key), so
+// every K_base, table and output access is a 16-byte run and the threads of a key cover its row
+// contiguously. The rank-r product (r = 8 or 16 multiply-adds per element) runs on the vector ALU
+// from the key's K_lr row (one broadcast load) and the B_k slice staged in LDS. The sum is taken in
+// fp32 and rounded once to fp16; a tile that meets |value| > 65504 or a NaN sets its flag.
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -25,73 +25,73 @@ namespace lra {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRankPad = 16;
 
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void key_expand_kernel(KeyExpandParams p) {
-    constexpr int NPAIR = D / 32;
-    __shared__ uint16_t bkt[D][kRankPad + 4];   // B_k slice transposed, rows padded by 8 bytes
+    constexpr int TPK = D / 16;                  // threads per key
+    constexpr int KPI = kThreads / TPK;          // keys per pass
+    static_assert(kKeyTile % KPI == 0, "tile split");
+    __shared__ float bk[R][D];                   // the agent's B_k slice of this head, fp32
 
     const int tile = blockIdx.x, g = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, n = lane & 15, q = lane >> 4;
+    const int tid = threadIdx.x;
     const int64_t kv_stride = int64_t(p.n_kv) * D;
-
-    const uint16_t* __restrict__ Bk = static_cast<const uint16_t*>(p.Bk);
-    for (int idx = tid; idx < D * kRankPad; idx += kThreads) {
-        const int d = idx / kRankPad, r = idx - d * kRankPad;
-        bkt[d][r] = r < R ? Bk[(int64_t(p.agent) * R + r) * kv_stride + int64_t(g) * D + d] : uint16_t(0);
+    const uint16_t* __restrict__ Bk = static_cast<const uint16_t*>(p.Bk) + int64_t(p.agent) * R * kv_stride + int64_t(g) * D;
+    for (int idx = tid; idx < R * D; idx += kThreads) {
+        const int r = idx / D, d = idx - r * D;
+        bk[r][d] = bf16_to_f32(Bk[int64_t(r) * kv_stride + d]);
     }
-
-    // B operand: K_lr row of key n, ranks 4q .. 4q+3 (zero past the rank)
-    const int64_t j = int64_t(tile) * kKeyTile + 16 * wv + n;
-    const bool valid = j < p.n_rows;
-    const int64_t jc = valid ? j : p.n_rows - 1;
-    const uint16_t* __restrict__ Klr = static_cast<const uint16_t*>(p.Klr);
-    const uint2 kl = 4 * q < R ? *reinterpret_cast<const uint2*>(Klr + jc * p.ld_klr + int64_t(p.agent) * R + 4 * q)
-                               : make_uint2(0u, 0u);
-    const uint16_t* __restrict__ krow = static_cast<const uint16_t*>(p.K) + jc * kv_stride + int64_t(g) * D;
-    const float* __restrict__ crow = p.rope_cos + jc * (D / 2);
-    const float* __restrict__ srow = p.rope_sin + jc * (D / 2);
-    uint16_t* __restrict__ orow = static_cast<uint16_t*>(p.Ka) + jc * kv_stride + int64_t(g) * D;
     __syncthreads();
 
-    bool out_of_range = false;   // |value| > 65504 or NaN (which compares false)
+    const int i0 = 8 * (tid % TPK);              // first dim of the low half
+    bool out_of_range = false;                   // |value| > 65504 or NaN (which compares false)
 #pragma unroll
-    for (int dp = 0; dp < NPAIR; ++dp) {
-        const int c0 = 16 * dp + 4 * q;   // this lane's first dim of the low half
-        const uint2 blo = *reinterpret_cast<const uint2*>(&bkt[16 * dp + n][4 * q]);
-        const uint2 bhi = *reinterpret_cast<const uint2*>(&bkt[16 * (dp + NPAIR) + n][4 * q]);
-        const f32x4 ylo = mma16x16x16_bf16(blo, kl, f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 yhi = mma16x16x16_bf16(bhi, kl, f32x4{0.f, 0.f, 0.f, 0.f});
-        const uint2 klo = *reinterpret_cast<const uint2*>(krow + c0);
-        const uint2 khi = *reinterpret_cast<const uint2*>(krow + c0 + D / 2);
-        const float4 c = *reinterpret_cast<const float4*>(crow + c0);
-        const float4 s = *reinterpret_cast<const float4*>(srow + c0);
-        const float cv[4] = {c.x, c.y, c.z, c.w}, sv[4] = {s.x, s.y, s.z, s.w};
-        const uint32_t kw_lo[2] = {klo.x, klo.y}, kw_hi[2] = {khi.x, khi.y};
-        uint32_t out_lo[2], out_hi[2];
+    for (int pass = 0; pass < kKeyTile / KPI; ++pass) {
+        const int64_t j = int64_t(tile) * kKeyTile + pass * KPI + tid / TPK;
+        if (j >= p.n_rows) break;
+        const uint16_t* krow = static_cast<const uint16_t*>(p.K) + j * kv_stride + int64_t(g) * D;
+        Vec<bf16, 8> lr[R / 8];   // the key's K_lr columns of the agent (same address for all its threads)
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
+        for (int h = 0; h < R / 8; ++h) lr[h].load(static_cast<const bf16*>(p.Klr) + j * p.ld_klr + int64_t(p.agent) * R + 8 * h);
+        float klr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) klr[r] = lr[r / 8].get(r % 8);
+        const uint4 klo = *reinterpret_cast<const uint4*>(krow + i0);
+        const uint4 khi = *reinterpret_cast<const uint4*>(krow + i0 + D / 2);
+        const float4 c0 = *reinterpret_cast<const float4*>(p.rope_cos + j * (D / 2) + i0);
+        const float4 c1 = *reinterpret_cast<const float4*>(p.rope_cos + j * (D / 2) + i0 + 4);
+        const float4 s0 = *reinterpret_cast<const float4*>(p.rope_sin + j * (D / 2) + i0);
+        const float4 s1 = *reinterpret_cast<const float4*>(p.rope_sin + j * (D / 2) + i0 + 4);
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const uint32_t wl[4] = {klo.x, klo.y, klo.z, klo.w}, wh[4] = {khi.x, khi.y, khi.z, khi.w};
+        uint32_t ol[4], oh[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
             float lo[2], hi[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int x = 2 * w2 + e;
-                const float kl0 = e ? bf16_hi(kw_lo[w2]) : bf16_lo(kw_lo[w2]);
-                const float kh0 = e ? bf16_hi(kw_hi[w2]) : bf16_lo(kw_hi[w2]);
-                lo[e] = kl0 + (ylo[x] * cv[x] - yhi[x] * sv[x]);
-                hi[e] = kh0 + (yhi[x] * cv[x] + ylo[x] * sv[x]);
+                const int x = 2 * w + e;
+                float ylo = 0.f, yhi = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    ylo = fmaf(klr[r], bk[r][i0 + x], ylo);
+                    yhi = fmaf(klr[r], bk[r][i0 + x + D / 2], yhi);
+                }
+                const float kl0 = e ? bf16_hi(wl[w]) : bf16_lo(wl[w]);
+                const float kh0 = e ? bf16_hi(wh[w]) : bf16_lo(wh[w]);
+                lo[e] = kl0 + (ylo * cv[x] - yhi * sv[x]);
+                hi[e] = kh0 + (yhi * cv[x] + ylo * sv[x]);
                 out_of_range = out_of_range || !(fabsf(lo[e]) <= kF16Max) || !(fabsf(hi[e]) <= kF16Max);
             }
-            out_lo[w2] = pack_f16x2(lo[0], lo[1]);
-            out_hi[w2] = pack_f16x2(hi[0], hi[1]);
+            ol[w] = pack_f16x2(lo[0], lo[1]);
+            oh[w] = pack_f16x2(hi[0], hi[1]);
         }
-        if (valid) {
-            *reinterpret_cast<uint2*>(orow + c0) = make_uint2(out_lo[0], out_lo[1]);
-            *reinterpret_cast<uint2*>(orow + c0 + D / 2) = make_uint2(out_hi[0], out_hi[1]);
-        }
+        uint16_t* orow = static_cast<uint16_t*>(p.Ka) + j * kv_stride + int64_t(g) * D;
+        *reinterpret_cast<uint4*>(orow + i0) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+        *reinterpret_cast<uint4*>(orow + i0 + D / 2) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
     }
-    const int bad = valid && out_of_range;
-    const int any_bad = __syncthreads_or(bad);
+    const int any_bad = __syncthreads_or(out_of_range);
     if (tid == 0) p.flags[int64_t(tile) * p.n_kv + g] = any_bad;
 }
 

@@ -222,6 +222,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     }
     if (tid == 0) sh.range_bad = 0;
     float vmax = 0.f;   // largest |V| / |V_lr| staged by this thread (fp16 range check)
+    // expanded keys: the range flags of the tiles this workgroup stages, read once up front
+    bool key_bad = false;
+    if constexpr (KLORA) {
+        for (int t = tid; t < n_tiles; t += kThreads) key_bad |= p.key_flags[int64_t(t) * n_kv + g] != 0;
+    }
 
     // ---- tile fetch (registers) and store (LDS); keys past kv_end read row kv_end-1 (finite, P = 0)
     Vec<T, 8> kpre[KF], vpre[KF], lpre;
@@ -232,7 +237,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     // instead and turns the workgroup's rows to NaN (the poison flag of the epilogue).
     int pg_vec = 0, pg_base = -(1 << 30);
     bool pg_bad = false;
-    bool key_bad = false;   // an expanded key tile met a value beyond the fp16 range
     const int n_blk = PAGED ? int((L_P + L_C + (int64_t(1) << p.page_shift) - 1) >> p.page_shift) : 0;
     auto fetch = [&](int t) {
         const int kb = t * kBK;
@@ -265,7 +269,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             const int64_t j = min(kb + key, kv_end - 1) + page_off;
             lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * R + r0);
         }
-        if constexpr (KLORA) key_bad = key_bad || p.key_flags[int64_t(t) * n_kv + g] != 0;
     };
     // 8 values of one key's row as fp16 (bf16 inputs; exact within the fp16 range) or fp32
     auto put8 = [&](TV* dst, const Vec<T, 8>& src) {

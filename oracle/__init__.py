@@ -38,6 +38,7 @@ from .lora_attention import (  # noqa: F401
     rope_rotate,
     attn_decode,
     attn_decode_paged,
+    attn_decode_qkvo,
     gather_pages,
     attn_factored,
     ADAPTER_FREE,

@@ -297,6 +297,26 @@ def attn_decode(Q, K_base, V_base, V_lr, B, kv_start, kv_len, agents, scale: flo
     return np.stack(out) if out else np.zeros((0, len(heads), d))
 
 
+def attn_decode_qkvo(Q, K_base, V_base, V_lr, K_lr, B, B_k, cos, sin, kv_start, kv_len, agents,
+                     scale: float, requests: Optional[Sequence[int]] = None) -> np.ndarray:
+    """``attn_decode`` with LoRA on the keys as well: request b's keys are ``agent_keys`` of its rows,
+    the row kv_start[b] + j sitting at position j (rows 0 .. of the tables cos / sin)."""
+    Q = _f64(Q)
+    n_q, d = Q.shape[1], Q.shape[2]
+    requests = range(Q.shape[0]) if requests is None else requests
+    out = []
+    for b in requests:
+        n = int(kv_len[b])
+        if n == 0:
+            out.append(np.zeros((n_q, d)))
+            continue
+        r0 = int(kv_start[b])
+        Ka = agent_keys(_f64(K_base[r0:r0 + n]), _f64(K_lr[r0:r0 + n]), B_k, int(agents[b]), cos, sin)
+        Va = agent_values(V_base[r0:r0 + n], V_lr[r0:r0 + n], B, int(agents[b]))
+        out.append(attention(Q[b:b + 1], Ka, Va, [n - 1], scale)[0])
+    return np.stack(out) if out else np.zeros((0, n_q, d))
+
+
 def gather_pages(pages, block_table_row, n_rows: int) -> np.ndarray:
     """Logical rows 0 .. n_rows-1 of a paged cache: row j lives in page block_table_row[j // P] at
     offset j % P (pages: [n_pages, P, ...]). The layout of concurrent serving (the pages' vLLM

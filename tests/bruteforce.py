@@ -60,6 +60,44 @@ def precompute(X, A):
     return [[math.fsum(X[t][c] * A[c][n] for c in range(len(A))) for n in range(len(A[0]))] for t in range(len(X))]
 
 
+def _key_rows(K, Klr, Bk, cos, sin, agent, rows, pos0):
+    """Key rows `rows` with their rotated rank-r part, row rows[t] at table position t + pos0."""
+    n_kv, d = len(K[0]), len(K[0][0])
+    r = len(Bk[0])
+    h = d // 2
+    Ka = []
+    for t, j in enumerate(rows):
+        p_ = t + pos0
+        row = []
+        for g in range(n_kv):
+            y = [math.fsum(Klr[j][agent * r + k] * Bk[agent][k][g * d + c] for k in range(r)) if agent >= 0 else 0.0
+                 for c in range(d)]
+            rot = [y[c] * cos[p_][c] - y[c + h] * sin[p_][c] if c < h else y[c] * cos[p_][c - h] + y[c - h] * sin[p_][c - h]
+                   for c in range(d)]
+            row.append([K[j][g][c] + rot[c] for c in range(d)])
+        Ka.append(row)
+    return Ka
+
+
+def decode_qkvo(Q, K, Vb, Klr, Vlr, B, Bk, cos, sin, kv_start, kv_len, agents, scale):
+    """Decode whose keys carry a rotated rank-r part; request b's key kv_start[b] + t sits at
+    table position t."""
+    Q, K, Vb, Klr, Vlr, B, Bk, cos, sin = map(_tolist, (Q, K, Vb, Klr, Vlr, B, Bk, cos, sin))
+    out = []
+    for b in range(len(Q)):
+        n = int(kv_len[b])
+        s0 = int(kv_start[b])
+        a = int(agents[b])
+        rows = list(range(s0, s0 + n))
+        Ka = _key_rows(K, Klr, Bk, cos, sin, a, rows, 0)
+        # re-index: the request's keys 0 .. n-1 over the same value rows
+        Kfull = list(K)
+        for t, j in enumerate(rows):
+            Kfull[j] = Ka[t]
+        out.append(decode([Q[b]], Kfull, Vb, Vlr, B, [s0], [n], [a], scale)[0])
+    return out
+
+
 def prefill_qkvo(Q, K, Vb, Klr, Vlr, B, Bk, cos, sin, agent, L_P, scale):
     """Causal prefill whose keys carry a rotated rank-r part: key row j of KV head g is
     K[j][g][c] + rot_j(Klr[j] Bk)[c], rot_j pairing element i with i + d/2 (cos / sin tables per j)."""

@@ -33,6 +33,7 @@ def _checks():
     yield lambda: pins.test_bruteforce_prefill_paged_cache()
     yield lambda: pins.test_bruteforce_prefill_with_key_lora(2)
     yield lambda: pins.test_key_lora_special_cases()
+    yield lambda: pins.test_bruteforce_decode_with_key_lora()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()
@@ -88,7 +89,21 @@ def _mut_rope_adjacent_pairs(Y, cos, sin):
     return out
 
 
+def _mut_decode_qkvo_absolute_rows(Q, K_base, V_base, V_lr, K_lr, B, B_k, cos, sin, kv_start, kv_len, agents,
+                                   scale, requests=None):
+    # rotates request b's keys at their absolute cache rows instead of positions 0 .. kv_len-1
+    out = []
+    for b in range(len(Q)):
+        n, r0 = int(kv_len[b]), int(kv_start[b])
+        Ka = LA.agent_keys(np.asarray(K_base[r0:r0 + n], float), np.asarray(K_lr[r0:r0 + n], float), B_k, int(agents[b]),
+                           np.asarray(cos)[r0:], np.asarray(sin)[r0:])
+        Va = LA.agent_values(V_base[r0:r0 + n], V_lr[r0:r0 + n], B, int(agents[b]))
+        out.append(LA.attention(np.asarray(Q, float)[b:b + 1], Ka, Va, [n - 1], scale)[0])
+    return np.stack(out)
+
+
 MUTANTS = {
+    "decode_key_rope_absolute_rows": ("attn_decode_qkvo", _mut_decode_qkvo_absolute_rows),
     "rope_adjacent_pairs": ("rope_rotate", _mut_rope_adjacent_pairs),
     "rope_sign": ("rope_rotate", lambda Y, c, s_: _orig_rope(Y, c, -np.asarray(s_, np.float64))),
     "page_offset_off_by_one": ("gather_pages", lambda pages, row, n: np.asarray(pages)[

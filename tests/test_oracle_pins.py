@@ -347,6 +347,33 @@ def test_bruteforce_prefill_with_key_lora(agent):
     assert rel_err(O, ref) <= 1e-13
 
 
+def test_bruteforce_decode_with_key_lora():
+    """Decode with LoRA on the keys: requests over shared and offset rows, mixed agents (incl. the
+    adapter-free view); each request's keys are rotated from table position 0 at its first row."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    rng = np.random.default_rng(918)
+    rows = 12
+    K = rng.standard_normal((rows, s.n_kv, s.d_head))
+    V = rng.standard_normal((rows, s.n_kv, s.d_head))
+    Klr = rng.standard_normal((rows, s.n_agents * s.rank))
+    Vlr = rng.standard_normal((rows, s.n_agents * s.rank))
+    B = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Bk = 0.7 * rng.standard_normal((s.n_agents, s.rank, s.d_kv))
+    Q = rng.standard_normal((5, s.n_q, s.d_head))
+    cos, sin = _rope_tables(rows, s.d_head)
+    kv_start, kv_len, agents = [0, 0, 5, 5, 11], [12, 12, 7, 7, 1], [1, -1, 2, 0, 2]
+    O = oracle.attn_decode_qkvo(Q, K, V, Vlr, Klr, B, Bk, cos, sin, kv_start, kv_len, agents, s.scale)
+    ref = bruteforce.decode_qkvo(Q, K, V, Klr, Vlr, B, Bk, cos, sin, kv_start, kv_len, agents, s.scale)
+    assert rel_err(O, ref) <= 1e-13
+    # a request at offset 5 uses table positions 0 .. 6, not 5 .. 11: same keys as a request at 0
+    O5 = oracle.attn_decode_qkvo(Q[2:3], K[5:], V[5:], Vlr[5:], Klr[5:], B, Bk, cos, sin, [0], [7], [2], s.scale)
+    assert rel_err(O[2:3], O5) <= 1e-14
+    # B_k = 0 is the plain decode
+    base = oracle.attn_decode(Q, K, V, Vlr, B, kv_start, kv_len, agents, s.scale)
+    Oz = oracle.attn_decode_qkvo(Q, K, V, Vlr, Klr, B, np.zeros_like(Bk), cos, sin, kv_start, kv_len, agents, s.scale)
+    assert rel_err(Oz, base) <= 1e-13
+
+
 def test_key_lora_special_cases():
     """B_k = 0 is the value-only method; cos = 1, sin = 0 is an unrotated LoRA key; a rotation keeps
     every pair's norm; with K_lr = 0 the keys are the base keys whatever the tables."""

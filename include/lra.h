@@ -258,6 +258,42 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                     void* O, void* stream);
 
+/* ------------------------------------------------------------------------------------------------
+ * lra_attn_decode with LoRA on the key projection as well (the qkvo configuration; LRAgent page,
+ * limitations): request b's key t (cache row kv_start[b] + t) is
+ *
+ *   K_a[t, g] = K_base[kv_start[b] + t, g] + RoPE_t( (K_lr[kv_start[b] + t, a*rank : a*rank+rank] B_k[a])[g*d : g*d+d] )
+ *
+ * with a = agent[b] and RoPE_t as for lra_attn_prefill_qkvo, at table row t (a request's keys sit at
+ * positions 0 .. kv_len[b]-1). The call runs two launches on `stream`: a pass that computes the
+ * rank-r part of every score, Q . RoPE_t(K_lr B_k), for all query heads and writes it as fp16 into
+ * the workspace, then the decode kernels, which add it to the base scores Q . K_base.
+ *
+ * K_lr     (device) [kv_rows x ld_klr], agent a owns columns a*rank .. a*rank+rank-1
+ * B_k      (device) [n_agents x rank x n_kv*d_head]
+ * rope_cos, rope_sin (device, fp32) [>= max_kv_len x d_head/2], row t = position t
+ * workspace(device) lra_attn_decode_qkvo_workspace_bytes() bytes (same arguments), 256-byte
+ *          aligned, no initialisation needed; calls sharing one workspace must be ordered.
+ * Every other argument is as for lra_attn_decode. Adapter-free requests (agent -1) attend K_base
+ * alone and read none of the key-side operands. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED);
+ * max_kv_len <= 2^27. Precision: the base part of a score is as in lra_attn_decode; the rank-r
+ * part is computed from fp16 operands (the rotated rank-r key and the query, fp32 accumulation)
+ * and stored as fp16. A request whose query, rotated rank-r key or rank-r score part leaves the
+ * fp16 range (|x| > 65504) gets NaN output (for the heads concerned).
+ */
+size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
+                                            int32_t rank, int64_t max_kv_len, int32_t keys_per_split);
+
+int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
+                         const void* K_base, const void* V_base, int64_t kv_rows,
+                         const void* V_lr, int64_t ld_vlr, const void* K_lr, int64_t ld_klr,
+                         const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                         const void* B, const void* B_k, const float* rope_cos, const float* rope_sin,
+                         int32_t n_agents, const int32_t* agent,
+                         int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                         int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                         void* O, void* stream);
+
 /* Keys per split the library picks for these sizes when keys_per_split = 0. */
 int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len);
 

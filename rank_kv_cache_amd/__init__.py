@@ -21,6 +21,7 @@ __all__ = [
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
+    "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
@@ -54,6 +55,9 @@ _SIGNATURES = {
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+    "lra_attn_decode_qkvo_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
+    "lra_attn_decode_qkvo": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p,
+                                        _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _p, _i32, _p, _i64, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged_default_split": (_i32, [_i32, _i32, _i64, _i32]),
@@ -378,6 +382,60 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O
+
+
+def lra_attn_decode_qkvo_workspace_bytes(batch: int, n_q: int, n_kv: int, d_head: int, rank: int, max_kv_len: int,
+                                         keys_per_split: int = 0) -> int:
+    return int(_lib.lra_attn_decode_qkvo_workspace_bytes(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split))
+
+
+def lra_attn_decode_qkvo(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                         K_lr: torch.Tensor, kv_start: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int,
+                         B: torch.Tensor, B_k: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                         agent: torch.Tensor, scale: float, keys_per_split: int = 0,
+                         workspace: Optional[torch.Tensor] = None, O: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """``lra_attn_decode`` with LoRA on the keys too: request b's key t is
+    K_base + RoPE_t(K_lr[row, agent cols] B_k[agent]) at table row t. K_lr [rows, ld]; B_k like B;
+    rope_cos, rope_sin fp32 [>= max_kv_len, d/2]. bf16 only. ``workspace`` (uint8,
+    lra_attn_decode_qkvo_workspace_bytes() bytes) is allocated when omitted."""
+    _same(Q, K_base, V_base, V_lr, K_lr, B, B_k)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("B_k", B_k),
+                    ("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    _rows_dense("K_lr", K_lr)
+    batch, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32 or agent.dtype != torch.int32:
+        raise TypeError("kv_start must be int64, kv_len and agent int32")
+    for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
+        if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
+    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or K_lr.shape[0] != K_base.shape[0] \
+            or B.shape[2] != n_kv * d or B_k.shape != B.shape:
+        raise ValueError("K_base/V_base/V_lr/K_lr/B/B_k shapes disagree")
+    if rope_cos.dtype != torch.float32 or rope_sin.dtype != torch.float32 or rope_cos.device != Q.device \
+            or rope_sin.device != Q.device:
+        raise ValueError("rope_cos / rope_sin must be float32 tensors on Q's device")
+    if rope_cos.shape[0] < max_kv_len or rope_sin.shape[0] < max_kv_len or rope_cos.shape[1:] != (d // 2,) \
+            or rope_sin.shape[1:] != (d // 2,):
+        raise ValueError("rope tables must be [>= max_kv_len, d/2]")
+    need = lra_attn_decode_qkvo_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_decode_qkvo(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
+                                     _ptr(V_lr), V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(kv_start), _ptr(kv_len),
+                                     max_kv_len, _ptr(B), _ptr(B_k), _ptr(rope_cos), _ptr(rope_sin), n_agents,
+                                     _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split, _ptr(workspace), ws_bytes,
+                                     _ptr(O), _stream(stream)), "lra_attn_decode_qkvo")
     return O
 
 

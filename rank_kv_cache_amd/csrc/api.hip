@@ -393,22 +393,45 @@ LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
     return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), "lra_attn_decode_paged launch");
 }
 
-LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
-                               const void* K_base, const void* V_base, int64_t kv_rows,
-                               const void* V_lr, int64_t ld_vlr,
-                               const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
-                               const void* B, int32_t n_agents, const int32_t* agent,
-                               int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
-                               int32_t keys_per_split, void* workspace, size_t workspace_bytes,
-                               void* O, void* stream) {
+namespace {
+
+// key-side LoRA operands of a decode (null: keys are K_base)
+struct DecodeKeyLora {
+    const void* K_lr;
+    int64_t ld_klr;
+    const void* B_k;
+    const float* cos;
+    const float* sin;
+};
+
+int64_t key_score_stride(int64_t max_kv_len) { return (max_kv_len + 63) / 64 * 64; }
+
+// decode workspace, then (LoRA on the keys) the fp16 key scores [batch x n_q x stride], 256-aligned
+size_t decode_qkvo_bytes(const DecodeLayout& L, int batch, int n_q, int64_t max_kv_len, size_t* ks_off) {
+    *ks_off = align_up(L.total, 256);
+    return *ks_off + size_t(batch) * size_t(n_q) * size_t(key_score_stride(max_kv_len)) * 2;
+}
+
+int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
+                const void* K_base, const void* V_base, int64_t kv_rows,
+                const void* V_lr, int64_t ld_vlr,
+                const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                const void* B, int32_t n_agents, const int32_t* agent,
+                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                void* O, void* stream, const DecodeKeyLora* kl) {
     if (int s = check_dtype(dtype)) return s;
+    if (kl && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "%s: bf16 only", name);
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
     if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
     if (kv_rows < 0 || max_kv_len < 0) return fail(LRA_ERR_SHAPE, "kv_rows and max_kv_len must be >= 0");
     if (max_kv_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^31 - 1");
+    if (kl && max_kv_len > (int64_t(1) << 27)) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^27 with LoRA on the keys");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
     if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (kl && (kl->ld_klr < int64_t(n_agents) * rank || kl->ld_klr % 8 != 0))
+        return fail(LRA_ERR_SHAPE, "ld_klr=%lld must be >= n_agents*rank and a multiple of 8", (long long)kl->ld_klr);
     if (keys_per_split < 0 || keys_per_split % 64 != 0)
         return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
@@ -417,12 +440,19 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
         return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    if (kl) {
+        if (!kl->K_lr || !kl->B_k || !kl->cos || !kl->sin) return fail(LRA_ERR_NULL, "K_lr, B_k, rope_cos and rope_sin must not be NULL");
+        if (!aligned(kl->K_lr, 16) || !aligned(kl->B_k, 16) || !aligned(kl->cos, 16) || !aligned(kl->sin, 16))
+            return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    }
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
     const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
-    if (L.total) {
-        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
+    size_t ks_off = 0;
+    const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, max_kv_len, &ks_off) : 0) : L.total;
+    if (need) {
+        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        if (workspace_bytes < L.total) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
+        if (workspace_bytes < need) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
     }
     lra::DecodeParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B;
@@ -433,7 +463,58 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
-    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), "lra_attn_decode launch");
+    if (kl && max_kv_len > 0) {
+        // the rank-r part of every score first, then the attention adds it to the base scores
+        lra::KeyScoreParams e{};
+        e.Q = Q; e.Klr = kl->K_lr; e.Bk = kl->B_k; e.rope_cos = kl->cos; e.rope_sin = kl->sin;
+        e.kv_start = kv_start; e.kv_len = kv_len; e.agent = agent;
+        e.S = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ks_off);
+        e.kv_rows = kv_rows; e.max_kv_len = max_kv_len; e.ld_klr = kl->ld_klr; e.ks_stride = key_score_stride(max_kv_len);
+        e.batch = batch; e.n_q = n_q; e.n_kv = n_kv; e.G = n_q / n_kv; e.n_agents = n_agents; e.d_head = d_head; e.rank = rank;
+        if (int s = hip_status(lra::launch_key_scores(e, static_cast<hipStream_t>(stream)), "lra_attn_decode_qkvo key scores"))
+            return s;
+        p.key_scores = e.S;
+        p.ks_stride = e.ks_stride;
+    }
+    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), name);
+}
+
+}  // namespace
+
+LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
+                               const void* K_base, const void* V_base, int64_t kv_rows,
+                               const void* V_lr, int64_t ld_vlr,
+                               const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                               const void* B, int32_t n_agents, const int32_t* agent,
+                               int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                               int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                               void* O, void* stream) {
+    return decode_call("lra_attn_decode launch", dtype, Q, batch, K_base, V_base, kv_rows, V_lr, ld_vlr, kv_start,
+                       kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
+                       workspace, workspace_bytes, O, stream, nullptr);
+}
+
+LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
+                                                       int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
+    if (batch <= 0 || n_q <= 0 || n_kv <= 0 || d_head <= 0 || rank <= 0 || max_kv_len <= 0 || keys_per_split < 0) return 0;
+    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
+    size_t ks_off = 0;
+    return decode_qkvo_bytes(decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk), batch, n_q, max_kv_len, &ks_off);
+}
+
+LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
+                                    const void* K_base, const void* V_base, int64_t kv_rows,
+                                    const void* V_lr, int64_t ld_vlr, const void* K_lr, int64_t ld_klr,
+                                    const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                                    const void* B, const void* B_k, const float* rope_cos, const float* rope_sin,
+                                    int32_t n_agents, const int32_t* agent,
+                                    int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                    int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                    void* O, void* stream) {
+    const DecodeKeyLora kl{K_lr, ld_klr, B_k, rope_cos, rope_sin};
+    return decode_call("lra_attn_decode_qkvo launch", dtype, Q, batch, K_base, V_base, kv_rows, V_lr, ld_vlr, kv_start,
+                       kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
+                       workspace, workspace_bytes, O, stream, &kl);
 }
 
 namespace lra {

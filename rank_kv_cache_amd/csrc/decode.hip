@@ -61,6 +61,7 @@ template <typename T, int D> struct DecodeTile {
     Vec<T, 8> k[2][KCH];   // K rows 16u + n, d = 32i + 8q .. +7
     Vec<T, VEC> v[8];      // V rows key(q, e), d = VEC*n .. +VEC-1
     Vec<T, 8> lr;          // V_lr[key(q, e)][agent*R + n % R] in slot e
+    uint2 ks[2];           // rank-r key scores (fp16) of head n, keys 16u + 4q .. +3 (LoRA on the keys)
 };
 
 // A operand of O^T tile t from the 8 loaded V rows: slot e <- v[e][t] (16-bit transpose).
@@ -73,7 +74,7 @@ __device__ __forceinline__ Vec<bf16, 8> v_operand(const Vec<bf16, VEC> (&v)[8], 
     return a;
 }
 
-template <typename T, int D, int R, int GP, bool PAGED>
+template <typename T, int D, int R, int GP, bool PAGED, bool KSC>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
     using Tile = DecodeTile<T, D>;
     constexpr int VEC = Tile::VEC, KCH = Tile::KCH;
@@ -154,6 +155,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         else qf[i].zero();
     }
 
+    // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key score
+    // pass as fp16 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head n
+    // (a wave-uniform base per request and KV head plus one 32-bit lane offset)
+    const bool ks_live = KSC && a != kAdapterFree;
+    const char* __restrict__ ksg = KSC ? reinterpret_cast<const char*>(p.key_scores + (int64_t(b) * p.n_q + int64_t(g) * G) * p.ks_stride) : nullptr;
+    const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 2);
+    auto load_ks = [&](Tile& t, int kt) {
+        if constexpr (KSC) {
+            if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
+                t.ks[0] = *reinterpret_cast<const uint2*>(ksg + ks_lane + 2 * kt);
+                t.ks[1] = *reinterpret_cast<const uint2*>(ksg + ks_lane + 2 * (kt + 16));
+            } else {
+                t.ks[0] = t.ks[1] = make_uint2(0u, 0u);
+            }
+        }
+    };
     // Tile loads. A full tile addresses each operand as a wave-uniform base (scalar registers) plus
     // one 32-bit lane offset. Only a split's last tile can run past k1: its rows are clamped to
     // k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads into the same
@@ -220,12 +237,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     auto tile_step = [&](Tile& t, int kt, auto prefetch) {
         constexpr bool PREFETCH = decltype(prefetch)::value;
         const int kn = kt + kWaves * kTile;
+        // the key scores are loaded here, not a tile ahead: prefetched, they overflow the registers
+        load_ks(t, kt);
         f32x4 sacc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < KCH; ++i) sacc[u] = mma16x16x32(t.k[u][i], qf[i], sacc[u]);
+        }
+        if constexpr (KSC) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                sacc[u][0] += f16_lo(t.ks[u].x);
+                sacc[u][1] += f16_hi(t.ks[u].x);
+                sacc[u][2] += f16_lo(t.ks[u].y);
+                sacc[u][3] += f16_hi(t.ks[u].y);
+            }
         }
         if constexpr (PREFETCH) load_k(t, kn);
         float sc[8];
@@ -445,10 +473,14 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     const int64_t groups = (bs + 7) / 8;
     const int64_t n_wg = groups * 8 * p.n_kv;
     if (n_wg > 0) {
-        if (p.block_table)
-            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, true>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+        if (p.key_scores) {
+            if constexpr (sizeof(T) == 2)
+                hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, true>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+        } else if (p.block_table) {
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, true, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+        } else {
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+        }
     }
     hipLaunchKernelGGL((decode_combine_kernel<T, D, R>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();

@@ -40,6 +40,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 constexpr float kF16Max = 65504.f;
+// the fp16 halves of a 32-bit word, widened exactly
+__device__ __forceinline__ float f16_lo(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[0]); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[1]); }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
@@ -125,6 +128,11 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mma16x16x16_bf16(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
                                                      c, 0, 0, 0);
+}
+// the same 16x16x16 step on fp16 operands (4 halves per lane in 2 dwords)
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma16x16x16_f16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma16x16x32_f16(const H8& a, const H8& b, f32x4 c) {
     f16x8_t av = __builtin_bit_cast(f16x8_t, a.w);

@@ -35,6 +35,10 @@ struct DecodeParams {
     int64_t n_pages;
     int max_blocks;
     int page_shift;
+    // LoRA on the keys (null: none): key_scores[(b*n_q + h)*ks_stride + j] = Q_bh . RoPE_j(K_lr B_k)
+    // of request b's key j as fp16 bits (bf16 only; ks_stride a multiple of 64)
+    const uint16_t* key_scores;
+    int64_t ks_stride;
 };
 
 struct PrecomputeParams {
@@ -110,6 +114,26 @@ struct KeyExpandParams {
     int n_kv, d_head, rank, agent;
 };
 hipError_t launch_key_expand(const KeyExpandParams& p, hipStream_t stream);
+
+// Decode with LoRA on the keys: the rank-r part of every score,
+// S[(b*n_q + h)*ks_stride + j] = fp16(Q[b, h] . RoPE_j(K_lr[kv_start[b] + j, agent_b] B_k[agent_b][:, g])),
+// for keys j < round_up(kv_len[b], 32) (later keys repeat the last row); NaN where the rotated
+// rank-r key or the query leaves the fp16 range. Requests that are invalid or adapter-free are skipped.
+struct KeyScoreParams {
+    const void* Q;              // bf16 [batch x n_q x d_head]
+    const void* Klr;            // bf16 [kv_rows x ld_klr]
+    const void* Bk;             // bf16 [n_agents x rank x n_kv*d_head]
+    const float* rope_cos;      // [>= max_kv_len x d_head/2]
+    const float* rope_sin;
+    const int64_t* kv_start;
+    const int32_t* kv_len;
+    const int32_t* agent;
+    uint16_t* S;                // fp16 [batch x n_q x ks_stride]
+    int64_t kv_rows, max_kv_len, ld_klr, ks_stride;
+    int batch, n_q, n_kv, G, n_agents, d_head, rank;
+};
+hipError_t launch_key_scores(const KeyScoreParams& p, hipStream_t stream);
+constexpr int kKeyScoreBlock = 256;   // keys per workgroup of the key score pass
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries
 int prefill_pairs(int64_t L_C, int G);

@@ -74,6 +74,41 @@ def test_decode_rejects_bad_arguments(kw, status):
     assert lra._lib.lra_last_error().decode() != ""
 
 
+def decode_qkvo(**kw):
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, Klr=P, ld_klr=24, kv_start=P, kv_len=P,
+             max_kv_len=100, B=P, Bk=P, cos=P, sin=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
+             split=0, ws=WS, ws_bytes=16, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode_qkvo(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"],
+                                         a["ld_vlr"], a["Klr"], a["ld_klr"], a["kv_start"], a["kv_len"], a["max_kv_len"],
+                                         a["B"], a["Bk"], a["cos"], a["sin"], a["n_agents"], a["agent"], a["n_q"],
+                                         a["n_kv"], a["d"], a["r"], a["scale"], a["split"], a["ws"], a["ws_bytes"],
+                                         a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), E_UNSUP), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_q=30, n_kv=8), E_SHAPE),
+    (dict(ld_klr=16), E_SHAPE), (dict(ld_klr=30), E_SHAPE), (dict(ld_vlr=16), E_SHAPE), (dict(split=100), E_SHAPE),
+    (dict(max_kv_len=(1 << 27) + 1), E_SHAPE), (dict(scale=0.0), E_SHAPE),
+    (dict(Klr=None), E_NULL), (dict(Bk=None), E_NULL), (dict(cos=None), E_NULL), (dict(sin=None), E_NULL),
+    (dict(agent=None), E_NULL), (dict(cos=P + 4), E_SHAPE), (dict(Klr=P + 8), E_SHAPE),
+    (dict(ws=None), E_WS), (dict(ws=WS + 64, ws_bytes=1 << 30), E_WS), (dict(ws_bytes=16), E_WS),
+])
+def test_decode_qkvo_rejects_bad_arguments(kw, status):
+    assert decode_qkvo(**kw) == status
+
+
+def test_decode_qkvo_workspace_size():
+    # the decode workspace, 256-aligned, then fp16 key scores [batch x n_q x round_up(max_kv_len, 64)]
+    plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
+    need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
+    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2
+    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, then 2 x 4 x 64 fp16 scores
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2
+    assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
+    assert decode_qkvo(batch=0, Q=None, O=None) == OK
+
+
 def test_decode_empty_batch_is_a_no_op():
     assert decode(batch=0, Q=None, ws=None, ws_bytes=0) == OK
 

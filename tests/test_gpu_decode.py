@@ -272,3 +272,106 @@ def test_decode_paged_bad_page_gives_nan_request_and_unnamed_pages_are_unread():
     got = run_decode_paged(cc)
     assert np.all(np.isnan(got[1]))
     check(got[[0, 2]], ref[[0, 2]], "bf16")
+
+
+# ---------------------------------------------------------------- LoRA on the keys (qkvo)
+def _dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def run_decode_qkvo(c: W.QkvoDecodeBatch, keys_per_split=0, K_lr=None, B_k=None, agent=None, Q=None):
+    b = c.base
+    O = lra.lra_attn_decode_qkvo(dev(b.Q if Q is None else Q), dev(b.K), dev(b.V), dev(b.V_lr),
+                                 dev(c.K_lr if K_lr is None else K_lr), dev_idx(b.kv_start, torch.int64),
+                                 dev_idx(b.kv_len, torch.int32), b.max_kv_len, dev(b.B),
+                                 dev(c.B_k if B_k is None else B_k), _dev_f32(c.cos), _dev_f32(c.sin),
+                                 dev_idx(b.agent if agent is None else agent, torch.int32), b.shape.scale,
+                                 keys_per_split)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+def ref_decode_qkvo(c: W.QkvoDecodeBatch, requests=None, Q=None):
+    b = c.base
+    return oracle.attn_decode_qkvo((b.Q if Q is None else Q).as_f64(), F64Rows(b.K), F64Rows(b.V), F64Rows(b.V_lr),
+                                   F64Rows(c.K_lr), b.B.as_f64(), c.B_k.as_f64(), c.cos, c.sin, b.kv_start,
+                                   b.kv_len, b.agent, b.shape.scale, requests=requests)
+
+
+QKVO_CASES = [
+    # n_q, n_kv, d, r, kv_lens, kv_starts, agents, keys_per_split
+    (32, 8, 128, 8, [300, 1, 65, 200], None, [0, 2, 1, -1], 0),
+    (32, 8, 128, 16, [513, 257, 31, 64], [0, 100, 400, 0], [2, 0, -1, 1], 128),
+    (8, 2, 64, 8, [700, 129, 2], None, [1, 1, 0], 64),
+    (8, 8, 64, 16, [97, 97, 33], [0, 0, 50], [0, 2, 1], 0),
+    (7, 1, 128, 8, [1000, 5], None, [2, 0], 256),
+    (64, 8, 128, 8, [160, 320], None, [1, 2], 64),
+]
+
+
+@pytest.mark.parametrize("n_q,n_kv,d,r,lens,starts,agents,split", QKVO_CASES)
+def test_decode_qkvo_cases(n_q, n_kv, d, r, lens, starts, agents, split):
+    """Decode with LoRA on the keys: ragged lengths, shared and offset rows, mixed agents (incl. the
+    adapter-free view), several split sizes; every request against the oracle."""
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype="bf16")
+    rows = None if starts is None else max(a + b for a, b in zip(starts, lens))
+    c = W.random_decode_qkvo((330, n_q, n_kv, d, r, len(lens)), s, lens, starts, rows, agents)
+    say(f"decode qkvo n_q={n_q} n_kv={n_kv} d={d} r={r} lens={lens} split={split}")
+    check(run_decode_qkvo(c, split), ref_decode_qkvo(c), "bf16", f"qkvo {n_q}/{n_kv} d={d} r={r}")
+
+
+def test_decode_qkvo_llama_long_sampled_requests():
+    """Three of the 16 x 66,400-token requests with LoRA on the keys, at the split the benchmark's
+    full batch uses, against the oracle."""
+    reqs = [0, 7, 15]
+    say("decode qkvo llama 66400: generating inputs")
+    c = W.llama_long_decode_qkvo(requests=reqs)
+    split = lra.lra_attn_decode_default_split(16, 8, 66400)
+    say(f"decode qkvo llama 66400: running (keys_per_split={split})")
+    got = run_decode_qkvo(c, split)
+    say("decode qkvo llama 66400: oracle")
+    check(got, ref_decode_qkvo(c), "bf16")
+
+
+def test_decode_qkvo_reduces_to_plain_decode_bits():
+    """B_k = 0 makes every rank-r score part exactly zero: the output equals lra_attn_decode's bit for
+    bit at the same split. All-adapter-free requests read none of K_lr / B_k (NaN here) and equal
+    the plain decode too."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode_qkvo((331,), s, [400, 130, 64], [0, 100, 300], 400, [2, 0, 1])
+    zero = W.to_storage(np.zeros(c.B_k.shape, np.float32), "bf16")
+    say("decode qkvo B_k = 0")
+    assert np.array_equal(run_decode_qkvo(c, 128, B_k=zero), run_decode(c.base, 128))
+    nan = lambda t: W.to_storage(np.full(t.shape, np.nan, np.float32), "bf16")
+    free = np.full(3, -1, np.int32)
+    say("decode qkvo adapter-free with NaN key operands")
+    got = run_decode_qkvo(c, 128, K_lr=nan(c.K_lr), B_k=nan(c.B_k), agent=free)
+    plain = W.DecodeBatch(s, c.base.Q, c.base.K, c.base.V, c.base.V_lr, c.base.B, c.base.kv_start, c.base.kv_len, free)
+    assert np.array_equal(got, run_decode(plain, 128))
+
+
+def test_decode_qkvo_key_part_matters_and_agents_are_isolated():
+    s = W.LLAMA_SHAPE
+    c = W.random_decode_qkvo((332,), s, [256, 256], None, None, [2, 2])
+    got = run_decode_qkvo(c)
+    assert np.max(np.abs(got - run_decode(c.base))) > 0.05
+    klr = c.K_lr.as_f64().astype(np.float32)
+    klr[:, : 2 * s.rank] = np.nan   # agents 0 and 1
+    assert np.array_equal(got, run_decode_qkvo(c, K_lr=W.to_storage(klr, "bf16")))
+
+
+def test_decode_qkvo_fp16_range_and_invalid_requests():
+    """A query entry beyond the fp16 range turns that head's output to NaN (its rank-r score part is
+    NaN); an invalid agent gives NaN rows; every other head and request stays correct."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode_qkvo((333,), s, [200, 150, 90], None, None, [0, 1, 2])
+    q = c.base.Q.as_f64().astype(np.float32)
+    q[1, 5, 3] = 1e5
+    Qb = W.to_storage(q, "bf16")
+    agents = np.array([0, 1, 7], np.int32)
+    got = run_decode_qkvo(c, agent=agents, Q=Qb)
+    assert np.all(np.isnan(got[1, 5])) and np.all(np.isnan(got[2]))
+    ok_heads = [h for h in range(s.n_q) if h != 5]
+    ref = ref_decode_qkvo(c, requests=[0, 1], Q=Qb)
+    check(got[0], ref[0], "bf16")
+    check(got[1, ok_heads], ref[1, ok_heads], "bf16")

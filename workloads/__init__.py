@@ -467,6 +467,40 @@ def random_decode(key: Sequence[int], s: Shape, kv_lens: Sequence[int], kv_start
     return DecodeBatch(s, Q, K, V, V_lr, B, kv_starts, kv_lens, np.asarray(agents, np.int32))
 
 
+@dataclass
+class QkvoDecodeBatch:
+    """A decode batch with LoRA on the keys as well (the qkvo configuration)."""
+    base: DecodeBatch
+    K_lr: HostTensor         # [rows, n_agents * rank]
+    B_k: HostTensor          # [n_agents, rank, n_kv * d]
+    cos: np.ndarray          # float32 [>= max_kv_len, d/2], row = a request's key position
+    sin: np.ndarray
+
+
+def random_decode_qkvo(key: Sequence[int], s: Shape, kv_lens: Sequence[int], kv_starts: Optional[Sequence[int]] = None,
+                       rows: Optional[int] = None, agents: Optional[Sequence[int]] = None, b_std: float = 0.05,
+                       bk_std: float = 0.3) -> QkvoDecodeBatch:
+    """random_decode plus K_lr ~ N(0, 1), B_k ~ N(0, bk_std^2) and rotary tables of max(kv_lens) rows."""
+    key = tuple(key)
+    base = random_decode(key, s, kv_lens, kv_starts, rows, agents, b_std)
+    K_lr = normal(key + (T_KLR,), (base.K.shape[0], s.n_agents * s.rank), 1.0, s.dtype)
+    B_k = normal(key + (T_BK,), (s.n_agents, s.rank, s.d_kv), bk_std, s.dtype)
+    cos, sin = rope_tables(max(1, base.max_kv_len), s.d_head)
+    return QkvoDecodeBatch(base, K_lr, B_k, cos, sin)
+
+
+def llama_long_decode_qkvo(n_req: int = 16, L: int = 66400, requests: Optional[Sequence[int]] = None) -> QkvoDecodeBatch:
+    """The 16 x 66,400 decode above with LoRA on the keys as well: request b's K_lr rows from its own
+    stream, B_k ~ N(0, 0.3^2), rotary tables of L rows."""
+    s = LLAMA_SHAPE
+    reqs = list(range(n_req)) if requests is None else list(requests)
+    base = llama_long_decode(n_req, L, reqs)
+    Klr = [normal((LLAMA_LONG_DECODE, 0, b, T_KLR), (L, s.n_agents * s.rank), 1.0, s.dtype).data for b in reqs]
+    B_k = normal((LLAMA_LONG_DECODE, 0, 10_000, T_BK), (s.n_agents, s.rank, s.d_kv), 0.3, s.dtype)
+    cos, sin = rope_tables(L, s.d_head)
+    return QkvoDecodeBatch(base, HostTensor(np.concatenate(Klr), s.dtype), B_k, cos, sin)
+
+
 def random_prefill(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int = 0, b_std: float = 0.05) -> PrefillCase:
     key = tuple(key)
     L = L_P + L_C

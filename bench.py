@@ -212,7 +212,26 @@ def bench_long_decode(args, torch, lra, W, out):
         "ms": round(ms_p, 4), "gbs": round(gbs_p, 1), "bytes": nbytes, "frac": round(gbs_p / HBM_PEAK_GBS, 4),
         "bound": "hbm", "page_size": P, "n_pages": n_pages, "keys_per_split": split_p,
         "block_table": "seeded permutation of all pages"}
-    del Q, K, V, L, B, O, ws, ws_p, Kp, Vp, Lp, table
+    # LoRA on the keys as well (qkvo): the key score pass plus the decode; algorithmic bytes add each
+    # request's K_lr slice (r values per key) and one read of the rotary table rows (d/2 cos + sin)
+    Klr_h, Bk_h, cos_h, sin_h = W.llama_long_decode_key_lora()
+    Klr, Bk = upload(Klr_h, torch), upload(Bk_h, torch)
+    rc, rs = torch.from_numpy(cos_h).cuda(), torch.from_numpy(sin_h).cuda()
+    ws_k = torch.empty(lra.lra_attn_decode_qkvo_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank,
+                                                                c.max_kv_len, 0), dtype=torch.uint8, device="cuda")
+
+    def step_qkvo():
+        lra.lra_attn_decode_qkvo(Q, K, V, L, Klr, ks, kl, c.max_kv_len, B, Bk, rc, rs, ag, s.scale, 0,
+                                 ws_k, O)
+
+    log("[bench] decode 16 x 66400 with LoRA on the keys")
+    ms_k = time_launches(step_qkvo, args.steps, args.warmup, torch)
+    nbytes_k = nbytes + int(sum(int(x) for x in c.kv_len)) * s.rank * 2 + int(c.max_kv_len) * s.d_head * 4
+    gbs_k = nbytes_k / (ms_k * 1e-3) / 1e9
+    out["decode_qkvo_llama_b16_L66400"] = {
+        "ms": round(ms_k, 4), "gbs": round(gbs_k, 1), "bytes": nbytes_k, "frac": round(gbs_k / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "keys": "K_base + RoPE(K_lr B_k), rank 8; key score pass + decode"}
+    del Q, K, V, L, B, O, ws, ws_p, Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
     torch.cuda.empty_cache()
 
 

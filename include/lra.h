@@ -278,8 +278,8 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
  * alone and read none of the key-side operands. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED);
  * max_kv_len <= 2^27. Precision: the base part of a score is as in lra_attn_decode; the rank-r
  * part is computed from fp16 operands (the rotated rank-r key and the query, fp32 accumulation)
- * and stored as fp16. A request whose query, rotated rank-r key or rank-r score part leaves the
- * fp16 range (|x| > 65504) gets NaN output (for the heads concerned).
+ * and stored as fp16. A query entry, rotated rank-r key entry or rank-r score part that rounds
+ * beyond the fp16 range (|x| >= 65520) gives NaN output for the heads concerned.
  */
 size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
                                             int32_t rank, int64_t max_kv_len, int32_t keys_per_split);

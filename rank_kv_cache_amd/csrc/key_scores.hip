@@ -1,0 +1,199 @@
+// Decode with LoRA on the key projection (the qkvo configuration) on gfx950: the rank-r part of
+// every score.
+//
+// LRAgent page (limitations): with LoRA on the keys, request b's key t is
+// K_base + RoPE_t(K_lr B_k), and the rotation between the up-projection and the dot product keeps
+// the rank-r part from being moved behind the softmax. Its contribution to the score of query head
+// h (KV head g) is
+//     S[t, h] = q_h . RoPE_t(y_t),    y_t = K_lr[t, agent] B_k[agent][:, g*d .. g*d+d].
+// With rotate-half pairing (element i < d/2 with i + d/2, cosine c_ti and sine s_ti) this is
+//     S[t, h] = sum_{r, i} (K_lr[t, r] c_ti) P_h[r, i] + (K_lr[t, r] s_ti) M_h[r, i],
+//     P_h[r, i] = B[r, i] q_h[i] + B[r, i + d/2] q_h[i + d/2],
+//     M_h[r, i] = B[r, i] q_h[i + d/2] - B[r, i + d/2] q_h[i],
+// (B = B_k[agent] restricted to KV head g), i.e. a dense product of per-key features
+// F_t = K_lr[t, :] (x) [c_t, s_t] (d*r values) with per-head weights W_h = [P_h, M_h]. The weights
+// depend on the request and head only, so one small pass computes them; the rotation then costs one
+// packed fp16 multiply per pair of features instead of a rotation per key and KV head, and the
+// reduction over d*r runs on 16x16x32 fp16 matrix-core steps.
+//
+// Mapping of the score pass: one workgroup = 4 waves = one 512-key block of one request and 16 or
+// 32 query heads (the weights of those heads staged in LDS). A wave takes 16 keys at a time. Step s
+// of the reduction covers 32 features: lane (key n, group q) builds its 8 = K_lr[t, r0 .. r0+7] x
+// trig(ci) in registers (trig = cosine for ci < d/2, else sine), and reads the matching 8 weights
+// of head n from LDS. The feature order k = ci * r + rr is shared by both operands; ci runs over a
+// contiguous range per lane group, so each lane reads its rotary entries as 16-byte runs.
+// Output lane (head n, group q) holds the scores of keys 4q .. 4q+3, stored as fp16 (NaN where the
+// value is not a finite fp16 number).
+#include "lra_device.h"
+#include "lra_kernels.h"
+
+namespace lra {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ bool key_score_request_ok(const KeyScoreParams& p, int64_t start, int32_t len, int32_t a) {
+    // adapter-free and invalid requests need no scores (the decode adds none / writes NaN)
+    return len > 0 && int64_t(len) <= p.max_kv_len && start >= 0 && start + int64_t(len) <= p.kv_rows && a >= 0 &&
+           a < p.n_agents;
+}
+
+// W[b, h, ci*R + r] = P_h[r, ci] (ci < d/2) or M_h[r, ci - d/2], as fp16; one workgroup per
+// (request, query head)
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void key_weights_kernel(KeyScoreParams p) {
+    const int b = blockIdx.x, h = blockIdx.y;
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b], a = p.agent[b];
+    if (!key_score_request_ok(p, start, len, a)) return;
+    const int g = h / p.G;
+    const int64_t kv_stride = int64_t(p.n_kv) * D;
+    const uint16_t* __restrict__ Bk = static_cast<const uint16_t*>(p.Bk) + int64_t(a) * R * kv_stride + int64_t(g) * D;
+    const uint16_t* __restrict__ qh = static_cast<const uint16_t*>(p.Q) + (int64_t(b) * p.n_q + h) * D;
+    uint16_t* __restrict__ W = p.W + (int64_t(b) * p.n_q + h) * (D * R);
+    for (int idx = threadIdx.x; idx < D * R; idx += kThreads) {
+        const int ci = idx / R, r = idx - ci * R;
+        const int i = ci < D / 2 ? ci : ci - D / 2;
+        const float bl = bf16_to_f32(Bk[int64_t(r) * kv_stride + i]);
+        const float bh = bf16_to_f32(Bk[int64_t(r) * kv_stride + i + D / 2]);
+        const float ql = bf16_to_f32(qh[i]), qu = bf16_to_f32(qh[i + D / 2]);
+        const float w = ci < D / 2 ? bl * ql + bh * qu : bl * qu - bh * ql;
+        W[idx] = uint16_t(pack_f16x2(w, 0.f) & 0xffffu);
+    }
+}
+
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t x, uint32_t y) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, x) * __builtin_bit_cast(f16x2_t, y));
+}
+
+template <int D, int R, int HB>
+__global__ __launch_bounds__(kThreads) void key_scores_kernel(KeyScoreParams p) {
+    constexpr int KF = D * R;          // features per key
+    constexpr int NS = KF / 32;        // reduction steps
+    constexpr int SLOTS = 32 / R;      // rotary entries per step; R/8 lane groups share one
+    constexpr int LDW = KF + 8;        // weight row in LDS (halves), padded by 16 bytes
+    static_assert((SLOTS / 2) * NS == D / 2, "each lane group owns a contiguous run of one table");
+    __shared__ uint16_t ws[HB * 16][LDW];
+
+    // request fastest: the workgroups of one key block (the same rotary table rows) run together
+    const int b = blockIdx.x, blk = blockIdx.y, h0 = blockIdx.z * (HB * 16);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, n = lane & 15, q = lane >> 4;
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b], a = p.agent[b];
+    const int32_t len32 = key_score_request_ok(p, start, len, a) ? (len + 31) / 32 * 32 : 0;   // keys the decode reads
+    if (int64_t(blk) * kKeyScoreBlock >= len32) return;   // workgroup-uniform
+    const int nhq = min(HB * 16, p.n_q - h0);
+
+    // this workgroup's head weights; rows past n_q are zero
+    const uint16_t* __restrict__ Wg = p.W + (int64_t(b) * p.n_q + h0) * KF;
+    for (int idx = tid; idx < HB * 16 * (KF / 8); idx += kThreads) {
+        const int row = idx / (KF / 8), c = (idx - row * (KF / 8)) * 8;
+        const uint4 v = row < nhq ? *reinterpret_cast<const uint4*>(Wg + int64_t(row) * KF + c) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&ws[row][c]) = v;
+    }
+    __syncthreads();
+
+    // lane group q: rotary slot (cosine for the first half of the slots), ranks r0 .. r0+7
+    const int slot = q / (R / 8), r0 = 8 * (q % (R / 8));
+    const float* __restrict__ tab = (slot < SLOTS / 2 ? p.rope_cos : p.rope_sin) + (slot % (SLOTS / 2)) * NS;
+    const int kbase = slot * NS * R + r0;   // feature of step s: kbase + s*R .. +7
+    const bf16* __restrict__ Klr = static_cast<const bf16*>(p.Klr);
+    // keys per pass: KT tiles of 16 (one measured fastest: 4 cut the LDS weight reads but not the
+    // time, which the rotary-table loads set)
+    constexpr int KT = 1;
+    const int jend = min(len32, (blk + 1) * kKeyScoreBlock);
+    for (int j0 = blk * kKeyScoreBlock + 16 * KT * wv; j0 < jend; j0 += 4 * 16 * KT) {
+        uint32_t l16[KT][4];
+        const float* __restrict__ trow[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int jn = min(j0 + 16 * kt + n, len - 1);   // later keys repeat the last row (masked by the decode)
+            Vec<bf16, 8> lr;
+            lr.load(Klr + (start + jn) * p.ld_klr + int64_t(a) * R + r0);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l16[kt][w] = pack_f16x2(bf16_lo(lr.w[w]), bf16_hi(lr.w[w]));
+            trow[kt] = tab + int64_t(jn) * (D / 2);
+        }
+
+        f32x4 acc[KT][HB];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) acc[kt][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // rotary entries of 4 steps, loaded one group of steps ahead
+        float4 tn[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) tn[kt] = *reinterpret_cast<const float4*>(trow[kt]);
+#pragma unroll 2
+        for (int s0 = 0; s0 < NS; s0 += 4) {
+            float tv[KT][4];
+            const int sn = min(s0 + 4, NS - 4);   // the last group reloads itself (unused)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                tv[kt][0] = tn[kt].x; tv[kt][1] = tn[kt].y; tv[kt][2] = tn[kt].z; tv[kt][3] = tn[kt].w;
+                tn[kt] = *reinterpret_cast<const float4*>(trow[kt] + sn);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = kbase + (s0 + u) * R;
+                H8 fb[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    const uint4 wb = *reinterpret_cast<const uint4*>(&ws[16 * hb + n][k]);
+                    fb[hb].w[0] = wb.x; fb[hb].w[1] = wb.y; fb[hb].w[2] = wb.z; fb[hb].w[3] = wb.w;
+                }
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const uint32_t t2 = pack_f16x2(tv[kt][u], tv[kt][u]);
+                    H8 fa;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) fa.w[w] = pk_mul_f16(l16[kt][w], t2);
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) acc[kt][hb] = mma16x16x32_f16(fa, fb[hb], acc[kt][hb]);
+                }
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const int jk = j0 + 16 * kt + 4 * q;   // this lane's first key
+            if (jk >= len32) continue;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                const int hl = 16 * hb + n;
+                if (hl < nhq) {
+                    float sv[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        sv[x] = fabsf(acc[kt][hb][x]) <= kF16Max ? acc[kt][hb][x] : __uint_as_float(0x7fc00000u);
+                    uint16_t* dst = p.S + (int64_t(b) * p.n_q + h0 + hl) * p.ks_stride + jk;
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16x2(sv[0], sv[1]), pack_f16x2(sv[2], sv[3]));
+                }
+            }
+        }
+    }
+}
+
+template <int D, int R>
+void launch_dr(const KeyScoreParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((key_weights_kernel<D, R>), dim3(unsigned(p.batch), unsigned(p.n_q)), dim3(kThreads), 0, stream, p);
+    constexpr int HB = D * R <= 1024 ? 2 : 1;   // weights of 16*HB heads in LDS (about 66 KB)
+    const dim3 grid(unsigned(p.batch), unsigned((p.max_kv_len + kKeyScoreBlock - 1) / kKeyScoreBlock),
+                    unsigned((p.n_q + 16 * HB - 1) / (16 * HB)));
+    hipLaunchKernelGGL((key_scores_kernel<D, R, HB>), grid, dim3(kThreads), 0, stream, p);
+}
+
+}  // namespace
+
+hipError_t launch_key_scores(const KeyScoreParams& p, hipStream_t stream) {
+    if (p.d_head == 64) {
+        if (p.rank == 8) launch_dr<64, 8>(p, stream);
+        else launch_dr<64, 16>(p, stream);
+    } else {
+        if (p.rank == 8) launch_dr<128, 8>(p, stream);
+        else launch_dr<128, 16>(p, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lra

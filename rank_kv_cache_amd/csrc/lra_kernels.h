@@ -117,8 +117,9 @@ hipError_t launch_key_expand(const KeyExpandParams& p, hipStream_t stream);
 
 // Decode with LoRA on the keys: the rank-r part of every score,
 // S[(b*n_q + h)*ks_stride + j] = fp16(Q[b, h] . RoPE_j(K_lr[kv_start[b] + j, agent_b] B_k[agent_b][:, g])),
-// for keys j < round_up(kv_len[b], 32) (later keys repeat the last row); NaN where the rotated
-// rank-r key or the query leaves the fp16 range. Requests that are invalid or adapter-free are skipped.
+// for keys j < round_up(kv_len[b], 32) (later keys repeat the last row); NaN where it is not a
+// finite fp16 number. Requests that are invalid or adapter-free are skipped. W holds the per-head
+// weights of the features K_lr (x) [cos, sin] (d_head*rank fp16 per request and query head).
 struct KeyScoreParams {
     const void* Q;              // bf16 [batch x n_q x d_head]
     const void* Klr;            // bf16 [kv_rows x ld_klr]
@@ -129,11 +130,12 @@ struct KeyScoreParams {
     const int32_t* kv_len;
     const int32_t* agent;
     uint16_t* S;                // fp16 [batch x n_q x ks_stride]
+    uint16_t* W;                // fp16 [batch x n_q x d_head*rank]
     int64_t kv_rows, max_kv_len, ld_klr, ks_stride;
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
 };
 hipError_t launch_key_scores(const KeyScoreParams& p, hipStream_t stream);
-constexpr int kKeyScoreBlock = 256;   // keys per workgroup of the key score pass
+constexpr int kKeyScoreBlock = 512;   // keys per workgroup of the key score pass
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries
 int prefill_pairs(int64_t L_C, int G);

@@ -99,12 +99,14 @@ def test_decode_qkvo_rejects_bad_arguments(kw, status):
 
 
 def test_decode_qkvo_workspace_size():
-    # the decode workspace, 256-aligned, then fp16 key scores [batch x n_q x round_up(max_kv_len, 64)]
+    # the decode workspace, 256-aligned, then fp16 key scores [batch x n_q x round_up(max_kv_len, 64)],
+    # then fp16 score weights [batch x n_q x d_head*rank]
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
-    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2
-    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, then 2 x 4 x 64 fp16 scores
-    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2
+    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2 + 16 * 32 * 1024 * 2
+    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, 2 x 4 x 64 fp16
+    # scores, 2 x 4 x 512 fp16 weights
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2 + 2 * 4 * 512 * 2
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 

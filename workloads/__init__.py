@@ -489,16 +489,21 @@ def random_decode_qkvo(key: Sequence[int], s: Shape, kv_lens: Sequence[int], kv_
     return QkvoDecodeBatch(base, K_lr, B_k, cos, sin)
 
 
-def llama_long_decode_qkvo(n_req: int = 16, L: int = 66400, requests: Optional[Sequence[int]] = None) -> QkvoDecodeBatch:
-    """The 16 x 66,400 decode above with LoRA on the keys as well: request b's K_lr rows from its own
-    stream, B_k ~ N(0, 0.3^2), rotary tables of L rows."""
+def llama_long_decode_key_lora(n_req: int = 16, L: int = 66400, requests: Optional[Sequence[int]] = None):
+    """The key-side operands of the 16 x 66,400 decode with LoRA on the keys: (K_lr, B_k, cos, sin).
+    Request b's K_lr rows come from its own stream, B_k ~ N(0, 0.3^2), rotary tables of L rows."""
     s = LLAMA_SHAPE
     reqs = list(range(n_req)) if requests is None else list(requests)
-    base = llama_long_decode(n_req, L, reqs)
     Klr = [normal((LLAMA_LONG_DECODE, 0, b, T_KLR), (L, s.n_agents * s.rank), 1.0, s.dtype).data for b in reqs]
     B_k = normal((LLAMA_LONG_DECODE, 0, 10_000, T_BK), (s.n_agents, s.rank, s.d_kv), 0.3, s.dtype)
     cos, sin = rope_tables(L, s.d_head)
-    return QkvoDecodeBatch(base, HostTensor(np.concatenate(Klr), s.dtype), B_k, cos, sin)
+    return HostTensor(np.concatenate(Klr), s.dtype), B_k, cos, sin
+
+
+def llama_long_decode_qkvo(n_req: int = 16, L: int = 66400, requests: Optional[Sequence[int]] = None) -> QkvoDecodeBatch:
+    """The 16 x 66,400 decode above with LoRA on the keys as well."""
+    base = llama_long_decode(n_req, L, requests)
+    return QkvoDecodeBatch(base, *llama_long_decode_key_lora(n_req, L, requests))
 
 
 def random_prefill(key: Sequence[int], s: Shape, L_P: int, L_C: int, agent: int = 0, b_std: float = 0.05) -> PrefillCase:

@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 (and fp16) matrix-core peak, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ("rank_kv_cache_amd/csrc/decode.hip", "rank_kv_cache_amd/csrc/lra_device.h")
+PREFILL_SOURCES = ("rank_kv_cache_amd/csrc/prefill.hip", "rank_kv_cache_amd/csrc/lra_device.h")
 
 
 def log(*a):
@@ -62,6 +63,20 @@ def source_hash(paths) -> str:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def counter_fields(name: str, sources) -> dict:
+    """The fields of a committed counter summary, or {} when its kernel source has changed since."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return {}
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    return fields if fields.get("source_sha256") == source_hash(sources) else {}
 
 
 def counter_traffic(name: str, sources) -> tuple:
@@ -255,6 +270,13 @@ def bench_prefill(args, torch, lra, W, out):
     out["prefill_llama_LP16384_LC2048_r8"] = {
         "ms": round(ms, 4), "tflops": round(tf, 2), "flops": fl, "peak_tflops": BF16_PEAK_TFLOPS,
         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma", "reps": reps}
+    # matrix-core counters of the same kernel (committed summary, used only while its source matches)
+    mf = counter_fields("prefill_llama_LP16384_LC2048_mfma_counters.txt", PREFILL_SOURCES)
+    if mf:
+        out["prefill_llama_LP16384_LC2048_r8"]["counters"] = {
+            "mfma_util": round(float(mf["mfma_util_percent"]) / 100.0, 4),
+            "mfma_flops_per_launch": int(float(mf["mfma_flops_per_launch"])),
+            "source": "profiles/prefill_llama_LP16384_LC2048_mfma_counters.txt"}
 
     # the same work as four chunk requests of 512 queries in one batched launch (request b: queries
     # 512b .., L_P = 16384 + 512b, all over the same cache rows)

@@ -406,13 +406,14 @@ struct DecodeKeyLora {
 
 int64_t key_score_stride(int64_t max_kv_len) { return (max_kv_len + 63) / 64 * 64; }
 
-// decode workspace, then (LoRA on the keys) the fp16 key scores [batch x n_q x stride] and the fp16
-// score weights [batch x n_q x d_head*rank], each part 256-aligned
+// decode workspace, then (LoRA on the keys) the fp16 key scores [batch x n_q x stride], the fp16
+// score weights [batch x n_q x d_head*rank] and the repacked rotary tables, each part 256-aligned
 size_t decode_qkvo_bytes(const DecodeLayout& L, int batch, int n_q, int d_head, int rank, int64_t max_kv_len,
-                         size_t* ks_off, size_t* w_off) {
+                         size_t* ks_off, size_t* w_off, size_t* t_off) {
     *ks_off = align_up(L.total, 256);
     *w_off = align_up(*ks_off + size_t(batch) * size_t(n_q) * size_t(key_score_stride(max_kv_len)) * 2, 256);
-    return *w_off + size_t(batch) * size_t(n_q) * size_t(d_head) * size_t(rank) * 2;
+    *t_off = align_up(*w_off + size_t(batch) * size_t(n_q) * size_t(d_head) * size_t(rank) * 2, 256);
+    return *t_off + lra::key_score_table_bytes(max_kv_len, d_head, rank);
 }
 
 int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
@@ -450,8 +451,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     }
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
     const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
-    size_t ks_off = 0, w_off = 0;
-    const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off) : 0)
+    size_t ks_off = 0, w_off = 0, t_off = 0;
+    const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off, &t_off) : 0)
                            : L.total;
     if (need) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
@@ -474,6 +475,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
         e.kv_start = kv_start; e.kv_len = kv_len; e.agent = agent;
         e.S = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ks_off);
         e.W = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + w_off);
+        e.Tp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + t_off);
         e.kv_rows = kv_rows; e.max_kv_len = max_kv_len; e.ld_klr = kl->ld_klr; e.ks_stride = key_score_stride(max_kv_len);
         e.batch = batch; e.n_q = n_q; e.n_kv = n_kv; e.G = n_q / n_kv; e.n_agents = n_agents; e.d_head = d_head; e.rank = rank;
         if (int s = hip_status(lra::launch_key_scores(e, static_cast<hipStream_t>(stream)), "lra_attn_decode_qkvo key scores"))
@@ -503,9 +505,9 @@ LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_
                                                        int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || d_head <= 0 || rank <= 0 || max_kv_len <= 0 || keys_per_split < 0) return 0;
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    size_t ks_off = 0, w_off = 0;
+    size_t ks_off = 0, w_off = 0, t_off = 0;
     return decode_qkvo_bytes(decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk), batch, n_q, d_head, rank,
-                             max_kv_len, &ks_off, &w_off);
+                             max_kv_len, &ks_off, &w_off, &t_off);
 }
 
 LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,

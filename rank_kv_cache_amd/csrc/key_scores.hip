@@ -21,7 +21,9 @@
 // of the reduction covers 32 features: lane (key n, group q) builds its 8 = K_lr[t, r0 .. r0+7] x
 // trig(ci) in registers (trig = cosine for ci < d/2, else sine), and reads the matching 8 weights
 // of head n from LDS. The feature order k = ci * r + rr is shared by both operands; ci runs over a
-// contiguous range per lane group, so each lane reads its rotary entries as 16-byte runs.
+// contiguous range per lane group. A small pass first repacks the rotary tables as fp16 in the
+// lanes' order (per 16-key tile and group of 8 steps, 1 KB per wave): read in their natural layout,
+// each load instruction touched 64 cache lines and those loads set the pass's time.
 // Output lane (head n, group q) holds the scores of keys 4q .. 4q+3, stored as fp16 (NaN where the
 // value is not a finite fp16 number).
 #include "lra_device.h"
@@ -96,87 +98,87 @@ __global__ __launch_bounds__(kThreads) void key_scores_kernel(KeyScoreParams p) 
 
     // lane group q: rotary slot (cosine for the first half of the slots), ranks r0 .. r0+7
     const int slot = q / (R / 8), r0 = 8 * (q % (R / 8));
-    const float* __restrict__ tab = (slot < SLOTS / 2 ? p.rope_cos : p.rope_sin) + (slot % (SLOTS / 2)) * NS;
     const int kbase = slot * NS * R + r0;   // feature of step s: kbase + s*R .. +7
     const bf16* __restrict__ Klr = static_cast<const bf16*>(p.Klr);
-    // keys per pass: KT tiles of 16 (one measured fastest: 4 cut the LDS weight reads but not the
-    // time, which the rotary-table loads set)
-    constexpr int KT = 1;
     const int jend = min(len32, (blk + 1) * kKeyScoreBlock);
-    for (int j0 = blk * kKeyScoreBlock + 16 * KT * wv; j0 < jend; j0 += 4 * 16 * KT) {
-        uint32_t l16[KT][4];
-        const float* __restrict__ trow[KT];
+    for (int j0 = blk * kKeyScoreBlock + 16 * wv; j0 < jend; j0 += 4 * 16) {
+        const int jn = min(j0 + n, len - 1);   // later keys repeat the last row (masked by the decode)
+        Vec<bf16, 8> lr;
+        lr.load(Klr + (start + jn) * p.ld_klr + int64_t(a) * R + r0);
+        uint32_t l16[4];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            const int jn = min(j0 + 16 * kt + n, len - 1);   // later keys repeat the last row (masked by the decode)
-            Vec<bf16, 8> lr;
-            lr.load(Klr + (start + jn) * p.ld_klr + int64_t(a) * R + r0);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) l16[kt][w] = pack_f16x2(bf16_lo(lr.w[w]), bf16_hi(lr.w[w]));
-            trow[kt] = tab + int64_t(jn) * (D / 2);
-        }
+        for (int w = 0; w < 4; ++w) l16[w] = pack_f16x2(bf16_lo(lr.w[w]), bf16_hi(lr.w[w]));
+        // this tile's rotary entries, 8 steps per 16-byte load (the packed table's lane order)
+        const uint4* __restrict__ tp = reinterpret_cast<const uint4*>(p.Tp) + int64_t(j0 / 16) * (NS / 8) * 64 + lane;
 
-        f32x4 acc[KT][HB];
+        f32x4 acc[HB];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) acc[kt][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // rotary entries of 4 steps, loaded one group of steps ahead
-        float4 tn[KT];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) tn[kt] = *reinterpret_cast<const float4*>(trow[kt]);
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 tn0 = tp[0], tn1 = tp[min(1, NS / 8 - 1) * 64];   // loaded two groups of 8 steps ahead
 #pragma unroll 2
-        for (int s0 = 0; s0 < NS; s0 += 4) {
-            float tv[KT][4];
-            const int sn = min(s0 + 4, NS - 4);   // the last group reloads itself (unused)
+        for (int s0 = 0; s0 < NS; s0 += 8) {
+            const uint32_t th[4] = {tn0.x, tn0.y, tn0.z, tn0.w};
+            tn0 = tn1;
+            tn1 = tp[min(s0 / 8 + 2, NS / 8 - 1) * 64];   // the last groups reload the last (unused)
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                tv[kt][0] = tn[kt].x; tv[kt][1] = tn[kt].y; tv[kt][2] = tn[kt].z; tv[kt][3] = tn[kt].w;
-                tn[kt] = *reinterpret_cast<const float4*>(trow[kt] + sn);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 const int k = kbase + (s0 + u) * R;
-                H8 fb[HB];
+                // the step's rotary entry in both halves
+                const uint32_t t2 = __builtin_amdgcn_perm(th[u >> 1], th[u >> 1], (u & 1) ? 0x07060706u : 0x05040504u);
+                H8 fa;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) fa.w[w] = pk_mul_f16(l16[w], t2);
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     const uint4 wb = *reinterpret_cast<const uint4*>(&ws[16 * hb + n][k]);
-                    fb[hb].w[0] = wb.x; fb[hb].w[1] = wb.y; fb[hb].w[2] = wb.z; fb[hb].w[3] = wb.w;
-                }
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const uint32_t t2 = pack_f16x2(tv[kt][u], tv[kt][u]);
-                    H8 fa;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) fa.w[w] = pk_mul_f16(l16[kt][w], t2);
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) acc[kt][hb] = mma16x16x32_f16(fa, fb[hb], acc[kt][hb]);
+                    H8 fb;
+                    fb.w[0] = wb.x; fb.w[1] = wb.y; fb.w[2] = wb.z; fb.w[3] = wb.w;
+                    acc[hb] = mma16x16x32_f16(fa, fb, acc[hb]);
                 }
             }
         }
+        const int jk = j0 + 4 * q;   // this lane's first key
+        if (jk >= len32) continue;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            const int jk = j0 + 16 * kt + 4 * q;   // this lane's first key
-            if (jk >= len32) continue;
+        for (int hb = 0; hb < HB; ++hb) {
+            const int hl = 16 * hb + n;
+            if (hl < nhq) {
+                float sv[4];
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                const int hl = 16 * hb + n;
-                if (hl < nhq) {
-                    float sv[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        sv[x] = fabsf(acc[kt][hb][x]) <= kF16Max ? acc[kt][hb][x] : __uint_as_float(0x7fc00000u);
-                    uint16_t* dst = p.S + (int64_t(b) * p.n_q + h0 + hl) * p.ks_stride + jk;
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16x2(sv[0], sv[1]), pack_f16x2(sv[2], sv[3]));
-                }
+                for (int x = 0; x < 4; ++x) sv[x] = fabsf(acc[hb][x]) <= kF16Max ? acc[hb][x] : __uint_as_float(0x7fc00000u);
+                uint16_t* dst = p.S + (int64_t(b) * p.n_q + h0 + hl) * p.ks_stride + jk;
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16x2(sv[0], sv[1]), pack_f16x2(sv[2], sv[3]));
             }
         }
     }
 }
 
+// The rotary tables in the score kernel's lane order, as fp16: entry ((tile*(NS/8) + g)*64 + lane)
+// holds, for key 16*tile + (lane & 15) and lane group q = lane >> 4, the 8 table values of steps
+// 8g .. 8g+7 of that group's slot. A tile's group is then one contiguous 1 KB load per wave.
+// Positions past the table's last row repeat it.
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void rope_pack_kernel(KeyScoreParams p) {
+    constexpr int NS = D * R / 32, SLOTS = 32 / R;
+    const int64_t e = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);   // (tile, group)
+    const int64_t n_tiles = key_score_table_tiles(p.max_kv_len);
+    if (e >= n_tiles * (NS / 8)) return;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int64_t tile = e / (NS / 8);
+    const int g = int(e - tile * (NS / 8));
+    const int slot = q / (R / 8);
+    const int64_t j = min<int64_t>(tile * 16 + n, p.max_kv_len - 1);
+    const float* row = (slot < SLOTS / 2 ? p.rope_cos : p.rope_sin) + j * (D / 2) + (slot % (SLOTS / 2)) * NS + 8 * g;
+    const float4 a = *reinterpret_cast<const float4*>(row), b = *reinterpret_cast<const float4*>(row + 4);
+    reinterpret_cast<uint4*>(p.Tp)[e * 64 + lane] =
+        make_uint4(pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w));
+}
+
 template <int D, int R>
 void launch_dr(const KeyScoreParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((key_weights_kernel<D, R>), dim3(unsigned(p.batch), unsigned(p.n_q)), dim3(kThreads), 0, stream, p);
+    const int64_t n_pack = key_score_table_tiles(p.max_kv_len) * (D * R / 32 / 8);   // (tile, group) pairs, one wave each
+    hipLaunchKernelGGL((rope_pack_kernel<D, R>), dim3(unsigned((n_pack + 3) / 4)), dim3(kThreads), 0, stream, p);
     constexpr int HB = D * R <= 1024 ? 2 : 1;   // weights of 16*HB heads in LDS (about 66 KB)
     const dim3 grid(unsigned(p.batch), unsigned((p.max_kv_len + kKeyScoreBlock - 1) / kKeyScoreBlock),
                     unsigned((p.n_q + 16 * HB - 1) / (16 * HB)));

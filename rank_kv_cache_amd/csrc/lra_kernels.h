@@ -131,10 +131,17 @@ struct KeyScoreParams {
     const int32_t* agent;
     uint16_t* S;                // fp16 [batch x n_q x ks_stride]
     uint16_t* W;                // fp16 [batch x n_q x d_head*rank]
+    uint16_t* Tp;               // fp16 rotary tables in the score kernel's lane order, key_score_table_bytes()
     int64_t kv_rows, max_kv_len, ld_klr, ks_stride;
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
 };
 hipError_t launch_key_scores(const KeyScoreParams& p, hipStream_t stream);
+// tiles of 16 keys of the repacked rotary tables: the score pass reads keys up to round_up(len, 32)
+__host__ __device__ inline int64_t key_score_table_tiles(int64_t max_kv_len) { return (max_kv_len + 31) / 32 * 2; }
+// bytes of the repacked rotary tables: per 16-key tile, d_head*rank/32 steps x 64 lanes x 2 bytes
+inline size_t key_score_table_bytes(int64_t max_kv_len, int d_head, int rank) {
+    return size_t(key_score_table_tiles(max_kv_len)) * size_t(d_head * rank / 32) * 128;
+}
 constexpr int kKeyScoreBlock = 512;   // keys per workgroup of the key score pass
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries

@@ -103,10 +103,10 @@ def test_decode_qkvo_workspace_size():
     # then fp16 score weights [batch x n_q x d_head*rank]
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
-    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2 + 16 * 32 * 1024 * 2
+    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128
     # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, 2 x 4 x 64 fp16
-    # scores, 2 x 4 x 512 fp16 weights
-    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2 + 2 * 4 * 512 * 2
+    # scores, 2 x 4 x 512 fp16 weights, then 2 tiles of 16 steps x 128 bytes of repacked tables
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2 + 2 * 4 * 512 * 2 + 2 * 16 * 128
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 

@@ -17,7 +17,8 @@
 //     workgroup and per SIMD; a wave stops multiplying after its own last visible key.
 //   * 64-key tiles are staged in LDS in their natural row layout with 128-bit stores, double
 //     buffered: the next tile's global loads are in flight while the current one is multiplied,
-//     one barrier per tile. The tile is consumed in two 32-key blocks.
+//     one barrier per tile. A wave takes the whole tile in one softmax step when it sees both of its
+//     32-key blocks (one block on its diagonal), which halves the per-step bookkeeping.
 //   * S^T = K Q^T: A operand = 16 keys x 8 d-elements of the K tile; output lane (q, n) holds keys
 //     4q..4q+3 of each 16-key group for query row n. The two groups of a block give the lane the 8
 //     keys it feeds as the B operand of O^T = V^T P^T, so P never leaves the lane.
@@ -29,10 +30,10 @@
 //   * one more 16-column tile holds the agent's V_lr slice (columns 0..r-1) and a column of ones:
 //     O_lr^T and the softmax normaliser l come out of the same matrix-core product as O (l is the
 //     sum of exactly the rounded P the products used). For r = 16 the ones column is a second tile.
-//   * online softmax per query row and 32-key block in base 2, scale*log2(e) folded into one fma
+//   * online softmax per query row and softmax step in base 2, scale*log2(e) folded into one fma
 //     per score. The reference max m only moves (and O, O_lr, l are rescaled) when a score of the
-//     block exceeds it by more than a factor 2^8 in P; otherwise P may reach 2^8, well inside fp16.
-//     Each lane tests its own 8 scores against that threshold; only when some lane of the wave
+//     step exceeds it by more than a factor 2^8 in P; otherwise P may reach 2^8, well inside fp16.
+//     Each lane tests its own 8 or 16 scores against that threshold; only when some lane of the wave
 //     crosses it is the row max reduced over the 4 lanes sharing a row (permlane swaps).
 //   * epilogue: gather O_lr and l of the row across its 4 lanes, add O_lr B_agent (B slice in LDS),
 //     divide by l, store in the input type (bf16 round-to-nearest-even)
@@ -337,23 +338,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const TV* vs = sh.v[buf];
         const TV* xs = sh.aux[buf];
 
-        // blocks of this tile holding a key visible to the wave (wave-uniform)
+        // blocks of this tile holding a key visible to the wave (wave-uniform); both blocks of a tile
+        // go through one softmax step when the wave sees them both
         const int nkb = min(NKB, max(0, (wave_end - t * kBK + 31) / 32));
-#pragma unroll 1
-        for (int kb2 = 0; kb2 < nkb; ++kb2) {
-            const int kblk = t * kBK + 32 * kb2;
-            // scores: lane (q, n) holds keys kblk + 16u + 4q + j (u = 0, 1; j = 0..3) of query row n
-            f32x4 sacc[MT][2];
+        auto step = [&](auto nb_tag) {
+            constexpr int NB = decltype(nb_tag)::value;   // 32-key blocks in this step
+            const int kblk = t * kBK;
+            // scores: lane (q, n) holds keys kblk + 16u + 4q + j (u < 2NB; j = 0..3) of query row n
+            f32x4 sacc[MT][2 * NB];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) sacc[mt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int u = 0; u < 2 * NB; ++u) sacc[mt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2 * NB; ++u)
 #pragma unroll
                 for (int i = 0; i < KCH; ++i) {
                     Vec<T, 8> ka;
-                    ka.load(&ks[(32 * kb2 + 16 * u + n) * LDK + 32 * i + 8 * q]);
+                    ka.load(&ks[(16 * u + n) * LDK + 32 * i + 8 * q]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         if constexpr (KLORA)
@@ -364,24 +366,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 }
 
             // online softmax per query row (raw scores; scale folded into the exponent)
-            PF pf[MT];
-            if (kblk + 32 > full_end) {
+            PF pf[MT][NB];
+            if (kblk + 32 * NB > full_end) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
+                    for (int u = 0; u < 2 * NB; ++u)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             if (kblk + 16 * u + 4 * q + j > qpos[mt]) sacc[mt][u][j] = -INFINITY;
             }
-            // a row moves its reference max only when P would otherwise exceed 2^8 (the first block
-            // always does: key 0 is visible to every row, so m stays finite)
             float lmx[MT];
             bool any_grow = false;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                lmx[mt] = fmaxf(fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3])),
-                                fmaxf(fmaxf(sacc[mt][1][0], sacc[mt][1][1]), fmaxf(sacc[mt][1][2], sacc[mt][1][3])));
+                float m = fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3]));
+#pragma unroll
+                for (int u = 1; u < 2 * NB; ++u)
+                    m = fmaxf(m, fmaxf(fmaxf(sacc[mt][u][0], sacc[mt][u][1]), fmaxf(sacc[mt][u][2], sacc[mt][u][3])));
+                lmx[mt] = m;
                 any_grow |= lmx[mt] > m_thr[mt];
             }
             if (__builtin_expect(__ballot(any_grow) != 0, 0)) {
@@ -402,64 +405,69 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const float mb = -m_run[mt] * sl2;
-                float pv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][e >> 2][e & 3], sl2, mb));
-                if constexpr (sizeof(T) == 2) {
+                for (int bb = 0; bb < NB; ++bb) {
+                    float pv[8];
 #pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) pf[mt].w[w2] = pack_f16x2(pv[2 * w2], pv[2 * w2 + 1]);
-                } else {
+                    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][2 * bb + (e >> 2)][e & 3], sl2, mb));
+                    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[mt].v[e] = pv[e];
+                        for (int w2 = 0; w2 < 4; ++w2) pf[mt][bb].w[w2] = pack_f16x2(pv[2 * w2], pv[2 * w2 + 1]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pf[mt][bb].v[e] = pv[e];
+                    }
                 }
             }
 
-            // O^T += V^T P^T; the lane's 8 keys of the block are key(e) = 32kb2 + 16(e/4) + 4q + e%4
-            if constexpr (sizeof(T) == 2) {
-                // transpose reads: lane j of group q points at key 32kb2 + 4q + j/4 (+16), columns
-                // c0 + 4(j%4); lane n then holds column c0 + n of the group's keys in slot order
-                const int rkey = 32 * kb2 + 4 * q + (n >> 2);
-                const int rcol = 4 * (n & 3);
+            // O^T += V^T P^T; the lane's 8 keys of block bb are 32bb + 16(e/4) + 4q + e%4
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const uint2 lo = lds_read_tr16(&vs[rkey * LDV + 16 * dt + rcol]);
-                    const uint2 hi = lds_read_tr16(&vs[(rkey + 16) * LDV + 16 * dt + rcol]);
-                    H8 va;
-                    va.w[0] = lo.x; va.w[1] = lo.y; va.w[2] = hi.x; va.w[3] = hi.y;
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) oacc[mt][dt] = mma16x16x32_f16(va, pf[mt], oacc[mt][dt]);
-                }
-#pragma unroll
-                for (int x = 0; x < NAUX; ++x) {
-                    const uint2 lo = lds_read_tr16(&xs[rkey * LDX + 16 * x + rcol]);
-                    const uint2 hi = lds_read_tr16(&xs[(rkey + 16) * LDX + 16 * x + rcol]);
-                    H8 xa;
-                    xa.w[0] = lo.x; xa.w[1] = lo.y; xa.w[2] = hi.x; xa.w[3] = hi.y;
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) xacc[mt][x] = mma16x16x32_f16(xa, pf[mt], xacc[mt][x]);
-                }
-            } else {
-                // fp32: one key per 16x16x4 step; lane n supplies column 16t + n of its key
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = 32 * kb2 + 16 * (e >> 2) + 4 * q + (e & 3);
+            for (int bb = 0; bb < NB; ++bb) {
+                if constexpr (sizeof(T) == 2) {
+                    const int rkey = 32 * bb + 4 * q + (n >> 2);
+                    const int rcol = 4 * (n & 3);
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        const float vv = vs[key * LDV + 16 * dt + n];
+                        const uint2 lo = lds_read_tr16(&vs[rkey * LDV + 16 * dt + rcol]);
+                        const uint2 hi = lds_read_tr16(&vs[(rkey + 16) * LDV + 16 * dt + rcol]);
+                        H8 va;
+                        va.w[0] = lo.x; va.w[1] = lo.y; va.w[2] = hi.x; va.w[3] = hi.y;
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            oacc[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, pf[mt].v[e], oacc[mt][dt], 0, 0, 0);
+                        for (int mt = 0; mt < MT; ++mt) oacc[mt][dt] = mma16x16x32_f16(va, pf[mt][bb], oacc[mt][dt]);
                     }
 #pragma unroll
                     for (int x = 0; x < NAUX; ++x) {
-                        const float xv = xs[key * LDX + 16 * x + n];
+                        const uint2 lo = lds_read_tr16(&xs[rkey * LDX + 16 * x + rcol]);
+                        const uint2 hi = lds_read_tr16(&xs[(rkey + 16) * LDX + 16 * x + rcol]);
+                        H8 xa;
+                        xa.w[0] = lo.x; xa.w[1] = lo.y; xa.w[2] = hi.x; xa.w[3] = hi.y;
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            xacc[mt][x] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, pf[mt].v[e], xacc[mt][x], 0, 0, 0);
+                        for (int mt = 0; mt < MT; ++mt) xacc[mt][x] = mma16x16x32_f16(xa, pf[mt][bb], xacc[mt][x]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int key = 32 * bb + 16 * (e >> 2) + 4 * q + (e & 3);
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            const float vv = vs[key * LDV + 16 * dt + n];
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+                                oacc[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, pf[mt][bb].v[e], oacc[mt][dt], 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int x = 0; x < NAUX; ++x) {
+                            const float xv = xs[key * LDX + 16 * x + n];
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt)
+                                xacc[mt][x] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, pf[mt][bb].v[e], xacc[mt][x], 0, 0, 0);
+                        }
                     }
                 }
             }
-        }
+        };
+        if (nkb == 2) step(std::integral_constant<int, 2>{});
+        else if (nkb == 1) step(std::integral_constant<int, 1>{});
 
         if (t + 1 < n_tiles) store(buf ^ 1);
         __syncthreads();

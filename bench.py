@@ -114,6 +114,15 @@ def time_launches(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps  # ms per call
 
 
+def time_launches_median(fn, groups, reps, warmup, torch):
+    """Median over `groups` timed groups of `reps` back-to-back launches (ms per launch). The clock
+    of a compute-bound kernel drifts over a run (power management); the median of the groups is the
+    steady-state figure, and the spread is returned beside it."""
+    fn_ms = [time_launches(fn, reps, warmup if g == 0 else 2, torch) for g in range(groups)]
+    fn_ms.sort()
+    return fn_ms[len(fn_ms) // 2], fn_ms[0], fn_ms[-1]
+
+
 def time_graph(fn, calls, replays, torch):
     """ms per fn() call with `calls` calls captured in one HIP graph and the graph replayed `replays`
     times: the device-side rate of short launches, without the host's per-call cost. Returns None
@@ -263,13 +272,14 @@ def bench_prefill(args, torch, lra, W, out):
 
     # ~20 ms of warm-up launches first: the first launches after the inputs are built run at
     # lower clocks (about 0.75 ms against 0.6 ms in steady state on MI355X)
-    reps = max(10, args.steps // 2)
-    ms = time_launches(step, reps, 30, torch)
+    reps = max(10, args.steps // 5)
+    ms, ms_lo, ms_hi = time_launches_median(step, 5, reps, 30, torch)
     fl = prefill_flops(c.L_P, c.L_C, s.n_q, s.d_head, s.rank)
     tf = fl / (ms * 1e-3) / 1e12
     out["prefill_llama_LP16384_LC2048_r8"] = {
         "ms": round(ms, 4), "tflops": round(tf, 2), "flops": fl, "peak_tflops": BF16_PEAK_TFLOPS,
-        "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma", "reps": reps}
+        "frac": round(tf / BF16_PEAK_TFLOPS, 4), "bound": "mfma",
+        "timing": f"median of 5 groups of {reps} launches (group means {ms_lo:.4f}-{ms_hi:.4f} ms)"}
     # matrix-core counters of the same kernel (committed summary, used only while its source matches)
     mf = counter_fields("prefill_llama_LP16384_LC2048_mfma_counters.txt", PREFILL_SOURCES)
     if mf:
@@ -290,7 +300,7 @@ def bench_prefill(args, torch, lra, W, out):
     def step_varlen():
         lra.lra_attn_prefill_varlen(Q, q_start, q_len, lc, K, V, L, kv_start, kv_prefix, B, agents, s.scale, O)
 
-    ms_v = time_launches(step_varlen, reps, 10, torch)
+    ms_v = time_launches_median(step_varlen, 5, reps, 10, torch)[0]
     tf_v = fl / (ms_v * 1e-3) / 1e12
     out["prefill_varlen_4x512_LP16384"] = {
         "ms": round(ms_v, 4), "tflops": round(tf_v, 2), "flops": fl, "frac": round(tf_v / BF16_PEAK_TFLOPS, 4),
@@ -311,7 +321,7 @@ def bench_prefill(args, torch, lra, W, out):
     def step_paged():
         lra.lra_attn_prefill_paged(Q, one64, len1, c.L_C, Kp, Vp, Lp, table, pre1, B, ag1, s.scale, O)
 
-    ms_p = time_launches(step_paged, reps, 10, torch)
+    ms_p = time_launches_median(step_paged, 5, reps, 10, torch)[0]
     tf_p = fl / (ms_p * 1e-3) / 1e12
     out["prefill_paged_llama_LP16384_LC2048_P64"] = {
         "ms": round(ms_p, 4), "tflops": round(tf_p, 2), "flops": fl, "frac": round(tf_p / BF16_PEAK_TFLOPS, 4),
@@ -328,7 +338,7 @@ def bench_prefill(args, torch, lra, W, out):
     def step_qkvo():
         lra.lra_attn_prefill_qkvo(Q, c.L_P, K, V, L, Klr, B, Bk, rc, rs, 0, s.scale, ws_k, O)
 
-    ms_k = time_launches(step_qkvo, reps, 10, torch)
+    ms_k = time_launches_median(step_qkvo, 5, reps, 10, torch)[0]
     fl_k = fl + 2 * (c.L_P + c.L_C) * s.n_kv * s.d_head * s.rank
     tf_k = fl_k / (ms_k * 1e-3) / 1e12
     out["prefill_qkvo_llama_LP16384_LC2048_r8"] = {

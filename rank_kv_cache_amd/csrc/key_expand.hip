@@ -4,9 +4,9 @@
 // the key projection carries LoRA too, an agent's key is K_base + RoPE(K_lr B_k). The rotation
 // sits between the up-projection and the dot product with the query, so the rank-r part cannot be
 // folded behind the softmax the way the value side is; each key has to be expanded and rotated at
-// its own position before the scores. A causal prefill reads every key once per 128-row piece of
-// queries, so the expansion runs once per call in this pass and the attention kernel reads the
-// result: Ka[j, g] = fp16(K_base[j, g] + RoPE_j(K_lr[j, agent] B_k[agent][:, g])).
+// its own position before the scores. A causal prefill stages every key once per workgroup (a pair
+// of 128-row query pieces), so the expansion runs once per call in this pass and the attention
+// kernel reads the result: Ka[j, g] = fp16(K_base[j, g] + RoPE_j(K_lr[j, agent] B_k[agent][:, g])).
 //
 // Rotation (rotate-half pairing): element i < d/2 pairs with i + d/2; with c = cos[j, i] and
 // s = sin[j, i], (y_i, y_{i+d/2}) -> (y_i c - y_{i+d/2} s, y_{i+d/2} c + y_i s).

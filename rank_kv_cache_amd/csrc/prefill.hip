@@ -402,14 +402,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                     for (int x = 0; x < NAUX; ++x) xacc[mt][x] *= alpha;
                 }
             }
+            float mbs[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float mb = -m_run[mt] * sl2;
+            for (int mt = 0; mt < MT; ++mt) mbs[mt] = -m_run[mt] * sl2;
+            // per 32-key block: its probabilities, then its P.V steps (the next block's exponentials
+            // can fill the matrix-core shadow of this block's steps)
 #pragma unroll
-                for (int bb = 0; bb < NB; ++bb) {
+            for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
                     float pv[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][2 * bb + (e >> 2)][e & 3], sl2, mb));
+                    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(sacc[mt][2 * bb + (e >> 2)][e & 3], sl2, mbs[mt]));
                     if constexpr (sizeof(T) == 2) {
 #pragma unroll
                         for (int w2 = 0; w2 < 4; ++w2) pf[mt][bb].w[w2] = pack_f16x2(pv[2 * w2], pv[2 * w2 + 1]);
@@ -418,11 +422,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                         for (int e = 0; e < 8; ++e) pf[mt][bb].v[e] = pv[e];
                     }
                 }
-            }
-
-            // O^T += V^T P^T; the lane's 8 keys of block bb are 32bb + 16(e/4) + 4q + e%4
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
                 if constexpr (sizeof(T) == 2) {
                     const int rkey = 32 * bb + 4 * q + (n >> 2);
                     const int rcol = 4 * (n & 3);

@@ -276,7 +276,7 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
  *          aligned, no initialisation needed; calls sharing one workspace must be ordered.
  * Every other argument is as for lra_attn_decode. Adapter-free requests (agent -1) attend K_base
  * alone and read none of the key-side operands. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED);
- * max_kv_len <= 2^27. Precision: the base part of a score is as in lra_attn_decode; the rank-r
+ * max_kv_len <= 2^24. Precision: the base part of a score is as in lra_attn_decode; the rank-r
  * part is computed from fp16 operands (the rotated rank-r key and the query, fp32 accumulation)
  * and stored as fp16. A query entry, rotated rank-r key entry or rank-r score part that rounds
  * beyond the fp16 range (|x| >= 65520) gives NaN output for the heads concerned.

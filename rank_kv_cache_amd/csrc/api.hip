@@ -430,7 +430,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
     if (kv_rows < 0 || max_kv_len < 0) return fail(LRA_ERR_SHAPE, "kv_rows and max_kv_len must be >= 0");
     if (max_kv_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^31 - 1");
-    if (kl && max_kv_len > (int64_t(1) << 27)) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^27 with LoRA on the keys");
+    // key-score grid: one workgroup row per 512-key block (at most 32,768)
+    if (kl && max_kv_len > (int64_t(1) << 24)) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^24 with LoRA on the keys");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
     if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);

@@ -89,7 +89,7 @@ def decode_qkvo(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=0), E_UNSUP), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_q=30, n_kv=8), E_SHAPE),
     (dict(ld_klr=16), E_SHAPE), (dict(ld_klr=30), E_SHAPE), (dict(ld_vlr=16), E_SHAPE), (dict(split=100), E_SHAPE),
-    (dict(max_kv_len=(1 << 27) + 1), E_SHAPE), (dict(scale=0.0), E_SHAPE),
+    (dict(max_kv_len=(1 << 24) + 1), E_SHAPE), (dict(scale=0.0), E_SHAPE),
     (dict(Klr=None), E_NULL), (dict(Bk=None), E_NULL), (dict(cos=None), E_NULL), (dict(sin=None), E_NULL),
     (dict(agent=None), E_NULL), (dict(cos=P + 4), E_SHAPE), (dict(Klr=P + 8), E_SHAPE),
     (dict(ws=None), E_WS), (dict(ws=WS + 64, ws_bytes=1 << 30), E_WS), (dict(ws_bytes=16), E_WS),

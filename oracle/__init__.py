@@ -26,6 +26,7 @@ from .lora_attention import (  # noqa: F401
     kv_head_of,
     agent_columns,
     agent_values,
+    expand_values,
     visible,
     softmax_rows,
     attention_probs,

@@ -102,6 +102,24 @@ def agent_values(V_base, V_lr, B, agent: int) -> np.ndarray:
     return V_base + lr.reshape(L, n_kv, d)
 
 
+def expand_values(V_out, V_base, V_lr, B, src_start, length, agents, dst_start) -> np.ndarray:
+    """Expand-then-attend's first pass over a batch of requests (the order the LRAgent page's
+    Flash-LoRA-Attention avoids): request b's full value rows ``agent_values`` of source rows
+    src_start[b] .. src_start[b]+length[b]-1 land in rows dst_start[b] .. of a copy of ``V_out``.
+    Rows no request names keep their values. Attending these rows with no LR term gives the same
+    result as attention with the LR term deferred (associativity, LRAgent page, core method).
+    V_out, V_base: [rows, n_kv, d]; V_lr: [rows, >= N*r]; B: [N, r, n_kv*d]. Returns float64.
+    """
+    out = _f64(V_out).copy()
+    for b in range(len(length)):
+        n = int(length[b])
+        if n <= 0:
+            continue
+        s0, d0 = int(src_start[b]), int(dst_start[b])
+        out[d0:d0 + n] = agent_values(V_base[s0:s0 + n], V_lr[s0:s0 + n], B, int(agents[b]))
+    return out
+
+
 # --------------------------------------------------------------------------- mask + softmax
 def visible(q_pos: Iterable[int], L: int) -> np.ndarray:
     """Causal visibility [len(q_pos), L]: key j is visible to a query at absolute position p iff j <= p."""

@@ -117,3 +117,18 @@ def prefill_qkvo(Q, K, Vb, Klr, Vlr, B, Bk, cos, sin, agent, L_P, scale):
             row.append([K[j][g][c] + rot[c] for c in range(d)])
         Ka.append(row)
     return prefill(Q, Ka, Vb, Vlr, B, agent, L_P, scale)
+
+
+def expand_values(V_out, Vb, Vlr, B, src_start, length, agents, dst_start):
+    """Request b's value rows (base row + LR row times B_agent, or the base row for agent -1) written
+    over rows dst_start[b] + t of a copy of V_out."""
+    out, Vb, Vlr, B = map(_tolist, (V_out, Vb, Vlr, B))
+    out = [[list(map(float, row)) for row in tok] for tok in out]
+    n_kv, d = len(Vb[0]), len(Vb[0][0])
+    r = len(B[0])
+    for b in range(len(length)):
+        for t in range(int(length[b])):
+            j = int(src_start[b]) + t
+            out[int(dst_start[b]) + t] = [[_value(Vb, Vlr, B, j, g, c, int(agents[b]), r, d) for c in range(d)]
+                                          for g in range(n_kv)]
+    return out

@@ -16,6 +16,7 @@ from tests import test_oracle_pins as pins
 _orig_softmax = LA.softmax_rows
 _orig_agent_values = LA.agent_values
 _orig_rope = LA.rope_rotate
+_orig_expand_values = LA.expand_values
 
 
 def _checks():
@@ -35,6 +36,7 @@ def _checks():
     yield lambda: pins.test_key_lora_special_cases()
     yield lambda: pins.test_bruteforce_decode_with_key_lora()
     yield lambda: pins.test_precompute_triple_loop_and_one_hot()
+    yield lambda: pins.test_bruteforce_expand_values_and_expand_then_attend()
     yield lambda: pins.test_projection_level_lora_split()
     yield lambda: pins.test_probability_rows_and_causal_zeros()
 
@@ -102,7 +104,19 @@ def _mut_decode_qkvo_absolute_rows(Q, K_base, V_base, V_lr, K_lr, B, B_k, cos, s
     return np.stack(out)
 
 
+def _mut_expand_values_at_source_rows(V_out, V_base, V_lr, B, src_start, length, agents, dst_start):
+    # writes each request's expanded rows at its source rows instead of its destination rows
+    return _orig_expand_values(V_out, V_base, V_lr, B, src_start, length, agents, src_start)
+
+
+def _mut_expand_values_first_agent(V_out, V_base, V_lr, B, src_start, length, agents, dst_start):
+    # expands every request with the first request's agent
+    return _orig_expand_values(V_out, V_base, V_lr, B, src_start, length, [agents[0]] * len(agents), dst_start)
+
+
 MUTANTS = {
+    "expand_at_source_rows": ("expand_values", _mut_expand_values_at_source_rows),
+    "expand_first_agent_only": ("expand_values", _mut_expand_values_first_agent),
     "decode_key_rope_absolute_rows": ("attn_decode_qkvo", _mut_decode_qkvo_absolute_rows),
     "rope_adjacent_pairs": ("rope_rotate", _mut_rope_adjacent_pairs),
     "rope_sign": ("rope_rotate", lambda Y, c, s_: _orig_rope(Y, c, -np.asarray(s_, np.float64))),

@@ -434,3 +434,31 @@ def test_precompute_scatter_leaves_other_rows_and_columns():
     np.testing.assert_array_equal(got[[1, 3, 4, 5]], cache[[1, 3, 4, 5]])
     np.testing.assert_array_equal(got[:, 4:], cache[:, 4:])
     np.testing.assert_array_equal(got[[6, 0, 2], :4], X @ A)
+
+
+def test_bruteforce_expand_values_and_expand_then_attend():
+    """Expand-then-attend (the order the LRAgent page's Flash-LoRA-Attention avoids): the expansion
+    against the brute force on a batch with shared sources, distinct destinations, an adapter-free
+    request and an empty one; rows no request names keep their values. Attending the expanded rows
+    with no LR term (agent -1) gives the adapted decode."""
+    s = small_shape(n_q=4, n_kv=2, d=6, r=2)
+    c = W.random_decode((913,), s, kv_lens=[5, 5, 3, 0, 4], kv_starts=[0, 0, 6, 2, 7], rows=12,
+                        agents=[2, 0, -1, 1, 1], b_std=0.8)
+    dst = [12, 0, 6, 3, 17]
+    g = np.random.default_rng(913)
+    V_out = g.standard_normal((22, s.n_kv, s.d_head))
+    got = oracle.expand_values(V_out, f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, dst)
+    ref = bruteforce.expand_values(V_out, f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, dst)
+    assert rel_err(got, ref) <= 1e-14
+    np.testing.assert_array_equal(got[[5, 9, 10, 11, 21]], V_out[[5, 9, 10, 11, 21]])
+    np.testing.assert_array_equal(got[6:9], f64(c.V)[6:9])     # agent -1 copies the base rows
+    # attention over the expanded rows without the LR term equals the adapted decode
+    K2 = np.zeros((22, s.n_kv, s.d_head))
+    for b in range(5):
+        n = int(c.kv_len[b])
+        K2[dst[b]:dst[b] + n] = f64(c.K)[int(c.kv_start[b]):int(c.kv_start[b]) + n]
+    none = np.full(5, oracle.ADAPTER_FREE)
+    O_exp = oracle.attn_decode(f64(c.Q), K2, got, np.zeros((22, f64(c.V_lr).shape[1])), f64(c.B), dst, c.kv_len,
+                               none, s.scale)
+    O_ref = bruteforce.decode(f64(c.Q), f64(c.K), f64(c.V), f64(c.V_lr), f64(c.B), c.kv_start, c.kv_len, c.agent, s.scale)
+    assert rel_err(O_exp, O_ref) <= 1e-13

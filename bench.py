@@ -50,6 +50,12 @@ def precompute_bytes(T, d_model, NR, elem=2) -> int:
     return (T * d_model + NR * d_model + T * NR) * elem
 
 
+def expand_bytes(rows, n_distinct_agents, n_kv, d, r, elem=2) -> int:
+    """HBM bytes of the value expansion: each row reads its V_base row and its agent's r V_lr
+    entries and writes the full row; B_a is read once per distinct agent."""
+    return rows * (2 * n_kv * d + r) * elem + n_distinct_agents * r * n_kv * d * elem
+
+
 def prefill_flops(L_P, L_C, n_q, d, r) -> int:
     """Unmasked (query, key) pairs x (4d: QK^T and PV_base, + 2r: PV_lr) per head, plus the
     up-projection O_lr B (2 r d per query row)."""
@@ -255,7 +261,32 @@ def bench_long_decode(args, torch, lra, W, out):
     out["decode_qkvo_llama_b16_L66400"] = {
         "ms": round(ms_k, 4), "gbs": round(gbs_k, 1), "bytes": nbytes_k, "frac": round(gbs_k / HBM_PEAK_GBS, 4),
         "bound": "hbm", "keys": "K_base + RoPE(K_lr B_k), rank 8; key score pass + decode"}
-    del Q, K, V, L, B, O, ws, ws_p, Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
+    del ws_p, Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
+
+    # expand-then-attend (the order Flash-LoRA-Attention avoids): every request's V_base + V_lr B_a
+    # written once at full width, then the same decode kernels with no LR term (agent -1)
+    V_exp = torch.empty_like(V)
+    none = torch.full((c.batch,), -1, dtype=torch.int32, device="cuda")
+
+    def step_expand():
+        lra.lra_expand_values(V, L, B, ks, kl, ag, c.max_kv_len, ks, V_exp)
+
+    def step_expand_attend():
+        step_expand()
+        lra.lra_attn_decode(Q, K, V_exp, L, ks, kl, c.max_kv_len, B, none, s.scale, 0, ws, O)
+
+    log("[bench] decode 16 x 66400, expand-then-attend")
+    ms_x = time_launches(step_expand, args.steps, args.warmup, torch)
+    ms_xa = time_launches(step_expand_attend, args.steps, args.warmup, torch)
+    rows = int(sum(int(x) for x in c.kv_len))
+    nbytes_x = expand_bytes(rows, len(set(int(a) for a in c.agent)), s.n_kv, s.d_head, s.rank)
+    out["decode_expand_then_attend_llama_b16_L66400"] = {
+        "ms": round(ms_xa, 4), "ms_expand": round(ms_x, 4), "ms_fused_decode": round(ms, 4),
+        "fused_speedup": round(ms_xa / ms, 3),
+        "expand_gbs": round(nbytes_x / (ms_x * 1e-3) / 1e9, 1), "expand_bytes": nbytes_x,
+        "expand_frac": round(nbytes_x / (ms_x * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
+        "order": "lra_expand_values (V_base + V_lr B_a per request) then lra_attn_decode with agent -1"}
+    del Q, K, V, L, B, O, ws, V_exp
     torch.cuda.empty_cache()
 
 
@@ -344,7 +375,30 @@ def bench_prefill(args, torch, lra, W, out):
     out["prefill_qkvo_llama_LP16384_LC2048_r8"] = {
         "ms": round(ms_k, 4), "tflops": round(tf_k, 2), "flops": fl_k, "frac": round(tf_k / BF16_PEAK_TFLOPS, 4),
         "bound": "mfma", "keys": "K_base + RoPE(K_lr B_k), rank 8, expanded once per call (one extra pass)"}
-    del Q, K, V, L, B, O, Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
+    del Kp, Vp, Lp, table, Klr, Bk, rc, rs, ws_k
+
+    # expand-then-attend: the agent's L_P + L_C value rows written at full width, then the prefill
+    # with no LR term (agent -1) over them
+    n_rows = c.L_P + c.L_C
+    V_exp = torch.empty_like(V)
+    one32 = torch.full((1,), n_rows, dtype=torch.int32, device="cuda")
+
+    def step_expand():
+        lra.lra_expand_values(V, L, B, one64, one32, ag1, n_rows, one64, V_exp)
+
+    def step_expand_attend():
+        step_expand()
+        lra.lra_attn_prefill(Q, c.L_P, K, V_exp, L, B, -1, s.scale, O)
+
+    ms_x = time_launches_median(step_expand, 5, reps, 10, torch)[0]
+    ms_xa = time_launches_median(step_expand_attend, 5, reps, 10, torch)[0]
+    nbytes_x = expand_bytes(n_rows, 1, s.n_kv, s.d_head, s.rank)
+    out["prefill_expand_then_attend_llama_LP16384_LC2048"] = {
+        "ms": round(ms_xa, 4), "ms_expand": round(ms_x, 4), "ms_fused_prefill": round(ms, 4),
+        "fused_speedup": round(ms_xa / ms, 3), "tflops": round(fl / (ms_xa * 1e-3) / 1e12, 2),
+        "expand_gbs": round(nbytes_x / (ms_x * 1e-3) / 1e9, 1), "expand_bytes": nbytes_x,
+        "order": "lra_expand_values (V_base + V_lr B_0) then lra_attn_prefill with agent -1"}
+    del Q, K, V, L, B, O, V_exp
     torch.cuda.empty_cache()
 
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 2   /* 2: agent index -1 selects the adapter-free view */
+#define LRA_ABI_VERSION 3   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values */
 
 typedef enum {
     LRA_OK = 0,
@@ -328,6 +328,36 @@ int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
 
 /* Keys per split lra_attn_decode_paged uses when keys_per_split = 0 (0 for an unsupported P). */
 int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size);
+
+/* ------------------------------------------------------------------------------------------------
+ * Value expansion: the expand-then-attend baseline (LRAgent page, Flash-LoRA-Attention: without the
+ * reordering, each agent's full value cache V_a = V_base + V_lr B_a is built before attention).
+ * Flash-LoRA-Attention never needs this call; it exists so the two orders can be compared on the same
+ * attention kernels: expand, then run lra_attn_prefill / lra_attn_decode with the adapter-free agent
+ * (-1) over K_base and V_out. For request b with a = agent[b], rows t < len[b]:
+ *
+ *   V_out[dst_start[b] + t, c] = V_base[src_start[b] + t, c]
+ *                                + sum_j V_lr[src_start[b] + t, a*rank + j] * B[a, j, c]     c < n_kv*d_head
+ *
+ * summed in fp32 and rounded once to the element type. Agent -1 copies V_base rows unchanged.
+ *
+ * V_base   (device) [kv_rows x n_kv x d_head];  V_lr (device) [kv_rows x ld_vlr]
+ * B        (device) [n_agents x rank x n_kv*d_head]
+ * src_start, dst_start (device) [batch] int64; len, agent (device) [batch] int32
+ * max_len  (host) an upper bound on every len[b]; it sizes the launch
+ * V_out    (device) [out_rows x n_kv x d_head] output; rows no request covers are not written.
+ *          Requests whose destination ranges overlap race.
+ * A request with len[b] <= 0 or a destination range outside [0, out_rows) is skipped. One with
+ * len[b] > max_len, a source range outside [0, kv_rows) or an agent outside [-1, n_agents) gets NaN
+ * in its destination rows dst_start[b] .. dst_start[b] + min(len[b], max_len) - 1.
+ * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 or max_len = 0
+ * enqueues nothing; batch * ceil(max_len / 256) must not exceed 2^24.
+ */
+int lra_expand_values(int dtype, const void* V_base, int64_t kv_rows, const void* V_lr, int64_t ld_vlr,
+                      const void* B, int32_t n_agents, int32_t n_kv, int32_t d_head, int32_t rank,
+                      int32_t batch, const int64_t* src_start, const int32_t* len,
+                      const int32_t* agent, int64_t max_len,
+                      void* V_out, int64_t out_rows, const int64_t* dst_start, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ __all__ = [
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
-    "lra_attn_decode_paged", "lra_attn_decode_paged_default_split",
+    "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_expand_values",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
@@ -61,6 +61,8 @@ _SIGNATURES = {
     "lra_attn_decode_paged": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _p, _i32, _p, _i64, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged_default_split": (_i32, [_i32, _i32, _i64, _i32]),
+    "lra_expand_values": (_c.c_int, [_c.c_int, _p, _i64, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
+                                     _i64, _p, _i64, _p, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -484,3 +486,41 @@ def lra_attn_decode_paged(Q: torch.Tensor, K_pages: torch.Tensor, V_pages: torch
                                       scale, keys_per_split, _ptr(workspace), workspace.numel(), _ptr(O),
                                       _stream(stream)), "lra_attn_decode_paged")
     return O
+
+
+# ---------------------------------------------------------------------------------- value expansion
+def lra_expand_values(V_base: torch.Tensor, V_lr: torch.Tensor, B: torch.Tensor, src_start: torch.Tensor,
+                      length: torch.Tensor, agent: torch.Tensor, max_len: int, dst_start: torch.Tensor,
+                      V_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Expand-then-attend baseline: V_out[dst_start[b] + t] = V_base[src_start[b] + t]
+    + V_lr[src_start[b] + t, agent cols] B[agent[b]] for t < length[b] (a copy for agent -1).
+
+    V_base [rows, n_kv, d]; V_lr [rows, ld]; B [N, r, n_kv*d]; src_start, dst_start int64 [batch];
+    length, agent int32 [batch]; V_out [out_rows, n_kv, d] (like V_base when omitted; rows no
+    request covers keep their contents, uninitialised when allocated here)."""
+    _same(V_base, V_lr, B)
+    for name, t in (("V_base", V_base), ("B", B)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    if V_base.dim() != 3:
+        raise ValueError("V_base must be [rows, n_kv, d]")
+    n_kv, d = V_base.shape[1], V_base.shape[2]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if V_lr.shape[0] != V_base.shape[0] or B.shape[2] != n_kv * d:
+        raise ValueError("V_base/V_lr/B shapes disagree")
+    batch = src_start.numel()
+    for name, t, dt in (("src_start", src_start, torch.int64), ("dst_start", dst_start, torch.int64),
+                        ("length", length, torch.int32), ("agent", agent, torch.int32)):
+        if t.dtype != dt or t.numel() != batch or not t.is_contiguous() or t.device != V_base.device:
+            raise TypeError(f"{name} must be a contiguous {dt} device tensor with one entry per request")
+    if V_out is None:
+        V_out = torch.empty_like(V_base)
+    _same(V_base, V_out)
+    _dense("V_out", V_out)
+    if V_out.dim() != 3 or V_out.shape[1:] != V_base.shape[1:]:
+        raise ValueError("V_out must be [out_rows, n_kv, d] like V_base")
+    _check(_lib.lra_expand_values(_dtype_code(V_base), _ptr(V_base), V_base.shape[0], _ptr(V_lr), V_lr.stride(0),
+                                  _ptr(B), n_agents, n_kv, d, rank, batch, _ptr(src_start), _ptr(length),
+                                  _ptr(agent), max_len, _ptr(V_out), V_out.shape[0], _ptr(dst_start),
+                                  _stream(stream)), "lra_expand_values")
+    return V_out

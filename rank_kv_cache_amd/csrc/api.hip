@@ -541,3 +541,40 @@ int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len) {
 }
 
 }  // namespace lra
+
+// ============================================================================ value expansion
+LRA_EXPORT int lra_expand_values(int dtype, const void* V_base, int64_t kv_rows, const void* V_lr, int64_t ld_vlr,
+                                 const void* B, int32_t n_agents, int32_t n_kv, int32_t d_head, int32_t rank,
+                                 int32_t batch, const int64_t* src_start, const int32_t* len,
+                                 const int32_t* agent, int64_t max_len,
+                                 void* V_out, int64_t out_rows, const int64_t* dst_start, void* stream) {
+    if (int s = check_dtype(dtype)) return s;
+    if (n_kv <= 0) return fail(LRA_ERR_SHAPE, "n_kv=%d must be positive", n_kv);
+    if (d_head != 64 && d_head != 128) return fail(LRA_ERR_UNSUPPORTED, "d_head=%d (supported: 64, 128)", d_head);
+    if (rank != 8 && rank != 16) return fail(LRA_ERR_UNSUPPORTED, "rank=%d (supported: 8, 16)", rank);
+    if (int64_t(n_kv) * d_head > (int64_t(1) << 24)) return fail(LRA_ERR_SHAPE, "n_kv*d_head exceeds 2^24");
+    if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
+    if (batch < 0 || kv_rows < 0 || out_rows < 0 || max_len < 0)
+        return fail(LRA_ERR_SHAPE, "batch, kv_rows, out_rows and max_len must be >= 0");
+    if (max_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_len exceeds 2^31 - 1");
+    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    const int rows_per_wg = lra::value_expand_rows(batch, max_len);
+    const int64_t n_chunks = (max_len + rows_per_wg - 1) / rows_per_wg;
+    // one-dimensional grid of (request, chunk) workgroups of 256 threads
+    if (int64_t(batch) * n_chunks > (int64_t(1) << 24))
+        return fail(LRA_ERR_SHAPE, "batch x ceil(max_len/256) exceeds 2^24 workgroups");
+    if (batch == 0 || max_len == 0) return LRA_OK;
+    if (!V_base || !V_lr || !B || !V_out || !src_start || !len || !agent || !dst_start)
+        return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
+    if (!aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(V_out, 16))
+        return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    lra::ValueExpandParams p{};
+    p.V = V_base; p.Vlr = V_lr; p.B = B; p.Vout = V_out;
+    p.src_start = src_start; p.len = len; p.agent = agent; p.dst_start = dst_start;
+    p.kv_rows = kv_rows; p.out_rows = out_rows; p.ld_vlr = ld_vlr; p.max_len = max_len; p.n_chunks = n_chunks;
+    p.batch = batch; p.n_agents = n_agents; p.row_elems = n_kv * d_head; p.rank = rank;
+    p.rows_per_wg = rows_per_wg;
+    p.bf16 = dtype == LRA_BF16;
+    return hip_status(lra::launch_value_expand(p, static_cast<hipStream_t>(stream)), "lra_expand_values launch");
+}

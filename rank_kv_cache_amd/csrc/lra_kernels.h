@@ -115,6 +115,27 @@ struct KeyExpandParams {
 };
 hipError_t launch_key_expand(const KeyExpandParams& p, hipStream_t stream);
 
+// Value expansion of the expand-then-attend baseline: request b's rows t < len[b] become
+// V_out[dst_start[b] + t] = V_base[src_start[b] + t] + V_lr[src_start[b] + t, agent cols] B_agent
+// (a copy of V_base for the adapter-free agent). Invalid requests as documented in lra.h.
+struct ValueExpandParams {
+    const void* V;              // [kv_rows x row_elems]
+    const void* Vlr;            // [kv_rows x ld_vlr]
+    const void* B;              // [n_agents x rank x row_elems]
+    void* Vout;                 // [out_rows x row_elems]
+    const int64_t* src_start;   // [batch]
+    const int32_t* len;         // [batch]
+    const int32_t* agent;       // [batch]
+    const int64_t* dst_start;   // [batch]
+    int64_t kv_rows, out_rows, ld_vlr, max_len, n_chunks;
+    int batch, n_agents, row_elems, rank, rows_per_wg;
+    bool bf16;
+};
+hipError_t launch_value_expand(const ValueExpandParams& p, hipStream_t stream);
+// rows of one request per workgroup for these sizes: 256, halved (down to 16) until the grid holds
+// about 2048 workgroups
+int value_expand_rows(int batch, int64_t max_len);
+
 // Decode with LoRA on the keys: the rank-r part of every score,
 // S[(b*n_q + h)*ks_stride + j] = fp16(Q[b, h] . RoPE_j(K_lr[kv_start[b] + j, agent_b] B_k[agent_b][:, g])),
 // for keys j < round_up(kv_len[b], 32) (later keys repeat the last row); NaN where it is not a

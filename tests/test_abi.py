@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 2
+    assert lra.abi_version() == 3
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -331,3 +331,32 @@ def test_prefill_paged_rejects_bad_arguments(kw, status):
 
 def test_prefill_paged_empty_batch_is_a_no_op():
     assert prefill_paged(batch=0, Q=None, O=None, table=None) == OK
+
+
+# ---------------------------------------------------------------------------------------- value expansion
+def expand(**kw):
+    a = dict(dtype=1, V=P, kv_rows=100, Vlr=P, ld_vlr=24, B=P, n_agents=3, n_kv=8, d=128, r=8, batch=2,
+             src=P, len=P, agent=P, max_len=100, out=P, out_rows=100, dst=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_expand_values(a["dtype"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"], a["B"], a["n_agents"],
+                                      a["n_kv"], a["d"], a["r"], a["batch"], a["src"], a["len"], a["agent"],
+                                      a["max_len"], a["out"], a["out_rows"], a["dst"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), E_UNSUP), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_kv=0), E_SHAPE),
+    (dict(n_agents=0), E_SHAPE), (dict(batch=-1), E_SHAPE), (dict(kv_rows=-1), E_SHAPE), (dict(out_rows=-1), E_SHAPE),
+    (dict(max_len=-1), E_SHAPE), (dict(max_len=1 << 31), E_SHAPE), (dict(ld_vlr=16), E_SHAPE), (dict(ld_vlr=28), E_SHAPE),
+    (dict(batch=1 << 20, max_len=1 << 20), E_SHAPE),
+    (dict(V=None), E_NULL), (dict(Vlr=None), E_NULL), (dict(B=None), E_NULL), (dict(out=None), E_NULL),
+    (dict(src=None), E_NULL), (dict(len=None), E_NULL), (dict(agent=None), E_NULL), (dict(dst=None), E_NULL),
+    (dict(V=P + 8), E_SHAPE), (dict(out=P + 2), E_SHAPE),
+])
+def test_expand_values_rejects_bad_arguments(kw, status):
+    assert expand(**kw) == status
+    assert lra._lib.lra_last_error().decode() != ""
+
+
+def test_expand_values_empty_is_a_no_op():
+    assert expand(batch=0, V=None, out=None, src=None) == OK
+    assert expand(max_len=0, V=None, out=None, src=None) == OK

@@ -199,3 +199,28 @@ def test_expand_long_decode_full_size_sampled():
                                  W.HostTensor(c.V_lr.data[r0:r0 + n], "bf16").as_f64(), c.B.as_f64(), [0], [n],
                                  [int(c.agent[b])], s.scale)
         check(got[b:b + 1], ref, "bf16", f"request {b}")
+
+
+def test_expand_then_attend_prefill_llama_full_size_sampled_rows():
+    """The Llama chunked prefill (L_P 16,384 + L_C 2,048) in the bench's launch configuration:
+    agent 1's 18,432 value rows expanded, sampled rows checked element by element, then the
+    adapter-free prefill over them against the adapted oracle on sampled query rows."""
+    say("expand-then-prefill llama 16384+2048: generating inputs")
+    c = W.llama_prefill(agent=1)
+    s = c.shape
+    n = c.L_P + c.L_C
+    zero = dev_idx([0], torch.int64)
+    V_exp = lra.lra_expand_values(dev(c.V), dev(c.V_lr), dev(c.B), zero, dev_idx([n], torch.int32),
+                                  dev_idx([1], torch.int32), n, zero)
+    O = lra.lra_attn_prefill(dev(c.Q), c.L_P, dev(c.K), V_exp, dev(c.V_lr), dev(c.B), lra.ADAPTER_FREE, s.scale)
+    torch.cuda.synchronize()
+    vrows = np.array([0, 15, 16, 255, 256, 4095, 16383, 16384, 18000, n - 1])
+    got_v = host64(V_exp[torch.as_tensor(vrows, device="cuda")])
+    ref_v = oracle.agent_values(W.HostTensor(c.V.data[vrows], "bf16").as_f64(),
+                                W.HostTensor(c.V_lr.data[vrows], "bf16").as_f64(), c.B.as_f64(), 1)
+    check(got_v, ref_v, "bf16", "expanded rows")
+    rows = np.array([0, 1, 31, 32, 127, 128, 1023, 1024, 2046, 2047])
+    say("expand-then-prefill llama 16384+2048: oracle on sampled rows")
+    ref = oracle.attn_prefill(c.Q.as_f64(), c.K.as_f64(), c.V.as_f64(), c.V_lr.as_f64(), c.B.as_f64(), 1, c.L_P,
+                              s.scale, rows=rows)
+    check(host64(O)[rows], ref, "bf16", "expand-then-prefill")

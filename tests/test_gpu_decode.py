@@ -375,3 +375,23 @@ def test_decode_qkvo_fp16_range_and_invalid_requests():
     ref = ref_decode_qkvo(c, requests=[0, 1], Q=Qb)
     check(got[0], ref[0], "bf16")
     check(got[1, ok_heads], ref[1, ok_heads], "bf16")
+
+
+def test_decode_split_boundaries_mixed_batch():
+    """The library's split (512 keys here) with lengths around 256, 512 and the split: a request
+    shorter than one split, one that ends on a split boundary, a long one, an empty and an invalid
+    request, adapter-free and adapted requests, checked against the oracle."""
+    s = W.Shape(n_q=32, n_kv=8, d_head=128, rank=16, n_agents=3, d_model=256, dtype="bf16")
+    C = lra.lra_attn_decode_default_split(12, 8, 40000)
+    assert C >= 512
+    lens = [1, 255, 256, 511, 512, 513, C - 1, C, C + 1, 3 * C + 300, 0, 40000]
+    agents = [0, 1, 2, -1, 0, 1, 2, 0, -1, 1, 0, 2]
+    c = W.random_decode((105,), s, lens, agents=agents)
+    c.agent = c.agent.copy()
+    c.agent[4] = 3   # invalid agent: NaN row, no split
+    say(f"decode split boundaries (chunk {C})")
+    got = run_decode(c)
+    ok = [b for b in range(12) if b != 4]
+    check(got[ok], ref_decode(c, requests=ok), "bf16", "split boundaries")
+    assert np.all(np.isnan(got[4]))
+    assert np.all(got[10] == 0.0)

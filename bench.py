@@ -286,7 +286,24 @@ def bench_long_decode(args, torch, lra, W, out):
         "expand_gbs": round(nbytes_x / (ms_x * 1e-3) / 1e9, 1), "expand_bytes": nbytes_x,
         "expand_frac": round(nbytes_x / (ms_x * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": "hbm",
         "order": "lra_expand_values (V_base + V_lr B_a per request) then lra_attn_decode with agent -1"}
-    del Q, K, V, L, B, O, ws, V_exp
+    del V_exp
+
+    # the same cache kept head-major ([n_kv, rows, d]): each split workgroup streams one contiguous
+    # range; same bytes, bit-identical outputs (lra_attn_decode_strided)
+    Khm = K.transpose(0, 1).contiguous()
+    Vhm = V.transpose(0, 1).contiguous()
+    Kv, Vv = Khm.transpose(0, 1), Vhm.transpose(0, 1)
+
+    def step_hm():
+        lra.lra_attn_decode_strided(Q, Kv, Vv, L, ks, kl, c.max_kv_len, B, ag, s.scale, 0, ws, O)
+
+    log("[bench] decode 16 x 66400, head-major cache")
+    ms_h = time_launches(step_hm, args.steps, args.warmup, torch)
+    gbs_h = nbytes / (ms_h * 1e-3) / 1e9
+    out["decode_head_major_llama_b16_L66400"] = {
+        "ms": round(ms_h, 4), "gbs": round(gbs_h, 1), "bytes": nbytes, "frac": round(gbs_h / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "layout": "K, V head-major [n_kv, rows, d] (lra_attn_decode_strided)"}
+    del Q, K, V, L, B, O, ws, Khm, Vhm, Kv, Vv
     torch.cuda.empty_cache()
 
 

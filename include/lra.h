@@ -54,7 +54,8 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 3   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values */
+#define LRA_ABI_VERSION 4   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
+                                4: lra_attn_decode_strided */
 
 typedef enum {
     LRA_OK = 0,
@@ -257,6 +258,30 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                     void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * lra_attn_decode over K and V caches with explicit strides, for caches kept head-major
+ * ([n_kv x rows x d_head], each KV head's rows contiguous) or in any other layout whose
+ * (row, KV head) vectors of d_head elements are contiguous. Element (row j, KV head g, dim c) of K
+ * and of V is at offset  j * kv_row_stride + g * kv_head_stride + c  (elements). Token-major
+ * ([rows x n_kv x d_head], what lra_attn_decode reads) is kv_row_stride = n_kv*d_head,
+ * kv_head_stride = d_head; head-major is kv_row_stride = d_head, kv_head_stride = rows*d_head. In the
+ * head-major layout each workgroup of the split kernel streams one contiguous range of memory.
+ * Both strides must be positive multiples of 8, kv_row_stride at most 2^24; the caller's K and V
+ * buffers must hold every element addressed for rows 0 .. kv_rows-1 (the row ranges are checked
+ * against kv_rows as in lra_attn_decode). Every other argument, the workspace
+ * (lra_attn_decode_workspace_bytes) and the results are as for lra_attn_decode: with the same
+ * values the outputs are bit-identical in either layout.
+ */
+int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            int64_t kv_row_stride, int64_t kv_head_stride,
+                            const void* V_lr, int64_t ld_vlr,
+                            const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                            const void* B, int32_t n_agents, const int32_t* agent,
+                            int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                            int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                            void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * lra_attn_decode with LoRA on the key projection as well (the qkvo configuration; LRAgent page,

@@ -20,7 +20,7 @@ __all__ = [
     "LraError", "LIB_PATH", "abi_version", "status_str",
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
-    "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split",
+    "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split", "lra_attn_decode_strided",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_expand_values",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
@@ -55,6 +55,8 @@ _SIGNATURES = {
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+    "lra_attn_decode_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p,
+                                           _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_qkvo_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
     "lra_attn_decode_qkvo": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p,
                                         _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
@@ -384,6 +386,46 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O
+
+
+def lra_attn_decode_strided(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                            kv_start: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int, B: torch.Tensor,
+                            agent: torch.Tensor, scale: float, keys_per_split: int = 0,
+                            workspace: Optional[torch.Tensor] = None, O: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """``lra_attn_decode`` over K/V views [rows, n_kv, d] of any layout with contiguous d-vectors,
+    e.g. ``K_hm.transpose(0, 1)`` of a head-major cache K_hm [n_kv, rows, d]. K_base and V_base
+    must have the same strides; the row and head strides are passed to the library as they are."""
+    _same(Q, K_base, V_base, V_lr, B)
+    for name, t in (("Q", Q), ("B", B)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    if K_base.dim() != 3 or K_base.stride(2) != 1 or V_base.shape != K_base.shape or V_base.stride() != K_base.stride():
+        raise ValueError("K_base and V_base must be [rows, n_kv, d] views with equal strides and unit last stride")
+    batch, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32 or agent.dtype != torch.int32:
+        raise TypeError("kv_start must be int64, kv_len and agent int32")
+    for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
+        if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
+    if K_base.shape[2] != d or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/V_lr/B shapes disagree")
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_decode_strided(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
+                                        K_base.stride(0), K_base.stride(1), _ptr(V_lr), V_lr.stride(0), _ptr(kv_start),
+                                        _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank,
+                                        scale, keys_per_split, _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)),
+           "lra_attn_decode_strided")
     return O
 
 

@@ -385,6 +385,7 @@ LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
     p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
+    p.kv_row_stride = int64_t(n_kv) * d_head; p.kv_head_stride = d_head;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
@@ -417,7 +418,7 @@ size_t decode_qkvo_bytes(const DecodeLayout& L, int batch, int n_q, int d_head, 
 }
 
 int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
-                const void* K_base, const void* V_base, int64_t kv_rows,
+                const void* K_base, const void* V_base, int64_t kv_rows, int64_t kv_row_stride, int64_t kv_head_stride,
                 const void* V_lr, int64_t ld_vlr,
                 const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                 const void* B, int32_t n_agents, const int32_t* agent,
@@ -440,6 +441,11 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     if (keys_per_split < 0 || keys_per_split % 64 != 0)
         return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
+    // strides: 16-byte aligned rows of d elements; a 32-key tile spans less than 2^31 bytes
+    if (kv_row_stride <= 0 || kv_head_stride <= 0 || kv_row_stride % 8 != 0 || kv_head_stride % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "K/V strides (%lld, %lld) must be positive multiples of 8",
+                    (long long)kv_row_stride, (long long)kv_head_stride);
+    if (kv_row_stride > (int64_t(1) << 24)) return fail(LRA_ERR_SHAPE, "K/V row stride exceeds 2^24 elements");
     if (batch == 0) return LRA_OK;
     if (!Q || !K_base || !V_base || !V_lr || !B || !O || !kv_start || !kv_len || !agent)
         return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
@@ -466,6 +472,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
+    p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
@@ -497,9 +504,24 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                                int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                                void* O, void* stream) {
-    return decode_call("lra_attn_decode launch", dtype, Q, batch, K_base, V_base, kv_rows, V_lr, ld_vlr, kv_start,
+    return decode_call("lra_attn_decode launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head, d_head,
+                       V_lr, ld_vlr, kv_start,
                        kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
                        workspace, workspace_bytes, O, stream, nullptr);
+}
+
+LRA_EXPORT int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
+                                       const void* K_base, const void* V_base, int64_t kv_rows,
+                                       int64_t kv_row_stride, int64_t kv_head_stride,
+                                       const void* V_lr, int64_t ld_vlr,
+                                       const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                                       const void* B, int32_t n_agents, const int32_t* agent,
+                                       int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                       int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                       void* O, void* stream) {
+    return decode_call("lra_attn_decode_strided launch", dtype, Q, batch, K_base, V_base, kv_rows, kv_row_stride,
+                       kv_head_stride, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv,
+                       d_head, rank, scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr);
 }
 
 LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
@@ -521,7 +543,8 @@ LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                                     void* O, void* stream) {
     const DecodeKeyLora kl{K_lr, ld_klr, B_k, rope_cos, rope_sin};
-    return decode_call("lra_attn_decode_qkvo launch", dtype, Q, batch, K_base, V_base, kv_rows, V_lr, ld_vlr, kv_start,
+    return decode_call("lra_attn_decode_qkvo launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
+                       d_head, V_lr, ld_vlr, kv_start,
                        kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
                        workspace, workspace_bytes, O, stream, &kl);
 }

@@ -135,10 +135,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 
     // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
     // offset per operand, so the loads use the scalar-base + vector-offset form.
-    const int64_t row_bytes = int64_t(p.n_kv) * D * sizeof(T);
+    const int64_t row_bytes = p.kv_row_stride * int64_t(sizeof(T));
     const int64_t lr_bytes = p.ld_vlr * int64_t(sizeof(T));
-    const char* __restrict__ Kg = static_cast<const char*>(p.K) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
-    const char* __restrict__ Vg = static_cast<const char*>(p.V) + (start * p.n_kv + g) * D * int64_t(sizeof(T));
+    const int64_t head_off = (start * p.kv_row_stride + g * p.kv_head_stride) * int64_t(sizeof(T));
+    const char* __restrict__ Kg = static_cast<const char*>(p.K) + head_off;
+    const char* __restrict__ Vg = static_cast<const char*>(p.V) + head_off;
     // an adapter-free request streams agent 0's columns (same rows, valid memory) through the same
     // instructions; the combine drops that product
     const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(max(a, 0)) * R) * int64_t(sizeof(T));

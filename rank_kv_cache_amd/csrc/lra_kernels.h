@@ -25,6 +25,9 @@ struct DecodeParams {
     int64_t ld_vlr;
     int64_t kv_rows;
     int64_t max_kv_len;
+    // elements between consecutive rows of one KV head, and between the KV heads of one row, of K
+    // and V (token-major [rows x n_kv x d]: n_kv*d and d; head-major [n_kv x rows x d]: d and rows*d)
+    int64_t kv_row_stride, kv_head_stride;
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
     int n_split, chunk;
     float scale;

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 3
+    assert lra.abi_version() == 4
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -360,3 +360,31 @@ def test_expand_values_rejects_bad_arguments(kw, status):
 def test_expand_values_empty_is_a_no_op():
     assert expand(batch=0, V=None, out=None, src=None) == OK
     assert expand(max_len=0, V=None, out=None, src=None) == OK
+
+
+# ---------------------------------------------------------------------------------------- strided decode
+def decode_strided(**kw):
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, rs=128, hs=12800, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+             max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088, split=0, ws=WS,
+             ws_bytes=1 << 30, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode_strided(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["rs"],
+                                            a["hs"], a["Vlr"], a["ld_vlr"], a["kv_start"], a["kv_len"],
+                                            a["max_kv_len"], a["B"], a["n_agents"], a["agent"], a["n_q"], a["n_kv"],
+                                            a["d"], a["r"], a["scale"], a["split"], a["ws"], a["ws_bytes"], a["O"],
+                                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rs=0), E_SHAPE), (dict(hs=-128), E_SHAPE), (dict(rs=100), E_SHAPE), (dict(hs=12), E_SHAPE),
+    (dict(rs=(1 << 24) + 8), E_SHAPE), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_q=30), E_SHAPE),
+    (dict(ld_vlr=16), E_SHAPE), (dict(split=100), E_SHAPE), (dict(scale=0.0), E_SHAPE), (dict(K=None), E_NULL),
+    (dict(agent=None), E_NULL), (dict(V=P + 8), E_SHAPE), (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS),
+])
+def test_decode_strided_rejects_bad_arguments(kw, status):
+    assert decode_strided(**kw) == status
+    assert lra._lib.lra_last_error().decode() != ""
+
+
+def test_decode_strided_empty_batch_is_a_no_op():
+    assert decode_strided(batch=0, Q=None, O=None, K=None) == OK

@@ -395,3 +395,53 @@ def test_decode_split_boundaries_mixed_batch():
     check(got[ok], ref_decode(c, requests=ok), "bf16", "split boundaries")
     assert np.all(np.isnan(got[4]))
     assert np.all(got[10] == 0.0)
+
+
+# ------------------------------------------------------------------------------ strided K/V (head-major)
+def run_decode_strided(c: W.DecodeBatch, K_view, V_view, keys_per_split=0):
+    s = c.shape
+    O = lra.lra_attn_decode_strided(dev(c.Q), K_view, V_view, dev(c.V_lr), dev_idx(c.kv_start, torch.int64),
+                                    dev_idx(c.kv_len, torch.int32), c.max_kv_len, dev(c.B),
+                                    dev_idx(c.agent, torch.int32), s.scale, keys_per_split)
+    torch.cuda.synchronize()
+    return host64(O)
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d,r", [("bf16", 32, 8, 128, 8), ("bf16", 32, 8, 128, 16), ("bf16", 8, 2, 64, 8),
+                                                ("f32", 4, 2, 64, 8), ("f32", 16, 2, 128, 16)])
+def test_decode_head_major_and_padded_layouts_are_bit_identical(dtype, n_q, n_kv, d, r):
+    """The same cache values laid out head-major ([n_kv, rows, d]) and with padded token rows give
+    bit-for-bit the token-major call's outputs, which match the oracle."""
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype=dtype)
+    lens = [1, 31, 64, 700, 0, 1900, 257]
+    c = W.random_decode((110, n_q, n_kv, d, r), s, lens, agents=[0, 1, 2, -1, 0, 2, 1])
+    say(f"decode strided {dtype} {n_q}/{n_kv} d={d} r={r}")
+    ref_tm = run_decode(c)
+    K, V = dev(c.K), dev(c.V)
+    Khm, Vhm = K.transpose(0, 1).contiguous(), V.transpose(0, 1).contiguous()   # [n_kv, rows, d]
+    got_hm = run_decode_strided(c, Khm.transpose(0, 1), Vhm.transpose(0, 1))
+    assert np.array_equal(got_hm, ref_tm)
+    rows = K.shape[0]
+    Kp = torch.zeros((rows, n_kv * d + 64), dtype=K.dtype, device="cuda")   # padded token rows
+    Vp = torch.zeros_like(Kp)
+    Kp[:, :n_kv * d] = K.reshape(rows, -1)
+    Vp[:, :n_kv * d] = V.reshape(rows, -1)
+    got_pad = run_decode_strided(c, Kp[:, :n_kv * d].view(rows, n_kv, d), Vp[:, :n_kv * d].view(rows, n_kv, d), 64)
+    assert np.array_equal(got_pad, run_decode(c, keys_per_split=64))
+    check(ref_tm, ref_decode(c), dtype, "token-major")
+
+
+def test_decode_head_major_16x66400_bit_identical():
+    """The 16 x 66,400 batch in the bench's launch configuration, head-major, against the token-major
+    call (bit for bit) and the oracle on two requests."""
+    say("decode head-major 16 x 66400: generating inputs")
+    c = W.llama_long_decode()
+    say("decode head-major 16 x 66400: running")
+    ref_tm = run_decode(c)
+    Khm = dev(c.K).transpose(0, 1).contiguous()
+    Vhm = dev(c.V).transpose(0, 1).contiguous()
+    got = run_decode_strided(c, Khm.transpose(0, 1), Vhm.transpose(0, 1))
+    assert np.array_equal(got, ref_tm)
+    for b in (3, 12):
+        say(f"decode head-major 16 x 66400: oracle request {b}")
+        check(got[b:b + 1], ref_decode(c, requests=[b]), "bf16", f"request {b}")

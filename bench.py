@@ -11,7 +11,7 @@ request at L = 1,900, and the Ministral-8B-shaped 36-layer step (precompute + de
 32 requests, r = 16). The CPU baseline is the fp64 oracle timed on a bounded sample of the
 headline workload on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--headline-only]
 """
 from __future__ import annotations
 
@@ -200,6 +200,10 @@ def bench_long_decode(args, torch, lra, W, out):
                    "parallelism": "none"},
     }
     out["_long_decode_case"] = c
+    if args.headline_only:   # the headline launch alone (for counter runs that must not mix variants)
+        del Q, K, V, L, B, O, ws
+        torch.cuda.empty_cache()
+        return
 
     # double batching: every other request adapter-free (agent -1: K and V_base only, no LR term)
     ag_dual = ag.clone()
@@ -602,6 +606,8 @@ def main():
     ap.add_argument("--only", nargs="*", default=None,
                     choices=["decode", "prefill", "precompute", "short", "ministral", "copy", "cpu"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode leg: time the headline launch only (no layout or variant lines)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)

@@ -246,6 +246,22 @@ def bench_long_decode(args, torch, lra, W, out):
         "ms": round(ms_p, 4), "gbs": round(gbs_p, 1), "bytes": nbytes, "frac": round(gbs_p / HBM_PEAK_GBS, 4),
         "bound": "hbm", "page_size": P, "n_pages": n_pages, "keys_per_split": split_p,
         "block_table": "seeded permutation of all pages"}
+    # the same pages head-major ([n_pages, n_kv, P, d]): each KV head's slice of a page is one run
+    Khnd = Kp.transpose(1, 2).contiguous()
+    Vhnd = Vp.transpose(1, 2).contiguous()
+    Kpv, Vpv = Khnd.transpose(1, 2), Vhnd.transpose(1, 2)
+
+    def step_paged_hnd():
+        lra.lra_attn_decode_paged_strided(Q, Kpv, Vpv, Lp, table, kl, c.max_kv_len, B, ag, s.scale, 0, ws_p, O)
+
+    log("[bench] paged decode 16 x 66400, 32-row head-major pages")
+    ms_ph = time_launches(step_paged_hnd, args.steps, args.warmup, torch)
+    gbs_ph = nbytes / (ms_ph * 1e-3) / 1e9
+    out["decode_paged_head_major_llama_b16_L66400_P32"] = {
+        "ms": round(ms_ph, 4), "gbs": round(gbs_ph, 1), "bytes": nbytes, "frac": round(gbs_ph / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "page_size": P, "layout": "pages [n_pages, n_kv, P, d] (lra_attn_decode_paged_strided)",
+        "block_table": "the same seeded permutation"}
+    del Khnd, Vhnd, Kpv, Vpv
     # LoRA on the keys as well (qkvo): the key score pass plus the decode; algorithmic bytes add each
     # request's K_lr slice (r values per key) and one read of the rotary table rows (d/2 cos + sin)
     Klr_h, Bk_h, cos_h, sin_h = W.llama_long_decode_key_lora()

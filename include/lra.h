@@ -54,8 +54,8 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 4   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
-                                4: lra_attn_decode_strided */
+#define LRA_ABI_VERSION 5   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
+                                4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided */
 
 typedef enum {
     LRA_OK = 0,
@@ -350,6 +350,29 @@ int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
                           int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                           int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                           void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * lra_attn_decode_paged with explicit strides for the K and V pages: element (page, row j of the
+ * page, KV head g, dim c) of K_pages and of V_pages is at offset
+ *   page * kv_page_stride + j * kv_row_stride + g * kv_head_stride + c      (elements).
+ * Token-major pages [n_pages x P x n_kv x d_head] (what lra_attn_decode_paged reads) are
+ * (P*n_kv*d_head, n_kv*d_head, d_head); head-major pages [n_pages x n_kv x P x d_head] are
+ * (n_kv*P*d_head, d_head, P*d_head), where each KV head's slice of a page is one contiguous run.
+ * Vlr_pages keeps its layout [n_pages x P x ld_vlr]. The strides must be positive multiples of 8,
+ * kv_row_stride at most 2^24; the caller's buffers must hold every element addressed for pages
+ * 0 .. n_pages-1. Every other argument, the workspace and the results are as for
+ * lra_attn_decode_paged: with the same values the outputs are bit-identical in either layout.
+ */
+int lra_attn_decode_paged_strided(int dtype, const void* Q, int32_t batch,
+                                  const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                                  int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                                  int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* kv_len, int64_t max_kv_len,
+                                  const void* B, int32_t n_agents, const int32_t* agent,
+                                  int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                  int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                  void* O, void* stream);
 
 /* Keys per split lra_attn_decode_paged uses when keys_per_split = 0 (0 for an unsupported P). */
 int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size);

@@ -22,7 +22,8 @@ __all__ = [
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split", "lra_attn_decode_strided",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
-    "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_expand_values",
+    "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_attn_decode_paged_strided",
+    "lra_expand_values",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
@@ -63,6 +64,9 @@ _SIGNATURES = {
     "lra_attn_decode_paged": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _p, _i32, _p, _i64, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged_default_split": (_i32, [_i32, _i32, _i64, _i32]),
+    "lra_attn_decode_paged_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _i64, _i64, _i64,
+                                                 _p, _i32, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32,
+                                                 _p, _sz, _p, _p]),
     "lra_expand_values": (_c.c_int, [_c.c_int, _p, _i64, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
                                      _i64, _p, _i64, _p, _p]),
 }
@@ -566,3 +570,48 @@ def lra_expand_values(V_base: torch.Tensor, V_lr: torch.Tensor, B: torch.Tensor,
                                   _ptr(agent), max_len, _ptr(V_out), V_out.shape[0], _ptr(dst_start),
                                   _stream(stream)), "lra_expand_values")
     return V_out
+
+
+def lra_attn_decode_paged_strided(Q: torch.Tensor, K_pages: torch.Tensor, V_pages: torch.Tensor,
+                                  Vlr_pages: torch.Tensor, block_table: torch.Tensor, kv_len: torch.Tensor,
+                                  max_kv_len: int, B: torch.Tensor, agent: torch.Tensor, scale: float,
+                                  keys_per_split: int = 0, workspace: Optional[torch.Tensor] = None,
+                                  O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``lra_attn_decode_paged`` over K/V page views [n_pages, P, n_kv, d] of any layout with
+    contiguous d-vectors, e.g. ``K_hnd.transpose(1, 2)`` of head-major pages K_hnd [n_pages, n_kv, P, d].
+    K_pages and V_pages must have the same strides; Vlr_pages is [n_pages, P, ld] as for the
+    token-major call."""
+    _same(Q, K_pages, V_pages, Vlr_pages, B)
+    for name, t in (("Q", Q), ("B", B)):
+        _dense(name, t)
+    if K_pages.dim() != 4 or K_pages.stride(3) != 1 or V_pages.shape != K_pages.shape or \
+            V_pages.stride() != K_pages.stride():
+        raise ValueError("K_pages and V_pages must be [n_pages, P, n_kv, d] views with equal strides")
+    batch, n_q, d = Q.shape
+    n_pages, P, n_kv = K_pages.shape[0], K_pages.shape[1], K_pages.shape[2]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if K_pages.shape[3] != d or B.shape[2] != n_kv * d:
+        raise ValueError("K_pages/V_pages/B shapes disagree with Q")
+    if Vlr_pages.dim() != 3 or Vlr_pages.shape[:2] != (n_pages, P) or Vlr_pages.stride(2) != 1 or \
+            Vlr_pages.stride(0) != P * Vlr_pages.stride(1):
+        raise ValueError("Vlr_pages must be [n_pages, P, ld] with rows of one page adjacent")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous() or \
+            block_table.shape[0] != batch:
+        raise TypeError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
+    for name, t in (("kv_len", kv_len), ("agent", agent)):
+        if t.dtype != torch.int32 or t.shape != (batch,) or not t.is_contiguous() or t.device != Q.device:
+            raise TypeError(f"{name} must be a contiguous int32 [batch] tensor on {Q.device}")
+    split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+    if O is None:
+        O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _check(_lib.lra_attn_decode_paged_strided(
+        _dtype_code(Q), _ptr(Q), batch, _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages), n_pages, P,
+        Vlr_pages.stride(1), K_pages.stride(0), K_pages.stride(1), K_pages.stride(2), _ptr(block_table),
+        block_table.shape[1], _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank, scale,
+        keys_per_split, _ptr(workspace), workspace.numel(), _ptr(O), _stream(stream)), "lra_attn_decode_paged_strided")
+    return O

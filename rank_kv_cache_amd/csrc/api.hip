@@ -340,15 +340,19 @@ LRA_EXPORT int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_
     return std::min(lra::decode_default_chunk(batch, n_kv, max_kv_len), paged_cap(page_size));
 }
 
-LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
-                                     const void* K_pages, const void* V_pages, const void* Vlr_pages,
-                                     int64_t n_pages, int32_t page_size, int64_t ld_vlr,
-                                     const int32_t* block_table, int32_t max_blocks,
-                                     const int32_t* kv_len, int64_t max_kv_len,
-                                     const void* B, int32_t n_agents, const int32_t* agent,
-                                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
-                                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
-                                     void* O, void* stream) {
+namespace {
+// paged decode with K / V element (page, row in page, KV head, c) at
+// page * page_stride + row * row_stride + head * head_stride + c
+int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
+                      const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                      int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                      int64_t page_stride, int64_t row_stride, int64_t head_stride,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* kv_len, int64_t max_kv_len,
+                      const void* B, int32_t n_agents, const int32_t* agent,
+                      int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                      int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                      void* O, void* stream) {
     if (int s = check_dtype(dtype)) return s;
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
     if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
@@ -366,6 +370,11 @@ LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
     if (keys_per_split && !paged_split_fits(keys_per_split, page_size))
         return fail(LRA_ERR_UNSUPPORTED, "keys_per_split=%d spans more than 64 pages of %d rows", keys_per_split, page_size);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
+    if (page_stride <= 0 || row_stride <= 0 || head_stride <= 0 || page_stride % 8 != 0 || row_stride % 8 != 0 ||
+        head_stride % 8 != 0)
+        return fail(LRA_ERR_SHAPE, "K/V strides (%lld, %lld, %lld) must be positive multiples of 8",
+                    (long long)page_stride, (long long)row_stride, (long long)head_stride);
+    if (row_stride > (int64_t(1) << 24)) return fail(LRA_ERR_SHAPE, "K/V row stride exceeds 2^24 elements");
     if (batch == 0) return LRA_OK;
     if (!Q || !K_pages || !V_pages || !Vlr_pages || !B || !O || !block_table || !kv_len || !agent)
         return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
@@ -385,13 +394,47 @@ LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
     p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
-    p.kv_row_stride = int64_t(n_kv) * d_head; p.kv_head_stride = d_head;
+    p.kv_row_stride = row_stride; p.kv_head_stride = head_stride; p.kv_page_stride = page_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
     p.block_table = block_table; p.n_pages = n_pages; p.max_blocks = max_blocks;
     p.page_shift = __builtin_ctz(unsigned(page_size));
-    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), "lra_attn_decode_paged launch");
+    return hip_status(lra::launch_decode(p, static_cast<hipStream_t>(stream)), name);
+}
+}  // namespace
+
+LRA_EXPORT int lra_attn_decode_paged(int dtype, const void* Q, int32_t batch,
+                                     const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                                     int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                                     const int32_t* block_table, int32_t max_blocks,
+                                     const int32_t* kv_len, int64_t max_kv_len,
+                                     const void* B, int32_t n_agents, const int32_t* agent,
+                                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                     void* O, void* stream) {
+    // token-major pages [n_pages x P x n_kv x d_head]
+    const int64_t row = int64_t(n_kv) * d_head;
+    return decode_paged_call("lra_attn_decode_paged launch", dtype, Q, batch, K_pages, V_pages, Vlr_pages, n_pages,
+                             page_size, ld_vlr, row * page_size, row, d_head, block_table, max_blocks, kv_len,
+                             max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
+                             workspace, workspace_bytes, O, stream);
+}
+
+LRA_EXPORT int lra_attn_decode_paged_strided(int dtype, const void* Q, int32_t batch,
+                                             const void* K_pages, const void* V_pages, const void* Vlr_pages,
+                                             int64_t n_pages, int32_t page_size, int64_t ld_vlr,
+                                             int64_t kv_page_stride, int64_t kv_row_stride, int64_t kv_head_stride,
+                                             const int32_t* block_table, int32_t max_blocks,
+                                             const int32_t* kv_len, int64_t max_kv_len,
+                                             const void* B, int32_t n_agents, const int32_t* agent,
+                                             int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                             int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                             void* O, void* stream) {
+    return decode_paged_call("lra_attn_decode_paged_strided launch", dtype, Q, batch, K_pages, V_pages, Vlr_pages,
+                             n_pages, page_size, ld_vlr, kv_page_stride, kv_row_stride, kv_head_stride, block_table,
+                             max_blocks, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale,
+                             keys_per_split, workspace, workspace_bytes, O, stream);
 }
 
 namespace {
@@ -472,7 +515,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
     p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
-    p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride;
+    p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride; p.kv_page_stride = 0;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;

@@ -120,13 +120,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         bad_pages = __ballot(lane_bad) != 0;
         page_vec = lane_bad ? 0 : id;
     }
-    // first cache row of the 32-key tile starting at key kt of the request
+    // first cache row of the 32-key tile starting at key kt of the request (V_lr rows), and the
+    // byte offset of that row in the request's K / V head (a page's rows are adjacent; pages sit
+    // kv_page_stride elements apart)
     auto tile_row = [&](int kt) -> int64_t {
         if constexpr (PAGED) {
             const int page = __builtin_amdgcn_readlane(page_vec, (kt >> p.page_shift) - first_page);
             return (int64_t(page) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
         } else {
             return kt;
+        }
+    };
+    auto tile_kv_off = [&](int kt) -> int64_t {
+        if constexpr (PAGED) {
+            const int page = __builtin_amdgcn_readlane(page_vec, (kt >> p.page_shift) - first_page);
+            return int64_t(page) * p.kv_page_stride * int64_t(sizeof(T)) +
+                   int64_t(kt & ((1 << p.page_shift) - 1)) * p.kv_row_stride * int64_t(sizeof(T));
+        } else {
+            return int64_t(kt) * p.kv_row_stride * int64_t(sizeof(T));
         }
     };
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     // k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads into the same
     // registers, so the choice is a uniform branch around address arithmetic only.
     auto load_k = [&](Tile& t, int kt) {
-        const char* kb = Kg + tile_row(kt) * row_bytes;
+        const char* kb = Kg + tile_kv_off(kt);
         if (kt + kTile <= k1) {
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -195,9 +206,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         }
     };
     auto load_v = [&](Tile& t, int kt) {
-        const int64_t row = tile_row(kt);
-        const char* vb = Vg + row * row_bytes;
-        const char* lb = Lg + row * lr_bytes;
+        const char* vb = Vg + tile_kv_off(kt);
+        const char* lb = Lg + tile_row(kt) * lr_bytes;
         // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
         // so no load sits behind a lane mask
         uint32_t h[8];

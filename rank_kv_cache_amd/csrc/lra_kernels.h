@@ -28,6 +28,7 @@ struct DecodeParams {
     // elements between consecutive rows of one KV head, and between the KV heads of one row, of K
     // and V (token-major [rows x n_kv x d]: n_kv*d and d; head-major [n_kv x rows x d]: d and rows*d)
     int64_t kv_row_stride, kv_head_stride;
+    int64_t kv_page_stride;     // paged cache: elements between consecutive pages of K and V
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
     int n_split, chunk;
     float scale;

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 4
+    assert lra.abi_version() == 5
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -388,3 +388,30 @@ def test_decode_strided_rejects_bad_arguments(kw, status):
 
 def test_decode_strided_empty_batch_is_a_no_op():
     assert decode_strided(batch=0, Q=None, O=None, K=None) == OK
+
+
+# ---------------------------------------------------------------------------------------- strided paged decode
+def decode_paged_strided(**kw):
+    a = dict(dtype=1, Q=P, batch=4, K=P, V=P, Vlr=P, n_pages=100, P=64, ld_vlr=24, ps=65536, rs=128, hs=8192,
+             table=P, max_blocks=10, kv_len=P, max_kv_len=600, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8,
+             scale=0.088, split=0, ws=P, ws_bytes=1 << 30, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode_paged_strided(
+        a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["Vlr"], a["n_pages"], a["P"], a["ld_vlr"], a["ps"], a["rs"],
+        a["hs"], a["table"], a["max_blocks"], a["kv_len"], a["max_kv_len"], a["B"], a["n_agents"], a["agent"],
+        a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"], a["split"], a["ws"], a["ws_bytes"], a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=0), E_SHAPE), (dict(rs=-8), E_SHAPE), (dict(hs=12), E_SHAPE), (dict(ps=65540), E_SHAPE),
+    (dict(rs=(1 << 24) + 8), E_SHAPE), (dict(P=48), E_UNSUP), (dict(d=96), E_UNSUP), (dict(n_pages=0), E_SHAPE),
+    (dict(max_kv_len=641), E_SHAPE), (dict(split=4096, P=32, max_kv_len=300), E_UNSUP), (dict(table=None), E_NULL),
+    (dict(K=P + 8), E_SHAPE), (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS),
+])
+def test_decode_paged_strided_rejects_bad_arguments(kw, status):
+    assert decode_paged_strided(**kw) == status
+    assert lra._lib.lra_last_error().decode() != ""
+
+
+def test_decode_paged_strided_empty_batch_is_a_no_op():
+    assert decode_paged_strided(batch=0, Q=None, O=None, table=None) == OK

@@ -445,3 +445,25 @@ def test_decode_head_major_16x66400_bit_identical():
     for b in (3, 12):
         say(f"decode head-major 16 x 66400: oracle request {b}")
         check(got[b:b + 1], ref_decode(c, requests=[b]), "bf16", f"request {b}")
+
+
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_decode_paged_head_major_pages_are_bit_identical(page_size):
+    """The same pages laid out head-major ([n_pages, n_kv, P, d], each KV head's slice of a page
+    contiguous) give bit-for-bit the token-major paged call's outputs, for the default and a
+    given split."""
+    s = W.LLAMA_SHAPE
+    lens = [1, 31, 32, 33, 700, 0, 1999, 513, 64]
+    c = W.random_paged_decode((132, page_size), s, lens, page_size, agents=[0, 1, 2, -1, 1, 0, 2, -1, 0],
+                              shared_prefix_pages=1)
+    say(f"decode paged head-major P={page_size}")
+    Khnd = dev(c.K_pages).transpose(1, 2).contiguous()   # [n_pages, n_kv, P, d]
+    Vhnd = dev(c.V_pages).transpose(1, 2).contiguous()
+    for split in (0, 128):
+        ref = run_decode_paged(c, keys_per_split=split)
+        O = lra.lra_attn_decode_paged_strided(dev(c.Q), Khnd.transpose(1, 2), Vhnd.transpose(1, 2), dev(c.Vlr_pages),
+                                              dev_idx(c.block_table, torch.int32), dev_idx(c.kv_len, torch.int32),
+                                              c.max_kv_len, dev(c.B), dev_idx(c.agents, torch.int32), s.scale, split)
+        torch.cuda.synchronize()
+        assert np.array_equal(host64(O), ref), f"split {split}"
+    check(ref, ref_decode_paged(c), "bf16", f"P={page_size}")

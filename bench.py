@@ -99,7 +99,7 @@ def counter_traffic(name: str, sources) -> tuple:
     if fields.get("source_sha256") != source_hash(sources):
         return None, "kernel source changed since the counters were taken"
     try:
-        return int(float(fields["hbm_bytes_per_launch"])), path
+        return int(float(fields["hbm_bytes_per_launch"])), os.path.relpath(path, ROOT)
     except (KeyError, ValueError):
         return None, "summary lacks hbm_bytes_per_launch"
 

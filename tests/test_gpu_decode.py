@@ -467,3 +467,41 @@ def test_decode_paged_head_major_pages_are_bit_identical(page_size):
         torch.cuda.synchronize()
         assert np.array_equal(host64(O), ref), f"split {split}"
     check(ref, ref_decode_paged(c), "bf16", f"P={page_size}")
+
+
+def test_decode_paged_bench_configuration_bit_identical():
+    """The 16 x 66,400 batch as the bench times its paged lines: 32-row pages in a seeded random
+    order, token-major and head-major pages, against the contiguous call with the same split."""
+    say("decode paged bench configuration: generating inputs")
+    c = W.llama_long_decode()
+    s = c.shape
+    Q, K, V, L, B = dev(c.Q), dev(c.K), dev(c.V), dev(c.V_lr), dev(c.B)
+    kl = dev_idx(c.kv_len, torch.int32)
+    ag = dev_idx(c.agent, torch.int32)
+    P = 32
+    split = lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P)
+    ref = lra.lra_attn_decode(Q, K, V, L, dev_idx(c.kv_start, torch.int64), kl, c.max_kv_len, B, ag, s.scale, split)
+    torch.cuda.synchronize()
+    ref = host64(ref)
+    n_pages = K.shape[0] // P
+    blocks = int(c.kv_len[0]) // P
+    g = torch.Generator(device="cpu")
+    g.manual_seed(42)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(c.batch, blocks)
+    tl = table.reshape(-1).long().cuda()   # request b's block j (rows b*L + 32 j ..) lives in page table[b, j]
+    Kp = torch.empty((n_pages, P, s.n_kv, s.d_head), dtype=K.dtype, device="cuda")
+    Vp, Lp = torch.empty_like(Kp), torch.empty((n_pages, P, L.shape[1]), dtype=L.dtype, device="cuda")
+    Kp[tl] = K.view(n_pages, P, s.n_kv, s.d_head)
+    Vp[tl] = V.view(n_pages, P, s.n_kv, s.d_head)
+    Lp[tl] = L.view(n_pages, P, L.shape[1])
+    table = table.cuda()
+    say("decode paged bench configuration: token-major pages")
+    O = lra.lra_attn_decode_paged(Q, Kp, Vp, Lp, table, kl, c.max_kv_len, B, ag, s.scale, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(O), ref)
+    say("decode paged bench configuration: head-major pages")
+    Khnd, Vhnd = Kp.transpose(1, 2).contiguous(), Vp.transpose(1, 2).contiguous()
+    O = lra.lra_attn_decode_paged_strided(Q, Khnd.transpose(1, 2), Vhnd.transpose(1, 2), Lp, table, kl, c.max_kv_len,
+                                          B, ag, s.scale, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(O), ref)

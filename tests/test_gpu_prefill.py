@@ -479,3 +479,49 @@ def test_prefill_qkvo_rejects_fp32():
     c = W.random_prefill_qkvo((323,), s, L_P=8, L_C=8, agent=0)
     with pytest.raises(lra.LraError, match="UNSUPPORTED"):
         run_prefill_qkvo(c)
+
+
+def test_prefill_varlen_and_paged_in_the_bench_configuration():
+    """The Llama prefill as the bench times its batched and paged lines: four chunk requests of 512
+    queries (request b at L_P = 16,384 + 512 b over the same cache rows) and the single chunk over
+    64-row pages in a seeded random order. Both give the single call's bits; sampled rows match the
+    oracle."""
+    say("prefill bench configuration: generating inputs")
+    c = W.llama_prefill()
+    s = c.shape
+    Q, K, V, L, B = dev(c.Q), dev(c.K), dev(c.V), dev(c.V_lr), dev(c.B)
+    one = lra.lra_attn_prefill(Q, c.L_P, K, V, L, B, 0, s.scale)
+    torch.cuda.synchronize()
+    ref_bits = host64(one)
+    nreq, lc = 4, c.L_C // 4
+    say("prefill bench configuration: varlen 4 x 512")
+    O = lra.lra_attn_prefill_varlen(Q, torch.arange(nreq, dtype=torch.int64, device="cuda") * lc,
+                                    torch.full((nreq,), lc, dtype=torch.int32, device="cuda"), lc, K, V, L,
+                                    torch.zeros(nreq, dtype=torch.int64, device="cuda"),
+                                    (c.L_P + torch.arange(nreq, device="cuda") * lc).to(torch.int32), B,
+                                    torch.zeros(nreq, dtype=torch.int32, device="cuda"), s.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(O), ref_bits)
+    say("prefill bench configuration: paged, 64-row pages")
+    P = 64
+    n_pages = K.shape[0] // P
+    g = torch.Generator(device="cpu")
+    g.manual_seed(42)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32)
+    # logical block j lives in page table[j]
+    Kp = torch.empty((n_pages, P) + tuple(K.shape[1:]), dtype=K.dtype, device="cuda")
+    Vp, Lp = torch.empty_like(Kp), torch.empty((n_pages, P, L.shape[1]), dtype=L.dtype, device="cuda")
+    tl = table.long().cuda()
+    Kp[tl] = K.view(n_pages, P, *K.shape[1:])
+    Vp[tl] = V.view(n_pages, P, *V.shape[1:])
+    Lp[tl] = L.view(n_pages, P, L.shape[1])
+    O = lra.lra_attn_prefill_paged(Q, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                                   torch.full((1,), c.L_C, dtype=torch.int32, device="cuda"), c.L_C, Kp, Vp, Lp,
+                                   table.reshape(1, n_pages).cuda(), torch.full((1,), c.L_P, dtype=torch.int32,
+                                                                                device="cuda"), B,
+                                   torch.zeros(1, dtype=torch.int32, device="cuda"), s.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(O), ref_bits)
+    rows = np.array([0, 511, 512, 1023, 1024, 1535, 1536, 2047])
+    say("prefill bench configuration: oracle on sampled rows")
+    check(ref_bits[rows], ref_prefill(c, rows=rows), "bf16")

@@ -3,7 +3,7 @@
     python -m rank_kv_cache_amd.build          # compile every source, link liblra.so
 
 Object files go to ``_build/`` at the repository root; the shared library is written next to
-this file so the Python binding (and a GPU machine receiving the tree) finds it without installing.
+this file so the Python binding (and a machine receiving a copy of the tree) finds it without installing.
 """
 from __future__ import annotations
 

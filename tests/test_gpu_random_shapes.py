@@ -108,3 +108,103 @@ def test_random_expand_then_decode_head_major(seed):
     check(host64(O_x), ref, s.dtype, f"seed {seed} expand-then-decode")
     check(host64(O_t), ref, s.dtype, f"seed {seed} decode")
     assert np.array_equal(host64(O_h), host64(O_t))
+
+
+def draw_bf16_shape(g: np.random.Generator) -> W.Shape:
+    s = draw_shape(g)
+    return W.Shape(n_q=s.n_q, n_kv=s.n_kv, d_head=s.d_head, rank=s.rank, n_agents=s.n_agents, d_model=256,
+                   dtype="bf16")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_paged_decode(seed):
+    """Random paged batches (page size, shared prefix pages, shuffled pages), token-major and
+    head-major pages (bit-identical), against the oracle."""
+    g = np.random.default_rng(4000 + seed)
+    s = draw_bf16_shape(g)
+    P = int(g.choice([32, 64, 128]))
+    batch = int(g.integers(1, 6))
+    lens = [draw_len(g, 2500) for _ in range(batch)]
+    if max(lens) == 0:
+        lens[0] = 1   # the block table needs one page
+    shared = int(g.integers(0, 2)) if min(lens) > P else 0
+    agents = [int(g.integers(-1, s.n_agents)) for _ in range(batch)]
+    say(f"random paged decode seed={seed} n_q={s.n_q} n_kv={s.n_kv} d={s.d_head} r={s.rank} N={s.n_agents} P={P} "
+        f"lens={lens} shared={shared} agents={agents}")
+    c = W.random_paged_decode((403, seed), s, lens, P, agents=agents, shared_prefix_pages=shared)
+    Q, Kp, Vp, Lp, B = dev(c.Q), dev(c.K_pages), dev(c.V_pages), dev(c.Vlr_pages), dev(c.B)
+    table, kl, ag = dev_idx(c.block_table, torch.int32), dev_idx(c.kv_len, torch.int32), dev_idx(c.agents, torch.int32)
+    mx = max(c.max_kv_len, 1)
+    O = lra.lra_attn_decode_paged(Q, Kp, Vp, Lp, table, kl, mx, B, ag, s.scale)
+    Khnd, Vhnd = Kp.transpose(1, 2).contiguous(), Vp.transpose(1, 2).contiguous()
+    O_h = lra.lra_attn_decode_paged_strided(Q, Khnd.transpose(1, 2), Vhnd.transpose(1, 2), Lp, table, kl, mx, B, ag,
+                                            s.scale)
+    torch.cuda.synchronize()
+    got = host64(O)
+    assert np.array_equal(host64(O_h), got)
+    ref = oracle.attn_decode_paged(c.Q.as_f64(), c.K_pages.as_f64(), c.V_pages.as_f64(), c.Vlr_pages.as_f64(),
+                                   c.B.as_f64(), c.block_table, c.kv_len, c.agents, s.scale)
+    live = [b for b in range(batch) if lens[b] > 0]
+    if live:
+        check(got[live], ref[live], "bf16", f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_prefill_varlen(seed):
+    g = np.random.default_rng(5000 + seed)
+    s = draw_shape(g)
+    nreq = int(g.integers(1, 5))
+    reqs = [(draw_len(g, 500) % 900, max(1, draw_len(g, 300) % 400), int(g.integers(-1, s.n_agents)))
+            for _ in range(nreq)]
+    say(f"random varlen prefill seed={seed} {s.dtype} n_q={s.n_q} n_kv={s.n_kv} d={s.d_head} r={s.rank} "
+        f"N={s.n_agents} requests={reqs}")
+    c = W.random_prefill_batch((404, seed), s, reqs)
+    O = lra.lra_attn_prefill_varlen(dev(c.Q), dev_idx(c.q_start, torch.int64), dev_idx(c.q_len, torch.int32),
+                                    c.max_q_len, dev(c.K), dev(c.V), dev(c.V_lr), dev_idx(c.kv_start, torch.int64),
+                                    dev_idx(c.kv_prefix, torch.int32), dev(c.B), dev_idx(c.agents, torch.int32),
+                                    s.scale)
+    torch.cuda.synchronize()
+    got = host64(O)
+    ref = oracle.attn_prefill_varlen(c.Q.as_f64(), c.K.as_f64(), c.V.as_f64(), c.V_lr.as_f64(), c.B.as_f64(),
+                                     c.q_start, c.q_len, c.kv_start, c.kv_prefix, c.agents, s.scale)
+    rows = np.concatenate([np.arange(int(c.q_start[b]), int(c.q_start[b]) + int(c.q_len[b])) for b in range(nreq)])
+    check(got[rows], ref[rows], s.dtype, f"seed {seed}")
+
+
+def _f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_qkvo_decode_and_prefill(seed):
+    """LoRA on the keys as well: a random decode batch and a random chunked prefill against the oracle."""
+    g = np.random.default_rng(6000 + seed)
+    s = draw_bf16_shape(g)
+    batch = int(g.integers(1, 5))
+    lens = [max(1, draw_len(g, 1500)) for _ in range(batch)]
+    agents = [int(g.integers(-1, s.n_agents)) for _ in range(batch)]
+    split = int(g.choice([0, 64, 256]))
+    say(f"random qkvo decode seed={seed} n_q={s.n_q} n_kv={s.n_kv} d={s.d_head} r={s.rank} N={s.n_agents} "
+        f"lens={lens} agents={agents} split={split}")
+    c = W.random_decode_qkvo((405, seed), s, lens, agents=agents)
+    b = c.base
+    O = lra.lra_attn_decode_qkvo(dev(b.Q), dev(b.K), dev(b.V), dev(b.V_lr), dev(c.K_lr),
+                                 dev_idx(b.kv_start, torch.int64), dev_idx(b.kv_len, torch.int32), b.max_kv_len,
+                                 dev(b.B), dev(c.B_k), _f32(c.cos), _f32(c.sin), dev_idx(b.agent, torch.int32),
+                                 s.scale, split)
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode_qkvo(b.Q.as_f64(), b.K.as_f64(), b.V.as_f64(), b.V_lr.as_f64(), c.K_lr.as_f64(),
+                                  b.B.as_f64(), c.B_k.as_f64(), c.cos, c.sin, b.kv_start, b.kv_len, b.agent, s.scale)
+    check(host64(O), ref, "bf16", f"seed {seed} decode")
+    L_P = draw_len(g, 600) % 900
+    L_C = max(1, draw_len(g, 300) % 400)
+    agent = int(g.integers(-1, s.n_agents))
+    say(f"random qkvo prefill seed={seed} L_P={L_P} L_C={L_C} agent={agent}")
+    cp = W.random_prefill_qkvo((406, seed), s, L_P, L_C, agent=agent)
+    bp = cp.base
+    O = lra.lra_attn_prefill_qkvo(dev(bp.Q), L_P, dev(bp.K), dev(bp.V), dev(bp.V_lr), dev(cp.K_lr), dev(bp.B),
+                                  dev(cp.B_k), _f32(cp.cos), _f32(cp.sin), agent, s.scale)
+    torch.cuda.synchronize()
+    ref = oracle.attn_prefill_qkvo(bp.Q.as_f64(), bp.K.as_f64(), bp.V.as_f64(), bp.V_lr.as_f64(), cp.K_lr.as_f64(),
+                                   bp.B.as_f64(), cp.B_k.as_f64(), cp.cos, cp.sin, agent, L_P, s.scale)
+    check(host64(O), ref, "bf16", f"seed {seed} prefill")

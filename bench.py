@@ -575,6 +575,26 @@ def bench_ministral_step(args, torch, lra, W, out):
                                          "timing": "HIP graph of one step" if graph_best else "eager launches",
                                          "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
                                          "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
+
+    # the same step with every layer's K and V kept head-major ([n_kv, rows, d]); same values, the
+    # decode through lra_attn_decode_strided (bit-identical outputs)
+    for i, (K, V, L, A, B, X, Q) in enumerate(layers):
+        layers[i] = (K.transpose(0, 1).contiguous().transpose(0, 1), V.transpose(0, 1).contiguous().transpose(0, 1),
+                     L, A, B, X, Q)
+        del K, V
+    torch.cuda.empty_cache()
+
+    def step_hm():
+        for (K, V, L, A, B, X, Q) in layers:
+            lra.lra_lr_precompute(X, A, s.n_agents, s.rank, L, new_rows, ws_pre)
+            lra.lra_attn_decode_strided(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, 0, ws_dec, O)
+
+    ms_h = time_launches(step_hm, reps, 1, torch)
+    gbs_h = nb / (ms_h * 1e-3) / 1e9
+    out["ministral_step_head_major_36x_b32_r16"] = {
+        "ms": round(ms_h, 3), "gbs": round(gbs_h, 1), "bytes": nb, "frac": round(gbs_h / HBM_PEAK_GBS, 4),
+        "bound": "hbm", "timing": "eager launches",
+        "layout": "K, V head-major [n_kv, rows, d] per layer (lra_attn_decode_strided)"}
     del layers
     torch.cuda.empty_cache()
 

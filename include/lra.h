@@ -54,8 +54,10 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 5   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
-                                4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided */
+#define LRA_ABI_VERSION 6   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
+                                4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided;
+                                6: finite inputs beyond the fp16 range accepted everywhere (range-safe
+                                   recomputation); the qkvo decode workspace holds fp32 key scores */
 
 typedef enum {
     LRA_OK = 0,
@@ -89,7 +91,10 @@ const char* lra_last_error(void);
  *
  * X        (device) [T x d_model], row stride ldx elements (ldx >= d_model, multiple of 8)
  * A        (device) [n_agents*rank x d_model] row-major: row k*rank + j holds column j of A_k,
- *          i.e. the agents' LoRA down-projection weights (each r x d_model) stacked
+ *          i.e. the agents' LoRA down-projection weights (each r x d_model) stacked. This is the
+ *          transpose of the pages' side-by-side [A_1 .. A_N] ([d_model x n_agents*rank]): stored
+ *          this way, both matrix-core operands (X rows and A rows) are contiguous along d_model,
+ *          and it is the usual storage of LoRA down-projection weights.
  * V_lr     (device) [vlr_rows x ld_vlr] output cache (ld_vlr >= n_agents*rank); only columns
  *          0 .. n_agents*rank-1 of the addressed rows are written
  * out_rows (device) [T] int64 destination row of each X row, or NULL for row t -> row t
@@ -123,10 +128,12 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * agent    (host) in [0, n_agents), or -1 for the adapter-free view (V_lr and B are not read);
  *          anything else returns LRA_ERR_INDEX
  * O        (device) [L_C x n_q x d_head] output
- * bf16 inputs: Q.K products are exact (bf16 operands, fp32 accumulation); for P.V the
- * probabilities are rounded to fp16 and V_base / V_lr converted exactly to fp16, so entries of the
- * KV head's V_base rows 0 .. L_P+L_C-1 and of the agent's V_lr slice must satisfy |v| <= 65504:
- * a query row whose workgroup meets a larger entry gets NaN. l, m, O and O_lr are fp32.
+ * bf16 inputs: Q.K products are exact (bf16 operands, fp32 accumulation). For P.V the
+ * probabilities are rounded to fp16 and V_base / V_lr converted exactly to fp16; a workgroup (256
+ * query rows of one KV head) that stages an entry beyond the fp16 range (|v| > 65504) recomputes
+ * its rows with bf16 V_base / V_lr (scaled by a power of two when huge) and the probabilities split
+ * into two bf16 parts, so every finite input is accepted. l, m, O and O_lr are fp32; scores and the
+ * unnormalised sums must stay finite in fp32.
  * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. L_C = 0 enqueues nothing.
  */
 int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
@@ -152,13 +159,15 @@ int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * rope_cos, rope_sin (device, fp32) [L_P+L_C x d_head/2], row j = position j
  * workspace(device) lra_attn_prefill_qkvo_workspace_bytes(L_P+L_C, n_kv, d_head) bytes, 256-byte
  *          aligned, no initialisation needed; calls sharing one workspace must be ordered (same
- *          stream). It holds the expanded keys (fp16) and per-tile range flags.
+ *          stream). It holds the expanded keys (fp16) and the largest |key| of each 64-key tile.
  * Every other argument is as for lra_attn_prefill. Agent -1 (adapter-free view) runs
  * lra_attn_prefill's kernel on K_base: none of V_lr, B, K_lr, B_k, the tables or the workspace is
  * read. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED). The Q.K products take fp16 operands with
  * fp32 accumulation: Q is converted exactly (up to fp16 subnormals) and K_a is summed in fp32 and
- * rounded to fp16 once. Entries of Q and K_a must therefore satisfy |x| <= 65504 like V_base and
- * V_lr: a query row whose workgroup meets a larger one (or a NaN key) gets NaN. ld_klr must be
+ * rounded to fp16 once. A workgroup whose queries or keys leave the fp16 range, or whose largest
+ * |query entry| times largest |key entry| exceeds 1024 (where fp16 rounding of the keys could move
+ * a score noticeably), recomputes its rows with bf16 queries against the keys rebuilt in fp32 and
+ * split into three bf16 parts (and the value side as for lra_attn_prefill). ld_klr must be
  * >= n_agents*rank and a multiple of 8; every tensor pointer 16-byte aligned.
  */
 size_t lra_attn_prefill_qkvo_workspace_bytes(int64_t n_rows, int32_t n_kv, int32_t d_head);
@@ -189,8 +198,8 @@ int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * B        (device) [n_agents x rank x n_kv*d_head]
  * A request with q_len[b] = 0 writes nothing; one whose query rows fall outside [0, q_rows) is
  * skipped. One with q_len[b] > max_q_len, a cache range outside [0, kv_rows), kv_prefix[b]+q_len[b]
- * >= 2^31 or an agent outside [-1, n_agents) gets NaN in all its output rows. Precision, the fp16
- * range condition on V_base / V_lr, alignment and ld_vlr are as for lra_attn_prefill.
+ * >= 2^31 or an agent outside [-1, n_agents) gets NaN in all its output rows. Precision (with the
+ * range-safe recomputation), alignment and ld_vlr are as for lra_attn_prefill.
  * batch = 0 or max_q_len = 0 enqueues nothing.
  */
 int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,
@@ -290,9 +299,9 @@ int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
  *   K_a[t, g] = K_base[kv_start[b] + t, g] + RoPE_t( (K_lr[kv_start[b] + t, a*rank : a*rank+rank] B_k[a])[g*d : g*d+d] )
  *
  * with a = agent[b] and RoPE_t as for lra_attn_prefill_qkvo, at table row t (a request's keys sit at
- * positions 0 .. kv_len[b]-1). The call runs two launches on `stream`: a pass that computes the
- * rank-r part of every score, Q . RoPE_t(K_lr B_k), for all query heads and writes it as fp16 into
- * the workspace, then the decode kernels, which add it to the base scores Q . K_base.
+ * positions 0 .. kv_len[b]-1). The call first computes the rank-r part of every score,
+ * Q . RoPE_t(K_lr B_k), for all query heads and writes it as fp32 into the workspace, then runs the
+ * decode kernels, which add it to the base scores Q . K_base.
  *
  * K_lr     (device) [kv_rows x ld_klr], agent a owns columns a*rank .. a*rank+rank-1
  * B_k      (device) [n_agents x rank x n_kv*d_head]
@@ -302,9 +311,10 @@ int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
  * Every other argument is as for lra_attn_decode. Adapter-free requests (agent -1) attend K_base
  * alone and read none of the key-side operands. bf16 only (LRA_F32 returns LRA_ERR_UNSUPPORTED);
  * max_kv_len <= 2^24. Precision: the base part of a score is as in lra_attn_decode; the rank-r
- * part is computed from fp16 operands (the rotated rank-r key and the query, fp32 accumulation)
- * and stored as fp16. A query entry, rotated rank-r key entry or rank-r score part that rounds
- * beyond the fp16 range (|x| >= 65520) gives NaN output for the heads concerned.
+ * part is computed from fp16 operands (per-head weights from B_k and the query, and K_lr times the
+ * rotary entries) with fp32 accumulation. A block of 512 keys whose rank-r parts come out
+ * non-finite (an operand beyond the fp16 range) or larger than 16 in the exponent (scale * |part|)
+ * is recomputed in fp32 from Q, K_lr, B_k and the tables, so every finite input is accepted.
  */
 size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
                                             int32_t rank, int64_t max_kv_len, int32_t keys_per_split);

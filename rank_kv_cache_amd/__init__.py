@@ -10,6 +10,7 @@ Importing this package loads ``liblra.so`` and fails loudly if it has not been b
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -121,11 +122,24 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _same(ref: torch.Tensor, *ts: torch.Tensor) -> None:
+    if not ref.is_cuda:
+        raise ValueError(f"tensors must be on a GPU (got {ref.device}): the kernels take device pointers")
     for t in ts:
         if t.dtype != ref.dtype:
             raise TypeError(f"dtype mismatch: {t.dtype} vs {ref.dtype}")
         if t.device != ref.device:
             raise ValueError(f"device mismatch: {t.device} vs {ref.device}")
+
+
+def _on_device(ref: torch.Tensor, **ts: Optional[torch.Tensor]) -> None:
+    """Index tensors, row maps and workspaces: on the same GPU as the data, contiguous."""
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device} (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
 
 
 def _dense(name: str, t: torch.Tensor) -> None:
@@ -144,6 +158,17 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _on(stream):
+    """Context for the buffers the binding allocates (workspaces, outputs): they are allocated on the
+    stream the kernels run on, so the caching allocator orders any reuse of that memory after them."""
+    if stream is None:
+        return contextlib.nullcontext()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(s)
 
 
 # ---------------------------------------------------------------------------------- LR precompute
@@ -169,8 +194,10 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
             raise ValueError("out_rows must be a contiguous int64 tensor with one entry per row of X")
     need = lra_lr_precompute_workspace_bytes(T, d_model, n_agents, rank)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _on_device(X, out_rows=out_rows, workspace=workspace)
     _check(_lib.lra_lr_precompute(_dtype_code(X), _ptr(X), T, d_model, X.stride(0), _ptr(A), n_agents, rank,
                                   _ptr(V_lr), V_lr.stride(0), V_lr.shape[0], _ptr(out_rows),
                                   _ptr(workspace), ws_bytes, _stream(stream)), "lra_lr_precompute")
@@ -199,7 +226,8 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
     if K_base.shape[1:] != (n_kv, d) or V_base.shape[1:] != (n_kv, d) or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/B shapes disagree with Q")
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
     _check(_lib.lra_attn_prefill(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
@@ -240,12 +268,15 @@ def lra_attn_prefill_qkvo(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_bas
     if rope_cos.shape[1:] != (d // 2,) or rope_sin.shape[1:] != (d // 2,):
         raise ValueError("rope tables must be [positions, d/2]")
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
     ws_bytes = lra_attn_prefill_qkvo_workspace_bytes(L, n_kv, d)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
+    _on_device(Q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
     _check(_lib.lra_attn_prefill_qkvo(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
                                       V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(B), _ptr(B_k), _ptr(rope_cos),
                                       _ptr(rope_sin), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(workspace),
@@ -289,11 +320,13 @@ def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch
     if any(t.shape[0] != batch for t in (q_len, kv_start, kv_prefix, agent)):
         raise ValueError("per-request tables disagree in length")
     if O is None:
-        O = torch.zeros_like(Q)
+        with _on(stream):
+            O = torch.zeros_like(Q)
     _same(Q, O)
     _dense("O", O)
     if O.shape != Q.shape:
         raise ValueError("O must have Q's shape")
+    _on_device(Q, q_start=q_start, q_len=q_len, kv_start=kv_start, kv_prefix=kv_prefix, agent=agent)
     _check(_lib.lra_attn_prefill_varlen(_dtype_code(Q), _ptr(Q), q_rows, batch, _ptr(q_start), _ptr(q_len), max_q_len,
                                         _ptr(K_base), _ptr(V_base), kv_rows, _ptr(V_lr), V_lr.stride(0),
                                         _ptr(kv_start), _ptr(kv_prefix), _ptr(B), n_agents, _ptr(agent),
@@ -329,11 +362,13 @@ def lra_attn_prefill_paged(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch.
             block_table.shape[0] != batch:
         raise TypeError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
     if O is None:
-        O = torch.zeros_like(Q)
+        with _on(stream):
+            O = torch.zeros_like(Q)
     _same(Q, O)
     _dense("O", O)
     if O.shape != Q.shape:
         raise ValueError("O must have Q's shape")
+    _on_device(Q, q_start=q_start, q_len=q_len, block_table=block_table, kv_prefix=kv_prefix, agent=agent)
     _check(_lib.lra_attn_prefill_paged(_dtype_code(Q), _ptr(Q), q_rows, batch, _ptr(q_start), _ptr(q_len), max_q_len,
                                        _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages), n_pages, P, Vlr_pages.stride(1),
                                        _ptr(block_table), block_table.shape[1], _ptr(kv_prefix), _ptr(B), n_agents,
@@ -380,12 +415,15 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
+    _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
@@ -419,12 +457,15 @@ def lra_attn_decode_strided(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
+    _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_strided(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
                                         K_base.stride(0), K_base.stride(1), _ptr(V_lr), V_lr.stride(0), _ptr(kv_start),
                                         _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank,
@@ -473,12 +514,15 @@ def lra_attn_decode_qkvo(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
         raise ValueError("rope tables must be [>= max_kv_len, d/2]")
     need = lra_attn_decode_qkvo_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
+    _on_device(Q, rope_cos=rope_cos, rope_sin=rope_sin, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_qkvo(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
                                      _ptr(V_lr), V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(kv_start), _ptr(kv_len),
                                      max_kv_len, _ptr(B), _ptr(B_k), _ptr(rope_cos), _ptr(rope_sin), n_agents,
@@ -521,11 +565,14 @@ def lra_attn_decode_paged(Q: torch.Tensor, K_pages: torch.Tensor, V_pages: torch
     split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
+    _on_device(Q, block_table=block_table, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_paged(_dtype_code(Q), _ptr(Q), batch, _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages),
                                       n_pages, P, Vlr_pages.stride(1), _ptr(block_table), block_table.shape[1],
                                       _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank,
@@ -560,11 +607,13 @@ def lra_expand_values(V_base: torch.Tensor, V_lr: torch.Tensor, B: torch.Tensor,
         if t.dtype != dt or t.numel() != batch or not t.is_contiguous() or t.device != V_base.device:
             raise TypeError(f"{name} must be a contiguous {dt} device tensor with one entry per request")
     if V_out is None:
-        V_out = torch.empty_like(V_base)
+        with _on(stream):
+            V_out = torch.empty_like(V_base)
     _same(V_base, V_out)
     _dense("V_out", V_out)
     if V_out.dim() != 3 or V_out.shape[1:] != V_base.shape[1:]:
         raise ValueError("V_out must be [out_rows, n_kv, d] like V_base")
+    _on_device(V_base, src_start=src_start, length=length, agent=agent, dst_start=dst_start)
     _check(_lib.lra_expand_values(_dtype_code(V_base), _ptr(V_base), V_base.shape[0], _ptr(V_lr), V_lr.stride(0),
                                   _ptr(B), n_agents, n_kv, d, rank, batch, _ptr(src_start), _ptr(length),
                                   _ptr(agent), max_len, _ptr(V_out), V_out.shape[0], _ptr(dst_start),
@@ -604,11 +653,14 @@ def lra_attn_decode_paged_strided(Q: torch.Tensor, K_pages: torch.Tensor, V_page
     split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+        with _on(stream):
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
     if O is None:
-        O = torch.empty_like(Q)
+        with _on(stream):
+            O = torch.empty_like(Q)
     _same(Q, O)
     _dense("O", O)
+    _on_device(Q, block_table=block_table, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_paged_strided(
         _dtype_code(Q), _ptr(Q), batch, _ptr(K_pages), _ptr(V_pages), _ptr(Vlr_pages), n_pages, P,
         Vlr_pages.stride(1), K_pages.stride(0), K_pages.stride(1), K_pages.stride(2), _ptr(block_table),

@@ -143,7 +143,8 @@ struct KeyLora {
     size_t workspace_bytes;
 };
 
-// qkvo workspace: [expanded keys: n_rows x n_kv x d_head fp16][range flags: tiles x n_kv int32]
+// qkvo workspace: [expanded keys: n_rows x n_kv x d_head fp16][largest |key| per (64-key tile, KV
+// head): tiles x n_kv fp32]
 struct KeyExpandLayout {
     size_t flags_off, total;
 };
@@ -210,6 +211,9 @@ int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int6
             return s;
         p.K = e.Ka;
         p.key_flags = e.flags;
+        // the range-safe pass rebuilds the agent's keys in fp32 from these
+        p.K_src = K_base; p.Klr = kl->K_lr; p.ld_klr = kl->ld_klr; p.Bk = kl->B_k;
+        p.rope_cos = kl->cos; p.rope_sin = kl->sin;
     }
     return hip_status(lra::launch_prefill(p, static_cast<hipStream_t>(stream)), name);
 }
@@ -450,14 +454,18 @@ struct DecodeKeyLora {
 
 int64_t key_score_stride(int64_t max_kv_len) { return (max_kv_len + 63) / 64 * 64; }
 
-// decode workspace, then (LoRA on the keys) the fp16 key scores [batch x n_q x stride], the fp16
-// score weights [batch x n_q x d_head*rank] and the repacked rotary tables, each part 256-aligned
+// decode workspace, then (LoRA on the keys) the fp32 key scores [batch x n_q x stride], the fp16
+// score weights [batch x n_q x d_head*rank], the repacked rotary tables and the score pass's range
+// flags [batch x key blocks x head blocks], each part 256-aligned
 size_t decode_qkvo_bytes(const DecodeLayout& L, int batch, int n_q, int d_head, int rank, int64_t max_kv_len,
-                         size_t* ks_off, size_t* w_off, size_t* t_off) {
+                         size_t* ks_off, size_t* w_off, size_t* t_off, size_t* f_off) {
     *ks_off = align_up(L.total, 256);
-    *w_off = align_up(*ks_off + size_t(batch) * size_t(n_q) * size_t(key_score_stride(max_kv_len)) * 2, 256);
+    *w_off = align_up(*ks_off + size_t(batch) * size_t(n_q) * size_t(key_score_stride(max_kv_len)) * 4, 256);
     *t_off = align_up(*w_off + size_t(batch) * size_t(n_q) * size_t(d_head) * size_t(rank) * 2, 256);
-    return *t_off + lra::key_score_table_bytes(max_kv_len, d_head, rank);
+    *f_off = align_up(*t_off + lra::key_score_table_bytes(max_kv_len, d_head, rank), 256);
+    const int hpb = lra::key_score_heads(d_head, rank);
+    const size_t blocks = size_t((max_kv_len + lra::kKeyScoreBlock - 1) / lra::kKeyScoreBlock);
+    return *f_off + size_t(batch) * blocks * size_t((n_q + hpb - 1) / hpb) * sizeof(int32_t);
 }
 
 int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
@@ -501,8 +509,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     }
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
     const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
-    size_t ks_off = 0, w_off = 0, t_off = 0;
-    const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off, &t_off) : 0)
+    size_t ks_off = 0, w_off = 0, t_off = 0, f_off = 0;
+    const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off, &t_off, &f_off) : 0)
                            : L.total;
     if (need) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
@@ -524,11 +532,13 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
         lra::KeyScoreParams e{};
         e.Q = Q; e.Klr = kl->K_lr; e.Bk = kl->B_k; e.rope_cos = kl->cos; e.rope_sin = kl->sin;
         e.kv_start = kv_start; e.kv_len = kv_len; e.agent = agent;
-        e.S = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ks_off);
+        e.S = reinterpret_cast<float*>(static_cast<char*>(workspace) + ks_off);
+        e.flags = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + f_off);
         e.W = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + w_off);
         e.Tp = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + t_off);
         e.kv_rows = kv_rows; e.max_kv_len = max_kv_len; e.ld_klr = kl->ld_klr; e.ks_stride = key_score_stride(max_kv_len);
         e.batch = batch; e.n_q = n_q; e.n_kv = n_kv; e.G = n_q / n_kv; e.n_agents = n_agents; e.d_head = d_head; e.rank = rank;
+        e.scale = scale;
         if (int s = hip_status(lra::launch_key_scores(e, static_cast<hipStream_t>(stream)), "lra_attn_decode_qkvo key scores"))
             return s;
         p.key_scores = e.S;
@@ -571,9 +581,9 @@ LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_
                                                        int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || d_head <= 0 || rank <= 0 || max_kv_len <= 0 || keys_per_split < 0) return 0;
     const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    size_t ks_off = 0, w_off = 0, t_off = 0;
+    size_t ks_off = 0, w_off = 0, t_off = 0, f_off = 0;
     return decode_qkvo_bytes(decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk), batch, n_q, d_head, rank,
-                             max_kv_len, &ks_off, &w_off, &t_off);
+                             max_kv_len, &ks_off, &w_off, &t_off, &f_off);
 }
 
 LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,

@@ -61,7 +61,7 @@ template <typename T, int D> struct DecodeTile {
     Vec<T, 8> k[2][KCH];   // K rows 16u + n, d = 32i + 8q .. +7
     Vec<T, VEC> v[8];      // V rows key(q, e), d = VEC*n .. +VEC-1
     Vec<T, 8> lr;          // V_lr[key(q, e)][agent*R + n % R] in slot e
-    uint2 ks[2];           // rank-r key scores (fp16) of head n, keys 16u + 4q .. +3 (LoRA on the keys)
+    float4 ks[2];          // rank-r key scores (fp32) of head n, keys 16u + 4q .. +3 (LoRA on the keys)
 };
 
 // A operand of O^T tile t from the 8 loaded V rows: slot e <- v[e][t] (16-bit transpose).
@@ -168,18 +168,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     }
 
     // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key score
-    // pass as fp16 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head n
+    // pass as fp32 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head n
     // (a wave-uniform base per request and KV head plus one 32-bit lane offset)
     const bool ks_live = KSC && a != kAdapterFree;
     const char* __restrict__ ksg = KSC ? reinterpret_cast<const char*>(p.key_scores + (int64_t(b) * p.n_q + int64_t(g) * G) * p.ks_stride) : nullptr;
-    const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 2);
+    const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 4);
     auto load_ks = [&](Tile& t, int kt) {
         if constexpr (KSC) {
             if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
-                t.ks[0] = *reinterpret_cast<const uint2*>(ksg + ks_lane + 2 * kt);
-                t.ks[1] = *reinterpret_cast<const uint2*>(ksg + ks_lane + 2 * (kt + 16));
+                t.ks[0] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * kt);
+                t.ks[1] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * (kt + 16));
             } else {
-                t.ks[0] = t.ks[1] = make_uint2(0u, 0u);
+                t.ks[0] = t.ks[1] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
     };
@@ -260,10 +260,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         if constexpr (KSC) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                sacc[u][0] += f16_lo(t.ks[u].x);
-                sacc[u][1] += f16_hi(t.ks[u].x);
-                sacc[u][2] += f16_lo(t.ks[u].y);
-                sacc[u][3] += f16_hi(t.ks[u].y);
+                sacc[u][0] += t.ks[u].x;
+                sacc[u][1] += t.ks[u].y;
+                sacc[u][2] += t.ks[u].z;
+                sacc[u][3] += t.ks[u].w;
             }
         }
         if constexpr (PREFETCH) load_k(t, kn);

@@ -16,7 +16,9 @@
 // every K_base, table and output access is a 16-byte run and the threads of a key cover its row
 // contiguously. The rank-r product (r = 8 or 16 multiply-adds per element) runs on the vector ALU
 // from the key's K_lr row (one broadcast load) and the B_k slice staged in LDS. The sum is taken in
-// fp32 and rounded once to fp16; a tile that meets |value| > 65504 or a NaN sets its flag.
+// fp32 and rounded once to fp16. Each (tile, KV head) records the largest |value| it produced (as
+// fp32 bits; +inf for a NaN), which tells the attention whether the fp16 keys are in range and
+// precise enough for its queries.
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(kThreads) void key_expand_kernel(KeyExpandParams p)
     __syncthreads();
 
     const int i0 = 8 * (tid % TPK);              // first dim of the low half
-    bool out_of_range = false;                   // |value| > 65504 or NaN (which compares false)
+    float vmax = 0.f;                            // largest |value| of this thread's keys
+    bool nan_seen = false;
 #pragma unroll
     for (int pass = 0; pass < kKeyTile / KPI; ++pass) {
         const int64_t j = int64_t(tile) * kKeyTile + pass * KPI + tid / TPK;
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void key_expand_kernel(KeyExpandParams p)
                 const float kh0 = e ? bf16_hi(wh[w]) : bf16_lo(wh[w]);
                 lo[e] = kl0 + (ylo * cv[x] - yhi * sv[x]);
                 hi[e] = kh0 + (yhi * cv[x] + ylo * sv[x]);
-                out_of_range = out_of_range || !(fabsf(lo[e]) <= kF16Max) || !(fabsf(hi[e]) <= kF16Max);
+                vmax = fmaxf(vmax, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+                nan_seen = nan_seen || lo[e] != lo[e] || hi[e] != hi[e];
             }
             ol[w] = pack_f16x2(lo[0], lo[1]);
             oh[w] = pack_f16x2(hi[0], hi[1]);
@@ -91,8 +95,12 @@ __global__ __launch_bounds__(kThreads) void key_expand_kernel(KeyExpandParams p)
         *reinterpret_cast<uint4*>(orow + i0) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
         *reinterpret_cast<uint4*>(orow + i0 + D / 2) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
     }
-    const int any_bad = __syncthreads_or(out_of_range);
-    if (tid == 0) p.flags[int64_t(tile) * p.n_kv + g] = any_bad;
+    __shared__ uint32_t tile_max;
+    if (tid == 0) tile_max = 0u;
+    __syncthreads();
+    atomicMax(&tile_max, nan_seen ? 0x7f800000u : __float_as_uint(vmax));   // |v| >= 0: the bits order like the values
+    __syncthreads();
+    if (tid == 0) p.flags[int64_t(tile) * p.n_kv + g] = int32_t(tile_max);
 }
 
 template <int D>

@@ -24,8 +24,16 @@
 // contiguous range per lane group. A small pass first repacks the rotary tables as fp16 in the
 // lanes' order (per 16-key tile and group of 8 steps, 1 KB per wave): read in their natural layout,
 // each load instruction touched 64 cache lines and those loads set the pass's time.
-// Output lane (head n, group q) holds the scores of keys 4q .. 4q+3, stored as fp16 (NaN where the
-// value is not a finite fp16 number).
+// Output lane (head n, group q) holds the scores of keys 4q .. 4q+3, stored as fp32.
+//
+// Range: the fp16 operands (weights, K_lr, rotary entries) hold magnitudes up to 65504. An operand
+// beyond that becomes infinite and makes every score it enters non-finite; and an operand inside the
+// range but large makes the fp16 rounding of the products (2^-11 relative) matter for the softmax.
+// So a workgroup that produces a non-finite score, or a rank-r score part worth more than
+// kSafeLogits in the exponent (scale * |S|; O(1) inputs give well under 1), sets its flag, and a
+// second kernel recomputes exactly those workgroups' scores in fp32 from Q, K_lr, B_k and the fp32
+// tables (rank-r up-projection, rotation, dot product, as in the expression above). Both kernels
+// write every score of their workgroup, so the flags need no clearing between calls.
 #include "lra_device.h"
 #include "lra_kernels.h"
 
@@ -34,6 +42,7 @@ namespace lra {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr float kSafeLogits = 16.f;
 
 __device__ __forceinline__ bool key_score_request_ok(const KeyScoreParams& p, int64_t start, int32_t len, int32_t a) {
     // adapter-free and invalid requests need no scores (the decode adds none / writes NaN)
@@ -84,8 +93,12 @@ __global__ __launch_bounds__(kThreads) void key_scores_kernel(KeyScoreParams p) 
     const int64_t start = p.kv_start[b];
     const int32_t len = p.kv_len[b], a = p.agent[b];
     const int32_t len32 = key_score_request_ok(p, start, len, a) ? (len + 31) / 32 * 32 : 0;   // keys the decode reads
-    if (int64_t(blk) * kKeyScoreBlock >= len32) return;   // workgroup-uniform
+    if (int64_t(blk) * kKeyScoreBlock >= len32) {   // workgroup-uniform
+        if (tid == 0) p.flags[(int64_t(b) * gridDim.y + blk) * gridDim.z + blockIdx.z] = 0;
+        return;
+    }
     const int nhq = min(HB * 16, p.n_q - h0);
+    bool nonfinite = false;   // some score of this workgroup is not finite or too large for fp16 rounding
 
     // this workgroup's head weights; rows past n_q are zero
     const uint16_t* __restrict__ Wg = p.W + (int64_t(b) * p.n_q + h0) * KF;
@@ -143,13 +156,65 @@ __global__ __launch_bounds__(kThreads) void key_scores_kernel(KeyScoreParams p) 
         for (int hb = 0; hb < HB; ++hb) {
             const int hl = 16 * hb + n;
             if (hl < nhq) {
-                float sv[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) sv[x] = fabsf(acc[hb][x]) <= kF16Max ? acc[hb][x] : __uint_as_float(0x7fc00000u);
-                uint16_t* dst = p.S + (int64_t(b) * p.n_q + h0 + hl) * p.ks_stride + jk;
-                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16x2(sv[0], sv[1]), pack_f16x2(sv[2], sv[3]));
+                for (int x = 0; x < 4; ++x) nonfinite = nonfinite || !(fabsf(acc[hb][x]) * p.scale <= kSafeLogits);
+                float* dst = p.S + (int64_t(b) * p.n_q + h0 + hl) * p.ks_stride + jk;
+                *reinterpret_cast<float4*>(dst) = make_float4(acc[hb][0], acc[hb][1], acc[hb][2], acc[hb][3]);
             }
         }
+    }
+    const int any_bad = __syncthreads_or(nonfinite);
+    if (tid == 0) p.flags[(int64_t(b) * gridDim.y + blk) * gridDim.z + blockIdx.z] = any_bad;
+}
+
+// fp32 recomputation of the scores of a workgroup of key_scores_kernel that produced a non-finite
+// value (an fp16 operand out of range): thread = (key, KV head) pair; it builds the key's rotated
+// rank-r part y = RoPE_t(K_lr[t] B_k[:, g]) pair by pair (i, i + d/2) and adds its dot product with
+// each query head of g in this workgroup's head range. Same grid and output as key_scores_kernel.
+template <int D, int R, int HB>
+__global__ __launch_bounds__(kThreads) void key_scores_exact_kernel(KeyScoreParams p) {
+    const int b = blockIdx.x, blk = blockIdx.y, h0 = blockIdx.z * (HB * 16);
+    if (p.flags[(int64_t(b) * gridDim.y + blk) * gridDim.z + blockIdx.z] == 0) return;   // workgroup-uniform
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b], a = p.agent[b];
+    if (!key_score_request_ok(p, start, len, a)) return;
+    const int len32 = (len + 31) / 32 * 32;
+    const int nhq = min(HB * 16, p.n_q - h0);
+    const int g0 = h0 / p.G, g1 = (h0 + nhq - 1) / p.G;   // KV heads of this head range
+    const int n_g = g1 - g0 + 1;
+    const int64_t kv_stride = int64_t(p.n_kv) * D;
+    const bf16* __restrict__ Bk = static_cast<const bf16*>(p.Bk) + int64_t(a) * R * kv_stride;
+    const bf16* __restrict__ Qb = static_cast<const bf16*>(p.Q) + int64_t(b) * p.n_q * D;
+    const bf16* __restrict__ Klr = static_cast<const bf16*>(p.Klr);
+    const int jbeg = blk * kKeyScoreBlock, jend = min(len32, (blk + 1) * kKeyScoreBlock);
+    for (int idx = threadIdx.x; idx < (jend - jbeg) * n_g; idx += kThreads) {
+        const int j = jbeg + idx / n_g;
+        const int g = g0 + idx % n_g;
+        const int jr = min(j, len - 1);   // later keys repeat the last row (masked by the decode)
+        float klr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) klr[r] = bf16_to_f32(Klr[(start + jr) * p.ld_klr + int64_t(a) * R + r]);
+        const int64_t trow = int64_t(jr) * (D / 2);
+        const int ha = max(h0, g * p.G), hz = min(h0 + nhq, (g + 1) * p.G);   // query heads of g here (<= 8)
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < D / 2; ++i) {
+            float ylo = 0.f, yhi = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                ylo = fmaf(klr[r], bf16_to_f32(Bk[int64_t(r) * kv_stride + int64_t(g) * D + i]), ylo);
+                yhi = fmaf(klr[r], bf16_to_f32(Bk[int64_t(r) * kv_stride + int64_t(g) * D + i + D / 2]), yhi);
+            }
+            const float c = p.rope_cos[trow + i], sn = p.rope_sin[trow + i];
+            const float rlo = ylo * c - yhi * sn, rhi = yhi * c + ylo * sn;
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                if (ha + x < hz)
+                    acc[x] = fmaf(bf16_to_f32(Qb[int64_t(ha + x) * D + i]), rlo,
+                                  fmaf(bf16_to_f32(Qb[int64_t(ha + x) * D + i + D / 2]), rhi, acc[x]));
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+            if (ha + x < hz) p.S[(int64_t(b) * p.n_q + ha + x) * p.ks_stride + j] = acc[x];
     }
 }
 
@@ -180,9 +245,11 @@ void launch_dr(const KeyScoreParams& p, hipStream_t stream) {
     const int64_t n_pack = key_score_table_tiles(p.max_kv_len) * (D * R / 32 / 8);   // (tile, group) pairs, one wave each
     hipLaunchKernelGGL((rope_pack_kernel<D, R>), dim3(unsigned((n_pack + 3) / 4)), dim3(kThreads), 0, stream, p);
     constexpr int HB = D * R <= 1024 ? 2 : 1;   // weights of 16*HB heads in LDS (about 66 KB)
+    static_assert(16 * HB == 32 || D * R > 1024, "key_score_heads");
     const dim3 grid(unsigned(p.batch), unsigned((p.max_kv_len + kKeyScoreBlock - 1) / kKeyScoreBlock),
                     unsigned((p.n_q + 16 * HB - 1) / (16 * HB)));
     hipLaunchKernelGGL((key_scores_kernel<D, R, HB>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((key_scores_exact_kernel<D, R, HB>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

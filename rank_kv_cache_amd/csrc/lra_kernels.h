@@ -40,8 +40,8 @@ struct DecodeParams {
     int max_blocks;
     int page_shift;
     // LoRA on the keys (null: none): key_scores[(b*n_q + h)*ks_stride + j] = Q_bh . RoPE_j(K_lr B_k)
-    // of request b's key j as fp16 bits (bf16 only; ks_stride a multiple of 64)
-    const uint16_t* key_scores;
+    // of request b's key j, fp32 (bf16 only; ks_stride a multiple of 64)
+    const float* key_scores;
     int64_t ks_stride;
 };
 
@@ -96,16 +96,23 @@ struct PrefillParams {
     int max_blocks;
     int page_shift;
     // LoRA on the keys too: non-null key_flags means K holds the agent's keys as fp16 bit patterns
-    // (the key expansion pass's output) and key_flags[t*n_kv + g] != 0 marks a 64-key tile of KV
-    // head g that met a value beyond the fp16 range
+    // (the key expansion pass's output) and key_flags[t*n_kv + g] holds the largest |key| of 64-key
+    // tile t of KV head g as fp32 bits. The range-safe pass rebuilds the keys in fp32 from K_src
+    // (K_base), K_lr, B_k and the rotary tables.
     const int32_t* key_flags;
+    const void* K_src;
+    const void* Klr;
+    int64_t ld_klr;
+    const void* Bk;
+    const float* rope_cos;
+    const float* rope_sin;
 };
 
 // keys per tile of the key expansion pass's range flags (the prefill's LDS key tile)
 constexpr int kKeyTile = 64;
 
 // Key expansion of the qkvo configuration: Ka[j, g] = fp16(K_base[j, g] + RoPE_j(K_lr[j, agent] B_k)),
-// with per-(64-key tile, KV head) range flags.
+// with the largest |value| of each (64-key tile, KV head) as fp32 bits in flags.
 struct KeyExpandParams {
     const void* K;              // bf16 [n_rows x n_kv x d_head]
     const void* Klr;            // bf16 [n_rows x ld_klr]
@@ -141,10 +148,12 @@ hipError_t launch_value_expand(const ValueExpandParams& p, hipStream_t stream);
 int value_expand_rows(int batch, int64_t max_len);
 
 // Decode with LoRA on the keys: the rank-r part of every score,
-// S[(b*n_q + h)*ks_stride + j] = fp16(Q[b, h] . RoPE_j(K_lr[kv_start[b] + j, agent_b] B_k[agent_b][:, g])),
-// for keys j < round_up(kv_len[b], 32) (later keys repeat the last row); NaN where it is not a
-// finite fp16 number. Requests that are invalid or adapter-free are skipped. W holds the per-head
-// weights of the features K_lr (x) [cos, sin] (d_head*rank fp16 per request and query head).
+// S[(b*n_q + h)*ks_stride + j] = Q[b, h] . RoPE_j(K_lr[kv_start[b] + j, agent_b] B_k[agent_b][:, g]) (fp32),
+// for keys j < round_up(kv_len[b], 32) (later keys repeat the last row). Requests that are invalid
+// or adapter-free are skipped. W holds the per-head weights of the features K_lr (x) [cos, sin]
+// (d_head*rank fp16 per request and query head); flags marks the score workgroups (request, key
+// block, head block) whose fp16 pass produced a non-finite or very large value and were
+// recomputed in fp32.
 struct KeyScoreParams {
     const void* Q;              // bf16 [batch x n_q x d_head]
     const void* Klr;            // bf16 [kv_rows x ld_klr]
@@ -154,11 +163,13 @@ struct KeyScoreParams {
     const int64_t* kv_start;
     const int32_t* kv_len;
     const int32_t* agent;
-    uint16_t* S;                // fp16 [batch x n_q x ks_stride]
+    float* S;                   // fp32 [batch x n_q x ks_stride]
+    int32_t* flags;             // [batch x key blocks x head blocks] (the score kernel's grid)
     uint16_t* W;                // fp16 [batch x n_q x d_head*rank]
     uint16_t* Tp;               // fp16 rotary tables in the score kernel's lane order, key_score_table_bytes()
     int64_t kv_rows, max_kv_len, ld_klr, ks_stride;
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
+    float scale;                // the softmax scale (decides when the fp32 recomputation runs)
 };
 hipError_t launch_key_scores(const KeyScoreParams& p, hipStream_t stream);
 // tiles of 16 keys of the repacked rotary tables: the score pass reads keys up to round_up(len, 32)
@@ -168,6 +179,8 @@ inline size_t key_score_table_bytes(int64_t max_kv_len, int d_head, int rank) {
     return size_t(key_score_table_tiles(max_kv_len)) * size_t(d_head * rank / 32) * 128;
 }
 constexpr int kKeyScoreBlock = 512;   // keys per workgroup of the key score pass
+// query heads per workgroup of the key score pass
+inline int key_score_heads(int d_head, int rank) { return d_head * rank <= 1024 ? 32 : 16; }
 
 // workgroups per (request, KV head) of the prefill grid for a chunk of L_C queries
 int prefill_pairs(int64_t L_C, int G);

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 5
+    assert lra.abi_version() == 6
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -99,14 +99,15 @@ def test_decode_qkvo_rejects_bad_arguments(kw, status):
 
 
 def test_decode_qkvo_workspace_size():
-    # the decode workspace, 256-aligned, then fp16 key scores [batch x n_q x round_up(max_kv_len, 64)],
-    # then fp16 score weights [batch x n_q x d_head*rank]
+    # the decode workspace, 256-aligned, then fp32 key scores [batch x n_q x round_up(max_kv_len, 64)],
+    # fp16 score weights [batch x n_q x d_head*rank], the repacked rotary tables, and one int32 flag
+    # per workgroup of the score pass [batch x ceil(max_kv_len / 512) x ceil(n_q / 32)]
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
-    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 2 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128
-    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, 2 x 4 x 64 fp16
-    # scores, 2 x 4 x 512 fp16 weights, then 2 tiles of 16 steps x 128 bytes of repacked tables
-    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 2 + 2 * 4 * 512 * 2 + 2 * 16 * 128
+    assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 4 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128 + 16 * 130 * 4
+    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, 2 x 4 x 64 fp32
+    # scores, 2 x 4 x 512 fp16 weights, 2 tiles of 16 steps x 128 bytes of repacked tables, 2 flags
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 
@@ -219,7 +220,7 @@ def test_prefill_qkvo_empty_chunk_is_a_no_op():
 
 
 def test_prefill_qkvo_workspace_size():
-    # fp16 expanded keys (256-byte aligned part), then one int32 flag per (64-key tile, KV head)
+    # fp16 expanded keys (256-byte aligned part), then the largest |key| (fp32) per (64-key tile, KV head)
     assert lra.lra_attn_prefill_qkvo_workspace_bytes(18432, 8, 128) == 18432 * 8 * 128 * 2 + 288 * 8 * 4
     assert lra.lra_attn_prefill_qkvo_workspace_bytes(65, 2, 64) == 65 * 2 * 64 * 2 + 2 * 2 * 4
     assert lra.lra_attn_prefill_qkvo_workspace_bytes(3, 1, 64) == 512 + 4
@@ -415,3 +416,21 @@ def test_decode_paged_strided_rejects_bad_arguments(kw, status):
 
 def test_decode_paged_strided_empty_batch_is_a_no_op():
     assert decode_paged_strided(batch=0, Q=None, O=None, table=None) == OK
+
+
+# ------------------------------------------------------------------------------ binding argument checks
+def test_binding_rejects_host_tensors_before_any_launch():
+    """The kernels take device pointers: host tensors (data, index tables) are refused by the binding
+    with a ValueError, before the library is called."""
+    import torch
+    Q = torch.zeros(2, 4, 64)
+    K = torch.zeros(10, 2, 64)
+    Vlr = torch.zeros(10, 24)
+    B = torch.zeros(3, 8, 128)
+    idx64, idx32 = torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        lra.lra_attn_decode(Q, K, K, Vlr, idx64, idx32, 10, B, idx32, 0.125)
+    with pytest.raises(ValueError, match="GPU"):
+        lra.lra_attn_prefill(Q, 8, K, K, Vlr, B, 0, 0.125)
+    with pytest.raises(ValueError, match="GPU"):
+        lra.lra_lr_precompute(torch.zeros(4, 64), torch.zeros(24, 64), 3, 8, Vlr)

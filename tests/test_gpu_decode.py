@@ -360,21 +360,29 @@ def test_decode_qkvo_key_part_matters_and_agents_are_isolated():
     assert np.array_equal(got, run_decode_qkvo(c, K_lr=W.to_storage(klr, "bf16")))
 
 
-def test_decode_qkvo_fp16_range_and_invalid_requests():
-    """A query entry beyond the fp16 range turns that head's output to NaN (its rank-r score part is
-    NaN); an invalid agent gives NaN rows; every other head and request stays correct."""
+@pytest.mark.parametrize("big", [1.0e5, 1.0e30])
+def test_decode_qkvo_beyond_fp16_range_matches_the_oracle(big):
+    """Large query, K_lr and B_k entries: the key-score blocks they reach come out non-finite or
+    too large for the fp16 pass and are recomputed in fp32; every head of every request matches the
+    oracle. An invalid agent still gives NaN rows."""
     s = W.LLAMA_SHAPE
-    c = W.random_decode_qkvo((333,), s, [200, 150, 90], None, None, [0, 1, 2])
+    c = W.random_decode_qkvo((333,), s, [200, 150, 90, 700], None, None, [0, 1, 2, 1])
     q = c.base.Q.as_f64().astype(np.float32)
-    q[1, 5, 3] = 1e5
-    Qb = W.to_storage(q, "bf16")
-    agents = np.array([0, 1, 7], np.int32)
-    got = run_decode_qkvo(c, agent=agents, Q=Qb)
-    assert np.all(np.isnan(got[1, 5])) and np.all(np.isnan(got[2]))
-    ok_heads = [h for h in range(s.n_q) if h != 5]
-    ref = ref_decode_qkvo(c, requests=[0, 1], Q=Qb)
-    check(got[0], ref[0], "bf16")
-    check(got[1, ok_heads], ref[1, ok_heads], "bf16")
+    q[1, 5, 3] = big
+    q[3, 30, 120] = -big
+    klr = c.K_lr.as_f64().astype(np.float32)
+    klr[int(c.base.kv_start[0]) + 17, 0 * s.rank + 4] = big    # request 0 (agent 0)
+    bk = c.B_k.as_f64().astype(np.float32)
+    bk[2, 1, 6 * s.d_head + 9] = big / 100                     # agent 2, KV head 6
+    Qb, Kb, Bb = W.to_storage(q, "bf16"), W.to_storage(klr, "bf16"), W.to_storage(bk, "bf16")
+    say(f"decode qkvo operands {big:g}")
+    got = run_decode_qkvo(c, Q=Qb, K_lr=Kb, B_k=Bb)
+    cc = W.QkvoDecodeBatch(c.base, Kb, Bb, c.cos, c.sin)
+    check(got, ref_decode_qkvo(cc, Q=Qb), "bf16", f"qkvo {big:g}")
+    agents = np.array([0, 1, 7, 1], np.int32)
+    got = run_decode_qkvo(c, agent=agents, Q=Qb, K_lr=Kb, B_k=Bb)
+    assert np.all(np.isnan(got[2]))
+    check(got[[0, 1, 3]], ref_decode_qkvo(cc, requests=[0, 1, 3], Q=Qb), "bf16")
 
 
 def test_decode_split_boundaries_mixed_batch():

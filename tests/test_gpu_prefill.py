@@ -1,4 +1,6 @@
 """GPU parity of lra_attn_prefill against the fp64 oracle (needs an MI355X and liblra.so)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -166,21 +168,62 @@ def test_prefill_is_deterministic():
     assert np.array_equal(run_prefill(c), run_prefill(c))
 
 
-def test_prefill_value_beyond_fp16_range_gives_nan_rows_of_that_head_only():
-    """|V| above 65504 cannot enter the fp16 P.V product: the affected KV head's rows come out NaN,
-    every other head stays exact."""
+@pytest.mark.parametrize("big", [1.0e5, 1.0e30])
+def test_prefill_values_beyond_fp16_range_match_the_oracle(big):
+    """Entries of V_base and of the agent's V_lr slice beyond the fp16 range (65504) send the
+    workgroups that stage them through the range-safe pass (bf16 values, P as hi + lo parts, a
+    power-of-two prescale when huge): every row still matches the oracle, including rows that never
+    see the large key but share its workgroup, and rows of other KV heads (fast pass)."""
     s = W.LLAMA_SHAPE
     c = W.random_prefill((306,), s, 40, 60, agent=1)
     V = c.V.as_f32()
-    V[10, 3, 7] = 1.0e5
-    cc = W.PrefillCase(s, c.Q, c.K, W.to_storage(V, "bf16"), c.V_lr, c.B, 40, 60, 1)
-    say("prefill fp16 range guard")
-    got = run_prefill(cc)
-    G = s.group
-    bad = list(range(3 * G, 4 * G))
-    good = [h for h in range(s.n_q) if h not in bad]
-    assert np.all(np.isnan(got[:, bad]))
-    check(got[:, good], ref_prefill(cc, heads=good), "bf16")
+    V[10, 3, 7] = big          # seen by every query row of KV head 3
+    V[95, 3, 0] = -big         # seen only by the last query rows (position 95 = L_P + 55)
+    V[50, 6, 127] = big
+    Vlr = c.V_lr.as_f32()
+    Vlr[33, 1 * s.rank + 2] = big   # agent 1's slice: every head's rows carry it through B
+    Vlr[7, 0] = np.float32(big)     # agent 0's columns: not read for agent 1
+    cc = W.PrefillCase(s, c.Q, c.K, W.to_storage(V, "bf16"), W.to_storage(Vlr, "bf16"), c.B, 40, 60, 1)
+    say(f"prefill values beyond the fp16 range ({big:g})")
+    check(run_prefill(cc), ref_prefill(cc), "bf16", f"V = {big:g}")
+    # the same with values just inside the fp16 range stay on the fast pass and match too
+    V2 = c.V.as_f32()
+    V2[10, 3, 7] = 65504.0
+    c2 = W.PrefillCase(s, c.Q, c.K, W.to_storage(V2, "bf16"), c.V_lr, c.B, 40, 60, 1)
+    check(run_prefill(c2), ref_prefill(c2), "bf16", "V = 65504")
+
+
+def test_prefill_huge_scores_match_the_oracle():
+    """Scores far beyond the usual range (|q.k| up to ~1e8): the fast pass's folded exponent (one
+    fma with the row max) would lose precision there, so those workgroups take the range-safe pass
+    (exact differences to the row max)."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill((308,), s, 100, 80, agent=2)
+    Q = c.Q.as_f32()
+    Q[7, 9, 11] = 3.0e4       # query head 9 -> KV head 2
+    Q[50, 20, 0] = -2.0e4     # query head 20 -> KV head 5
+    K = c.K.as_f32()
+    K[:, 2, 11] *= 1000.0
+    K[:, 5, 0] *= 1000.0
+    cc = W.PrefillCase(s, W.to_storage(Q, "bf16"), W.to_storage(K, "bf16"), c.V, c.V_lr, c.B, 100, 80, 2)
+    say("prefill huge scores")
+    check(run_prefill(cc), ref_prefill(cc), "bf16", "huge scores")
+
+
+def test_prefill_values_beyond_fp16_range_varlen_and_paged():
+    """The range-safe pass serves the batched and the paged calls too (same kernel): a huge value in
+    one request's rows leaves every request's rows at the oracle's values."""
+    s = W.LLAMA_SHAPE
+    c = W.random_prefill_batch((307,), s, [(30, 70, 0), (0, 1, -1), (200, 300, 2)])
+    V = c.V.as_f32()
+    V[int(c.kv_start[2]) + 5, 1, 3] = 3.0e20
+    Vlr = c.V_lr.as_f32()
+    Vlr[int(c.kv_start[0]) + 2, 0 * s.rank + 1] = -2.0e6
+    cb = dataclasses.replace(c, V=W.to_storage(V, "bf16"), V_lr=W.to_storage(Vlr, "bf16"))
+    say("prefill varlen values beyond the fp16 range")
+    got = run_prefill_varlen(cb)
+    rows = covered_rows(cb)
+    check(got[rows], ref_prefill_varlen(cb)[rows], "bf16")
 
 
 # ------------------------------------------------------------------------------ batched variable length
@@ -352,9 +395,9 @@ def _dev_f32(a: np.ndarray) -> torch.Tensor:
 
 
 def run_prefill_qkvo(c: W.QkvoPrefillCase, agent=None, K_lr=None, B_k=None, V_lr=None, B=None, K=None,
-                     workspace=None):
+                     workspace=None, V=None):
     b = c.base
-    O = lra.lra_attn_prefill_qkvo(dev(b.Q), b.L_P, dev(b.K if K is None else K), dev(b.V),
+    O = lra.lra_attn_prefill_qkvo(dev(b.Q), b.L_P, dev(b.K if K is None else K), dev(b.V if V is None else V),
                                   dev(b.V_lr if V_lr is None else V_lr), dev(c.K_lr if K_lr is None else K_lr),
                                   dev(b.B if B is None else B), dev(c.B_k if B_k is None else B_k),
                                   _dev_f32(c.cos), _dev_f32(c.sin), b.agent if agent is None else agent,
@@ -415,19 +458,20 @@ def test_prefill_qkvo_without_key_part_reduces_to_plain_prefill():
     check(got, ref_prefill(b, agent=-1), "bf16")
 
 
-def test_prefill_qkvo_out_of_fp16_range_gives_nan_rows():
-    """A query or summed key entry beyond the fp16 range turns the rows of the workgroups that meet
-    it to NaN (the score operands are fp16); other KV heads stay finite and correct."""
+@pytest.mark.parametrize("big", [1.0e5, 1.0e30])
+def test_prefill_qkvo_query_beyond_fp16_range_matches_the_oracle(big):
+    """A query entry beyond the fp16 range (the fast pass takes fp16 scores) sends its workgroups
+    through the range-safe pass: bf16 queries against the keys rebuilt in fp32 (three bf16 parts).
+    Every row matches the oracle."""
     s = W.LLAMA_SHAPE
     c = W.random_prefill_qkvo((324,), s, L_P=0, L_C=64, agent=0)
     q = c.base.Q.as_f64().astype(np.float32)
-    q[5, 3 * s.group, 7] = 1e5   # query head of KV head 3
+    q[5, 3 * s.group, 7] = big    # query head of KV head 3
+    q[40, 6 * s.group + 1, 100] = -big
     cq = W.QkvoPrefillCase(W.PrefillCase(s, W.to_storage(q, "bf16"), *[getattr(c.base, f) for f in ("K", "V", "V_lr", "B")],
                                          c.base.L_P, c.base.L_C, 0), c.K_lr, c.B_k, c.cos, c.sin)
-    got = run_prefill_qkvo(cq)
-    g = np.arange(s.n_q) // s.group
-    assert np.all(np.isnan(got[:, g == 3]))
-    check(got[:, g != 3], ref_prefill_qkvo(cq)[:, g != 3], "bf16")
+    say(f"prefill qkvo query {big:g}")
+    check(run_prefill_qkvo(cq), ref_prefill_qkvo(cq), "bf16", f"Q = {big:g}")
 
 
 def test_prefill_qkvo_expanded_keys_in_the_workspace():
@@ -447,17 +491,26 @@ def test_prefill_qkvo_expanded_keys_in_the_workspace():
     check(run_prefill_qkvo(c2, workspace=ws), ref_prefill_qkvo(c2), "bf16")
 
 
-def test_prefill_qkvo_key_beyond_fp16_range_gives_nan_rows_of_that_head():
-    """A summed key beyond the fp16 range flags its 64-key tile: every query row of that KV head that
-    sees the tile gets NaN; the other heads are unaffected."""
+@pytest.mark.parametrize("big", [7.0e4, 1.0e30])
+def test_prefill_qkvo_key_beyond_fp16_range_matches_the_oracle(big):
+    """A summed key beyond the fp16 range (here through K_base) records its tile's largest |key|;
+    every workgroup that stages the tile takes the range-safe pass and matches the oracle, and so do
+    huge V_base / V_lr entries on the same call."""
     s = W.LLAMA_SHAPE
     c = W.random_prefill_qkvo((327,), s, L_P=100, L_C=50, agent=1)
     k = c.base.K.as_f64().astype(np.float32)
-    k[10, 2, 0] = 7.0e4
-    got = run_prefill_qkvo(c, K=W.to_storage(k, "bf16"))
-    g = np.arange(s.n_q) // s.group
-    assert np.all(np.isnan(got[:, g == 2]))
-    check(got[:, g != 2], ref_prefill_qkvo(c)[:, g != 2], "bf16")
+    k[10, 2, 0] = big
+    k[120, 5, 64] = -big
+    klr = c.K_lr.as_f64().astype(np.float32)
+    klr[60, 1 * s.rank + 3] = big / 10
+    v = c.base.V.as_f64().astype(np.float32)
+    v[130, 2, 9] = big
+    say(f"prefill qkvo keys {big:g}")
+    got = run_prefill_qkvo(c, K=W.to_storage(k, "bf16"), K_lr=W.to_storage(klr, "bf16"), V=W.to_storage(v, "bf16"))
+    ck = W.QkvoPrefillCase(W.PrefillCase(s, c.base.Q, W.to_storage(k, "bf16"), W.to_storage(v, "bf16"), c.base.V_lr,
+                                         c.base.B, c.base.L_P, c.base.L_C, 1), W.to_storage(klr, "bf16"), c.B_k,
+                           c.cos, c.sin)
+    check(got, ref_prefill_qkvo(ck), "bf16", f"K = {big:g}")
 
 
 def test_prefill_qkvo_key_part_matters():

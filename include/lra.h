@@ -57,7 +57,8 @@ extern "C" {
 #define LRA_ABI_VERSION 6   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
                                 4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided;
                                 6: finite inputs beyond the fp16 range accepted everywhere (range-safe
-                                   recomputation); the qkvo decode workspace holds fp32 key scores */
+                                   recomputation); the qkvo decode workspace holds fp32 key scores;
+                                   lra_attn_decode_noalloc */
 
 typedef enum {
     LRA_OK = 0,
@@ -291,6 +292,31 @@ int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
                             int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                             int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                             void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * lra_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid allocation. It takes no workspace: the split
+ * partials live in a static device array of the library, LRA_NOALLOC_SCRATCH_BYTES bytes, of which
+ * each GPU the library runs on holds its own copy until the process ends. The call allocates
+ * nothing (no hipMalloc, no allocating library routine); it looks the array's address up once per
+ * device, on its first call there.
+ *
+ * Arguments, results and errors are those of lra_attn_decode with the same keys_per_split (same
+ * kernels, same output bits). A call whose lra_attn_decode_workspace_bytes() exceeds
+ * LRA_NOALLOC_SCRATCH_BYTES returns LRA_ERR_WORKSPACE and enqueues nothing. The array keeps the
+ * last call's contents, which no call needs cleared. Every call on one GPU uses the same array, so
+ * calls on one GPU that overlap in time (different streams, or host threads without ordering)
+ * race: order them, e.g. on one stream.
+ */
+#define LRA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            const void* V_lr, int64_t ld_vlr,
+                            const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                            const void* B, int32_t n_agents, const int32_t* agent,
+                            int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                            int32_t keys_per_split, void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * lra_attn_decode with LoRA on the key projection as well (the qkvo configuration; LRAgent page,

@@ -22,6 +22,7 @@ __all__ = [
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split", "lra_attn_decode_strided",
+    "lra_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_attn_decode_paged_strided",
     "lra_expand_values",
@@ -31,6 +32,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
 LRA_F32, LRA_BF16 = 0, 1
 ADAPTER_FREE = -1   # agent index of the adapter-free view (attention over the base cache alone)
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the static partials array of lra_attn_decode_noalloc
 
 _c = ctypes
 _p = _c.c_void_p
@@ -57,6 +59,8 @@ _SIGNATURES = {
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+    "lra_attn_decode_noalloc": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
+                                           _i32, _i32, _i32, _i32, _f, _i32, _p, _p]),
     "lra_attn_decode_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p,
                                            _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_qkvo_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
@@ -428,6 +432,35 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O
+
+
+def lra_attn_decode_noalloc(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                            kv_start: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int, B: torch.Tensor,
+                            agent: torch.Tensor, scale: float, O: torch.Tensor, keys_per_split: int = 0,
+                            stream=None) -> torch.Tensor:
+    """lra_attn_decode without a workspace: the library keeps the split partials in its own static
+    device array (NOALLOC_SCRATCH_BYTES per GPU), so the call allocates nothing. The caller passes
+    the output O. Calls on one GPU share that array: order them (e.g. on one stream)."""
+    _same(Q, K_base, V_base, V_lr, B, O)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("O", O)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    batch, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32 or agent.dtype != torch.int32:
+        raise TypeError("kv_start must be int64, kv_len and agent int32")
+    for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
+        if t.numel() != batch:
+            raise ValueError(f"{name} must have one entry per request")
+    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d or O.shape != Q.shape:
+        raise ValueError("K_base/V_base/V_lr/B/O shapes disagree")
+    _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent)
+    _check(_lib.lra_attn_decode_noalloc(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
+                                        _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                        n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split, _ptr(O),
+                                        _stream(stream)), "lra_attn_decode_noalloc")
     return O
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/lra.h"
@@ -575,6 +576,55 @@ LRA_EXPORT int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
     return decode_call("lra_attn_decode_strided launch", dtype, Q, batch, K_base, V_base, kv_rows, kv_row_stride,
                        kv_head_stride, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv,
                        d_head, rank, scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr);
+}
+
+// ============================================================================ decode without allocation
+// The split partials of lra_attn_decode_noalloc live here. In host code this name is only a stand-in
+// for the symbol: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[LRA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// device address of `scratch` on the current device (looked up on the first call there)
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (int s = hip_status(hipGetDevice(&dev), "hipGetDevice")) return s;
+    if (dev < 0 || dev >= kMaxDevices) return fail(LRA_ERR_UNSUPPORTED, "device %d: the library tracks devices 0..%d", dev, kMaxDevices - 1);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (int s = hip_status(g_scratch_err[dev], "hipGetSymbolAddress(scratch)")) return s;
+    *out = g_scratch_ptr[dev];
+    return LRA_OK;
+}
+
+}  // namespace
+
+LRA_EXPORT int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
+                                       const void* K_base, const void* V_base, int64_t kv_rows,
+                                       const void* V_lr, int64_t ld_vlr,
+                                       const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                                       const void* B, int32_t n_agents, const int32_t* agent,
+                                       int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                       int32_t keys_per_split, void* O, void* stream) {
+    const size_t need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split);
+    if (need > LRA_NOALLOC_SCRATCH_BYTES)
+        return fail(LRA_ERR_WORKSPACE, "lra_attn_decode_noalloc: these sizes need %zu bytes of partials, the static "
+                    "array holds %zu (use lra_attn_decode with a workspace)", need, size_t(LRA_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (need && batch > 0) {
+        if (int s = scratch_on_current_device(&ws)) return s;
+    }
+    return decode_call("lra_attn_decode_noalloc launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
+                       d_head, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
+                       scale, keys_per_split, ws, ws ? size_t(LRA_NOALLOC_SCRATCH_BYTES) : 0, O, stream, nullptr);
 }
 
 LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,

@@ -191,7 +191,7 @@ def bench_long_decode(args, torch, lra, W, out):
         "ms_per_step": ms, "gbs": gbs, "bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "lra_attn_decode = decode_split_kernel<bf16,128,8,4> + decode_combine_kernel<bf16,128,8>",
+                     "kernel": "lra_attn_decode = decode_split_kernel<bf16,128,8,4,false,false> + decode_combine_kernel<bf16,128,8,false>",
                      "bytes_per_launch": nbytes,
                      "traffic_source": src},
         "config": {"workload": W.WORKLOAD_NAMES[W.LLAMA_LONG_DECODE], "batch": c.batch, "kv_len": int(c.kv_len[0]),
@@ -234,7 +234,7 @@ def bench_long_decode(args, torch, lra, W, out):
     Lp = L.view(n_pages, P, L.shape[1])
     split_p = lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P)
     ws_p = torch.empty(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len,
-                                                           split_p), dtype=torch.uint8, device="cuda")
+                                                           0), dtype=torch.uint8, device="cuda")
 
     def step_paged():
         lra.lra_attn_decode_paged(Q, Kp, Vp, Lp, table, kl, c.max_kv_len, B, ag, s.scale, 0, ws_p, O)
@@ -466,7 +466,28 @@ def bench_precompute(args, torch, lra, W, out):
                                            "us_eager": round(ms * 1e3, 2),
                                            "timing": "HIP graph of 40 launches" if ms_g is not None else "eager",
                                            "x_copies_rotated": n_copies}
-    del Xs, X0, A, Vlr, ws
+    del Xs, X0, Vlr, ws
+    torch.cuda.empty_cache()
+
+    # the prefill's whole context (L_P + L_C = 18,432 rows, 151 MB of X): long enough to stream at
+    # the HBM rate; two copies of X alternate (302 MB, beyond the 256 MB Infinity Cache)
+    T = 18432
+    big = W.llama_precompute(T=T)
+    Xb = [upload(big.X, torch) for _ in range(2)]
+    Vb = torch.zeros((T, s.n_agents * s.rank), dtype=torch.bfloat16, device="cuda")
+    jt = [0]
+
+    def step_big():
+        lra.lra_lr_precompute(Xb[jt[0] % 2], A, s.n_agents, s.rank, Vb)
+        jt[0] += 1
+
+    ms_b = time_launches(step_big, 40, 4, torch)
+    nb_b = precompute_bytes(T, s.d_model, s.n_agents * s.rank)
+    gbs_b = nb_b / (ms_b * 1e-3) / 1e9
+    out["precompute_llama_18432x4096_r8"] = {"us": round(ms_b * 1e3, 2), "gbs": round(gbs_b, 1), "bytes": nb_b,
+                                            "frac": round(gbs_b / HBM_PEAK_GBS, 4), "bound": "hbm",
+                                            "timing": "eager, two copies of X alternating"}
+    del Xb, Vb, A
     torch.cuda.empty_cache()
 
 

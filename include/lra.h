@@ -100,9 +100,9 @@ const char* lra_last_error(void);
  *          0 .. n_agents*rank-1 of the addressed rows are written
  * out_rows (device) [T] int64 destination row of each X row, or NULL for row t -> row t
  *          (then vlr_rows >= T is required)
- * workspace(device) scratch of lra_lr_precompute_workspace_bytes() bytes (0 when the reduction is
- *          not split: then workspace may be NULL), 256-byte aligned; its contents need no
- *          initialisation. Calls that share one workspace must be ordered (same stream).
+ * workspace(device) lra_lr_precompute_workspace_bytes() bytes, which is 0: the reduction over
+ *          d_model finishes inside one launch. workspace may be NULL; the argument is kept so
+ *          that a later kernel may use scratch without changing the call.
  * T = 0 is allowed and enqueues nothing. d_model must be a multiple of 32; ld_vlr a multiple of 8.
  * Every tensor pointer must be 16-byte aligned.
  */
@@ -237,9 +237,10 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
 
 /* ------------------------------------------------------------------------------------------------
  * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
- * (3)-(4) with L_C = 1): each (request, KV head, split) writes a partial (m, l, O, O_lr) in fp32 to
- * the workspace; a second kernel merges the partials of a (request, KV head) with the log-sum-exp
- * rule, applies B_agent once and normalises. Request b attends all rows
+ * (3)-(4) with L_C = 1). The batch's keys, counted in 32-key tiles request after request, are cut
+ * into equal contiguous slices; each (slice, KV head) writes one fp32 partial (m, l, O, O_lr) per
+ * request piece it covers to the workspace, and a second kernel merges a request's partials with
+ * the log-sum-exp rule, applies B_agent once and normalises. Request b attends all rows
  * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
  * kv_len[b] = 0 gives a zero output row.
  *
@@ -251,7 +252,10 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  *          kernel streams agent 0's V_lr columns of the range and the merge drops that product)
  * max_kv_len (host) an upper bound on every kv_len[b]; it sizes the launch
  * B        (device) [n_agents x rank x n_kv*d_head]
- * keys_per_split  keys handled by one split (multiple of 64), or 0 for the library's choice
+ * keys_per_split  keys per slice at full lengths (batch * max_kv_len / keys_per_split slices,
+ *          rounded up to a multiple of 8; keys_per_split a multiple of 64), or 0 for the library's
+ *          choice (up to two rounds of the chip's workgroup slots, fewer when the batch's actual
+ *          lengths hold few tiles). The slicing changes the rounding of the result only.
  * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
  *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output
@@ -355,7 +359,8 @@ int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                          int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                          void* O, void* stream);
 
-/* Keys per split the library picks for these sizes when keys_per_split = 0. */
+/* Keys per slice of the library's choice (keys_per_split = 0) when every request has max_kv_len
+ * keys, rounded up to a multiple of 64 (passing it may round the slice count differently). */
 int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len);
 
 /* ------------------------------------------------------------------------------------------------
@@ -370,10 +375,10 @@ int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_k
  * block_table (device) [batch x max_blocks] int32; entries past a request's last page are unread
  * kv_len, agent (device) [batch] int32; agent[b] in [0, n_agents) or -1 (adapter-free view)
  * max_kv_len (host) an upper bound on every kv_len[b], at most max_blocks * P
- * keys_per_split  0 for lra_attn_decode_paged_default_split(), or a multiple of 64 that spans at
- *          most 64 pages (ceil(keys_per_split / P) + 1 <= 64), else LRA_ERR_UNSUPPORTED
- * workspace(device) lra_attn_decode_workspace_bytes(..., keys_per_split) bytes, with the split the
- *          call uses (the paged default split when keys_per_split = 0); no initialisation needed
+ * keys_per_split  as for lra_attn_decode (0: the library's choice, the same as for contiguous
+ *          caches); a slice may span any number of pages
+ * workspace(device) lra_attn_decode_workspace_bytes(..., keys_per_split) bytes; no initialisation
+ *          needed
  * A request whose pages include an id outside [0, n_pages) gets NaN in every output element and
  * reads page 0 in place of the bad ones. Everything else is as for lra_attn_decode.
  */
@@ -410,7 +415,7 @@ int lra_attn_decode_paged_strided(int dtype, const void* Q, int32_t batch,
                                   int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                                   void* O, void* stream);
 
-/* Keys per split lra_attn_decode_paged uses when keys_per_split = 0 (0 for an unsupported P). */
+/* lra_attn_decode_default_split for a supported page size P, else 0. */
 int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size);
 
 /* ------------------------------------------------------------------------------------------------

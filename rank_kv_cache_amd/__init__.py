@@ -595,8 +595,7 @@ def lra_attn_decode_paged(Q: torch.Tensor, K_pages: torch.Tensor, V_pages: torch
     for name, t in (("kv_len", kv_len), ("agent", agent)):
         if t.dtype != torch.int32 or t.shape != (batch,) or not t.is_contiguous() or t.device != Q.device:
             raise TypeError(f"{name} must be a contiguous int32 [batch] tensor on {Q.device}")
-    split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
-    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None:
         with _on(stream):
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
@@ -683,8 +682,7 @@ def lra_attn_decode_paged_strided(Q: torch.Tensor, K_pages: torch.Tensor, V_page
     for name, t in (("kv_len", kv_len), ("agent", agent)):
         if t.dtype != torch.int32 or t.shape != (batch,) or not t.is_contiguous() or t.device != Q.device:
             raise TypeError(f"{name} must be a contiguous int32 [batch] tensor on {Q.device}")
-    split = keys_per_split or lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, P)
-    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, split)
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None:
         with _on(stream):
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)

@@ -39,16 +39,17 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // -------------------------------------------------------------------------- decode workspace
 struct DecodeLayout {
-    int chunk, n_split;
+    int n_slices, per_round;
     size_t ml_off, o_off, total;
 };
 
-// [m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], recs = batch * n_q * n_split, 256-aligned parts
-DecodeLayout decode_layout(int batch, int n_q, int d_head, int rank, int64_t max_kv_len, int chunk) {
+// [m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], recs = (n_slices + batch) * n_q (a slice
+// holds at most one piece of each request it touches, and its pieces' records k + b are distinct),
+// 256-aligned parts. n_slices < 0: the sizes are too large for one launch.
+DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, int64_t max_kv_len, int keys_per_split) {
     DecodeLayout L{};
-    L.chunk = chunk;
-    L.n_split = max_kv_len > 0 ? int((max_kv_len + chunk - 1) / chunk) : 0;
-    const size_t recs = size_t(batch) * size_t(n_q) * size_t(L.n_split);
+    L.n_slices = lra::decode_slices(batch, n_kv, max_kv_len, keys_per_split, &L.per_round);
+    const size_t recs = L.n_slices > 0 ? size_t(L.n_slices + batch) * size_t(n_q) : 0;
     L.ml_off = 0;
     L.o_off = align_up(recs * 2 * sizeof(float), 256);
     L.total = recs ? L.o_off + recs * size_t(d_head + rank) * sizeof(float) : 0;
@@ -90,15 +91,15 @@ LRA_EXPORT const char* lra_last_error(void) { return g_last_error.c_str(); }
 
 // ============================================================================ LR precompute
 LRA_EXPORT size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, int32_t n_agents, int32_t rank) {
-    if (T <= 0 || d_model <= 0 || n_agents <= 0 || rank <= 0) return 0;
-    const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, n_agents * rank, true);
-    return pl.part_bytes;
+    (void)T; (void)d_model; (void)n_agents; (void)rank;
+    return 0;   // one launch, no partials
 }
 
 LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
                                  const void* A, int32_t n_agents, int32_t rank,
                                  void* V_lr, int64_t ld_vlr, int64_t vlr_rows, const int64_t* out_rows,
                                  void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace; (void)workspace_bytes;
     if (int s = check_dtype(dtype)) return s;
     if (T < 0) return fail(LRA_ERR_SHAPE, "T=%lld is negative", (long long)T);
     if (n_agents <= 0 || rank <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d, rank=%d must be positive", n_agents, rank);
@@ -109,23 +110,17 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
     if (ld_vlr < NR || ld_vlr % 8 != 0) return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
     if (vlr_rows < 0) return fail(LRA_ERR_SHAPE, "vlr_rows is negative");
     if (!out_rows && vlr_rows < T) return fail(LRA_ERR_SHAPE, "vlr_rows=%lld < T=%lld with identity row map", (long long)vlr_rows, (long long)T);
+    const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, int(NR), dtype == LRA_BF16);
+    if (int64_t(pl.n_rg + 7) / 8 * 8 * pl.n_cg > INT32_MAX) return fail(LRA_ERR_SHAPE, "n_agents*rank too large for one launch");
     if (T == 0) return LRA_OK;
     if (!X || !A || !V_lr) return fail(LRA_ERR_NULL, "X, A and V_lr must not be NULL");
     if (!aligned(X, 16) || !aligned(A, 16) || !aligned(V_lr, 16)) return fail(LRA_ERR_SHAPE, "X, A and V_lr must be 16-byte aligned");
 
-    const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, int(NR), dtype == LRA_BF16);
     lra::PrecomputeParams p{};
-    if (pl.ksplit > 1) {
-        const size_t need = pl.part_bytes;
-        if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-        if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-        if (workspace_bytes < need) return fail(LRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
-        p.ws_part = static_cast<float*>(workspace);
-    }
     p.X = X; p.A = A; p.Vlr = V_lr; p.out_rows = out_rows;
     p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_rows = vlr_rows;
-    p.d_model = d_model; p.NR = int(NR); p.kr = pl.kr; p.ksplit = pl.ksplit; p.n_cg = pl.n_cg;
-    p.rows_per_wg = pl.rows_per_wg;
+    p.d_model = d_model; p.NR = int(NR);
+    p.n_rg = pl.n_rg; p.n_cg = pl.n_cg; p.cols_per_group = pl.cols_per_group;
     p.bf16 = dtype == LRA_BF16;
     return hip_status(lra::launch_precompute(p, static_cast<hipStream_t>(stream)), "lra_lr_precompute launch");
 }
@@ -323,26 +318,26 @@ LRA_EXPORT int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, 
 
 // ============================================================================ decode
 LRA_EXPORT int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len) {
-    return lra::decode_default_chunk(batch, n_kv, max_kv_len);
+    // keys per slice of the library's choice when every request has max_kv_len keys
+    int per_round = 0;
+    const int n_max = lra::decode_slices(batch, n_kv, max_kv_len, 0, &per_round);
+    if (n_max <= 0) return 0;
+    const int64_t units = int64_t(batch) * ((max_kv_len + 31) / 32);
+    const int n = lra::decode_active_slices(int(std::min<int64_t>(units, INT32_MAX)), n_max, per_round);
+    const int64_t keys = (int64_t(batch) * max_kv_len + n - 1) / n;   // a valid keys_per_split: multiple of 64
+    return int32_t(std::min<int64_t>((keys + 63) / 64 * 64, INT32_MAX / 64 * 64));
 }
 
 LRA_EXPORT size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
                                                   int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || max_kv_len <= 0 || d_head <= 0 || rank <= 0) return 0;
     if (keys_per_split < 0 || keys_per_split % 64 != 0) return 0;
-    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    return decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk).total;
+    return decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split).total;
 }
-
-namespace {
-// keys per split for a paged cache: the library's choice, capped so a split spans at most 64 pages
-int paged_cap(int page_size) { return std::max(128, int(std::min<int64_t>(int64_t(63) * page_size, 1 << 30) / 128 * 128)); }
-bool paged_split_fits(int chunk, int page_size) { return (int64_t(chunk) + page_size - 1) / page_size + 1 <= 64; }
-}  // namespace
 
 LRA_EXPORT int32_t lra_attn_decode_paged_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len, int32_t page_size) {
     if (page_size < 32 || (page_size & (page_size - 1)) != 0) return 0;
-    return std::min(lra::decode_default_chunk(batch, n_kv, max_kv_len), paged_cap(page_size));
+    return lra_attn_decode_default_split(batch, n_kv, max_kv_len);
 }
 
 namespace {
@@ -372,8 +367,6 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
         return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
     if (keys_per_split < 0 || keys_per_split % 64 != 0)
         return fail(LRA_ERR_SHAPE, "keys_per_split=%d must be 0 or a positive multiple of 64", keys_per_split);
-    if (keys_per_split && !paged_split_fits(keys_per_split, page_size))
-        return fail(LRA_ERR_UNSUPPORTED, "keys_per_split=%d spans more than 64 pages of %d rows", keys_per_split, page_size);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
     if (page_stride <= 0 || row_stride <= 0 || head_stride <= 0 || page_stride % 8 != 0 || row_stride % 8 != 0 ||
         head_stride % 8 != 0)
@@ -386,8 +379,8 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
     if (!aligned(Q, 16) || !aligned(K_pages, 16) || !aligned(V_pages, 16) || !aligned(Vlr_pages, 16) || !aligned(B, 16) ||
         !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
-    const int chunk = keys_per_split ? keys_per_split : lra_attn_decode_paged_default_split(batch, n_kv, max_kv_len, page_size);
-    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
+    const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split);
+    if (L.n_slices < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
     if (L.total) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -401,7 +394,7 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
     p.kv_row_stride = row_stride; p.kv_head_stride = head_stride; p.kv_page_stride = page_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
-    p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
+    p.d_head = d_head; p.rank = rank; p.n_slices = L.n_slices; p.slices_per_round = L.per_round; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
     p.block_table = block_table; p.n_pages = n_pages; p.max_blocks = max_blocks;
     p.page_shift = __builtin_ctz(unsigned(page_size));
@@ -508,8 +501,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
         if (!aligned(kl->K_lr, 16) || !aligned(kl->B_k, 16) || !aligned(kl->cos, 16) || !aligned(kl->sin, 16))
             return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     }
-    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
-    const DecodeLayout L = decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk);
+    const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split);
+    if (L.n_slices < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
     size_t ks_off = 0, w_off = 0, t_off = 0, f_off = 0;
     const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off, &t_off, &f_off) : 0)
                            : L.total;
@@ -526,7 +519,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
     p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride; p.kv_page_stride = 0;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
-    p.d_head = d_head; p.rank = rank; p.n_split = L.n_split; p.chunk = chunk; p.scale = scale;
+    p.d_head = d_head; p.rank = rank; p.n_slices = L.n_slices; p.slices_per_round = L.per_round; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
     if (kl && max_kv_len > 0) {
         // the rank-r part of every score first, then the attention adds it to the base scores
@@ -630,10 +623,10 @@ LRA_EXPORT int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
 LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
                                                        int32_t rank, int64_t max_kv_len, int32_t keys_per_split) {
     if (batch <= 0 || n_q <= 0 || n_kv <= 0 || d_head <= 0 || rank <= 0 || max_kv_len <= 0 || keys_per_split < 0) return 0;
-    const int chunk = keys_per_split ? keys_per_split : lra::decode_default_chunk(batch, n_kv, max_kv_len);
+    if (keys_per_split % 64 != 0) return 0;
     size_t ks_off = 0, w_off = 0, t_off = 0, f_off = 0;
-    return decode_qkvo_bytes(decode_layout(batch, n_q, d_head, rank, max_kv_len, chunk), batch, n_q, d_head, rank,
-                             max_kv_len, &ks_off, &w_off, &t_off, &f_off);
+    return decode_qkvo_bytes(decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split), batch, n_q,
+                             d_head, rank, max_kv_len, &ks_off, &w_off, &t_off, &f_off);
 }
 
 LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
@@ -654,16 +647,29 @@ LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
 
 namespace lra {
 
-int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len) {
-    // about 8k (request, KV head, split) workgroups for batch x max_kv_len keys. On MI355X the 16 x
-    // 66,400-key batch is flat within 2% from 1,152 to 4,096 keys per split; batches of mixed
-    // lengths (fewer live splits than the grid) keep their balance only with the smaller splits.
-    // Splits are whole 128-key rounds of the 4 waves' 32-key tiles, between 128 and 8192 keys.
-    const int64_t work = int64_t(batch) * n_kv * max_kv_len;
-    int64_t chunk = (work + 8191) / 8192;
-    chunk = (chunk + 127) / 128 * 128;
-    if (chunk < 128) chunk = 128;
-    return int(chunk > 8192 ? 8192 : chunk);
+int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* per_round) {
+    if (per_round) *per_round = 0;
+    if (batch <= 0 || n_kv <= 0 || max_kv_len <= 0) return 0;
+    const int64_t units_max = int64_t(batch) * ((max_kv_len + 31) / 32);   // 32-key tiles
+    const int64_t n_hg = (n_kv + 7) / 8;                                   // workgroups per slice
+    int64_t n, round = 0;
+    if (keys_per_split > 0) {
+        n = (int64_t(batch) * max_kv_len + keys_per_split - 1) / keys_per_split;
+    } else {
+        // One 8-wave workgroup (one wave per KV head, 256 registers per lane) per CU on the 256 CUs
+        // of MI355X: a full round is 2048 waves. Measured on MI355X, a slice count just past a
+        // whole number of rounds costs a whole extra round, and 15/16 of a round does better than
+        // a full one (16 x 66,400 keys: 0.74 ms at 480-504 slices, 0.755 at 512; 32 requests of
+        // 1.9k-29k keys: 8.22-8.24 ms per 36 calls at 224-240 slices, 8.33 at 256). So the kernels
+        // use one such round, or two when the batch holds enough tiles (decode_active_slices).
+        round = std::max<int64_t>(8, 2048 * 15 / 16 / (n_hg * std::min(n_kv, 8)) / 8 * 8);
+        n = std::min(2 * round, (units_max + 3) / 4);
+    }
+    n = (std::max<int64_t>(n, 1) + 7) / 8 * 8;
+    // the grid (n x n_hg workgroups) and the 32-bit unit counts of the kernels stay in range
+    if (n > (int64_t(1) << 24) || n * n_hg > INT32_MAX || units_max > INT32_MAX) return -1;
+    if (per_round) *per_round = int(round);
+    return int(n);
 }
 
 }  // namespace lra

@@ -7,11 +7,17 @@
 // d_head (LRAgent page, "core method" / "technical novelty": associativity moves the d_out-wide
 // product out of the key loop).
 //
-// One kernel, one workgroup per (request b, KV head g, key split s), 4 waves. Each wave streams
-// 32-key tiles (tiles w, w+4, ... of the split): the K registers of the next tile are refilled as
-// soon as the scores are computed and the V registers as soon as P.V is done, so one tile's loads
-// are always in flight behind the arithmetic. Everything per key runs on the matrix cores; the
-// vector ALUs only do the softmax and an in-register transpose.
+// Work split: the batch's keys, counted in 32-key tiles per request, are cut into n_slices
+// contiguous slices of equal size (stream-K style), and one workgroup of 8 waves takes one slice
+// for 8 KV heads, one wave per head. Every workgroup streams the same number of bytes whatever the
+// request lengths, so the launch drains evenly; a slice covers the end of one request and the
+// start of the next as two pieces, each with its own partial. The 8 waves read the same keys of 8
+// heads, i.e. whole 2 KB token rows of a token-major cache, and the V_lr rows they share come into
+// the CU once. Workgroup w runs on XCD w % 8. In a piece, a wave streams its head's 32-key tiles:
+// the K registers of the next tile are refilled as soon as the scores are computed and the V
+// registers as soon as P.V is done, so one tile's loads are always in flight behind the
+// arithmetic. Everything per key runs on the matrix cores; the vector ALUs only do the
+// softmax and an in-register transpose.
 //   * S^T = K Q^T (16x16x32 steps): A = 16 keys x 8 d-elements (128-bit loads of K rows),
 //     B = the G query heads of the group as columns (columns >= G are zero). Lane (n, q) then
 //     holds the scores of head n for keys 4q..4q+3 of each 16-key half: the lane's 8 keys of the
@@ -23,15 +29,15 @@
 //   * P enters the bf16 step as a hi + lo pair (two steps), so the product keeps ~16 bits of P.
 //   * O_lr^T = V_lr^T P^T on one more step: row n is column n of the agent's V_lr slice.
 //   * fp32 inputs run the same loads on 16x16x4 fp32 steps (one key per slot, no transpose).
-//   * keys past the split end are clamped to its last row (finite data) and get P = 0, so no row
+//   * keys past the piece's end are clamped to its last row (finite data) and get P = 0, so no row
 //     outside [kv_start, kv_start+kv_len) is read
-//   * the 4 waves merge their states in LDS and write one fp32 partial (m, l, O, O_lr) per head
-//   * a second kernel, one workgroup per (request, query head), merges the partials with weights
-//     2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d..]) / l once per query row and rounds
-//     to the output type. Empty requests get zeros and requests with an invalid range or agent NaN.
-//     The kernel boundary orders the partial writes before the merge: a device-scope fence per
-//     workgroup (to let the last split merge in place) writes back and invalidates an XCD's L2,
-//     which cost more than the whole merge at thousands of splits.
+//   * each wave writes one fp32 partial (m, l, O, O_lr) per query head of its group and piece
+//   * a second kernel, one workgroup per (request, query head), merges the request's partials with
+//     weights 2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d..]) / l once per query row and
+//     rounds to the output type. Empty requests get zeros and requests with an invalid range or
+//     agent NaN. The kernel boundary orders the partial writes before the merge: a device-scope
+//     fence per workgroup (to let the last piece merge in place) writes back and invalidates an
+//     XCD's L2, which cost more than the whole merge at thousands of workgroups.
 #include <type_traits>
 
 #include "lra_device.h"
@@ -41,8 +47,10 @@ namespace lra {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                      // merge kernel
 constexpr int kThreads = 64 * kWaves;
+constexpr int kSplitWaves = 8;                 // split kernel: one wave per KV head of a group of 8
+constexpr int kSplitThreads = 64 * kSplitWaves;
 constexpr int kTile = 32;   // keys per wave tile
 
 __device__ __forceinline__ bool decode_request_ok(int64_t start, int32_t len, int32_t a, const DecodeParams& p) {
@@ -74,333 +82,380 @@ __device__ __forceinline__ Vec<bf16, 8> v_operand(const Vec<bf16, VEC> (&v)[8], 
     return a;
 }
 
+// Units of work: 32-key tiles. A request's units (0 when it is empty or invalid), the slice of the
+// batch's units a workgroup takes, and the slice that owns a unit. Both kernels use these integer
+// formulas, so the merge finds exactly the partials the split kernel wrote.
+// The host bounds batch x tiles(max_kv_len) below 2^31, so unit counts are 32-bit.
+template <bool PAGED>
+__device__ __forceinline__ int request_units(const DecodeParams& p, int b) {
+    const int64_t start = PAGED ? 0 : p.kv_start[b];
+    const int32_t len = p.kv_len[b];
+    return decode_request_ok(start, len, p.agent[b], p) ? (len + kTile - 1) / kTile : 0;
+}
+__device__ __forceinline__ int slice_begin(int U, int k, int n_slices) { return int(int64_t(U) * k / n_slices); }
+__device__ __forceinline__ int slice_owner(int U, int u, int n_slices) { return int((int64_t(u + 1) * n_slices - 1) / U); }
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
 template <typename T, int D, int R, int GP, bool PAGED, bool KSC>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodeParams p) {
     using Tile = DecodeTile<T, D>;
     constexpr int VEC = Tile::VEC, KCH = Tile::KCH;
     static_assert(R <= 16 && GP <= 16, "one 16-wide matrix-core tile covers the rank and the group");
 
-    __shared__ float red_o[kWaves][GP][D + R];      // per-wave O | O_lr
-    __shared__ float red_m[kWaves][GP], red_l[kWaves][GP];
-
-    // XCD-aware order: workgroup w runs on XCD w % 8. All KV heads of one (request, split) get the
-    // same w % 8, so the LR rows they all read stay in one L2.
+    // workgroup w = (slice k, group of 8 KV heads); wave wv takes KV head g. Workgroup w runs on XCD
+    // w % 8, and the head groups of one slice get the same w % 8.
     const int w = blockIdx.x;
     const int xcd = w & 7;
     const int rest = w >> 3;
-    const int g = rest % p.n_kv;
-    const int bs = (rest / p.n_kv) * 8 + xcd;
-    if (bs >= p.batch * p.n_split) return;
-    const int b = bs / p.n_split;
-    const int s = bs - b * p.n_split;
-
-    const int64_t start = PAGED ? 0 : p.kv_start[b];   // a paged request starts at its page 0
-    const int32_t len = p.kv_len[b];
-    const int32_t a = p.agent[b];
-    const int G = p.G;
-    if (!decode_request_ok(start, len, a, p)) return;   // the combine writes zeros / NaN
-    const int k0 = s * p.chunk;
-    if (k0 >= len) return;                                   // splits past the request's end do nothing
-    const int k1 = min(k0 + p.chunk, len);
-
-    const int lane = threadIdx.x & 63;
-
-    // Paged cache: lane i holds the page of the split's i-th block (at most 64 blocks per split,
-    // checked on the host); a tile never crosses a page (P is a power of two >= 32 and tiles are
-    // 32-aligned), so its page is one readlane away. Out-of-range page ids read page 0 instead
-    // and poison the split's partial with NaN.
-    int page_vec = 0, first_page = 0;
-    bool bad_pages = false;
-    if constexpr (PAGED) {
-        first_page = k0 >> p.page_shift;
-        const int n_pg = ((k1 - 1) >> p.page_shift) - first_page + 1;
-        int id = 0;
-        if (lane < n_pg) id = p.block_table[int64_t(b) * p.max_blocks + first_page + lane];
-        const bool lane_bad = lane < n_pg && (id < 0 || int64_t(id) >= p.n_pages);
-        bad_pages = __ballot(lane_bad) != 0;
-        page_vec = lane_bad ? 0 : id;
-    }
-    // first cache row of the 32-key tile starting at key kt of the request (V_lr rows), and the
-    // byte offset of that row in the request's K / V head (a page's rows are adjacent; pages sit
-    // kv_page_stride elements apart)
-    auto tile_row = [&](int kt) -> int64_t {
-        if constexpr (PAGED) {
-            const int page = __builtin_amdgcn_readlane(page_vec, (kt >> p.page_shift) - first_page);
-            return (int64_t(page) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
-        } else {
-            return kt;
-        }
-    };
-    auto tile_kv_off = [&](int kt) -> int64_t {
-        if constexpr (PAGED) {
-            const int page = __builtin_amdgcn_readlane(page_vec, (kt >> p.page_shift) - first_page);
-            return int64_t(page) * p.kv_page_stride * int64_t(sizeof(T)) +
-                   int64_t(kt & ((1 << p.page_shift) - 1)) * p.kv_row_stride * int64_t(sizeof(T));
-        } else {
-            return int64_t(kt) * p.kv_row_stride * int64_t(sizeof(T));
-        }
-    };
+    const int n_hg = (p.n_kv + kSplitWaves - 1) / kSplitWaves;
+    const int k = (rest / n_hg) * 8 + xcd;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = (rest % n_hg) * kSplitWaves + wv;
+    if (k >= p.n_slices || g >= p.n_kv) return;   // no barrier in this kernel: a wave may leave early
+    const int lane = threadIdx.x & 63;
+    const int G = p.G;
+
+    // ---- this workgroup's slice of the batch's units: [s0, s1). Every wave scans the request
+    // table itself (64 requests per step): the total, then the first request reaching past s0.
+    const int ub_first = lane < p.batch ? request_units<PAGED>(p, lane) : 0;   // the first 64 requests
+    int U = wave_sum(ub_first);
+    for (int c0 = 64; c0 < p.batch; c0 += 64) {
+        const int bb = c0 + lane;
+        U += wave_sum(bb < p.batch ? request_units<PAGED>(p, bb) : 0);
+    }
+    U = __builtin_amdgcn_readfirstlane(U);
+    const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
+    if (k >= n_act) return;
+    const int s0 = slice_begin(U, k, n_act), s1 = slice_begin(U, k + 1, n_act);
+    if (s0 >= s1) return;   // an empty slice (fewer units than slices)
+    int b = 0;
+    int Pb = 0;   // units before request b
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+        const int bb = c0 + lane;
+        const int ub = c0 == 0 ? ub_first : bb < p.batch ? request_units<PAGED>(p, bb) : 0;
+        const int incl = wave_incl_scan(ub, lane);
+        const uint64_t past = __ballot(bb < p.batch && Pb + incl > s0);
+        if (past) {
+            const int l = __builtin_ctzll(past);
+            b = c0 + l;
+            Pb += __shfl(incl - ub, l);
+            break;
+        }
+        Pb += __shfl(incl, 63);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    Pb = __builtin_amdgcn_readfirstlane(Pb);
+
     const int n = lane & 15;   // key row of K, head column of Q^T / P^T, O^T row
     const int q = lane >> 4;   // reduction slot group
-
-    // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
-    // offset per operand, so the loads use the scalar-base + vector-offset form.
     const int64_t row_bytes = p.kv_row_stride * int64_t(sizeof(T));
     const int64_t lr_bytes = p.ld_vlr * int64_t(sizeof(T));
-    const int64_t head_off = (start * p.kv_row_stride + g * p.kv_head_stride) * int64_t(sizeof(T));
-    const char* __restrict__ Kg = static_cast<const char*>(p.K) + head_off;
-    const char* __restrict__ Vg = static_cast<const char*>(p.V) + head_off;
-    // an adapter-free request streams agent 0's columns (same rows, valid memory) through the same
-    // instructions; the combine drops that product
-    const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(max(a, 0)) * R) * int64_t(sizeof(T));
-    const T* __restrict__ Qp = static_cast<const T*>(p.Q);
-    const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
-    const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
-    const uint32_t l_lane = uint32_t(4 * q * lr_bytes + (n % R) * sizeof(T));
-
-    // the group's queries as the B operand (columns >= G are zero)
-    Vec<T, 8> qf[KCH];
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        if (n < G) qf[i].load(Qp + (int64_t(b) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * q);
-        else qf[i].zero();
-    }
-
-    // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key score
-    // pass as fp32 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head n
-    // (a wave-uniform base per request and KV head plus one 32-bit lane offset)
-    const bool ks_live = KSC && a != kAdapterFree;
-    const char* __restrict__ ksg = KSC ? reinterpret_cast<const char*>(p.key_scores + (int64_t(b) * p.n_q + int64_t(g) * G) * p.ks_stride) : nullptr;
-    const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 4);
-    auto load_ks = [&](Tile& t, int kt) {
-        if constexpr (KSC) {
-            if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
-                t.ks[0] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * kt);
-                t.ks[1] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * (kt + 16));
-            } else {
-                t.ks[0] = t.ks[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-    };
-    // Tile loads. A full tile addresses each operand as a wave-uniform base (scalar registers) plus
-    // one 32-bit lane offset. Only a split's last tile can run past k1: its rows are clamped to
-    // k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads into the same
-    // registers, so the choice is a uniform branch around address arithmetic only.
-    auto load_k = [&](Tile& t, int kt) {
-        const char* kb = Kg + tile_kv_off(kt);
-        if (kt + kTile <= k1) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < KCH; ++i)
-                    t.k[u][i].load(reinterpret_cast<const T*>(kb + 16 * u * row_bytes + k_lane) + 32 * i);
-        } else {
-            const int lim = k1 - 1 - kt;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint32_t o = uint32_t(min(16 * u + n, lim) * row_bytes + 8 * q * sizeof(T));
-#pragma unroll
-                for (int i = 0; i < KCH; ++i) t.k[u][i].load(reinterpret_cast<const T*>(kb + o) + 32 * i);
-            }
-        }
-    };
-    auto load_v = [&](Tile& t, int kt) {
-        const char* vb = Vg + tile_kv_off(kt);
-        const char* lb = Lg + tile_row(kt) * lr_bytes;
-        // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
-        // so no load sits behind a lane mask
-        uint32_t h[8];
-        if (kt + kTile <= k1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                t.v[e].load(reinterpret_cast<const T*>(vb + tile_key(0, e) * row_bytes + v_lane));
-                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + tile_key(0, e) * lr_bytes + l_lane);
-                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + tile_key(0, e) * lr_bytes + l_lane);
-            }
-        } else {
-            const int lim = k1 - 1 - kt;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = min(tile_key(q, e), lim);
-                t.v[e].load(reinterpret_cast<const T*>(vb + uint32_t(key * row_bytes + VEC * n * sizeof(T))));
-                const uint32_t lo = uint32_t(key * lr_bytes + (n % R) * sizeof(T));
-                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + lo);
-                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + lo);
-            }
-        }
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
-        }
-    };
-
-    f32x4 acc[VEC];
-    f32x4 acc_lr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < VEC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale * kLog2e;
 
-    // One tile: scores, online softmax, P.V. With PREFETCH the K registers are refilled with the
-    // next tile as soon as the scores are done and the V registers as soon as P.V is done, so one
-    // tile's loads are always in flight behind the arithmetic.
-    auto tile_step = [&](Tile& t, int kt, auto prefetch) {
-        constexpr bool PREFETCH = decltype(prefetch)::value;
-        const int kn = kt + kWaves * kTile;
-        // the key scores are loaded here, not a tile ahead: prefetched, they overflow the registers
-        load_ks(t, kt);
-        f32x4 sacc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < KCH; ++i) sacc[u] = mma16x16x32(t.k[u][i], qf[i], sacc[u]);
+    // ---- the slice's pieces: the part of each request's units that falls in [s0, s1)
+    int u = s0;
+    while (u < s1) {   // workgroup-uniform
+        const int ub = request_units<PAGED>(p, b);
+        const int Pn = Pb + ub;
+        if (ub == 0 || Pn <= u) {   // a request with no units (empty or invalid)
+            Pb = Pn;
+            ++b;
+            continue;
         }
-        if constexpr (KSC) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                sacc[u][0] += t.ks[u].x;
-                sacc[u][1] += t.ks[u].y;
-                sacc[u][2] += t.ks[u].z;
-                sacc[u][3] += t.ks[u].w;
+        const int pe = min(Pn, s1);
+        const int64_t start = PAGED ? 0 : p.kv_start[b];
+        const int32_t len = p.kv_len[b];
+        const int32_t a = p.agent[b];
+        const int k0 = (u - Pb) * kTile;                  // keys [k0, k1) of request b
+        const int k1 = min((pe - Pb) * kTile, int(len));
+        u = pe;
+        Pb = Pn;
+        ++b;
+
+        // Paged cache: each wave keeps the page ids of 64 consecutive blocks of the request, one
+        // per lane, and reloads that window when a tile moves past it; a tile never crosses a page
+        // (P is a power of two >= 32 and tiles are 32-aligned), so its page is one readlane away.
+        // Out-of-range page ids read page 0 instead and poison the piece's partial with NaN.
+        int page_vec = 0, pg_base = -(1 << 30);
+        bool bad_pages = false;
+        const int n_blk = PAGED ? ((len - 1) >> p.page_shift) + 1 : 0;
+        auto page_of = [&](int kt) -> int {
+            const int blk = kt >> p.page_shift;   // wave-uniform
+            if (blk - pg_base >= 64) {
+                pg_base = blk;
+                int id = 0;
+                if (pg_base + lane < n_blk) id = p.block_table[int64_t(b - 1) * p.max_blocks + pg_base + lane];
+                const bool lane_bad = pg_base + lane < n_blk && (id < 0 || int64_t(id) >= p.n_pages);
+                bad_pages = bad_pages || __ballot(lane_bad) != 0;
+                page_vec = lane_bad ? 0 : id;
             }
-        }
-        if constexpr (PREFETCH) load_k(t, kn);
-        float sc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = sacc[e >> 2][e & 3] * sl2;
-        if (!PREFETCH && kt + kTile > k1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (kt + tile_key(q, e) >= k1) sc[e] = -INFINITY;
-        }
-        float mx = sc[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // online softmax (base 2); key kt is live, so mnew is finite
-        const float mnew = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - mnew);
-        m_run = mnew;
-        float pr[8], ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pr[e] = fast_exp2(sc[e] - mnew);
-            ls += pr[e];
-        }
-        l_run = fmaf(l_run, alpha, ls);
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
-            acc_lr *= alpha;
-        }
-        // O^T += V^T P^T, O_lr^T += V_lr^T P^T
-        if constexpr (sizeof(T) == 2) {
-            Vec<bf16, 8> phi, plo;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
-                plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
+            return __builtin_amdgcn_readlane(page_vec, blk - pg_base);
+        };
+        // first cache row of the 32-key tile starting at key kt of the request (V_lr rows), and the
+        // byte offset of that row in the request's K / V head (a page's rows are adjacent; pages sit
+        // kv_page_stride elements apart)
+        auto tile_row = [&](int kt) -> int64_t {
+            if constexpr (PAGED) return (int64_t(page_of(kt)) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
+            else return kt;
+        };
+        auto tile_kv_off = [&](int kt) -> int64_t {
+            if constexpr (PAGED) {
+                return int64_t(page_of(kt)) * p.kv_page_stride * int64_t(sizeof(T)) +
+                       int64_t(kt & ((1 << p.page_shift) - 1)) * row_bytes;
+            } else {
+                return int64_t(kt) * row_bytes;
             }
+        };
+
+        // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
+        // offset per operand, so the loads use the scalar-base + vector-offset form.
+        const int64_t head_off = (start * p.kv_row_stride + g * p.kv_head_stride) * int64_t(sizeof(T));
+        const char* __restrict__ Kg = static_cast<const char*>(p.K) + head_off;
+        const char* __restrict__ Vg = static_cast<const char*>(p.V) + head_off;
+        // an adapter-free request streams agent 0's columns (same rows, valid memory) through the
+        // same instructions; the merge drops that product
+        const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(max(a, 0)) * R) * int64_t(sizeof(T));
+        const T* __restrict__ Qp = static_cast<const T*>(p.Q);
+        const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
+        const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
+        const uint32_t l_lane = uint32_t(4 * q * lr_bytes + (n % R) * sizeof(T));
+
+        // the group's queries as the B operand (columns >= G are zero)
+        const int bq = b - 1;   // this piece's request
+        Vec<T, 8> qf[KCH];
 #pragma unroll
-            for (int tt = 0; tt < VEC; ++tt) {
-                const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
-                acc[tt] = mma16x16x32(va, phi, acc[tt]);
-                acc[tt] = mma16x16x32(va, plo, acc[tt]);
+        for (int i = 0; i < KCH; ++i) {
+            if (n < G) qf[i].load(Qp + (int64_t(bq) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * q);
+            else qf[i].zero();
+        }
+
+        // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key
+        // score pass as fp32 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head
+        // n (a wave-uniform base per request and KV head plus one 32-bit lane offset)
+        const bool ks_live = KSC && a != kAdapterFree;
+        const char* __restrict__ ksg = KSC ? reinterpret_cast<const char*>(p.key_scores + (int64_t(bq) * p.n_q + int64_t(g) * G) * p.ks_stride) : nullptr;
+        const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 4);
+        auto load_ks = [&](Tile& t, int kt) {
+            if constexpr (KSC) {
+                if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
+                    t.ks[0] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * kt);
+                    t.ks[1] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * (kt + 16));
+                } else {
+                    t.ks[0] = t.ks[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
-            acc_lr = mma16x16x32(t.lr, phi, acc_lr);
-            acc_lr = mma16x16x32(t.lr, plo, acc_lr);
-        } else {
+        };
+        // Tile loads. A full tile addresses each operand as a wave-uniform base (scalar registers)
+        // plus one 32-bit lane offset. Only a piece's last tile can run past k1: its rows are
+        // clamped to k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads
+        // into the same registers, so the choice is a uniform branch around address arithmetic only.
+        auto load_k = [&](Tile& t, int kt) {
+            const char* kb = Kg + tile_kv_off(kt);
+            if (kt + kTile <= k1) {
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                    for (int i = 0; i < KCH; ++i)
+                        t.k[uu][i].load(reinterpret_cast<const T*>(kb + 16 * uu * row_bytes + k_lane) + 32 * i);
+            } else {
+                const int lim = k1 - 1 - kt;
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const uint32_t o = uint32_t(min(16 * uu + n, lim) * row_bytes + 8 * q * sizeof(T));
+#pragma unroll
+                    for (int i = 0; i < KCH; ++i) t.k[uu][i].load(reinterpret_cast<const T*>(kb + o) + 32 * i);
+                }
+            }
+        };
+        auto load_v = [&](Tile& t, int kt) {
+            const char* vb = Vg + tile_kv_off(kt);
+            const char* lb = Lg + tile_row(kt) * lr_bytes;
+            // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
+            // so no load sits behind a lane mask
+            uint32_t h[8];
+            if (kt + kTile <= k1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    t.v[e].load(reinterpret_cast<const T*>(vb + tile_key(0, e) * row_bytes + v_lane));
+                    if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + tile_key(0, e) * lr_bytes + l_lane);
+                    else t.lr.v[e] = *reinterpret_cast<const float*>(lb + tile_key(0, e) * lr_bytes + l_lane);
+                }
+            } else {
+                const int lim = k1 - 1 - kt;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int key = min(tile_key(q, e), lim);
+                    t.v[e].load(reinterpret_cast<const T*>(vb + uint32_t(key * row_bytes + VEC * n * sizeof(T))));
+                    const uint32_t lo = uint32_t(key * lr_bytes + (n % R) * sizeof(T));
+                    if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + lo);
+                    else t.lr.v[e] = *reinterpret_cast<const float*>(lb + lo);
+                }
+            }
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
+            }
+        };
+
+        f32x4 acc[VEC];
+        f32x4 acc_lr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run = -INFINITY, l_run = 0.f;
+
+        // One tile: scores, online softmax, P.V. With PREFETCH the K registers are refilled with the
+        // next tile as soon as the scores are done and the V registers as soon as P.V is done, so
+        // one tile's loads are always in flight behind the arithmetic.
+        auto tile_step = [&](Tile& t, int kt, auto prefetch) {
+            constexpr bool PREFETCH = decltype(prefetch)::value;
+            const int kn = kt + kTile;
+            // the key scores are loaded here, not a tile ahead: prefetched, they overflow the registers
+            load_ks(t, kt);
+            f32x4 sacc[2];
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                sacc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) sacc[uu] = mma16x16x32(t.k[uu][i], qf[i], sacc[uu]);
+            }
+            if constexpr (KSC) {
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    sacc[uu][0] += t.ks[uu].x;
+                    sacc[uu][1] += t.ks[uu].y;
+                    sacc[uu][2] += t.ks[uu].z;
+                    sacc[uu][3] += t.ks[uu].w;
+                }
+            }
+            if constexpr (PREFETCH) load_k(t, kn);
+            float sc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = sacc[e >> 2][e & 3] * sl2;
+            if (!PREFETCH && kt + kTile > k1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (kt + tile_key(q, e) >= k1) sc[e] = -INFINITY;
+            }
+            float mx = sc[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // online softmax (base 2); key kt is live, so mnew is finite
+            const float mnew = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - mnew);
+            m_run = mnew;
+            float pr[8], ls = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-#pragma unroll
-                for (int tt = 0; tt < VEC; ++tt)
-                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
-                acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
+                pr[e] = fast_exp2(sc[e] - mnew);
+                ls += pr[e];
             }
-        }
-        if constexpr (PREFETCH) load_v(t, kn);
-    };
+            l_run = fmaf(l_run, alpha, ls);
+            if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
+                acc_lr *= alpha;
+            }
+            // O^T += V^T P^T, O_lr^T += V_lr^T P^T
+            if constexpr (sizeof(T) == 2) {
+                Vec<bf16, 8> phi, plo;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
+                    plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
+                }
+#pragma unroll
+                for (int tt = 0; tt < VEC; ++tt) {
+                    const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
+                    acc[tt] = mma16x16x32(va, phi, acc[tt]);
+                    acc[tt] = mma16x16x32(va, plo, acc[tt]);
+                }
+                acc_lr = mma16x16x32(t.lr, phi, acc_lr);
+                acc_lr = mma16x16x32(t.lr, plo, acc_lr);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                    for (int tt = 0; tt < VEC; ++tt)
+                        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
+                    acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
+                }
+            }
+            if constexpr (PREFETCH) load_v(t, kn);
+        };
 
-    // the wave's tiles kt = k0 + 32*wv + 128*j, j < nt; only the last one can be partial
-    {
-        constexpr int step = kWaves * kTile;
-        const int kt0 = k0 + kTile * wv;
-        const int nt = kt0 < k1 ? (k1 - kt0 + step - 1) / step : 0;
-        if (nt > 0) {
+        // the piece's tiles kt = k0 + 32*j, j < nt (at least one); only the last one can be partial
+        {
+            const int nt = (k1 - k0 + kTile - 1) / kTile;
             Tile t;
-            load_k(t, kt0);
-            load_v(t, kt0);
-            int kt = kt0;
-            for (int j = 0; j + 1 < nt; ++j, kt += step) tile_step(t, kt, std::true_type{});
+            load_k(t, k0);
+            load_v(t, k0);
+            int kt = k0;
+            for (int j = 0; j + 1 < nt; ++j, kt += kTile) tile_step(t, kt, std::true_type{});
             tile_step(t, kt, std::false_type{});
         }
-    }
 
-    // ---- per-wave state to LDS: lane (n, q) holds O^T rows 4q+j (d = VEC*(4q+j) + t) of head n
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (n < G) {
+        // ---- this piece's partial of head n (lanes n < G): lane (n, q) holds O^T rows 4q+j of each
+        // tile tt, i.e. d = VEC*(4q+j) + tt, VEC consecutive d per j
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        if (n < G) {
+            // partial record k + b of (slice, request): unique over the launch
+            const int64_t r = (int64_t(k) + bq) * p.n_q + int64_t(g) * G + n;
+            float* orec = p.ws_o + r * (D + R);
 #pragma unroll
-        for (int tt = 0; tt < VEC; ++tt)
+            for (int j = 0; j < 4; ++j) {
+                float* dst = orec + VEC * (4 * q + j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) red_o[wv][n][VEC * (4 * q + j) + tt] = acc[tt][j];
+                for (int tt = 0; tt < VEC; tt += 4)
+                    *reinterpret_cast<float4*>(dst + tt) = make_float4(acc[tt][j], acc[tt + 1][j], acc[tt + 2][j], acc[tt + 3][j]);
+            }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * q + j < R) red_o[wv][n][D + 4 * q + j] = acc_lr[j];
-        if (q == 0) {
-            red_m[wv][n] = m_run;
-            red_l[wv][n] = l_run;
-        }
-    }
-    __syncthreads();
-
-    // ---- merge the 4 waves (weights 2^(m_w - M)) and write this split's partial per query head
-    const int64_t bh0 = int64_t(b) * p.n_q + int64_t(g) * G;
-    for (int idx = threadIdx.x; idx < G * (D + R); idx += kThreads) {
-        const int h = idx / (D + R);
-        const int col = idx - h * (D + R);
-        float M = red_m[0][h];
-#pragma unroll
-        for (int v = 1; v < kWaves; ++v) M = fmaxf(M, red_m[v][h]);
-        float accv = 0.f, L = 0.f;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const float mv = red_m[v][h];
-            const float wgt = (mv == -INFINITY) ? 0.f : fast_exp2(mv - M);
-            accv = fmaf(wgt, red_o[v][h][col], accv);
-            L = fmaf(wgt, red_l[v][h], L);
-        }
-        const int64_t rec = (bh0 + h) * p.n_split + s;
-        p.ws_o[rec * (D + R) + col] = accv;
-        if (col == 0) {
-            p.ws_ml[rec * 2 + 0] = bad_pages ? __builtin_nanf("") : M;
-            p.ws_ml[rec * 2 + 1] = L;
+            for (int j = 0; j < 4; ++j)
+                if (4 * q + j < R) orec[D + 4 * q + j] = acc_lr[j];
+            if (q == 0) {
+                p.ws_ml[r * 2 + 0] = bad_pages ? __builtin_nanf("") : m_run;
+                p.ws_ml[r * 2 + 1] = l_run;
+            }
         }
     }
 }
 
-// Merge of the splits of one (request b, query head h) by the log-sum-exp rule, then the
+// Merge of the partials of one (request b, query head h) by the log-sum-exp rule, then the
 // up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l (O / l for an adapter-free request),
-// rounded to the output type.
-// Wave w merges the splits s = w, w+4, ... in one pass with a running maximum (lane c holds columns
-// c, c+64, c+128 of O | O_lr), so the loads of all its splits are independent of each other; the
-// four wave states are merged in LDS. The B slice is fetched first and used last. Requests with
-// no key get zeros; requests with an invalid range or agent NaN.
-template <typename T, int D, int R>
+// rounded to the output type. The request's units [P_b, P_b + units) lie in slices
+// slice_owner(P_b) .. slice_owner(P_b + units - 1); slice k wrote its piece to record k + b (an
+// empty slice in between wrote none). Wave w merges the slices w, w+4, ... in one pass with a
+// running maximum (lane c holds columns c, c+64, c+128 of O | O_lr), so the loads of all its
+// partials are independent of each other; the four wave states are merged in LDS. The B slice is
+// fetched first and used last. Requests with no key get zeros; invalid requests NaN.
+template <typename T, int D, int R, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
     constexpr int W = D + R;
     constexpr int NC = (W + 63) / 64;
     __shared__ float part[kWaves][NC * 64];
     __shared__ float wm[kWaves], wl[kWaves];
     __shared__ float comb[NC * 64];
+    __shared__ int red_u[2][kWaves];
     const int b = blockIdx.x / p.n_q;
     const int h = blockIdx.x - b * p.n_q;
     const int g = h / p.G;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t start = p.kv_start ? p.kv_start[b] : 0;
+    const int64_t start = PAGED ? 0 : p.kv_start[b];
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
     const int64_t bh = int64_t(b) * p.n_q + h;
@@ -421,21 +476,44 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) bcol[rr] = to_f32<T>(Bp[int64_t(rr) * d_kv + threadIdx.x]);
     }
-    const int ns = (len + p.chunk - 1) / p.chunk;   // splits that hold a partial (each has a key)
-    const float* ml = p.ws_ml + bh * p.n_split * 2;
-    const float* po = p.ws_o + bh * p.n_split * W;
+    // units of the requests before b, and of the whole batch
+    int before = 0, total = 0;
+    for (int bb = threadIdx.x; bb < p.batch; bb += kThreads) {
+        const int ub = request_units<PAGED>(p, bb);
+        total += ub;
+        if (bb < b) before += ub;
+    }
+    before = wave_sum(before);
+    total = wave_sum(total);
+    if (lane == 0) {
+        red_u[0][wv] = before;
+        red_u[1][wv] = total;
+    }
+    __syncthreads();
+    int Pb = 0, U = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        Pb += red_u[0][v];
+        U += red_u[1][v];
+    }
+    const int Pn = Pb + (len + kTile - 1) / kTile;
+    const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
+    const int kf = slice_owner(U, Pb, n_act), kl = slice_owner(U, Pn - 1, n_act);
+
     float m = -INFINITY, l = 0.f;
     float acc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-#pragma unroll 4
-    for (int s = wv; s < ns; s += kWaves) {
-        const float ms = ml[2 * s], ls = ml[2 * s + 1];
+#pragma unroll 2
+    for (int kk = kf + wv; kk <= kl; kk += kWaves) {
+        if (max(slice_begin(U, kk, n_act), Pb) >= min(slice_begin(U, kk + 1, n_act), Pn)) continue;
+        const int64_t r = (int64_t(kk) + b) * p.n_q + h;
+        const float ms = p.ws_ml[2 * r], ls = p.ws_ml[2 * r + 1];
         float v[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) v[c] = (64 * c + lane < W) ? po[int64_t(s) * W + 64 * c + lane] : 0.f;
-        const float mn = fmaxf(m, ms);            // finite: every merged split holds a key
-        const float keep = fast_exp2(m - mn);     // 0 for the first split (m = -inf)
+        for (int c = 0; c < NC; ++c) v[c] = (64 * c + lane < W) ? p.ws_o[r * W + 64 * c + lane] : 0.f;
+        const float mn = fmaxf(m, ms);            // finite: every merged piece holds a key
+        const float keep = fast_exp2(m - mn);     // 0 for the first piece (m = -inf)
         const float wgt = fast_exp2(ms - mn);
         l = fmaf(l, keep, wgt * ls);
 #pragma unroll
@@ -449,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
         wl[wv] = l;
     }
     __syncthreads();
-    // the four wave states (a wave without splits has m = -inf and weight 0)
+    // the four wave states (a wave without pieces has m = -inf and weight 0)
     float M = wm[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
@@ -480,20 +558,23 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
 
 template <typename T, int D, int R, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-    const int64_t bs = int64_t(p.batch) * p.n_split;
-    const int64_t groups = (bs + 7) / 8;
-    const int64_t n_wg = groups * 8 * p.n_kv;
+    // slices x head groups of 8 (n_slices is a multiple of 8)
+    const int64_t n_wg = int64_t(p.n_slices) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves);
     if (n_wg > 0) {
+        const dim3 grid{unsigned(n_wg)}, block{unsigned(kSplitThreads)};
         if (p.key_scores) {
             if constexpr (sizeof(T) == 2)
-                hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, true>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+                hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, true>), grid, block, 0, stream, p);
         } else if (p.block_table) {
-            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, true, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, true, false>), grid, block, 0, stream, p);
         } else {
-            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, false>), dim3(unsigned(n_wg)), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((decode_split_kernel<T, D, R, GP, false, false>), grid, block, 0, stream, p);
         }
     }
-    hipLaunchKernelGGL((decode_combine_kernel<T, D, R>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, true>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, false>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

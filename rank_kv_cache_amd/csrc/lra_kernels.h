@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace lra {
 
 // agent index of the adapter-free view (double batching: attends the base cache alone, no LR term)
@@ -19,8 +21,8 @@ struct DecodeParams {
     const int64_t* kv_start;
     const int32_t* kv_len;
     const int32_t* agent;
-    float* ws_ml;   // [batch*n_q*n_split][2]: running max (base-2 units) and sum of each split
-    float* ws_o;    // [batch*n_q*n_split][d_head + rank]: unnormalised O | O_lr of each split
+    float* ws_ml;   // [(n_slices+batch)*n_q][2]: running max (base-2 units) and sum of each piece
+    float* ws_o;    // [(n_slices+batch)*n_q][d_head + rank]: unnormalised O | O_lr of each piece
     void* O;
     int64_t ld_vlr;
     int64_t kv_rows;
@@ -30,7 +32,11 @@ struct DecodeParams {
     int64_t kv_row_stride, kv_head_stride;
     int64_t kv_page_stride;     // paged cache: elements between consecutive pages of K and V
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
-    int n_split, chunk;
+    // slices of the batch's 32-key tiles (a multiple of 8); the piece of request b in slice k has
+    // partial record k + b. With slices_per_round > 0 the kernels use fewer slices when the batch
+    // holds few tiles (decode_active_slices); n_slices is then the grid's (and workspace's) maximum.
+    int n_slices;
+    int slices_per_round;
     float scale;
     bool bf16;
     // paged cache (null block_table: contiguous rows addressed by kv_start). Request b's logical row
@@ -50,17 +56,15 @@ struct PrecomputeParams {
     const void* A;
     void* Vlr;
     const int64_t* out_rows;
-    float* ws_part;      // [ksplit][T][NR] fp32 partial products (ksplit > 1)
     int64_t T;
     int64_t ldx;
     int64_t ld_vlr;
     int64_t vlr_rows;
     int d_model;
-    int NR;        // n_agents * rank
-    int kr;        // reduction length handled by one workgroup (multiple of 32)
-    int ksplit;    // workgroups along the reduction
-    int n_cg;      // column groups of up to 64 columns
-    int rows_per_wg;   // X rows per workgroup (16 or 32)
+    int NR;               // n_agents * rank
+    int n_rg;             // row ranges (one per workgroup and column group)
+    int n_cg;             // column groups
+    int cols_per_group;   // 16 or 32
     bool bf16;
 };
 
@@ -189,13 +193,26 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_precompute(const PrecomputeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
-// Host-side launch geometry shared by the workspace-size query and the launch itself.
+// Host-side launch geometry of the LR precompute.
 struct PrecomputePlan {
-    int kr, ksplit, n_rt, n_cg, rows_per_wg;
-    size_t part_bytes;
+    int n_rg, n_cg, cols_per_group;
+    int chunks_per_wave;  // 32-element reduction chunks per wave
+    int cb;               // chunks a wave holds in registers (the kernel's limit)
 };
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);
 
-int decode_default_chunk(int batch, int n_kv, int64_t max_kv_len);
+// slices of a decode launch: about keys_per_split keys each at full lengths, or (0) the library's
+// choice (at most two rounds of one 8-wave workgroup per CU); 0 when there is nothing to do, -1
+// when the sizes are too large. *per_round: slices of one round for the library's choice, else 0.
+int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* per_round = nullptr);
+// the slices in use for a batch of U tiles (the kernels' rule; see decode.hip)
+__host__ __device__ inline int decode_active_slices(int U, int n_slices, int per_round) {
+    if (per_round <= 0) return n_slices;
+    // two rounds when each workgroup still streams at least 48 tiles (1,536 keys) of its head, one
+    // round otherwise, and never under 4 tiles per slice
+    int64_t n = int64_t(U) >= int64_t(48) * 2 * per_round ? 2 * per_round : std::min<int64_t>(per_round, (int64_t(U) + 3) / 4);
+    n = (std::max<int64_t>(n, 1) + 7) / 8 * 8;
+    return int(std::min<int64_t>(n, n_slices));
+}
 
 }  // namespace lra

@@ -105,9 +105,10 @@ def test_decode_qkvo_workspace_size():
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 4 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128 + 16 * 130 * 4
-    # 8 partial records: (m, l) part padded to 256 bytes, 8 x (64 + 8) fp32 partials, 2 x 4 x 64 fp32
-    # scores, 2 x 4 x 512 fp16 weights, 2 tiles of 16 steps x 128 bytes of repacked tables, 2 flags
-    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 256 + 8 * 72 * 4 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
+    # 8 slices + 2 requests = 10 records per query head, 40 in all: (m, l) part padded to 512 bytes,
+    # 40 x (64 + 8) fp32 partials, 2 x 4 x 64 fp32 scores, 2 x 4 x 512 fp16 weights, 2 tiles of 16
+    # steps x 128 bytes of repacked tables, 2 flags
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 512 + 40 * 72 * 4 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 
@@ -116,22 +117,35 @@ def test_decode_empty_batch_is_a_no_op():
     assert decode(batch=0, Q=None, ws=None, ws_bytes=0) == OK
 
 
-def test_decode_workspace_size_follows_split():
+def test_decode_workspace_size_follows_slices():
+    """The batch's 32-key tiles are cut into n slices (a multiple of 8): about keys_per_split keys
+    each at full lengths, or by default up to two rounds of 15/16 of the chip's 8-wave workgroup
+    slots (2 x 240 slices at n_kv = 8) with at least 4 tiles each; the workspace holds the grid's
+    maximum. A slice
+    holds one piece of each request it touches, with its own record per query head: (n + batch) *
+    n_q records of (m, l) and (O, O_lr)."""
     b, n_q, d, r = 16, 32, 128, 8
-    chunk = lra.lra_attn_decode_default_split(b, 8, 66400)
-    assert chunk % 64 == 0 and chunk >= 64
     up = lambda v: -(-v // 256) * 256
 
-    def layout(n_split):
-        recs = b * n_q * n_split
+    def layout(n_slices, batch=b):
+        recs = (n_slices + batch) * n_q
         return up(recs * 2 * 4) + recs * (d + r) * 4   # m, l | O, O_lr
 
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(-(-66400 // chunk))
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(65)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(480)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 4, d, r, 66400, 0) == layout(960)   # 1920 waves / 4 heads
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 16, d, r, 66400, 0) == layout(240)   # two workgroups per slice
+    assert lra.lra_attn_decode_workspace_bytes(1, n_q, 8, d, r, 1900, 0) == layout(16, 1)   # ceil(60 tiles / 4) -> 16
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(1040)   # ceil(16 * 66400 / 1024) = 1038 -> 1040
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
+    # the default keys per slice at full lengths: 16 x 66,400 keys (33,200 tiles, at least 48 per
+    # slice at two rounds) over 480 slices; 4 x 66,400 (8,300 tiles) over one round of 240; one
+    # 1,900-key request over ceil(60 tiles / 4) -> 16 slices
+    assert lra.lra_attn_decode_default_split(16, 8, 66400) == 2240   # 2,213.3 rounded up to a multiple of 64
+    assert lra.lra_attn_decode_default_split(4, 8, 66400) == 1152    # 1,106.7 -> 1,152
     assert lra.lra_attn_decode_default_split(1, 8, 1900) == 128
-    assert chunk % 128 == 0 and 128 <= chunk <= 8192
+    assert lra.lra_attn_decode_default_split(1, 1, 1900) == 128
+    assert lra.lra_attn_decode_default_split(0, 8, 1900) == 0
 
 
 # ---------------------------------------------------------------------------------------- prefill
@@ -245,8 +259,6 @@ def precompute(**kw):
     (dict(T=-1), E_SHAPE), (dict(ldx=4095), E_SHAPE), (dict(ldx=4092), E_SHAPE), (dict(ld_vlr=20), E_SHAPE),
     (dict(vlr_rows=100), E_SHAPE), (dict(vlr_rows=-1, out_rows=P), E_SHAPE), (dict(n_agents=0), E_SHAPE),
     (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(Vlr=P + 4), E_SHAPE),
-    (dict(T=32, ws=None), E_WS), (dict(T=32, ws_bytes=100), E_WS), (dict(T=32, ws=WS + 16), E_WS),
-    (dict(T=256, ws_bytes=8 * 256 * 24 * 4 - 1), E_WS),
 ])
 def test_precompute_rejects_bad_arguments(kw, status):
     assert precompute(**kw) == status
@@ -256,17 +268,12 @@ def test_precompute_empty_is_a_no_op():
     assert precompute(T=0, X=None, ws=None, ws_bytes=0) == OK
 
 
-def test_precompute_workspace_sizes():
-    # the reduction is split until the grid holds 256 workgroups: 2048 rows = 128 tiles of 16 ->
-    # two splits, whose fp32 partials need 2 planes of 2048 x 24; 8192 rows = 256 tiles of 32 ->
-    # no split, no workspace; one new token per request (32 rows): two splits of 32 x 48
-    assert lra.lra_lr_precompute_workspace_bytes(2048, 4096, 3, 8) == 2 * 2048 * 24 * 4
-    assert lra.lra_lr_precompute_workspace_bytes(8192, 4096, 3, 8) == 0
-    assert lra.lra_lr_precompute_workspace_bytes(32, 4096, 3, 16) == 2 * 32 * 48 * 4
-    assert lra.lra_lr_precompute_workspace_bytes(1, 256, 3, 8) == 0
-    assert lra.lra_lr_precompute_workspace_bytes(0, 4096, 3, 8) == 0
-    # 256 rows = 16 tiles: split 16 ways (256 elements each, the minimum)
-    assert lra.lra_lr_precompute_workspace_bytes(256, 4096, 3, 8) == 16 * 256 * 24 * 4
+def test_precompute_needs_no_workspace():
+    # one launch: each workgroup sums its 16 waves' partials itself, so no partials leave it
+    for T, d_model, n_agents, r in ((2048, 4096, 3, 8), (8192, 4096, 3, 8), (32, 4096, 3, 16), (1, 256, 3, 8),
+                                    (0, 4096, 3, 8), (18432, 8192, 3, 8)):
+        assert lra.lra_lr_precompute_workspace_bytes(T, d_model, n_agents, r) == 0
+    assert precompute(T=32, ws=None, ws_bytes=0, X=P, A=P, Vlr=None) == E_NULL   # validation still runs
 
 
 # ---------------------------------------------------------------------------------------- paged decode
@@ -284,7 +291,7 @@ def decode_paged(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(P=48), E_UNSUP), (dict(P=16), E_UNSUP), (dict(P=1 << 17), E_UNSUP), (dict(n_pages=0), E_SHAPE),
     (dict(max_blocks=0), E_SHAPE), (dict(max_kv_len=641), E_SHAPE), (dict(max_kv_len=-1), E_SHAPE),
-    (dict(P=32, max_kv_len=320, split=64 * 32), E_UNSUP), (dict(split=100), E_SHAPE), (dict(batch=-1), E_SHAPE),
+    (dict(split=100), E_SHAPE), (dict(batch=-1), E_SHAPE),
     (dict(n_agents=0), E_SHAPE), (dict(ld_vlr=8), E_SHAPE), (dict(scale=0.0), E_SHAPE), (dict(d=32), E_UNSUP),
     (dict(table=None), E_NULL), (dict(kv_len=None), E_NULL), (dict(agent=None), E_NULL), (dict(Vlr=None), E_NULL),
     (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS), (dict(O=P + 4), E_SHAPE),
@@ -297,12 +304,10 @@ def test_decode_paged_empty_batch_is_a_no_op():
     assert decode_paged(batch=0, Q=None, O=None, ws=None) == OK
 
 
-def test_decode_paged_default_split_spans_at_most_64_pages():
+def test_decode_paged_default_split_is_the_contiguous_one():
     for P in (32, 64, 128, 1024):
         for batch, L in ((1, 1900), (16, 66400), (64, 131072), (1, 10 ** 6)):
-            split = lra.lra_attn_decode_paged_default_split(batch, 8, L, P)
-            assert split % 128 == 0 and 128 <= split <= lra.lra_attn_decode_default_split(batch, 8, L)
-            assert (split + P - 1) // P + 1 <= 64
+            assert lra.lra_attn_decode_paged_default_split(batch, 8, L, P) == lra.lra_attn_decode_default_split(batch, 8, L)
     assert lra.lra_attn_decode_paged_default_split(16, 8, 66400, 48) == 0
 
 
@@ -406,7 +411,7 @@ def decode_paged_strided(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(ps=0), E_SHAPE), (dict(rs=-8), E_SHAPE), (dict(hs=12), E_SHAPE), (dict(ps=65540), E_SHAPE),
     (dict(rs=(1 << 24) + 8), E_SHAPE), (dict(P=48), E_UNSUP), (dict(d=96), E_UNSUP), (dict(n_pages=0), E_SHAPE),
-    (dict(max_kv_len=641), E_SHAPE), (dict(split=4096, P=32, max_kv_len=300), E_UNSUP), (dict(table=None), E_NULL),
+    (dict(max_kv_len=641), E_SHAPE), (dict(table=None), E_NULL),
     (dict(K=P + 8), E_SHAPE), (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS),
 ])
 def test_decode_paged_strided_rejects_bad_arguments(kw, status):

@@ -479,7 +479,8 @@ def test_decode_paged_head_major_pages_are_bit_identical(page_size):
 
 def test_decode_paged_bench_configuration_bit_identical():
     """The 16 x 66,400 batch as the bench times its paged lines: 32-row pages in a seeded random
-    order, token-major and head-major pages, against the contiguous call with the same split."""
+    order, token-major and head-major pages, against the contiguous call; all three take the
+    library's default slices, which do not depend on the cache layout."""
     say("decode paged bench configuration: generating inputs")
     c = W.llama_long_decode()
     s = c.shape
@@ -487,8 +488,9 @@ def test_decode_paged_bench_configuration_bit_identical():
     kl = dev_idx(c.kv_len, torch.int32)
     ag = dev_idx(c.agent, torch.int32)
     P = 32
-    split = lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P)
-    ref = lra.lra_attn_decode(Q, K, V, L, dev_idx(c.kv_start, torch.int64), kl, c.max_kv_len, B, ag, s.scale, split)
+    assert lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P) == \
+        lra.lra_attn_decode_default_split(c.batch, s.n_kv, c.max_kv_len)
+    ref = lra.lra_attn_decode(Q, K, V, L, dev_idx(c.kv_start, torch.int64), kl, c.max_kv_len, B, ag, s.scale, 0)
     torch.cuda.synchronize()
     ref = host64(ref)
     n_pages = K.shape[0] // P

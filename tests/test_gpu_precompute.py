@@ -51,8 +51,13 @@ def test_ministral_precompute_scatter_into_cache():
     ("bf16", 1, 4096, 3, 8), ("bf16", 37, 4096, 3, 16), ("bf16", 100, 256, 3, 8), ("bf16", 513, 1024, 2, 16),
     ("bf16", 64, 512, 9, 8), ("bf16", 20, 2048, 5, 16), ("f32", 1, 256, 3, 8), ("f32", 300, 256, 3, 8),
     ("f32", 17, 1024, 9, 16),
-    # 8192 rows and more run 32-row tiles
-    ("bf16", 8200, 512, 3, 8), ("bf16", 9000, 256, 2, 16),
+    # long X: 256 row ranges of 16-17 (35-36) rows, so tiles end inside a range
+    ("bf16", 4100, 512, 3, 8), ("bf16", 9000, 256, 2, 16),
+    # 16 output columns (one group); d_model past what a wave keeps in registers (At reloaded per
+    # batch of chunks: beyond 4096 for bf16, 2048 for fp32)
+    ("bf16", 33, 4096, 2, 8), ("bf16", 70, 8192, 3, 8), ("f32", 40, 4096, 3, 8), ("bf16", 300, 12288, 3, 16),
+    # 4096 rows and more take 32-column groups: with At reloaded per batch, and in fp32
+    ("bf16", 4200, 8192, 3, 8), ("f32", 4500, 256, 3, 8),
 ])
 def test_precompute_shapes(dtype, T, d_model, N, r):
     s = W.Shape(n_q=4, n_kv=2, d_head=64, rank=r, n_agents=N, d_model=d_model, dtype=dtype)
@@ -62,11 +67,11 @@ def test_precompute_shapes(dtype, T, d_model, N, r):
     check(got, oracle.lr_precompute(case.X.as_f64(), case.A.as_f64()), dtype)
 
 
-def test_precompute_workspace_reuse_and_bad_rows():
-    """One workspace (split reduction partials) for several calls of different sizes in a row;
-    out_rows entries outside the cache are skipped."""
+def test_precompute_calls_in_a_row_and_bad_rows():
+    """Calls of different sizes in a row (a workspace argument is accepted and unused); out_rows
+    entries outside the cache are skipped."""
     s = W.MINISTRAL_SHAPE
-    ws = torch.zeros(lra.lra_lr_precompute_workspace_bytes(64, 4096, 3, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
     for T in (64, 32, 7, 64):
         case = W.random_precompute((201, T), s, T)
         rows = np.arange(T, dtype=np.int64) * 2
@@ -84,3 +89,12 @@ def test_precompute_is_deterministic():
     a = run_pre(case, np.zeros((300, 24)))
     b = run_pre(case, np.zeros((300, 24)))
     assert np.array_equal(a, b)
+
+
+def test_llama_precompute_whole_context_every_row():
+    """The Llama prefill's whole context through the precompute in one call (18,432 x 4,096 -> 24
+    columns, 151 MB of X), every output against the oracle."""
+    case = W.llama_precompute(T=18432)
+    say("precompute 18432 x 4096 -> 24")
+    got = run_pre(case, np.zeros((18432, 24)))
+    check(got, oracle.lr_precompute(case.X.as_f64(), case.A.as_f64()), "bf16")

@@ -191,7 +191,7 @@ def bench_long_decode(args, torch, lra, W, out):
         "ms_per_step": ms, "gbs": gbs, "bytes": nbytes,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "lra_attn_decode = decode_split_kernel<bf16,128,8,4,false,false> + decode_combine_kernel<bf16,128,8,false>",
+                     "kernel": "lra_attn_decode = decode_split_kernel<bf16,128,8,4,false,false> + decode_combine_kernel<bf16,128,8,4,false>",
                      "bytes_per_launch": nbytes,
                      "traffic_source": src},
         "config": {"workload": W.WORKLOAD_NAMES[W.LLAMA_LONG_DECODE], "batch": c.batch, "kv_len": int(c.kv_len[0]),
@@ -233,7 +233,7 @@ def bench_long_decode(args, torch, lra, W, out):
     Vp = V.view(n_pages, P, s.n_kv, s.d_head)
     Lp = L.view(n_pages, P, L.shape[1])
     split_p = lra.lra_attn_decode_paged_default_split(c.batch, s.n_kv, c.max_kv_len, P)
-    ws_p = torch.empty(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len,
+    ws_p = torch.zeros(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len,
                                                            0), dtype=torch.uint8, device="cuda")
 
     def step_paged():
@@ -267,7 +267,7 @@ def bench_long_decode(args, torch, lra, W, out):
     Klr_h, Bk_h, cos_h, sin_h = W.llama_long_decode_key_lora()
     Klr, Bk = upload(Klr_h, torch), upload(Bk_h, torch)
     rc, rs = torch.from_numpy(cos_h).cuda(), torch.from_numpy(sin_h).cuda()
-    ws_k = torch.empty(lra.lra_attn_decode_qkvo_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank,
+    ws_k = torch.zeros(lra.lra_attn_decode_qkvo_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank,
                                                                 c.max_kv_len, 0), dtype=torch.uint8, device="cuda")
 
     def step_qkvo():

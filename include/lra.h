@@ -54,11 +54,13 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 6   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
+#define LRA_ABI_VERSION 7   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
                                 4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided;
                                 6: finite inputs beyond the fp16 range accepted everywhere (range-safe
                                    recomputation); the qkvo decode workspace holds fp32 key scores;
-                                   lra_attn_decode_noalloc */
+                                   lra_attn_decode_noalloc;
+                                7: stream-K decode slices and a new record layout (workspace sizes
+                                   changed); the LR precompute needs no workspace */
 
 typedef enum {
     LRA_OK = 0,
@@ -239,8 +241,9 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
  * (3)-(4) with L_C = 1). The batch's keys, counted in 32-key tiles request after request, are cut
  * into equal contiguous slices; each (slice, KV head) writes one fp32 partial (m, l, O, O_lr) per
- * request piece it covers to the workspace, and a second kernel merges a request's partials with
- * the log-sum-exp rule, applies B_agent once and normalises. Request b attends all rows
+ * request piece it covers to the workspace, and a second kernel merges the partials of each
+ * (request, KV head) with the log-sum-exp rule, applies B_agent once and normalises. Request b
+ * attends all rows
  * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
  * kv_len[b] = 0 gives a zero output row.
  *
@@ -259,7 +262,9 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
  *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output
- * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues nothing.
+ * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues
+ * nothing. The workspace size is 0 when no request can have a key (max_kv_len = 0); the call then
+ * only writes the zero and NaN rows.
  */
 size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d_head,
                                        int32_t rank, int64_t max_kv_len, int32_t keys_per_split);

@@ -185,7 +185,7 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
                       stream=None) -> torch.Tensor:
     """V_lr[out_rows[t], :n_agents*rank] = X[t] @ A.T, with A = [A_1^T; ...; A_N^T] ([N*r, d_model]).
 
-    ``workspace`` (uint8, any contents) is allocated when omitted and the reduction is split."""
+    ``workspace`` is accepted for compatibility; the kernel needs none (0 bytes)."""
     _same(X, A, V_lr)
     _rows_dense("X", X)
     _dense("A", A)

@@ -40,19 +40,20 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // -------------------------------------------------------------------------- decode workspace
 struct DecodeLayout {
     int n_slices, per_round;
-    size_t ml_off, o_off, total;
+    size_t rec_off, rec_bytes, total;
 };
 
-// [m, l: recs x 2 fp32][O | O_lr: recs x (d + r) fp32], recs = (n_slices + batch) * n_q (a slice
-// holds at most one piece of each request it touches, and its pieces' records k + b are distinct),
-// 256-aligned parts. n_slices < 0: the sizes are too large for one launch.
+// records: (n_slices + batch) * n_kv blocks of decode_record_slots() 16-byte slots (a slice holds
+// at most one piece of each request it touches, and its pieces' blocks (k + b) * n_kv + g are
+// distinct). n_slices < 0: the sizes are too large for one launch.
 DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, int64_t max_kv_len, int keys_per_split) {
     DecodeLayout L{};
     L.n_slices = lra::decode_slices(batch, n_kv, max_kv_len, keys_per_split, &L.per_round);
-    const size_t recs = L.n_slices > 0 ? size_t(L.n_slices + batch) * size_t(n_q) : 0;
-    L.ml_off = 0;
-    L.o_off = align_up(recs * 2 * sizeof(float), 256);
-    L.total = recs ? L.o_off + recs * size_t(d_head + rank) * sizeof(float) : 0;
+    const size_t blocks = L.n_slices > 0 ? size_t(L.n_slices + batch) * size_t(n_kv) : 0;
+    L.rec_off = 0;
+    L.rec_bytes = n_kv > 0 && n_q % n_kv == 0 ? blocks * size_t(lra::decode_record_slots(n_q / n_kv, d_head, rank)) * 16 : 0;
+    if (L.rec_bytes >= (size_t(1) << 31)) L.n_slices = -1;   // 32-bit record offsets
+    L.total = L.rec_bytes ? L.rec_off + L.rec_bytes : 0;
     return L;
 }
 
@@ -389,8 +390,8 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
     lra::DecodeParams p{};
     p.Q = Q; p.K = K_pages; p.V = V_pages; p.Vlr = Vlr_pages; p.B = B;
     p.kv_start = nullptr; p.kv_len = kv_len; p.agent = agent;
-    p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
-    p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
+    p.records = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.rec_off) : nullptr;
+    p.record_bytes = uint32_t(L.rec_bytes);
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
     p.kv_row_stride = row_stride; p.kv_head_stride = head_stride; p.kv_page_stride = page_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
@@ -514,8 +515,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     lra::DecodeParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B;
     p.kv_start = kv_start; p.kv_len = kv_len; p.agent = agent;
-    p.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off) : nullptr;
-    p.ws_o = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.o_off) : nullptr;
+    p.records = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.rec_off) : nullptr;
+    p.record_bytes = uint32_t(L.rec_bytes);
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
     p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride; p.kv_page_stride = 0;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
@@ -656,14 +657,14 @@ int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, i
     if (keys_per_split > 0) {
         n = (int64_t(batch) * max_kv_len + keys_per_split - 1) / keys_per_split;
     } else {
-        // One 8-wave workgroup (one wave per KV head, 256 registers per lane) per CU on the 256 CUs
-        // of MI355X: a full round is 2048 waves. Measured on MI355X, a slice count just past a
+        // One 8-wave workgroup (one wave per KV head) per CU on the 256 CUs of MI355X is a round
+        // of 2048 waves. Measured on MI355X, a slice count just past a
         // whole number of rounds costs a whole extra round, and 15/16 of a round does better than
         // a full one (16 x 66,400 keys: 0.74 ms at 480-504 slices, 0.755 at 512; 32 requests of
         // 1.9k-29k keys: 8.22-8.24 ms per 36 calls at 224-240 slices, 8.33 at 256). So the kernels
         // use one such round, or two when the batch holds enough tiles (decode_active_slices).
         round = std::max<int64_t>(8, 2048 * 15 / 16 / (n_hg * std::min(n_kv, 8)) / 8 * 8);
-        n = std::min(2 * round, (units_max + 3) / 4);
+        n = std::min(2 * round, units_max);   // down to one tile per slice for small batches
     }
     n = (std::max<int64_t>(n, 1) + 7) / 8 * 8;
     // the grid (n x n_hg workgroups) and the 32-bit unit counts of the kernels stay in range

@@ -38,6 +38,7 @@
 //     agent NaN. The kernel boundary orders the partial writes before the merge: a device-scope
 //     fence per workgroup (to let the last piece merge in place) writes back and invalidates an
 //     XCD's L2, which cost more than the whole merge at thousands of workgroups.
+#include <algorithm>
 #include <type_traits>
 
 #include "lra_device.h"
@@ -47,8 +48,8 @@ namespace lra {
 
 namespace {
 
-constexpr int kWaves = 4;                      // merge kernel
-constexpr int kThreads = 64 * kWaves;
+constexpr int kCombineWaves = 8;
+constexpr int kCombineThreads = 64 * kCombineWaves;
 constexpr int kSplitWaves = 8;                 // split kernel: one wave per KV head of a group of 8
 constexpr int kSplitThreads = 64 * kSplitWaves;
 constexpr int kTile = 32;   // keys per wave tile
@@ -95,6 +96,42 @@ __device__ __forceinline__ int request_units(const DecodeParams& p, int b) {
 __device__ __forceinline__ int slice_begin(int U, int k, int n_slices) { return int(int64_t(U) * k / n_slices); }
 __device__ __forceinline__ int slice_owner(int U, int u, int n_slices) { return int((int64_t(u + 1) * n_slices - 1) / U); }
 
+// Partial records. A piece of request b in slice k writes, per KV head g, one block of 16-byte
+// slots at block (k + b) * n_kv + g (GP = the group size rounded up to 4 or 8; n < G, q < 4):
+//   O:   slot c * 4GP + 4n + q, c < VEC  <- O^T of head n, d = VEC*(4q + c/(VEC/4)) + 4*(c%(VEC/4)) + 0..3
+//   O_lr: slot VEC*4GP + n*(R/4) + q, q < R/4  <- O_lr of head n, ranks 4q .. 4q+3
+//   m, l: slot VEC*4GP + GP*R/4 + n  <- (m, l, 0, 0) of head n
+// padded to a multiple of 16 slots, so a wave's store instructions write contiguous runs of
+// 16 * 4G bytes (measured on MI355X: faster than the strided stores of one record per head). The records are
+// written and read with the device-coherent cache policy (sc1, the one the compiler uses for
+// agent-scope atomic stores and loads): the stores write through this XCD's L2, and the merging
+// wave's loads do not take a stale copy from its own. Measured on MI355X, these stores cost less
+// than plain write-back ones, and no whole-L2 write-back or invalidate is needed.
+template <int D, int R, int GP> struct RecordFormat {
+    static constexpr int VEC = D / 16;
+    static constexpr int O_SLOTS = VEC * 4 * GP;
+    static constexpr int LR_SLOT = O_SLOTS;
+    static constexpr int ML_SLOT = O_SLOTS + GP * R / 4;
+    static constexpr int SLOTS = (ML_SLOT + GP + 15) / 16 * 16;   // blocks of whole 256-byte runs
+    static constexpr int REGS = (SLOTS + 63) / 64;      // slots per lane in the merge
+    static constexpr int LR_REG = O_SLOTS / 64;          // the register holding the O_lr and (m, l) slots
+    static_assert(O_SLOTS % 64 == 0 || O_SLOTS < 64, "O slots fill whole registers");
+};
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;   // sc1: device-coherent cache policy of a buffer access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ void record_store(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<u32x4_t*>(&v), rs, off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 record_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent);
+    return *reinterpret_cast<const f32x4*>(&v);
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -139,8 +176,8 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
     U = __builtin_amdgcn_readfirstlane(U);
     const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
     if (k >= n_act) return;
+    // n_act <= U: every slice in use holds at least one unit
     const int s0 = slice_begin(U, k, n_act), s1 = slice_begin(U, k + 1, n_act);
-    if (s0 >= s1) return;   // an empty slice (fewer units than slices)
     int b = 0;
     int Pb = 0;   // units before request b
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
@@ -409,79 +446,85 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
             tile_step(t, kt, std::false_type{});
         }
 
-        // ---- this piece's partial of head n (lanes n < G): lane (n, q) holds O^T rows 4q+j of each
-        // tile tt, i.e. d = VEC*(4q+j) + tt, VEC consecutive d per j
+        // ---- this piece's record block (lanes n < G; see RecordFormat): lane (n, q) holds O^T rows
+        // 4q+j of each tile tt, i.e. d = VEC*(4q+j) + tt, and O_lr rows 4q .. 4q+3
+        using F = RecordFormat<D, R, GP>;
+        const __amdgpu_buffer_rsrc_t rs = record_rsrc(p.records, p.record_bytes);
+        const uint32_t blk = uint32_t((int64_t(k) + bq) * p.n_kv + g) * (F::SLOTS * 16);
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
         if (n < G) {
-            // partial record k + b of (slice, request): unique over the launch
-            const int64_t r = (int64_t(k) + bq) * p.n_q + int64_t(g) * G + n;
-            float* orec = p.ws_o + r * (D + R);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float* dst = orec + VEC * (4 * q + j);
-#pragma unroll
-                for (int tt = 0; tt < VEC; tt += 4)
-                    *reinterpret_cast<float4*>(dst + tt) = make_float4(acc[tt][j], acc[tt + 1][j], acc[tt + 2][j], acc[tt + 3][j]);
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (4 * q + j < R) orec[D + 4 * q + j] = acc_lr[j];
-            if (q == 0) {
-                p.ws_ml[r * 2 + 0] = bad_pages ? __builtin_nanf("") : m_run;
-                p.ws_ml[r * 2 + 1] = l_run;
-            }
+#pragma unroll
+                for (int tt = 0; tt < VEC; tt += 4) {
+                    const int c = j * (VEC / 4) + tt / 4;
+                    record_store(rs, blk + (c * 4 * GP + 4 * n + q) * 16, f32x4{acc[tt][j], acc[tt + 1][j], acc[tt + 2][j], acc[tt + 3][j]});
+                }
+            if (4 * q < R) record_store(rs, blk + (F::LR_SLOT + n * (R / 4) + q) * 16, acc_lr);
+            if (q == 0) record_store(rs, blk + (F::ML_SLOT + n) * 16, f32x4{bad_pages ? __builtin_nanf("") : m_run, l_run, 0.f, 0.f});
         }
+
     }
 }
 
-// Merge of the partials of one (request b, query head h) by the log-sum-exp rule, then the
-// up-projection O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l (O / l for an adapter-free request),
-// rounded to the output type. The request's units [P_b, P_b + units) lie in slices
-// slice_owner(P_b) .. slice_owner(P_b + units - 1); slice k wrote its piece to record k + b (an
-// empty slice in between wrote none). Wave w merges the slices w, w+4, ... in one pass with a
-// running maximum (lane c holds columns c, c+64, c+128 of O | O_lr), so the loads of all its
-// partials are independent of each other; the four wave states are merged in LDS. The B slice is
-// fetched first and used last. Requests with no key get zeros; invalid requests NaN.
-template <typename T, int D, int R, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p) {
-    constexpr int W = D + R;
-    constexpr int NC = (W + 63) / 64;
-    __shared__ float part[kWaves][NC * 64];
-    __shared__ float wm[kWaves], wl[kWaves];
-    __shared__ float comb[NC * 64];
-    __shared__ int red_u[2][kWaves];
-    const int b = blockIdx.x / p.n_q;
-    const int h = blockIdx.x - b * p.n_q;
-    const int g = h / p.G;
+// Merge of the pieces of one (request b, KV head g), one 8-wave workgroup each: the request's units
+// [P_b, P_b + units) lie in slices kf = slice_owner(P_b) .. slice_owner(P_b + units - 1), which
+// wrote record blocks (kk + b) * n_kv + g. Wave w takes the pieces w, w+8, ...; lane L takes slots
+// L + 64t of each block (RecordFormat: its O slots all belong to head n = (L % 4GP) / 4, and lanes
+// L < GP*R/4 hold the O_lr slots of head L / (R/4) in register LR_REG). Every slot keeps its own
+// running maximum and sum (the log-sum-exp rule with weights 2^(m_s - max m)); the slots of one head
+// see the same (m, l) sequence, so they agree. A wave issues the loads of up to 8 pieces at once;
+// the eight wave states are merged in LDS. Wave 0 then applies the up-projection
+// O = (O + O_lr B_agent[:, g*d .. g*d+d-1]) / l (O / l for an adapter-free request), rounded to the
+// output type; NaN when a piece had a bad page id. Requests without a key get zeros, invalid
+// requests NaN.
+template <typename T, int D, int R, int GP, bool PAGED>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeParams p) {
+    using F = RecordFormat<D, R, GP>;
+    constexpr int VEC = F::VEC;
+    constexpr int NO = F::LR_REG;   // registers of O slots
+    constexpr int PB = 8;           // pieces per batch of loads of a wave
+    __shared__ f32x4 st_acc[kCombineWaves][NO + 1][64];
+    __shared__ float st_m[kCombineWaves][2][64], st_l[kCombineWaves][64];
+    __shared__ int st_bad[kCombineWaves];
+    __shared__ int red_u[2][kCombineWaves];
+    const int b = blockIdx.x / p.n_kv;
+    const int g = blockIdx.x - b * p.n_kv;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // the request's range and agent, and the units of the requests before b and of the whole batch,
+    // read in one round
     const int64_t start = PAGED ? 0 : p.kv_start[b];
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
-    const int64_t bh = int64_t(b) * p.n_q + h;
-    T* __restrict__ Op = static_cast<T*>(p.O) + bh * D;
-    const bool ok = decode_request_ok(start, len, a, p);
-    if (!ok || len == 0) {
-        const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
-        for (int c = threadIdx.x; c < D; c += kThreads) Op[c] = fill;
-        return;
-    }
-    // column c of the agent's B slice for this KV head (threads c < D); the adapter-free view has
-    // no LR term
-    const bool adapted = a != kAdapterFree;
-    const int64_t d_kv = int64_t(p.n_kv) * D;
-    const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(max(a, 0)) * R * d_kv + int64_t(g) * D;
-    float bcol[R];
-    if (threadIdx.x < D && adapted) {
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) bcol[rr] = to_f32<T>(Bp[int64_t(rr) * d_kv + threadIdx.x]);
-    }
-    // units of the requests before b, and of the whole batch
     int before = 0, total = 0;
-    for (int bb = threadIdx.x; bb < p.batch; bb += kThreads) {
+    for (int bb = threadIdx.x; bb < p.batch; bb += kCombineThreads) {
         const int ub = request_units<PAGED>(p, bb);
         total += ub;
         if (bb < b) before += ub;
+    }
+    const bool ok = decode_request_ok(start, len, a, p);
+    if (!ok || len == 0) {
+        const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
+        T* Op = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * p.G) * D;
+        for (int i = threadIdx.x; i < p.G * D; i += kCombineThreads) Op[i] = fill;
+        return;
+    }
+    // wave 0 fetches its B values now, while the partials are read: B[rr][g*d + d0 .. d0+3] of
+    // each of its O slots (see below)
+    const int64_t d_kv = int64_t(p.n_kv) * D;
+    const bool adapted = a != kAdapterFree;
+    const int q = lane & 3;
+    Vec<T, 4> bv[NO][R];
+    if (wv == 0 && adapted) {
+        const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
+#pragma unroll
+        for (int t = 0; t < NO; ++t) {
+            const int c = (64 * t + lane) / (4 * GP);
+            const int d0 = VEC * (4 * q + c / (VEC / 4)) + 4 * (c % (VEC / 4));
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) bv[t][rr].load(Bp + int64_t(rr) * d_kv + d0);
+        }
     }
     before = wave_sum(before);
     total = wave_sum(total);
@@ -492,67 +535,101 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeParams p
     __syncthreads();
     int Pb = 0, U = 0;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < kCombineWaves; ++v) {
         Pb += red_u[0][v];
         U += red_u[1][v];
     }
-    const int Pn = Pb + (len + kTile - 1) / kTile;
     const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
-    const int kf = slice_owner(U, Pb, n_act), kl = slice_owner(U, Pn - 1, n_act);
+    const int kf = slice_owner(U, Pb, n_act);
+    const int n_pieces = slice_owner(U, Pb + (len + kTile - 1) / kTile - 1, n_act) - kf + 1;
 
-    float m = -INFINITY, l = 0.f;
-    float acc[NC];
+    const __amdgpu_buffer_rsrc_t rs = record_rsrc(p.records, p.record_bytes);
+    const int n_o = (lane % (4 * GP)) / 4;
+    const int n_lr = min(lane / (R / 4), GP - 1);
+    const uint32_t block = F::SLOTS * 16;
+    float M = -INFINITY, L = 0.f, M2 = -INFINITY;
+    bool bad = false;
+    f32x4 acc[NO + 1];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-#pragma unroll 2
-    for (int kk = kf + wv; kk <= kl; kk += kWaves) {
-        if (max(slice_begin(U, kk, n_act), Pb) >= min(slice_begin(U, kk + 1, n_act), Pn)) continue;
-        const int64_t r = (int64_t(kk) + b) * p.n_q + h;
-        const float ms = p.ws_ml[2 * r], ls = p.ws_ml[2 * r + 1];
-        float v[NC];
+    for (int t = 0; t <= NO; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = wv; i0 < n_pieces; i0 += PB * kCombineWaves) {
+        f32x4 v[PB][NO + 1], ml[PB], ml2[PB];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) v[c] = (64 * c + lane < W) ? p.ws_o[r * W + 64 * c + lane] : 0.f;
-        const float mn = fmaxf(m, ms);            // finite: every merged piece holds a key
-        const float keep = fast_exp2(m - mn);     // 0 for the first piece (m = -inf)
-        const float wgt = fast_exp2(ms - mn);
-        l = fmaf(l, keep, wgt * ls);
+        for (int u = 0; u < PB; ++u) {
+            const int i = min(i0 + u * kCombineWaves, n_pieces - 1);
+            const uint32_t base = uint32_t((int64_t(kf) + i + b) * p.n_kv + g) * block;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] = fmaf(acc[c], keep, wgt * v[c]);
-        m = mn;
+            for (int t = 0; t <= NO; ++t) v[u][t] = record_load(rs, base + (64 * t + lane) * 16);
+            ml[u] = record_load(rs, base + (F::ML_SLOT + n_o) * 16);
+            ml2[u] = record_load(rs, base + (F::ML_SLOT + n_lr) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            if (i0 + u * kCombineWaves >= n_pieces) break;
+            bad = bad || ml[u][0] != ml[u][0];
+            const float mn = fmaxf(M, ml[u][0]), mn2 = fmaxf(M2, ml2[u][0]);
+            const float keep = fast_exp2(M - mn), w = fast_exp2(ml[u][0] - mn);
+            const float keep2 = fast_exp2(M2 - mn2), w2 = fast_exp2(ml2[u][0] - mn2);
+            L = fmaf(L, keep, w * ml[u][1]);
+#pragma unroll
+            for (int t = 0; t < NO; ++t) acc[t] = acc[t] * keep + v[u][t] * w;
+            acc[NO] = acc[NO] * keep2 + v[u][NO] * w2;
+            M = mn;
+            M2 = mn2;
+        }
     }
+    // the eight wave states (a wave without pieces has M = -inf and weight 0)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) part[wv][64 * c + lane] = acc[c];
-    if (lane == 0) {
-        wm[wv] = m;
-        wl[wv] = l;
-    }
+    for (int t = 0; t <= NO; ++t) st_acc[wv][t][lane] = acc[t];
+    st_m[wv][0][lane] = M;
+    st_m[wv][1][lane] = M2;
+    st_l[wv][lane] = L;
+    const uint64_t any_bad = __ballot(bad);
+    if (lane == 0) st_bad[wv] = any_bad != 0;
     __syncthreads();
-    // the four wave states (a wave without pieces has m = -inf and weight 0)
-    float M = wm[0];
+    if (wv != 0) return;
+    float Ms = -INFINITY, Ms2 = -INFINITY;
+    bad = false;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w]);
-    float e[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) e[w] = fast_exp2(wm[w] - M);
-    if (threadIdx.x < W) {
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) o = fmaf(e[w], part[w][threadIdx.x], o);
-        comb[threadIdx.x] = o;
+    for (int w = 0; w < kCombineWaves; ++w) {
+        Ms = fmaxf(Ms, st_m[w][0][lane]);
+        Ms2 = fmaxf(Ms2, st_m[w][1][lane]);
+        bad = bad || st_bad[w];
     }
-    float L = 0.f;
+    L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) L = fmaf(e[w], wl[w], L);
-    __syncthreads();
-    // up-projection once per query row, normalise, store
-    if (threadIdx.x < D) {
-        const int c = threadIdx.x;
-        float o = comb[c];
+    for (int t = 0; t <= NO; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; ++w) {
+        const float e = fast_exp2(st_m[w][0][lane] - Ms), e2 = fast_exp2(st_m[w][1][lane] - Ms2);
+        L = fmaf(e, st_l[w][lane], L);
+#pragma unroll
+        for (int t = 0; t < NO; ++t) acc[t] += st_acc[w][t][lane] * e;
+        acc[NO] += st_acc[w][NO][lane] * e2;
+    }
+    // O_lr column rr of head n_o: lane n_o*(R/4) + rr/4, component rr%4 of register LR_REG
+    float lr[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) lr[rr] = __shfl(acc[NO][rr & 3], n_o * (R / 4) + (rr >> 2));
+    const float inv = bad ? __builtin_nanf("") : 1.f / L;
+#pragma unroll
+    for (int t = 0; t < NO; ++t) {
+        const int c = (64 * t + lane) / (4 * GP);
+        const int d0 = VEC * (4 * q + c / (VEC / 4)) + 4 * (c % (VEC / 4));
+        f32x4 o = acc[t];
         if (adapted) {
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) o = fmaf(comb[D + rr], bcol[rr], o);
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(lr[rr], bv[t][rr].get(e), o[e]);
         }
-        Op[c] = from_f32<T>(o / L);
+        if (n_o < p.G) {
+            T* dst = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * p.G + n_o) * D + d0;
+            if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+            else
+                *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+        }
     }
 }
 
@@ -572,9 +649,9 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
         }
     }
     if (p.block_table)
-        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, true>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, GP, true>), dim3(unsigned(p.batch * p.n_kv)), dim3(kCombineThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, false>), dim3(unsigned(p.batch * p.n_q)), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_combine_kernel<T, D, R, GP, false>), dim3(unsigned(p.batch * p.n_kv)), dim3(kCombineThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -21,8 +21,11 @@ struct DecodeParams {
     const int64_t* kv_start;
     const int32_t* kv_len;
     const int32_t* agent;
-    float* ws_ml;   // [(n_slices+batch)*n_q][2]: running max (base-2 units) and sum of each piece
-    float* ws_o;    // [(n_slices+batch)*n_q][d_head + rank]: unnormalised O | O_lr of each piece
+    // partial records of the pieces: (n_slices + batch) * n_kv blocks of decode_record_slots()
+    // 16-byte slots (unnormalised O and O_lr, running max in base-2 units and sum), record_bytes
+    // in all (below 2^31)
+    float* records;
+    uint32_t record_bytes;
     void* O;
     int64_t ld_vlr;
     int64_t kv_rows;
@@ -205,14 +208,26 @@ PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);
 // choice (at most two rounds of one 8-wave workgroup per CU); 0 when there is nothing to do, -1
 // when the sizes are too large. *per_round: slices of one round for the library's choice, else 0.
 int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* per_round = nullptr);
-// the slices in use for a batch of U tiles (the kernels' rule; see decode.hip)
+// 16-byte slots of one decode record block (one piece, one KV head, GP query heads; GP = the
+// group size rounded up to 4 or 8): O (d_head/16 * 4GP), O_lr (GP * rank/4), (m, l) (GP), padded to
+// a multiple of 16 slots (256 bytes)
+inline int decode_record_slots(int G, int d_head, int rank) {
+    const int GP = G <= 4 ? 4 : 8;
+    return (GP * (d_head / 4 + rank / 4 + 1) + 15) / 16 * 16;
+}
+
+// the slices in use for a batch of U tiles (the kernels' rule; see decode.hip): never more than U,
+// so that every slice in use holds at least one tile
 __host__ __device__ inline int decode_active_slices(int U, int n_slices, int per_round) {
-    if (per_round <= 0) return n_slices;
-    // two rounds when each workgroup still streams at least 48 tiles (1,536 keys) of its head, one
-    // round otherwise, and never under 4 tiles per slice
-    int64_t n = int64_t(U) >= int64_t(48) * 2 * per_round ? 2 * per_round : std::min<int64_t>(per_round, (int64_t(U) + 3) / 4);
-    n = (std::max<int64_t>(n, 1) + 7) / 8 * 8;
-    return int(std::min<int64_t>(n, n_slices));
+    if (U <= 0) return 0;
+    int64_t n = n_slices;
+    if (per_round > 0) {
+        // two rounds when each workgroup still streams at least 48 tiles (1,536 keys) of its head,
+        // one round otherwise
+        n = int64_t(U) >= int64_t(48) * 2 * per_round ? 2 * per_round : per_round;
+        n = std::min<int64_t>(n, n_slices);
+    }
+    return int(std::min<int64_t>(n, U));
 }
 
 }  // namespace lra

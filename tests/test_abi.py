@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 6
+    assert lra.abi_version() == 7
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -105,10 +105,11 @@ def test_decode_qkvo_workspace_size():
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 4 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128 + 16 * 130 * 4
-    # 8 slices + 2 requests = 10 records per query head, 40 in all: (m, l) part padded to 512 bytes,
-    # 40 x (64 + 8) fp32 partials, 2 x 4 x 64 fp32 scores, 2 x 4 x 512 fp16 weights, 2 tiles of 16
-    # steps x 128 bytes of repacked tables, 2 flags
-    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == 512 + 40 * 72 * 4 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
+    # (8 slices + 2 requests) x 2 KV heads = 20 record blocks of 4 x (64/4 + 8/4 + 1) = 76 slots
+    # of 16 bytes, padded to 80, 2 x 4 x 64 fp32 scores, 2 x 4 x 512 fp16 weights,
+    # 2 tiles of 16 steps x 128 bytes of repacked tables, 2 flags
+    assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == \
+        20 * 80 * 16 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 
@@ -120,31 +121,34 @@ def test_decode_empty_batch_is_a_no_op():
 def test_decode_workspace_size_follows_slices():
     """The batch's 32-key tiles are cut into n slices (a multiple of 8): about keys_per_split keys
     each at full lengths, or by default up to two rounds of 15/16 of the chip's 8-wave workgroup
-    slots (2 x 240 slices at n_kv = 8) with at least 4 tiles each; the workspace holds the grid's
-    maximum. A slice
+    slots (2 x 240 slices at n_kv = 8) and at most one slice per tile; the workspace holds the
+    grid's maximum. A slice
     holds one piece of each request it touches, with its own record per query head: (n + batch) *
-    n_q records of (m, l) and (O, O_lr)."""
+    n_q records of (m, l) and (O, O_lr), in blocks per KV head."""
     b, n_q, d, r = 16, 32, 128, 8
     up = lambda v: -(-v // 256) * 256
 
-    def layout(n_slices, batch=b):
-        recs = (n_slices + batch) * n_q
-        return up(recs * 2 * 4) + recs * (d + r) * 4   # m, l | O, O_lr
+    def layout(n_slices, batch=b, n_kv=8):
+        # one block per (slice + request, KV head) of 16-byte slots: O (d/16 x 4 x 4
+        # heads), O_lr (4 heads x r/4), (m, l) (4 heads); group size n_q/n_kv rounded up to 4 or 8
+        gp = 4 if n_q // n_kv <= 4 else 8
+        slots = -(-gp * (d // 4 + r // 4 + 1) // 16) * 16   # padded to whole 256-byte runs
+        return (n_slices + batch) * n_kv * slots * 16
 
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(480)
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 4, d, r, 66400, 0) == layout(960)   # 1920 waves / 4 heads
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 16, d, r, 66400, 0) == layout(240)   # two workgroups per slice
-    assert lra.lra_attn_decode_workspace_bytes(1, n_q, 8, d, r, 1900, 0) == layout(16, 1)   # ceil(60 tiles / 4) -> 16
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 4, d, r, 66400, 0) == layout(960, n_kv=4)   # 1920 waves / 4 heads (group of 8)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 16, d, r, 66400, 0) == layout(240, n_kv=16)   # two workgroups per slice (group of 2)
+    assert lra.lra_attn_decode_workspace_bytes(1, n_q, 8, d, r, 1900, 0) == layout(64, 1)   # 60 tiles -> 64 slices
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(1040)   # ceil(16 * 66400 / 1024) = 1038 -> 1040
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
     # the default keys per slice at full lengths: 16 x 66,400 keys (33,200 tiles, at least 48 per
     # slice at two rounds) over 480 slices; 4 x 66,400 (8,300 tiles) over one round of 240; one
-    # 1,900-key request over ceil(60 tiles / 4) -> 16 slices
+    # 1,900-key request (60 tiles) over 60 slices of one tile each
     assert lra.lra_attn_decode_default_split(16, 8, 66400) == 2240   # 2,213.3 rounded up to a multiple of 64
     assert lra.lra_attn_decode_default_split(4, 8, 66400) == 1152    # 1,106.7 -> 1,152
-    assert lra.lra_attn_decode_default_split(1, 8, 1900) == 128
-    assert lra.lra_attn_decode_default_split(1, 1, 1900) == 128
+    assert lra.lra_attn_decode_default_split(1, 8, 1900) == 64
+    assert lra.lra_attn_decode_default_split(1, 1, 1900) == 64
     assert lra.lra_attn_decode_default_split(0, 8, 1900) == 0
 
 

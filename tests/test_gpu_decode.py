@@ -515,3 +515,30 @@ def test_decode_paged_bench_configuration_bit_identical():
                                           B, ag, s.scale, 0)
     torch.cuda.synchronize()
     assert np.array_equal(host64(O), ref)
+
+
+# ------------------------------------------------------------------------------ shared workspace
+def test_decode_workspace_shared_across_shapes_needs_no_initialisation():
+    """One workspace, filled with NaN bytes once, serves decodes of growing batch and length in a
+    row: every call gives the bits of a call with its own fresh workspace (no part of the workspace
+    is read before the same launch writes it)."""
+    s = W.LLAMA_SHAPE
+    cases = [
+        W.random_decode((930,), s, kv_lens=[40], agents=[1]),
+        W.random_decode((931,), s, kv_lens=[2000, 3, 0, 1700, 64], agents=[0, 2, 1, -1, 1]),
+        W.random_decode((932,), s, kv_lens=[900] * 24 + [33, 4100], agents=[b % 3 for b in range(26)]),
+        W.random_decode((933,), s, kv_lens=[1], agents=[2]),
+    ]
+    need = max(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len, kps)
+               for c in cases for kps in (0, 64))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for i, c in enumerate(cases):
+        for kps in (0, 64):
+            args = (dev(c.Q), dev(c.K), dev(c.V), dev(c.V_lr), dev_idx(c.kv_start, torch.int64),
+                    dev_idx(c.kv_len, torch.int32), c.max_kv_len, dev(c.B), dev_idx(c.agent, torch.int32), s.scale, kps)
+            say(f"decode shared workspace case {i} batch={c.batch} keys_per_split={kps}")
+            got = lra.lra_attn_decode(*args, ws)
+            fresh = lra.lra_attn_decode(*args)
+            torch.cuda.synchronize()
+            assert torch.equal(got, fresh)
+        check(host64(got), ref_decode(c), "bf16", f"shared workspace case {i}")

@@ -29,7 +29,8 @@ __all__ = [
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
+# the in-tree build; LRA_LIB_PATH names another build of the same sources (e.g. the sanitized one)
+LIB_PATH = os.environ.get("LRA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
 LRA_F32, LRA_BF16 = 0, 1
 ADAPTER_FREE = -1   # agent index of the adapter-free view (attention over the base cache alone)
 NOALLOC_SCRATCH_BYTES = 32 << 20   # the static partials array of lra_attn_decode_noalloc

@@ -541,8 +541,9 @@ def bench_short_decode(args, torch, lra, W, out):
 
 def bench_ministral_step(args, torch, lra, W, out):
     """36 layers x (LR precompute of the 32 newest tokens -> decode of 32 requests), per-layer caches.
-    Layer caches are drawn on the GPU (seeded torch generator) to keep set-up to seconds; the host
-    generator with identical shapes feeds the parity tests of layers 0 and 35."""
+    Layer caches are drawn on the GPU (workloads.ministral_layer_device, seeded torch generator) to
+    keep set-up to seconds; a GPU parity test checks layer 0 of these exact inputs against the
+    oracle, and the host streams with identical shapes feed the tests of layers 0, 3 and 35."""
     s = W.MINISTRAL_SHAPE
     lens = W.ministral_lengths()
     agents = W.ministral_agents()
@@ -551,19 +552,11 @@ def bench_ministral_step(args, torch, lra, W, out):
         starts.append(starts[-1] + int(x))
     rows = int(sum(int(x) for x in lens))
     n_layers = W.MINISTRAL_LAYERS
-    g = torch.Generator(device="cuda")
     layers = []
     log(f"[bench] ministral step: drawing {n_layers} layer caches ({rows} rows each) on the GPU")
     for layer in range(n_layers):
-        g.manual_seed(1_000_003 * (layer + 1) + 42)
-        K = torch.randn((rows, s.n_kv, s.d_head), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-        V = torch.randn((rows, s.n_kv, s.d_head), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-        L = torch.randn((rows, s.n_agents * s.rank), generator=g, device="cuda").to(torch.bfloat16)
-        A = (torch.randn((s.n_agents * s.rank, s.d_model), generator=g, device="cuda") / 64.0).to(torch.bfloat16)
-        B = (torch.randn((s.n_agents, s.rank, s.d_kv), generator=g, device="cuda") * 0.05).to(torch.bfloat16)
-        X = torch.randn((len(lens), s.d_model), generator=g, device="cuda").to(torch.bfloat16)
-        Q = torch.randn((len(lens), s.n_q, s.d_head), generator=g, device="cuda").to(torch.bfloat16)
-        layers.append((K, V, L, A, B, X, Q))
+        d = W.ministral_layer_device(layer, torch)
+        layers.append((d["K"], d["V"], d["V_lr"], d["A"], d["B"], d["X"], d["Q"]))
     ks = torch.as_tensor(starts, dtype=torch.int64).cuda()
     kl = torch.as_tensor(lens, dtype=torch.int32).cuda()
     ag = torch.as_tensor(agents, dtype=torch.int32).cuda()

@@ -68,9 +68,10 @@ def test_tiny_fp32_precompute_prefill_and_eight_decode_steps():
         check(dec_out[st], ref, "f32", f"decode step {st}")
 
 
-@pytest.mark.parametrize("layer", [0, 35])
+@pytest.mark.parametrize("layer", [0, 3, 35])
 def test_ministral_layer_precompute_then_decode(layer):
-    """One layer of the 36-layer step: the precompute writes each request's newest LR row, then decode."""
+    """One layer of the 36-layer step: the precompute writes each request's newest LR row, then the
+    decode; every request of the layer against the oracle."""
     say(f"ministral layer {layer}: generating inputs")
     dec, pre = W.ministral_layer(layer)
     s = dec.shape
@@ -83,7 +84,8 @@ def test_ministral_layer_precompute_then_decode(layer):
                             dev_idx(dec.agent, torch.int32), s.scale)
     got = host64(O)
     lr_ref = oracle.lr_precompute(pre.X.as_f64(), pre.A.as_f64())
-    for b in (0, 9, 31, int(np.argmax(dec.kv_len))):
+    for b in range(dec.batch):
+        say(f"ministral layer {layer}: oracle request {b}")
         r0, n = int(dec.kv_start[b]), int(dec.kv_len[b])
         Vlr_b = W.HostTensor(dec.V_lr.data[r0:r0 + n], "bf16").as_f64()
         Vlr_b[-1, :] = lr_ref[b]
@@ -91,3 +93,41 @@ def test_ministral_layer_precompute_then_decode(layer):
                                  W.HostTensor(dec.V.data[r0:r0 + n], "bf16").as_f64(), Vlr_b, dec.B.as_f64(),
                                  [0], [n], [int(dec.agent[b])], s.scale)
         check(got[b:b + 1], ref, "bf16", f"layer {layer} request {b}")
+
+
+def _host(t: torch.Tensor) -> W.HostTensor:
+    """A device bf16 tensor as the host bit pattern (the oracle reads the stored values)."""
+    return W.HostTensor(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+
+
+def test_ministral_bench_layer_all_requests():
+    """Layer 0 of the benchmark's 36-layer step, with the exact inputs the benchmark times (drawn on
+    the GPU by workloads.ministral_layer_device): the precompute of the 32 newest LR rows, then the
+    decode of all 32 requests in the benchmark's launch configuration, every output against the
+    oracle (precompute in fp64, then the decode over the oracle's own new rows)."""
+    s = W.MINISTRAL_SHAPE
+    say("ministral bench layer 0: drawing inputs on the GPU")
+    d = W.ministral_layer_device(0, torch)
+    starts, lens, agents = d["kv_start"], d["kv_len"], d["agent"]
+    new_rows = starts + lens.astype(np.int64) - 1
+    host = {k: _host(d[k]) for k in ("K", "V", "V_lr", "A", "B", "X", "Q")}   # before the precompute writes
+    Vlr = d["V_lr"].clone()
+    say("ministral bench layer 0: precompute + decode")
+    lra.lra_lr_precompute(d["X"], d["A"], s.n_agents, s.rank, Vlr, dev_idx(new_rows, torch.int64))
+    O = lra.lra_attn_decode(d["Q"], d["K"], d["V"], Vlr, dev_idx(starts, torch.int64), dev_idx(lens, torch.int32),
+                            int(lens.max()), d["B"], dev_idx(agents, torch.int32), s.scale, 0)
+    got = host64(O)
+    got_rows = host64(Vlr[torch.as_tensor(new_rows, device="cuda")])
+    # the pages' A_k side by side is the transpose of the stacked LoRA weights
+    lr_ref = oracle.lr_precompute(host["X"].as_f64(), host["A"].as_f64().T)
+    check(got_rows, lr_ref, "bf16", "newest LR rows")
+    B64, Q64 = host["B"].as_f64(), host["Q"].as_f64()
+    for b in range(len(lens)):
+        r0, n = int(starts[b]), int(lens[b])
+        say(f"ministral bench layer 0: oracle request {b} (L={n})")
+        Vlr_b = W.HostTensor(host["V_lr"].data[r0:r0 + n], "bf16").as_f64()
+        Vlr_b[-1, :] = lr_ref[b]
+        ref = oracle.attn_decode(Q64[b:b + 1], W.HostTensor(host["K"].data[r0:r0 + n], "bf16").as_f64(),
+                                 W.HostTensor(host["V"].data[r0:r0 + n], "bf16").as_f64(), Vlr_b, B64,
+                                 [0], [n], [int(agents[b])], s.scale)
+        check(got[b:b + 1], ref, "bf16", f"request {b}")

@@ -65,6 +65,18 @@ def test_llama_prefill_full_size_sampled_rows():
     check(got[rows], ref, "bf16")
 
 
+def test_llama_prefill_full_size_every_row_of_one_group():
+    """The timed launch (16,384 + 2,048 over 18,432 keys): all 2,048 query rows of KV head 0's query
+    group (query heads 0-3), the oracle run one head at a time."""
+    say("prefill llama 16384+2048 all rows: generating inputs")
+    c = W.llama_prefill()
+    say("prefill llama 16384+2048 all rows: running")
+    got = run_prefill(c)
+    for h in range(c.shape.n_q // c.shape.n_kv):
+        say(f"prefill llama 16384+2048 all rows: oracle head {h}")
+        check(got[:, h:h + 1], ref_prefill(c, heads=[h]), "bf16", f"head {h}")
+
+
 @pytest.mark.parametrize("agent", [0, 1, 2])
 def test_prefill_every_agent(agent):
     s = W.LLAMA_SHAPE

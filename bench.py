@@ -355,6 +355,21 @@ def bench_prefill(args, torch, lra, W, out):
             "mfma_util": round(float(mf["mfma_util_percent"]) / 100.0, 4),
             "mfma_flops_per_launch": int(float(mf["mfma_flops_per_launch"])),
             "source": "profiles/prefill_llama_LP16384_LC2048_mfma_counters.txt"}
+    if args.oracle_budget > 0:
+        # a bounded sample: 64 query rows spread over the chunk, the query group of KV head 0
+        import numpy as np
+        import oracle
+        rows = np.linspace(0, c.L_C - 1, 64).astype(np.int64)
+        heads = list(range(s.n_q // s.n_kv))
+        f = [t.as_f64() for t in (c.Q, c.K, c.V, c.V_lr, c.B)]
+        per, calls, tot = oracle_seconds(lambda: oracle.attn_prefill(*f, c.agent, c.L_P, s.scale, rows=rows, heads=heads),
+                                         args.oracle_budget)
+        fl_s = sum(int(c.L_P + r + 1) for r in rows) * len(heads) * (4 * s.d_head + 2 * s.rank) \
+            + len(rows) * len(heads) * 2 * s.rank * s.d_head
+        out["prefill_llama_LP16384_LC2048_r8"]["oracle"] = oracle_entry(
+            fl_s / per / 1e12, "TFLOP/s", per, calls, tot,
+            f"{len(rows)} of the {c.L_C} query rows x query heads {heads[0]}-{heads[-1]} over their causal keys, "
+            "the same per-pair FLOP count as the line; input widening excluded")
 
     # the same work as four chunk requests of 512 queries in one batched launch (request b: queries
     # 512b .., L_P = 16384 + 512b, all over the same cache rows)
@@ -466,6 +481,12 @@ def bench_precompute(args, torch, lra, W, out):
                                            "us_eager": round(ms * 1e3, 2),
                                            "timing": "HIP graph of 40 launches" if ms_g is not None else "eager",
                                            "x_copies_rotated": n_copies}
+    if args.oracle_budget > 0:
+        import oracle
+        Xf, Af = case.X.as_f64(), case.A.as_f64()
+        per, calls, tot = oracle_seconds(lambda: oracle.lr_precompute(Xf, Af), args.oracle_budget)
+        out["precompute_llama_2048x4096_r8"]["oracle"] = oracle_entry(
+            nb / per / 1e9, "GB/s", per, calls, tot, "all 2,048 rows x 24 columns; input widening excluded")
     del Xs, X0, Vlr, ws
     torch.cuda.empty_cache()
 
@@ -487,6 +508,13 @@ def bench_precompute(args, torch, lra, W, out):
     out["precompute_llama_18432x4096_r8"] = {"us": round(ms_b * 1e3, 2), "gbs": round(gbs_b, 1), "bytes": nb_b,
                                             "frac": round(gbs_b / HBM_PEAK_GBS, 4), "bound": "hbm",
                                             "timing": "eager, two copies of X alternating"}
+    if args.oracle_budget > 0:
+        import oracle
+        Xf, Af = big.X.as_f64()[:4096], big.A.as_f64()
+        nb_s = precompute_bytes(4096, s.d_model, s.n_agents * s.rank)
+        per, calls, tot = oracle_seconds(lambda: oracle.lr_precompute(Xf, Af), args.oracle_budget)
+        out["precompute_llama_18432x4096_r8"]["oracle"] = oracle_entry(
+            nb_s / per / 1e9, "GB/s", per, calls, tot, "the first 4,096 of the 18,432 rows; input widening excluded")
     del Xb, Vb, A
     torch.cuda.empty_cache()
 
@@ -535,6 +563,13 @@ def bench_short_decode(args, torch, lra, W, out):
                                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "latency (7.8 MB)",
                                        "us_eager": round(ms * 1e3, 2),
                                        "timing": "HIP graph of 64 calls" if ms_g is not None else "eager"}
+    if args.oracle_budget > 0:
+        import oracle
+        f = [t.as_f64() for t in (c.Q, c.K, c.V, c.V_lr, c.B)]
+        per, calls, tot = oracle_seconds(lambda: oracle.attn_decode(*f, c.kv_start, c.kv_len, c.agent, s.scale),
+                                         args.oracle_budget)
+        out["decode_llama_b1_L1900_r8"]["oracle"] = oracle_entry(
+            nb / per / 1e9, "GB/s", per, calls, tot, "the whole 1 x 1,900-key request; input widening excluded")
     del Ks, Vs
     torch.cuda.empty_cache()
 
@@ -589,6 +624,31 @@ def bench_ministral_step(args, torch, lra, W, out):
                                          "timing": "HIP graph of one step" if graph_best else "eager launches",
                                          "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
                                          "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
+    if args.oracle_budget > 0:
+        # a bounded sample of layer 0 of these inputs: the precompute of the 32 newest rows, then whole
+        # requests (cycling over the 32) until the budget is spent; bytes as the line counts them
+        import numpy as np
+        import oracle
+        K0, V0, L0, A0, B0, X0, Q0 = layers[0]
+        hostf = lambda t: t.float().cpu().numpy().astype(np.float64)
+        Xf, Af, Bf, Qf = hostf(X0), hostf(A0).T, hostf(B0), hostf(Q0)
+        t0 = time.perf_counter()
+        oracle.lr_precompute(Xf, Af)
+        t_pre = time.perf_counter() - t0
+        t_dec, nbytes_s, done = 0.0, precompute_bytes(len(lens), s.d_model, s.n_agents * s.rank), 0
+        while t_dec + t_pre < args.oracle_budget or done == 0:
+            b = done % len(lens)
+            r0, n = int(starts[b]), int(lens[b])
+            Kb, Vb_, Lb = hostf(K0[r0:r0 + n]), hostf(V0[r0:r0 + n]), hostf(L0[r0:r0 + n])
+            t0 = time.perf_counter()
+            oracle.attn_decode(Qf[b:b + 1], Kb, Vb_, Lb, Bf, [0], [n], [int(agents[b])], s.scale)
+            t_dec += time.perf_counter() - t0
+            nbytes_s += decode_bytes([n], [int(agents[b])], s.n_q, s.n_kv, s.d_head, s.rank)
+            done += 1
+        tot = t_pre + t_dec
+        out["ministral_step_36x_b32_r16"]["oracle"] = oracle_entry(
+            nbytes_s / tot / 1e9, "GB/s", tot, 1, tot,
+            f"layer 0: the 32-row precompute and {done} whole requests; copies to the host excluded")
 
     # the same step with every layer's K and V kept head-major ([n_kv, rows, d]); same values, the
     # decode through lra_attn_decode_strided (bit-identical outputs)
@@ -611,6 +671,46 @@ def bench_ministral_step(args, torch, lra, W, out):
         "layout": "K, V head-major [n_kv, rows, d] per layer (lra_attn_decode_strided)"}
     del layers
     torch.cuda.empty_cache()
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: cores available to this process, CPU model, NumPy's BLAS."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": int(i.get("num_threads", 1))}
+                break
+    except Exception:  # pragma: no cover
+        pass
+    return {"host_cores": len(os.sched_getaffinity(0)), "cpu_model": model, "blas": blas}
+
+
+def oracle_seconds(fn, budget_s: float):
+    """Seconds per call of ``fn`` (the oracle as it stands), repeated until about budget_s of work."""
+    t_total, calls = 0.0, 0
+    while t_total < budget_s or calls == 0:
+        t0 = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t0
+        calls += 1
+    return t_total / calls, calls, t_total
+
+
+def oracle_entry(value, unit, per_call, calls, total, sample) -> dict:
+    return {"value": round(value, 4), "unit": unit, "seconds_per_call": round(per_call, 4), "calls": calls,
+            "seconds": round(total, 2), "kind": "oracle", "sample": sample}
 
 
 def cpu_baseline(case, W, budget_s: float):
@@ -642,10 +742,12 @@ def cpu_baseline(case, W, budget_s: float):
         t_total += time.perf_counter() - t0
         done += 1
         nbytes += decode_bytes([n], [int(case.agent[b])], s.n_q, s.n_kv, s.d_head, s.rank)
+    info = host_info()
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} whole requests (cycling over the {case.batch}) of the 16 x 66,400 decode, fp64 oracle; "
                       f"{t_total:.1f} s of CPU work, input widening excluded",
-            "seconds": round(t_total, 2)}
+            "seconds": round(t_total, 2), **info,
+            "cores_note": "cores = BLAS threads the oracle used; host_cores = len(os.sched_getaffinity(0))"}
 
 
 def main():
@@ -656,6 +758,8 @@ def main():
     ap.add_argument("--only", nargs="*", default=None,
                     choices=["decode", "prefill", "precompute", "short", "ministral", "copy", "cpu"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--oracle-budget", type=float, default=2.0,
+                    help="seconds of oracle work timed beside each other line (0: none)")
     ap.add_argument("--headline-only", action="store_true",
                     help="decode leg: time the headline launch only (no layout or variant lines)")
     args = ap.parse_args()

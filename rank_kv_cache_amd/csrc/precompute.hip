@@ -9,13 +9,14 @@
 // the LoRA "A" weights), so both MFMA operands are contiguous 8-element runs along d_model:
 //   A operand: lane (row n, slot q) <- X[row][k + 8q .. +7]
 //   B operand: lane (col n, slot q) <- At[col][k + 8q .. +7]   (small, L2-resident)
-// One launch, no second pass: a workgroup of 16 waves owns a contiguous range of X rows (the rows
-// are divided evenly, so every workgroup streams the same bytes) and one group of 16 or 32 output
-// columns. Its waves split d_model 16 ways; each wave holds the At fragments of its share in
-// registers for the whole range (loaded once; for d_model beyond 4096 bf16 / 2048 fp32 they are
-// reloaded per batch of chunks) and streams 16-row tiles of X: a tile's loads all go out at once,
-// and each chunk of the next tile as soon as this tile's multiplies have read that chunk's
-// registers, so the next tile is in flight while the 16 partials are summed. The 16 partial tiles are summed through LDS in a fixed order (deterministic)
+// One launch, no second pass: a workgroup of 16 waves (8 for 32 bf16 columns with d_model up to
+// 4096, which need 256 registers per lane) owns a contiguous range of X rows (the rows are divided
+// evenly, so every workgroup streams the same bytes) and one group of 16 or 32 output columns. Its
+// waves split d_model 16 (8) ways; each wave holds the At fragments of its share in registers for
+// the whole range (loaded once; for d_model beyond what fits they are reloaded per batch of chunks)
+// and streams 16-row tiles of X: a tile's loads all go out at once, and each chunk of the next tile
+// as soon as this tile's multiplies have read that chunk's registers, so the next tile is in flight
+// while the partials are summed. The partial tiles are summed through LDS in a fixed order (deterministic)
 // and stored with the optional row map. Workgroup w runs on XCD w % 8; the column groups of one row
 // range get the same XCD and run side by side, so all but the first read X from L2, not HBM.
 #include <algorithm>
@@ -27,17 +28,18 @@ namespace lra {
 
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = 64 * kWaves;
-
+// WAVES: waves per workgroup, splitting d_model WAVES ways (16: 128 registers per lane; 8: 256).
 // ARES: the wave's share of d_model is at most CB chunks, so its At fragments stay in registers for
 // the whole row range; otherwise they are reloaded with each batch of CB chunks. NT: 16-column MFMA
-// tiles per column group. With ARES and NT = 1 each X chunk's registers are refilled with the next
-// tile's chunk as soon as its multiplies have read them (with NT = 2 that would spill registers).
-template <typename T, int CB, bool ARES, int NT>
-__global__ __launch_bounds__(kThreads) void precompute_kernel(PrecomputeParams p) {
+// tiles per column group. With ARES each X chunk's registers are refilled with the next tile's chunk
+// as soon as its multiplies have read them, when the registers allow it: one column tile at 16 waves,
+// two at 8 waves (bf16: 16 chunks of A for two tiles, 128 registers, beside 16 chunks of X).
+template <typename T, int CB, bool ARES, int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams p) {
+    constexpr int kWaves = WAVES;
+    constexpr int kThreads = 64 * WAVES;
     constexpr int NC = 16 * NT;   // columns of a group
-    constexpr bool PREFETCH = ARES && NT == 1;
+    constexpr bool PREFETCH = ARES && (NT == 1 || WAVES == 8);
     __shared__ float red[kWaves][16][NC + 1];
 
     const int w = blockIdx.x, xcd = w & 7, rest = w >> 3;
@@ -132,14 +134,22 @@ __global__ __launch_bounds__(kThreads) void precompute_kernel(PrecomputeParams p
 template <typename T, int CB>
 void launch_t(const PrecomputeParams& p, hipStream_t stream) {
     const int64_t n_wg = (int64_t(p.n_rg) + 7) / 8 * 8 * p.n_cg;
-    const int cpw = (p.d_model / 32 + kWaves - 1) / kWaves;
-    const dim3 grid{unsigned(n_wg)}, block{unsigned(kThreads)};
+    const int nch = p.d_model / 32;
+    const int cpw16 = (nch + 15) / 16, cpw8 = (nch + 7) / 8;
+    const dim3 grid{unsigned(n_wg)}, b16{1024u}, b8{512u};
     if (p.cols_per_group == 32) {
-        if (cpw <= CB) hipLaunchKernelGGL((precompute_kernel<T, CB, true, 2>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((precompute_kernel<T, CB, false, 2>), grid, block, 0, stream, p);
+        // bf16 with d_model <= 4096: 8 waves, A resident for both column tiles, X prefetched
+        if constexpr (sizeof(T) == 2) {
+            if (cpw8 <= 2 * CB) {
+                hipLaunchKernelGGL((precompute_kernel<T, 2 * CB, true, 2, 8>), grid, b8, 0, stream, p);
+                return;
+            }
+        }
+        if (cpw16 <= CB) hipLaunchKernelGGL((precompute_kernel<T, CB, true, 2, 16>), grid, b16, 0, stream, p);
+        else hipLaunchKernelGGL((precompute_kernel<T, CB, false, 2, 16>), grid, b16, 0, stream, p);
     } else {
-        if (cpw <= CB) hipLaunchKernelGGL((precompute_kernel<T, CB, true, 1>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((precompute_kernel<T, CB, false, 1>), grid, block, 0, stream, p);
+        if (cpw16 <= CB) hipLaunchKernelGGL((precompute_kernel<T, CB, true, 1, 16>), grid, b16, 0, stream, p);
+        else hipLaunchKernelGGL((precompute_kernel<T, CB, false, 1, 16>), grid, b16, 0, stream, p);
     }
 }
 
@@ -156,7 +166,7 @@ PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16) {
     pl.n_cg = (NR + pl.cols_per_group - 1) / pl.cols_per_group;
     const int64_t max_rg = std::max<int64_t>(1, 256 / pl.n_cg);
     pl.n_rg = int(std::max<int64_t>(1, std::min<int64_t>((T + 15) / 16, max_rg)));
-    pl.chunks_per_wave = (d_model / 32 + kWaves - 1) / kWaves;
+    pl.chunks_per_wave = (d_model / 32 + 15) / 16;
     pl.cb = bf16 ? 8 : 4;
     return pl;
 }

@@ -575,7 +575,8 @@ def bench_short_decode(args, torch, lra, W, out):
 
 
 def bench_ministral_step(args, torch, lra, W, out):
-    """36 layers x (LR precompute of the 32 newest tokens -> decode of 32 requests), per-layer caches.
+    """36 layers x (LR precompute of the 32 newest tokens -> decode of 32 requests), per-layer caches,
+    timed as one lra_attn_decode_step per layer and, beside it, as lra_lr_precompute + lra_attn_decode.
     Layer caches are drawn on the GPU (workloads.ministral_layer_device, seeded torch generator) to
     keep set-up to seconds; a GPU parity test checks layer 0 of these exact inputs against the
     oracle, and the host streams with identical shapes feed the tests of layers 0, 3 and 35."""
@@ -603,12 +604,18 @@ def bench_ministral_step(args, torch, lra, W, out):
                          dtype=torch.uint8, device="cuda")
     O = torch.empty((len(lens), s.n_q, s.d_head), dtype=torch.bfloat16, device="cuda")
 
-    def step():
+    def step_unfused():
         for (K, V, L, A, B, X, Q) in layers:
             lra.lra_lr_precompute(X, A, s.n_agents, s.rank, L, new_rows, ws_pre)
             lra.lra_attn_decode(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, 0, ws_dec, O)
 
+    # the step as one call per layer: the newest LR rows formed in the decode's own launch
+    def step():
+        for (K, V, L, A, B, X, Q) in layers:
+            lra.lra_attn_decode_step(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, X, A, 0, ws_dec, O)
+
     reps = max(3, args.steps // 10)
+    ms_u = time_launches(step_unfused, reps, 1, torch)
     ms = time_launches(step, reps, 1, torch)
     ms_g = time_graph(step, 1, reps, torch)
     # the step is 72 launches of 0.01-0.25 ms: the faster of the graph replay and the eager loop
@@ -622,6 +629,8 @@ def bench_ministral_step(args, torch, lra, W, out):
                                          "ms_eager": round(ms, 3),
                                          "ms_graph": round(ms_g, 3) if ms_g is not None else None,
                                          "timing": "HIP graph of one step" if graph_best else "eager launches",
+                                         "call": "lra_attn_decode_step per layer (newest LR rows formed in the decode launch)",
+                                         "ms_precompute_then_decode": round(ms_u, 3),
                                          "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
                                          "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
     if args.oracle_budget > 0:

@@ -60,7 +60,8 @@ extern "C" {
                                    recomputation); the qkvo decode workspace holds fp32 key scores;
                                    lra_attn_decode_noalloc;
                                 7: stream-K decode slices and a new record layout (workspace sizes
-                                   changed); the LR precompute needs no workspace */
+                                   changed); the LR precompute needs no workspace;
+                                   lra_attn_decode_step */
 
 typedef enum {
     LRA_OK = 0,
@@ -277,6 +278,40 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                     int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                     void* O, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * One decode step with the LR rows of the step's newest tokens formed in the same launch
+ * (PReCache paper page §3, PreLRShared: each new token's hidden state goes through every agent's
+ * down-projection once; LRAgent method steps (2)-(4)). For every request b with kv_len[b] > 0 and a
+ * valid range and agent, the newest key is cache row n_b = kv_start[b] + kv_len[b] - 1, and
+ *
+ *   V_lr[n_b, k*rank + j] = sum_c X_new[b, c] * A[k*rank + j, c]      (k < n_agents, j < rank)
+ *
+ * is written into the cache (rounded once to the element type), then the decode runs as
+ * lra_attn_decode over all kv_len[b] keys, that row included. This is lra_lr_precompute with
+ * out_rows = n_b followed by lra_attn_decode, in one launch plus the merge kernel: the rows are
+ * formed by extra workgroups of the split launch while the others stream the caches, the split
+ * kernel leaves the newest key out of O_lr and records its score, and the merge kernel adds that
+ * key's LR term from the written row. Results agree with the two calls within the decode's
+ * tolerance (the newest key's LR term is summed in fp32 instead of on the matrix cores).
+ *
+ * X_new    (device) [batch x d_model], row stride ldx elements (ldx >= d_model, multiple of 8)
+ * A        (device) [n_agents*rank x d_model], the stacked down-projections (as lra_lr_precompute)
+ * d_model  a positive multiple of 64
+ * V_lr     (device) the cache, written at the rows n_b (all n_agents*rank columns); the newest rows
+ *          of different requests must be distinct
+ * Every other argument, the workspace (lra_attn_decode_workspace_bytes) and the errors are those
+ * of lra_attn_decode.
+ */
+int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
+                         const void* K_base, const void* V_base, int64_t kv_rows,
+                         void* V_lr, int64_t ld_vlr,
+                         const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                         const void* B, int32_t n_agents, const int32_t* agent,
+                         int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                         const void* X_new, int64_t ldx, const void* A, int32_t d_model,
+                         int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                         void* O, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * lra_attn_decode over K and V caches with explicit strides, for caches kept head-major

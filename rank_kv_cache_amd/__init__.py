@@ -22,7 +22,7 @@ __all__ = [
     "lra_lr_precompute", "lra_lr_precompute_workspace_bytes",
     "lra_attn_prefill", "lra_attn_prefill_qkvo", "lra_attn_prefill_qkvo_workspace_bytes", "lra_attn_prefill_varlen", "lra_attn_prefill_paged",
     "lra_attn_decode", "lra_attn_decode_workspace_bytes", "lra_attn_decode_default_split", "lra_attn_decode_strided",
-    "lra_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "lra_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "lra_attn_decode_step",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_attn_decode_paged_strided",
     "lra_expand_values",
@@ -60,6 +60,8 @@ _SIGNATURES = {
     "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
+    "lra_attn_decode_step": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
+                                        _i32, _i32, _i32, _i32, _f, _p, _i64, _p, _i32, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_noalloc": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
                                            _i32, _i32, _i32, _i32, _f, _i32, _p, _p]),
     "lra_attn_decode_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p,
@@ -433,6 +435,51 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
                                 _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
+    return O
+
+
+def lra_attn_decode_step(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor, V_lr: torch.Tensor,
+                         kv_start: torch.Tensor, kv_len: torch.Tensor, max_kv_len: int, B: torch.Tensor,
+                         agent: torch.Tensor, scale: float, X_new: torch.Tensor, A: torch.Tensor,
+                         keys_per_split: int = 0, workspace: Optional[torch.Tensor] = None,
+                         O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``lra_attn_decode`` after writing each request's newest LR row in the same launch:
+    V_lr[kv_start[b] + kv_len[b] - 1, :N*r] = X_new[b] @ A.T (X_new [batch, d_model], A the stacked
+    [N*r, d_model] down-projections). V_lr is updated in place."""
+    _same(Q, K_base, V_base, V_lr, B, X_new, A)
+    for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("A", A)):
+        _dense(name, t)
+    _rows_dense("V_lr", V_lr)
+    _rows_dense("X_new", X_new)
+    batch, n_q, d = Q.shape
+    n_kv = K_base.shape[1]
+    n_agents, rank = B.shape[0], B.shape[1]
+    d_model = X_new.shape[1]
+    if kv_start.dtype != torch.int64 or kv_len.dtype != torch.int32 or agent.dtype != torch.int32:
+        raise TypeError("kv_start must be int64, kv_len and agent int32")
+    for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
+        if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
+    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+        raise ValueError("K_base/V_base/V_lr/B shapes disagree")
+    if X_new.shape[0] != batch or A.shape != (n_agents * rank, d_model):
+        raise ValueError("X_new must be [batch, d_model] and A [n_agents*rank, d_model]")
+    need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
+    if workspace is None and need:
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if O is None:
+        with _on(stream):
+            O = torch.empty_like(Q)
+    _same(Q, O)
+    _dense("O", O)
+    _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
+    _check(_lib.lra_attn_decode_step(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
+                                     _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                     n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, _ptr(X_new), X_new.stride(0),
+                                     _ptr(A), d_model, keys_per_split, _ptr(workspace), ws_bytes, _ptr(O),
+                                     _stream(stream)), "lra_attn_decode_step")
     return O
 
 

@@ -463,6 +463,14 @@ size_t decode_qkvo_bytes(const DecodeLayout& L, int batch, int n_q, int d_head, 
     return *f_off + size_t(batch) * blocks * size_t((n_q + hpb - 1) / hpb) * sizeof(int32_t);
 }
 
+// the newest tokens' hidden states of a decode step (null: a plain decode)
+struct DecodeStep {
+    const void* X_new;
+    int64_t ldx;
+    const void* A;
+    int32_t d_model;
+};
+
 int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
                 const void* K_base, const void* V_base, int64_t kv_rows, int64_t kv_row_stride, int64_t kv_head_stride,
                 const void* V_lr, int64_t ld_vlr,
@@ -470,8 +478,14 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
                 const void* B, int32_t n_agents, const int32_t* agent,
                 int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                 int32_t keys_per_split, void* workspace, size_t workspace_bytes,
-                void* O, void* stream, const DecodeKeyLora* kl) {
+                void* O, void* stream, const DecodeKeyLora* kl, const DecodeStep* st = nullptr) {
     if (int s = check_dtype(dtype)) return s;
+    if (st) {
+        if (st->d_model <= 0 || st->d_model % 64 != 0)
+            return fail(LRA_ERR_SHAPE, "d_model=%d must be a positive multiple of 64", st->d_model);
+        if (st->ldx < st->d_model || st->ldx % 8 != 0)
+            return fail(LRA_ERR_SHAPE, "ldx=%lld must be >= d_model and a multiple of 8", (long long)st->ldx);
+    }
     if (kl && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "%s: bf16 only", name);
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
     if (batch < 0) return fail(LRA_ERR_SHAPE, "batch=%d is negative", batch);
@@ -497,6 +511,10 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
         return fail(LRA_ERR_NULL, "tensor and index pointers must not be NULL");
     if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(V_lr, 16) || !aligned(B, 16) || !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    if (st) {
+        if (!st->X_new || !st->A) return fail(LRA_ERR_NULL, "X_new and A must not be NULL");
+        if (!aligned(st->X_new, 16) || !aligned(st->A, 16)) return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
+    }
     if (kl) {
         if (!kl->K_lr || !kl->B_k || !kl->cos || !kl->sin) return fail(LRA_ERR_NULL, "K_lr, B_k, rope_cos and rope_sin must not be NULL");
         if (!aligned(kl->K_lr, 16) || !aligned(kl->B_k, 16) || !aligned(kl->cos, 16) || !aligned(kl->sin, 16))
@@ -522,6 +540,17 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_slices = L.n_slices; p.slices_per_round = L.per_round; p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
+    if (st) {
+        p.X_new = st->X_new;
+        p.A_new = st->A;
+        p.ldx = st->ldx;
+        p.d_model = st->d_model;
+        p.n_pre = (batch + 1) / 2;
+        p.n_pre = (p.n_pre + 7) / 8 * 8;
+        if (L.n_slices <= 0) p.n_slices = 0;   // no key anywhere: only the rows (none live) and the merge
+        if (int64_t(p.n_pre) + int64_t(std::max(L.n_slices, 0)) * ((n_kv + 7) / 8) > INT32_MAX)
+            return fail(LRA_ERR_SHAPE, "batch too large for one launch");
+    }
     if (kl && max_kv_len > 0) {
         // the rank-r part of every score first, then the attention adds it to the base scores
         lra::KeyScoreParams e{};
@@ -570,6 +599,21 @@ LRA_EXPORT int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
     return decode_call("lra_attn_decode_strided launch", dtype, Q, batch, K_base, V_base, kv_rows, kv_row_stride,
                        kv_head_stride, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv,
                        d_head, rank, scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr);
+}
+
+LRA_EXPORT int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
+                                    const void* K_base, const void* V_base, int64_t kv_rows,
+                                    void* V_lr, int64_t ld_vlr,
+                                    const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
+                                    const void* B, int32_t n_agents, const int32_t* agent,
+                                    int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
+                                    const void* X_new, int64_t ldx, const void* A, int32_t d_model,
+                                    int32_t keys_per_split, void* workspace, size_t workspace_bytes,
+                                    void* O, void* stream) {
+    const DecodeStep st{X_new, ldx, A, d_model};
+    return decode_call("lra_attn_decode_step launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
+                       d_head, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
+                       scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr, &st);
 }
 
 // ============================================================================ decode without allocation

@@ -146,15 +146,85 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
+// Decode step: workgroup i of the first n_pre forms the LR rows of the newest tokens of requests
+// 2i and 2i+1 (PReCache paper page, PreLRShared: every agent's columns of a new token's row, from its
+// hidden state). Wave w takes d_model elements [w*d_model/8, (w+1)*d_model/8); lane c takes column
+// c0 + c of the stacked A (one 16-byte run per 8 elements; X rows are broadcast loads). The eight
+// wave sums are added in wave order through LDS (deterministic) and rounded once to the cache type.
+template <typename T>
+__device__ void newest_lr_rows(const DecodeParams& p, int i, float (*red)[2][64]) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int NR = p.n_agents * p.rank;
+    const int ks = p.d_model / kSplitWaves;
+    int64_t row[2];
+    bool live[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = 2 * i + h;
+        live[h] = false;
+        row[h] = 0;
+        if (b < p.batch) {
+            const int64_t start = p.kv_start[b];
+            const int32_t len = p.kv_len[b];
+            live[h] = len > 0 && decode_request_ok(start, len, p.agent[b], p);
+            row[h] = start + len - 1;
+        }
+    }
+    const T* __restrict__ X0 = static_cast<const T*>(p.X_new) + int64_t(min(2 * i, p.batch - 1)) * p.ldx;
+    const T* __restrict__ X1 = static_cast<const T*>(p.X_new) + int64_t(min(2 * i + 1, p.batch - 1)) * p.ldx;
+    for (int c0 = 0; c0 < NR; c0 += 64) {
+        const int c = min(c0 + lane, NR - 1);
+        const T* __restrict__ Ac = static_cast<const T*>(p.A_new) + int64_t(c) * p.d_model;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 4
+        for (int k = wv * ks; k < (wv + 1) * ks; k += 8) {
+            Vec<T, 8> av, x0, x1;
+            av.load(Ac + k);
+            x0.load(X0 + k);
+            x1.load(X1 + k);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc0 = fmaf(av.get(e), x0.get(e), acc0);
+                acc1 = fmaf(av.get(e), x1.get(e), acc1);
+            }
+        }
+        red[wv][0][lane] = acc0;
+        red[wv][1][lane] = acc1;
+        __syncthreads();
+        if (threadIdx.x < 128) {
+            const int h = threadIdx.x >> 6, cc = c0 + (threadIdx.x & 63);
+            if (cc < NR && live[h]) {
+                float v = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kSplitWaves; ++ww) v += red[ww][h][threadIdx.x & 63];
+                static_cast<T*>(const_cast<void*>(p.Vlr))[row[h] * p.ld_vlr + cc] = from_f32<T>(v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <typename T, int D, int R, int GP, bool PAGED, bool KSC>
 __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodeParams p) {
     using Tile = DecodeTile<T, D>;
     constexpr int VEC = Tile::VEC, KCH = Tile::KCH;
     static_assert(R <= 16 && GP <= 16, "one 16-wide matrix-core tile covers the rank and the group");
 
+    // decode step: the first n_pre workgroups form the newest LR rows (n_pre is a multiple of 8,
+    // so the XCD of every slice's workgroup stays w % 8)
+    int w = blockIdx.x;
+    if constexpr (!PAGED && !KSC) {
+        if (p.X_new) {
+            __shared__ float red[kSplitWaves][2][64];
+            if (w < p.n_pre) {
+                newest_lr_rows<T>(p, w, red);
+                return;
+            }
+            w -= p.n_pre;
+        }
+    }
     // workgroup w = (slice k, group of 8 KV heads); wave wv takes KV head g. Workgroup w runs on XCD
     // w % 8, and the head groups of one slice get the same w % 8.
-    const int w = blockIdx.x;
     const int xcd = w & 7;
     const int rest = w >> 3;
     const int n_hg = (p.n_kv + kSplitWaves - 1) / kSplitWaves;
@@ -218,6 +288,10 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
         const int32_t a = p.agent[b];
         const int k0 = (u - Pb) * kTile;                  // keys [k0, k1) of request b
         const int k1 = min((pe - Pb) * kTile, int(len));
+        // decode step: this piece holds the request's newest key, whose LR row is being formed in
+        // this launch: that key is left out of O_lr and its score recorded
+        const bool has_new = !PAGED && !KSC && p.X_new != nullptr && k1 == len;
+        float s_new = -INFINITY;
         u = pe;
         Pb = Pn;
         ++b;
@@ -407,6 +481,22 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
                 for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
                 acc_lr *= alpha;
             }
+            if (has_new && kt + kTile >= len) {   // the newest key (len - 1) is in this tile
+                const int kk = len - 1 - kt;
+                const int qk = (kk & 15) >> 2, ek = 4 * (kk >> 4) + (kk & 3);
+                float v = sc[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) v = e == ek ? sc[e] : v;
+                s_new = __shfl(v, n + 16 * qk);
+                // its V_lr entries (and those of the clamped keys past it, which have P = 0) drop out
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (kt + tile_key(q, e) >= len - 1) {
+                        if constexpr (sizeof(T) == 2) t.lr.w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                        else t.lr.v[e] = 0.f;
+                    }
+                }
+            }
             // O^T += V^T P^T, O_lr^T += V_lr^T P^T
             if constexpr (sizeof(T) == 2) {
                 Vec<bf16, 8> phi, plo;
@@ -462,7 +552,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
                     record_store(rs, blk + (c * 4 * GP + 4 * n + q) * 16, f32x4{acc[tt][j], acc[tt + 1][j], acc[tt + 2][j], acc[tt + 3][j]});
                 }
             if (4 * q < R) record_store(rs, blk + (F::LR_SLOT + n * (R / 4) + q) * 16, acc_lr);
-            if (q == 0) record_store(rs, blk + (F::ML_SLOT + n) * 16, f32x4{bad_pages ? __builtin_nanf("") : m_run, l_run, 0.f, 0.f});
+            if (q == 0) record_store(rs, blk + (F::ML_SLOT + n) * 16, f32x4{bad_pages ? __builtin_nanf("") : m_run, l_run, s_new, 0.f});
         }
 
     }
@@ -516,6 +606,13 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     const bool adapted = a != kAdapterFree;
     const int q = lane & 3;
     Vec<T, 4> bv[NO][R];
+    // decode step: the newest key's V_lr entries (ranks 4(L % (R/4)) .. +3 of the agent, for lanes
+    // holding O_lr slots), formed by the split launch; its recorded score follows the merge
+    Vec<T, 4> vnew;
+    vnew.zero();
+    const bool step_new = !PAGED && p.X_new != nullptr && adapted;
+    if (wv == 0 && step_new)
+        vnew.load(static_cast<const T*>(p.Vlr) + (start + len - 1) * p.ld_vlr + int64_t(a) * R + 4 * (lane % (R / 4)));
     if (wv == 0 && adapted) {
         const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
 #pragma unroll
@@ -607,6 +704,14 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
         for (int t = 0; t < NO; ++t) acc[t] += st_acc[w][t][lane] * e;
         acc[NO] += st_acc[w][NO][lane] * e2;
     }
+    if (step_new) {
+        // the newest key's LR term: weight 2^(s_new - M) against the merged maximum of the head
+        const uint32_t last = uint32_t((int64_t(kf) + n_pieces - 1 + b) * p.n_kv + g) * (F::SLOTS * 16);
+        const float s_new = record_load(rs, last + (F::ML_SLOT + n_lr) * 16)[2];
+        const float w_new = fast_exp2(s_new - Ms2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[NO][e] = fmaf(w_new, vnew.get(e), acc[NO][e]);
+    }
     // O_lr column rr of head n_o: lane n_o*(R/4) + rr/4, component rr%4 of register LR_REG
     float lr[R];
 #pragma unroll
@@ -636,7 +741,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
 template <typename T, int D, int R, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     // slices x head groups of 8 (n_slices is a multiple of 8)
-    const int64_t n_wg = int64_t(p.n_slices) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves);
+    const int64_t n_wg = int64_t(p.n_slices) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves) + (p.X_new ? p.n_pre : 0);
     if (n_wg > 0) {
         const dim3 grid{unsigned(n_wg)}, block{unsigned(kSplitThreads)};
         if (p.key_scores) {

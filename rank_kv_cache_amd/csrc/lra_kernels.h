@@ -52,6 +52,15 @@ struct DecodeParams {
     // of request b's key j, fp32 (bf16 only; ks_stride a multiple of 64)
     const float* key_scores;
     int64_t ks_stride;
+    // decode step (null X_new: none): the newest key of request b (row kv_start[b] + kv_len[b] - 1)
+    // gets its LR row V_lr[row, 0 .. n_agents*rank) = X_new[b] . A_new^T, computed by the first
+    // n_pre workgroups of the split launch (a multiple of 8, two requests each); the split kernel
+    // leaves that key out of O_lr and records its score, and the merge kernel adds its LR term
+    const void* X_new;
+    const void* A_new;   // [n_agents*rank x d_model], stacked like the precompute's A
+    int64_t ldx;
+    int d_model;
+    int n_pre;
 };
 
 struct PrecomputeParams {

@@ -114,6 +114,27 @@ def test_decode_qkvo_workspace_size():
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 
 
+def decode_step(**kw):
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+             max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
+             X=P, ldx=4096, A=P, d_model=4096, split=0, ws=WS, ws_bytes=1 << 30, O=P, stream=0)
+    a.update(kw)
+    return lra._lib.lra_attn_decode_step(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"],
+                                         a["ld_vlr"], a["kv_start"], a["kv_len"], a["max_kv_len"], a["B"],
+                                         a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"],
+                                         a["X"], a["ldx"], a["A"], a["d_model"], a["split"], a["ws"], a["ws_bytes"],
+                                         a["O"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=4000), E_SHAPE), (dict(d_model=0), E_SHAPE), (dict(ldx=4088), E_SHAPE), (dict(ldx=4100), E_SHAPE),
+    (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(X=P + 8), E_SHAPE), (dict(A=P + 4), E_SHAPE),
+    (dict(dtype=2), E_UNSUP), (dict(n_q=30), E_SHAPE), (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS),
+])
+def test_decode_step_rejects_bad_arguments(kw, status):
+    assert decode_step(**kw) == status
+
+
 def test_decode_empty_batch_is_a_no_op():
     assert decode(batch=0, Q=None, ws=None, ws_bytes=0) == OK
 

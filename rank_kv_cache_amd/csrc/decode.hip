@@ -644,6 +644,12 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     const int n_o = (lane % (4 * GP)) / 4;
     const int n_lr = min(lane / (R / 4), GP - 1);
     const uint32_t block = F::SLOTS * 16;
+    // decode step: the newest key's recorded score, from the last piece, read beside the partials
+    float s_new = -INFINITY;
+    if (wv == 0 && step_new) {
+        const uint32_t last = uint32_t((int64_t(kf) + n_pieces - 1 + b) * p.n_kv + g) * (F::SLOTS * 16);
+        s_new = record_load(rs, last + (F::ML_SLOT + n_lr) * 16)[2];
+    }
     float M = -INFINITY, L = 0.f, M2 = -INFINITY;
     bool bad = false;
     f32x4 acc[NO + 1];
@@ -706,8 +712,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     }
     if (step_new) {
         // the newest key's LR term: weight 2^(s_new - M) against the merged maximum of the head
-        const uint32_t last = uint32_t((int64_t(kf) + n_pieces - 1 + b) * p.n_kv + g) * (F::SLOTS * 16);
-        const float s_new = record_load(rs, last + (F::ML_SLOT + n_lr) * 16)[2];
         const float w_new = fast_exp2(s_new - Ms2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[NO][e] = fmaf(w_new, vnew.get(e), acc[NO][e]);

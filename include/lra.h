@@ -54,14 +54,16 @@
 extern "C" {
 #endif
 
-#define LRA_ABI_VERSION 7   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
+#define LRA_ABI_VERSION 8   /* 2: agent index -1 selects the adapter-free view; 3: lra_expand_values;
                                 4: lra_attn_decode_strided; 5: lra_attn_decode_paged_strided;
                                 6: finite inputs beyond the fp16 range accepted everywhere (range-safe
                                    recomputation); the qkvo decode workspace holds fp32 key scores;
                                    lra_attn_decode_noalloc;
                                 7: stream-K decode slices and a new record layout (workspace sizes
                                    changed); the LR precompute needs no workspace;
-                                   lra_attn_decode_step */
+                                   lra_attn_decode_step;
+                                8: one round of decode workgroups, each streaming its slice as
+                                   one sequence of tiles (workspace sizes changed) */
 
 typedef enum {
     LRA_OK = 0,
@@ -241,10 +243,10 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
 /* ------------------------------------------------------------------------------------------------
  * Batched decode, one new query token per request, split along the key axis (LRAgent method steps
  * (3)-(4) with L_C = 1). The batch's keys, counted in 32-key tiles request after request, are cut
- * into equal contiguous slices; each (slice, KV head) writes one fp32 partial (m, l, O, O_lr) per
- * request piece it covers to the workspace, and a second kernel merges the partials of each
- * (request, KV head) with the log-sum-exp rule, applies B_agent once and normalises. Request b
- * attends all rows
+ * into equal contiguous slices, one per workgroup; each (slice, KV head) writes one fp32 partial
+ * (m, l, O, O_lr) per request piece it covers to the workspace, and a second kernel merges the
+ * partials of each (request, KV head) with the log-sum-exp rule, applies B_agent once and
+ * normalises. Request b attends all rows
  * kv_start[b] .. kv_start[b]+kv_len[b]-1 of the shared caches; requests may share rows.
  * kv_len[b] = 0 gives a zero output row.
  *
@@ -258,8 +260,9 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  * B        (device) [n_agents x rank x n_kv*d_head]
  * keys_per_split  keys per slice at full lengths (batch * max_kv_len / keys_per_split slices,
  *          rounded up to a multiple of 8; keys_per_split a multiple of 64), or 0 for the library's
- *          choice (up to two rounds of the chip's workgroup slots, fewer when the batch's actual
- *          lengths hold few tiles). The slicing changes the rounding of the result only.
+ *          choice (one round of 8-wave workgroups on 15/16 of the chip's CUs: 240 slices per
+ *          group of 8 KV heads, fewer when the batch's actual lengths hold fewer tiles). The
+ *          slicing changes the rounding of the result only.
  * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
  *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output

@@ -39,21 +39,25 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // -------------------------------------------------------------------------- decode workspace
 struct DecodeLayout {
-    int n_slices, per_round;
+    int n_slots;
     size_t rec_off, rec_bytes, total;
 };
 
-// records: (n_slices + batch) * n_kv blocks of decode_record_slots() 16-byte slots (a slice holds
-// at most one piece of each request it touches, and its pieces' blocks (k + b) * n_kv + g are
-// distinct). n_slices < 0: the sizes are too large for one launch.
+// records: (slices + batch) * n_kv blocks of decode_record_slots() 16-byte slots, with the most
+// slices the sizes allow, min(n_slots, units at max_kv_len) (a slice holds at most one piece of
+// each request it touches, and its pieces' blocks (k + b) * n_kv + g are distinct). n_slots < 0:
+// the sizes are too large for one launch.
 DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, int64_t max_kv_len, int keys_per_split) {
     DecodeLayout L{};
-    L.n_slices = lra::decode_slices(batch, n_kv, max_kv_len, keys_per_split, &L.per_round);
-    const size_t blocks = L.n_slices > 0 ? size_t(L.n_slices + batch) * size_t(n_kv) : 0;
+    L.n_slots = lra::decode_slots(batch, n_kv, max_kv_len, keys_per_split);
+    if (L.n_slots <= 0 || n_kv <= 0 || n_q % n_kv != 0) return L;
+    const int64_t units_max = int64_t(batch) * ((max_kv_len + 31) / 32);   // below 2^31 (decode_slots)
+    const int slices = lra::decode_slices(int(units_max), L.n_slots);
+    const size_t blocks = (size_t(slices) + size_t(batch)) * size_t(n_kv);
     L.rec_off = 0;
-    L.rec_bytes = n_kv > 0 && n_q % n_kv == 0 ? blocks * size_t(lra::decode_record_slots(n_q / n_kv, d_head, rank)) * 16 : 0;
-    if (L.rec_bytes >= (size_t(1) << 31)) L.n_slices = -1;   // 32-bit record offsets
-    L.total = L.rec_bytes ? L.rec_off + L.rec_bytes : 0;
+    L.rec_bytes = blocks * size_t(lra::decode_record_slots(n_q / n_kv, d_head, rank)) * 16;
+    if (L.rec_bytes >= (size_t(1) << 31)) L.n_slots = -1;   // 32-bit record offsets
+    L.total = L.rec_off + L.rec_bytes;
     return L;
 }
 
@@ -320,12 +324,11 @@ LRA_EXPORT int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, 
 // ============================================================================ decode
 LRA_EXPORT int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len) {
     // keys per slice of the library's choice when every request has max_kv_len keys
-    int per_round = 0;
-    const int n_max = lra::decode_slices(batch, n_kv, max_kv_len, 0, &per_round);
-    if (n_max <= 0) return 0;
+    const int n = lra::decode_slots(batch, n_kv, max_kv_len, 0);
+    if (n <= 0) return 0;
     const int64_t units = int64_t(batch) * ((max_kv_len + 31) / 32);
-    const int n = lra::decode_active_slices(int(std::min<int64_t>(units, INT32_MAX)), n_max, per_round);
-    const int64_t keys = (int64_t(batch) * max_kv_len + n - 1) / n;   // a valid keys_per_split: multiple of 64
+    const int64_t n_act = std::min<int64_t>(n, units);
+    const int64_t keys = (int64_t(batch) * max_kv_len + n_act - 1) / n_act;   // a valid keys_per_split: multiple of 64
     return int32_t(std::min<int64_t>((keys + 63) / 64 * 64, INT32_MAX / 64 * 64));
 }
 
@@ -381,7 +384,7 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
         !aligned(O, 16))
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split);
-    if (L.n_slices < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
+    if (L.n_slots < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
     if (L.total) {
         if (!workspace) return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes required", L.total);
         if (!aligned(workspace, 256)) return fail(LRA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -395,7 +398,7 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
     p.kv_row_stride = row_stride; p.kv_head_stride = head_stride; p.kv_page_stride = page_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
-    p.d_head = d_head; p.rank = rank; p.n_slices = L.n_slices; p.slices_per_round = L.per_round; p.scale = scale;
+    p.d_head = d_head; p.rank = rank; p.n_slots = std::max(L.n_slots, 0); p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
     p.block_table = block_table; p.n_pages = n_pages; p.max_blocks = max_blocks;
     p.page_shift = __builtin_ctz(unsigned(page_size));
@@ -521,7 +524,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
             return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     }
     const DecodeLayout L = decode_layout(batch, n_q, n_kv, d_head, rank, max_kv_len, keys_per_split);
-    if (L.n_slices < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
+    if (L.n_slots < 0) return fail(LRA_ERR_SHAPE, "batch x max_kv_len too large for one launch");
     size_t ks_off = 0, w_off = 0, t_off = 0, f_off = 0;
     const size_t need = kl ? (max_kv_len > 0 ? decode_qkvo_bytes(L, batch, n_q, d_head, rank, max_kv_len, &ks_off, &w_off, &t_off, &f_off) : 0)
                            : L.total;
@@ -538,7 +541,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
     p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride; p.kv_page_stride = 0;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
-    p.d_head = d_head; p.rank = rank; p.n_slices = L.n_slices; p.slices_per_round = L.per_round; p.scale = scale;
+    p.d_head = d_head; p.rank = rank; p.n_slots = std::max(L.n_slots, 0); p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
     if (st) {
         p.X_new = st->X_new;
@@ -547,8 +550,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
         p.d_model = st->d_model;
         p.n_pre = (batch + 1) / 2;
         p.n_pre = (p.n_pre + 7) / 8 * 8;
-        if (L.n_slices <= 0) p.n_slices = 0;   // no key anywhere: only the rows (none live) and the merge
-        if (int64_t(p.n_pre) + int64_t(std::max(L.n_slices, 0)) * ((n_kv + 7) / 8) > INT32_MAX)
+        if (int64_t(p.n_pre) + int64_t(p.n_slots) * ((n_kv + 7) / 8) > INT32_MAX)
             return fail(LRA_ERR_SHAPE, "batch too large for one launch");
     }
     if (kl && max_kv_len > 0) {
@@ -692,28 +694,24 @@ LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
 
 namespace lra {
 
-int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* per_round) {
-    if (per_round) *per_round = 0;
+int decode_slots(int batch, int n_kv, int64_t max_kv_len, int keys_per_split) {
     if (batch <= 0 || n_kv <= 0 || max_kv_len <= 0) return 0;
     const int64_t units_max = int64_t(batch) * ((max_kv_len + 31) / 32);   // 32-key tiles
-    const int64_t n_hg = (n_kv + 7) / 8;                                   // workgroups per slice
-    int64_t n, round = 0;
+    const int64_t n_hg = (n_kv + 7) / 8;                                   // workgroups per slot
+    int64_t n;
     if (keys_per_split > 0) {
         n = (int64_t(batch) * max_kv_len + keys_per_split - 1) / keys_per_split;
     } else {
-        // One 8-wave workgroup (one wave per KV head) per CU on the 256 CUs of MI355X is a round
-        // of 2048 waves. Measured on MI355X, a slice count just past a
-        // whole number of rounds costs a whole extra round, and 15/16 of a round does better than
-        // a full one (16 x 66,400 keys: 0.74 ms at 480-504 slices, 0.755 at 512; 32 requests of
-        // 1.9k-29k keys: 8.22-8.24 ms per 36 calls at 224-240 slices, 8.33 at 256). So the kernels
-        // use one such round, or two when the batch holds enough tiles (decode_active_slices).
-        round = std::max<int64_t>(8, 2048 * 15 / 16 / (n_hg * std::min(n_kv, 8)) / 8 * 8);
-        n = std::min(2 * round, units_max);   // down to one tile per slice for small batches
+        // One 8-wave workgroup per CU on 15/16 of the 256 CUs of MI355X, each streaming its slice
+        // as one sequence of tiles. Measured on MI355X: 16 x 66,400 keys take 0.722 ms this way
+        // against 0.740 with two rounds of half-size slices (the previous kernel's best), and
+        // counter-fed slices for the stragglers cost more in merge pieces than they saved.
+        n = std::max<int64_t>(8, 256 * 15 / 16 / n_hg / 8 * 8);
+        n = std::min(n, units_max);   // down to one tile per slice for small batches
     }
     n = (std::max<int64_t>(n, 1) + 7) / 8 * 8;
     // the grid (n x n_hg workgroups) and the 32-bit unit counts of the kernels stay in range
     if (n > (int64_t(1) << 24) || n * n_hg > INT32_MAX || units_max > INT32_MAX) return -1;
-    if (per_round) *per_round = int(round);
     return int(n);
 }
 

@@ -7,15 +7,16 @@
 // d_head (LRAgent page, "core method" / "technical novelty": associativity moves the d_out-wide
 // product out of the key loop).
 //
-// Work split: the batch's keys, counted in 32-key tiles per request, are cut into n_slices
-// contiguous slices of equal size (stream-K style), and one workgroup of 8 waves takes one slice
-// for 8 KV heads, one wave per head. Every workgroup streams the same number of bytes whatever the
-// request lengths, so the launch drains evenly; a slice covers the end of one request and the
-// start of the next as two pieces, each with its own partial. The 8 waves read the same keys of 8
-// heads, i.e. whole 2 KB token rows of a token-major cache, and the V_lr rows they share come into
-// the CU once. Workgroup w runs on XCD w % 8. In a piece, a wave streams its head's 32-key tiles:
-// the K registers of the next tile are refilled as soon as the scores are computed and the V
-// registers as soon as P.V is done, so one tile's loads are always in flight behind the
+// Work split: the batch's keys, counted in 32-key tiles (units) per request, are cut into equal
+// contiguous slices (stream-K style), one per workgroup slot: 15/16 of the chip's CUs, so the
+// whole launch is one round of workgroups; one workgroup of 8 waves takes a slice for 8 KV heads,
+// one wave per head. Every workgroup streams the same number of bytes whatever the request
+// lengths; a slice covers the end of one request and the start of the next as two pieces, each
+// with its own partial. The 8 waves read the same keys of 8 heads, i.e. whole 2 KB token rows of
+// a token-major cache, and the V_lr rows they share come into the CU once. Workgroup w runs on
+// XCD w % 8. A wave streams its head's 32-key tiles: the K registers of the next tile are refilled
+// as soon as the scores are computed and the V registers as soon as P.V is done, also when the
+// next tile starts the next piece, so one tile's loads are always in flight behind the
 // arithmetic. Everything per key runs on the matrix cores; the vector ALUs only do the
 // softmax and an in-register transpose.
 //   * S^T = K Q^T (16x16x32 steps): A = 16 keys x 8 d-elements (128-bit loads of K rows),
@@ -83,9 +84,9 @@ __device__ __forceinline__ Vec<bf16, 8> v_operand(const Vec<bf16, VEC> (&v)[8], 
     return a;
 }
 
-// Units of work: 32-key tiles. A request's units (0 when it is empty or invalid), the slice of the
-// batch's units a workgroup takes, and the slice that owns a unit. Both kernels use these integer
-// formulas, so the merge finds exactly the partials the split kernel wrote.
+// Units of work: 32-key tiles. A request's units (0 when it is empty or invalid); the slices of the
+// batch's units and the slice that owns a unit come from decode_schedule, the same integer formulas
+// in both kernels, so the merge finds exactly the partials the split kernel wrote.
 // The host bounds batch x tiles(max_kv_len) below 2^31, so unit counts are 32-bit.
 template <bool PAGED>
 __device__ __forceinline__ int request_units(const DecodeParams& p, int b) {
@@ -93,8 +94,6 @@ __device__ __forceinline__ int request_units(const DecodeParams& p, int b) {
     const int32_t len = p.kv_len[b];
     return decode_request_ok(start, len, p.agent[b], p) ? (len + kTile - 1) / kTile : 0;
 }
-__device__ __forceinline__ int slice_begin(int U, int k, int n_slices) { return int(int64_t(U) * k / n_slices); }
-__device__ __forceinline__ int slice_owner(int U, int u, int n_slices) { return int((int64_t(u + 1) * n_slices - 1) / U); }
 
 // Partial records. A piece of request b in slice k writes, per KV head g, one block of 16-byte
 // slots at block (k + b) * n_kv + g (GP = the group size rounded up to 4 or 8; n < G, q < 4):
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
     static_assert(R <= 16 && GP <= 16, "one 16-wide matrix-core tile covers the rank and the group");
 
     // decode step: the first n_pre workgroups form the newest LR rows (n_pre is a multiple of 8,
-    // so the XCD of every slice's workgroup stays w % 8)
+    // so the XCD of every slot's workgroup stays w % 8)
     int w = blockIdx.x;
     if constexpr (!PAGED && !KSC) {
         if (p.X_new) {
@@ -223,324 +222,345 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
             w -= p.n_pre;
         }
     }
-    // workgroup w = (slice k, group of 8 KV heads); wave wv takes KV head g. Workgroup w runs on XCD
-    // w % 8, and the head groups of one slice get the same w % 8.
+    // workgroup w = (slot, group hg of 8 KV heads); wave wv takes KV head g. Workgroup w runs on
+    // XCD w % 8, and the head groups of one slot get the same w % 8.
     const int xcd = w & 7;
     const int rest = w >> 3;
     const int n_hg = (p.n_kv + kSplitWaves - 1) / kSplitWaves;
-    const int k = (rest / n_hg) * 8 + xcd;
+    const int slot = (rest / n_hg) * 8 + xcd;
+    const int hg = rest % n_hg;
+    if (slot >= p.n_slots) return;   // the whole workgroup
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = (rest % n_hg) * kSplitWaves + wv;
-    if (k >= p.n_slices || g >= p.n_kv) return;   // no barrier in this kernel: a wave may leave early
+    // a wave past the last KV head (n_kv not a multiple of 8) follows its workgroup through the
+    // same tiles on head n_kv - 1, so that it meets the same barriers, and stores nothing
+    const bool live = hg * kSplitWaves + wv < p.n_kv;
+    const int g = min(hg * kSplitWaves + wv, p.n_kv - 1);
     const int lane = threadIdx.x & 63;
     const int G = p.G;
 
-    // ---- this workgroup's slice of the batch's units: [s0, s1). Every wave scans the request
-    // table itself (64 requests per step): the total, then the first request reaching past s0.
-    const int ub_first = lane < p.batch ? request_units<PAGED>(p, lane) : 0;   // the first 64 requests
-    int U = wave_sum(ub_first);
+    // ---- the request table, 64 requests at a time: lane l holds request wb + l's range, agent and
+    // units, and the units' inclusive prefix sum in the window; wP = units before request wb. Every
+    // wave reads it; pieces then take their request's entries by readlane, with no memory access.
+    int wb = 0, wP = 0;
+    int64_t w_start = 0;
+    int w_len = 0, w_agent = 0, w_ub = 0, w_incl = 0;
+    auto load_window = [&]() {
+        const int bb = wb + lane;
+        w_start = 0;
+        w_len = w_agent = w_ub = 0;
+        if (bb < p.batch) {
+            w_start = PAGED ? 0 : p.kv_start[bb];
+            w_len = p.kv_len[bb];
+            w_agent = p.agent[bb];
+            w_ub = decode_request_ok(w_start, w_len, w_agent, p) ? (w_len + kTile - 1) / kTile : 0;
+        }
+        // consumed here, so that no later read of the window waits for the loads (a piece's
+        // request always has units)
+        w_start = w_ub > 0 ? w_start : 0;
+        w_len = w_ub > 0 ? w_len : 0;
+        w_agent = w_ub > 0 ? w_agent : 0;
+        w_incl = wave_incl_scan(w_ub, lane);
+    };
+    load_window();
+    int U = __builtin_amdgcn_readlane(w_incl, 63);
     for (int c0 = 64; c0 < p.batch; c0 += 64) {
         const int bb = c0 + lane;
         U += wave_sum(bb < p.batch ? request_units<PAGED>(p, bb) : 0);
     }
     U = __builtin_amdgcn_readfirstlane(U);
-    const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
-    if (k >= n_act) return;
-    // n_act <= U: every slice in use holds at least one unit
-    const int s0 = slice_begin(U, k, n_act), s1 = slice_begin(U, k + 1, n_act);
-    int b = 0;
-    int Pb = 0;   // units before request b
-    for (int c0 = 0; c0 < p.batch; c0 += 64) {
-        const int bb = c0 + lane;
-        const int ub = c0 == 0 ? ub_first : bb < p.batch ? request_units<PAGED>(p, bb) : 0;
-        const int incl = wave_incl_scan(ub, lane);
-        const uint64_t past = __ballot(bb < p.batch && Pb + incl > s0);
-        if (past) {
-            const int l = __builtin_ctzll(past);
-            b = c0 + l;
-            Pb += __shfl(incl - ub, l);
-            break;
+    const int n_act = decode_slices(U, p.n_slots);
+    if (slot >= n_act) return;   // the whole workgroup (U is the same in every wave)
+    const int s0 = slice_begin(U, slot, n_act), s1 = slice_begin(U, slot + 1, n_act);   // this slice's units
+
+    // ---- pieces: the part of one request's units in the slice
+    struct Piece {
+        int b;          // request
+        int u0, pe;     // units [u0, pe) of the batch
+        int k0, k1;     // keys [k0, k1) of the request
+        int len, a;
+        int64_t start;
+    };
+    // the piece that starts at unit u (s0 <= u < s1)
+    auto piece_at = [&](int u, Piece& pc) {
+        int l = 0;
+        for (;;) {   // the request holding u, never before the window: units only increase
+            const uint64_t past = __ballot(wb + lane < p.batch && wP + w_incl > u);
+            if (past) {
+                l = __builtin_ctzll(past);
+                break;
+            }
+            if (wb + 64 >= p.batch) {   // not reached (u < U); ends the search on a valid request
+                l = p.batch - 1 - wb;
+                break;
+            }
+            wP += __builtin_amdgcn_readlane(w_incl, 63);
+            wb += 64;
+            load_window();
         }
-        Pb += __shfl(incl, 63);
-    }
-    b = __builtin_amdgcn_readfirstlane(b);
-    Pb = __builtin_amdgcn_readfirstlane(Pb);
+        const int ub = __builtin_amdgcn_readlane(w_ub, l);
+        const int Pb = wP + __builtin_amdgcn_readlane(w_incl, l) - ub;   // units before the request
+        pc.b = wb + l;
+        pc.u0 = u;
+        pc.pe = min(Pb + ub, s1);
+        pc.start = PAGED ? 0 : int64_t(__builtin_amdgcn_readlane(int(uint64_t(w_start) >> 32), l)) << 32 |
+                                   uint32_t(__builtin_amdgcn_readlane(int(w_start), l));
+        pc.len = __builtin_amdgcn_readlane(w_len, l);
+        pc.a = __builtin_amdgcn_readlane(w_agent, l);
+        pc.k0 = (u - Pb) * kTile;
+        pc.k1 = min((pc.pe - Pb) * kTile, pc.len);
+    };
 
     const int n = lane & 15;   // key row of K, head column of Q^T / P^T, O^T row
     const int q = lane >> 4;   // reduction slot group
     const int64_t row_bytes = p.kv_row_stride * int64_t(sizeof(T));
     const int64_t lr_bytes = p.ld_vlr * int64_t(sizeof(T));
+    const int64_t head_bytes = int64_t(g) * p.kv_head_stride * int64_t(sizeof(T));
     const float sl2 = p.scale * kLog2e;
 
-    // ---- the slice's pieces: the part of each request's units that falls in [s0, s1)
-    int u = s0;
-    while (u < s1) {   // workgroup-uniform
-        const int ub = request_units<PAGED>(p, b);
-        const int Pn = Pb + ub;
-        if (ub == 0 || Pn <= u) {   // a request with no units (empty or invalid)
-            Pb = Pn;
-            ++b;
-            continue;
+    // Paged cache: each wave keeps the page ids of 64 consecutive blocks of one request, one per
+    // lane, and reloads that window when a tile moves past it or to another request; a tile never
+    // crosses a page (P is a power of two >= 32 and tiles are 32-aligned), so its page is one
+    // readlane away. Out-of-range page ids read page 0 instead and poison the piece with NaN.
+    int page_vec = 0, pg_base = 0, pg_req = -1;
+    bool pg_bad = false;
+    auto page_of = [&](const Piece& pc, int kt, bool& bad) -> int {
+        const int blk = kt >> p.page_shift;   // wave-uniform
+        if (pc.b != pg_req || blk - pg_base >= 64 || blk < pg_base) {
+            pg_req = pc.b;
+            pg_base = blk;
+            const int n_blk = ((pc.len - 1) >> p.page_shift) + 1;
+            int id = 0;
+            if (pg_base + lane < n_blk) id = p.block_table[int64_t(pc.b) * p.max_blocks + pg_base + lane];
+            const bool lane_bad = pg_base + lane < n_blk && (id < 0 || int64_t(id) >= p.n_pages);
+            pg_bad = __ballot(lane_bad) != 0;
+            page_vec = lane_bad ? 0 : id;
         }
-        const int pe = min(Pn, s1);
-        const int64_t start = PAGED ? 0 : p.kv_start[b];
-        const int32_t len = p.kv_len[b];
-        const int32_t a = p.agent[b];
-        const int k0 = (u - Pb) * kTile;                  // keys [k0, k1) of request b
-        const int k1 = min((pe - Pb) * kTile, int(len));
-        // decode step: this piece holds the request's newest key, whose LR row is being formed in
-        // this launch: that key is left out of O_lr and its score recorded
-        const bool has_new = !PAGED && !KSC && p.X_new != nullptr && k1 == len;
-        float s_new = -INFINITY;
-        u = pe;
-        Pb = Pn;
-        ++b;
+        bad = bad || pg_bad;
+        return __builtin_amdgcn_readlane(page_vec, blk - pg_base);
+    };
+    // first cache row of the 32-key tile starting at key kt of the piece's request (V_lr rows), and
+    // the byte offset of that row from the request's first row in K / V (a page's rows are
+    // adjacent; pages sit kv_page_stride elements apart)
+    auto tile_row = [&](const Piece& pc, int kt, bool& bad) -> int64_t {
+        if constexpr (PAGED) return (int64_t(page_of(pc, kt, bad)) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
+        else return kt;
+    };
+    auto tile_kv_off = [&](const Piece& pc, int kt, bool& bad) -> int64_t {
+        if constexpr (PAGED) {
+            return int64_t(page_of(pc, kt, bad)) * p.kv_page_stride * int64_t(sizeof(T)) +
+                   int64_t(kt & ((1 << p.page_shift) - 1)) * row_bytes;
+        } else {
+            return int64_t(kt) * row_bytes;
+        }
+    };
 
-        // Paged cache: each wave keeps the page ids of 64 consecutive blocks of the request, one
-        // per lane, and reloads that window when a tile moves past it; a tile never crosses a page
-        // (P is a power of two >= 32 and tiles are 32-aligned), so its page is one readlane away.
-        // Out-of-range page ids read page 0 instead and poison the piece's partial with NaN.
-        int page_vec = 0, pg_base = -(1 << 30);
-        bool bad_pages = false;
-        const int n_blk = PAGED ? ((len - 1) >> p.page_shift) + 1 : 0;
-        auto page_of = [&](int kt) -> int {
-            const int blk = kt >> p.page_shift;   // wave-uniform
-            if (blk - pg_base >= 64) {
-                pg_base = blk;
-                int id = 0;
-                if (pg_base + lane < n_blk) id = p.block_table[int64_t(b - 1) * p.max_blocks + pg_base + lane];
-                const bool lane_bad = pg_base + lane < n_blk && (id < 0 || int64_t(id) >= p.n_pages);
-                bad_pages = bad_pages || __ballot(lane_bad) != 0;
-                page_vec = lane_bad ? 0 : id;
-            }
-            return __builtin_amdgcn_readlane(page_vec, blk - pg_base);
-        };
-        // first cache row of the 32-key tile starting at key kt of the request (V_lr rows), and the
-        // byte offset of that row in the request's K / V head (a page's rows are adjacent; pages sit
-        // kv_page_stride elements apart)
-        auto tile_row = [&](int kt) -> int64_t {
-            if constexpr (PAGED) return (int64_t(page_of(kt)) << p.page_shift) + (kt & ((1 << p.page_shift) - 1));
-            else return kt;
-        };
-        auto tile_kv_off = [&](int kt) -> int64_t {
-            if constexpr (PAGED) {
-                return int64_t(page_of(kt)) * p.kv_page_stride * int64_t(sizeof(T)) +
-                       int64_t(kt & ((1 << p.page_shift) - 1)) * row_bytes;
-            } else {
-                return int64_t(kt) * row_bytes;
-            }
-        };
+    // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
+    // offset per operand, so the loads use the scalar-base + vector-offset form. An adapter-free
+    // request streams agent 0's columns of V_lr (same rows, valid memory) through the same
+    // instructions; the merge drops that product.
+    const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
+    const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
+    const uint32_t l_lane = uint32_t(4 * q * lr_bytes + (n % R) * sizeof(T));
+    auto kv_base = [&](const void* X, const Piece& pc) -> const char* {
+        return static_cast<const char*>(X) + pc.start * row_bytes + head_bytes;
+    };
+    auto lr_base = [&](const Piece& pc) -> const char* {
+        return static_cast<const char*>(p.Vlr) + (pc.start * p.ld_vlr + int64_t(max(pc.a, 0)) * R) * int64_t(sizeof(T));
+    };
 
-        // Addresses: a wave-uniform base per tile and slot (scalar registers) plus one 32-bit lane
-        // offset per operand, so the loads use the scalar-base + vector-offset form.
-        const int64_t head_off = (start * p.kv_row_stride + g * p.kv_head_stride) * int64_t(sizeof(T));
-        const char* __restrict__ Kg = static_cast<const char*>(p.K) + head_off;
-        const char* __restrict__ Vg = static_cast<const char*>(p.V) + head_off;
-        // an adapter-free request streams agent 0's columns (same rows, valid memory) through the
-        // same instructions; the merge drops that product
-        const char* __restrict__ Lg = static_cast<const char*>(p.Vlr) + (start * p.ld_vlr + int64_t(max(a, 0)) * R) * int64_t(sizeof(T));
-        const T* __restrict__ Qp = static_cast<const T*>(p.Q);
-        const uint32_t k_lane = uint32_t(n * row_bytes + 8 * q * sizeof(T));
-        const uint32_t v_lane = uint32_t(4 * q * row_bytes + VEC * n * sizeof(T));
-        const uint32_t l_lane = uint32_t(4 * q * lr_bytes + (n % R) * sizeof(T));
-
-        // the group's queries as the B operand (columns >= G are zero)
-        const int bq = b - 1;   // this piece's request
-        Vec<T, 8> qf[KCH];
+    // the group's queries as the B operand (columns >= G are zero)
+    const T* __restrict__ Qp = static_cast<const T*>(p.Q);
+    Vec<T, 8> qf[KCH];
+    auto load_q = [&](const Piece& pc) {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            if (n < G) qf[i].load(Qp + (int64_t(bq) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * q);
+            if (n < G) qf[i].load(Qp + (int64_t(pc.b) * p.n_q + int64_t(g) * G + n) * D + 32 * i + 8 * q);
             else qf[i].zero();
         }
+    };
 
-        // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key
-        // score pass as fp32 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head
-        // n (a wave-uniform base per request and KV head plus one 32-bit lane offset)
-        const bool ks_live = KSC && a != kAdapterFree;
-        const char* __restrict__ ksg = KSC ? reinterpret_cast<const char*>(p.key_scores + (int64_t(bq) * p.n_q + int64_t(g) * G) * p.ks_stride) : nullptr;
-        const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 4);
-        auto load_ks = [&](Tile& t, int kt) {
-            if constexpr (KSC) {
-                if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
-                    t.ks[0] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * kt);
-                    t.ks[1] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * (kt + 16));
-                } else {
-                    t.ks[0] = t.ks[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-        };
-        // Tile loads. A full tile addresses each operand as a wave-uniform base (scalar registers)
-        // plus one 32-bit lane offset. Only a piece's last tile can run past k1: its rows are
-        // clamped to k1 - 1 (finite data; those keys get P = 0). Both forms issue the same loads
-        // into the same registers, so the choice is a uniform branch around address arithmetic only.
-        auto load_k = [&](Tile& t, int kt) {
-            const char* kb = Kg + tile_kv_off(kt);
-            if (kt + kTile <= k1) {
-#pragma unroll
-                for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-                    for (int i = 0; i < KCH; ++i)
-                        t.k[uu][i].load(reinterpret_cast<const T*>(kb + 16 * uu * row_bytes + k_lane) + 32 * i);
+    // LoRA on the keys: the rank-r part of the scores, Q . RoPE(K_lr B_k), comes from the key
+    // score pass as fp32 [request][query head][key]; lane (n, q) adds keys 16u + 4q .. +3 of head
+    // n (a wave-uniform base per request and KV head plus one 32-bit lane offset)
+    bool ks_live = false;
+    const char* __restrict__ ksg = nullptr;
+    const uint32_t ks_lane = uint32_t((min(n, G - 1) * p.ks_stride + 4 * q) * 4);
+    auto load_ks = [&](Tile& t, int kt) {
+        if constexpr (KSC) {
+            if (ks_live) {   // request-uniform; rows are padded to whole 64-key blocks
+                t.ks[0] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * kt);
+                t.ks[1] = *reinterpret_cast<const float4*>(ksg + ks_lane + 4 * (kt + 16));
             } else {
-                const int lim = k1 - 1 - kt;
-#pragma unroll
-                for (int uu = 0; uu < 2; ++uu) {
-                    const uint32_t o = uint32_t(min(16 * uu + n, lim) * row_bytes + 8 * q * sizeof(T));
-#pragma unroll
-                    for (int i = 0; i < KCH; ++i) t.k[uu][i].load(reinterpret_cast<const T*>(kb + o) + 32 * i);
-                }
+                t.ks[0] = t.ks[1] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-        };
-        auto load_v = [&](Tile& t, int kt) {
-            const char* vb = Vg + tile_kv_off(kt);
-            const char* lb = Lg + tile_row(kt) * lr_bytes;
-            // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
-            // so no load sits behind a lane mask
-            uint32_t h[8];
-            if (kt + kTile <= k1) {
+        }
+    };
+    // Tile loads of the tile at key kt of a piece. A full tile addresses each operand as a
+    // wave-uniform base plus one 32-bit lane offset. Only a piece's last tile can run past k1: its
+    // rows are clamped to k1 - 1 (finite data; those keys get P = 0). Both forms issue the same
+    // loads into the same registers, so the choice is a uniform branch around address arithmetic.
+    auto load_k = [&](Tile& t, const Piece& pc, int kt, bool& bad) {
+        const char* kb = kv_base(p.K, pc) + tile_kv_off(pc, kt, bad);
+        if (kt + kTile <= pc.k1) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    t.v[e].load(reinterpret_cast<const T*>(vb + tile_key(0, e) * row_bytes + v_lane));
-                    if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + tile_key(0, e) * lr_bytes + l_lane);
-                    else t.lr.v[e] = *reinterpret_cast<const float*>(lb + tile_key(0, e) * lr_bytes + l_lane);
-                }
-            } else {
-                const int lim = k1 - 1 - kt;
+            for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = min(tile_key(q, e), lim);
-                    t.v[e].load(reinterpret_cast<const T*>(vb + uint32_t(key * row_bytes + VEC * n * sizeof(T))));
-                    const uint32_t lo = uint32_t(key * lr_bytes + (n % R) * sizeof(T));
-                    if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + lo);
-                    else t.lr.v[e] = *reinterpret_cast<const float*>(lb + lo);
-                }
-            }
-            if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
-            }
-        };
-
-        f32x4 acc[VEC];
-        f32x4 acc_lr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < VEC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY, l_run = 0.f;
-
-        // One tile: scores, online softmax, P.V. With PREFETCH the K registers are refilled with the
-        // next tile as soon as the scores are done and the V registers as soon as P.V is done, so
-        // one tile's loads are always in flight behind the arithmetic.
-        auto tile_step = [&](Tile& t, int kt, auto prefetch) {
-            constexpr bool PREFETCH = decltype(prefetch)::value;
-            const int kn = kt + kTile;
-            // the key scores are loaded here, not a tile ahead: prefetched, they overflow the registers
-            load_ks(t, kt);
-            f32x4 sacc[2];
+                for (int i = 0; i < KCH; ++i)
+                    t.k[uu][i].load(reinterpret_cast<const T*>(kb + 16 * uu * row_bytes + k_lane) + 32 * i);
+        } else {
+            const int lim = pc.k1 - 1 - kt;
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu) {
-                sacc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const uint32_t o = uint32_t(min(16 * uu + n, lim) * row_bytes + 8 * q * sizeof(T));
 #pragma unroll
-                for (int i = 0; i < KCH; ++i) sacc[uu] = mma16x16x32(t.k[uu][i], qf[i], sacc[uu]);
+                for (int i = 0; i < KCH; ++i) t.k[uu][i].load(reinterpret_cast<const T*>(kb + o) + 32 * i);
             }
-            if constexpr (KSC) {
-#pragma unroll
-                for (int uu = 0; uu < 2; ++uu) {
-                    sacc[uu][0] += t.ks[uu].x;
-                    sacc[uu][1] += t.ks[uu].y;
-                    sacc[uu][2] += t.ks[uu].z;
-                    sacc[uu][3] += t.ks[uu].w;
-                }
-            }
-            if constexpr (PREFETCH) load_k(t, kn);
-            float sc[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sc[e] = sacc[e >> 2][e & 3] * sl2;
-            if (!PREFETCH && kt + kTile > k1) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (kt + tile_key(q, e) >= k1) sc[e] = -INFINITY;
-            }
-            float mx = sc[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // online softmax (base 2); key kt is live, so mnew is finite
-            const float mnew = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - mnew);
-            m_run = mnew;
-            float pr[8], ls = 0.f;
+        }
+    };
+    auto load_v = [&](Tile& t, const Piece& pc, int kt, bool& bad) {
+        const char* vb = kv_base(p.V, pc) + tile_kv_off(pc, kt, bad);
+        const char* lb = lr_base(pc) + tile_row(pc, kt, bad) * lr_bytes;
+        // every lane loads V_lr (lanes n >= R repeat a column; their O_lr^T rows are never used),
+        // so no load sits behind a lane mask
+        uint32_t h[8];
+        if (kt + kTile <= pc.k1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pr[e] = fast_exp2(sc[e] - mnew);
-                ls += pr[e];
+                t.v[e].load(reinterpret_cast<const T*>(vb + tile_key(0, e) * row_bytes + v_lane));
+                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + tile_key(0, e) * lr_bytes + l_lane);
+                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + tile_key(0, e) * lr_bytes + l_lane);
             }
-            l_run = fmaf(l_run, alpha, ls);
-            if (__ballot(alpha != 1.f)) {
+        } else {
+            const int lim = pc.k1 - 1 - kt;
 #pragma unroll
-                for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
-                acc_lr *= alpha;
+            for (int e = 0; e < 8; ++e) {
+                const int key = min(tile_key(q, e), lim);
+                t.v[e].load(reinterpret_cast<const T*>(vb + uint32_t(key * row_bytes + VEC * n * sizeof(T))));
+                const uint32_t lo = uint32_t(key * lr_bytes + (n % R) * sizeof(T));
+                if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(lb + lo);
+                else t.lr.v[e] = *reinterpret_cast<const float*>(lb + lo);
             }
-            if (has_new && kt + kTile >= len) {   // the newest key (len - 1) is in this tile
-                const int kk = len - 1 - kt;
-                const int qk = (kk & 15) >> 2, ek = 4 * (kk >> 4) + (kk & 3);
-                float v = sc[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) v = e == ek ? sc[e] : v;
-                s_new = __shfl(v, n + 16 * qk);
-                // its V_lr entries (and those of the clamped keys past it, which have P = 0) drop out
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (kt + tile_key(q, e) >= len - 1) {
-                        if constexpr (sizeof(T) == 2) t.lr.w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                        else t.lr.v[e] = 0.f;
-                    }
-                }
-            }
-            // O^T += V^T P^T, O_lr^T += V_lr^T P^T
-            if constexpr (sizeof(T) == 2) {
-                Vec<bf16, 8> phi, plo;
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
-                    plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
-                }
-#pragma unroll
-                for (int tt = 0; tt < VEC; ++tt) {
-                    const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
-                    acc[tt] = mma16x16x32(va, phi, acc[tt]);
-                    acc[tt] = mma16x16x32(va, plo, acc[tt]);
-                }
-                acc_lr = mma16x16x32(t.lr, phi, acc_lr);
-                acc_lr = mma16x16x32(t.lr, plo, acc_lr);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-#pragma unroll
-                    for (int tt = 0; tt < VEC; ++tt)
-                        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
-                    acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
-                }
-            }
-            if constexpr (PREFETCH) load_v(t, kn);
-        };
-
-        // the piece's tiles kt = k0 + 32*j, j < nt (at least one); only the last one can be partial
-        {
-            const int nt = (k1 - k0 + kTile - 1) / kTile;
-            Tile t;
-            load_k(t, k0);
-            load_v(t, k0);
-            int kt = k0;
-            for (int j = 0; j + 1 < nt; ++j, kt += kTile) tile_step(t, kt, std::true_type{});
-            tile_step(t, kt, std::false_type{});
         }
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
+        }
+    };
 
-        // ---- this piece's record block (lanes n < G; see RecordFormat): lane (n, q) holds O^T rows
-        // 4q+j of each tile tt, i.e. d = VEC*(4q+j) + tt, and O_lr rows 4q .. 4q+3
-        using F = RecordFormat<D, R, GP>;
-        const __amdgpu_buffer_rsrc_t rs = record_rsrc(p.records, p.record_bytes);
-        const uint32_t blk = uint32_t((int64_t(k) + bq) * p.n_kv + g) * (F::SLOTS * 16);
+    f32x4 acc[VEC];
+    f32x4 acc_lr;
+    float m_run, l_run, s_new;
+
+    // One tile of piece pc at key kt: scores, online softmax, P.V. With pf, the tile's registers
+    // are refilled with tile nkt of piece np (the next tile of pc, or the first tile of the next
+    // piece, whose queries are then loaded too: new_q) as soon as they have been read: K after the
+    // scores, V after P.V, so one tile's loads are always in flight behind the arithmetic, also
+    // across pieces and slices. Returns whether a page id of those loads was out of range.
+    auto tile_step = [&](Tile& t, const Piece& pc, int kt, bool pf, const Piece& np, int nkt, bool new_q) -> bool {
+        bool nbad = false;
+        // the key scores are loaded here, not a tile ahead: prefetched, they overflow the registers
+        load_ks(t, kt);
+        f32x4 sacc[2];
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            sacc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) sacc[uu] = mma16x16x32(t.k[uu][i], qf[i], sacc[uu]);
+        }
+        if constexpr (KSC) {
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                sacc[uu][0] += t.ks[uu].x;
+                sacc[uu][1] += t.ks[uu].y;
+                sacc[uu][2] += t.ks[uu].z;
+                sacc[uu][3] += t.ks[uu].w;
+            }
+        }
+        if (pf) load_k(t, np, nkt, nbad);
+        if (new_q) load_q(np);
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = sacc[e >> 2][e & 3] * sl2;
+        if (kt + kTile > pc.k1) {   // a partial last tile
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (kt + tile_key(q, e) >= pc.k1) sc[e] = -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // online softmax (base 2); key kt is live, so mnew is finite
+        const float mnew = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+        float pr[8], ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = fast_exp2(sc[e] - mnew);
+            ls += pr[e];
+        }
+        l_run = fmaf(l_run, alpha, ls);
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int tt = 0; tt < VEC; ++tt) acc[tt] *= alpha;
+            acc_lr *= alpha;
+        }
+        // decode step: the piece holding the request's newest key, whose LR row is formed in this
+        // launch, leaves that key out of O_lr and records its score
+        const bool has_new = !PAGED && !KSC && p.X_new != nullptr && pc.k1 == pc.len;
+        if (has_new && kt + kTile >= pc.len) {   // the newest key (len - 1) is in this tile
+            const int kk = pc.len - 1 - kt;
+            const int qk = (kk & 15) >> 2, ek = 4 * (kk >> 4) + (kk & 3);
+            float v = sc[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) v = e == ek ? sc[e] : v;
+            s_new = __shfl(v, n + 16 * qk);
+            // its V_lr entries (and those of the clamped keys past it, which have P = 0) drop out
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (kt + tile_key(q, e) >= pc.len - 1) {
+                    if constexpr (sizeof(T) == 2) t.lr.w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+                    else t.lr.v[e] = 0.f;
+                }
+            }
+        }
+        // O^T += V^T P^T, O_lr^T += V_lr^T P^T
+        if constexpr (sizeof(T) == 2) {
+            Vec<bf16, 8> phi, plo;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
+                plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
+            }
+#pragma unroll
+            for (int tt = 0; tt < VEC; ++tt) {
+                const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
+                acc[tt] = mma16x16x32(va, phi, acc[tt]);
+                acc[tt] = mma16x16x32(va, plo, acc[tt]);
+            }
+            acc_lr = mma16x16x32(t.lr, phi, acc_lr);
+            acc_lr = mma16x16x32(t.lr, plo, acc_lr);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                for (int tt = 0; tt < VEC; ++tt)
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
+                acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
+            }
+        }
+        if (pf) load_v(t, np, nkt, nbad);
+        return nbad;
+    };
+
+    // ---- the piece's record block (lanes n < G; see RecordFormat): lane (n, q) holds O^T rows
+    // 4q+j of each tile tt, i.e. d = VEC*(4q+j) + tt, and O_lr rows 4q .. 4q+3
+    using F = RecordFormat<D, R, GP>;
+    const __amdgpu_buffer_rsrc_t rs = record_rsrc(p.records, p.record_bytes);
+    auto write_record = [&](const Piece& pc, bool bad) {
+        const uint32_t blk = uint32_t((int64_t(slot) + pc.b) * p.n_kv + g) * (F::SLOTS * 16);
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
         if (n < G) {
@@ -552,9 +572,49 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
                     record_store(rs, blk + (c * 4 * GP + 4 * n + q) * 16, f32x4{acc[tt][j], acc[tt + 1][j], acc[tt + 2][j], acc[tt + 3][j]});
                 }
             if (4 * q < R) record_store(rs, blk + (F::LR_SLOT + n * (R / 4) + q) * 16, acc_lr);
-            if (q == 0) record_store(rs, blk + (F::ML_SLOT + n) * 16, f32x4{bad_pages ? __builtin_nanf("") : m_run, l_run, s_new, 0.f});
+            if (q == 0)
+                record_store(rs, blk + (F::ML_SLOT + n) * 16,
+                             f32x4{bad ? __builtin_nanf("") : m_run, l_run, s_new, 0.f});
         }
+    };
 
+    // ---- the slice's pieces, each tile prefetched during the one before it
+    Piece cur{}, nxt{};
+    piece_at(s0, cur);
+    bool cur_bad = false, nxt_bad = false;
+    Tile t;
+    load_q(cur);
+    load_k(t, cur, cur.k0, cur_bad);
+    load_v(t, cur, cur.k0, cur_bad);
+    for (;;) {   // workgroup-uniform
+        const bool has_nxt = cur.pe < s1;
+        if (has_nxt) piece_at(cur.pe, nxt);
+        if constexpr (KSC) {
+            ks_live = cur.a != kAdapterFree;
+            ksg = reinterpret_cast<const char*>(p.key_scores + (int64_t(cur.b) * p.n_q + int64_t(g) * G) * p.ks_stride);
+        }
+#pragma unroll
+        for (int tt = 0; tt < VEC; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_lr = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        s_new = -INFINITY;
+        // the piece's tiles kt = k0 + 32 j, j < nt (at least one); only the last one can be partial
+        const int nt = (cur.k1 - cur.k0 + kTile - 1) / kTile;
+        int kt = cur.k0;
+        for (int j = 0; j < nt; ++j, kt += kTile) {
+            // one instance of the tile code: the next tile's piece is picked by scalar selects
+            const bool more = j + 1 < nt;
+            const Piece np = more ? cur : nxt;
+            const bool pb = tile_step(t, cur, kt, more || has_nxt, np, more ? kt + kTile : nxt.k0, !more && has_nxt);
+            if (more) cur_bad = cur_bad || pb;
+            else nxt_bad = nxt_bad || pb;
+        }
+        if (live) write_record(cur, cur_bad);
+        if (!has_nxt) break;
+        cur = nxt;
+        cur_bad = nxt_bad;
+        nxt_bad = false;
     }
 }
 
@@ -587,6 +647,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     const int64_t start = PAGED ? 0 : p.kv_start[b];
     const int32_t len = p.kv_len[b];
     const int32_t a = p.agent[b];
+    // units of the requests before b and of the batch
     int before = 0, total = 0;
     for (int bb = threadIdx.x; bb < p.batch; bb += kCombineThreads) {
         const int ub = request_units<PAGED>(p, bb);
@@ -636,9 +697,11 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
         Pb += red_u[0][v];
         U += red_u[1][v];
     }
-    const int n_act = decode_active_slices(U, p.n_slices, p.slices_per_round);
+    // the request's pieces: slices kf .. kf + n_pieces - 1, piece i in record block kf + i + b
+    const int n_act = decode_slices(U, p.n_slots);
     const int kf = slice_owner(U, Pb, n_act);
     const int n_pieces = slice_owner(U, Pb + (len + kTile - 1) / kTile - 1, n_act) - kf + 1;
+    auto piece_block = [&](int i) -> int64_t { return int64_t(kf) + i + b; };
 
     const __amdgpu_buffer_rsrc_t rs = record_rsrc(p.records, p.record_bytes);
     const int n_o = (lane % (4 * GP)) / 4;
@@ -647,7 +710,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     // decode step: the newest key's recorded score, from the last piece, read beside the partials
     float s_new = -INFINITY;
     if (wv == 0 && step_new) {
-        const uint32_t last = uint32_t((int64_t(kf) + n_pieces - 1 + b) * p.n_kv + g) * (F::SLOTS * 16);
+        const uint32_t last = uint32_t(piece_block(n_pieces - 1) * p.n_kv + g) * (F::SLOTS * 16);
         s_new = record_load(rs, last + (F::ML_SLOT + n_lr) * 16)[2];
     }
     float M = -INFINITY, L = 0.f, M2 = -INFINITY;
@@ -660,7 +723,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
             const int i = min(i0 + u * kCombineWaves, n_pieces - 1);
-            const uint32_t base = uint32_t((int64_t(kf) + i + b) * p.n_kv + g) * block;
+            const uint32_t base = uint32_t(piece_block(i) * p.n_kv + g) * block;
 #pragma unroll
             for (int t = 0; t <= NO; ++t) v[u][t] = record_load(rs, base + (64 * t + lane) * 16);
             ml[u] = record_load(rs, base + (F::ML_SLOT + n_o) * 16);
@@ -744,8 +807,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
 
 template <typename T, int D, int R, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-    // slices x head groups of 8 (n_slices is a multiple of 8)
-    const int64_t n_wg = int64_t(p.n_slices) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves) + (p.X_new ? p.n_pre : 0);
+    // slots x head groups of 8 (n_slots is a multiple of 8)
+    const int64_t n_wg = int64_t(p.n_slots) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves) + (p.X_new ? p.n_pre : 0);
     if (n_wg > 0) {
         const dim3 grid{unsigned(n_wg)}, block{unsigned(kSplitThreads)};
         if (p.key_scores) {

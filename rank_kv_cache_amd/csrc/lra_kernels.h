@@ -21,7 +21,7 @@ struct DecodeParams {
     const int64_t* kv_start;
     const int32_t* kv_len;
     const int32_t* agent;
-    // partial records of the pieces: (n_slices + batch) * n_kv blocks of decode_record_slots()
+    // partial records of the pieces: (slices + batch) * n_kv blocks of decode_record_slots()
     // 16-byte slots (unnormalised O and O_lr, running max in base-2 units and sum), record_bytes
     // in all (below 2^31)
     float* records;
@@ -35,11 +35,9 @@ struct DecodeParams {
     int64_t kv_row_stride, kv_head_stride;
     int64_t kv_page_stride;     // paged cache: elements between consecutive pages of K and V
     int batch, n_q, n_kv, G, n_agents, d_head, rank;
-    // slices of the batch's 32-key tiles (a multiple of 8); the piece of request b in slice k has
-    // partial record k + b. With slices_per_round > 0 the kernels use fewer slices when the batch
-    // holds few tiles (decode_active_slices); n_slices is then the grid's (and workspace's) maximum.
-    int n_slices;
-    int slices_per_round;
+    // workgroup slots per group of 8 KV heads (a multiple of 8): the batch's units are cut into
+    // min(n_slots, units) slices of equal size, one per slot (decode_slices)
+    int n_slots;
     float scale;
     bool bf16;
     // paged cache (null block_table: contiguous rows addressed by kv_start). Request b's logical row
@@ -213,10 +211,10 @@ struct PrecomputePlan {
 };
 PrecomputePlan plan_precompute(int64_t T, int d_model, int NR, bool bf16);
 
-// slices of a decode launch: about keys_per_split keys each at full lengths, or (0) the library's
-// choice (at most two rounds of one 8-wave workgroup per CU); 0 when there is nothing to do, -1
-// when the sizes are too large. *per_round: slices of one round for the library's choice, else 0.
-int decode_slices(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* per_round = nullptr);
+// workgroup slots of a decode launch per group of 8 KV heads: one per about keys_per_split keys at
+// full lengths, or (0) the library's choice (one 8-wave workgroup per CU on 15/16 of the chip); 0
+// when there is nothing to do, -1 when the sizes are too large
+int decode_slots(int batch, int n_kv, int64_t max_kv_len, int keys_per_split);
 // 16-byte slots of one decode record block (one piece, one KV head, GP query heads; GP = the
 // group size rounded up to 4 or 8): O (d_head/16 * 4GP), O_lr (GP * rank/4), (m, l) (GP), padded to
 // a multiple of 16 slots (256 bytes)
@@ -225,18 +223,13 @@ inline int decode_record_slots(int G, int d_head, int rank) {
     return (GP * (d_head / 4 + rank / 4 + 1) + 15) / 16 * 16;
 }
 
-// the slices in use for a batch of U tiles (the kernels' rule; see decode.hip): never more than U,
-// so that every slice in use holds at least one tile
-__host__ __device__ inline int decode_active_slices(int U, int n_slices, int per_round) {
-    if (U <= 0) return 0;
-    int64_t n = n_slices;
-    if (per_round > 0) {
-        // two rounds when each workgroup still streams at least 48 tiles (1,536 keys) of its head,
-        // one round otherwise
-        n = int64_t(U) >= int64_t(48) * 2 * per_round ? 2 * per_round : per_round;
-        n = std::min<int64_t>(n, n_slices);
-    }
-    return int(std::min<int64_t>(n, U));
-}
+// The slices of a decode launch over the batch's U units (32-key tiles, request after request):
+// min(n_slots, U) slices, slice k starting at unit U*k/n (equal to within a unit), so every slice
+// holds at least one unit. A function of U and the slots alone, so the split kernel, the merge
+// kernel and the host agree. A slice holds at most one piece of each request it touches, and the
+// piece of request b in slice k has record block k + b.
+__host__ __device__ inline int decode_slices(int U, int n_slots) { return U < n_slots ? (U > 0 ? U : 0) : n_slots; }
+__host__ __device__ inline int slice_begin(int U, int k, int n) { return int(int64_t(U) * k / n); }
+__host__ __device__ inline int slice_owner(int U, int u, int n) { return int((int64_t(u + 1) * n - 1) / U); }
 
 }  // namespace lra

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lra.abi_version() == 7
+    assert lra.abi_version() == 8
     names = {s: lra.status_str(s) for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_INDEX, E_WS, E_HIP, -99)}
     assert names[OK] == "LRA_OK" and names[E_HIP] == "LRA_ERR_HIP" and names[-99] == "LRA_ERR_UNKNOWN"
 
@@ -105,11 +105,11 @@ def test_decode_qkvo_workspace_size():
     plain = lra.lra_attn_decode_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     need = lra.lra_attn_decode_qkvo_workspace_bytes(16, 32, 8, 128, 8, 66400, 0)
     assert need == (plain + 255) // 256 * 256 + 16 * 32 * 66432 * 4 + 16 * 32 * 1024 * 2 + 4150 * 32 * 128 + 16 * 130 * 4
-    # (8 slices + 2 requests) x 2 KV heads = 20 record blocks of 4 x (64/4 + 8/4 + 1) = 76 slots
-    # of 16 bytes, padded to 80, 2 x 4 x 64 fp32 scores, 2 x 4 x 512 fp16 weights,
+    # (2 slices (one per tile) + 2 requests) x 2 KV heads = 8 record blocks of 4 x (64/4 + 8/4 + 1)
+    # = 76 slots of 16 bytes, padded to 80, 2 x 4 x 64 fp32 scores, 2 x 4 x 512 fp16 weights,
     # 2 tiles of 16 steps x 128 bytes of repacked tables, 2 flags
     assert lra.lra_attn_decode_qkvo_workspace_bytes(2, 4, 2, 64, 8, 1, 64) == \
-        20 * 80 * 16 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
+        8 * 80 * 16 + 2 * 4 * 64 * 4 + 2 * 4 * 512 * 2 + 2 * 16 * 128 + 2 * 4
     assert decode_qkvo(ws=WS, ws_bytes=lra.lra_attn_decode_qkvo_workspace_bytes(2, 32, 8, 128, 8, 100, 0) - 1) == E_WS
     assert decode_qkvo(batch=0, Q=None, O=None) == OK
 
@@ -141,13 +141,12 @@ def test_decode_empty_batch_is_a_no_op():
 
 def test_decode_workspace_size_follows_slices():
     """The batch's 32-key tiles are cut into n slices (a multiple of 8): about keys_per_split keys
-    each at full lengths, or by default up to two rounds of 15/16 of the chip's 8-wave workgroup
-    slots (2 x 240 slices at n_kv = 8) and at most one slice per tile; the workspace holds the
-    grid's maximum. A slice
-    holds one piece of each request it touches, with its own record per query head: (n + batch) *
-    n_q records of (m, l) and (O, O_lr), in blocks per KV head."""
+    each at full lengths, or by default one round of 15/16 of the chip's 8-wave workgroup slots
+    (240 slices at n_kv <= 8, 120 per group of 8 KV heads at n_kv = 16), and at most one slice
+    per tile; the workspace holds the most that max_kv_len allows. A slice holds one piece of each
+    request it touches, with its own record per query head: (n + batch) * n_q records of (m, l)
+    and (O, O_lr), in blocks per KV head."""
     b, n_q, d, r = 16, 32, 128, 8
-    up = lambda v: -(-v // 256) * 256
 
     def layout(n_slices, batch=b, n_kv=8):
         # one block per (slice + request, KV head) of 16-byte slots: O (d/16 x 4 x 4
@@ -156,17 +155,16 @@ def test_decode_workspace_size_follows_slices():
         slots = -(-gp * (d // 4 + r // 4 + 1) // 16) * 16   # padded to whole 256-byte runs
         return (n_slices + batch) * n_kv * slots * 16
 
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(480)
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 4, d, r, 66400, 0) == layout(960, n_kv=4)   # 1920 waves / 4 heads (group of 8)
-    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 16, d, r, 66400, 0) == layout(240, n_kv=16)   # two workgroups per slice (group of 2)
-    assert lra.lra_attn_decode_workspace_bytes(1, n_q, 8, d, r, 1900, 0) == layout(64, 1)   # 60 tiles -> 64 slices
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 0) == layout(240)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 4, d, r, 66400, 0) == layout(240, n_kv=4)
+    assert lra.lra_attn_decode_workspace_bytes(b, n_q, 16, d, r, 66400, 0) == layout(120, n_kv=16)
+    assert lra.lra_attn_decode_workspace_bytes(1, n_q, 8, d, r, 1900, 0) == layout(60, 1)   # 60 tiles: one each
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 66400, 1024) == layout(1040)   # ceil(16 * 66400 / 1024) = 1038 -> 1040
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 0, 0) == 0
     assert lra.lra_attn_decode_workspace_bytes(b, n_q, 8, d, r, 100, 65) == 0
-    # the default keys per slice at full lengths: 16 x 66,400 keys (33,200 tiles, at least 48 per
-    # slice at two rounds) over 480 slices; 4 x 66,400 (8,300 tiles) over one round of 240; one
-    # 1,900-key request (60 tiles) over 60 slices of one tile each
-    assert lra.lra_attn_decode_default_split(16, 8, 66400) == 2240   # 2,213.3 rounded up to a multiple of 64
+    # the default keys per slice at full lengths: 16 x 66,400 keys over 240 slices; 4 x 66,400
+    # over 240; one 1,900-key request (60 tiles) over 60 slices of one tile each
+    assert lra.lra_attn_decode_default_split(16, 8, 66400) == 4480   # 4,426.7 rounded up to a multiple of 64
     assert lra.lra_attn_decode_default_split(4, 8, 66400) == 1152    # 1,106.7 -> 1,152
     assert lra.lra_attn_decode_default_split(1, 8, 1900) == 64
     assert lra.lra_attn_decode_default_split(1, 1, 1900) == 64

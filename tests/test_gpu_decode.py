@@ -201,6 +201,22 @@ def test_ministral_layer_decode_full_size():
 
 
 
+@pytest.mark.parametrize("n_kv", [4, 12, 16])
+def test_decode_long_batches_every_head_group(n_kv):
+    """The library's split of long batches (8-16 slices per request) for KV head counts that
+    leave waves of a workgroup without a head (4, 12) and that need two head groups (12, 16), with
+    empty, adapter-free and one-tile requests between long ones."""
+    s = W.Shape(n_q=2 * n_kv, n_kv=n_kv, d_head=64, rank=8, n_agents=3, d_model=256, dtype="bf16")
+    long = 16000 if n_kv == 4 else 8200   # 4,006 tiles over 240 slices; 2,062 over 120
+    lens = [long] * 7 + [1, 0, 33] + [long + 96]
+    agents = [0, 1, 2, -1, 0, 1, 2, 1, 0, 2, 1]
+    c = W.random_decode((940, n_kv), s, lens, agents=agents)
+    say(f"decode long batch n_kv={n_kv}")
+    got = run_decode(c)
+    for b in range(c.batch):
+        check(got[b:b + 1], ref_decode(c, requests=[b]), "bf16", f"n_kv={n_kv} request {b}")
+    assert np.all(got[8] == 0.0)
+
 # ------------------------------------------------------------------------------ paged cache
 def run_decode_paged(c: W.PagedDecodeBatch, keys_per_split=0, max_kv_len=None):
     s = c.shape
@@ -527,6 +543,7 @@ def test_decode_workspace_shared_across_shapes_needs_no_initialisation():
         W.random_decode((930,), s, kv_lens=[40], agents=[1]),
         W.random_decode((931,), s, kv_lens=[2000, 3, 0, 1700, 64], agents=[0, 2, 1, -1, 1]),
         W.random_decode((932,), s, kv_lens=[900] * 24 + [33, 4100], agents=[b % 3 for b in range(26)]),
+        W.random_decode((935,), s, kv_lens=[5000] * 24 + [70, 4100], agents=[b % 3 for b in range(26)]),
         W.random_decode((933,), s, kv_lens=[1], agents=[2]),
     ]
     need = max(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len, kps)

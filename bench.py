@@ -533,6 +533,31 @@ def bench_copy(args, torch, lra, W, out):
     torch.cuda.empty_cache()
 
 
+def bench_stream_read(args, torch, lra, W, out):
+    """The read bandwidth a plain streaming kernel reaches (lra_stream_read over 4 GiB, the size of
+    the 16 x 66,400 caches): the practical ceiling of the decode, a read-only stream of the caches.
+    The headline's roofline reports its fraction of this figure beside the fraction of the
+    published peak."""
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.int32, device="cuda")
+    best = None
+    for n_wg in (256, 2048):
+        ms = time_launches(lambda: lra.lra_stream_read(x, n_wg), 20, 3, torch)
+        if best is None or ms < best[0]:
+            best = (ms, n_wg)
+    ms, n_wg = best
+    gbs = 4 * n / (ms * 1e-3) / 1e9
+    out["stream_read_4GiB"] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "bytes": 4 * n, "n_workgroups": n_wg,
+                               "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "kernel": "lra_stream_read (16-byte loads, 8 in flight per lane, 8 waves per workgroup)"}
+    head = out.get("headline")
+    if head:
+        head["roofline"]["practical_peak"] = round(gbs, 1)
+        head["roofline"]["frac_of_practical_peak"] = round(head["gbs"] / gbs, 4)
+    del x
+    torch.cuda.empty_cache()
+
+
 def bench_short_decode(args, torch, lra, W, out):
     """One request over 1,900 keys (7.8 MB): latency-bound; caches rotate over 64 copies."""
     c = W.llama_decode()
@@ -765,7 +790,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", nargs="*", default=None,
-                    choices=["decode", "prefill", "precompute", "short", "ministral", "copy", "cpu"])
+                    choices=["decode", "prefill", "precompute", "short", "ministral", "copy", "read", "cpu"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--oracle-budget", type=float, default=2.0,
                     help="seconds of oracle work timed beside each other line (0: none)")
@@ -783,12 +808,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     only = set(args.only) if args.only is not None else {"decode", "prefill", "precompute", "short", "ministral", "copy",
-                                                          "cpu"}
+                                                          "read", "cpu"}
     out = {}
     if "decode" in only or "cpu" in only:
         bench_long_decode(args, torch, lra, W, out)
     for name, fn in (("prefill", bench_prefill), ("precompute", bench_precompute), ("short", bench_short_decode),
-                     ("ministral", bench_ministral_step), ("copy", bench_copy)):
+                     ("ministral", bench_ministral_step), ("copy", bench_copy), ("read", bench_stream_read)):
         if name in only:
             log(f"[bench] {name}")
             fn(args, torch, lra, W, out)

@@ -63,7 +63,8 @@ extern "C" {
                                    changed); the LR precompute needs no workspace;
                                    lra_attn_decode_step;
                                 8: one round of decode workgroups, each streaming its slice as
-                                   one sequence of tiles (workspace sizes changed) */
+                                   one sequence of tiles (workspace sizes changed);
+                                   lra_stream_read */
 
 typedef enum {
     LRA_OK = 0,
@@ -490,6 +491,18 @@ int lra_expand_values(int dtype, const void* V_base, int64_t kv_rows, const void
                       int32_t batch, const int64_t* src_start, const int32_t* len,
                       const int32_t* agent, int64_t max_len,
                       void* V_out, int64_t out_rows, const int64_t* dst_start, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Measurement helper: reads bytes of device memory at x with 16-byte loads, one contiguous chunk of
+ * bytes / n_workgroups per 8-wave workgroup, and writes the XOR fold of chunk w's 32-bit words to
+ * out[w]. Timed, it gives the read bandwidth a plain streaming kernel reaches on this GPU: the
+ * practical ceiling for the decode, whose work is a read-only stream of the caches.
+ *
+ * x        (device) bytes bytes, 16-byte aligned; bytes a positive multiple of 16 * n_workgroups
+ * out      (device) [n_workgroups] uint32
+ * n_workgroups in [1, 2^20]. Errors: LRA_ERR_NULL, LRA_ERR_SHAPE; nothing is enqueued then.
+ */
+int lra_stream_read(const void* x, int64_t bytes, int32_t n_workgroups, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

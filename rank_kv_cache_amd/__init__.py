@@ -25,7 +25,7 @@ __all__ = [
     "lra_attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "lra_attn_decode_step",
     "lra_attn_decode_qkvo", "lra_attn_decode_qkvo_workspace_bytes",
     "lra_attn_decode_paged", "lra_attn_decode_paged_default_split", "lra_attn_decode_paged_strided",
-    "lra_expand_values",
+    "lra_expand_values", "lra_stream_read",
     "LRA_F32", "LRA_BF16", "ADAPTER_FREE", "EXPORTED_SYMBOLS",
 ]
 
@@ -77,6 +77,7 @@ _SIGNATURES = {
                                                  _p, _sz, _p, _p]),
     "lra_expand_values": (_c.c_int, [_c.c_int, _p, _i64, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p,
                                      _i64, _p, _i64, _p, _p]),
+    "lra_stream_read": (_c.c_int, [_p, _i64, _i32, _p, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -746,3 +747,19 @@ def lra_attn_decode_paged_strided(Q: torch.Tensor, K_pages: torch.Tensor, V_page
         block_table.shape[1], _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank, scale,
         keys_per_split, _ptr(workspace), workspace.numel(), _ptr(O), _stream(stream)), "lra_attn_decode_paged_strided")
     return O
+
+
+def lra_stream_read(x: torch.Tensor, n_workgroups: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Reads all of the contiguous device tensor ``x`` (16-byte aligned, a multiple of
+    16 * n_workgroups bytes) in n_workgroups contiguous chunks and returns the XOR fold of each
+    chunk's 32-bit words (uint32 viewed as int32, [n_workgroups]): a measurement of the streaming
+    read bandwidth, the practical ceiling for the decode."""
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    nbytes = x.numel() * x.element_size()
+    if out is None:
+        with _on(stream):
+            out = torch.empty(n_workgroups, dtype=torch.int32, device=x.device)
+    _on_device(x, out=out)
+    _check(_lib.lra_stream_read(_ptr(x), nbytes, n_workgroups, _ptr(out), _stream(stream)), "lra_stream_read")
+    return out

@@ -22,7 +22,8 @@ LIB_NAME = "liblra.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "key_expand.hip", "key_scores.hip", "precompute.hip", "prefill.hip", "value_expand.hip"]
+SOURCES = ["api.hip", "decode.hip", "key_expand.hip", "key_scores.hip", "precompute.hip", "prefill.hip", "read_probe.hip",
+           "value_expand.hip"]
 # per-source flags: the prefill kernel takes row maxima of matrix-core outputs, which are never
 # signalling NaNs; without this the compiler quiets every input of every max first
 SOURCE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}

@@ -647,6 +647,16 @@ int scratch_on_current_device(void** out) {
 
 }  // namespace
 
+LRA_EXPORT int lra_stream_read(const void* x, int64_t bytes, int32_t n_workgroups, uint32_t* out, void* stream) {
+    if (!x || !out) return fail(LRA_ERR_NULL, "x and out must not be NULL");
+    if (!aligned(x, 16)) return fail(LRA_ERR_SHAPE, "x must be 16-byte aligned");
+    if (n_workgroups < 1 || n_workgroups > (1 << 20))
+        return fail(LRA_ERR_SHAPE, "n_workgroups=%d must be in [1, 2^20]", n_workgroups);
+    if (bytes <= 0 || bytes % (int64_t(16) * n_workgroups) != 0)
+        return fail(LRA_ERR_SHAPE, "bytes=%lld must be a positive multiple of 16 x n_workgroups", (long long)bytes);
+    return hip_status(lra::launch_read_probe(x, bytes, n_workgroups, out, static_cast<hipStream_t>(stream)), "lra_stream_read launch");
+}
+
 LRA_EXPORT int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
                                        const void* K_base, const void* V_base, int64_t kv_rows,
                                        const void* V_lr, int64_t ld_vlr,

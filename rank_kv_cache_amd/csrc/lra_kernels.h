@@ -200,6 +200,8 @@ inline int key_score_heads(int d_head, int rank) { return d_head * rank <= 1024 
 int prefill_pairs(int64_t L_C, int G);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// streaming-read probe: n_workgroups chunks of bytes / n_workgroups bytes, one XOR fold per chunk
+hipError_t launch_read_probe(const void* x, int64_t bytes, int n_workgroups, uint32_t* out, hipStream_t stream);
 hipError_t launch_precompute(const PrecomputeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 

@@ -462,3 +462,12 @@ def test_binding_rejects_host_tensors_before_any_launch():
         lra.lra_attn_prefill(Q, 8, K, K, Vlr, B, 0, 0.125)
     with pytest.raises(ValueError, match="GPU"):
         lra.lra_lr_precompute(torch.zeros(4, 64), torch.zeros(24, 64), 3, 8, Vlr)
+
+
+@pytest.mark.parametrize("x,nbytes,n_wg,out,status", [
+    (None, 1 << 20, 16, P, E_NULL), (P, 1 << 20, 16, None, E_NULL), (P + 8, 1 << 20, 16, P, E_SHAPE),
+    (P, 1 << 20, 0, P, E_SHAPE), (P, 1 << 20, (1 << 20) + 1, P, E_SHAPE), (P, 0, 16, P, E_SHAPE),
+    (P, (1 << 20) + 16, 16, P, E_SHAPE), (P, 16 * 15, 16, P, E_SHAPE),
+])
+def test_stream_read_rejects_bad_arguments(x, nbytes, n_wg, out, status):
+    assert lra._lib.lra_stream_read(x, nbytes, n_wg, out, 0) == status

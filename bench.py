@@ -167,6 +167,12 @@ def upload(t, torch):
     return torch.from_numpy(np.ascontiguousarray(t.data)).cuda()
 
 
+def agent_major(L, n_agents: int, rank: int):
+    """[rows, N*r] LR cache (agent k in columns k*r .. k*r + r - 1) -> [N, rows, r], each agent's rows
+    contiguous: a request then reads whole cache lines of its own agent's values only."""
+    return L.view(L.shape[0], n_agents, rank).permute(1, 0, 2).contiguous()
+
+
 def bench_long_decode(args, torch, lra, W, out):
     log("[bench] decode 16 x 66400: generating inputs")
     c = W.llama_long_decode()
@@ -178,17 +184,23 @@ def bench_long_decode(args, torch, lra, W, out):
     ws = torch.zeros(lra.lra_attn_decode_workspace_bytes(c.batch, s.n_q, s.n_kv, s.d_head, s.rank, c.max_kv_len),
                      dtype=torch.uint8, device="cuda")
     O = torch.empty_like(Q)
+    L_am = agent_major(L, s.n_agents, s.rank)
 
     def step():
+        lra.lra_attn_decode(Q, K, V, L_am, ks, kl, c.max_kv_len, B, ag, s.scale, 0, ws, O)
+
+    def step_interleaved():
         lra.lra_attn_decode(Q, K, V, L, ks, kl, c.max_kv_len, B, ag, s.scale, 0, ws, O)
 
     log(f"[bench] decode 16 x 66400: {args.warmup} warmup + {args.steps} timed steps")
     ms = time_launches(step, args.steps, args.warmup, torch)
+    # (not in a counter run of the headline launch alone, which must count one variant)
+    ms_i = None if args.headline_only else time_launches(step_interleaved, args.steps, args.warmup, torch)
     nbytes = decode_bytes(c.kv_len, c.agent, s.n_q, s.n_kv, s.d_head, s.rank)
     gbs = nbytes / (ms * 1e-3) / 1e9
     traffic, src = counter_traffic("decode_16x66400_counters.txt", DECODE_SOURCES)
     out["headline"] = {
-        "ms_per_step": ms, "gbs": gbs, "bytes": nbytes,
+        "ms_per_step": ms, "gbs": gbs, "bytes": nbytes, "ms_interleaved_lr_cache": None if ms_i is None else round(ms_i, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "lra_attn_decode = decode_split_kernel<bf16,128,8,4,false,false> + decode_combine_kernel<bf16,128,8,4,false>",
@@ -197,11 +209,11 @@ def bench_long_decode(args, torch, lra, W, out):
         "config": {"workload": W.WORKLOAD_NAMES[W.LLAMA_LONG_DECODE], "batch": c.batch, "kv_len": int(c.kv_len[0]),
                    "n_q": s.n_q, "n_kv": s.n_kv, "d_head": s.d_head, "rank": s.rank, "n_agents": s.n_agents,
                    "keys_per_split": lra.lra_attn_decode_default_split(c.batch, s.n_kv, c.max_kv_len),
-                   "parallelism": "none"},
+                   "lr_cache": "agent-major [n_agents, rows, rank]", "parallelism": "none"},
     }
     out["_long_decode_case"] = c
     if args.headline_only:   # the headline launch alone (for counter runs that must not mix variants)
-        del Q, K, V, L, B, O, ws
+        del Q, K, V, L, L_am, B, O, ws
         torch.cuda.empty_cache()
         return
 
@@ -210,7 +222,7 @@ def bench_long_decode(args, torch, lra, W, out):
     ag_dual[1::2] = -1
 
     def step_dual():
-        lra.lra_attn_decode(Q, K, V, L, ks, kl, c.max_kv_len, B, ag_dual, s.scale, 0, ws, O)
+        lra.lra_attn_decode(Q, K, V, L_am, ks, kl, c.max_kv_len, B, ag_dual, s.scale, 0, ws, O)
 
     ms_d = time_launches(step_dual, args.steps, args.warmup, torch)
     adapted = [int(a) for a in c.agent[0::2]]
@@ -604,7 +616,9 @@ def bench_ministral_step(args, torch, lra, W, out):
     timed as one lra_attn_decode_step per layer and, beside it, as lra_lr_precompute + lra_attn_decode.
     Layer caches are drawn on the GPU (workloads.ministral_layer_device, seeded torch generator) to
     keep set-up to seconds; a GPU parity test checks layer 0 of these exact inputs against the
-    oracle, and the host streams with identical shapes feed the tests of layers 0, 3 and 35."""
+    oracle, and the host streams with identical shapes feed the tests of layers 0, 3 and 35. Each
+    layer's LR cache is kept agent-major ([N, rows, r]); the same step over the interleaved cache
+    ([rows, N*r], bit-identical outputs) is timed beside it."""
     s = W.MINISTRAL_SHAPE
     lens = W.ministral_lengths()
     agents = W.ministral_agents()
@@ -613,11 +627,12 @@ def bench_ministral_step(args, torch, lra, W, out):
         starts.append(starts[-1] + int(x))
     rows = int(sum(int(x) for x in lens))
     n_layers = W.MINISTRAL_LAYERS
-    layers = []
+    layers, inter = [], []   # per layer: the inputs with the agent-major LR cache; the interleaved cache
     log(f"[bench] ministral step: drawing {n_layers} layer caches ({rows} rows each) on the GPU")
     for layer in range(n_layers):
         d = W.ministral_layer_device(layer, torch)
-        layers.append((d["K"], d["V"], d["V_lr"], d["A"], d["B"], d["X"], d["Q"]))
+        layers.append((d["K"], d["V"], agent_major(d["V_lr"], s.n_agents, s.rank), d["A"], d["B"], d["X"], d["Q"]))
+        inter.append(d["V_lr"])
     ks = torch.as_tensor(starts, dtype=torch.int64).cuda()
     kl = torch.as_tensor(lens, dtype=torch.int32).cuda()
     ag = torch.as_tensor(agents, dtype=torch.int32).cuda()
@@ -639,10 +654,15 @@ def bench_ministral_step(args, torch, lra, W, out):
         for (K, V, L, A, B, X, Q) in layers:
             lra.lra_attn_decode_step(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, X, A, 0, ws_dec, O)
 
+    def step_interleaved():
+        for (K, V, _, A, B, X, Q), L in zip(layers, inter):
+            lra.lra_attn_decode_step(Q, K, V, L, ks, kl, max_len, B, ag, s.scale, X, A, 0, ws_dec, O)
+
     reps = max(3, args.steps // 10)
     ms_u = time_launches(step_unfused, reps, 1, torch)
     ms = time_launches(step, reps, 1, torch)
     ms_g = time_graph(step, 1, reps, torch)
+    ms_i = time_launches(step_interleaved, reps, 1, torch)
     # the step is 72 launches of 0.01-0.25 ms: the faster of the graph replay and the eager loop
     graph_best = ms_g is not None and ms_g <= ms
     best = ms_g if graph_best else ms
@@ -656,6 +676,8 @@ def bench_ministral_step(args, torch, lra, W, out):
                                          "timing": "HIP graph of one step" if graph_best else "eager launches",
                                          "call": "lra_attn_decode_step per layer (newest LR rows formed in the decode launch)",
                                          "ms_precompute_then_decode": round(ms_u, 3),
+                                         "lr_cache": "agent-major [n_agents, rows, rank] per layer",
+                                         "ms_eager_interleaved_lr_cache": round(ms_i, 3),
                                          "kv_rows_per_layer": rows, "min_len": int(min(lens)), "max_len": max_len,
                                          "inputs": "drawn on the GPU (torch generator, seeded per layer)"}
     if args.oracle_budget > 0:
@@ -663,7 +685,8 @@ def bench_ministral_step(args, torch, lra, W, out):
         # requests (cycling over the 32) until the budget is spent; bytes as the line counts them
         import numpy as np
         import oracle
-        K0, V0, L0, A0, B0, X0, Q0 = layers[0]
+        K0, V0, _, A0, B0, X0, Q0 = layers[0]
+        L0 = inter[0]   # the same values, [rows, N*r]
         hostf = lambda t: t.float().cpu().numpy().astype(np.float64)
         Xf, Af, Bf, Qf = hostf(X0), hostf(A0).T, hostf(B0), hostf(Q0)
         t0 = time.perf_counter()
@@ -686,6 +709,7 @@ def bench_ministral_step(args, torch, lra, W, out):
 
     # the same step with every layer's K and V kept head-major ([n_kv, rows, d]); same values, the
     # decode through lra_attn_decode_strided (bit-identical outputs)
+    del inter
     for i, (K, V, L, A, B, X, Q) in enumerate(layers):
         layers[i] = (K.transpose(0, 1).contiguous().transpose(0, 1), V.transpose(0, 1).contiguous().transpose(0, 1),
                      L, A, B, X, Q)

@@ -40,6 +40,16 @@
  *    adapter-free decode requests can share one launch.
  *  - Supported: d_head in {64, 128}; rank in {8, 16}; n_q % n_kv == 0 with
  *    group size n_q / n_kv in 1..8. Anything else returns LRA_ERR_UNSUPPORTED.
+ *  - The LR cache V_lr holds, for cache row t, agent k and rank column j, the
+ *    element at t * ld_vlr + k * vlr_agent_stride + j. Two layouts are accepted
+ *    where an entry point takes vlr_agent_stride: interleaved rows (each row
+ *    holds every agent's columns: vlr_agent_stride = rank, ld_vlr >= N*rank),
+ *    or agent-major (each agent's cache contiguous, [N x rows x ld_vlr] with
+ *    ld_vlr >= rank and vlr_agent_stride >= rows * ld_vlr). Both strides are
+ *    multiples of 8; anything else returns LRA_ERR_SHAPE. In the agent-major
+ *    layout a request reads only its own agent's bytes of each row. Entry
+ *    points without vlr_agent_stride (paged caches, lra_expand_values) take
+ *    interleaved rows.
  *
  * Names follow the pages: Q, K_base, V_base, V_lr, B_i, agent i, L_P (tokens
  * already cached), L_C (new tokens of the chunk), r (rank), N (agents).
@@ -64,7 +74,8 @@ extern "C" {
                                    lra_attn_decode_step;
                                 8: one round of decode workgroups, each streaming its slice as
                                    one sequence of tiles (workspace sizes changed);
-                                   lra_stream_read */
+                                   lra_stream_read; the LR cache's agent stride (vlr_agent_stride)
+                                   on every entry point over contiguous caches: agent-major caches */
 
 typedef enum {
     LRA_OK = 0,
@@ -94,7 +105,7 @@ const char* lra_last_error(void);
  * LR precompute (PReCache, PreLRShared: when a segment is first processed, every agent's
  * down-projection is applied to its hidden states; LRAgent method step (2): V_lr = X A, L x r).
  *
- *   V_lr[out_rows[t], k*rank + j] = sum_c X[t, c] * A[k*rank + j, c]    t < T, k < n_agents, j < rank
+ *   V_lr(row out_rows[t], agent k, column j) = sum_c X[t, c] * A[k*rank + j, c]    t < T, k < N, j < rank
  *
  * X        (device) [T x d_model], row stride ldx elements (ldx >= d_model, multiple of 8)
  * A        (device) [n_agents*rank x d_model] row-major: row k*rank + j holds column j of A_k,
@@ -102,22 +113,23 @@ const char* lra_last_error(void);
  *          transpose of the pages' side-by-side [A_1 .. A_N] ([d_model x n_agents*rank]): stored
  *          this way, both matrix-core operands (X rows and A rows) are contiguous along d_model,
  *          and it is the usual storage of LoRA down-projection weights.
- * V_lr     (device) [vlr_rows x ld_vlr] output cache (ld_vlr >= n_agents*rank); only columns
- *          0 .. n_agents*rank-1 of the addressed rows are written
+ * V_lr     (device) output cache of vlr_rows rows in either layout (conventions above; with the
+ *          agent-major one, vlr_agent_stride >= vlr_rows * ld_vlr); only the n_agents*rank
+ *          entries of the addressed rows are written
  * out_rows (device) [T] int64 destination row of each X row, or NULL for row t -> row t
  *          (then vlr_rows >= T is required)
  * workspace(device) lra_lr_precompute_workspace_bytes() bytes, which is 0: the reduction over
  *          d_model finishes inside one launch. workspace may be NULL; the argument is kept so
  *          that a later kernel may use scratch without changing the call.
- * T = 0 is allowed and enqueues nothing. d_model must be a multiple of 32; ld_vlr a multiple of 8.
+ * T = 0 is allowed and enqueues nothing. d_model must be a multiple of 32.
  * Every tensor pointer must be 16-byte aligned.
  */
 size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, int32_t n_agents, int32_t rank);
 
 int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
                       const void* A, int32_t n_agents, int32_t rank,
-                      void* V_lr, int64_t ld_vlr, int64_t vlr_rows, const int64_t* out_rows,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride, int64_t vlr_rows,
+                      const int64_t* out_rows, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Causal chunked prefill for one agent (LRAgent method steps (3)-(4); PReCache: the new chunk of
@@ -130,7 +142,7 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * Q        (device) [L_C x n_q x d_head]
  * K_base   (device) [L_P+L_C x n_kv x d_head]    (rows 0 .. L_P+L_C-1 are read)
  * V_base   (device) [L_P+L_C x n_kv x d_head]
- * V_lr     (device) [L_P+L_C x ld_vlr], agent a owns columns a*rank .. a*rank+rank-1
+ * V_lr     (device) L_P+L_C rows in either layout (conventions above; rows = L_P+L_C)
  * B        (device) [n_agents x rank x n_kv*d_head]: B_a, one r x (n_kv*d_head) matrix per agent
  * agent    (host) in [0, n_agents), or -1 for the adapter-free view (V_lr and B are not read);
  *          anything else returns LRA_ERR_INDEX
@@ -141,11 +153,11 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * its rows with bf16 V_base / V_lr (scaled by a power of two when huge) and the probabilities split
  * into two bf16 parts, so every finite input is accepted. l, m, O and O_lr are fp32; scores and the
  * unnormalised sums must stay finite in fp32.
- * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. L_C = 0 enqueues nothing.
+ * Every tensor pointer must be 16-byte aligned. L_C = 0 enqueues nothing.
  */
 int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
-                     const void* B, int32_t n_agents, int32_t agent,
+                     int64_t vlr_agent_stride, const void* B, int32_t n_agents, int32_t agent,
                      int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                      void* O, void* stream);
 
@@ -181,7 +193,7 @@ size_t lra_attn_prefill_qkvo_workspace_bytes(int64_t n_rows, int32_t n_kv, int32
 
 int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                           const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
-                          const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
+                          int64_t vlr_agent_stride, const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
                           const float* rope_cos, const float* rope_sin, int32_t n_agents, int32_t agent,
                           int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                           void* workspace, size_t workspace_bytes, void* O, void* stream);
@@ -200,19 +212,19 @@ int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * Q, O     (device) [q_rows x n_q x d_head]; rows no request covers are not written
  * q_start  (device) [batch] int64, q_len (device) [batch] int32
  * max_q_len (host) an upper bound on every q_len[b]; it sizes the launch
- * K_base, V_base (device) [kv_rows x n_kv x d_head]; V_lr (device) [kv_rows x ld_vlr]
+ * K_base, V_base (device) [kv_rows x n_kv x d_head]; V_lr (device) kv_rows rows in either layout
  * kv_start (device) [batch] int64, kv_prefix (device) [batch] int32, agent (device) [batch] int32
  * B        (device) [n_agents x rank x n_kv*d_head]
  * A request with q_len[b] = 0 writes nothing; one whose query rows fall outside [0, q_rows) is
  * skipped. One with q_len[b] > max_q_len, a cache range outside [0, kv_rows), kv_prefix[b]+q_len[b]
  * >= 2^31 or an agent outside [-1, n_agents) gets NaN in all its output rows. Precision (with the
- * range-safe recomputation), alignment and ld_vlr are as for lra_attn_prefill.
+ * range-safe recomputation) and alignment are as for lra_attn_prefill.
  * batch = 0 or max_q_len = 0 enqueues nothing.
  */
 int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,
                             const int64_t* q_start, const int32_t* q_len, int64_t max_q_len,
                             const void* K_base, const void* V_base, int64_t kv_rows,
-                            const void* V_lr, int64_t ld_vlr,
+                            const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                             const int64_t* kv_start, const int32_t* kv_prefix,
                             const void* B, int32_t n_agents, const int32_t* agent,
                             int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -253,7 +265,7 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  *
  * Q        (device) [batch x n_q x d_head]
  * K_base, V_base (device) [kv_rows x n_kv x d_head]
- * V_lr     (device) [kv_rows x ld_vlr]
+ * V_lr     (device) kv_rows rows in either layout (conventions above)
  * kv_start (device) [batch] int64, kv_len (device) [batch] int32, agent (device) [batch] int32:
  *          agent[b] in [0, n_agents), or -1 for the adapter-free view (B is not read; the split
  *          kernel streams agent 0's V_lr columns of the range and the merge drops that product)
@@ -267,7 +279,7 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
  *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output
- * ld_vlr must be a multiple of 8 and every tensor pointer 16-byte aligned. batch = 0 enqueues
+ * Every tensor pointer must be 16-byte aligned. batch = 0 enqueues
  * nothing. The workspace size is 0 when no request can have a key (max_kv_len = 0); the call then
  * only writes the zero and NaN rows.
  */
@@ -276,7 +288,7 @@ size_t lra_attn_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t n_kv,
 
 int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                     const void* K_base, const void* V_base, int64_t kv_rows,
-                    const void* V_lr, int64_t ld_vlr,
+                    const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                     const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                     const void* B, int32_t n_agents, const int32_t* agent,
                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -289,7 +301,7 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
  * down-projection once; LRAgent method steps (2)-(4)). For every request b with kv_len[b] > 0 and a
  * valid range and agent, the newest key is cache row n_b = kv_start[b] + kv_len[b] - 1, and
  *
- *   V_lr[n_b, k*rank + j] = sum_c X_new[b, c] * A[k*rank + j, c]      (k < n_agents, j < rank)
+ *   V_lr(row n_b, agent k, column j) = sum_c X_new[b, c] * A[k*rank + j, c]      (k < n_agents, j < rank)
  *
  * is written into the cache (rounded once to the element type), then the decode runs as
  * lra_attn_decode over all kv_len[b] keys, that row included. This is lra_lr_precompute with
@@ -309,7 +321,7 @@ int lra_attn_decode(int dtype, const void* Q, int32_t batch,
  */
 int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
                          const void* K_base, const void* V_base, int64_t kv_rows,
-                         void* V_lr, int64_t ld_vlr,
+                         void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                          const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                          const void* B, int32_t n_agents, const int32_t* agent,
                          int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -334,7 +346,7 @@ int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
 int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
                             const void* K_base, const void* V_base, int64_t kv_rows,
                             int64_t kv_row_stride, int64_t kv_head_stride,
-                            const void* V_lr, int64_t ld_vlr,
+                            const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                             const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                             const void* B, int32_t n_agents, const int32_t* agent,
                             int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -360,7 +372,7 @@ int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
 
 int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
                             const void* K_base, const void* V_base, int64_t kv_rows,
-                            const void* V_lr, int64_t ld_vlr,
+                            const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                             const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                             const void* B, int32_t n_agents, const int32_t* agent,
                             int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -395,7 +407,8 @@ size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_q, int32_t 
 
 int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                          const void* K_base, const void* V_base, int64_t kv_rows,
-                         const void* V_lr, int64_t ld_vlr, const void* K_lr, int64_t ld_klr,
+                         const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
+                         const void* K_lr, int64_t ld_klr,
                          const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                          const void* B, const void* B_k, const float* rope_cos, const float* rope_sin,
                          int32_t n_agents, const int32_t* agent,

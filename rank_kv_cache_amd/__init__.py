@@ -45,30 +45,30 @@ _SIGNATURES = {
     "lra_status_str": (_c.c_char_p, [_c.c_int]),
     "lra_last_error": (_c.c_char_p, []),
     "lra_lr_precompute_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
-    "lra_lr_precompute": (_c.c_int, [_c.c_int, _p, _i64, _i32, _i64, _p, _i32, _i32, _p, _i64, _i64, _p,
-                                     _p, _sz, _p]),
-    "lra_attn_prefill": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
-                                    _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_lr_precompute": (_c.c_int, [_c.c_int, _p, _i64, _i32, _i64, _p, _i32, _i32, _p, _i64, _i64, _i64, _p, _p,
+                                     _sz, _p]),
+    "lra_attn_prefill": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _f, _p, _p]),
     "lra_attn_prefill_qkvo_workspace_bytes": (_sz, [_i64, _i32, _i32]),
-    "lra_attn_prefill_qkvo": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p, _p, _p, _p,
+    "lra_attn_prefill_qkvo": (_c.c_int, [_c.c_int, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _f, _p, _sz, _p, _p]),
-    "lra_attn_prefill_varlen": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _i64, _p, _i64, _p, _p,
-                                           _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
+    "lra_attn_prefill_varlen": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _i64, _p, _i64, _i64, _p,
+                                           _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_prefill_paged": (_c.c_int, [_c.c_int, _p, _i64, _i32, _p, _p, _i64, _p, _p, _p, _i64, _i32, _i64, _p,
                                           _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _p, _p]),
     "lra_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
-    "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
+    "lra_attn_decode": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _p,
                                    _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_default_split": (_i32, [_i32, _i32, _i64]),
-    "lra_attn_decode_step": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
+    "lra_attn_decode_step": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _p,
                                         _i32, _i32, _i32, _i32, _f, _p, _i64, _p, _i32, _i32, _p, _sz, _p, _p]),
-    "lra_attn_decode_noalloc": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _p,
-                                           _i32, _i32, _i32, _i32, _f, _i32, _p, _p]),
-    "lra_attn_decode_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p,
-                                           _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
+    "lra_attn_decode_noalloc": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _p, _i32,
+                                           _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _p]),
+    "lra_attn_decode_strided": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _i64, _i64, _p, _i64, _i64, _p, _p,
+                                           _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_qkvo_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i64, _i32]),
-    "lra_attn_decode_qkvo": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p,
-                                        _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
+    "lra_attn_decode_qkvo": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _p, _i64, _p,
+                                        _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged": (_c.c_int, [_c.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _i64, _p, _i32, _p, _i64, _p, _i32,
                                          _p, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz, _p, _p]),
     "lra_attn_decode_paged_default_split": (_i32, [_i32, _i32, _i64, _i32]),
@@ -160,6 +160,23 @@ def _rows_dense(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
 
 
+def _vlr_check(name: str, t: torch.Tensor) -> None:
+    """An LR cache: [rows, ld] with interleaved agents, or an agent-major [N, rows, ld] view."""
+    if not ((t.dim() == 2 and t.stride(1) == 1) or (t.dim() == 3 and t.stride(2) == 1)):
+        raise ValueError(f"{name} must be [rows, ld] (interleaved agents) or [N, rows, ld] (agent-major), unit column stride")
+
+
+def _vlr_rows(t: torch.Tensor) -> int:
+    return t.shape[-2]
+
+
+def _vlr_strides(t: torch.Tensor, rank: int) -> tuple:
+    """(ld_vlr, vlr_agent_stride) of an LR cache tensor."""
+    if t.dim() == 2:
+        return t.stride(0), rank
+    return t.stride(1), t.stride(0)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -193,7 +210,7 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
     _same(X, A, V_lr)
     _rows_dense("X", X)
     _dense("A", A)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     T, d_model = X.shape
     if A.shape != (n_agents * rank, d_model):
         raise ValueError(f"A has shape {tuple(A.shape)}, expected {(n_agents * rank, d_model)}")
@@ -207,7 +224,7 @@ def lra_lr_precompute(X: torch.Tensor, A: torch.Tensor, n_agents: int, rank: int
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _on_device(X, out_rows=out_rows, workspace=workspace)
     _check(_lib.lra_lr_precompute(_dtype_code(X), _ptr(X), T, d_model, X.stride(0), _ptr(A), n_agents, rank,
-                                  _ptr(V_lr), V_lr.stride(0), V_lr.shape[0], _ptr(out_rows),
+                                  _ptr(V_lr), *_vlr_strides(V_lr, rank), _vlr_rows(V_lr), _ptr(out_rows),
                                   _ptr(workspace), ws_bytes, _stream(stream)), "lra_lr_precompute")
     return V_lr
 
@@ -224,12 +241,12 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     L_C, n_q, d = Q.shape
     n_kv = K_base.shape[1]
     n_agents, rank = B.shape[0], B.shape[1]
     L = L_P + L_C
-    if K_base.shape[0] < L or V_base.shape[0] < L or V_lr.shape[0] < L:
+    if K_base.shape[0] < L or V_base.shape[0] < L or _vlr_rows(V_lr) < L:
         raise ValueError(f"caches hold fewer than L_P + L_C = {L} rows")
     if K_base.shape[1:] != (n_kv, d) or V_base.shape[1:] != (n_kv, d) or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/B shapes disagree with Q")
@@ -239,7 +256,7 @@ def lra_attn_prefill(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_base: to
     _same(Q, O)
     _dense("O", O)
     _check(_lib.lra_attn_prefill(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
-                                 V_lr.stride(0), _ptr(B), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(O),
+                                 *_vlr_strides(V_lr, rank), _ptr(B), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(O),
                                  _stream(stream)), "lra_attn_prefill")
     return O
 
@@ -258,13 +275,13 @@ def lra_attn_prefill_qkvo(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_bas
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("B_k", B_k),
                     ("rope_cos", rope_cos), ("rope_sin", rope_sin)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     _rows_dense("K_lr", K_lr)
     L_C, n_q, d = Q.shape
     n_kv = K_base.shape[1]
     n_agents, rank = B.shape[0], B.shape[1]
     L = L_P + L_C
-    if min(K_base.shape[0], V_base.shape[0], V_lr.shape[0], K_lr.shape[0], rope_cos.shape[0], rope_sin.shape[0]) < L:
+    if min(K_base.shape[0], V_base.shape[0], _vlr_rows(V_lr), K_lr.shape[0], rope_cos.shape[0], rope_sin.shape[0]) < L:
         raise ValueError(f"caches and angle tables hold fewer than L_P + L_C = {L} rows")
     if K_base.shape[1:] != (n_kv, d) or V_base.shape[1:] != (n_kv, d) or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/B shapes disagree with Q")
@@ -286,7 +303,7 @@ def lra_attn_prefill_qkvo(Q: torch.Tensor, L_P: int, K_base: torch.Tensor, V_bas
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
     _on_device(Q, rope_cos=rope_cos, rope_sin=rope_sin, workspace=workspace)
     _check(_lib.lra_attn_prefill_qkvo(_dtype_code(Q), _ptr(Q), L_C, L_P, _ptr(K_base), _ptr(V_base), _ptr(V_lr),
-                                      V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(B), _ptr(B_k), _ptr(rope_cos),
+                                      *_vlr_strides(V_lr, rank), _ptr(K_lr), K_lr.stride(0), _ptr(B), _ptr(B_k), _ptr(rope_cos),
                                       _ptr(rope_sin), n_agents, agent, n_q, n_kv, d, rank, scale, _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _ptr(O), _stream(stream)),
            "lra_attn_prefill_qkvo")
@@ -311,13 +328,13 @@ def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     q_rows, n_q, d = Q.shape
     kv_rows, n_kv = K_base.shape[0], K_base.shape[1]
     n_agents, rank = B.shape[0], B.shape[1]
     if K_base.shape[1:] != (n_kv, d) or V_base.shape != K_base.shape or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/B shapes disagree with Q")
-    if V_lr.shape[0] != kv_rows:
+    if _vlr_rows(V_lr) != kv_rows:
         raise ValueError("V_lr must have as many rows as K_base")
     for name, t, dt in (("q_start", q_start, torch.int64), ("q_len", q_len, torch.int32),
                         ("kv_start", kv_start, torch.int64), ("kv_prefix", kv_prefix, torch.int32),
@@ -336,7 +353,7 @@ def lra_attn_prefill_varlen(Q: torch.Tensor, q_start: torch.Tensor, q_len: torch
         raise ValueError("O must have Q's shape")
     _on_device(Q, q_start=q_start, q_len=q_len, kv_start=kv_start, kv_prefix=kv_prefix, agent=agent)
     _check(_lib.lra_attn_prefill_varlen(_dtype_code(Q), _ptr(Q), q_rows, batch, _ptr(q_start), _ptr(q_len), max_q_len,
-                                        _ptr(K_base), _ptr(V_base), kv_rows, _ptr(V_lr), V_lr.stride(0),
+                                        _ptr(K_base), _ptr(V_base), kv_rows, _ptr(V_lr), *_vlr_strides(V_lr, rank),
                                         _ptr(kv_start), _ptr(kv_prefix), _ptr(B), n_agents, _ptr(agent),
                                         n_q, n_kv, d, rank, scale, _ptr(O), _stream(stream)),
            "lra_attn_prefill_varlen")
@@ -410,7 +427,7 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     batch, n_q, d = Q.shape
     n_kv = K_base.shape[1]
     n_agents, rank = B.shape[0], B.shape[1]
@@ -419,7 +436,7 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
     for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
         if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
             raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
-    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+    if V_base.shape != K_base.shape or _vlr_rows(V_lr) != K_base.shape[0] or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
@@ -433,7 +450,7 @@ def lra_attn_decode(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Tensor,
     _dense("O", O)
     _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
-                                _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                _ptr(V_lr), *_vlr_strides(V_lr, rank), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                 n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split,
                                 _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)), "lra_attn_decode")
     return O
@@ -450,7 +467,7 @@ def lra_attn_decode_step(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     _same(Q, K_base, V_base, V_lr, B, X_new, A)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("A", A)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     _rows_dense("X_new", X_new)
     batch, n_q, d = Q.shape
     n_kv = K_base.shape[1]
@@ -461,7 +478,7 @@ def lra_attn_decode_step(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
         if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
             raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
-    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+    if V_base.shape != K_base.shape or _vlr_rows(V_lr) != K_base.shape[0] or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     if X_new.shape[0] != batch or A.shape != (n_agents * rank, d_model):
         raise ValueError("X_new must be [batch, d_model] and A [n_agents*rank, d_model]")
@@ -477,7 +494,7 @@ def lra_attn_decode_step(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     _dense("O", O)
     _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_step(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
-                                     _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                     _ptr(V_lr), *_vlr_strides(V_lr, rank), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                      n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, _ptr(X_new), X_new.stride(0),
                                      _ptr(A), d_model, keys_per_split, _ptr(workspace), ws_bytes, _ptr(O),
                                      _stream(stream)), "lra_attn_decode_step")
@@ -494,7 +511,7 @@ def lra_attn_decode_noalloc(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
     _same(Q, K_base, V_base, V_lr, B, O)
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("O", O)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     batch, n_q, d = Q.shape
     n_kv = K_base.shape[1]
     n_agents, rank = B.shape[0], B.shape[1]
@@ -503,11 +520,11 @@ def lra_attn_decode_noalloc(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
     for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
         if t.numel() != batch:
             raise ValueError(f"{name} must have one entry per request")
-    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d or O.shape != Q.shape:
+    if V_base.shape != K_base.shape or _vlr_rows(V_lr) != K_base.shape[0] or B.shape[2] != n_kv * d or O.shape != Q.shape:
         raise ValueError("K_base/V_base/V_lr/B/O shapes disagree")
     _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent)
     _check(_lib.lra_attn_decode_noalloc(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
-                                        _ptr(V_lr), V_lr.stride(0), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
+                                        _ptr(V_lr), *_vlr_strides(V_lr, rank), _ptr(kv_start), _ptr(kv_len), max_kv_len, _ptr(B),
                                         n_agents, _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split, _ptr(O),
                                         _stream(stream)), "lra_attn_decode_noalloc")
     return O
@@ -524,7 +541,7 @@ def lra_attn_decode_strided(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
     _same(Q, K_base, V_base, V_lr, B)
     for name, t in (("Q", Q), ("B", B)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     if K_base.dim() != 3 or K_base.stride(2) != 1 or V_base.shape != K_base.shape or V_base.stride() != K_base.stride():
         raise ValueError("K_base and V_base must be [rows, n_kv, d] views with equal strides and unit last stride")
     batch, n_q, d = Q.shape
@@ -535,7 +552,7 @@ def lra_attn_decode_strided(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
     for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
         if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
             raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
-    if K_base.shape[2] != d or V_lr.shape[0] != K_base.shape[0] or B.shape[2] != n_kv * d:
+    if K_base.shape[2] != d or _vlr_rows(V_lr) != K_base.shape[0] or B.shape[2] != n_kv * d:
         raise ValueError("K_base/V_base/V_lr/B shapes disagree")
     need = lra_attn_decode_workspace_bytes(batch, n_q, n_kv, d, rank, max_kv_len, keys_per_split)
     if workspace is None and need:
@@ -549,7 +566,7 @@ def lra_attn_decode_strided(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch
     _dense("O", O)
     _on_device(Q, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_strided(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
-                                        K_base.stride(0), K_base.stride(1), _ptr(V_lr), V_lr.stride(0), _ptr(kv_start),
+                                        K_base.stride(0), K_base.stride(1), _ptr(V_lr), *_vlr_strides(V_lr, rank), _ptr(kv_start),
                                         _ptr(kv_len), max_kv_len, _ptr(B), n_agents, _ptr(agent), n_q, n_kv, d, rank,
                                         scale, keys_per_split, _ptr(workspace), ws_bytes, _ptr(O), _stream(stream)),
            "lra_attn_decode_strided")
@@ -575,7 +592,7 @@ def lra_attn_decode_qkvo(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     for name, t in (("Q", Q), ("K_base", K_base), ("V_base", V_base), ("B", B), ("B_k", B_k),
                     ("rope_cos", rope_cos), ("rope_sin", rope_sin)):
         _dense(name, t)
-    _rows_dense("V_lr", V_lr)
+    _vlr_check("V_lr", V_lr)
     _rows_dense("K_lr", K_lr)
     batch, n_q, d = Q.shape
     n_kv = K_base.shape[1]
@@ -585,7 +602,7 @@ def lra_attn_decode_qkvo(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     for name, t in (("kv_start", kv_start), ("kv_len", kv_len), ("agent", agent)):
         if t.numel() != batch or not t.is_contiguous() or t.device != Q.device:
             raise ValueError(f"{name} must be a contiguous device tensor with one entry per request")
-    if V_base.shape != K_base.shape or V_lr.shape[0] != K_base.shape[0] or K_lr.shape[0] != K_base.shape[0] \
+    if V_base.shape != K_base.shape or _vlr_rows(V_lr) != K_base.shape[0] or K_lr.shape[0] != K_base.shape[0] \
             or B.shape[2] != n_kv * d or B_k.shape != B.shape:
         raise ValueError("K_base/V_base/V_lr/K_lr/B/B_k shapes disagree")
     if rope_cos.dtype != torch.float32 or rope_sin.dtype != torch.float32 or rope_cos.device != Q.device \
@@ -606,7 +623,7 @@ def lra_attn_decode_qkvo(Q: torch.Tensor, K_base: torch.Tensor, V_base: torch.Te
     _dense("O", O)
     _on_device(Q, rope_cos=rope_cos, rope_sin=rope_sin, kv_start=kv_start, kv_len=kv_len, agent=agent, workspace=workspace)
     _check(_lib.lra_attn_decode_qkvo(_dtype_code(Q), _ptr(Q), batch, _ptr(K_base), _ptr(V_base), K_base.shape[0],
-                                     _ptr(V_lr), V_lr.stride(0), _ptr(K_lr), K_lr.stride(0), _ptr(kv_start), _ptr(kv_len),
+                                     _ptr(V_lr), *_vlr_strides(V_lr, rank), _ptr(K_lr), K_lr.stride(0), _ptr(kv_start), _ptr(kv_len),
                                      max_kv_len, _ptr(B), _ptr(B_k), _ptr(rope_cos), _ptr(rope_sin), n_agents,
                                      _ptr(agent), n_q, n_kv, d, rank, scale, keys_per_split, _ptr(workspace), ws_bytes,
                                      _ptr(O), _stream(stream)), "lra_attn_decode_qkvo")

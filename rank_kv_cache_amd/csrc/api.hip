@@ -37,6 +37,21 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// V_lr layouts: row r, agent a, rank column j at r * ld_vlr + a * vlr_agent_stride + j, either
+// interleaved (each row holds every agent's columns: vlr_agent_stride = rank, ld_vlr >=
+// n_agents * rank) or agent-major (each agent's rows contiguous: ld_vlr >= rank, vlr_agent_stride >=
+// rows * ld_vlr). Both strides are multiples of 8 elements (16-byte aligned runs).
+int check_vlr(int64_t ld_vlr, int64_t agent_stride, int64_t rows, int32_t n_agents, int32_t rank) {
+    const bool aligned8 = ld_vlr > 0 && agent_stride > 0 && ld_vlr % 8 == 0 && agent_stride % 8 == 0;
+    const bool interleaved = agent_stride == rank && ld_vlr >= int64_t(n_agents) * rank;
+    const bool agent_major = ld_vlr >= rank && agent_stride >= std::max<int64_t>(rows, 1) * ld_vlr;
+    if (!aligned8 || !(interleaved || agent_major))
+        return fail(LRA_ERR_SHAPE, "V_lr strides (ld_vlr=%lld, vlr_agent_stride=%lld) are neither interleaved (agent "
+                    "stride = rank, ld_vlr >= n_agents*rank) nor agent-major (ld_vlr >= rank, agent stride >= %lld "
+                    "rows x ld_vlr), or not multiples of 8", (long long)ld_vlr, (long long)agent_stride, (long long)rows);
+    return LRA_OK;
+}
+
 // -------------------------------------------------------------------------- decode workspace
 struct DecodeLayout {
     int n_slots;
@@ -102,8 +117,8 @@ LRA_EXPORT size_t lra_lr_precompute_workspace_bytes(int64_t T, int32_t d_model, 
 
 LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int64_t ldx,
                                  const void* A, int32_t n_agents, int32_t rank,
-                                 void* V_lr, int64_t ld_vlr, int64_t vlr_rows, const int64_t* out_rows,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride, int64_t vlr_rows,
+                                 const int64_t* out_rows, void* workspace, size_t workspace_bytes, void* stream) {
     (void)workspace; (void)workspace_bytes;
     if (int s = check_dtype(dtype)) return s;
     if (T < 0) return fail(LRA_ERR_SHAPE, "T=%lld is negative", (long long)T);
@@ -112,8 +127,8 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
     if (NR % 8 != 0 || NR > (1 << 20)) return fail(LRA_ERR_UNSUPPORTED, "n_agents*rank=%lld must be a multiple of 8", (long long)NR);
     if (d_model <= 0 || d_model % 32 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model=%d must be a positive multiple of 32", d_model);
     if (ldx < d_model || ldx % 8 != 0) return fail(LRA_ERR_SHAPE, "ldx=%lld must be >= d_model and a multiple of 8", (long long)ldx);
-    if (ld_vlr < NR || ld_vlr % 8 != 0) return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
     if (vlr_rows < 0) return fail(LRA_ERR_SHAPE, "vlr_rows is negative");
+    if (int s = check_vlr(ld_vlr, vlr_agent_stride, vlr_rows, n_agents, rank)) return s;
     if (!out_rows && vlr_rows < T) return fail(LRA_ERR_SHAPE, "vlr_rows=%lld < T=%lld with identity row map", (long long)vlr_rows, (long long)T);
     const lra::PrecomputePlan pl = lra::plan_precompute(T, d_model, int(NR), dtype == LRA_BF16);
     if (int64_t(pl.n_rg + 7) / 8 * 8 * pl.n_cg > INT32_MAX) return fail(LRA_ERR_SHAPE, "n_agents*rank too large for one launch");
@@ -123,8 +138,8 @@ LRA_EXPORT int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_
 
     lra::PrecomputeParams p{};
     p.X = X; p.A = A; p.Vlr = V_lr; p.out_rows = out_rows;
-    p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_rows = vlr_rows;
-    p.d_model = d_model; p.NR = int(NR);
+    p.T = T; p.ldx = ldx; p.ld_vlr = ld_vlr; p.vlr_agent_stride = vlr_agent_stride; p.vlr_rows = vlr_rows;
+    p.d_model = d_model; p.rank = rank; p.NR = int(NR);
     p.n_rg = pl.n_rg; p.n_cg = pl.n_cg; p.cols_per_group = pl.cols_per_group;
     p.bf16 = dtype == LRA_BF16;
     return hip_status(lra::launch_precompute(p, static_cast<hipStream_t>(stream)), "lra_lr_precompute launch");
@@ -159,7 +174,7 @@ KeyExpandLayout key_expand_layout(int64_t n_rows, int n_kv, int d_head) {
 }
 
 int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int64_t L_P,
-                   const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
+                   const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                    const void* B, int32_t n_agents, int32_t agent,
                    int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                    void* O, void* stream, const KeyLora* kl) {
@@ -171,8 +186,7 @@ int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int6
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
     if (agent < lra::kAdapterFree || agent >= n_agents)
         return fail(LRA_ERR_INDEX, "agent=%d outside [-1, %d)", agent, n_agents);
-    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
-        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (int s = check_vlr(ld_vlr, vlr_agent_stride, L_P + L_C, n_agents, rank)) return s;
     if (kl && (kl->ld_klr < int64_t(n_agents) * rank || kl->ld_klr % 8 != 0))
         return fail(LRA_ERR_SHAPE, "ld_klr=%lld must be >= n_agents*rank and a multiple of 8", (long long)kl->ld_klr);
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
@@ -194,7 +208,7 @@ int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int6
     }
     lra::PrefillParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B; p.O = O;
-    p.L_C = L_C; p.L_P = L_P; p.ld_vlr = ld_vlr;
+    p.L_C = L_C; p.L_P = L_P; p.ld_vlr = ld_vlr; p.vlr_agent_stride = vlr_agent_stride;
     p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.d_head = d_head; p.rank = rank;
     p.agent = agent; p.n_agents = n_agents; p.scale = scale; p.bf16 = dtype == LRA_BF16;
     p.batch = 1;
@@ -223,10 +237,10 @@ int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int6
 
 LRA_EXPORT int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                                 const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
-                                const void* B, int32_t n_agents, int32_t agent,
+                                int64_t vlr_agent_stride, const void* B, int32_t n_agents, int32_t agent,
                                 int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                                 void* O, void* stream) {
-    return prefill_single("lra_attn_prefill launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr, B,
+    return prefill_single("lra_attn_prefill launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr, vlr_agent_stride, B,
                           n_agents, agent, n_q, n_kv, d_head, rank, scale, O, stream, nullptr);
 }
 
@@ -237,19 +251,20 @@ LRA_EXPORT size_t lra_attn_prefill_qkvo_workspace_bytes(int64_t n_rows, int32_t 
 
 LRA_EXPORT int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                                      const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
-                                     const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
+                                     int64_t vlr_agent_stride, const void* K_lr, int64_t ld_klr, const void* B, const void* B_k,
                                      const float* rope_cos, const float* rope_sin, int32_t n_agents, int32_t agent,
                                      int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                                      void* workspace, size_t workspace_bytes, void* O, void* stream) {
     const KeyLora kl{K_lr, ld_klr, B_k, rope_cos, rope_sin, workspace, workspace_bytes};
-    return prefill_single("lra_attn_prefill_qkvo launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr, B,
+    return prefill_single("lra_attn_prefill_qkvo launch", dtype, Q, L_C, L_P, K_base, V_base, V_lr, ld_vlr,
+                          vlr_agent_stride, B,
                           n_agents, agent, n_q, n_kv, d_head, rank, scale, O, stream, &kl);
 }
 
 LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,
                                        const int64_t* q_start, const int32_t* q_len, int64_t max_q_len,
                                        const void* K_base, const void* V_base, int64_t kv_rows,
-                                       const void* V_lr, int64_t ld_vlr,
+                                       const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                                        const int64_t* kv_start, const int32_t* kv_prefix,
                                        const void* B, int32_t n_agents, const int32_t* agent,
                                        int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -260,8 +275,7 @@ LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows,
         return fail(LRA_ERR_SHAPE, "batch, q_rows, kv_rows and max_q_len must be >= 0");
     if (max_q_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_q_len exceeds 2^31 - 1");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
-    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
-        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (int s = check_vlr(ld_vlr, vlr_agent_stride, kv_rows, n_agents, rank)) return s;
     if (!(std::isfinite(scale) && scale > 0.f)) return fail(LRA_ERR_SHAPE, "scale must be positive and finite");
     if (batch == 0 || max_q_len == 0) return LRA_OK;
     if (!Q || !K_base || !V_base || !V_lr || !B || !O || !q_start || !q_len || !kv_start || !kv_prefix || !agent)
@@ -270,7 +284,7 @@ LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows,
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     lra::PrefillParams p{};
     p.Q = Q; p.K = K_base; p.V = V_base; p.Vlr = V_lr; p.B = B; p.O = O;
-    p.ld_vlr = ld_vlr;
+    p.ld_vlr = ld_vlr; p.vlr_agent_stride = vlr_agent_stride;
     p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.d_head = d_head; p.rank = rank;
     p.n_agents = n_agents; p.scale = scale; p.bf16 = dtype == LRA_BF16;
     p.q_start = q_start; p.q_len = q_len; p.kv_start = kv_start; p.kv_prefix = kv_prefix; p.agents = agent;
@@ -308,7 +322,7 @@ LRA_EXPORT int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, 
         return fail(LRA_ERR_SHAPE, "tensor pointers must be 16-byte aligned");
     lra::PrefillParams p{};
     p.Q = Q; p.K = K_pages; p.V = V_pages; p.Vlr = Vlr_pages; p.B = B; p.O = O;
-    p.ld_vlr = ld_vlr;
+    p.ld_vlr = ld_vlr; p.vlr_agent_stride = rank;   // pages hold interleaved rows
     p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.d_head = d_head; p.rank = rank;
     p.n_agents = n_agents; p.scale = scale; p.bf16 = dtype == LRA_BF16;
     p.q_start = q_start; p.q_len = q_len; p.kv_start = nullptr; p.kv_prefix = kv_prefix; p.agents = agent;
@@ -395,7 +409,7 @@ int decode_paged_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.kv_start = nullptr; p.kv_len = kv_len; p.agent = agent;
     p.records = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.rec_off) : nullptr;
     p.record_bytes = uint32_t(L.rec_bytes);
-    p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
+    p.O = O; p.ld_vlr = ld_vlr; p.vlr_agent_stride = rank; p.kv_rows = int64_t(max_blocks) * page_size; p.max_kv_len = max_kv_len;
     p.kv_row_stride = row_stride; p.kv_head_stride = head_stride; p.kv_page_stride = page_stride;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_slots = std::max(L.n_slots, 0); p.scale = scale;
@@ -476,7 +490,7 @@ struct DecodeStep {
 
 int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
                 const void* K_base, const void* V_base, int64_t kv_rows, int64_t kv_row_stride, int64_t kv_head_stride,
-                const void* V_lr, int64_t ld_vlr,
+                const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                 const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                 const void* B, int32_t n_agents, const int32_t* agent,
                 int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -497,8 +511,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     // key-score grid: one workgroup row per 512-key block (at most 32,768)
     if (kl && max_kv_len > (int64_t(1) << 24)) return fail(LRA_ERR_SHAPE, "max_kv_len exceeds 2^24 with LoRA on the keys");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
-    if (ld_vlr < int64_t(n_agents) * rank || ld_vlr % 8 != 0)
-        return fail(LRA_ERR_SHAPE, "ld_vlr=%lld must be >= n_agents*rank and a multiple of 8", (long long)ld_vlr);
+    if (int s = check_vlr(ld_vlr, vlr_agent_stride, kv_rows, n_agents, rank)) return s;
     if (kl && (kl->ld_klr < int64_t(n_agents) * rank || kl->ld_klr % 8 != 0))
         return fail(LRA_ERR_SHAPE, "ld_klr=%lld must be >= n_agents*rank and a multiple of 8", (long long)kl->ld_klr);
     if (keys_per_split < 0 || keys_per_split % 64 != 0)
@@ -538,7 +551,7 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.kv_start = kv_start; p.kv_len = kv_len; p.agent = agent;
     p.records = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.rec_off) : nullptr;
     p.record_bytes = uint32_t(L.rec_bytes);
-    p.O = O; p.ld_vlr = ld_vlr; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
+    p.O = O; p.ld_vlr = ld_vlr; p.vlr_agent_stride = vlr_agent_stride; p.kv_rows = kv_rows; p.max_kv_len = max_kv_len;
     p.kv_row_stride = kv_row_stride; p.kv_head_stride = kv_head_stride; p.kv_page_stride = 0;
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_slots = std::max(L.n_slots, 0); p.scale = scale;
@@ -577,14 +590,14 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
 
 LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
                                const void* K_base, const void* V_base, int64_t kv_rows,
-                               const void* V_lr, int64_t ld_vlr,
+                               const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                                const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                                const void* B, int32_t n_agents, const int32_t* agent,
                                int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                                int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                                void* O, void* stream) {
     return decode_call("lra_attn_decode launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head, d_head,
-                       V_lr, ld_vlr, kv_start,
+                       V_lr, ld_vlr, vlr_agent_stride, kv_start,
                        kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
                        workspace, workspace_bytes, O, stream, nullptr);
 }
@@ -592,20 +605,20 @@ LRA_EXPORT int lra_attn_decode(int dtype, const void* Q, int32_t batch,
 LRA_EXPORT int lra_attn_decode_strided(int dtype, const void* Q, int32_t batch,
                                        const void* K_base, const void* V_base, int64_t kv_rows,
                                        int64_t kv_row_stride, int64_t kv_head_stride,
-                                       const void* V_lr, int64_t ld_vlr,
+                                       const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                                        const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                                        const void* B, int32_t n_agents, const int32_t* agent,
                                        int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
                                        int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                                        void* O, void* stream) {
     return decode_call("lra_attn_decode_strided launch", dtype, Q, batch, K_base, V_base, kv_rows, kv_row_stride,
-                       kv_head_stride, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv,
+                       kv_head_stride, V_lr, ld_vlr, vlr_agent_stride, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv,
                        d_head, rank, scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr);
 }
 
 LRA_EXPORT int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
                                     const void* K_base, const void* V_base, int64_t kv_rows,
-                                    void* V_lr, int64_t ld_vlr,
+                                    void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                                     const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                                     const void* B, int32_t n_agents, const int32_t* agent,
                                     int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -614,7 +627,7 @@ LRA_EXPORT int lra_attn_decode_step(int dtype, const void* Q, int32_t batch,
                                     void* O, void* stream) {
     const DecodeStep st{X_new, ldx, A, d_model};
     return decode_call("lra_attn_decode_step launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
-                       d_head, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
+                       d_head, V_lr, ld_vlr, vlr_agent_stride, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
                        scale, keys_per_split, workspace, workspace_bytes, O, stream, nullptr, &st);
 }
 
@@ -659,7 +672,7 @@ LRA_EXPORT int lra_stream_read(const void* x, int64_t bytes, int32_t n_workgroup
 
 LRA_EXPORT int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
                                        const void* K_base, const void* V_base, int64_t kv_rows,
-                                       const void* V_lr, int64_t ld_vlr,
+                                       const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
                                        const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                                        const void* B, int32_t n_agents, const int32_t* agent,
                                        int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank, float scale,
@@ -673,7 +686,7 @@ LRA_EXPORT int lra_attn_decode_noalloc(int dtype, const void* Q, int32_t batch,
         if (int s = scratch_on_current_device(&ws)) return s;
     }
     return decode_call("lra_attn_decode_noalloc launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
-                       d_head, V_lr, ld_vlr, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
+                       d_head, V_lr, ld_vlr, vlr_agent_stride, kv_start, kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank,
                        scale, keys_per_split, ws, ws ? size_t(LRA_NOALLOC_SCRATCH_BYTES) : 0, O, stream, nullptr);
 }
 
@@ -688,7 +701,8 @@ LRA_EXPORT size_t lra_attn_decode_qkvo_workspace_bytes(int32_t batch, int32_t n_
 
 LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                                     const void* K_base, const void* V_base, int64_t kv_rows,
-                                    const void* V_lr, int64_t ld_vlr, const void* K_lr, int64_t ld_klr,
+                                    const void* V_lr, int64_t ld_vlr, int64_t vlr_agent_stride,
+                                    const void* K_lr, int64_t ld_klr,
                                     const int64_t* kv_start, const int32_t* kv_len, int64_t max_kv_len,
                                     const void* B, const void* B_k, const float* rope_cos, const float* rope_sin,
                                     int32_t n_agents, const int32_t* agent,
@@ -697,7 +711,7 @@ LRA_EXPORT int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                                     void* O, void* stream) {
     const DecodeKeyLora kl{K_lr, ld_klr, B_k, rope_cos, rope_sin};
     return decode_call("lra_attn_decode_qkvo launch", dtype, Q, batch, K_base, V_base, kv_rows, int64_t(n_kv) * d_head,
-                       d_head, V_lr, ld_vlr, kv_start,
+                       d_head, V_lr, ld_vlr, vlr_agent_stride, kv_start,
                        kv_len, max_kv_len, B, n_agents, agent, n_q, n_kv, d_head, rank, scale, keys_per_split,
                        workspace, workspace_bytes, O, stream, &kl);
 }

@@ -196,7 +196,8 @@ __device__ void newest_lr_rows(const DecodeParams& p, int i, float (*red)[2][64]
                 float v = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < kSplitWaves; ++ww) v += red[ww][h][threadIdx.x & 63];
-                static_cast<T*>(const_cast<void*>(p.Vlr))[row[h] * p.ld_vlr + cc] = from_f32<T>(v);
+                const int ka = cc / p.rank;   // agent of column cc
+                static_cast<T*>(const_cast<void*>(p.Vlr))[row[h] * p.ld_vlr + ka * p.vlr_agent_stride + (cc - ka * p.rank)] = from_f32<T>(v);
             }
         }
         __syncthreads();
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kSplitThreads, 2) void decode_split_kernel(DecodePa
         return static_cast<const char*>(X) + pc.start * row_bytes + head_bytes;
     };
     auto lr_base = [&](const Piece& pc) -> const char* {
-        return static_cast<const char*>(p.Vlr) + (pc.start * p.ld_vlr + int64_t(max(pc.a, 0)) * R) * int64_t(sizeof(T));
+        return static_cast<const char*>(p.Vlr) + (pc.start * p.ld_vlr + int64_t(max(pc.a, 0)) * p.vlr_agent_stride) * int64_t(sizeof(T));
     };
 
     // the group's queries as the B operand (columns >= G are zero)
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     vnew.zero();
     const bool step_new = !PAGED && p.X_new != nullptr && adapted;
     if (wv == 0 && step_new)
-        vnew.load(static_cast<const T*>(p.Vlr) + (start + len - 1) * p.ld_vlr + int64_t(a) * R + 4 * (lane % (R / 4)));
+        vnew.load(static_cast<const T*>(p.Vlr) + (start + len - 1) * p.ld_vlr + int64_t(a) * p.vlr_agent_stride + 4 * (lane % (R / 4)));
     if (wv == 0 && adapted) {
         const T* __restrict__ Bp = static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D;
 #pragma unroll

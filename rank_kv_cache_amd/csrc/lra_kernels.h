@@ -27,7 +27,9 @@ struct DecodeParams {
     float* records;
     uint32_t record_bytes;
     void* O;
-    int64_t ld_vlr;
+    // V_lr: row r, agent a, rank column j at r * ld_vlr + a * vlr_agent_stride + j (the rows'
+    // layout: vlr_agent_stride = rank; agent-major: ld_vlr = rank, vlr_agent_stride >= rows * rank)
+    int64_t ld_vlr, vlr_agent_stride;
     int64_t kv_rows;
     int64_t max_kv_len;
     // elements between consecutive rows of one KV head, and between the KV heads of one row, of K
@@ -68,9 +70,10 @@ struct PrecomputeParams {
     const int64_t* out_rows;
     int64_t T;
     int64_t ldx;
-    int64_t ld_vlr;
+    int64_t ld_vlr, vlr_agent_stride;   // output column a * rank + j at row * ld_vlr + a * vlr_agent_stride + j
     int64_t vlr_rows;
     int d_model;
+    int rank;
     int NR;               // n_agents * rank
     int n_rg;             // row ranges (one per workgroup and column group)
     int n_cg;             // column groups
@@ -87,7 +90,7 @@ struct PrefillParams {
     void* O;
     int64_t L_C;
     int64_t L_P;
-    int64_t ld_vlr;
+    int64_t ld_vlr, vlr_agent_stride;   // as in DecodeParams
     int n_q, n_kv, G, d_head, rank, agent, n_agents;
     float scale;
     bool bf16;

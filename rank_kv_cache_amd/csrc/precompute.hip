@@ -125,7 +125,9 @@ __global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) v += red[ww][rr][c];
             const int64_t orow = p.out_rows ? p.out_rows[rt + rr] : rt + rr;
-            if (orow >= 0 && orow < p.vlr_rows) static_cast<T*>(p.Vlr)[orow * p.ld_vlr + c0 + c] = from_f32<T>(v);
+            const int ka = (c0 + c) / p.rank;   // agent of output column c0 + c
+            if (orow >= 0 && orow < p.vlr_rows)
+                static_cast<T*>(p.Vlr)[orow * p.ld_vlr + ka * p.vlr_agent_stride + (c0 + c - ka * p.rank)] = from_f32<T>(v);
         }
         __syncthreads();   // red is reused by the next tile
     }

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 const int key = tid / (R / 8);
                 const int r0 = (tid - key * (R / 8)) * 8;
                 const int64_t j = min(kb + key, kv_end - 1) + page_off;
-                lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * R + r0);
+                lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride + r0);
             }
         };
         // 8 values of one key's row in the pass's P.V element type: fp16 (exact within its range;

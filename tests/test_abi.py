@@ -49,11 +49,11 @@ def test_version_and_status_strings():
 
 # ---------------------------------------------------------------------------------------- decode
 def decode(**kw):
-    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, vas=8, kv_start=P, kv_len=P,
              max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
              split=0, ws=WS, ws_bytes=1 << 30, O=P, stream=0)
     a.update(kw)
-    return lra._lib.lra_attn_decode(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"],
+    return lra._lib.lra_attn_decode(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"], a["vas"],
                                     a["kv_start"], a["kv_len"], a["max_kv_len"], a["B"], a["n_agents"], a["agent"],
                                     a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"], a["split"], a["ws"],
                                     a["ws_bytes"], a["O"], a["stream"])
@@ -63,6 +63,9 @@ def decode(**kw):
     (dict(dtype=2), E_UNSUP), (dict(d=96), E_UNSUP), (dict(r=4), E_UNSUP), (dict(n_q=36, n_kv=4), E_UNSUP),
     (dict(n_q=30, n_kv=8), E_SHAPE), (dict(n_kv=0), E_SHAPE), (dict(batch=-1), E_SHAPE),
     (dict(ld_vlr=16), E_SHAPE), (dict(ld_vlr=28), E_SHAPE), (dict(split=100), E_SHAPE), (dict(split=-64), E_SHAPE),
+    # V_lr layouts: interleaved needs an agent stride of rank, agent-major one of at least kv_rows x ld_vlr
+    (dict(vas=16), E_SHAPE), (dict(vas=12), E_SHAPE), (dict(vas=0), E_SHAPE), (dict(ld_vlr=8, vas=792), E_SHAPE),
+    (dict(ld_vlr=4, vas=800), E_SHAPE),
     (dict(max_kv_len=-1), E_SHAPE), (dict(kv_rows=-5), E_SHAPE), (dict(n_agents=0), E_SHAPE),
     (dict(scale=float("nan")), E_SHAPE), (dict(scale=0.0), E_SHAPE), (dict(scale=-0.1), E_SHAPE), (dict(Q=None), E_NULL), (dict(kv_len=None), E_NULL),
     (dict(agent=None), E_NULL), (dict(O=None), E_NULL), (dict(K=P + 8), E_SHAPE),
@@ -75,12 +78,12 @@ def test_decode_rejects_bad_arguments(kw, status):
 
 
 def decode_qkvo(**kw):
-    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, Klr=P, ld_klr=24, kv_start=P, kv_len=P,
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, vas=8, Klr=P, ld_klr=24, kv_start=P, kv_len=P,
              max_kv_len=100, B=P, Bk=P, cos=P, sin=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
              split=0, ws=WS, ws_bytes=16, O=P, stream=0)
     a.update(kw)
     return lra._lib.lra_attn_decode_qkvo(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"],
-                                         a["ld_vlr"], a["Klr"], a["ld_klr"], a["kv_start"], a["kv_len"], a["max_kv_len"],
+                                         a["ld_vlr"], a["vas"], a["Klr"], a["ld_klr"], a["kv_start"], a["kv_len"], a["max_kv_len"],
                                          a["B"], a["Bk"], a["cos"], a["sin"], a["n_agents"], a["agent"], a["n_q"],
                                          a["n_kv"], a["d"], a["r"], a["scale"], a["split"], a["ws"], a["ws_bytes"],
                                          a["O"], a["stream"])
@@ -115,12 +118,12 @@ def test_decode_qkvo_workspace_size():
 
 
 def decode_step(**kw):
-    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, Vlr=P, ld_vlr=24, vas=8, kv_start=P, kv_len=P,
              max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
              X=P, ldx=4096, A=P, d_model=4096, split=0, ws=WS, ws_bytes=1 << 30, O=P, stream=0)
     a.update(kw)
     return lra._lib.lra_attn_decode_step(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["Vlr"],
-                                         a["ld_vlr"], a["kv_start"], a["kv_len"], a["max_kv_len"], a["B"],
+                                         a["ld_vlr"], a["vas"], a["kv_start"], a["kv_len"], a["max_kv_len"], a["B"],
                                          a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"],
                                          a["X"], a["ldx"], a["A"], a["d_model"], a["split"], a["ws"], a["ws_bytes"],
                                          a["O"], a["stream"])
@@ -173,10 +176,10 @@ def test_decode_workspace_size_follows_slices():
 
 # ---------------------------------------------------------------------------------------- prefill
 def prefill(**kw):
-    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, B=P, n_agents=3, agent=0,
+    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, vas=8, B=P, n_agents=3, agent=0,
              n_q=4, n_kv=2, d=64, r=8, scale=0.125, O=P, stream=0)
     a.update(kw)
-    return lra._lib.lra_attn_prefill(a["dtype"], a["Q"], a["L_C"], a["L_P"], a["K"], a["V"], a["Vlr"], a["ld_vlr"],
+    return lra._lib.lra_attn_prefill(a["dtype"], a["Q"], a["L_C"], a["L_P"], a["K"], a["V"], a["Vlr"], a["ld_vlr"], a["vas"],
                                      a["B"], a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"],
                                      a["scale"], a["O"], a["stream"])
 
@@ -200,11 +203,11 @@ def test_prefill_accepts_the_adapter_free_view():
 
 def prefill_varlen(**kw):
     a = dict(dtype=1, Q=P, q_rows=100, batch=3, q_start=P, q_len=P, max_q_len=64, K=P, V=P, kv_rows=500, Vlr=P,
-             ld_vlr=24, kv_start=P, kv_prefix=P, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
+             ld_vlr=24, vas=8, kv_start=P, kv_prefix=P, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088,
              O=P, stream=0)
     a.update(kw)
     return lra._lib.lra_attn_prefill_varlen(a["dtype"], a["Q"], a["q_rows"], a["batch"], a["q_start"], a["q_len"],
-                                            a["max_q_len"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"],
+                                            a["max_q_len"], a["K"], a["V"], a["kv_rows"], a["Vlr"], a["ld_vlr"], a["vas"],
                                             a["kv_start"], a["kv_prefix"], a["B"], a["n_agents"], a["agent"], a["n_q"],
                                             a["n_kv"], a["d"], a["r"], a["scale"], a["O"], a["stream"])
 
@@ -231,11 +234,11 @@ def test_prefill_empty_chunk_is_a_no_op():
 
 
 def prefill_qkvo(**kw):
-    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, Klr=P, ld_klr=24, B=P, Bk=P, cos=P, sin=P,
+    a = dict(dtype=1, Q=P, L_C=64, L_P=192, K=P, V=P, Vlr=P, ld_vlr=24, vas=8, Klr=P, ld_klr=24, B=P, Bk=P, cos=P, sin=P,
              n_agents=3, agent=0, n_q=4, n_kv=2, d=64, r=8, scale=0.125, ws=None, ws_bytes=0, O=P, stream=0)
     a.update(kw)
     return lra._lib.lra_attn_prefill_qkvo(a["dtype"], a["Q"], a["L_C"], a["L_P"], a["K"], a["V"], a["Vlr"],
-                                          a["ld_vlr"], a["Klr"], a["ld_klr"], a["B"], a["Bk"], a["cos"], a["sin"],
+                                          a["ld_vlr"], a["vas"], a["Klr"], a["ld_klr"], a["B"], a["Bk"], a["cos"], a["sin"],
                                           a["n_agents"], a["agent"], a["n_q"], a["n_kv"], a["d"], a["r"], a["scale"],
                                           a["ws"], a["ws_bytes"], a["O"], a["stream"])
 
@@ -269,17 +272,18 @@ def test_prefill_qkvo_workspace_size():
 
 # ---------------------------------------------------------------------------------------- precompute
 def precompute(**kw):
-    a = dict(dtype=1, X=P, T=2048, d_model=4096, ldx=4096, A=P, n_agents=3, r=8, Vlr=P, ld_vlr=24,
+    a = dict(dtype=1, X=P, T=2048, d_model=4096, ldx=4096, A=P, n_agents=3, r=8, Vlr=P, ld_vlr=24, vas=8,
              vlr_rows=18432, out_rows=None, ws=WS, ws_bytes=1 << 30, stream=0)
     a.update(kw)
     return lra._lib.lra_lr_precompute(a["dtype"], a["X"], a["T"], a["d_model"], a["ldx"], a["A"], a["n_agents"],
-                                      a["r"], a["Vlr"], a["ld_vlr"], a["vlr_rows"], a["out_rows"], a["ws"],
+                                      a["r"], a["Vlr"], a["ld_vlr"], a["vas"], a["vlr_rows"], a["out_rows"], a["ws"],
                                       a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=5), E_UNSUP), (dict(d_model=4004), E_UNSUP), (dict(n_agents=3, r=3), E_UNSUP),
     (dict(T=-1), E_SHAPE), (dict(ldx=4095), E_SHAPE), (dict(ldx=4092), E_SHAPE), (dict(ld_vlr=20), E_SHAPE),
+    (dict(vas=16), E_SHAPE), (dict(ld_vlr=8, vas=8 * 2047), E_SHAPE),
     (dict(vlr_rows=100), E_SHAPE), (dict(vlr_rows=-1, out_rows=P), E_SHAPE), (dict(n_agents=0), E_SHAPE),
     (dict(X=None), E_NULL), (dict(A=None), E_NULL), (dict(Vlr=P + 4), E_SHAPE),
 ])
@@ -393,12 +397,12 @@ def test_expand_values_empty_is_a_no_op():
 
 # ---------------------------------------------------------------------------------------- strided decode
 def decode_strided(**kw):
-    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, rs=128, hs=12800, Vlr=P, ld_vlr=24, kv_start=P, kv_len=P,
+    a = dict(dtype=1, Q=P, batch=2, K=P, V=P, kv_rows=100, rs=128, hs=12800, Vlr=P, ld_vlr=24, vas=8, kv_start=P, kv_len=P,
              max_kv_len=100, B=P, n_agents=3, agent=P, n_q=32, n_kv=8, d=128, r=8, scale=0.088, split=0, ws=WS,
              ws_bytes=1 << 30, O=P, stream=0)
     a.update(kw)
     return lra._lib.lra_attn_decode_strided(a["dtype"], a["Q"], a["batch"], a["K"], a["V"], a["kv_rows"], a["rs"],
-                                            a["hs"], a["Vlr"], a["ld_vlr"], a["kv_start"], a["kv_len"],
+                                            a["hs"], a["Vlr"], a["ld_vlr"], a["vas"], a["kv_start"], a["kv_len"],
                                             a["max_kv_len"], a["B"], a["n_agents"], a["agent"], a["n_q"], a["n_kv"],
                                             a["d"], a["r"], a["scale"], a["split"], a["ws"], a["ws_bytes"], a["O"],
                                             a["stream"])

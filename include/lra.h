@@ -75,7 +75,8 @@ extern "C" {
                                 8: one round of decode workgroups, each streaming its slice as
                                    one sequence of tiles (workspace sizes changed);
                                    lra_stream_read; the LR cache's agent stride (vlr_agent_stride)
-                                   on every entry point over contiguous caches: agent-major caches */
+                                   on every entry point over contiguous caches: agent-major caches;
+                                   small batches of lra_attn_decode in 128/256-key chunks */
 
 typedef enum {
     LRA_OK = 0,
@@ -274,8 +275,12 @@ int lra_attn_prefill_paged(int dtype, const void* Q, int64_t q_rows, int32_t bat
  * keys_per_split  keys per slice at full lengths (batch * max_kv_len / keys_per_split slices,
  *          rounded up to a multiple of 8; keys_per_split a multiple of 64), or 0 for the library's
  *          choice (one round of 8-wave workgroups on 15/16 of the chip's CUs: 240 slices per
- *          group of 8 KV heads, fewer when the batch's actual lengths hold fewer tiles). The
- *          slicing changes the rounding of the result only.
+ *          group of 8 KV heads, fewer when the batch's actual lengths hold fewer tiles). With 0
+ *          and a small batch (batch x n_kv x ceil(max_kv_len / 128) <= 256, else with 256-key
+ *          chunks <= 512) lra_attn_decode and its strided and no-allocation forms instead give
+ *          each (request, KV head, 128- or 256-key chunk) one workgroup, which merges its tiles
+ *          in LDS; requests of one chunk finish in that launch, longer ones in a merge launch over
+ *          their chunk records. The slicing changes the rounding of the result only.
  * workspace(device) lra_attn_decode_workspace_bytes() bytes, 256-byte aligned; its contents need
  *          no initialisation. Calls that share one workspace must be ordered (same stream).
  * O        (device) [batch x n_q x d_head] output

@@ -71,6 +71,12 @@ DecodeLayout decode_layout(int batch, int n_q, int n_kv, int d_head, int rank, i
     const size_t blocks = (size_t(slices) + size_t(batch)) * size_t(n_kv);
     L.rec_off = 0;
     L.rec_bytes = blocks * size_t(lra::decode_record_slots(n_q / n_kv, d_head, rank)) * 16;
+    // the small-batch launch's chunk records, when the sizes select it (plain decodes only, but the
+    // workspace query serves every decode entry point)
+    const int chunks = lra::decode_small_chunks(batch, n_kv, max_kv_len, keys_per_split);
+    if (chunks > 1)
+        L.rec_bytes = std::max(L.rec_bytes, size_t(batch) * size_t(n_kv) * size_t(chunks) *
+                                                size_t(lra::decode_small_record_slots(n_q / n_kv, d_head)) * 16);
     if (L.rec_bytes >= (size_t(1) << 31)) L.n_slots = -1;   // 32-bit record offsets
     L.total = L.rec_off + L.rec_bytes;
     return L;
@@ -556,6 +562,8 @@ int decode_call(const char* name, int dtype, const void* Q, int32_t batch,
     p.batch = batch; p.n_q = n_q; p.n_kv = n_kv; p.G = n_q / n_kv; p.n_agents = n_agents;
     p.d_head = d_head; p.rank = rank; p.n_slots = std::max(L.n_slots, 0); p.scale = scale;
     p.bf16 = dtype == LRA_BF16;
+    // small batches of plain decodes: one workgroup per (request, KV head, 256-key chunk)
+    if (!st && !kl) p.n_chunks = lra::decode_small_chunks(batch, n_kv, max_kv_len, keys_per_split, &p.chunk_keys);
     if (st) {
         p.X_new = st->X_new;
         p.A_new = st->A;

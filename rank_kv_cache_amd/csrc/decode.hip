@@ -806,8 +806,385 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeP
     }
 }
 
+// ---- small batches ---------------------------------------------------------------------------
+// When the batch holds few tiles, the split launch above gives each of its slots a tile or two of
+// eight heads, and the merge reads one record per 32-key tile and head. Here workgroup (b, g, c)
+// instead takes chunk c (32*CW keys) of request b on KV head g, wave w its 32-key tile w, with the same matrix-core tile as the split kernel (one tile per wave: its softmax maximum is
+// the tile's). The wave partials are merged in LDS with weights 2^(m_w - max m), so a chunk leaves
+// one record; a request of one chunk is finished in the same launch, otherwise a second launch
+// merges its chunk records the same way and applies the up-projection. Both kernels issue every
+// load that does not need the request's range before that range arrives (the queries, the
+// records, the B values of every agent when there are few), so each is about one memory round
+// trip more than its launch.
+template <int D, int GP, int CW> struct SmallRecord {
+    static constexpr int VEC = D / 16;
+    static constexpr int ENT = VEC + 1;      // fragments per lane: the O^T tiles, then O_lr^T
+    static constexpr int FR = 4 * GP;        // lanes (n, q) with n < GP, at index q * GP + n
+    static constexpr int ML = ENT * FR;      // then m[GP], l[GP] as floats
+    static constexpr int SLOTS = ML + (2 * GP + 3) / 4;
+    static constexpr int FPT = (ENT * FR + 64 * CW - 1) / (64 * CW);   // fragments per thread
+};
+
+// merged state of one (request, KV head) in LDS: O[n][d], O_lr[n][r] (unnormalised) and l[n]
+template <int D, int R, int GP> struct SmallOut {
+    float o[GP][D];
+    float lr[GP][R];
+    float l[GP];
+};
+
+// fragment tt of lane index i = q * GP + n (n < GP) into the LDS state: O^T tile tt, lane (n, q),
+// register j is O[n][VEC*(4q + j) + tt]; the O_lr^T fragment (tt = VEC) register j is O_lr[n][4q + j]
+template <int D, int R, int GP>
+__device__ __forceinline__ void small_put(SmallOut<D, R, GP>& so, int tt, int i, f32x4 v) {
+    constexpr int VEC = D / 16;
+    const int n = i % GP, q = i / GP;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (tt < VEC) so.o[n][VEC * (4 * q + j) + tt] = v[j];
+        else if (4 * q + j < R) so.lr[n][4 * q + j] = v[j];
+    }
+}
+
+// The epilogue thread i < G*D/4 takes 4 consecutive elements d0 .. d0+3 of head n = i / (D/4) and
+// needs B_a[r][g*D + d0 .. +3], r < R. With at most kSpecAgents agents (bf16) every agent's values
+// are loaded before the request's agent is known; otherwise they are loaded once it is.
+template <typename T, int D, int R> struct SmallB {
+    static constexpr int kSpecAgents = sizeof(T) == 2 ? 4 : 0;
+    Vec<T, 4> bs[kSpecAgents > 0 ? kSpecAgents : 1][R];
+    __device__ __forceinline__ const T* at(const DecodeParams& p, int g, int a, int d0) const {
+        const int64_t d_kv = int64_t(p.n_kv) * D;
+        return static_cast<const T*>(p.B) + int64_t(a) * R * d_kv + int64_t(g) * D + d0;
+    }
+    __device__ __forceinline__ void prefetch(const DecodeParams& p, int g) {
+        if constexpr (kSpecAgents > 0) {
+            const int i = threadIdx.x;
+            if (p.n_agents > kSpecAgents || i >= p.G * (D / 4)) return;
+            const int d0 = 4 * (i % (D / 4));
+            const int64_t d_kv = int64_t(p.n_kv) * D;
+#pragma unroll
+            for (int k = 0; k < kSpecAgents; ++k)
+                if (k < p.n_agents) {
+                    const T* Bp = at(p, g, k, d0);
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) bs[k][rr].load(Bp + rr * d_kv);
+                }
+        }
+    }
+    // agent a's values (a >= 0)
+    __device__ __forceinline__ void get(const DecodeParams& p, int g, int a, int d0, Vec<T, 4> (&bv)[R]) const {
+        if (kSpecAgents > 0 && p.n_agents <= kSpecAgents) {
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) bv[rr] = bs[0][rr];
+#pragma unroll
+            for (int k = 1; k < (kSpecAgents > 0 ? kSpecAgents : 1); ++k)
+                if (a == k) {
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr) bv[rr] = bs[k][rr];
+                }
+        } else {
+            const int64_t d_kv = int64_t(p.n_kv) * D;
+            const T* Bp = at(p, g, a, d0);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) bv[rr].load(Bp + rr * d_kv);
+        }
+    }
+};
+
+// O rows of (b, g) from the LDS state: (O + O_lr B_a[:, g*d .. g*d + d)) / l, rounded to T
+template <typename T, int D, int R, int GP>
+__device__ __forceinline__ void small_epilogue(const DecodeParams& p, int b, int g, int a, const SmallOut<D, R, GP>& so,
+                                               const SmallB<T, D, R>& sb) {
+    const int i = threadIdx.x;
+    if (i >= p.G * (D / 4)) return;
+    const int n = i / (D / 4), d0 = 4 * (i % (D / 4));
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = so.o[n][d0 + e];
+    if (a != kAdapterFree) {
+        Vec<T, 4> bv[R];
+        sb.get(p, g, a, d0, bv);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = fmaf(so.lr[n][rr], bv[rr].get(e), o[e]);
+    }
+    const float inv = 1.f / so.l[n];
+    T* dst = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * p.G + n) * D + d0;
+    if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+    else
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+}
+
+// O rows of (b, g) for a request without keys (zeros) or with an invalid range or agent (NaN)
+template <typename T, int D>
+__device__ __forceinline__ void small_fill(const DecodeParams& p, int b, int g, bool ok) {
+    const T fill = from_f32<T>(ok ? 0.f : __builtin_nanf(""));
+    T* Op = static_cast<T*>(p.O) + (int64_t(b) * p.n_q + int64_t(g) * p.G) * D;
+    for (int i = threadIdx.x; i < p.G * D; i += blockDim.x) Op[i] = fill;
+}
+
+template <typename T, int D, int R, int GP, int CW, bool FINAL>
+__global__ __launch_bounds__(64 * CW, 2) void decode_small_kernel(DecodeParams p) {
+    constexpr int kSmallWaves = CW, kSmallThreads = 64 * CW, kChunk = kTile * CW;
+    using Tile = DecodeTile<T, D>;
+    using F = SmallRecord<D, GP, CW>;
+    constexpr int VEC = Tile::VEC, KCH = Tile::KCH, ENT = F::ENT, FR = F::FR;
+    __shared__ f32x4 st[kSmallWaves][ENT][FR];
+    __shared__ float st_m[kSmallWaves][GP], st_l[kSmallWaves][GP];
+    __shared__ SmallOut<D, R, GP> so;
+
+    const int c = blockIdx.x % p.n_chunks;
+    const int bg = blockIdx.x / p.n_chunks;
+    const int b = bg / p.n_kv, g = bg - b * p.n_kv;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int G = p.G;
+    // the group's queries as the B operand (columns >= G are zero), and with one chunk the B values,
+    // requested together with the request's range
+    Vec<T, 8> qf[KCH];
+    {
+        const T* __restrict__ Qp = static_cast<const T*>(p.Q) + (int64_t(b) * p.n_q + int64_t(g) * G + min(n, G - 1)) * D + 8 * q;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            if (n < G) qf[i].load(Qp + 32 * i);
+            else qf[i].zero();
+        }
+    }
+    SmallB<T, D, R> sb;
+    if constexpr (FINAL) sb.prefetch(p, g);
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b];
+    const int32_t a = p.agent[b];
+    const bool ok = decode_request_ok(start, len, a, p);
+    if (!ok || int64_t(len) <= int64_t(c) * kChunk) {   // workgroup-uniform
+        if (FINAL && c == 0) small_fill<T, D>(p, b, g, ok);
+        return;
+    }
+    const int kt = c * kChunk + wv * kTile;   // this wave's tile (wave 0's is never empty)
+    const bool live = kt < len;
+
+    f32x4 acc[VEC];
+#pragma unroll
+    for (int tt = 0; tt < VEC; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc_lr = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+    if (live) {   // wave-uniform
+        const int lim = len - 1 - kt;   // keys past it read row len - 1 and get P = 0
+        const int64_t row0 = start + kt;
+        const T* __restrict__ Kp = static_cast<const T*>(p.K) + row0 * p.kv_row_stride + int64_t(g) * p.kv_head_stride;
+        const T* __restrict__ Vp = static_cast<const T*>(p.V) + row0 * p.kv_row_stride + int64_t(g) * p.kv_head_stride;
+        const T* __restrict__ Lp = static_cast<const T*>(p.Vlr) + row0 * p.ld_vlr + int64_t(max(a, 0)) * p.vlr_agent_stride + n % R;
+        Tile t;
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            const int64_t o = int64_t(min(16 * uu + n, lim)) * p.kv_row_stride + 8 * q;
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) t.k[uu][i].load(Kp + o + 32 * i);
+        }
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = min(tile_key(q, e), lim);
+            t.v[e].load(Vp + int64_t(key) * p.kv_row_stride + VEC * n);
+            if constexpr (sizeof(T) == 2) h[e] = *reinterpret_cast<const uint16_t*>(Lp + int64_t(key) * p.ld_vlr);
+            else t.lr.v[e] = Lp[int64_t(key) * p.ld_vlr];
+        }
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) t.lr.w[qq] = h[2 * qq] | (h[2 * qq + 1] << 16);
+        }
+        // S^T = K Q^T; lane (n, q) holds head n's scores of keys tile_key(q, e)
+        f32x4 sacc[2];
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            sacc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) sacc[uu] = mma16x16x32(t.k[uu][i], qf[i], sacc[uu]);
+        }
+        const float sl2 = p.scale * kLog2e;
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = tile_key(q, e) <= lim ? sacc[e >> 2][e & 3] * sl2 : -INFINITY;
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m = mx;   // key kt is live: finite
+        float pr[8], ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = fast_exp2(sc[e] - m);
+            ls += pr[e];
+        }
+        ls += __shfl_xor(ls, 16);
+        l = ls + __shfl_xor(ls, 32);
+        if constexpr (sizeof(T) == 2) {
+            Vec<bf16, 8> phi, plo;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                phi.w[qq] = pack_bf16x2(pr[2 * qq], pr[2 * qq + 1]);
+                plo.w[qq] = pack_bf16x2(pr[2 * qq] - bf16_lo(phi.w[qq]), pr[2 * qq + 1] - bf16_hi(phi.w[qq]));
+            }
+#pragma unroll
+            for (int tt = 0; tt < VEC; ++tt) {
+                const Vec<bf16, 8> va = v_operand<VEC>(t.v, tt);
+                acc[tt] = mma16x16x32(va, phi, acc[tt]);
+                acc[tt] = mma16x16x32(va, plo, acc[tt]);
+            }
+            acc_lr = mma16x16x32(t.lr, phi, acc_lr);
+            acc_lr = mma16x16x32(t.lr, plo, acc_lr);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                for (int tt = 0; tt < VEC; ++tt)
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[e].v[tt], pr[e], acc[tt], 0, 0, 0);
+                acc_lr = __builtin_amdgcn_mfma_f32_16x16x4f32(t.lr.v[e], pr[e], acc_lr, 0, 0, 0);
+            }
+        }
+    }
+    // the wave partials (an empty wave: m = -inf, zeros) -> LDS
+    if (n < GP) {
+        const int i = q * GP + n;
+#pragma unroll
+        for (int tt = 0; tt < VEC; ++tt) st[wv][tt][i] = acc[tt];
+        st[wv][VEC][i] = acc_lr;
+        if (q == 0) {
+            st_m[wv][n] = m;
+            st_l[wv][n] = l;
+        }
+    }
+    __syncthreads();
+    // fragment (tt, i) summed over the waves in order with weights 2^(m_w - max m)
+    float* rec = p.records + (int64_t(bg) * p.n_chunks + c) * (F::SLOTS * 4);
+#pragma unroll
+    for (int u = 0; u < F::FPT; ++u) {
+        const int fi = threadIdx.x + u * kSmallThreads;
+        if (fi < ENT * FR) {
+            const int tt = fi / FR, i = fi % FR, hn = i % GP;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kSmallWaves; ++w) M = fmaxf(M, st_m[w][hn]);
+            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kSmallWaves; ++w) {
+                const float e = fast_exp2(st_m[w][hn] - M);
+                v += st[w][tt][i] * e;
+                L = fmaf(st_l[w][hn], e, L);
+            }
+            if constexpr (FINAL) {
+                small_put<D, R, GP>(so, tt, i, v);
+                if (fi < GP) so.l[fi] = L;
+            } else {
+                reinterpret_cast<f32x4*>(rec)[fi] = v;
+                if (fi < GP) {
+                    rec[F::ML * 4 + fi] = M;
+                    rec[F::ML * 4 + GP + fi] = L;
+                }
+            }
+        }
+    }
+    if constexpr (FINAL) {
+        __syncthreads();
+        small_epilogue<T, D, R, GP>(p, b, g, a, so, sb);
+    }
+}
+
+// merge of the chunk records of one (request b, KV head g): thread (tt, i) keeps its fragment's
+// running maximum and sum over the chunks (the log-sum-exp rule). The first CB chunks' records are
+// requested before the request's length is known (chunks past it hold stale values and are not used).
+template <typename T, int D, int R, int GP, int CW>
+__global__ __launch_bounds__(kCombineThreads) void decode_small_combine_kernel(DecodeParams p) {
+    constexpr int kSmallThreads = kCombineThreads, kChunk = kTile * CW;
+    using F = SmallRecord<D, GP, kCombineWaves>;
+    constexpr int ENT = F::ENT, FR = F::FR, FPT = F::FPT, CB = 16;
+    __shared__ SmallOut<D, R, GP> so;
+    const int bg = blockIdx.x;
+    const int b = bg / p.n_kv, g = bg - b * p.n_kv;
+    const float* rec = p.records + int64_t(bg) * p.n_chunks * (F::SLOTS * 4);
+    f32x4 x[FPT][CB];
+    float mc[FPT][CB], lc[FPT][CB];
+    auto load_batch = [&](int c0, int nc) {
+#pragma unroll
+        for (int u = 0; u < FPT; ++u) {
+            const int fi = min(int(threadIdx.x) + u * kSmallThreads, ENT * FR - 1);
+            const int hn = (fi % FR) % GP;
+#pragma unroll
+            for (int k = 0; k < CB; ++k) {
+                const float* r = rec + int64_t(min(c0 + k, nc - 1)) * (F::SLOTS * 4);
+                x[u][k] = reinterpret_cast<const f32x4*>(r)[fi];
+                mc[u][k] = r[F::ML * 4 + hn];
+                lc[u][k] = r[F::ML * 4 + GP + hn];
+            }
+        }
+    };
+    load_batch(0, p.n_chunks);
+    SmallB<T, D, R> sb;
+    sb.prefetch(p, g);
+    const int64_t start = p.kv_start[b];
+    const int32_t len = p.kv_len[b];
+    const int32_t a = p.agent[b];
+    const bool ok = decode_request_ok(start, len, a, p);
+    if (!ok || len == 0) {
+        small_fill<T, D>(p, b, g, ok);
+        return;
+    }
+    const int nc = (len + kChunk - 1) / kChunk;   // <= n_chunks
+    float M[FPT], L[FPT];
+    f32x4 v[FPT];
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) {
+        M[u] = -INFINITY;
+        L[u] = 0.f;
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c0 = 0; c0 < nc; c0 += CB) {
+        if (c0 > 0) load_batch(c0, nc);
+#pragma unroll
+        for (int u = 0; u < FPT; ++u)
+#pragma unroll
+            for (int k = 0; k < CB; ++k) {
+                if (c0 + k < nc) {
+                    const float mn = fmaxf(M[u], mc[u][k]);
+                    const float keep = fast_exp2(M[u] - mn), w = fast_exp2(mc[u][k] - mn);
+                    v[u] = v[u] * keep + x[u][k] * w;
+                    L[u] = fmaf(L[u], keep, lc[u][k] * w);
+                    M[u] = mn;
+                }
+            }
+    }
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) {
+        const int fi = threadIdx.x + u * kSmallThreads;
+        if (fi < ENT * FR) {
+            small_put<D, R, GP>(so, fi / FR, fi % FR, v[u]);
+            if (fi < GP) so.l[fi] = L[u];
+        }
+    }
+    __syncthreads();
+    small_epilogue<T, D, R, GP>(p, b, g, a, so, sb);
+}
+
+template <typename T, int D, int R, int GP, int CW>
+hipError_t launch_small(const DecodeParams& p, hipStream_t stream) {
+    const dim3 block{unsigned(64 * CW)};
+    const unsigned n_bg = unsigned(p.batch * p.n_kv);
+    if (p.n_chunks == 1) {
+        hipLaunchKernelGGL((decode_small_kernel<T, D, R, GP, CW, true>), dim3(n_bg), block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((decode_small_kernel<T, D, R, GP, CW, false>), dim3(n_bg * unsigned(p.n_chunks)), block, 0, stream, p);
+        hipLaunchKernelGGL((decode_small_combine_kernel<T, D, R, GP, CW>), dim3(n_bg), dim3(kCombineThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
 template <typename T, int D, int R, int GP>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+    if (p.n_chunks > 0)
+        return p.chunk_keys == 128 ? launch_small<T, D, R, GP, 4>(p, stream) : launch_small<T, D, R, GP, 8>(p, stream);
     // slots x head groups of 8 (n_slots is a multiple of 8)
     const int64_t n_wg = int64_t(p.n_slots) * ((p.n_kv + kSplitWaves - 1) / kSplitWaves) + (p.X_new ? p.n_pre : 0);
     if (n_wg > 0) {

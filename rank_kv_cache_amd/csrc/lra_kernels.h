@@ -61,6 +61,11 @@ struct DecodeParams {
     int64_t ldx;
     int d_model;
     int n_pre;
+    // small batches (n_chunks 0: the split launch above): one workgroup per (request, KV head, chunk
+    // of chunk_keys = 128 or 256 keys), n_chunks chunks per request at max_kv_len; the records are
+    // then decode_small_record_slots() 16-byte slots per (request, KV head, chunk), merged by a
+    // second launch when n_chunks > 1
+    int n_chunks, chunk_keys;
 };
 
 struct PrecomputeParams {
@@ -226,6 +231,32 @@ int decode_slots(int batch, int n_kv, int64_t max_kv_len, int keys_per_split);
 inline int decode_record_slots(int G, int d_head, int rank) {
     const int GP = G <= 4 ? 4 : 8;
     return (GP * (d_head / 4 + rank / 4 + 1) + 15) / 16 * 16;
+}
+
+// Small-batch decode: requests are cut into chunks of 128 or 256 keys, one workgroup of 4 or 8 waves
+// (a 32-key tile each) per (request, KV head, chunk). Used for the library's default split when
+// few such workgroups cover the batch at max_kv_len (the split launch would give each of its slots
+// a tile or two): 128-key chunks while they fit one workgroup per CU, else 256-key chunks up to
+// two per CU (measured on MI355X: 64-key chunks, one per CU, cost more in the merge than they save
+// in the streaming). Returns the chunks per request (and their keys), or 0 for the split launch.
+constexpr int kDecodeSmallCUs = 256;
+inline int decode_small_chunks(int batch, int n_kv, int64_t max_kv_len, int keys_per_split, int* chunk_keys = nullptr) {
+    if (keys_per_split != 0 || batch <= 0 || n_kv <= 0 || max_kv_len <= 0) return 0;
+    const int64_t bg = int64_t(batch) * n_kv;
+    const int64_t c128 = (max_kv_len + 127) / 128, c256 = (max_kv_len + 255) / 256;
+    int keys = 0;
+    int64_t chunks = 0;
+    if (bg * c128 <= kDecodeSmallCUs) keys = 128, chunks = c128;
+    else if (bg * c256 <= 2 * kDecodeSmallCUs) keys = 256, chunks = c256;
+    if (chunk_keys) *chunk_keys = keys;
+    return int(chunks);
+}
+// 16-byte slots of one small-batch record (one request, KV head and chunk): the merged O^T and
+// O_lr^T fragments of the GP heads (d_head/16 + 1 tiles of 4*GP slots), then m and l of the GP
+// heads as floats
+inline int decode_small_record_slots(int G, int d_head) {
+    const int GP = G <= 4 ? 4 : 8;
+    return (d_head / 16 + 1) * 4 * GP + (2 * GP + 3) / 4;
 }
 
 // The slices of a decode launch over the batch's U units (32-key tiles, request after request):

@@ -559,3 +559,64 @@ def test_decode_workspace_shared_across_shapes_needs_no_initialisation():
             torch.cuda.synchronize()
             assert torch.equal(got, fresh)
         check(host64(got), ref_decode(c), "bf16", f"shared workspace case {i}")
+
+
+SMALL_SHAPES = [("bf16", 32, 8, 128, 8), ("bf16", 32, 8, 128, 16), ("bf16", 64, 8, 128, 8), ("bf16", 8, 2, 64, 8),
+                ("bf16", 24, 8, 64, 16), ("f32", 32, 8, 128, 8), ("f32", 8, 4, 64, 16)]
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d,r", SMALL_SHAPES)
+def test_small_batch_single_launch(dtype, n_q, n_kv, d, r):
+    """Requests of at most 128 keys (one chunk of 4 tiles): finished in one launch, empty ones zero,
+    invalid ones NaN."""
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype=dtype)
+    lens = [1, 31, 32, 33, 0, 100, 128, 97]
+    c = W.random_decode((120, n_q, n_kv, d, r), s, lens, agents=[0, 1, 2, -1, 1, 2, 0, 1])
+    say(f"decode small single launch {dtype} {n_q}/{n_kv} d={d} r={r}")
+    assert lra.lra_attn_decode_workspace_bytes(len(lens), n_q, n_kv, d, r, 128) > 0
+    got = run_decode(c)
+    check(got, ref_decode(c), dtype, "one chunk")
+    assert np.all(got[4] == 0.0)
+    kv_start = c.kv_start.copy()
+    kv_start[7] = -5
+    cc = W.DecodeBatch(s, c.Q, c.K, c.V, c.V_lr, c.B, kv_start, c.kv_len, c.agent)
+    got = run_decode(cc)
+    assert np.all(np.isnan(got[7]))
+    check(got[:7], ref_decode(c, requests=list(range(7))), dtype, "one chunk, an invalid request")
+
+
+@pytest.mark.parametrize("dtype,n_q,n_kv,d,r", SMALL_SHAPES)
+def test_small_batch_chunks_match_the_split_launch(dtype, n_q, n_kv, d, r):
+    """Several 256-key chunks per request (the small-batch launch and its merge) against the oracle,
+    and against the split launch (an explicit keys_per_split) within the same tolerance."""
+    s = W.Shape(n_q=n_q, n_kv=n_kv, d_head=d, rank=r, n_agents=3, d_model=256, dtype=dtype)
+    lens = [1900, 257, 512, 0, 1, 1300]
+    c = W.random_decode((121, n_q, n_kv, d, r), s, lens, agents=[0, 1, 2, 0, -1, 1])
+    say(f"decode small chunks {dtype} {n_q}/{n_kv} d={d} r={r}")
+    ref = ref_decode(c)
+    got = run_decode(c)
+    check(got, ref, dtype, "small-batch launch")
+    assert np.all(got[3] == 0.0)
+    check(run_decode(c, keys_per_split=256), ref, dtype, "split launch")
+
+
+def test_small_batch_single_launch_256_key_chunks():
+    """40 requests of at most 256 keys over 8 KV heads: one launch of 8-wave workgroups (256-key chunks)."""
+    s = W.LLAMA_SHAPE
+    lens = [int(x) for x in np.random.default_rng(123).integers(0, 257, size=40)]
+    lens[:4] = [256, 1, 0, 129]
+    c = W.random_decode((123,), s, lens, agents=[i % 4 - 1 for i in range(40)])
+    say("decode 40 requests of <= 256 keys")
+    got = run_decode(c)
+    check(got, ref_decode(c), "bf16", "one 256-key chunk")
+    assert np.all(got[2] == 0.0)
+
+
+def test_small_batch_threshold():
+    """Every regime of the small-batch choice over 8 KV heads: 2 requests of 1,900 keys (128-key
+    chunks), 3, 7 and 8 (256-key chunks, up to 512 workgroups) and 9 (the split launch)."""
+    s = W.LLAMA_SHAPE
+    for nreq in (2, 3, 7, 8, 9):
+        c = W.random_decode((122, nreq), s, [1900] * nreq, agents=[i % 3 for i in range(nreq)])
+        say(f"decode {nreq} x 1900 around the small-batch limit")
+        check(run_decode(c), ref_decode(c), "bf16", f"{nreq} requests")

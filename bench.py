@@ -493,6 +493,26 @@ def bench_precompute(args, torch, lra, W, out):
                                            "us_eager": round(ms * 1e3, 2),
                                            "timing": "HIP graph of 40 launches" if ms_g is not None else "eager",
                                            "x_copies_rotated": n_copies}
+    # the ceiling at this size: a plain streaming read of the same X copies, timed the same way
+    rd = torch.empty(1024, dtype=torch.int32, device="cuda")
+    best_rd = None
+    for n_wg in (256, 1024):
+        kt = [0]
+
+        def step_read():
+            lra.lra_stream_read(Xs[kt[0] % n_copies], n_wg, rd)
+            kt[0] += 1
+
+        ms_r = time_graph(step_read, n_copies, 10, torch)
+        if ms_r is not None and (best_rd is None or ms_r < best_rd[0]):
+            best_rd = (ms_r, n_wg)
+    if best_rd is not None:
+        x_bytes = Xs[0].numel() * Xs[0].element_size()
+        gbs_rd = x_bytes / (best_rd[0] * 1e-3) / 1e9
+        out["precompute_llama_2048x4096_r8"]["read_ceiling"] = {
+            "us": round(best_rd[0] * 1e3, 2), "gbs": round(gbs_rd, 1), "frac": round(gbs_rd / HBM_PEAK_GBS, 4),
+            "n_workgroups": best_rd[1], "bytes": x_bytes, "kernel": "lra_stream_read over the same X copies"}
+        out["precompute_llama_2048x4096_r8"]["frac_of_read_ceiling"] = round(gbs / gbs_rd, 4)
     if args.oracle_budget > 0:
         import oracle
         Xf, Af = case.X.as_f64(), case.A.as_f64()
@@ -517,9 +537,29 @@ def bench_precompute(args, torch, lra, W, out):
     ms_b = time_launches(step_big, 40, 4, torch)
     nb_b = precompute_bytes(T, s.d_model, s.n_agents * s.rank)
     gbs_b = nb_b / (ms_b * 1e-3) / 1e9
+    # the ceiling at this size: a plain streaming read of the same two copies of X, timed the same way
+    rd = torch.empty(2048, dtype=torch.int32, device="cuda")
+    best_rd = None
+    for n_wg in (256, 512, 1024, 2048):
+        kt = [0]
+
+        def step_read():
+            lra.lra_stream_read(Xb[kt[0] % 2], n_wg, rd)
+            kt[0] += 1
+
+        ms_r = time_launches(step_read, 40, 4, torch)
+        if best_rd is None or ms_r < best_rd[0]:
+            best_rd = (ms_r, n_wg)
+    x_bytes = Xb[0].numel() * Xb[0].element_size()
+    gbs_rd = x_bytes / (best_rd[0] * 1e-3) / 1e9
     out["precompute_llama_18432x4096_r8"] = {"us": round(ms_b * 1e3, 2), "gbs": round(gbs_b, 1), "bytes": nb_b,
                                             "frac": round(gbs_b / HBM_PEAK_GBS, 4), "bound": "hbm",
-                                            "timing": "eager, two copies of X alternating"}
+                                            "timing": "eager, two copies of X alternating",
+                                            "read_ceiling": {"us": round(best_rd[0] * 1e3, 2), "gbs": round(gbs_rd, 1),
+                                                             "frac": round(gbs_rd / HBM_PEAK_GBS, 4),
+                                                             "n_workgroups": best_rd[1], "bytes": x_bytes,
+                                                             "kernel": "lra_stream_read over the same X copies"},
+                                            "frac_of_read_ceiling": round(gbs_b / gbs_rd, 4)}
     if args.oracle_budget > 0:
         import oracle
         Xf, Af = big.X.as_f64()[:4096], big.A.as_f64()

@@ -58,6 +58,9 @@ def test_ministral_precompute_scatter_into_cache():
     ("bf16", 33, 4096, 2, 8), ("bf16", 70, 8192, 3, 8), ("f32", 40, 4096, 3, 8), ("bf16", 300, 12288, 3, 16),
     # 4096 rows and more take 32-column groups: with At reloaded per batch, and in fp32
     ("bf16", 4200, 8192, 3, 8), ("f32", 4500, 256, 3, 8),
+    # 8-wave workgroups with both column tiles' At in registers (bf16, 17..32 columns, d_model up to
+    # 4096): ragged row ranges, 32 columns, one agent of rank 24
+    ("bf16", 4100, 4096, 2, 16), ("bf16", 5000, 2048, 3, 8), ("bf16", 4111, 4096, 1, 24), ("bf16", 8200, 4096, 3, 8),
 ])
 def test_precompute_shapes(dtype, T, d_model, N, r):
     s = W.Shape(n_q=4, n_kv=2, d_head=64, rank=r, n_agents=N, d_model=d_model, dtype=dtype)
@@ -98,3 +101,20 @@ def test_llama_precompute_whole_context_every_row():
     say("precompute 18432 x 4096 -> 24")
     got = run_pre(case, np.zeros((18432, 24)))
     check(got, oracle.lr_precompute(case.X.as_f64(), case.A.as_f64()), "bf16")
+
+
+def test_precompute_long_x_scatter():
+    """6,000 rows of 4,096 -> 24 (32-column groups) written through a row map: a permutation of the
+    cache's rows with some entries outside it (skipped)."""
+    s = W.LLAMA_SHAPE
+    T = 6000
+    case = W.random_precompute((202, T), s, T)
+    rows = np.random.default_rng(202).permutation(T + 100)[:T].astype(np.int64)
+    rows[5] = -1
+    rows[77] = T + 100
+    cache = np.full((T + 100, 24), 3.0)
+    say("precompute long X, scattered rows")
+    got = run_pre(case, cache, rows)
+    keep = (rows >= 0) & (rows < T + 100)
+    ref = oracle.lr_precompute_into(cache, case.X.as_f64()[keep], case.A.as_f64(), rows[keep])
+    check(got, ref, "bf16")

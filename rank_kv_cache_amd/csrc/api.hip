@@ -91,6 +91,13 @@ int check_heads(int32_t n_q, int32_t n_kv, int32_t d_head, int32_t rank) {
     return LRA_OK;
 }
 
+// contiguous prefill caches are read through 32-bit buffer offsets over 64-row tiles
+int check_prefill_rows(int32_t n_kv, int32_t d_head, int64_t ld_vlr) {
+    if (int64_t(n_kv) * d_head > (int64_t(1) << 22)) return fail(LRA_ERR_SHAPE, "n_kv*d_head exceeds 2^22");
+    if (ld_vlr > (int64_t(1) << 22)) return fail(LRA_ERR_SHAPE, "ld_vlr=%lld exceeds 2^22", (long long)ld_vlr);
+    return LRA_OK;
+}
+
 int check_dtype(int dtype) {
     if (dtype != LRA_F32 && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "dtype=%d", dtype);
     return LRA_OK;
@@ -187,6 +194,7 @@ int prefill_single(const char* name, int dtype, const void* Q, int64_t L_C, int6
     if (int s = check_dtype(dtype)) return s;
     if (kl && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "%s: bf16 only", name);
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (int s = check_prefill_rows(n_kv, d_head, ld_vlr)) return s;
     if (L_C < 0 || L_P < 0) return fail(LRA_ERR_SHAPE, "L_C=%lld and L_P=%lld must be >= 0", (long long)L_C, (long long)L_P);
     if (L_P + L_C > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "L_P + L_C exceeds 2^31 - 1");
     if (n_agents <= 0) return fail(LRA_ERR_SHAPE, "n_agents=%d must be positive", n_agents);
@@ -277,6 +285,7 @@ LRA_EXPORT int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows,
                                        void* O, void* stream) {
     if (int s = check_dtype(dtype)) return s;
     if (int s = check_heads(n_q, n_kv, d_head, rank)) return s;
+    if (int s = check_prefill_rows(n_kv, d_head, ld_vlr)) return s;
     if (batch < 0 || q_rows < 0 || kv_rows < 0 || max_q_len < 0)
         return fail(LRA_ERR_SHAPE, "batch, q_rows, kv_rows and max_q_len must be >= 0");
     if (max_q_len > (int64_t(1) << 31) - 1) return fail(LRA_ERR_SHAPE, "max_q_len exceeds 2^31 - 1");

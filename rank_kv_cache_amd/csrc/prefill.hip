@@ -48,6 +48,25 @@ namespace lra {
 
 namespace {
 
+typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
+// 8 elements at byte offset off of a buffer (zeros past its range)
+template <typename T>
+__device__ __forceinline__ void buffer_load8(Vec<T, 8>& v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    if constexpr (sizeof(T) == 2) {
+        const pf_u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v.w[i] = x[i];
+    } else {
+        const pf_u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const pf_u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v.v[i] = __uint_as_float(x0[i]);
+            v.v[4 + i] = __uint_as_float(x1[i]);
+        }
+    }
+}
+
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMT = 2;                          // 16-row tiles per wave
@@ -299,12 +318,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             }
         }
 
-        // ---- tile fetch (registers) and store (LDS); keys past kv_end read row kv_end-1 (finite, P = 0)
+        // ---- tile fetch (registers) and store (LDS). A contiguous cache is read through a buffer
+        // at the tile's first row whose range ends at row kv_end, with this thread's byte offsets in
+        // a tile fixed for the pass: the loads take no vector address arithmetic, and keys past
+        // kv_end read zeros. A paged cache reads row kv_end-1 for them. Either way they get P = 0.
         Vec<T, 8> kpre[KF], vpre[KF], lpre;
         lpre.zero();   // the adapter-free view stages zero V_lr columns
         pg_base = -(1 << 30);
+        uint32_t koff[KF];
+#pragma unroll
+        for (int c = 0; c < KF; ++c) {
+            const int f = tid + kThreads * c;
+            const int key = f / (D / 8);
+            koff[c] = uint32_t((int64_t(key) * kv_stride + int64_t(g) * D + (f - key * (D / 8)) * 8) * int64_t(sizeof(T)));
+        }
+        const uint32_t loff = uint32_t((int64_t(tid / (R / 8)) * p.ld_vlr + (tid % (R / 8)) * 8) * int64_t(sizeof(T)));
         auto fetch = [&](int t) {
             const int kb = t * kBK;
+            if constexpr (!PAGED) {
+                const uint32_t rows = uint32_t(min(kBK, kv_end - kb));   // >= 1
+                const uint32_t kv_bytes = rows * uint32_t(kv_stride * int64_t(sizeof(T)));   // < 2^31 (host bound)
+                const __amdgpu_buffer_rsrc_t rk =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Kp + int64_t(kb) * kv_stride), 0, int(kv_bytes), 0x00020000);
+                const __amdgpu_buffer_rsrc_t rv =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Vp + int64_t(kb) * kv_stride), 0, int(kv_bytes), 0x00020000);
+#pragma unroll
+                for (int c = 0; c < KF; ++c) {
+                    if constexpr (!KREBUILD) buffer_load8(kpre[c], rk, koff[c]);
+                    buffer_load8(vpre[c], rv, koff[c]);
+                }
+                if (tid < LF && adapted) {
+                    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<T*>(Lp + int64_t(kb) * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride), 0,
+                        int(rows * uint32_t(p.ld_vlr * int64_t(sizeof(T)))), 0x00020000);
+                    buffer_load8(lpre, rl, loff);
+                }
+                return;
+            }
             int64_t page_off = 0;   // cache row of key j = j + page_off for every key j of the tile
             if constexpr (PAGED) {
                 const int pi = kb >> p.page_shift;
@@ -442,6 +492,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             for (int x = 0; x < NAUX; ++x) xacc[mt][x] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
+        // a lane's transpose reads start at key 4q + n/4 of a 32-key block, columns 4(n%4) ..
+        const int tr_v = (4 * q + (n >> 2)) * LDV + 4 * (n & 3);
+        const int tr_x = (4 * q + (n >> 2)) * LDX + 4 * (n & 3);
         // scores, softmax and P.V of tile t staged in buffer buf
         auto tile_step = [&](int t, int buf) {
             const T* ks = sh.k[buf];
@@ -587,12 +640,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                             }
                         }
                         if constexpr (sizeof(T) == 2) {
-                            const int rkey = 32 * bb + 4 * q + (n >> 2);
-                            const int rcol = 4 * (n & 3);
+                            // this lane's transpose-read addresses: one add per buffer, the rest immediates
+                            const TV* vrow = vs + tr_v + 32 * bb * LDV;
+                            const TV* xrow = xs + tr_x + 32 * bb * LDX;
 #pragma unroll
                             for (int dt = 0; dt < NDT; ++dt) {
-                                const uint2 lo = lds_read_tr16(&vs[rkey * LDV + 16 * dt + rcol]);
-                                const uint2 hi = lds_read_tr16(&vs[(rkey + 16) * LDV + 16 * dt + rcol]);
+                                const uint2 lo = lds_read_tr16(vrow + 16 * dt);
+                                const uint2 hi = lds_read_tr16(vrow + 16 * LDV + 16 * dt);
                                 H8 va;
                                 va.w[0] = lo.x; va.w[1] = lo.y; va.w[2] = hi.x; va.w[3] = hi.y;
 #pragma unroll
@@ -600,8 +654,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                             }
 #pragma unroll
                             for (int x = 0; x < NAUX; ++x) {
-                                const uint2 lo = lds_read_tr16(&xs[rkey * LDX + 16 * x + rcol]);
-                                const uint2 hi = lds_read_tr16(&xs[(rkey + 16) * LDX + 16 * x + rcol]);
+                                const uint2 lo = lds_read_tr16(xrow + 16 * x);
+                                const uint2 hi = lds_read_tr16(xrow + 16 * LDX + 16 * x);
                                 H8 xa;
                                 xa.w[0] = lo.x; xa.w[1] = lo.y; xa.w[2] = hi.x; xa.w[3] = hi.y;
 #pragma unroll

@@ -154,7 +154,9 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * its rows with bf16 V_base / V_lr (scaled by a power of two when huge) and the probabilities split
  * into two bf16 parts, so every finite input is accepted. l, m, O and O_lr are fp32; scores and the
  * unnormalised sums must stay finite in fp32.
- * Every tensor pointer must be 16-byte aligned. L_C = 0 enqueues nothing.
+ * Every tensor pointer must be 16-byte aligned. n_kv*d_head and ld_vlr must not exceed 2^22 (the
+ * kernel reads 64-row tiles through 32-bit offsets); larger values return LRA_ERR_SHAPE. L_C = 0
+ * enqueues nothing.
  */
 int lra_attn_prefill(int dtype, const void* Q, int64_t L_C, int64_t L_P,
                      const void* K_base, const void* V_base, const void* V_lr, int64_t ld_vlr,
@@ -219,7 +221,7 @@ int lra_attn_prefill_qkvo(int dtype, const void* Q, int64_t L_C, int64_t L_P,
  * A request with q_len[b] = 0 writes nothing; one whose query rows fall outside [0, q_rows) is
  * skipped. One with q_len[b] > max_q_len, a cache range outside [0, kv_rows), kv_prefix[b]+q_len[b]
  * >= 2^31 or an agent outside [-1, n_agents) gets NaN in all its output rows. Precision (with the
- * range-safe recomputation) and alignment are as for lra_attn_prefill.
+ * range-safe recomputation), alignment and the 2^22 bounds are as for lra_attn_prefill.
  * batch = 0 or max_q_len = 0 enqueues nothing.
  */
 int lra_attn_prefill_varlen(int dtype, const void* Q, int64_t q_rows, int32_t batch,

@@ -475,3 +475,11 @@ def test_binding_rejects_host_tensors_before_any_launch():
 ])
 def test_stream_read_rejects_bad_arguments(x, nbytes, n_wg, out, status):
     assert lra._lib.lra_stream_read(x, nbytes, n_wg, out, 0) == status
+
+
+
+def test_prefill_rejects_rows_beyond_32_bit_tile_offsets():
+    """n_kv*d_head or ld_vlr above 2^22: the contiguous prefill reads 64-row tiles through 32-bit
+    buffer offsets, so the host refuses them (before any pointer is used)."""
+    assert prefill(n_q=32769, n_kv=32769, d=128) == E_SHAPE           # n_kv*d_head = 2^22 + 128
+    assert prefill(ld_vlr=(1 << 22) + 8, vas=8) == E_SHAPE

@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                     if constexpr (WIDE) {
                         hv[e2] = pack_bf16x2(lo * vscale, hi * vscale);
                     } else {
-                        vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+                        vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));   // one three-input max per pair
                         hv[e2] = pack_f16x2(lo, hi);
                     }
                 }
@@ -558,10 +558,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 bool any_grow = false;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    float m = fmaxf(fmaxf(sacc[mt][0][0], sacc[mt][0][1]), fmaxf(sacc[mt][0][2], sacc[mt][0][3]));
+                    // a chain of three-input maxima (the row tiles' chains are independent)
+                    float m = fmaxf(sacc[mt][0][0], sacc[mt][0][1]);
+                    m = fmaxf(fmaxf(m, sacc[mt][0][2]), sacc[mt][0][3]);
 #pragma unroll
-                    for (int u = 1; u < 2 * NB; ++u)
-                        m = fmaxf(m, fmaxf(fmaxf(sacc[mt][u][0], sacc[mt][u][1]), fmaxf(sacc[mt][u][2], sacc[mt][u][3])));
+                    for (int u = 1; u < 2 * NB; ++u) {
+                        m = fmaxf(fmaxf(m, sacc[mt][u][0]), sacc[mt][u][1]);
+                        m = fmaxf(fmaxf(m, sacc[mt][u][2]), sacc[mt][u][3]);
+                    }
                     lmx[mt] = m;
                     any_grow |= lmx[mt] > m_thr[mt];
                 }

@@ -423,8 +423,10 @@ int lra_attn_decode_qkvo(int dtype, const void* Q, int32_t batch,
                          int32_t keys_per_split, void* workspace, size_t workspace_bytes,
                          void* O, void* stream);
 
-/* Keys per slice of the library's choice (keys_per_split = 0) when every request has max_kv_len
- * keys, rounded up to a multiple of 64 (passing it may round the slice count differently). */
+/* Keys per slice of the library's choice for the split launch (keys_per_split = 0) when every
+ * request has max_kv_len keys, rounded up to a multiple of 64 (passing it may round the slice count
+ * differently). Passing it explicitly always selects the split launch; with 0, small batches take the
+ * chunked launch described at lra_attn_decode instead. */
 int32_t lra_attn_decode_default_split(int32_t batch, int32_t n_kv, int64_t max_kv_len);
 
 /* ------------------------------------------------------------------------------------------------

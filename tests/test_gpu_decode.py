@@ -620,3 +620,21 @@ def test_small_batch_threshold():
         c = W.random_decode((122, nreq), s, [1900] * nreq, agents=[i % 3 for i in range(nreq)])
         say(f"decode {nreq} x 1900 around the small-batch limit")
         check(run_decode(c), ref_decode(c), "bf16", f"{nreq} requests")
+
+
+def test_small_batch_chunks_invalid_and_empty_requests():
+    """The chunked launch's merge: requests with a bad range, a bad agent, no keys, and valid ones
+    of several chunks side by side; valid rows match the oracle, invalid rows are NaN, empty zero."""
+    s = W.LLAMA_SHAPE
+    c = W.random_decode((124,), s, kv_lens=[900, 300, 0, 700, 513], kv_starts=[0, 100, 0, 50, 200], rows=1000,
+                        agents=[0, 1, 2, 2, 1])
+    kv_start = c.kv_start.copy()
+    agent = c.agent.copy()
+    kv_start[1] = 800          # 800 + 300 runs past the 1,000 cache rows
+    agent[3] = 7               # no such agent
+    cc = W.DecodeBatch(s, c.Q, c.K, c.V, c.V_lr, c.B, kv_start, c.kv_len, agent)
+    say("decode chunked launch, invalid and empty requests")
+    got = run_decode(cc)
+    assert np.all(np.isnan(got[[1, 3]]))
+    assert np.all(got[2] == 0.0)
+    check(got[[0, 4]], ref_decode(c, requests=[0, 4]), "bf16", "valid requests beside invalid ones")

@@ -33,12 +33,14 @@
 //   * keys past the piece's end are clamped to its last row (finite data) and get P = 0, so no row
 //     outside [kv_start, kv_start+kv_len) is read
 //   * each wave writes one fp32 partial (m, l, O, O_lr) per query head of its group and piece
-//   * a second kernel, one workgroup per (request, query head), merges the request's partials with
+//   * a second kernel, one workgroup per (request, KV head), merges the request's partials with
 //     weights 2^(m_s - max m), applies O = (O + O_lr B_agent[:, g*d..]) / l once per query row and
 //     rounds to the output type. Empty requests get zeros and requests with an invalid range or
 //     agent NaN. The kernel boundary orders the partial writes before the merge: a device-scope
 //     fence per workgroup (to let the last piece merge in place) writes back and invalidates an
 //     XCD's L2, which cost more than the whole merge at thousands of workgroups.
+// Small batches (few tiles in all) take a chunked launch instead, defined further down: one
+// workgroup per (request, KV head, 128- or 256-key chunk), its tiles merged in LDS.
 #include <algorithm>
 #include <type_traits>
 

@@ -645,6 +645,26 @@ def bench_short_decode(args, torch, lra, W, out):
                                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "latency (7.8 MB)",
                                        "us_eager": round(ms * 1e3, 2),
                                        "timing": "HIP graph of 64 calls" if ms_g is not None else "eager"}
+    # context: one plain streaming read of about the same bytes per call, rotated and timed the same way
+    n_rd = 7 << 20   # 7 MiB, a multiple of 16 x 1024
+    bufs = [torch.empty(n_rd // 4, dtype=torch.int32, device="cuda") for _ in range(n_copies)]
+    rd = torch.empty(1024, dtype=torch.int32, device="cuda")
+    best_rd = None
+    for n_wg in (128, 256, 1024):
+        kt = [0]
+
+        def step_read():
+            lra.lra_stream_read(bufs[kt[0] % n_copies], n_wg, rd)
+            kt[0] += 1
+
+        t_rd = time_graph(step_read, n_copies, 10, torch)
+        if t_rd is not None and (best_rd is None or t_rd < best_rd[0]):
+            best_rd = (t_rd, n_wg)
+    if best_rd is not None:
+        out["decode_llama_b1_L1900_r8"]["read_floor"] = {
+            "us": round(best_rd[0] * 1e3, 2), "bytes": n_rd, "n_workgroups": best_rd[1],
+            "kernel": "lra_stream_read of 7 MiB in one launch (HIP graph, 64 rotated buffers)"}
+    del bufs
     if args.oracle_budget > 0:
         import oracle
         f = [t.as_f64() for t in (c.Q, c.K, c.V, c.V_lr, c.B)]

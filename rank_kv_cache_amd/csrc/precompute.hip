@@ -40,7 +40,9 @@ __global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams
     constexpr int kThreads = 64 * WAVES;
     constexpr int NC = 16 * NT;   // columns of a group
     constexpr bool PREFETCH = ARES && (NT == 1 || WAVES == 8);
-    __shared__ float red[kWaves][16][NC + 1];
+    // partial tiles, double-buffered: tile t sums from half t % 2, so one barrier per tile orders
+    // both the partials before the sums and the sums before the next writes to that half
+    __shared__ float red[2][kWaves][16][NC + 1];
 
     const int w = blockIdx.x, xcd = w & 7, rest = w >> 3;
     const int cg = rest % p.n_cg;
@@ -85,6 +87,7 @@ __global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams
     };
     if constexpr (PREFETCH) load_x(r0, kc0);
 
+    int rb = 0;
     for (int64_t rt = r0; rt < r1; rt += 16) {
         f32x4 acc[NT];
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) red[wv][4 * q + j][16 * nt + n] = acc[nt][j];
+            for (int j = 0; j < 4; ++j) red[rb][wv][4 * q + j][16 * nt + n] = acc[nt][j];
         __syncthreads();
         const int nrows = int(min<int64_t>(16, r1 - rt));
         for (int idx = tid; idx < nrows * ncol; idx += kThreads) {
@@ -123,13 +126,13 @@ __global__ __launch_bounds__(64 * WAVES) void precompute_kernel(PrecomputeParams
             const int c = idx - rr * ncol;
             float v = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) v += red[ww][rr][c];
+            for (int ww = 0; ww < kWaves; ++ww) v += red[rb][ww][rr][c];
             const int64_t orow = p.out_rows ? p.out_rows[rt + rr] : rt + rr;
             const int ka = (c0 + c) / p.rank;   // agent of output column c0 + c
             if (orow >= 0 && orow < p.vlr_rows)
                 static_cast<T*>(p.Vlr)[orow * p.ld_vlr + ka * p.vlr_agent_stride + (c0 + c - ka * p.rank)] = from_f32<T>(v);
         }
-        __syncthreads();   // red is reused by the next tile
+        rb ^= 1;
     }
 }
 

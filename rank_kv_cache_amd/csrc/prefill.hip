@@ -26,9 +26,11 @@
 //     operand directly: two per 16-d tile give lane n column d0+n of the lane group's 8 keys.
 //   * bf16 inputs: Q.K runs on bf16 steps; P.V on fp16 steps, with V and V_lr converted bf16 ->
 //     fp16 once while they are staged (exact for |v| <= 65504) and P rounded to fp16. A workgroup
-//     that meets a value beyond the fp16 range runs a second, range-safe pass over its tiles
+//     whose fp32 sums left the finite range (a value beyond the fp16 range became inf) or whose
+//     scores are too large for the folded exponent runs a second, range-safe pass over its tiles
 //     (workgroup-uniform, so the fast pass never pays for it): bf16 V and V_lr, scaled by a power
-//     of two when huge, and P split into bf16 hi + lo parts (two steps, ~16 bits of P).
+//     of two when huge, exact differences to the row max, and P split into bf16 hi + lo parts (two
+//     steps, ~16 bits of P).
 //   * one more 16-column tile holds the agent's V_lr slice (columns 0..r-1) and a column of ones:
 //     O_lr^T and the softmax normaliser l come out of the same matrix-core product as O (l is the
 //     sum of exactly the rounded P the products used). For r = 16 the ones column is a second tile.
@@ -100,7 +102,8 @@ struct PrefillShared {
     // k[0], middle in k[1], low here; and the agent's B_k slice of this KV head
     alignas(16) T klo[KLORA ? kBK * LDK : 1];
     alignas(16) float bk[KLORA ? R * D : 1];
-    int range_bad;    // bit 1: a bad page id; bit 2: a row max too large for the fast pass's fma
+    int range_bad;    // bit 1: a bad page id; bit 2: a row max too large for the fast pass's fma;
+                      // bit 3: a non-finite accumulator after the fast pass
     uint32_t vmax_bits, qmax_bits, kmax_bits;   // largest |V|, |Q|, |expanded key| met (fp32 bits)
 };
 
@@ -244,7 +247,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         for (int t = tid; t < n_tiles; t += kThreads) kmax = fmaxf(kmax, __int_as_float(p.key_flags[int64_t(t) * n_kv + g]));
     }
 
-    float vmax = 0.f;     // largest |V| / |V_lr| staged by this thread in the fast pass
     float qmax = 0.f;     // largest |Q| entry of this lane's rows (LoRA on the keys)
     float vscale = 1.f;   // power of two the range-safe pass applies to V and V_lr as it stages them
     float unscale = 1.f;  // its inverse, applied to the outputs
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
     // One pass over the key tiles, then the epilogue. The fast pass (WIDE = false) takes P.V on fp16
     // steps (and, with LoRA on the keys, the scores on fp16 steps over the expanded fp16 keys), with
-    // double-buffered tiles. A workgroup whose staged values left the fp16 range (or, with LoRA on
+    // double-buffered tiles. A workgroup whose fp32 sums left the finite range (a staged value
+    // beyond the fp16 range), whose scores are too large for the folded exponent (or, with LoRA on
     // the keys, whose queries and keys are too large for fp16 precision) runs the range-safe pass
     // (WIDE = true) after it, which rewrites the same rows; it stages one tile at a time: bf16 V and
     // V_lr (scaled by vscale, a power of two, when they are huge), P as a bf16 hi + lo pair, and with
@@ -385,20 +388,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride + r0);
             }
         };
-        // 8 values of one key's row in the pass's P.V element type: fp16 (exact within its range;
-        // the largest magnitude is tracked), bf16 times vscale (range-safe pass), or fp32
+        // 8 values of one key's row in the pass's P.V element type: fp16 (exact within its range),
+        // bf16 times vscale (range-safe pass), or fp32
         auto put8 = [&](TV* dst, const Vec<T, 8>& src) {
             if constexpr (sizeof(T) == 2) {
                 uint32_t hv[4];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const float lo = bf16_lo(src.w[e2]), hi = bf16_hi(src.w[e2]);
-                    if constexpr (WIDE) {
-                        hv[e2] = pack_bf16x2(lo * vscale, hi * vscale);
-                    } else {
-                        vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));   // one three-input max per pair
-                        hv[e2] = pack_f16x2(lo, hi);
-                    }
+                    if constexpr (WIDE) hv[e2] = pack_bf16x2(lo * vscale, hi * vscale);
+                    else hv[e2] = pack_f16x2(lo, hi);   // beyond the fp16 range: inf (checked after the pass)
                 }
                 *reinterpret_cast<uint4*>(dst) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
             } else {
@@ -705,6 +704,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 __syncthreads();
             }
         } else {
+            // the largest |V| / |V_lr| of the staged keys (read once more) brings them to at most 2^64
+            // by a power of two, so the unnormalised fp32 sums (at most 2^31 keys, P < 2^9) cannot
+            // overflow; the outputs are multiplied back
+            if constexpr (sizeof(T) == 2) {
+                float vm = 0.f;
+                for (int t = 0; t < n_tiles; ++t) {
+                    fetch(t);
+#pragma unroll
+                    for (int c = 0; c < KF; ++c)
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2)
+                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(vpre[c].w[e2]))), fabsf(bf16_hi(vpre[c].w[e2])));
+                    if (tid < LF && adapted) {
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2)
+                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(lpre.w[e2]))), fabsf(bf16_hi(lpre.w[e2])));
+                    }
+                }
+                atomicMax(&sh.vmax_bits, __float_as_uint(vm));   // |v| >= 0: the bits order like the values
+                __syncthreads();
+                const int ex = int((sh.vmax_bits >> 23) & 0xffu) - 127;
+                const int e = max(0, ex - 63);   // <= 65
+                vscale = __uint_as_float(uint32_t(127 - e) << 23);
+                unscale = __uint_as_float(uint32_t(127 + e) << 23);
+            }
             // one tile at a time (the key parts use both K buffers)
             for (int t = 0; t < n_tiles; ++t) {
                 fetch(t);
@@ -716,9 +740,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             }
         }
 
-        // ---- after the fast pass: the workgroup's largest |V| / |V_lr| (and, with LoRA on the keys,
-        // |Q| and |expanded key|) decide whether the range-safe pass runs next; a bad page id poisons
-        // the rows
+        // ---- after the fast pass: non-finite sums (a staged value beyond the fp16 range), a row max
+        // too large for the folded exponent (and, with LoRA on the keys, the largest |Q| and
+        // |expanded key|) decide whether the range-safe pass runs next; a bad page id poisons the rows
         if constexpr (!WIDE) {
             // The fast pass folds the row max m into one fma per score; that fma's rounding, 2^-24 of
             // |m| scale log2(e), must stay negligible in the exponent. m only grows, and an earlier
@@ -727,7 +751,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             bool big_scores = false;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) big_scores = big_scores || !(fabsf(m_run[mt] * sl2) <= kFoldedMaxLog2 - 256.f);
-            if constexpr (sizeof(T) == 2) atomicMax(&sh.vmax_bits, __float_as_uint(vmax));   // |v| >= 0: the bits order like the values
+            if constexpr (sizeof(T) == 2) {
+                // A staged V / V_lr entry beyond the fp16 range became inf, and every staged key is
+                // multiplied by some row's probability (inf x 0 is NaN on the matrix cores), so it
+                // leaves a non-finite accumulator; so does a non-finite input. Either sends the
+                // workgroup to the range-safe pass.
+                // (Exponent bits, hidden from the optimiser, not a float compare: this file is built
+                // without NaN semantics, which would let a NaN test fold away.)
+                auto inf_or_nan = [](float x) {
+                    uint32_t b = __float_as_uint(x);
+                    asm("" : "+v"(b));
+                    return uint32_t((b & 0x7f800000u) == 0x7f800000u);
+                };
+                uint32_t nonfinite = 0u;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) nonfinite |= inf_or_nan(oacc[mt][dt][j]);
+#pragma unroll
+                    for (int x = 0; x < NAUX; ++x)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) nonfinite |= inf_or_nan(xacc[mt][x][j]);
+                }
+                if (nonfinite) atomicOr(&sh.range_bad, 8);
+            }
             if constexpr (KLORA) {
                 atomicMax(&sh.qmax_bits, __float_as_uint(qmax));
                 atomicMax(&sh.kmax_bits, __float_as_uint(kmax));
@@ -775,21 +824,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
     pass(std::false_type{});
     if constexpr (sizeof(T) == 2) {
-        const float vm = __uint_as_float(sh.vmax_bits);
-        bool wide = !(vm <= kF16Max) || (sh.range_bad & 4) != 0;
+        bool wide = (sh.range_bad & (4 | 8)) != 0;
         if constexpr (KLORA) {
             const float qm = __uint_as_float(sh.qmax_bits), km = __uint_as_float(sh.kmax_bits);
             wide = wide || !(qm <= kF16Max) || !(km <= kF16Max) || !(qm * km <= kKeyQueryProductMax);
         }
-        if (wide) {   // workgroup-uniform
-            // bring the largest |V| / |V_lr| to at most 2^64, so the unnormalised fp32 sums (at most
-            // 2^31 keys, P < 2^9) cannot overflow; the outputs are multiplied back
-            const int ex = int((sh.vmax_bits >> 23) & 0xffu) - 127;
-            const int e = max(0, ex - 63);   // <= 65
-            vscale = __uint_as_float(uint32_t(127 - e) << 23);
-            unscale = __uint_as_float(uint32_t(127 + e) << 23);
-            pass(std::true_type{});
-        }
+        if (wide) pass(std::true_type{});   // workgroup-uniform
     }
 }
 

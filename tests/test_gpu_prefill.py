@@ -180,25 +180,31 @@ def test_prefill_is_deterministic():
     assert np.array_equal(run_prefill(c), run_prefill(c))
 
 
-@pytest.mark.parametrize("big", [1.0e5, 1.0e30])
-def test_prefill_values_beyond_fp16_range_match_the_oracle(big):
-    """Entries of V_base and of the agent's V_lr slice beyond the fp16 range (65504) send the
-    workgroups that stage them through the range-safe pass (bf16 values, P as hi + lo parts, a
-    power-of-two prescale when huge): every row still matches the oracle, including rows that never
-    see the large key but share its workgroup, and rows of other KV heads (fast pass)."""
+@pytest.mark.parametrize("big", [1.0e5, 1.0e30, 3.0e38])
+def test_prefill_large_values_match_the_oracle(big):
+    """Large entries of V_base and of the agent's V_lr slice: beyond the fp16 range (1e5, 1e30) they
+    stage as inf in the fast pass's fp16 operands, and near the bf16 maximum (3e38 on several keys)
+    even exact fp32 sums would overflow; either leaves non-finite sums, which send the workgroup
+    through the range-safe pass (bf16 values prescaled by a power of two, P as hi + lo parts). Every
+    row still matches the oracle, including rows that never see the large keys but share their
+    workgroup, and rows of other KV heads."""
     s = W.LLAMA_SHAPE
     c = W.random_prefill((306,), s, 40, 60, agent=1)
     V = c.V.as_f32()
-    V[10, 3, 7] = big          # seen by every query row of KV head 3
+    if big > 1e36:
+        V[10:22, 3, 7] = big   # twelve keys seen by every query row of KV head 3: their sum overflows
+    else:
+        V[10, 3, 7] = big      # seen by every query row of KV head 3
     V[95, 3, 0] = -big         # seen only by the last query rows (position 95 = L_P + 55)
     V[50, 6, 127] = big
+    lr_big = min(big, 1.0e30)  # O_lr B must stay inside the bf16 range of the output
     Vlr = c.V_lr.as_f32()
-    Vlr[33, 1 * s.rank + 2] = big   # agent 1's slice: every head's rows carry it through B
-    Vlr[7, 0] = np.float32(big)     # agent 0's columns: not read for agent 1
+    Vlr[33, 1 * s.rank + 2] = lr_big   # agent 1's slice: every head's rows carry it through B
+    Vlr[7, 0] = np.float32(lr_big)     # agent 0's columns: not read for agent 1
     cc = W.PrefillCase(s, c.Q, c.K, W.to_storage(V, "bf16"), W.to_storage(Vlr, "bf16"), c.B, 40, 60, 1)
-    say(f"prefill values beyond the fp16 range ({big:g})")
+    say(f"prefill large values ({big:g})")
     check(run_prefill(cc), ref_prefill(cc), "bf16", f"V = {big:g}")
-    # the same with values just inside the fp16 range stay on the fast pass and match too
+    # the fp16 maximum itself stays on the fast pass
     V2 = c.V.as_f32()
     V2[10, 3, 7] = 65504.0
     c2 = W.PrefillCase(s, c.Q, c.K, W.to_storage(V2, "bf16"), c.V_lr, c.B, 40, 60, 1)
@@ -222,7 +228,7 @@ def test_prefill_huge_scores_match_the_oracle():
     check(run_prefill(cc), ref_prefill(cc), "bf16", "huge scores")
 
 
-def test_prefill_values_beyond_fp16_range_varlen_and_paged():
+def test_prefill_large_values_varlen_and_paged():
     """The range-safe pass serves the batched and the paged calls too (same kernel): a huge value in
     one request's rows leaves every request's rows at the oracle's values."""
     s = W.LLAMA_SHAPE
@@ -232,7 +238,7 @@ def test_prefill_values_beyond_fp16_range_varlen_and_paged():
     Vlr = c.V_lr.as_f32()
     Vlr[int(c.kv_start[0]) + 2, 0 * s.rank + 1] = -2.0e6
     cb = dataclasses.replace(c, V=W.to_storage(V, "bf16"), V_lr=W.to_storage(Vlr, "bf16"))
-    say("prefill varlen values beyond the fp16 range")
+    say("prefill varlen large values")
     got = run_prefill_varlen(cb)
     rows = covered_rows(cb)
     check(got[rows], ref_prefill_varlen(cb)[rows], "bf16")

@@ -150,10 +150,11 @@ int lra_lr_precompute(int dtype, const void* X, int64_t T, int32_t d_model, int6
  * O        (device) [L_C x n_q x d_head] output
  * bf16 inputs: Q.K products are exact (bf16 operands, fp32 accumulation). For P.V the
  * probabilities are rounded to fp16 and V_base / V_lr converted exactly to fp16; a workgroup (256
- * query rows of one KV head) that stages an entry beyond the fp16 range (|v| > 65504) recomputes
- * its rows with bf16 V_base / V_lr (scaled by a power of two when huge) and the probabilities split
- * into two bf16 parts, so every finite input is accepted. l, m, O and O_lr are fp32; scores and the
- * unnormalised sums must stay finite in fp32.
+ * query rows of one KV head) whose sums come out non-finite (it staged an entry beyond the fp16
+ * range, |v| > 65504, or its fp32 sums overflowed near the bf16 maximum) recomputes its rows with
+ * bf16 V_base / V_lr (scaled by a power of two when huge) and the probabilities split into two bf16
+ * parts, so every finite input is accepted. l, m, O and O_lr are fp32; scores must stay finite in
+ * fp32.
  * Every tensor pointer must be 16-byte aligned. n_kv*d_head and ld_vlr must not exceed 2^22 (the
  * kernel reads 64-row tiles through 32-bit offsets); larger values return LRA_ERR_SHAPE. L_C = 0
  * enqueues nothing.

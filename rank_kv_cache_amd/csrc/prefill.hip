@@ -16,7 +16,8 @@
 //     one with a short causal key range and one with a long one, which evens out the work per
 //     workgroup and per SIMD; a wave stops multiplying after its own last visible key.
 //   * 64-key tiles are staged in LDS in their natural row layout with 128-bit stores, double
-//     buffered: the next tile's global loads are in flight while the current one is multiplied,
+//     buffered; two register sets keep the next two tiles' global loads in flight while the
+//     current one is multiplied (a tile's loads have two tile steps to arrive),
 //     one barrier per tile. A wave takes the whole tile in one softmax step when it sees both of its
 //     32-key blocks (one block on its diagonal), which halves the per-step bookkeeping.
 //   * S^T = K Q^T: A operand = 16 keys x 8 d-elements of the K tile; output lane (q, n) holds keys
@@ -325,8 +326,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         // at the tile's first row whose range ends at row kv_end, with this thread's byte offsets in
         // a tile fixed for the pass: the loads take no vector address arithmetic, and keys past
         // kv_end read zeros. A paged cache reads row kv_end-1 for them. Either way they get P = 0.
-        Vec<T, 8> kpre[KF], vpre[KF], lpre;
-        lpre.zero();   // the adapter-free view stages zero V_lr columns
+        // two register sets: the fast pass keeps two tiles' loads in flight
+        Vec<T, 8> kpre[2][KF], vpre[2][KF], lpre[2];
+        lpre[0].zero();   // the adapter-free view stages zero V_lr columns
+        lpre[1].zero();
         pg_base = -(1 << 30);
         uint32_t koff[KF];
 #pragma unroll
@@ -336,7 +339,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             koff[c] = uint32_t((int64_t(key) * kv_stride + int64_t(g) * D + (f - key * (D / 8)) * 8) * int64_t(sizeof(T)));
         }
         const uint32_t loff = uint32_t((int64_t(tid / (R / 8)) * p.ld_vlr + (tid % (R / 8)) * 8) * int64_t(sizeof(T)));
-        auto fetch = [&](int t) {
+        auto fetch = [&](int t, auto set_tag) {
+            constexpr int S = decltype(set_tag)::value;
             const int kb = t * kBK;
             if constexpr (!PAGED) {
                 const uint32_t rows = uint32_t(min(kBK, kv_end - kb));   // >= 1
@@ -347,14 +351,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                     __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Vp + int64_t(kb) * kv_stride), 0, int(kv_bytes), 0x00020000);
 #pragma unroll
                 for (int c = 0; c < KF; ++c) {
-                    if constexpr (!KREBUILD) buffer_load8(kpre[c], rk, koff[c]);
-                    buffer_load8(vpre[c], rv, koff[c]);
+                    if constexpr (!KREBUILD) buffer_load8(kpre[S][c], rk, koff[c]);
+                    buffer_load8(vpre[S][c], rv, koff[c]);
                 }
                 if (tid < LF && adapted) {
                     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
                         const_cast<T*>(Lp + int64_t(kb) * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride), 0,
                         int(rows * uint32_t(p.ld_vlr * int64_t(sizeof(T)))), 0x00020000);
-                    buffer_load8(lpre, rl, loff);
+                    buffer_load8(lpre[S], rl, loff);
                 }
                 return;
             }
@@ -378,14 +382,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 const int key = f / (D / 8);
                 const int d0 = (f - key * (D / 8)) * 8;
                 const int64_t j = min(kb + key, kv_end - 1) + page_off;
-                if constexpr (!KREBUILD) kpre[c].load(Kp + j * kv_stride + int64_t(g) * D + d0);
-                vpre[c].load(Vp + j * kv_stride + int64_t(g) * D + d0);
+                if constexpr (!KREBUILD) kpre[S][c].load(Kp + j * kv_stride + int64_t(g) * D + d0);
+                vpre[S][c].load(Vp + j * kv_stride + int64_t(g) * D + d0);
             }
             if (tid < LF && adapted) {
                 const int key = tid / (R / 8);
                 const int r0 = (tid - key * (R / 8)) * 8;
                 const int64_t j = min(kb + key, kv_end - 1) + page_off;
-                lpre.load(Lp + j * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride + r0);
+                lpre[S].load(Lp + j * p.ld_vlr + int64_t(agent) * p.vlr_agent_stride + r0);
             }
         };
         // 8 values of one key's row in the pass's P.V element type: fp16 (exact within its range),
@@ -405,7 +409,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 *reinterpret_cast<float4*>(dst + 4) = make_float4(src.v[4], src.v[5], src.v[6], src.v[7]);
             }
         };
-        auto store = [&](int buf) {
+        auto store = [&](int buf, auto set_tag) {
+            constexpr int S = decltype(set_tag)::value;
 #pragma unroll
             for (int c = 0; c < KF; ++c) {
                 const int f = tid + kThreads * c;
@@ -413,18 +418,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
                 const int d0 = (f - key * (D / 8)) * 8;
                 if constexpr (sizeof(T) == 2) {
                     if constexpr (!KREBUILD)
-                        *reinterpret_cast<uint4*>(&sh.k[buf][key * LDK + d0]) = *reinterpret_cast<const uint4*>(kpre[c].w);
+                        *reinterpret_cast<uint4*>(&sh.k[buf][key * LDK + d0]) = *reinterpret_cast<const uint4*>(kpre[S][c].w);
                 } else {
                     float* kd = &sh.k[buf][key * LDK + d0];
-                    *reinterpret_cast<float4*>(kd) = make_float4(kpre[c].v[0], kpre[c].v[1], kpre[c].v[2], kpre[c].v[3]);
-                    *reinterpret_cast<float4*>(kd + 4) = make_float4(kpre[c].v[4], kpre[c].v[5], kpre[c].v[6], kpre[c].v[7]);
+                    *reinterpret_cast<float4*>(kd) = make_float4(kpre[S][c].v[0], kpre[S][c].v[1], kpre[S][c].v[2], kpre[S][c].v[3]);
+                    *reinterpret_cast<float4*>(kd + 4) = make_float4(kpre[S][c].v[4], kpre[S][c].v[5], kpre[S][c].v[6], kpre[S][c].v[7]);
                 }
-                put8(&sh.v[buf][key * LDV + d0], vpre[c]);
+                put8(&sh.v[buf][key * LDV + d0], vpre[S][c]);
             }
             if (tid < LF) {
                 const int key = tid / (R / 8);
                 const int r0 = (tid - key * (R / 8)) * 8;
-                put8(&sh.aux[buf][key * LDX + r0], lpre);
+                put8(&sh.aux[buf][key * LDX + r0], lpre[S]);
             }
         };
         // range-safe pass with LoRA on the keys: key j of the tile rebuilt in fp32 from K_base, K_lr,
@@ -692,15 +697,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         };
 
         if constexpr (!WIDE) {
-            // double-buffered: the next tile's loads are in flight while this one is multiplied
-            fetch(0);
-            store(0);
+            // double-buffered LDS tiles, two tiles' loads in flight: tile t is multiplied while the
+            // loads of t+1 (issued a tile earlier) and t+2 are outstanding
+            constexpr std::integral_constant<int, 0> s0{};
+            constexpr std::integral_constant<int, 1> s1{};
+            fetch(0, s0);
+            if (1 < n_tiles) fetch(1, s1);
+            store(0, s0);
             __syncthreads();
-            for (int t = 0; t < n_tiles; ++t) {
-                const int buf = t & 1;
-                if (t + 1 < n_tiles) fetch(t + 1);
-                tile_step(t, buf);
-                if (t + 1 < n_tiles) store(buf ^ 1);
+            for (int t = 0; t < n_tiles; t += 2) {
+                if (t + 2 < n_tiles) fetch(t + 2, s0);
+                tile_step(t, 0);
+                if (t + 1 < n_tiles) store(1, s1);
+                __syncthreads();
+                if (t + 1 >= n_tiles) break;
+                if (t + 3 < n_tiles) fetch(t + 3, s1);
+                tile_step(t + 1, 1);
+                if (t + 2 < n_tiles) store(0, s0);
                 __syncthreads();
             }
         } else {
@@ -710,16 +723,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             if constexpr (sizeof(T) == 2) {
                 float vm = 0.f;
                 for (int t = 0; t < n_tiles; ++t) {
-                    fetch(t);
+                    fetch(t, std::integral_constant<int, 0>{});
 #pragma unroll
                     for (int c = 0; c < KF; ++c)
 #pragma unroll
                         for (int e2 = 0; e2 < 4; ++e2)
-                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(vpre[c].w[e2]))), fabsf(bf16_hi(vpre[c].w[e2])));
+                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(vpre[0][c].w[e2]))), fabsf(bf16_hi(vpre[0][c].w[e2])));
                     if (tid < LF && adapted) {
 #pragma unroll
                         for (int e2 = 0; e2 < 4; ++e2)
-                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(lpre.w[e2]))), fabsf(bf16_hi(lpre.w[e2])));
+                            vm = fmaxf(fmaxf(vm, fabsf(bf16_lo(lpre[0].w[e2]))), fabsf(bf16_hi(lpre[0].w[e2])));
                     }
                 }
                 atomicMax(&sh.vmax_bits, __float_as_uint(vm));   // |v| >= 0: the bits order like the values
@@ -731,9 +744,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             }
             // one tile at a time (the key parts use both K buffers)
             for (int t = 0; t < n_tiles; ++t) {
-                fetch(t);
+                fetch(t, std::integral_constant<int, 0>{});
                 __syncthreads();   // the previous tile's readers are done
-                store(0);
+                store(0, std::integral_constant<int, 0>{});
                 stage_keys_wide(t);
                 __syncthreads();
                 tile_step(t, 0);

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         // at the tile's first row whose range ends at row kv_end, with this thread's byte offsets in
         // a tile fixed for the pass: the loads take no vector address arithmetic, and keys past
         // kv_end read zeros. A paged cache reads row kv_end-1 for them. Either way they get P = 0.
-        // two register sets: the fast pass keeps two tiles' loads in flight
+        // two register sets: the fast pass keeps two tiles' loads in flight where they fit
         Vec<T, 8> kpre[2][KF], vpre[2][KF], lpre[2];
         lpre[0].zero();   // the adapter-free view stages zero V_lr columns
         lpre[1].zero();
@@ -698,23 +698,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
         if constexpr (!WIDE) {
             // double-buffered LDS tiles, two tiles' loads in flight: tile t is multiplied while the
-            // loads of t+1 (issued a tile earlier) and t+2 are outstanding
+            // loads of t+1 (issued a tile earlier) and t+2 are outstanding. Where the second register
+            // set would not fit beside the accumulators (fp32 inputs; paged rank-16 bf16 with
+            // d_head 128) one tile's loads are in flight instead.
             constexpr std::integral_constant<int, 0> s0{};
             constexpr std::integral_constant<int, 1> s1{};
-            fetch(0, s0);
-            if (1 < n_tiles) fetch(1, s1);
-            store(0, s0);
-            __syncthreads();
-            for (int t = 0; t < n_tiles; t += 2) {
-                if (t + 2 < n_tiles) fetch(t + 2, s0);
-                tile_step(t, 0);
-                if (t + 1 < n_tiles) store(1, s1);
+            constexpr bool DEEP = sizeof(T) == 2 && !(PAGED && R == 16 && D == 128);
+            if constexpr (!DEEP) {
+                fetch(0, s0);
+                store(0, s0);
                 __syncthreads();
-                if (t + 1 >= n_tiles) break;
-                if (t + 3 < n_tiles) fetch(t + 3, s1);
-                tile_step(t + 1, 1);
-                if (t + 2 < n_tiles) store(0, s0);
+                for (int t = 0; t < n_tiles; ++t) {
+                    const int buf = t & 1;
+                    if (t + 1 < n_tiles) fetch(t + 1, s0);
+                    tile_step(t, buf);
+                    if (t + 1 < n_tiles) store(buf ^ 1, s0);
+                    __syncthreads();
+                }
+            } else {
+                fetch(0, s0);
+                if (1 < n_tiles) fetch(1, s1);
+                store(0, s0);
                 __syncthreads();
+                for (int t = 0; t < n_tiles; t += 2) {
+                    if (t + 2 < n_tiles) fetch(t + 2, s0);
+                    tile_step(t, 0);
+                    if (t + 1 < n_tiles) store(1, s1);
+                    __syncthreads();
+                    if (t + 1 >= n_tiles) break;
+                    if (t + 3 < n_tiles) fetch(t + 3, s1);
+                    tile_step(t + 1, 1);
+                    if (t + 2 < n_tiles) store(0, s0);
+                    __syncthreads();
+                }
             }
         } else {
             // the largest |V| / |V_lr| of the staged keys (read once more) brings them to at most 2^64

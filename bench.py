@@ -355,11 +355,10 @@ def bench_prefill(args, torch, lra, W, out):
     def step():
         lra.lra_attn_prefill(Q, c.L_P, K, V, L, B, 0, s.scale, O)
 
-    # ~0.1 s of warm-up launches first: the first launches after the inputs are built run at
-    # lower clocks (about 0.75 ms against 0.55 ms in steady state on MI355X), and the clock keeps
-    # rising over the first tens of launches after the idle time of the input generation
+    # ~20 ms of warm-up launches first: the first launches after the inputs are built run at
+    # lower clocks (about 0.75 ms against 0.55-0.6 ms in steady state on MI355X)
     reps = max(10, args.steps // 5)
-    ms, ms_lo, ms_hi = time_launches_median(step, 5, reps, 200, torch)
+    ms, ms_lo, ms_hi = time_launches_median(step, 5, reps, 30, torch)
     fl = prefill_flops(c.L_P, c.L_C, s.n_q, s.d_head, s.rank)
     tf = fl / (ms * 1e-3) / 1e12
     out["prefill_llama_LP16384_LC2048_r8"] = {
